@@ -1,0 +1,202 @@
+"""Compact (DMS-style) decode attention for MI355X (gfx950).
+
+Python face of libcda_hip.so.  The two calls of the C ABI are exposed under
+their own names (:func:`kv_compact`, :func:`decode_attn_compact`); the class
+:class:`CompactKVCache` holds one layer's device buffers (torch tensors) and
+forwards to them.  All arithmetic runs in the library's HIP kernels; this
+module only checks shapes and passes pointers.  There is no CPU path: if the
+library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_KV_BF16, CDA_KV_FP8_E4M3,
+                   CDA_OP_APPEND, CDA_OP_COUNT, CDA_OP_PACK, CDA_OUT_BF16, CDA_OUT_F32,
+                   CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
+
+__all__ = ["CompactKVCache", "kv_compact", "decode_attn_compact", "CdaError",
+           "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY", "CDA_DEVERR_POOL"]
+
+_DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3}
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def kv_compact(cache: "CompactKVCache", op: int, *, T: int = 0, reserve: int = 0,
+               scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None) -> None:
+    """One kv_compact call (COUNT, PACK or APPEND) on ``cache``'s stream."""
+    a = CdaCompactArgs()
+    a.op, a.T, a.reserve, a.scale_mode = op, T, reserve, scale_mode
+    if keep is not None:
+        if keep.dtype != torch.uint8:
+            raise TypeError("keep must be uint8")
+        if op == CDA_OP_APPEND:
+            if not keep.is_contiguous() or keep.numel() != cache.B * cache.Hkv:
+                raise ValueError("APPEND keep must be a contiguous [B, Hkv] uint8 tensor")
+            a.keep_ld = 1
+        else:
+            if keep.dim() != 3 or keep.shape[0] != cache.B or keep.shape[1] != cache.Hkv:
+                raise ValueError("keep must be [B, Hkv, >=T]")
+            if keep.shape[2] < T or keep.stride(2) != 1 or keep.stride(0) != cache.Hkv * keep.stride(1):
+                raise ValueError("keep rows must be contiguous with a uniform pitch")
+            a.keep_ld = keep.stride(1)
+        a.keep = _ptr(keep)
+    if k is not None:
+        for x in (k, v):
+            if x.dtype != torch.bfloat16 or x.shape[-1] != cache.D or x.stride(-1) != 1:
+                raise ValueError("k, v must be bfloat16 with contiguous rows of D elements")
+        if k.stride() != v.stride():
+            raise ValueError("k and v must share strides")
+        if op == CDA_OP_PACK:      # [B, >=T, Hkv, D]
+            a.stride_b, a.stride_t, a.stride_h = k.stride(0), k.stride(1), k.stride(2)
+        else:                      # [B, Hkv, D]
+            a.stride_b, a.stride_t, a.stride_h = k.stride(0), 0, k.stride(1)
+        a.k, a.v = _ptr(k), _ptr(v)
+    if dst_out is not None:
+        if dst_out.dtype != torch.int32 or not dst_out.is_contiguous() or dst_out.numel() < cache.B * cache.Hkv * T:
+            raise ValueError("dst_out must be a contiguous int32 tensor of B*Hkv*T elements")
+        a.dst_out = _ptr(dst_out)
+    st = _lib.kv_compact(cache.struct, a, _stream(cache.device))
+    if st != 0:
+        raise CdaError(st, "kv_compact")
+
+
+def decode_attn_compact(cache: "CompactKVCache", q: torch.Tensor, out: torch.Tensor,
+                        lse: torch.Tensor | None = None, sm_scale: float = 0.0,
+                        split_tokens: int = 0, workspace: torch.Tensor | None = None) -> None:
+    """One decode_attn_compact call: q [B, Hq, D] bf16 -> out [B, Hq, D]."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3:
+        raise ValueError("q must be a contiguous bfloat16 [B, Hq, D] tensor")
+    B, Hq, D = q.shape
+    if B != cache.B or D != cache.D:
+        raise ValueError("q shape does not match the cache")
+    if out.shape != q.shape or not out.is_contiguous() or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be a contiguous [B, Hq, D] bfloat16 or float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    if workspace is None:
+        workspace = cache.workspace(Hq, split_tokens)
+    out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
+    st = _lib.decode_attn_compact(cache.struct, _ptr(q), Hq, sm_scale, _ptr(out), out_dtype,
+                                  _ptr(lse), split_tokens, _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0,
+                                  _stream(cache.device))
+    if st != 0:
+        raise CdaError(st, "decode_attn_compact")
+
+
+class CompactKVCache:
+    """One layer's compact KV store: metadata and pools as device tensors."""
+
+    def __init__(self, B: int, Hkv: int, D: int, W: int, kv_dtype: str = "bf16",
+                 device="cuda"):
+        if kv_dtype not in _DTYPES:
+            raise ValueError("kv_dtype must be 'bf16' or 'fp8'")
+        _lib.load()
+        self.B, self.Hkv, self.D, self.W = B, Hkv, D, W
+        self.kv_dtype = kv_dtype
+        self.elem_bytes = 2 if kv_dtype == "bf16" else 1
+        self.device = torch.device(device)
+        nh = B * Hkv
+        dev = self.device
+        self.seg_base = torch.zeros(nh + 1, dtype=torch.int64, device=dev)
+        self.seg_cap = torch.zeros(nh, dtype=torch.int32, device=dev)
+        self.comp_len = torch.zeros(nh, dtype=torch.int32, device=dev)
+        self.pos = torch.zeros(max(B, 1), dtype=torch.int32, device=dev)
+        self.ring_keep = torch.zeros(max(nh * W, 1), dtype=torch.uint8, device=dev)
+        self.k_amax = torch.zeros(max(nh, 1), dtype=torch.float32, device=dev)
+        self.v_amax = torch.zeros(max(nh, 1), dtype=torch.float32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.k_pool = None
+        self.v_pool = None
+        self.pool_rows = 0
+        self._ws = {}
+        self.struct = CdaKvCache()
+        self._refresh()
+
+    def _refresh(self):
+        s = self.struct
+        s.B, s.Hkv, s.D, s.W = self.B, self.Hkv, self.D, self.W
+        s.kv_dtype = _DTYPES[self.kv_dtype]
+        s.reserved0 = 0
+        s.pool_rows = self.pool_rows
+        s.k_pool, s.v_pool = _ptr(self.k_pool), _ptr(self.v_pool)
+        s.seg_base, s.seg_cap = _ptr(self.seg_base), _ptr(self.seg_cap)
+        s.comp_len, s.pos = _ptr(self.comp_len), _ptr(self.pos)
+        s.ring_keep = _ptr(self.ring_keep)
+        s.k_amax, s.v_amax = _ptr(self.k_amax), _ptr(self.v_amax)
+        s.err = _ptr(self.err)
+
+    # ---- prefill
+    def count(self, keep, T: int, reserve: int, dst_out=None) -> None:
+        kv_compact(self, CDA_OP_COUNT, T=T, reserve=reserve, keep=keep, dst_out=dst_out)
+
+    def rows_needed(self) -> int:
+        """Pool rows the layout needs (reads seg_base[B*Hkv]: synchronises)."""
+        return int(self.seg_base[-1].item())
+
+    def allocate(self, rows: int | None = None) -> None:
+        rows = self.rows_needed() if rows is None else rows
+        rows = -(-rows // CDA_SEG_ALIGN) * CDA_SEG_ALIGN
+        nbytes = max(rows, 1) * self.D * self.elem_bytes
+        self.k_pool = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.v_pool = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.pool_rows = rows
+        self._ws.clear()
+        self._refresh()
+
+    def pack(self, k, v, keep, T: int, scale_mode: int = 0) -> None:
+        kv_compact(self, CDA_OP_PACK, T=T, scale_mode=scale_mode, keep=keep, k=k, v=v)
+
+    def compact(self, k, v, keep, T: int, reserve: int, scale_mode: int = 0,
+                dst_out=None) -> None:
+        """COUNT, size the pools, PACK (one host synchronisation)."""
+        self.count(keep, T, reserve, dst_out)
+        self.allocate()
+        self.pack(k, v, keep, T, scale_mode)
+
+    # ---- decode
+    def append(self, k_new, v_new, keep_new) -> None:
+        kv_compact(self, CDA_OP_APPEND, keep=keep_new, k=k_new, v=v_new)
+
+    def workspace(self, Hq: int, split_tokens: int = 0) -> torch.Tensor:
+        key = (Hq, split_tokens)
+        if key not in self._ws:
+            n = _lib.attn_workspace_bytes(self.struct, Hq, split_tokens)
+            self._ws[key] = torch.empty(max(n, 16), dtype=torch.uint8, device=self.device)
+        return self._ws[key]
+
+    def attention(self, q, out=None, out_dtype=torch.bfloat16, lse=None, sm_scale: float = 0.0,
+                  split_tokens: int = 0, workspace=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
+        decode_attn_compact(self, q, out, lse, sm_scale, split_tokens, workspace)
+        return out
+
+    # ---- inspection (synchronise)
+    def error_word(self) -> int:
+        return int(self.err.item())
+
+    def stored_rows(self) -> torch.Tensor:
+        ring = torch.clamp(self.pos[: self.B].to(torch.int64), max=self.W)
+        return ring.repeat_interleave(self.Hkv) + self.comp_len.to(torch.int64)
+
+    def v_rows(self) -> torch.Tensor:
+        """The V pool as [pool_rows, D * elem_bytes] bytes in row order (a
+        gather of the column-major tiles, for inspection and tests)."""
+        e, D = self.elem_bytes, self.D
+        t = self.v_pool[: self.pool_rows * D * e].view(-1, D, CDA_SEG_ALIGN, e)
+        return t.permute(0, 2, 1, 3).reshape(self.pool_rows, D * e)
+
+    def k_rows(self) -> torch.Tensor:
+        return self.k_pool[: self.pool_rows * self.D * self.elem_bytes].view(self.pool_rows, -1)

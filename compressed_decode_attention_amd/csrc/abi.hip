@@ -1,0 +1,130 @@
+// C-ABI entry points declared in include/cda.h: argument validation, then
+// the launchers.  Nothing here allocates, frees, synchronises or prints.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/cda.h"
+#include "cda_launch.h"
+
+namespace {
+
+constexpr int kDefaultSplit = 256;   // rows per attention work unit
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_cache(const cda_kv_cache* c) {
+  if (!c) return CDA_ERR_INVALID_ARG;
+  if (c->B < 0 || c->Hkv < 1 || c->W < 0 || c->reserved0 != 0) return CDA_ERR_INVALID_ARG;
+  if (c->W > (1 << 28)) return CDA_ERR_INVALID_ARG;
+  if (c->D != 64 && c->D != 128) return CDA_ERR_UNSUPPORTED;
+  if (c->kv_dtype != CDA_KV_BF16 && c->kv_dtype != CDA_KV_FP8_E4M3) return CDA_ERR_UNSUPPORTED;
+  if ((int64_t)c->B * c->Hkv > (1 << 24)) return CDA_ERR_INVALID_ARG;
+  if (!c->seg_base || !c->seg_cap || !c->comp_len || !c->err) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+// Pools and per-sequence state used by PACK, APPEND and attention.
+int32_t check_pools(const cda_kv_cache* c) {
+  if (c->pool_rows < 0 || c->pool_rows % CDA_SEG_ALIGN != 0) return CDA_ERR_INVALID_ARG;
+  if (c->pool_rows > 0 && (!c->k_pool || !c->v_pool)) return CDA_ERR_INVALID_ARG;
+  if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16)) return CDA_ERR_INVALID_ARG;
+  if (!c->pos || (c->W > 0 && !c->ring_keep)) return CDA_ERR_INVALID_ARG;
+  if (c->kv_dtype == CDA_KV_FP8_E4M3 && (!c->k_amax || !c->v_amax)) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+int32_t check_bf16_rows(const void* k, const void* v, int64_t sb, int64_t st, int64_t sh) {
+  if (!k || !v) return CDA_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16)) return CDA_ERR_INVALID_ARG;
+  if (sb < 0 || st < 0 || sh < 0 || sb % 8 || st % 8 || sh % 8) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? CDA_OK : CDA_ERR_HIP; }
+
+int tiles_per_unit(int32_t split_tokens) {
+  const int s = split_tokens > 0 ? split_tokens : kDefaultSplit;
+  return (s + CDA_SEG_ALIGN - 1) / CDA_SEG_ALIGN;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kv_compact(const cda_kv_cache* c, const cda_compact_args* a, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != CDA_OK) return st;
+  if (!a) return CDA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nh = (int64_t)c->B * c->Hkv;
+  switch (a->op) {
+    case CDA_OP_COUNT:
+    case CDA_OP_PACK: {
+      if (a->T < 0 || a->T > (1 << 24) || a->keep_ld < a->T) return CDA_ERR_INVALID_ARG;
+      if (nh > 0 && a->T > 0 && !a->keep) return CDA_ERR_INVALID_ARG;
+      if (a->op == CDA_OP_COUNT) {
+        if (a->reserve < 0 || a->reserve > (1 << 28)) return CDA_ERR_INVALID_ARG;
+        return hip_status(cda::launch_count(*c, *a, s));
+      }
+      if ((st = check_pools(c)) != CDA_OK) return st;
+      if (a->scale_mode != 0 && a->scale_mode != 1) return CDA_ERR_INVALID_ARG;
+      if (nh > 0 && a->T > 0 &&
+          (st = check_bf16_rows(a->k, a->v, a->stride_b, a->stride_t, a->stride_h)) != CDA_OK)
+        return st;
+      return hip_status(cda::launch_pack(*c, *a, s));
+    }
+    case CDA_OP_APPEND: {
+      if ((st = check_pools(c)) != CDA_OK) return st;
+      if (nh > 0) {
+        if (!a->keep) return CDA_ERR_INVALID_ARG;
+        if ((st = check_bf16_rows(a->k, a->v, a->stride_b, 0, a->stride_h)) != CDA_OK) return st;
+      }
+      return hip_status(cda::launch_append(*c, *a, s));
+    }
+    default:
+      return CDA_ERR_INVALID_ARG;
+  }
+}
+
+size_t cda_attn_workspace_bytes(const cda_kv_cache* c, int32_t Hq, int32_t split_tokens) {
+  if (check_cache(c) != CDA_OK || Hq <= 0 || Hq % c->Hkv != 0 || split_tokens < 0) return 0;
+  return cda::attn_workspace_bytes(*c, Hq / c->Hkv, tiles_per_unit(split_tokens));
+}
+
+int32_t decode_attn_compact(const cda_kv_cache* c, const void* q, int32_t Hq, float sm_scale,
+                            void* out, int32_t out_dtype, float* lse, int32_t split_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != CDA_OK) return st;
+  if ((st = check_pools(c)) != CDA_OK) return st;
+  if (Hq <= 0 || split_tokens < 0) return CDA_ERR_INVALID_ARG;
+  if (Hq % c->Hkv != 0 || Hq / c->Hkv > CDA_MAX_GQA) return CDA_ERR_UNSUPPORTED;
+  if (out_dtype != CDA_OUT_BF16 && out_dtype != CDA_OUT_F32) return CDA_ERR_UNSUPPORTED;
+  if (c->B > 0) {
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 4)) return CDA_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return CDA_ERR_INVALID_ARG;
+  }
+  const int tpu = tiles_per_unit(split_tokens);
+  const size_t need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, tpu);
+  if (workspace_bytes < need) return CDA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned(workspace, 16))) return CDA_ERR_INVALID_ARG;
+  if (cda::attn_max_units(*c, tpu) > 0x7FFFFFFF) return CDA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(cda::launch_attn(*c, q, Hq, sm_scale, out, out_dtype == CDA_OUT_F32, lse,
+                                     tpu, workspace, s));
+}
+
+const char* cda_status_string(int32_t status) {
+  switch (status) {
+    case CDA_OK: return "ok";
+    case CDA_ERR_INVALID_ARG: return "invalid argument";
+    case CDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case CDA_ERR_WORKSPACE: return "workspace too small";
+    case CDA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t cda_version(void) { return CDA_VERSION; }
+
+}  // extern "C"

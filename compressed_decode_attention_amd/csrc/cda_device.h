@@ -1,0 +1,115 @@
+// Device-side types and helpers shared by the gfx950 kernels of the compact
+// decode-attention library.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/cda.h"
+
+namespace cda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kTile = CDA_SEG_ALIGN;   // rows per V tile and per segment granule
+constexpr int kBlock = 256;            // threads per workgroup of every kernel
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// OCP E4M3FN encode of one f32, round-to-nearest-even, saturating at +-448,
+// NaN -> 0x7F with the input's sign.  Integer arithmetic on the binary32
+// fields: the 3 kept mantissa bits are rounded on the 20 dropped ones, with
+// the carry running into the exponent field; values below 2^-6 are rounded
+// to a multiple of 2^-9 from the full 24-bit significand.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;   // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // >= 448 or infinite
+  const uint32_t e = a >> 23;
+  if (e >= 121u) {                            // >= 2^-6: normal code
+    const uint32_t m = a & 0x7FFFFFu;
+    uint32_t code = ((e - 120u) << 3) | (m >> 20);
+    const uint32_t rem = m & 0xFFFFFu;
+    code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+    return sign | code;
+  }
+  if (e < 110u) return sign;                  // below 2^-17: rounds to zero
+  const uint32_t full = (a & 0x7FFFFFu) | 0x800000u;  // value = full * 2^(e-150)
+  const uint32_t shift = 141u - e;                     // in units of 2^-9
+  uint32_t q = full >> shift;
+  const uint32_t rem = full & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1u);
+  q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+  return sign | q;
+}
+
+// Dequantisation and quantisation factors from a per-head absmax.
+__device__ __forceinline__ float fp8_scale(float amax) {
+  return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(amax, 448.0f) : 1.0f;
+}
+__device__ __forceinline__ float fp8_inv_scale(float amax) {
+  return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(448.0f, amax) : 1.0f;
+}
+
+// Four FP8 codes (one dword) -> four bf16 / f16 values, exact.
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  bf16x2 a, b, c, d;
+  fp8x4_to_bf16(w0, a, b);
+  fp8x4_to_bf16(w1, c, d);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Exclusive prefix sum over the 256 threads of a workgroup.  smem: >= 4 ints.
+// Every thread of the workgroup must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* smem) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) smem[wid] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / 64; ++w) {
+    int s = smem[w];
+    before += (w < wid) ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__device__ __forceinline__ int block_sum(int v, int* smem) {
+  int total;
+  block_exclusive_scan(v, &total, smem);
+  return total;
+}
+
+}  // namespace cda

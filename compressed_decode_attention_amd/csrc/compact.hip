@@ -1,0 +1,461 @@
+// Prefill compaction and decode-time append of the compact KV store
+// (FastDMS page, release paragraph: a compact store that physically
+// reclaims evicted slots; memory-table paragraph: cache + staging window).
+//
+//   count_kernel     keep mask -> per-segment kept count, optional dst map
+//   seg_scan_kernel  aligned segment sizes -> seg_base (exclusive prefix sum)
+//   amax_kernel      per-segment absmax of the stored prefill K and V (FP8)
+//   pack_kernel      stored prefill rows -> pool rows (BF16 copy / FP8 encode)
+//   append_kernel    one decode step: ring exit -> compact tail, new token -> ring
+//
+// All of these run once per prefill or move at most one row per segment per
+// step; the decode hot loop is the attention kernel.
+#include "cda_device.h"
+#include "cda_launch.h"
+
+namespace cda {
+namespace {
+
+// ---------------------------------------------------------------- COUNT
+
+__global__ __launch_bounds__(kBlock) void count_kernel(
+    const uint8_t* __restrict__ keep, int64_t keep_ld, int T, int W, int reserve,
+    int32_t* __restrict__ comp_len, int32_t* __restrict__ seg_cap,
+    int32_t* __restrict__ dst_out) {
+  __shared__ int smem[4];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const uint8_t* row = keep + (int64_t)i * keep_ld;
+  const int ncand = T - W > 0 ? T - W : 0;       // positions older than the window
+  const int limit = dst_out ? T : ncand;
+  int running = 0;
+  for (int base = 0; base < limit; base += kBlock * 16) {
+    const int p0 = base + tid * 16;
+    uint32_t flags = 0;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int p = p0 + j;
+      const int f = (p < ncand) && row[p] != 0;
+      flags |= (uint32_t)f << j;
+      cnt += f;
+    }
+    int total;
+    int rank = block_exclusive_scan(cnt, &total, smem) + running;
+    if (dst_out) {
+      int32_t* d = dst_out + (int64_t)i * T;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int p = p0 + j;
+        if (p < T) {
+          int r = -1;
+          if (p >= ncand) r = p % W;                 // ring row (W > 0 here)
+          else if ((flags >> j) & 1u) r = W + rank++;
+          d[p] = r;
+        }
+      }
+    }
+    running += total;
+  }
+  if (tid == 0) {
+    comp_len[i] = running;
+    seg_cap[i] = running + reserve;
+  }
+}
+
+// Exclusive prefix sum (int64) over the 256 threads of a workgroup.
+__device__ __forceinline__ long long block_exclusive_scan64(long long v, long long* total,
+                                                            long long* smem) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  long long x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    long long y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) smem[wid] = x;
+  __syncthreads();
+  long long before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / 64; ++w) {
+    before += (w < wid) ? smem[w] : 0;
+    all += smem[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kBlock) void seg_scan_kernel(
+    int nh, int W, const int32_t* __restrict__ seg_cap, int64_t* __restrict__ seg_base,
+    int32_t* __restrict__ err) {
+  __shared__ long long smem[4];
+  long long carry = 0;
+  for (int base = 0; base < nh; base += kBlock) {
+    const int i = base + threadIdx.x;
+    long long size = 0;
+    if (i < nh) size = ((long long)W + seg_cap[i] + kTile - 1) / kTile * kTile;
+    long long total;
+    long long ex = block_exclusive_scan64(size, &total, smem) + carry;
+    if (i < nh) seg_base[i] = ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    seg_base[nh] = carry;
+    err[0] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- PACK
+
+// |x| of a bf16 as the upper half of a binary32 bit pattern; unsigned
+// comparison of these orders magnitudes, and any NaN compares largest.
+__device__ __forceinline__ uint32_t abs_bits(uint32_t word, int half) {
+  return ((word >> (16 * half)) & 0x7FFFu) << 16;
+}
+
+__global__ __launch_bounds__(kBlock) void amax_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t sb, int64_t st,
+    int64_t sh, const uint8_t* __restrict__ keep, int64_t keep_ld, int T, int W, int Hkv,
+    int D, float* __restrict__ k_amax, float* __restrict__ v_amax) {
+  __shared__ uint32_t red[2][kBlock / 64];
+  const int i = blockIdx.x, b = i / Hkv, h = i - b * Hkv;
+  const int lpr = D / 8;                 // lanes per row, 8 bf16 (16 B) each
+  const int rows_per_pass = kBlock / lpr;
+  const int lr = threadIdx.x % lpr, r = threadIdx.x / lpr;
+  const uint8_t* krow = keep + (int64_t)i * keep_ld;
+  uint32_t mk = 0, mv = 0;
+  for (int p = r; p < T; p += rows_per_pass) {
+    if (p < T - W && krow[p] == 0) continue;   // evicted: not stored
+    const int64_t off = (int64_t)b * sb + (int64_t)p * st + (int64_t)h * sh + lr * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(k + off);
+    const u32x4 c = *reinterpret_cast<const u32x4*>(v + off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        mk = max(mk, abs_bits(a[w], hf));
+        mv = max(mv, abs_bits(c[w], hf));
+      }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, 64));
+    mv = max(mv, (uint32_t)__shfl_xor((int)mv, o, 64));
+  }
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wid] = mk;
+    red[1][wid] = mv;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0, c = 0;
+    for (int w = 0; w < kBlock / 64; ++w) {
+      a = max(a, red[0][w]);
+      c = max(c, red[1][w]);
+    }
+    k_amax[i] = __uint_as_float(a);
+    v_amax[i] = __uint_as_float(c);
+  }
+}
+
+struct PackParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t sb, st, sh;
+  const uint8_t* keep;
+  int64_t keep_ld;
+  int T, W, Hkv, D;
+  const int64_t* seg_base;
+  int64_t pool_rows;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  uint8_t* ring_keep;
+  int32_t* pos;
+  const float* k_amax;
+  const float* v_amax;
+  int32_t* err;
+};
+
+// Byte offset of element (row, d) in a V pool of column-major 64-row tiles.
+__device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
+  return (row / kTile) * kTile * D + (int64_t)d * kTile + (row % kTile);
+}
+
+// Workgroup (segment i, chunk c) handles prefill positions [256c, 256c+256).
+template <bool FP8>
+__global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
+  __shared__ int smem[4];
+  __shared__ int s_pos[kBlock], s_dst[kBlock];
+  const int i = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int T = p.T, W = p.W, D = p.D;
+  const uint8_t* row = p.keep + (int64_t)i * p.keep_ld;
+  const int ncand = T - W > 0 ? T - W : 0;
+
+  // kept older positions before this chunk
+  int before = 0;
+  const int lim = min(c * kBlock, ncand);
+  for (int q = tid; q < lim; q += kBlock) before += row[q] != 0;
+  before = block_sum(before, smem);
+
+  const int pp = c * kBlock + tid;
+  const int flag = (pp < ncand) && row[pp] != 0;
+  int dummy;
+  const int rank = block_exclusive_scan(flag, &dummy, smem);
+  int stored = 0, dst = -1;
+  if (pp < T) {
+    if (pp >= ncand) {
+      dst = pp % W;
+      stored = 1;
+    } else if (flag) {
+      dst = W + before + rank;
+      stored = 1;
+    }
+  }
+  if (stored && dst < W) p.ring_keep[(int64_t)i * W + dst] = row[pp] != 0;
+  if (c == 0) {
+    for (int r = T + tid; r < W; r += kBlock) p.ring_keep[(int64_t)i * W + r] = 0;
+    if (h == 0 && tid == 0) p.pos[b] = T;
+  }
+  int nst;
+  const int slot = block_exclusive_scan(stored, &nst, smem);
+  if (stored) {
+    s_pos[slot] = pp;
+    s_dst[slot] = dst;
+  }
+  __syncthreads();
+
+  float kinv = 1.0f, vinv = 1.0f;
+  if (FP8) {
+    kinv = fp8_inv_scale(p.k_amax[i]);
+    vinv = fp8_inv_scale(p.v_amax[i]);
+  }
+  const int64_t base = p.seg_base[i];
+  const int lpr = D / 8;
+  for (int e = tid / lpr; e < nst; e += kBlock / lpr) {
+    const int64_t r = base + s_dst[e];
+    if (r < 0 || r >= p.pool_rows) {
+      if (tid % lpr == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+      continue;
+    }
+    const int d0 = (tid % lpr) * 8;
+    const int64_t off = (int64_t)b * p.sb + (int64_t)s_pos[e] * p.st + (int64_t)h * p.sh + d0;
+    const u32x4 kin = *reinterpret_cast<const u32x4*>(p.k + off);
+    const u32x4 vin = *reinterpret_cast<const u32x4*>(p.v + off);
+    if (FP8) {
+      uint32_t kc[2] = {0, 0};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t kb = (kin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        const uint32_t vb = (vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        kc[j >> 2] |= e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv)) << (8 * (j & 3));
+        p.v_pool[v_elem(r, d0 + j, D)] =
+            (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+      }
+      *reinterpret_cast<u32x2*>(p.k_pool + r * D + d0) = u32x2{kc[0], kc[1]};
+    } else {
+      *reinterpret_cast<u32x4*>(p.k_pool + (r * D + d0) * 2) = kin;
+      uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        vp[v_elem(r, d0 + j, D)] = (uint16_t)((vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- APPEND
+
+struct AppendParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t sb, sh;
+  const uint8_t* keep;
+  int W, Hkv, D;
+  const int64_t* seg_base;
+  const int32_t* seg_cap;
+  int32_t* comp_len;
+  int32_t* pos;
+  uint8_t* ring_keep;
+  const float* k_amax;
+  const float* v_amax;
+  int64_t pool_rows;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int32_t* err;
+};
+
+// Copy (or encode) one element of K and V between rows / from the input.
+template <bool FP8>
+__device__ __forceinline__ void move_elem(const AppendParams& p, int64_t from, int64_t to, int d) {
+  if (FP8) {
+    p.k_pool[to * p.D + d] = p.k_pool[from * p.D + d];
+    p.v_pool[v_elem(to, d, p.D)] = p.v_pool[v_elem(from, d, p.D)];
+  } else {
+    uint16_t* kp = reinterpret_cast<uint16_t*>(p.k_pool);
+    uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool);
+    kp[to * p.D + d] = kp[from * p.D + d];
+    vp[v_elem(to, d, p.D)] = vp[v_elem(from, d, p.D)];
+  }
+}
+
+// Workgroup b handles sequence b: every head's ring exit, then every new token.
+template <bool FP8>
+__global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
+  __shared__ long long s_from[kBlock], s_to[kBlock], s_new[kBlock];
+  __shared__ float s_kinv[kBlock], s_vinv[kBlock];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int W = p.W, D = p.D;
+  const int P = p.pos[b];
+  for (int h0 = 0; h0 < p.Hkv; h0 += kBlock) {
+    const int nhc = min(kBlock, p.Hkv - h0);
+    if (tid < nhc) {
+      const int h = h0 + tid;
+      const int64_t i = (int64_t)b * p.Hkv + h;
+      const int64_t base = p.seg_base[i];
+      int cl = p.comp_len[i];
+      const int cap = p.seg_cap[i];
+      long long from = -1, to = -1, nw = -1;
+      const int kept = p.keep[i] != 0;
+      if (W > 0) {
+        const int exit_pos = P - W;
+        if (exit_pos >= 0 && p.ring_keep[i * W + exit_pos % W]) {
+          if (cl < cap) {
+            from = base + exit_pos % W;
+            to = base + W + cl;
+            ++cl;
+          } else {
+            atomicOr(p.err, CDA_DEVERR_CAPACITY);
+          }
+        }
+        nw = base + P % W;
+        p.ring_keep[i * W + P % W] = (uint8_t)kept;
+      } else if (kept) {
+        if (cl < cap) {
+          nw = base + cl;
+          ++cl;
+        } else {
+          atomicOr(p.err, CDA_DEVERR_CAPACITY);
+        }
+      }
+      if ((from >= 0 && (from >= p.pool_rows || to >= p.pool_rows)) || nw >= p.pool_rows) {
+        atomicOr(p.err, CDA_DEVERR_POOL);
+        from = to = -1;
+        if (nw >= p.pool_rows) nw = -1;
+      }
+      p.comp_len[i] = cl;
+      s_from[tid] = from;
+      s_to[tid] = to;
+      s_new[tid] = nw;
+      s_kinv[tid] = FP8 ? fp8_inv_scale(p.k_amax[i]) : 1.0f;
+      s_vinv[tid] = FP8 ? fp8_inv_scale(p.v_amax[i]) : 1.0f;
+    }
+    __syncthreads();
+    // the token leaving the window moves out of its ring row first ...
+    for (int w = tid; w < nhc * D; w += kBlock) {
+      const int t = w / D, d = w - t * D;
+      if (s_from[t] >= 0) move_elem<FP8>(p, s_from[t], s_to[t], d);
+    }
+    __syncthreads();
+    // ... then the new token takes the row
+    for (int w = tid; w < nhc * D; w += kBlock) {
+      const int t = w / D, d = w - t * D;
+      const long long r = s_new[t];
+      if (r < 0) continue;
+      const int64_t off = (int64_t)b * p.sb + (int64_t)(h0 + t) * p.sh + d;
+      const uint16_t kb = p.k[off], vb = p.v[off];
+      if (FP8) {
+        p.k_pool[r * D + d] = (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), s_kinv[t]));
+        p.v_pool[v_elem(r, d, D)] =
+            (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), s_vinv[t]));
+      } else {
+        reinterpret_cast<uint16_t*>(p.k_pool)[r * D + d] = kb;
+        reinterpret_cast<uint16_t*>(p.v_pool)[v_elem(r, d, D)] = vb;
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) p.pos[b] = P + 1;
+}
+
+}  // namespace
+
+hipError_t launch_count(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
+  const int nh = c.B * c.Hkv;
+  if (nh > 0) {
+    count_kernel<<<nh, kBlock, 0, s>>>(a.keep, a.keep_ld, a.T, c.W, a.reserve, c.comp_len,
+                                       c.seg_cap, a.dst_out);
+  }
+  seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
+  const int nh = c.B * c.Hkv;
+  if (nh == 0) return hipGetLastError();
+  const bool fp8 = c.kv_dtype == CDA_KV_FP8_E4M3;
+  if (fp8 && a.scale_mode == 0) {
+    amax_kernel<<<nh, kBlock, 0, s>>>(static_cast<const uint16_t*>(a.k),
+                                      static_cast<const uint16_t*>(a.v), a.stride_b, a.stride_t,
+                                      a.stride_h, a.keep, a.keep_ld, a.T, c.W, c.Hkv, c.D,
+                                      c.k_amax, c.v_amax);
+  }
+  PackParams p;
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.sb = a.stride_b;
+  p.st = a.stride_t;
+  p.sh = a.stride_h;
+  p.keep = a.keep;
+  p.keep_ld = a.keep_ld;
+  p.T = a.T;
+  p.W = c.W;
+  p.Hkv = c.Hkv;
+  p.D = c.D;
+  p.seg_base = c.seg_base;
+  p.pool_rows = c.pool_rows;
+  p.k_pool = static_cast<uint8_t*>(c.k_pool);
+  p.v_pool = static_cast<uint8_t*>(c.v_pool);
+  p.ring_keep = c.ring_keep;
+  p.pos = c.pos;
+  p.k_amax = c.k_amax;
+  p.v_amax = c.v_amax;
+  p.err = c.err;
+  dim3 grid(nh, a.T > 0 ? (a.T + kBlock - 1) / kBlock : 1);
+  if (fp8)
+    pack_kernel<true><<<grid, kBlock, 0, s>>>(p);
+  else
+    pack_kernel<false><<<grid, kBlock, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
+  if (c.B * c.Hkv == 0) return hipGetLastError();
+  AppendParams p;
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.sb = a.stride_b;
+  p.sh = a.stride_h;
+  p.keep = a.keep;
+  p.W = c.W;
+  p.Hkv = c.Hkv;
+  p.D = c.D;
+  p.seg_base = c.seg_base;
+  p.seg_cap = c.seg_cap;
+  p.comp_len = c.comp_len;
+  p.pos = c.pos;
+  p.ring_keep = c.ring_keep;
+  p.k_amax = c.k_amax;
+  p.v_amax = c.v_amax;
+  p.pool_rows = c.pool_rows;
+  p.k_pool = static_cast<uint8_t*>(c.k_pool);
+  p.v_pool = static_cast<uint8_t*>(c.v_pool);
+  p.err = c.err;
+  if (c.kv_dtype == CDA_KV_FP8_E4M3)
+    append_kernel<true><<<c.B, kBlock, 0, s>>>(p);
+  else
+    append_kernel<false><<<c.B, kBlock, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace cda

@@ -1,0 +1,189 @@
+/*
+ * cda.h -- C ABI of the compact decode-attention library (libcda_hip.so).
+ *
+ * What it implements (FastDMS page, "FastDMS: 6.4X KV-cache compression
+ * running faster than vLLM BF16/FP8"):
+ *   - DMS paragraph: each (layer, KV head) keeps only the tokens its learned
+ *     eviction decision retains.  The decision is an input here: one keep
+ *     byte per (sequence, KV head, position), nonzero = keep.
+ *   - Release paragraph: a compact KV store that physically reclaims evicted
+ *     slots.  kv_compact turns a keep mask into prefix-sum offsets and
+ *     stream-compacts K and V into one packed segment per (sequence, KV head).
+ *   - Memory-table paragraph, "cache or cache + staging": the W most recent
+ *     tokens (the current one included) are always kept, in a ring of W rows
+ *     at the front of each segment; a token leaving the ring moves to the
+ *     compact tail if its keep bit is set (decode-time append).
+ *   - Summary bullets, FP8 and BF16: rows are stored as BF16 or as OCP
+ *     E4M3FN FP8 with one absmax scale per (sequence, KV head) for K and one
+ *     for V.
+ *   - decode_attn_compact: single-token GQA decode attention over the
+ *     variable-length compact segments, split into work units whose partial
+ *     softmax states are combined by a log-sum-exp merge.  With FP8 the
+ *     codes are converted in registers and the scales are folded into the
+ *     logit scale and the output (the decompress-in-matvec idea of the
+ *     PackKV abstract).
+ *
+ * One library call = one layer.  All buffers are device memory owned by the
+ * caller; the library never allocates, frees or synchronises, and enqueues
+ * everything on the caller's stream (a hipStream_t passed as void*, NULL =
+ * the null stream).  It keeps no global state and is re-entrant; two calls
+ * that touch the same cache must be ordered by the caller (same stream).
+ *
+ * Storage layout of one layer (all sizes in rows of D elements):
+ *   segment i = b*Hkv + h starts at pool row seg_base[i]; its rows are
+ *     [0, W)               ring: position p lives in row p mod W
+ *     [W, W + seg_cap[i])  compact rows, in ascending position order
+ *   and its size W + seg_cap[i] is rounded up to CDA_SEG_ALIGN rows, so
+ *   seg_base[i+1] = seg_base[i] + roundup(W + seg_cap[i], CDA_SEG_ALIGN).
+ *   The rows holding data are always the contiguous run [0, n_i) with
+ *   n_i = min(W, pos[b]) + comp_len[i].
+ *   k_pool: row-major, row r at byte r * D * e (e = 2 for BF16, 1 for FP8).
+ *   v_pool: tiles of CDA_SEG_ALIGN rows stored column-major: element (r, d)
+ *     at byte ((r / 64) * 64 * D + d * 64 + r % 64) * e, so that the 64
+ *     values of one column of a tile are contiguous.
+ *   FP8: code = E4M3FN_RNE_SATURATE(f32(x) * inv), inv = 448 / amax and
+ *   value = code * s, s = amax / 448 (both single f32 divisions; s = inv = 1
+ *   when amax is 0 or not finite).  amax is the largest |x| over the
+ *   stored prefill tokens, per (sequence, KV head), for K and V separately;
+ *   decode-time tokens use these frozen scales and saturate at +-448.
+ */
+#ifndef CDA_H
+#define CDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CDA_VERSION 1
+#define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
+#define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
+
+/* Return codes of every call. */
+enum cda_status {
+    CDA_OK = 0,
+    CDA_ERR_INVALID_ARG = 1,    /* NULL or misaligned pointer, bad size/stride */
+    CDA_ERR_UNSUPPORTED = 2,    /* head_dim not 64/128, Hq % Hkv != 0, Hq/Hkv > 16, dtype */
+    CDA_ERR_WORKSPACE = 3,      /* workspace smaller than cda_attn_workspace_bytes */
+    CDA_ERR_HIP = 4             /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Bits of the device error word cache->err (set with atomic OR on the GPU;
+ * the host sees them only after it synchronises and copies the word). */
+#define CDA_DEVERR_CAPACITY 1   /* APPEND: a segment's compact region was full; that token was dropped */
+#define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written */
+
+enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1 };
+enum cda_out_dtype { CDA_OUT_BF16 = 0, CDA_OUT_F32 = 1 };
+enum cda_compact_op { CDA_OP_COUNT = 0, CDA_OP_PACK = 1, CDA_OP_APPEND = 2 };
+
+/*
+ * One layer's compact store.  The struct itself is host memory read by
+ * each call; every pointer in it is device memory owned by the caller.
+ * Pointers must be 16-byte aligned (k_pool, v_pool) or naturally aligned.
+ */
+typedef struct cda_kv_cache {
+    int32_t B;          /* sequences */
+    int32_t Hkv;        /* KV heads */
+    int32_t D;          /* head_dim: 64 or 128 */
+    int32_t W;          /* always-kept recent window (ring rows), >= 0 */
+    int32_t kv_dtype;   /* enum cda_kv_dtype */
+    int32_t reserved0;  /* must be 0 */
+    int64_t pool_rows;  /* rows allocated in k_pool and v_pool (multiple of 64) */
+    void *k_pool;       /* [pool_rows, D] */
+    void *v_pool;       /* [pool_rows / 64][D][64] */
+    int64_t *seg_base;  /* [B*Hkv + 1]; written by COUNT; [B*Hkv] = rows needed */
+    int32_t *seg_cap;   /* [B*Hkv]; written by COUNT */
+    int32_t *comp_len;  /* [B*Hkv]; written by COUNT, grown by APPEND */
+    int32_t *pos;       /* [B]; tokens seen so far (next position); PACK sets T */
+    uint8_t *ring_keep; /* [B*Hkv*W]; keep bit of the token each ring row holds */
+    float *k_amax;      /* [B*Hkv]; FP8 absmax of K (PACK computes or takes it) */
+    float *v_amax;      /* [B*Hkv]; FP8 absmax of V */
+    int32_t *err;       /* [1]; device error word, CDA_DEVERR_* bits; COUNT clears it */
+} cda_kv_cache;
+
+/*
+ * Arguments of kv_compact.  Element strides are in elements of the BF16
+ * input; rows of D elements must be contiguous and 16-byte aligned.
+ */
+typedef struct cda_compact_args {
+    int32_t op;         /* enum cda_compact_op */
+    int32_t T;          /* COUNT, PACK: prefill length, 0 <= T <= 2^24 */
+    int32_t reserve;    /* COUNT: spare compact rows per segment for decode growth (>= 0) */
+    int32_t scale_mode; /* PACK with FP8: 0 = compute k_amax/v_amax, 1 = use them as given */
+    const uint8_t *keep;/* COUNT, PACK: row i = b*Hkv+h at keep + i*keep_ld, first T bytes used;
+                           APPEND: [B*Hkv] bytes, one per head for the new token */
+    int64_t keep_ld;    /* COUNT, PACK: bytes between keep rows (>= T) */
+    const void *k;      /* PACK: BF16, (b,t,h,d) at b*stride_b + t*stride_t + h*stride_h + d;
+                           APPEND: BF16, (b,h,d) at b*stride_b + h*stride_h + d */
+    const void *v;      /* same layout as k */
+    int64_t stride_b, stride_t, stride_h;
+    int32_t *dst_out;   /* COUNT, optional (may be NULL): [B*Hkv*T] int32, the segment row
+                           each position is stored in (ring p mod W or W + rank), -1 if evicted */
+} cda_compact_args;
+
+/*
+ * kv_compact -- prefill compaction and decode-time append of one layer.
+ *
+ * CDA_OP_COUNT: per segment, counts kept positions p <= T-1-W (comp_len),
+ *   sets seg_cap = comp_len + reserve, and writes seg_base by an exclusive
+ *   prefix sum of the aligned segment sizes; seg_base[B*Hkv] is the number
+ *   of pool rows to allocate.  Optionally writes dst_out.  Clears *err.
+ *   Reads keep; needs seg_base, seg_cap, comp_len, err (pools may be NULL).
+ * CDA_OP_PACK: after COUNT (same keep, T), writes every stored prefill row
+ *   (the W most recent positions and every kept older one) to its pool row,
+ *   fills ring_keep, sets pos[b] = T and, for FP8 with scale_mode 0,
+ *   computes k_amax/v_amax first.  Rows the layout leaves unused are not
+ *   written.
+ * CDA_OP_APPEND: one decode step: for each sequence b (P = pos[b]) and head,
+ *   the token at P-W leaves the ring and, if its keep bit is set, is copied
+ *   to compact row W + comp_len (comp_len += 1; CDA_DEVERR_CAPACITY if
+ *   comp_len == seg_cap); then the new token is written to ring row P mod W
+ *   (W = 0: straight to the compact tail if kept) and pos[b] = P + 1.
+ *
+ * Returns CDA_OK or an error code; errors are detected before anything is
+ * enqueued, except CDA_ERR_HIP.  Never prints, never aborts.
+ */
+int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void *stream);
+
+/*
+ * decode_attn_compact -- single-token GQA decode attention of one layer.
+ *
+ * For sequence b and query head j (KV head h = j / (Hq / Hkv)):
+ *   z_p = sm_scale * q[b,j,:] . k^_p    over the n_i stored rows of segment i
+ *   out[b,j,:] = sum_p softmax(z)_p v^_p,   lse[b,j] = log sum_p exp(z_p)
+ * where k^, v^ are the stored values (BF16, or FP8 code * scale).  A segment
+ * with no stored rows gives out = 0 and lse = -inf.
+ *
+ *   q            BF16 [B, Hq, D] contiguous, 16-byte aligned
+ *   sm_scale     softmax scale; <= 0 means 1/sqrt(D)
+ *   out          [B, Hq, D] contiguous, BF16 or F32 per out_dtype
+ *   lse          optional F32 [B, Hq] (natural log), may be NULL
+ *   split_tokens rows per work unit (one workgroup), rounded up to a
+ *                multiple of 64; 0 = default (256).  Heads longer than one
+ *                unit are split and their partials merged.
+ *   workspace    device scratch of at least cda_attn_workspace_bytes()
+ *                bytes (partials of the split heads); contents need no
+ *                initialisation and are not preserved.
+ */
+int32_t decode_attn_compact(const cda_kv_cache *cache, const void *q, int32_t Hq,
+                            float sm_scale, void *out, int32_t out_dtype, float *lse,
+                            int32_t split_tokens, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Workspace bytes decode_attn_compact needs for this cache, Hq and split. */
+size_t cda_attn_workspace_bytes(const cda_kv_cache *cache, int32_t Hq, int32_t split_tokens);
+
+/* Static text for a cda_status value. */
+const char *cda_status_string(int32_t status);
+
+/* CDA_VERSION of the built library. */
+int32_t cda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CDA_H */

@@ -55,9 +55,9 @@ def lib():
             L.orc_scales_from_amax.argtypes = [f32, P, P]
             L.orc_stored_count.argtypes = [P, i32, i32]
             L.orc_stored_count.restype = i64
-            L.orc_prefill_layout.argtypes = [i32, i32, i32, i32, i32, P, i64, P, P, P, P]
+            L.orc_prefill_layout.argtypes = [i32, i32, i32, i32, i32, i32, P, i64, P, P, P, P]
             L.orc_prefill_amax.argtypes = [i32, i32, i32, i32, i32, P, P, i64, i64, i64, P, i64, P, P]
-            L.orc_prefill_pack.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, i64, i64, i64,
+            L.orc_prefill_pack.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64, i64, i64,
                                            P, i64, i32, P, P, P, P, P, P, P, P, P]
             L.orc_append.argtypes = [i32, i32, i32, i32, i32, P, P, i64, i64, P, P, P, P, P,
                                      P, P, P, P, P, P]
@@ -118,9 +118,9 @@ def stored_count(keep_row: np.ndarray, P: int, W: int) -> int:
 
 # ---------------------------------------------------------------- prefill
 
-def prefill_layout(keep, T: int, W: int, reserve: int):
+def prefill_layout(keep, T: int, W: int, reserve: int, align: int = 1):
     """keep: [B, Hkv, >=T] bytes.  Returns dict of comp_len, seg_cap,
-    seg_base, dst (numpy)."""
+    seg_base, dst (numpy).  align: segment sizes are rounded up to it."""
     k = _u8(keep)
     B, Hkv, ld = k.shape
     nh = B * Hkv
@@ -128,7 +128,7 @@ def prefill_layout(keep, T: int, W: int, reserve: int):
     seg_cap = np.zeros(nh, np.int32)
     seg_base = np.zeros(nh + 1, np.int64)
     dst = np.zeros((B, Hkv, T), np.int32)
-    lib().orc_prefill_layout(B, Hkv, T, W, reserve, _p(k), ld, _p(comp_len),
+    lib().orc_prefill_layout(B, Hkv, T, W, reserve, align, _p(k), ld, _p(comp_len),
                              _p(seg_cap), _p(seg_base), _p(dst))
     return dict(comp_len=comp_len, seg_cap=seg_cap, seg_base=seg_base, dst=dst)
 
@@ -183,13 +183,13 @@ def prefill_amax(k, v, keep, T: int, W: int):
 
 
 def prefill_pack(k, v, keep, T: int, W: int, reserve: int, kv_dtype: int,
-                 amax=None) -> OracleCache:
+                 amax=None, align: int = 1) -> OracleCache:
     """Prefill compaction of one layer.  k, v: bf16 [B, >=T, Hkv, D] (only the
     first T positions are read); keep: [B, Hkv, >=T].  amax: optional
     (k_amax, v_amax) to use instead of computing them (FP8)."""
     kb, vb, kp = _bits(k), _bits(v), _u8(keep)
     B, Tt, Hkv, D = kb.shape
-    lay = prefill_layout(kp, T, W, reserve)
+    lay = prefill_layout(kp, T, W, reserve, align)
     rows = int(lay["seg_base"][-1])
     c = OracleCache(B, Hkv, D, W, kv_dtype, rows)
     scale_mode = 0
@@ -197,7 +197,7 @@ def prefill_pack(k, v, keep, T: int, W: int, reserve: int, kv_dtype: int,
         c.k_amax[:] = amax[0]
         c.v_amax[:] = amax[1]
         scale_mode = 1
-    lib().orc_prefill_pack(B, Hkv, D, T, W, reserve, kv_dtype, _p(kb), _p(vb),
+    lib().orc_prefill_pack(B, Hkv, D, T, W, reserve, align, kv_dtype, _p(kb), _p(vb),
                            Tt * Hkv * D, Hkv * D, D, _p(kp), kp.shape[2], scale_mode,
                            _p(c.k_amax), _p(c.v_amax), _p(c.k_pool), _p(c.v_pool),
                            _p(c.ring_keep), _p(c.comp_len), _p(c.seg_cap),

@@ -148,14 +148,16 @@ int64_t orc_stored_count(const uint8_t *keep_row, int P, int W)
  * For head i = b*Hkv + h:
  *   comp_len[i]  = number of kept positions p <= T-1-W
  *   seg_cap[i]   = comp_len[i] + reserve          (room for decode growth)
- *   seg_base[i]  = sum over j < i of (W + seg_cap[j]); seg_base[B*Hkv] = total
+ *   seg_base[i]  = sum over j < i of roundup(W + seg_cap[j], align);
+ *                  seg_base[B*Hkv] = total rows.  align >= 1 is a storage
+ *                  granularity of the store (1 = no padding).
  *   segment rows = W ring rows, then seg_cap compact rows
  *   dst[i*T + p] = ring row p mod W for the W most recent positions,
  *                  W + (rank of p among the kept older positions) for a kept
  *                  older position (ascending position order), -1 if evicted.
  * keep is [B*Hkv] rows of keep_ld bytes.
  */
-void orc_prefill_layout(int B, int Hkv, int T, int W, int reserve,
+void orc_prefill_layout(int B, int Hkv, int T, int W, int reserve, int align,
                         const uint8_t *keep, int64_t keep_ld,
                         int32_t *comp_len, int32_t *seg_cap, int64_t *seg_base,
                         int32_t *dst)
@@ -176,7 +178,8 @@ void orc_prefill_layout(int B, int Hkv, int T, int W, int reserve,
         comp_len[i] = n;
         seg_cap[i] = n + reserve;
         seg_base[i] = base;
-        base += (int64_t)W + n + reserve;
+        int64_t size = (int64_t)W + n + reserve;
+        base += (size + align - 1) / align * align;
     }
     seg_base[B * Hkv] = base;
 }
@@ -247,7 +250,7 @@ static int64_t store_row(int D, int kv_dtype, const uint16_t *src, float inv,
  * orc_prefill_layout with the same arguments.
  */
 void orc_prefill_pack(int B, int Hkv, int D, int T, int W, int reserve,
-                      int kv_dtype, const uint16_t *k, const uint16_t *v,
+                      int align, int kv_dtype, const uint16_t *k, const uint16_t *v,
                       int64_t sb, int64_t st, int64_t sh,
                       const uint8_t *keep, int64_t keep_ld, int scale_mode,
                       float *k_amax, float *v_amax, uint8_t *k_pool,
@@ -256,8 +259,8 @@ void orc_prefill_pack(int B, int Hkv, int D, int T, int W, int reserve,
 {
     int nh = B * Hkv;
     int32_t *dst = (int32_t *)malloc(sizeof(int32_t) * (size_t)nh * (size_t)(T > 0 ? T : 1));
-    orc_prefill_layout(B, Hkv, T, W, reserve, keep, keep_ld, comp_len, seg_cap,
-                       seg_base, dst);
+    orc_prefill_layout(B, Hkv, T, W, reserve, align, keep, keep_ld, comp_len,
+                       seg_cap, seg_base, dst);
     if (kv_dtype == ORC_FP8 && scale_mode == 0)
         orc_prefill_amax(B, Hkv, D, T, W, k, v, sb, st, sh, keep, keep_ld,
                          k_amax, v_amax);

@@ -1,0 +1,96 @@
+"""Helpers shared by the GPU parity tests: run the same seeded inputs through
+the HIP path (via the C ABI) and through the CPU oracle, and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from compressed_decode_attention_amd import CDA_SEG_ALIGN, CompactKVCache
+
+ATOL, RTOL = 2e-3, 1e-2     # attention tolerance: |gpu - oracle| <= ATOL + RTOL |oracle|
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def odt(kv_dtype: str) -> int:
+    return oracle.BF16 if kv_dtype == "bf16" else oracle.FP8
+
+
+def log(msg: str):
+    print(msg, flush=True)
+
+
+def gpu_prefill(k, v, keep, T, W, reserve, kv_dtype, amax=None, with_dst=True):
+    """COUNT (+dst), allocate, PACK on the GPU.  k, v: bf16 CPU or GPU
+    [B, >=T, Hkv, D]; keep [B, Hkv, >=T].  Returns (cache, dst or None)."""
+    d = dev()
+    B, _, Hkv, D = k.shape
+    kd, vd, keepd = k.to(d), v.to(d), keep.to(d)
+    c = CompactKVCache(B, Hkv, D, W, kv_dtype, d)
+    dst = torch.full((max(B * Hkv * T, 1),), -7, dtype=torch.int32, device=d) if with_dst else None
+    c.count(keepd, T, reserve, dst)
+    c.allocate()
+    # pool bytes not written by the kernels are set to a marker first
+    c.k_pool.fill_(0xA5)
+    c.v_pool.fill_(0x5A)
+    scale_mode = 0
+    if amax is not None:
+        c.k_amax.copy_(torch.as_tensor(amax[0], dtype=torch.float32))
+        c.v_amax.copy_(torch.as_tensor(amax[1], dtype=torch.float32))
+        scale_mode = 1
+    c.pack(kd, vd, keepd, T, scale_mode)
+    return c, dst
+
+
+def oracle_prefill(k, v, keep, T, W, reserve, kv_dtype, amax=None):
+    return oracle.prefill_pack(k, v, keep, T, W, reserve, odt(kv_dtype), amax=amax,
+                               align=CDA_SEG_ALIGN)
+
+
+def compare_state(c: CompactKVCache, o: oracle.OracleCache, what: str = ""):
+    """Bit-exact comparison of offsets, lengths, scales and every row in use."""
+    torch.cuda.synchronize()
+    nh = c.B * c.Hkv
+    assert np.array_equal(c.seg_base.cpu().numpy(), o.seg_base), what + " seg_base"
+    assert np.array_equal(c.seg_cap.cpu().numpy(), o.seg_cap), what + " seg_cap"
+    assert np.array_equal(c.comp_len.cpu().numpy(), o.comp_len), what + " comp_len"
+    assert np.array_equal(c.pos[: c.B].cpu().numpy(), o.pos), what + " pos"
+    assert c.pool_rows >= int(o.seg_base[-1])
+    if c.W:
+        assert np.array_equal(c.ring_keep.cpu().numpy()[: nh * c.W], o.ring_keep[: nh * c.W]), \
+            what + " ring_keep"
+    if c.kv_dtype == "fp8":
+        ga, oa = c.k_amax.cpu().numpy()[:nh], o.k_amax
+        assert np.array_equal(np.isnan(ga), np.isnan(oa)) and np.array_equal(ga[~np.isnan(ga)], oa[~np.isnan(oa)]), what + " k_amax"
+        ga, oa = c.v_amax.cpu().numpy()[:nh], o.v_amax
+        assert np.array_equal(np.isnan(ga), np.isnan(oa)) and np.array_equal(ga[~np.isnan(ga)], oa[~np.isnan(oa)]), what + " v_amax"
+    kr = c.k_rows().cpu().numpy()
+    vr = c.v_rows().cpu().numpy()
+    n = o.stored_rows()
+    for i in range(nh):
+        a = int(o.seg_base[i])
+        if n[i] == 0:
+            continue
+        if not np.array_equal(kr[a:a + n[i]], o.k_pool[a:a + n[i]]):
+            bad = np.nonzero(np.any(kr[a:a + n[i]] != o.k_pool[a:a + n[i]], axis=1))[0]
+            raise AssertionError(f"{what} K rows differ in segment {i}: rows {bad[:8]}")
+        if not np.array_equal(vr[a:a + n[i]], o.v_pool[a:a + n[i]]):
+            bad = np.nonzero(np.any(vr[a:a + n[i]] != o.v_pool[a:a + n[i]], axis=1))[0]
+            raise AssertionError(f"{what} V rows differ in segment {i}: rows {bad[:8]}")
+
+
+def check_close(got, ref, what="", atol=ATOL, rtol=RTOL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    bound = atol + rtol * np.abs(ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; "
+                             f"max abs err {err.max():.3e}; first {idx.tolist()} "
+                             f"got {got[bad][:5]} want {ref[bad][:5]}")
+    return float(err.max()) if err.size else 0.0

@@ -1,0 +1,115 @@
+"""The C-ABI library loads and exports every symbol include/cda.h declares;
+host-side argument validation returns the documented status codes.  None of
+these calls reach a kernel, so they run without a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from compressed_decode_attention_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from compressed_decode_attention_amd import build
+        build.build()
+    return _lib
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "cda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == set(lib.EXPORTS), declared
+    L = lib.load()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.version() == 1
+    assert lib.status_string(0) == "ok"
+    assert lib.status_string(3) == "workspace too small"
+    assert lib.status_string(99) == "unknown status"
+
+
+def _cache(lib, **kw):
+    c = lib.CdaKvCache()
+    c.B, c.Hkv, c.D, c.W, c.kv_dtype = 1, 2, 64, 16, 0
+    fake = 0x100000   # never dereferenced: validation fails or the call is not made
+    c.seg_base = c.seg_cap = c.comp_len = c.err = c.pos = c.ring_keep = fake
+    c.k_amax = c.v_amax = fake
+    c.pool_rows = 64
+    c.k_pool = c.v_pool = fake
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("D", 96, 2), ("D", 256, 2), ("kv_dtype", 7, 2), ("Hkv", 0, 1), ("W", -1, 1),
+    ("B", -1, 1), ("reserved0", 3, 1), ("seg_base", 0, 1), ("err", 0, 1),
+])
+def test_cache_validation(lib, field, value, status):
+    L = lib.load()
+    c = _cache(lib, **{field: value})
+    a = lib.CdaCompactArgs()
+    a.op = lib.CDA_OP_COUNT
+    a.T, a.keep_ld, a.keep = 4, 4, 0x100000
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == status
+
+
+def test_compact_args_validation(lib):
+    L = lib.load()
+    c = _cache(lib)
+    a = lib.CdaCompactArgs()
+    assert L.kv_compact(C.byref(c), None, None) == 1
+    assert L.kv_compact(None, C.byref(a), None) == 1
+    a.op = 9
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    a.op, a.T, a.keep_ld, a.keep = lib.CDA_OP_COUNT, 10, 5, 0x100000   # keep_ld < T
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    a.keep_ld, a.keep = 10, 0                                          # keep NULL
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    a.keep, a.reserve = 0x100000, -1
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    # PACK: misaligned k, stride not a multiple of 8, bad scale mode, bad pool_rows
+    a.op, a.reserve, a.k, a.v = lib.CDA_OP_PACK, 0, 0x100002, 0x100000
+    a.stride_b = a.stride_t = a.stride_h = 64
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    a.k, a.stride_t = 0x100000, 12
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    a.stride_t, a.scale_mode = 64, 2
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    c2 = _cache(lib, pool_rows=100)
+    a.scale_mode = 0
+    assert L.kv_compact(C.byref(c2), C.byref(a), None) == 1
+    # APPEND without keep
+    a.op, a.keep = lib.CDA_OP_APPEND, 0
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+
+
+def test_attention_validation(lib):
+    L = lib.load()
+    c = _cache(lib)
+    q = out = ws = C.c_void_p(0x100000)
+    need = L.cda_attn_workspace_bytes(C.byref(c), 8, 0)
+    assert need > 0
+    f = L.decode_attn_compact
+    assert f(C.byref(c), q, 7, 0.0, out, 0, None, 0, ws, need, None) == 2        # Hq % Hkv
+    assert f(C.byref(c), q, 2 * 17, 0.0, out, 0, None, 0, ws, need, None) == 2   # G > 16
+    assert f(C.byref(c), q, 8, 0.0, out, 5, None, 0, ws, need, None) == 2        # out dtype
+    assert f(C.byref(c), q, 8, 0.0, out, 0, None, 0, ws, need - 1, None) == 3    # workspace
+    assert f(C.byref(c), C.c_void_p(0x100001), 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    assert f(C.byref(c), q, 8, 0.0, out, 0, None, -5, ws, need, None) == 1       # split < 0
+    assert f(None, q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    # a bigger split never needs more workspace
+    assert L.cda_attn_workspace_bytes(C.byref(c), 8, 4096) <= need
+    assert L.cda_attn_workspace_bytes(C.byref(c), 7, 0) == 0

@@ -1,0 +1,132 @@
+"""GPU parity of decode_attn_compact against the CPU oracle's fp64 attention
+computed from its definition on the dense history (F32 output, tolerance
+|gpu - oracle| <= 2e-3 + 1e-2 |oracle|), including the split-K merge, the
+log-sum-exp output, the edge cases of the method, and decode loops."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from _cda_testlib import (check_close, dev, gpu_prefill, log, odt, oracle_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(B, Hq, Hkv, D, T, W, rate, kv_dtype, seed, split=0, sm_scale=0.0, reserve=4,
+         kscale=1.0, vscale=1.0):
+    keep = workload.random_keep((B, Hkv, T), rate, seed=seed)
+    k = workload.random_bf16((B, T, Hkv, D), seed=seed + 1, scale=kscale)
+    v = workload.random_bf16((B, T, Hkv, D), seed=seed + 2, scale=vscale)
+    q = workload.random_bf16((B, Hq, D), seed=seed + 3)
+    c, _ = gpu_prefill(k, v, keep, T, W, reserve, kv_dtype, with_dst=False)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev())
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev())
+    c.attention(q.to(dev()), out=out, lse=lse, sm_scale=sm_scale, split_tokens=split)
+    torch.cuda.synchronize()
+    ka = c.k_amax.cpu().numpy() if kv_dtype == "fp8" else None
+    va = c.v_amax.cpu().numpy() if kv_dtype == "fp8" else None
+    if kv_dtype == "fp8":   # the scales themselves are pinned bit-exact elsewhere
+        oa = oracle.prefill_amax(k, v, keep, T, W)
+        assert np.array_equal(ka[: B * Hkv], oa[0]) and np.array_equal(va[: B * Hkv], oa[1])
+    ref, rlse = oracle.attention(q, k, v, keep, T - 1, W, odt(kv_dtype), ka, va, sm_scale)
+    return c, out.cpu().numpy(), lse.cpu().numpy(), ref, rlse
+
+
+CASES = [
+    # B, Hq, Hkv, D, T, W, rate, kv_dtype, seed
+    (1, 8, 2, 64, 512, 64, 1 / 6.4, "bf16", 1),
+    (1, 8, 2, 64, 512, 64, 1 / 6.4, "fp8", 1),
+    (2, 32, 8, 128, 1500, 256, 0.15, "fp8", 2),
+    (2, 32, 8, 128, 1500, 256, 0.15, "bf16", 3),
+    (3, 32, 8, 64, 2100, 256, 0.3, "fp8", 4),
+    (1, 16, 16, 128, 777, 20, 0.4, "bf16", 5),     # G = 1
+    (2, 16, 2, 64, 900, 10, 0.25, "fp8", 6),       # G = 8
+    (1, 32, 2, 128, 650, 33, 0.5, "bf16", 7),      # G = 16
+    (2, 12, 4, 64, 333, 7, 0.2, "fp8", 8),         # G = 3
+    (1, 8, 2, 128, 50, 64, 0.5, "fp8", 9),         # T < W
+    (2, 8, 4, 64, 4100, 1, 0.02, "bf16", 10),      # W = 1, very sparse
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"a{i}" for i in range(len(CASES))])
+def test_attention_matches_oracle(case):
+    B, Hq, Hkv, D, T, W, rate, kv_dtype, seed = case
+    log(f"attention case B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} W={W} {kv_dtype}")
+    c, out, lse, ref, rlse = _run(*case)
+    err = check_close(out, ref, "out")
+    check_close(lse, rlse, "lse", atol=1e-4, rtol=1e-5)
+    log(f"  max abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("split", [64, 128, 192, 256, 1024, 100000])
+def test_split_invariance(split):
+    case = (2, 32, 8, 128, 3000, 256, 0.2, "fp8", 21)
+    c, out, lse, ref, rlse = _run(*case, split=split)
+    check_close(out, ref, f"split {split}")
+    check_close(lse, rlse, f"split {split} lse", atol=1e-4, rtol=1e-5)
+
+
+def test_outliers_and_custom_scale():
+    # large-magnitude K and V (FP8 scales far from 1) and an explicit sm_scale
+    case = (2, 16, 4, 128, 1200, 64, 0.2, "fp8", 31)
+    c, out, lse, ref, rlse = _run(*case, sm_scale=0.05, kscale=40.0, vscale=0.01)
+    check_close(out, ref, "scaled", atol=2e-3 * 0.01, rtol=1e-2)
+
+
+def test_empty_segments_give_zero_and_neg_inf_lse():
+    B, Hq, Hkv, D, T = 2, 8, 2, 64, 200
+    keep = torch.zeros((B, Hkv, T), dtype=torch.uint8)
+    keep[1, 0, 17] = 1                  # one segment holds one token
+    k = workload.random_bf16((B, T, Hkv, D), seed=1)
+    v = workload.random_bf16((B, T, Hkv, D), seed=2)
+    q = workload.random_bf16((B, Hq, D), seed=3)
+    for kv_dtype in ("bf16", "fp8"):
+        c, _ = gpu_prefill(k, v, keep, T, 0, 0, kv_dtype, with_dst=False)
+        out = torch.full((B, Hq, D), 7.0, dtype=torch.float32, device=dev())
+        lse = torch.zeros((B, Hq), dtype=torch.float32, device=dev())
+        c.attention(q.to(dev()), out=out, lse=lse)
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        ka = c.k_amax.cpu().numpy() if kv_dtype == "fp8" else None
+        va = c.v_amax.cpu().numpy() if kv_dtype == "fp8" else None
+        ref, rlse = oracle.attention(q, k, v, keep, T - 1, 0, odt(kv_dtype), ka, va)
+        empty = np.isneginf(rlse)
+        assert empty.sum() == B * Hq - 4
+        assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
+        check_close(o, ref, "single token")
+
+
+def test_bf16_output_is_rounded_f32_output():
+    case = (2, 32, 8, 128, 1500, 256, 0.15, "fp8", 41)
+    c, out32, _, ref, _ = _run(*case)
+    q = workload.random_bf16((2, 32, 128), seed=44).to(dev())
+    o32 = c.attention(q, out_dtype=torch.float32)
+    o16 = c.attention(q, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("kv_dtype,D,W", [("fp8", 128, 64), ("bf16", 64, 64), ("fp8", 64, 0)])
+def test_decode_loop_matches_oracle(kv_dtype, D, W):
+    B, Hq, Hkv, T, S = 2, 16, 4, 700, 80
+    log(f"decode loop {kv_dtype} D={D} W={W}")
+    keep = workload.random_keep((B, Hkv, T + S), 0.2, seed=51)
+    k = workload.random_bf16((B, T + S, Hkv, D), seed=52)
+    v = workload.random_bf16((B, T + S, Hkv, D), seed=53)
+    q = workload.random_bf16((S, B, Hq, D), seed=54)
+    c, _ = gpu_prefill(k, v, keep, T, W, S, kv_dtype, with_dst=False)
+    kd, vd, keepd, qd = k.to(dev()), v.to(dev()), keep.to(dev()), q.to(dev())
+    ka = c.k_amax.cpu().numpy() if kv_dtype == "fp8" else None
+    va = c.v_amax.cpu().numpy() if kv_dtype == "fp8" else None
+    worst = 0.0
+    for s in range(S):
+        c.append(kd[:, T + s], vd[:, T + s], keepd[:, :, T + s].contiguous())
+        out = c.attention(qd[s], out_dtype=torch.float32)
+        if s % 9 == 0 or s == S - 1:
+            torch.cuda.synchronize()
+            ref, _ = oracle.attention(q[s], k, v, keep, T + s, W, odt(kv_dtype), ka, va)
+            worst = max(worst, check_close(out.cpu().numpy(), ref, f"step {s}"))
+    assert c.error_word() == 0
+    log(f"  worst abs err {worst:.2e}")

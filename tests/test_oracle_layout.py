@@ -20,7 +20,7 @@ import torch
 import workload
 
 
-def _check_layout(keep_rows, T, W, reserve, lay):
+def _check_layout(keep_rows, T, W, reserve, lay, align=1):
     nh = keep_rows.shape[0]
     base = 0
     for i in range(nh):
@@ -29,7 +29,8 @@ def _check_layout(keep_rows, T, W, reserve, lay):
         cl = int(lay["comp_len"][i])
         assert int(lay["seg_base"][i]) == base
         assert int(lay["seg_cap"][i]) == cl + reserve
-        base += W + cl + reserve
+        base += -(-(W + cl + reserve) // align) * align
+        assert base % align == 0
         recent = set(range(max(0, T - W), T))
         stored = {p for p in range(T) if p in recent or row[p] != 0}
         # stored <-> has a row
@@ -48,8 +49,8 @@ def _check_layout(keep_rows, T, W, reserve, lay):
     assert int(lay["seg_base"][nh]) == base
 
 
-@pytest.mark.parametrize("W", [0, 1, 3])
-def test_layout_brute_force_all_masks(orc, W):
+@pytest.mark.parametrize("W,align", [(0, 1), (1, 1), (3, 1), (3, 4), (0, 64)])
+def test_layout_brute_force_all_masks(orc, W, align):
     for T in range(0, 11):
         # all masks of this T at once, as heads of one layer (B = #masks, Hkv = 1)
         if T == 0:
@@ -57,8 +58,8 @@ def test_layout_brute_force_all_masks(orc, W):
         else:
             masks = np.array(list(itertools.product([0, 1], repeat=T)), np.uint8)
             keep = np.ascontiguousarray(masks.reshape(-1, 1, T))
-        lay = orc.prefill_layout(keep, T, W, reserve=2)
-        _check_layout(keep.reshape(-1, keep.shape[2]), T, W, 2, lay)
+        lay = orc.prefill_layout(keep, T, W, reserve=2, align=align)
+        _check_layout(keep.reshape(-1, keep.shape[2]), T, W, 2, lay, align)
 
 
 def test_layout_nonbinary_keep_bytes(orc):
