@@ -1,0 +1,251 @@
+"""Benchmark of compact decode attention on one MI355X.
+
+Workload: the Qwen3-8B attention shape at c = 8 (36 layers, 32 query / 8 KV
+heads, head_dim 128, batch 8, ctx 8192, gen 128), FP8-E4M3 compact KV with
+per-(sequence, head) scales, keep rates U[0.04, 0.25] per head, 1% outlier
+channels x8, always-kept window 256 -- the FastDMS page's Qwen3-8B c = 8
+memory-table row, on synthetic inputs (no weights, no dataset).
+
+One step = one pass of the whole path over the batch, everything already
+resident in HBM:
+  prefill compaction of every layer (kv_compact COUNT + PACK), then
+  128 decode steps x 36 layers of kv_compact APPEND + decode_attn_compact,
+all enqueued on one stream with no host synchronisation inside the step.
+
+Reported: value = decode-attention KV bytes moved per second over the whole
+step (algorithmic bytes: every stored row's K and V read once per decode
+step and layer, divided by the step's wall time); roofline of the attention
+kernel from HIP events around every attention call in the timed region;
+the CPU oracle timed on a bounded sample; and parity of that sample.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compact decode-attn HBM GB/s (% of peak) + attn tokens/s, Qwen3-8B ctx8192"
+HBM_PEAK_GBS = 8000.0
+ATTN_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stored_rows_host(keep_np, T, W, S):
+    """n[s, b, h]: stored rows of every segment after the append of step s
+    (W most recent positions + kept older ones) -- byte accounting only."""
+    B, Hkv, _ = keep_np.shape
+    kept = (keep_np != 0).astype(np.int64)
+    csum = np.concatenate([np.zeros((B, Hkv, 1), np.int64), np.cumsum(kept, axis=2)], axis=2)
+    out = np.zeros((S, B, Hkv), np.int64)
+    for s in range(S):
+        P = T + s
+        older = max(P - W + 1, 0)           # positions 0 .. P-W are "older"
+        out[s] = min(W, P + 1) + csum[:, :, older]
+    return out
+
+
+def traffic_from_profile():
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current attention kernel source."""
+    path = os.path.join(ROOT, "profiles", "attn_qwen_c8_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("attn_src_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, layers, outs, kv_dtype, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample: for layer 0, 1, ...
+    (until the budget is spent) the prefill absmax and the attention of all
+    B x Hq query heads at the last decode step.  Returns the record and the
+    worst parity error of the GPU outputs of those layers."""
+    import oracle
+    from workload import make_layer
+    od = oracle.FP8 if kv_dtype == "fp8" else oracle.BF16
+    T, S, W = cfg.T, cfg.S, cfg.W
+    nbytes, t_used, worst, done = 0, 0.0, 0.0, 0
+    for l in layers:
+        lay = make_layer(cfg, l)
+        t0 = time.perf_counter()
+        ka, va = oracle.prefill_amax(lay.k, lay.v, lay.keep, T, W)
+        ref, _ = oracle.attention(lay.q[S - 1], lay.k, lay.v, lay.keep, T + S - 1, W, od,
+                                  ka, va)
+        t_used += time.perf_counter() - t0
+        n = stored_rows_host(lay.keep.numpy(), T, W, S)[S - 1]
+        nbytes += int(n.sum()) * 2 * cfg.D * (1 if kv_dtype == "fp8" else 2)
+        got = outs[l].float().cpu().numpy()
+        err = np.abs(got - ref)
+        tol = 2e-3 + 1e-2 * np.abs(ref) + np.abs(ref) * 2.0 ** -8   # bf16 output rounding
+        if not np.all(err <= tol):
+            raise AssertionError(f"bench parity failed on layer {l}: max err {err.max():.3e}")
+        worst = max(worst, float(err.max()))
+        done += 1
+        if t_used >= budget_s:
+            break
+    rec = {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"layers 0..{done - 1}: prefill absmax + fp64 attention of all "
+                     f"{cfg.B}x{cfg.Hq} query heads at the last decode step "
+                     f"({nbytes / 1e6:.1f} MB of compact KV, {t_used:.1f} s)"}
+    return rec, worst, done
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="qwen_c8")
+    ap.add_argument("--layers", type=int, default=0, help="0 = all layers of the config")
+    ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the compact decode-attention path runs on a "
+              "single device; there is no multi-GPU mode (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workload
+    from compressed_decode_attention_amd import CompactKVCache, _lib
+
+    dev = torch.device("cuda:0")
+    cfg = workload.CONFIGS[args.config]
+    L = args.layers or cfg.L
+    B, Hq, Hkv, D, T, S, W = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.T, cfg.S, cfg.W
+    ebytes = 1 if cfg.kv_dtype == "fp8" else 2
+    log(f"config {cfg.name}: L={L} B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} S={S} W={W} "
+        f"{cfg.kv_dtype}; generating inputs")
+
+    t0 = time.perf_counter()
+    kd, vd, keepd, keep_new, qd, caches, nrows = [], [], [], [], [], [], []
+    for l in range(L):
+        lay = workload.make_layer(cfg, l)
+        kd.append(lay.k.to(dev))
+        vd.append(lay.v.to(dev))
+        keepd.append(lay.keep.to(dev))
+        keep_new.append(lay.keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev))
+        qd.append(lay.q.to(dev))
+        nrows.append(stored_rows_host(lay.keep.numpy(), T, W, S))
+        c = CompactKVCache(B, Hkv, D, W, cfg.kv_dtype, dev)
+        c.count(keepd[l], T, reserve=S)
+        c.allocate()
+        c.workspace(Hq, args.split)
+        caches.append(c)
+    outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.perf_counter() - t0:.1f} s")
+
+    # algorithmic bytes of every attention call: stored rows x 2 x D x e
+    attn_bytes = np.array([[int(nrows[l][s].sum()) * 2 * D * ebytes for l in range(L)]
+                           for s in range(S)], np.float64)          # [S, L]
+    step_attn_bytes = float(attn_bytes.sum())
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L)] for _ in range(S)]
+
+    def run_step(timed_events: bool):
+        for l in range(L):
+            c = caches[l]
+            c.count(keepd[l], T, reserve=S)
+            c.pack(kd[l], vd[l], keepd[l], T)
+        for s in range(S):
+            for l in range(L):
+                c = caches[l]
+                c.append(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s])
+                if timed_events:
+                    ev[s][l][0].record(stream)
+                c.attention(qd[l][s], out=outs[l], split_tokens=args.split)
+                if timed_events:
+                    ev[s][l][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step(False)
+    torch.cuda.synchronize()
+    for c in caches:
+        if c.error_word() != 0:
+            raise RuntimeError("device error word set during warm-up")
+    log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
+
+    step_ms, attn_us = [], []
+    for k in range(args.steps):
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        run_step(True)
+        torch.cuda.synchronize()
+        step_ms.append((time.perf_counter() - t_start) * 1e3)
+        attn_us.append(np.array([[ev[s][l][0].elapsed_time(ev[s][l][1]) * 1e3
+                                  for l in range(L)] for s in range(S)]))
+        log(f"step {k}: {step_ms[-1]:.2f} ms")
+    attn_us = np.stack(attn_us)                 # [K, S, L]
+
+    # the device state after the last step must match the host accounting
+    for l in range(L):
+        got = caches[l].stored_rows().cpu().numpy().reshape(B, Hkv)
+        if not np.array_equal(got, nrows[l][S - 1]):
+            raise RuntimeError(f"layer {l}: device stored-row counts differ from the keep mask")
+
+    ms = float(np.mean(step_ms))
+    value = step_attn_bytes / (ms * 1e-3) / 1e9
+    tokens_per_s = B * S / (ms * 1e-3)
+    mean_launch_us = float(attn_us.mean())
+    bytes_per_launch = float(attn_bytes.mean())
+    achieved = bytes_per_launch / (mean_launch_us * 1e-6) / 1e9
+    traffic = traffic_from_profile()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu, worst, nl = cpu_baseline(cfg, list(range(L)), outs, cfg.kv_dtype)
+        log(f"oracle sample: {nl} layers, GPU max abs err {worst:.2e}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Qwen3-8B attention shape, ctx {T}, gen {S}, "
+                               f"c={B}, {cfg.kv_dtype} compact KV, W={W}",
+                   "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
+                   "kv_storage": cfg.kv_dtype, "split_tokens": args.split or 256,
+                   "parallelism": "single GPU"},
+        "attn_tokens_per_s": round(tokens_per_s, 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "attn_call_us_mean": round(mean_launch_us, 3),
+        "attn_call_us_p10_p90": [round(float(np.percentile(attn_us, 10)), 3),
+                                 round(float(np.percentile(attn_us, 90)), 3)],
+        "kv_bytes_per_decode_step": round(float(attn_bytes.sum(axis=1).mean())),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,7 +173,8 @@ class CompactKVCache:
         key = (Hq, split_tokens)
         if key not in self._ws:
             n = _lib.attn_workspace_bytes(self.struct, Hq, split_tokens)
-            self._ws[key] = torch.empty(max(n, 16), dtype=torch.uint8, device=self.device)
+            # zero-filled once; the library keeps its counters at zero
+            self._ws[key] = torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
         return self._ws[key]
 
     def attention(self, q, out=None, out_dtype=torch.bfloat16, lse=None, sm_scale: float = 0.0,
@@ -199,4 +200,10 @@ class CompactKVCache:
         return t.permute(0, 2, 1, 3).reshape(self.pool_rows, D * e)
 
     def k_rows(self) -> torch.Tensor:
-        return self.k_pool[: self.pool_rows * self.D * self.elem_bytes].view(self.pool_rows, -1)
+        """The K pool as [pool_rows, D * elem_bytes] bytes in row order (undoes
+        the in-tile chunk permutation described in include/cda.h)."""
+        rb = self.D * self.elem_bytes
+        kl = rb // 64
+        t = self.k_pool[: self.pool_rows * rb].view(-1, 4, kl, 4, 4, 4, 16)
+        # [tile, m, j, kg, gh, gl, byte] -> [tile, gh, m, gl, j, kg, byte]
+        return t.permute(0, 4, 1, 5, 2, 3, 6).reshape(self.pool_rows, rb)

@@ -9,17 +9,22 @@
 // tiles into work units of `tpu` tiles; one workgroup (4 waves) takes one
 // unit and each wave one tile at a time.  Every workgroup derives the unit
 // -> (segment, tiles) map itself from pos / comp_len / seg_cap, so the host
-// needs no copy of the lengths.  A segment with one unit writes its output
-// directly; otherwise each unit writes an unnormalised partial (m, l, o) and
-// attn_merge_kernel combines them with a log-sum-exp merge.
+// needs no copy of the lengths; all per-segment metadata it needs is read in
+// that one pass, so the K/V loads start after a single dependent round trip.
+// A segment with one unit writes its output directly; otherwise each unit
+// writes an unnormalised partial (m, l, o), counts itself in with a
+// device-scope atomic, and the last unit of the segment to finish combines
+// all of them with a log-sum-exp merge and resets the counter (so the
+// counters are zero between calls).
 //
 // Inside a wave, the G query rows of the KV head (G <= 16) are the N = 16
 // columns of two MFMA products per tile:
 //   S^T[token][g] = K_tile[token][:] . Q^T[:][g]     v_mfma_f32_16x16x32_bf16
 //   O^T[d][g]    += V^T[d][token] . P^T[token][g]    v_mfma_f32_16x16x32_{f16,bf16}
-// K is row-major in the pool, so the S operand is 16-byte loads of rows; V
-// is stored in 64-row column-major tiles, so the O operand is 16-byte loads
-// of 8 or 16 consecutive tokens of one column.  Tokens are assigned to MFMA
+// K is stored in 64-row tiles permuted so that each 64-lane load of the S
+// operand is 1 KB of consecutive bytes; V is stored in 64-row column-major
+// tiles, so the O operand is 16-byte loads of 8 or 16 consecutive tokens of
+// one column.  Tokens are assigned to MFMA
 // rows so that the S accumulator of each lane holds exactly the 16 tokens
 // that lane needs for its P operand, so P never moves between lanes.  FP8
 // codes are converted to bf16 (K) or f16 (V) in registers, exactly; the K
@@ -34,6 +39,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMergeBatch = 8;   // partials loaded per round trip in the merge
 
 struct AttnParams {
   const uint8_t* k_pool;
@@ -50,19 +56,10 @@ struct AttnParams {
   float* lse;
   float* part_o;       // [units][G][D]
   float* part_ml;      // [units][G][2]
-  int32_t* head_units; // [nh][2]: first unit, unit count
+  int32_t* sem;        // [nh]: units of the segment finished so far (0 between calls)
   int Hkv, G, Hq, W, nh, tpu, out_f32;
   float sm_scale;
 };
-
-__device__ __forceinline__ int stored_rows(const AttnParams& p, int i) {
-  const int b = i / p.Hkv;
-  const int P = p.pos[b];
-  const int ring = min(p.W, max(P, 0));
-  const int cap = max(p.seg_cap[i], 0);
-  const int cl = min(max(p.comp_len[i], 0), cap);
-  return ring + cl;
-}
 
 __device__ __forceinline__ int units_of(int n, int tpu) {
   const int tiles = (n + kTile - 1) / kTile;
@@ -82,6 +79,14 @@ __device__ __forceinline__ void store_out(const AttnParams& p, int64_t idx, floa
     static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16_rne(v);
 }
 
+// Final output of query row gg of segment (b, h) from its merged state.
+__device__ __forceinline__ void write_final(const AttnParams& p, int b, int h, int gg, int d,
+                                            int D, float M, float L, float O, float sv) {
+  const int64_t row = (int64_t)b * p.Hq + h * p.G + gg;
+  store_out(p, row * D + d, L > 0.0f ? O / L * sv : 0.0f);
+  if (d == 0 && p.lse) p.lse[row] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 template <bool FP8, int D>
 __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
   constexpr int E = FP8 ? 1 : 2;            // bytes per stored element
@@ -90,48 +95,66 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
   constexpr int KL = FP8 ? D / 64 : D / 32; // 16-byte K loads per (lane, token group)
   constexpr int VL = FP8 ? 1 : 2;           // 16-byte V loads per (lane, d tile)
 
-  __shared__ int s_head, s_first, s_units;
-  __shared__ int s_scan[4];
+  __shared__ int s_last;
   __shared__ float s_m[4][16], s_l[4][16];
   __shared__ f32x4 s_o[4][16][D / 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u = blockIdx.x;
 
-  // ---- which segment and which tiles this workgroup covers
-  if (tid == 0) s_head = -1;
+  // ---- which segment and which tiles this workgroup covers.  Every wave
+  //      works this out by itself (lane l looks at segment base + l; a
+  //      wave-wide scan of unit counts finds the segment holding unit u), so
+  //      no workgroup barrier delays the K/V loads; all the metadata the
+  //      kernel needs about the segment is read in this one pass.
+  int i = -1, first = 0, U = 1, n = 0;
+  long long sb = 0;
+  float ks = 1.0f, vs = 1.0f;
   int carry = 0;
-  for (int base = 0; base < p.nh; base += kBlock) {
-    const int i = base + tid;
-    int U = 0;
-    if (i < p.nh) U = units_of(stored_rows(p, i), p.tpu);
-    int total;
-    const int ex = block_exclusive_scan(U, &total, s_scan) + carry;
-    if (i < p.nh) {
-      if (u >= ex && u < ex + U) {
-        s_head = i;
-        s_first = ex;
-        s_units = U;
+  for (int base = 0; base < p.nh && i < 0; base += 64) {
+    const int hi = base + lane;
+    int Ui = 0, ni = 0;
+    long long sbi = 0;
+    float ka = 1.0f, va = 1.0f;
+    if (hi < p.nh) {
+      const int P = p.pos[hi / p.Hkv];
+      const int cap = max(p.seg_cap[hi], 0);
+      const int cl = p.comp_len[hi];
+      sbi = p.seg_base[hi];
+      if (FP8) {
+        ka = p.k_amax[hi];
+        va = p.v_amax[hi];
       }
-      if (u == 0) {
-        p.head_units[2 * i] = ex;
-        p.head_units[2 * i + 1] = U;
-      }
+      ni = min(p.W, max(P, 0)) + min(max(cl, 0), cap);
+      Ui = units_of(ni, p.tpu);
     }
-    carry += total;
+    int x = Ui;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    const int ex = carry + x - Ui;
+    const unsigned long long mine = __ballot(hi < p.nh && u >= ex && u < ex + Ui);
+    if (mine) {
+      const int src = __ffsll((long long)mine) - 1;
+      i = base + src;
+      first = __shfl(ex, src, 64);
+      U = __shfl(Ui, src, 64);
+      n = __shfl(ni, src, 64);
+      sb = __shfl(sbi, src, 64);
+      ks = fp8_scale(__shfl(ka, src, 64));
+      vs = fp8_scale(__shfl(va, src, 64));
+    }
+    carry += __shfl(x, 63, 64);
   }
-  __syncthreads();
-  const int i = s_head;
-  if (i < 0) return;
+  if (i < 0) return;        // the same for every wave of the workgroup
   const int b = i / p.Hkv, h = i - b * p.Hkv;
   const int G = p.G;
-  const int n = stored_rows(p, i);
-  const int64_t sb = p.seg_base[i];
   const int64_t in_pool = p.pool_rows - sb;
   const int ntiles = (n + kTile - 1) / kTile;
-  const int t_begin = (u - s_first) * p.tpu;
+  const int t_begin = (u - first) * p.tpu;
   const int t_end = min(t_begin + p.tpu, ntiles);
-  const int U = s_units;
 
   const int g = lane & 15, kg = lane >> 4;
 
@@ -147,8 +170,7 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
       qop[s] = as_bf16x8(w);
     }
   }
-  float c1 = p.sm_scale * kLog2e;
-  if (FP8) c1 *= fp8_scale(p.k_amax[i]);
+  const float c1 = p.sm_scale * kLog2e * (FP8 ? ks : 1.0f);
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 acc[NT];
@@ -162,7 +184,8 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
     const uint8_t* ktile = p.k_pool + (sb + r0) * (int64_t)(D * E);
     const uint8_t* vtile = p.v_pool + (sb + r0) * (int64_t)(D * E);
 
-    // -- loads: K rows for the 4 token groups, V columns for the NT d tiles
+    // -- loads: K rows for the 4 token groups (each instruction 1 KB of the
+    //    permuted K tile), V columns for the NT d tiles
     u32x4 kr[4][KL];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -171,7 +194,7 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
       for (int j = 0; j < KL; ++j)
         kr[m][j] = row < valid
                        ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                             ktile + row * (D * E) + 64 * j + 16 * kg))
+                             ktile + ((m * KL + j) << 10) + lane * 16))
                        : u32x4{0, 0, 0, 0};
     }
     u32x4 vr[NT][VL];
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
   for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
   __syncthreads();
 
-  const float sv = FP8 ? fp8_scale(p.v_amax[i]) : 1.0f;
+  const float sv = FP8 ? vs : 1.0f;
   for (int w = tid; w < G * D; w += kBlock) {
     const int gg = w / D, d = w - gg * D;
     float M = -INFINITY;
@@ -312,47 +335,65 @@ __global__ __launch_bounds__(kBlock) void attn_kernel(AttnParams p) {
       }
     }
     if (U == 1) {
-      const int64_t oi = ((int64_t)b * p.Hq + h * G + gg) * D + d;
-      store_out(p, oi, L > 0.0f ? O / L * sv : 0.0f);
-      if (d == 0 && p.lse)
-        p.lse[(int64_t)b * p.Hq + h * G + gg] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      write_final(p, b, h, gg, d, D, M, L, O, sv);
     } else {
-      p.part_o[((int64_t)u * G + gg) * D + d] = O;
+      // agent-scope stores write through to where every XCD reads them
+      __hip_atomic_store(p.part_o + ((int64_t)u * G + gg) * D + d, O, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
       if (d == 0) {
-        p.part_ml[((int64_t)u * G + gg) * 2] = M;
-        p.part_ml[((int64_t)u * G + gg) * 2 + 1] = L;
+        __hip_atomic_store(p.part_ml + ((int64_t)u * G + gg) * 2, M, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.part_ml + ((int64_t)u * G + gg) * 2 + 1, L, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-}
+  if (U == 1) return;
 
-// Log-sum-exp merge of the unit partials of every segment with > 1 unit.
-template <bool FP8>
-__global__ __launch_bounds__(kBlock) void attn_merge_kernel(AttnParams p, int D) {
-  const int i = blockIdx.x;
-  const int first = p.head_units[2 * i], U = p.head_units[2 * i + 1];
-  if (U <= 1) return;
-  const int b = i / p.Hkv, h = i - b * p.Hkv, G = p.G;
-  const float sv = FP8 ? fp8_scale(p.v_amax[i]) : 1.0f;
-  for (int w = threadIdx.x; w < G * D; w += kBlock) {
+  // ---- split segment: the last of its units to get here merges the partials.
+  // Every wave waits for its partial stores to complete before the workgroup
+  // counts itself in; no cache-wide fence is needed because both the stores
+  // and the merge's loads are agent-scope.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(p.sem + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == U - 1;
+    if (prev == U - 1) __hip_atomic_store(p.sem + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  for (int w = tid; w < G * D; w += kBlock) {
     const int gg = w / D, d = w - gg * D;
-    float M = -INFINITY;
-    for (int k = 0; k < U; ++k) M = fmaxf(M, p.part_ml[((int64_t)(first + k) * G + gg) * 2]);
-    float O = 0.0f, L = 0.0f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < U; ++k) {
-        const int64_t slot = (int64_t)(first + k) * G + gg;
-        const float mk = p.part_ml[slot * 2];
-        if (mk == -INFINITY) continue;
-        const float f = exp2f(mk - M);
-        O += f * p.part_o[slot * D + d];
-        L += f * p.part_ml[slot * 2 + 1];
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int k0 = 0; k0 < U; k0 += kMergeBatch) {
+      float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {   // unconditional loads, clamped index
+        const int64_t slot = (int64_t)(first + min(k0 + j, U - 1)) * G + gg;
+        mv[j] = __hip_atomic_load(p.part_ml + slot * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lv[j] = __hip_atomic_load(p.part_ml + slot * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ov[j] = __hip_atomic_load(p.part_o + slot * D + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j)
+        if (k0 + j >= U) mv[j] = -INFINITY;
+      float Mb = M;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, mv[j]);
+      if (Mb == -INFINITY) continue;
+      const float a = (M == -INFINITY) ? 0.0f : exp2f(M - Mb);
+      O *= a;
+      L *= a;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float f = (mv[j] == -INFINITY) ? 0.0f : exp2f(mv[j] - Mb);
+        O += f * ov[j];
+        L += f * lv[j];
+      }
+      M = Mb;
     }
-    const int64_t oi = ((int64_t)b * p.Hq + h * G + gg) * D + d;
-    store_out(p, oi, L > 0.0f ? O / L * sv : 0.0f);
-    if (d == 0 && p.lse)
-      p.lse[(int64_t)b * p.Hq + h * G + gg] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    write_final(p, b, h, gg, d, D, M, L, O, sv);
   }
 }
 
@@ -368,8 +409,8 @@ int64_t attn_max_units(const cda_kv_cache& c, int tpu) {
 size_t attn_workspace_bytes(const cda_kv_cache& c, int G, int tpu) {
   const int64_t units = attn_max_units(c, tpu);
   const int64_t nh = (int64_t)c.B * c.Hkv;
-  return align256((size_t)units * G * c.D * 4) + align256((size_t)units * G * 2 * 4) +
-         align256((size_t)nh * 2 * 4);
+  return align256((size_t)nh * 4) + align256((size_t)units * G * 2 * 4) +
+         align256((size_t)units * G * c.D * 4);
 }
 
 hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_scale, void* out,
@@ -391,12 +432,13 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.q = static_cast<const uint16_t*>(q);
   p.out = out;
   p.lse = lse;
+  // workspace: [sem: nh int32][part_ml: units*G*2 f32][part_o: units*G*D f32]
   char* ws = static_cast<char*>(workspace);
-  p.part_o = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)units * G * c.D * 4);
+  p.sem = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)nh * 4);
   p.part_ml = reinterpret_cast<float*>(ws);
   ws += align256((size_t)units * G * 2 * 4);
-  p.head_units = reinterpret_cast<int32_t*>(ws);
+  p.part_o = reinterpret_cast<float*>(ws);
   p.Hkv = c.Hkv;
   p.G = G;
   p.Hq = Hq;
@@ -417,12 +459,6 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
       attn_kernel<false, 64><<<grid, kBlock, 0, s>>>(p);
     else
       attn_kernel<false, 128><<<grid, kBlock, 0, s>>>(p);
-  }
-  if (units > nh) {
-    if (fp8)
-      attn_merge_kernel<true><<<nh, kBlock, 0, s>>>(p, c.D);
-    else
-      attn_merge_kernel<false><<<nh, kBlock, 0, s>>>(p, c.D);
   }
   return hipGetLastError();
 }

@@ -20,6 +20,24 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kTile = CDA_SEG_ALIGN;   // rows per V tile and per segment granule
 constexpr int kBlock = 256;            // threads per workgroup of every kernel
 
+// Byte offset, inside its 64-row tile, of the 16-byte chunk c of row r of a
+// K pool whose rows are rb = D * e bytes.  The permutation puts the data one
+// 64-lane load instruction of the attention kernel needs (16 rows x 64 bytes,
+// in MFMA operand order) into 1 KB of consecutive bytes:
+//   instruction (m, j) = ((r >> 2) & 3, c >> 2), lane = (c & 3) * 16 + g,
+//   g = ((r >> 4) << 2) | (r & 3).
+__host__ __device__ __forceinline__ int k_chunk_offset(int r, int c, int rb) {
+  const int m = (r >> 2) & 3, g = ((r >> 4) << 2) | (r & 3);
+  return ((m * (rb >> 6) + (c >> 2)) << 10) + ((c & 3) << 8) + (g << 4);
+}
+
+// Byte offset of the 8 consecutive elements starting at d0 (a multiple of
+// 8) of pool row `row` in a K pool of D-element rows of e-byte elements.
+__device__ __forceinline__ int64_t k_elem8(int64_t row, int d0, int D, int e) {
+  const int rb = D * e, b = d0 * e;
+  return (row / kTile) * kTile * rb + k_chunk_offset((int)(row % kTile), b >> 4, rb) + (b & 15);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

@@ -10,6 +10,8 @@
 //
 // All of these run once per prefill or move at most one row per segment per
 // step; the decode hot loop is the attention kernel.
+#include <type_traits>
+
 #include "cda_device.h"
 #include "cda_launch.h"
 
@@ -32,10 +34,12 @@ __global__ __launch_bounds__(kBlock) void count_kernel(
     const int p0 = base + tid * 16;
     uint32_t flags = 0;
     int cnt = 0;
+    uint8_t kb[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kb[j] = ncand > 0 ? row[min(p0 + j, ncand - 1)] : 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int p = p0 + j;
-      const int f = (p < ncand) && row[p] != 0;
+      const int f = (p0 + j < ncand) && kb[j] != 0;
       flags |= (uint32_t)f << j;
       cnt += f;
     }
@@ -113,49 +117,76 @@ __device__ __forceinline__ uint32_t abs_bits(uint32_t word, int half) {
   return ((word >> (16 * half)) & 0x7FFFu) << 16;
 }
 
+__global__ void amax_zero_kernel(int nh, float* __restrict__ k_amax, float* __restrict__ v_amax) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nh) {
+    k_amax[i] = 0.0f;
+    v_amax[i] = 0.0f;
+  }
+}
+
+// Workgroup (segment i, chunk c): absmax of K and V over the stored prefill
+// rows of positions [256c, 256c+256), folded into k_amax / v_amax with an
+// unsigned atomic max on the magnitude bit patterns.
 __global__ __launch_bounds__(kBlock) void amax_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t sb, int64_t st,
     int64_t sh, const uint8_t* __restrict__ keep, int64_t keep_ld, int T, int W, int Hkv,
     int D, float* __restrict__ k_amax, float* __restrict__ v_amax) {
+  __shared__ int smem[4];
+  __shared__ int s_pos[kBlock];
   __shared__ uint32_t red[2][kBlock / 64];
-  const int i = blockIdx.x, b = i / Hkv, h = i - b * Hkv;
+  const int i = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int b = i / Hkv, h = i - b * Hkv;
+  const uint8_t* krow = keep + (int64_t)i * keep_ld;
+  const int pp = c * kBlock + tid;
+  const int stored = pp < T && (pp >= T - W || krow[pp] != 0);
+  int nst;
+  const int slot = block_exclusive_scan(stored, &nst, smem);
+  if (stored) s_pos[slot] = pp;
+  __syncthreads();
   const int lpr = D / 8;                 // lanes per row, 8 bf16 (16 B) each
   const int rows_per_pass = kBlock / lpr;
-  const int lr = threadIdx.x % lpr, r = threadIdx.x / lpr;
-  const uint8_t* krow = keep + (int64_t)i * keep_ld;
+  const int lr = tid % lpr;
   uint32_t mk = 0, mv = 0;
-  for (int p = r; p < T; p += rows_per_pass) {
-    if (p < T - W && krow[p] == 0) continue;   // evicted: not stored
-    const int64_t off = (int64_t)b * sb + (int64_t)p * st + (int64_t)h * sh + lr * 8;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(k + off);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(v + off);
+  for (int e0 = tid / lpr; e0 < nst; e0 += 4 * rows_per_pass) {
+    u32x4 a[4], cc[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int j = 0; j < 4; ++j) {
+      // rows past the end repeat the last stored row: same maximum
+      const int e = min(e0 + j * rows_per_pass, nst - 1);
+      const int64_t off = (int64_t)b * sb + (int64_t)s_pos[e] * st + (int64_t)h * sh + lr * 8;
+      a[j] = *reinterpret_cast<const u32x4*>(k + off);
+      cc[j] = *reinterpret_cast<const u32x4*>(v + off);
+    }
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        mk = max(mk, abs_bits(a[w], hf));
-        mv = max(mv, abs_bits(c[w], hf));
-      }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          mk = max(mk, abs_bits(a[j][w], hf));
+          mv = max(mv, abs_bits(cc[j][w], hf));
+        }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     mk = max(mk, (uint32_t)__shfl_xor((int)mk, o, 64));
     mv = max(mv, (uint32_t)__shfl_xor((int)mv, o, 64));
   }
-  const int wid = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int wid = tid >> 6;
+  if ((tid & 63) == 0) {
     red[0][wid] = mk;
     red[1][wid] = mv;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t a = 0, c = 0;
+  if (tid == 0 && nst > 0) {
+    uint32_t x = 0, y = 0;
     for (int w = 0; w < kBlock / 64; ++w) {
-      a = max(a, red[0][w]);
-      c = max(c, red[1][w]);
+      x = max(x, red[0][w]);
+      y = max(y, red[1][w]);
     }
-    k_amax[i] = __uint_as_float(a);
-    v_amax[i] = __uint_as_float(c);
+    atomicMax(reinterpret_cast<unsigned int*>(k_amax + i), x);
+    atomicMax(reinterpret_cast<unsigned int*>(v_amax + i), y);
   }
 }
 
@@ -182,9 +213,34 @@ __device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
   return (row / kTile) * kTile * D + (int64_t)d * kTile + (row % kTile);
 }
 
+// Store 8 consecutive elements (d0 .. d0+7) of one row: K row-major, V into
+// its column-major tile; FP8 encodes x * inv.
+template <bool FP8>
+__device__ __forceinline__ void store_row8(uint8_t* k_pool, uint8_t* v_pool, int64_t r, int d0,
+                                           int D, u32x4 kin, u32x4 vin, float kinv, float vinv) {
+  if (FP8) {
+    uint32_t kc[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t kb = (kin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const uint32_t vb = (vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      kc[j >> 2] |= e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv)) << (8 * (j & 3));
+      v_pool[v_elem(r, d0 + j, D)] = (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+    }
+    *reinterpret_cast<u32x2*>(k_pool + k_elem8(r, d0, D, 1)) = u32x2{kc[0], kc[1]};
+  } else {
+    *reinterpret_cast<u32x4*>(k_pool + k_elem8(r, d0, D, 2)) = kin;
+    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pool);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vp[v_elem(r, d0 + j, D)] = (uint16_t)((vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+  }
+}
+
 // Workgroup (segment i, chunk c) handles prefill positions [256c, 256c+256).
 template <bool FP8>
 __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
+  constexpr int kPre = 32;   // keep bytes per thread of the prefix count
   __shared__ int smem[4];
   __shared__ int s_pos[kBlock], s_dst[kBlock];
   const int i = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
@@ -192,15 +248,23 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
   const int T = p.T, W = p.W, D = p.D;
   const uint8_t* row = p.keep + (int64_t)i * p.keep_ld;
   const int ncand = T - W > 0 ? T - W : 0;
+  const int pp = c * kBlock + tid;
 
-  // kept older positions before this chunk
-  int before = 0;
+  // kept older positions before this chunk (up to 8192 bytes per pass, one
+  // round trip), and this thread's own keep byte
   const int lim = min(c * kBlock, ncand);
-  for (int q = tid; q < lim; q += kBlock) before += row[q] != 0;
+  const int own = (pp < ncand) ? row[pp] : 0;
+  int before = 0;
+  for (int q0 = tid * kPre; q0 < lim; q0 += kBlock * kPre) {
+    uint8_t kb[kPre];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) kb[j] = row[min(q0 + j, lim - 1)];
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) before += (q0 + j < lim) && kb[j] != 0;
+  }
   before = block_sum(before, smem);
 
-  const int pp = c * kBlock + tid;
-  const int flag = (pp < ncand) && row[pp] != 0;
+  const int flag = (pp < ncand) && own != 0;
   int dummy;
   const int rank = block_exclusive_scan(flag, &dummy, smem);
   int stored = 0, dst = -1;
@@ -233,33 +297,27 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
   }
   const int64_t base = p.seg_base[i];
   const int lpr = D / 8;
-  for (int e = tid / lpr; e < nst; e += kBlock / lpr) {
-    const int64_t r = base + s_dst[e];
-    if (r < 0 || r >= p.pool_rows) {
-      if (tid % lpr == 0) atomicOr(p.err, CDA_DEVERR_POOL);
-      continue;
+  const int rows_per_pass = kBlock / lpr;
+  const int d0 = (tid % lpr) * 8;
+  for (int e0 = tid / lpr; e0 < nst; e0 += 4 * rows_per_pass) {
+    u32x4 kin[4], vin[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = min(e0 + j * rows_per_pass, nst - 1);
+      const int64_t off = (int64_t)b * p.sb + (int64_t)s_pos[e] * p.st + (int64_t)h * p.sh + d0;
+      kin[j] = *reinterpret_cast<const u32x4*>(p.k + off);
+      vin[j] = *reinterpret_cast<const u32x4*>(p.v + off);
     }
-    const int d0 = (tid % lpr) * 8;
-    const int64_t off = (int64_t)b * p.sb + (int64_t)s_pos[e] * p.st + (int64_t)h * p.sh + d0;
-    const u32x4 kin = *reinterpret_cast<const u32x4*>(p.k + off);
-    const u32x4 vin = *reinterpret_cast<const u32x4*>(p.v + off);
-    if (FP8) {
-      uint32_t kc[2] = {0, 0};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t kb = (kin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        const uint32_t vb = (vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        kc[j >> 2] |= e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv)) << (8 * (j & 3));
-        p.v_pool[v_elem(r, d0 + j, D)] =
-            (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + j * rows_per_pass;
+      if (e >= nst) continue;
+      const int64_t r = base + s_dst[e];
+      if (r < 0 || r >= p.pool_rows) {
+        if (d0 == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+        continue;
       }
-      *reinterpret_cast<u32x2*>(p.k_pool + r * D + d0) = u32x2{kc[0], kc[1]};
-    } else {
-      *reinterpret_cast<u32x4*>(p.k_pool + (r * D + d0) * 2) = kin;
-      uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        vp[v_elem(r, d0 + j, D)] = (uint16_t)((vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      store_row8<FP8>(p.k_pool, p.v_pool, r, d0, D, kin[j], vin[j], kinv, vinv);
     }
   }
 }
@@ -285,96 +343,114 @@ struct AppendParams {
   int32_t* err;
 };
 
-// Copy (or encode) one element of K and V between rows / from the input.
+// 8 consecutive K elements of a row (8 FP8 bytes or 8 bf16 = 16 bytes).
 template <bool FP8>
-__device__ __forceinline__ void move_elem(const AppendParams& p, int64_t from, int64_t to, int d) {
-  if (FP8) {
-    p.k_pool[to * p.D + d] = p.k_pool[from * p.D + d];
-    p.v_pool[v_elem(to, d, p.D)] = p.v_pool[v_elem(from, d, p.D)];
-  } else {
-    uint16_t* kp = reinterpret_cast<uint16_t*>(p.k_pool);
-    uint16_t* vp = reinterpret_cast<uint16_t*>(p.v_pool);
-    kp[to * p.D + d] = kp[from * p.D + d];
-    vp[v_elem(to, d, p.D)] = vp[v_elem(from, d, p.D)];
-  }
-}
+struct Row8 {
+  typedef typename std::conditional<FP8, u32x2, u32x4>::type type;
+};
 
-// Workgroup b handles sequence b: every head's ring exit, then every new token.
+// Workgroup b handles sequence b.  Thread t owns elements [8c, 8c+8) of one
+// head's K and V rows (c = t mod D/8).  Straight-line code, two dependent
+// round trips: (1) position, segment metadata and its slice of the new
+// token; (2) the exiting ring row's keep bit and its slice of that row.
+// Then it writes the moved slice (if kept) and the new token's slice into
+// the ring row; the old slice was read by the same thread, before.
 template <bool FP8>
 __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
-  __shared__ long long s_from[kBlock], s_to[kBlock], s_new[kBlock];
-  __shared__ float s_kinv[kBlock], s_vinv[kBlock];
+  typedef typename std::conditional<FP8, uint8_t, uint16_t>::type elem_t;
+  typedef typename Row8<FP8>::type krow_t;
+  constexpr int E = FP8 ? 1 : 2;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int W = p.W, D = p.D;
+  const int cpr = D / 8;                       // 8-element chunks per row
   const int P = p.pos[b];
-  for (int h0 = 0; h0 < p.Hkv; h0 += kBlock) {
-    const int nhc = min(kBlock, p.Hkv - h0);
-    if (tid < nhc) {
-      const int h = h0 + tid;
-      const int64_t i = (int64_t)b * p.Hkv + h;
-      const int64_t base = p.seg_base[i];
-      int cl = p.comp_len[i];
-      const int cap = p.seg_cap[i];
-      long long from = -1, to = -1, nw = -1;
-      const int kept = p.keep[i] != 0;
-      if (W > 0) {
-        const int exit_pos = P - W;
-        if (exit_pos >= 0 && p.ring_keep[i * W + exit_pos % W]) {
-          if (cl < cap) {
-            from = base + exit_pos % W;
-            to = base + W + cl;
-            ++cl;
-          } else {
-            atomicOr(p.err, CDA_DEVERR_CAPACITY);
-          }
-        }
-        nw = base + P % W;
-        p.ring_keep[i * W + P % W] = (uint8_t)kept;
-      } else if (kept) {
+  elem_t* vp = reinterpret_cast<elem_t*>(p.v_pool);
+  for (int h0 = 0; h0 < p.Hkv; h0 += kBlock / cpr) {
+    const int h = h0 + tid / cpr, d0 = (tid % cpr) * 8;
+    if (h >= p.Hkv) continue;
+    const int64_t i = (int64_t)b * p.Hkv + h;
+    const int64_t base = p.seg_base[i];
+    const int cl0 = p.comp_len[i];
+    const int cap = p.seg_cap[i];
+    const int kept = p.keep[i] != 0;
+    const float kinv = FP8 ? fp8_inv_scale(p.k_amax[i]) : 1.0f;
+    const float vinv = FP8 ? fp8_inv_scale(p.v_amax[i]) : 1.0f;
+    const int64_t off = (int64_t)b * p.sb + (int64_t)h * p.sh + d0;
+    const u32x4 kn = *reinterpret_cast<const u32x4*>(p.k + off);
+    const u32x4 vn = *reinterpret_cast<const u32x4*>(p.v + off);
+
+    int64_t from = -1, to = -1, nw = -1;
+    int cl = cl0, full = 0, bad = 0;
+    if (W > 0) {
+      const int exit_pos = P - W;
+      const int eslot = exit_pos >= 0 ? exit_pos % W : 0;
+      const int64_t slot = base + eslot;
+      // the exiting row's keep bit and slice are read whether or not it moves
+      // (unconditional loads, clamped into the pool, so they share one trip)
+      const bool readable = slot < p.pool_rows;
+      const int64_t rslot = readable ? slot : 0;
+      const int rk = p.ring_keep[i * W + eslot];
+      const krow_t ok = *reinterpret_cast<const krow_t*>(p.k_pool + k_elem8(rslot, d0, D, E));
+      elem_t ov[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ov[j] = vp[v_elem(rslot, d0 + j, D)];
+      if (exit_pos >= 0 && rk) {
         if (cl < cap) {
-          nw = base + cl;
+          from = slot;
+          to = base + W + cl;
           ++cl;
         } else {
-          atomicOr(p.err, CDA_DEVERR_CAPACITY);
+          full = 1;
         }
       }
-      if ((from >= 0 && (from >= p.pool_rows || to >= p.pool_rows)) || nw >= p.pool_rows) {
-        atomicOr(p.err, CDA_DEVERR_POOL);
-        from = to = -1;
-        if (nw >= p.pool_rows) nw = -1;
+      nw = base + P % W;
+      if (from >= 0 && (!readable || to >= p.pool_rows)) {
+        from = -1;
+        bad = 1;
       }
-      p.comp_len[i] = cl;
-      s_from[tid] = from;
-      s_to[tid] = to;
-      s_new[tid] = nw;
-      s_kinv[tid] = FP8 ? fp8_inv_scale(p.k_amax[i]) : 1.0f;
-      s_vinv[tid] = FP8 ? fp8_inv_scale(p.v_amax[i]) : 1.0f;
-    }
-    __syncthreads();
-    // the token leaving the window moves out of its ring row first ...
-    for (int w = tid; w < nhc * D; w += kBlock) {
-      const int t = w / D, d = w - t * D;
-      if (s_from[t] >= 0) move_elem<FP8>(p, s_from[t], s_to[t], d);
-    }
-    __syncthreads();
-    // ... then the new token takes the row
-    for (int w = tid; w < nhc * D; w += kBlock) {
-      const int t = w / D, d = w - t * D;
-      const long long r = s_new[t];
-      if (r < 0) continue;
-      const int64_t off = (int64_t)b * p.sb + (int64_t)(h0 + t) * p.sh + d;
-      const uint16_t kb = p.k[off], vb = p.v[off];
-      if (FP8) {
-        p.k_pool[r * D + d] = (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), s_kinv[t]));
-        p.v_pool[v_elem(r, d, D)] =
-            (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), s_vinv[t]));
+      if (from >= 0) {
+        *reinterpret_cast<krow_t*>(p.k_pool + k_elem8(to, d0, D, E)) = ok;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vp[v_elem(to, d0 + j, D)] = ov[j];
+      }
+    } else if (kept) {
+      if (cl < cap) {
+        nw = base + cl;
+        ++cl;
       } else {
-        reinterpret_cast<uint16_t*>(p.k_pool)[r * D + d] = kb;
-        reinterpret_cast<uint16_t*>(p.v_pool)[v_elem(r, d, D)] = vb;
+        full = 1;
       }
     }
-    __syncthreads();
+    if (nw >= p.pool_rows) {
+      nw = -1;
+      bad = 1;
+    }
+    if (nw >= 0) {
+      if (FP8) {
+        uint32_t kc[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t kb = (kn[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+          const uint32_t vb = (vn[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+          kc[j >> 2] |= e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv)) << (8 * (j & 3));
+          vp[v_elem(nw, d0 + j, D)] = (elem_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+        }
+        *reinterpret_cast<u32x2*>(p.k_pool + k_elem8(nw, d0, D, 1)) = u32x2{kc[0], kc[1]};
+      } else {
+        *reinterpret_cast<u32x4*>(p.k_pool + k_elem8(nw, d0, D, 2)) = kn;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          vp[v_elem(nw, d0 + j, D)] = (elem_t)((vn[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      }
+    }
+    if (d0 == 0) {
+      p.comp_len[i] = cl;
+      if (W > 0) p.ring_keep[i * W + P % W] = (uint8_t)kept;
+      if (full) atomicOr(p.err, CDA_DEVERR_CAPACITY);
+      if (bad) atomicOr(p.err, CDA_DEVERR_POOL);
+    }
   }
+  __syncthreads();                  // every thread has read pos[b]
   if (tid == 0) p.pos[b] = P + 1;
 }
 
@@ -394,8 +470,10 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   const int nh = c.B * c.Hkv;
   if (nh == 0) return hipGetLastError();
   const bool fp8 = c.kv_dtype == CDA_KV_FP8_E4M3;
+  const dim3 grid(nh, a.T > 0 ? (a.T + kBlock - 1) / kBlock : 1);
   if (fp8 && a.scale_mode == 0) {
-    amax_kernel<<<nh, kBlock, 0, s>>>(static_cast<const uint16_t*>(a.k),
+    amax_zero_kernel<<<(nh + kBlock - 1) / kBlock, kBlock, 0, s>>>(nh, c.k_amax, c.v_amax);
+    amax_kernel<<<grid, kBlock, 0, s>>>(static_cast<const uint16_t*>(a.k),
                                       static_cast<const uint16_t*>(a.v), a.stride_b, a.stride_t,
                                       a.stride_h, a.keep, a.keep_ld, a.T, c.W, c.Hkv, c.D,
                                       c.k_amax, c.v_amax);
@@ -421,7 +499,6 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   p.k_amax = c.k_amax;
   p.v_amax = c.v_amax;
   p.err = c.err;
-  dim3 grid(nh, a.T > 0 ? (a.T + kBlock - 1) / kBlock : 1);
   if (fp8)
     pack_kernel<true><<<grid, kBlock, 0, s>>>(p);
   else

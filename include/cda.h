@@ -37,10 +37,17 @@
  *   seg_base[i+1] = seg_base[i] + roundup(W + seg_cap[i], CDA_SEG_ALIGN).
  *   The rows holding data are always the contiguous run [0, n_i) with
  *   n_i = min(W, pos[b]) + comp_len[i].
- *   k_pool: row-major, row r at byte r * D * e (e = 2 for BF16, 1 for FP8).
- *   v_pool: tiles of CDA_SEG_ALIGN rows stored column-major: element (r, d)
- *     at byte ((r / 64) * 64 * D + d * 64 + r % 64) * e, so that the 64
- *     values of one column of a tile are contiguous.
+ *   Both pools are split into tiles of CDA_SEG_ALIGN = 64 rows (tile t =
+ *   pool rows [64t, 64t+64), 64 * D * e bytes, e = 2 for BF16, 1 for FP8).
+ *   k_pool: rows are cut into 16-byte chunks; chunk c of row r (r taken
+ *     inside its tile) is at tile byte
+ *       ((m * (D*e/64) + c / 4) * 1024) + (c % 4) * 256 + g * 16,
+ *       m = (r / 4) % 4,  g = (r / 16) * 4 + r % 4,
+ *     so that every 1 KB of a tile is what one 64-lane load of the attention
+ *     kernel needs (the rows of a tile are a permutation of its bytes).
+ *   v_pool: tiles stored column-major: element (r, d) at byte
+ *     ((r / 64) * 64 * D + d * 64 + r % 64) * e, so that the 64 values of one
+ *     column of a tile are contiguous.
  *   FP8: code = E4M3FN_RNE_SATURATE(f32(x) * inv), inv = 448 / amax and
  *   value = code * s, s = amax / 448 (both single f32 divisions; s = inv = 1
  *   when amax is 0 or not finite).  amax is the largest |x| over the
@@ -92,7 +99,7 @@ typedef struct cda_kv_cache {
     int32_t kv_dtype;   /* enum cda_kv_dtype */
     int32_t reserved0;  /* must be 0 */
     int64_t pool_rows;  /* rows allocated in k_pool and v_pool (multiple of 64) */
-    void *k_pool;       /* [pool_rows, D] */
+    void *k_pool;       /* [pool_rows / 64] tiles of 64 x D, chunk-permuted (see above) */
     void *v_pool;       /* [pool_rows / 64][D][64] */
     int64_t *seg_base;  /* [B*Hkv + 1]; written by COUNT; [B*Hkv] = rows needed */
     int32_t *seg_cap;   /* [B*Hkv]; written by COUNT */
@@ -165,8 +172,13 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  *                multiple of 64; 0 = default (256).  Heads longer than one
  *                unit are split and their partials merged.
  *   workspace    device scratch of at least cda_attn_workspace_bytes()
- *                bytes (partials of the split heads); contents need no
- *                initialisation and are not preserved.
+ *                bytes: one completion counter per segment, then the
+ *                partial states of split segments.  It must be zero-filled
+ *                before its first use; every completed call leaves the
+ *                counters at zero again, so one workspace can serve any
+ *                later call (any cache, any split) ordered after it on a
+ *                stream.  Calls that may run concurrently need separate
+ *                workspaces.
  */
 int32_t decode_attn_compact(const cda_kv_cache *cache, const void *q, int32_t Hq,
                             float sm_scale, void *out, int32_t out_dtype, float *lse,

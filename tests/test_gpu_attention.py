@@ -69,6 +69,32 @@ def test_split_invariance(split):
     check_close(lse, rlse, f"split {split} lse", atol=1e-4, rtol=1e-5)
 
 
+def test_one_workspace_reused_across_splits_and_caches():
+    # the completion counters are left at zero by every call, so a single
+    # zero-filled workspace serves calls with different splits and caches
+    B, Hq, Hkv, D, T, W = 2, 16, 4, 128, 2000, 64
+    keep = workload.random_keep((B, Hkv, T), 0.3, seed=91)
+    k = workload.random_bf16((B, T, Hkv, D), seed=92)
+    v = workload.random_bf16((B, T, Hkv, D), seed=93)
+    q = workload.random_bf16((B, Hq, D), seed=94)
+    caches = [gpu_prefill(k, v, keep, T, W, 0, dt, with_dst=False)[0] for dt in ("fp8", "bf16")]
+    n = max(c.workspace(Hq, 64).numel() for c in caches)
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev())
+    refs = {}
+    for c in caches:
+        ka = c.k_amax.cpu().numpy() if c.kv_dtype == "fp8" else None
+        va = c.v_amax.cpu().numpy() if c.kv_dtype == "fp8" else None
+        refs[c.kv_dtype] = oracle.attention(q, k, v, keep, T - 1, W, odt(c.kv_dtype), ka, va)[0]
+    qd = q.to(dev())
+    for rep in range(3):
+        for split in (64, 320, 128, 100000, 0):
+            for c in caches:
+                out = c.attention(qd, out_dtype=torch.float32, split_tokens=split, workspace=ws)
+                check_close(out.cpu().numpy(), refs[c.kv_dtype], f"{c.kv_dtype} split {split} rep {rep}")
+    nh = B * Hkv
+    assert torch.count_nonzero(ws[: 4 * nh]) == 0
+
+
 def test_outliers_and_custom_scale():
     # large-magnitude K and V (FP8 scales far from 1) and an explicit sm_scale
     case = (2, 16, 4, 128, 1200, 64, 0.2, "fp8", 31)
