@@ -14,12 +14,12 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_KV_BF16, CDA_KV_FP8_E4M3,
+from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD, CDA_KV_BF16, CDA_KV_FP8_E4M3,
                    CDA_OP_APPEND, CDA_OP_COUNT, CDA_OP_PACK, CDA_OUT_BF16, CDA_OUT_F32,
                    CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
 __all__ = ["CompactKVCache", "kv_compact", "decode_attn_compact", "CdaError",
-           "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY", "CDA_DEVERR_POOL"]
+           "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY", "CDA_DEVERR_POOL", "CDA_DEVERR_XCD"]
 
 _DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3}
 

@@ -81,6 +81,9 @@ enum cda_status {
  * the host sees them only after it synchronises and copies the word). */
 #define CDA_DEVERR_CAPACITY 1   /* APPEND: a segment's compact region was full; that token was dropped */
 #define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written */
+#define CDA_DEVERR_XCD 4        /* attention: a workgroup ran on an XCD other than the one the
+                                   XCD-local merge assumes (workgroup w on XCD w mod #XCDs);
+                                   that call's outputs are not reliable */
 
 enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1 };
 enum cda_out_dtype { CDA_OUT_BF16 = 0, CDA_OUT_F32 = 1 };
@@ -171,6 +174,8 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  *   split_tokens rows per work unit (one workgroup), rounded up to a
  *                multiple of 64; 0 = default (256).  Heads longer than one
  *                unit are split and their partials merged.
+ *   The call reads the device's XCD count (hipDeviceGetAttribute) on the
+ *   current device; the attention may set CDA_DEVERR_XCD in cache->err.
  *   workspace    device scratch of at least cda_attn_workspace_bytes()
  *                bytes: one completion counter per segment, then the
  *                partial states of split segments.  It must be zero-filled
