@@ -14,9 +14,10 @@ all enqueued on one stream with no host synchronisation inside the step.
 
 Reported: value = decode-attention KV bytes moved per second over the whole
 step (algorithmic bytes: every stored row's K and V read once per decode
-step and layer, divided by the step's wall time); roofline of the attention
-kernel from HIP events around every attention call in the timed region;
-the CPU oracle timed on a bounded sample; and parity of that sample.
+step and layer, divided by the step's wall time); the roofline of the
+attention kernel, its per-launch duration measured with HIP events on its
+stream around back-to-back launches over all layers right after the timed
+steps; the CPU oracle timed on a bounded sample; and parity of that sample.
 """
 from __future__ import annotations
 
@@ -113,6 +114,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="0 = all layers of the config")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 64 MiB device copy 3 times (the reference kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the compact decode-attention path runs on a "
@@ -125,6 +129,14 @@ def main():
     from compressed_decode_attention_amd import CompactKVCache, _lib
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 64 MiB three times")
+        return
     cfg = workload.CONFIGS[args.config]
     L = args.layers or cfg.L
     B, Hq, Hkv, D, T, S, W = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.T, cfg.S, cfg.W
@@ -157,10 +169,8 @@ def main():
     step_attn_bytes = float(attn_bytes.sum())
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(L)] for _ in range(S)]
 
-    def run_step(timed_events: bool):
+    def run_step():
         for l in range(L):
             c = caches[l]
             c.count(keepd[l], T, reserve=S)
@@ -169,31 +179,24 @@ def main():
             for l in range(L):
                 c = caches[l]
                 c.append(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s])
-                if timed_events:
-                    ev[s][l][0].record(stream)
                 c.attention(qd[l][s], out=outs[l], split_tokens=args.split)
-                if timed_events:
-                    ev[s][l][1].record(stream)
 
     for _ in range(args.warmup):
-        run_step(False)
+        run_step()
     torch.cuda.synchronize()
     for c in caches:
         if c.error_word() != 0:
             raise RuntimeError("device error word set during warm-up")
     log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
 
-    step_ms, attn_us = [], []
+    step_ms = []
     for k in range(args.steps):
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        run_step(True)
+        run_step()
         torch.cuda.synchronize()
         step_ms.append((time.perf_counter() - t_start) * 1e3)
-        attn_us.append(np.array([[ev[s][l][0].elapsed_time(ev[s][l][1]) * 1e3
-                                  for l in range(L)] for s in range(S)]))
         log(f"step {k}: {step_ms[-1]:.2f} ms")
-    attn_us = np.stack(attn_us)                 # [K, S, L]
 
     # the device state after the last step must match the host accounting
     for l in range(L):
@@ -201,12 +204,38 @@ def main():
         if not np.array_equal(got, nrows[l][S - 1]):
             raise RuntimeError(f"layer {l}: device stored-row counts differ from the keep mask")
 
+    # Per-launch duration of the attention kernel: HIP events on the kernel's
+    # stream around back-to-back launches over all layers, at the decode
+    # state the timed steps ended in (last step).  One event pair per layer
+    # sweep, so event overhead does not land inside the average.
+    reps = 5
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for l in range(L):
+        caches[l].attention(qd[l][S - 1], out=outs[l], split_tokens=args.split)
+    ev_a.record(stream)
+    for _ in range(reps):
+        for l in range(L):
+            caches[l].attention(qd[l][S - 1], out=outs[l], split_tokens=args.split)
+    ev_b.record(stream)
+    torch.cuda.synchronize()
+    kernel_us = ev_a.elapsed_time(ev_b) * 1e3 / (reps * L)
+    bytes_per_launch = float(attn_bytes[S - 1].mean())
+
+    # prefill compaction alone (COUNT + PACK of every layer), for the split
+    # of the step time; this leaves the caches in their prefill state
+    ev_a.record(stream)
+    for _ in range(reps):
+        for l in range(L):
+            caches[l].count(keepd[l], T, reserve=S)
+            caches[l].pack(kd[l], vd[l], keepd[l], T)
+    ev_b.record(stream)
+    torch.cuda.synchronize()
+    prefill_ms = ev_a.elapsed_time(ev_b) / reps
+
     ms = float(np.mean(step_ms))
     value = step_attn_bytes / (ms * 1e-3) / 1e9
     tokens_per_s = B * S / (ms * 1e-3)
-    mean_launch_us = float(attn_us.mean())
-    bytes_per_launch = float(attn_bytes.mean())
-    achieved = bytes_per_launch / (mean_launch_us * 1e-6) / 1e9
+    achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
     traffic = traffic_from_profile()
 
     cpu = None
@@ -228,16 +257,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: Qwen3-8B attention shape, ctx {T}, gen {S}, "
-                               f"c={B}, {cfg.kv_dtype} compact KV, W={W}",
+        "config": {"workload": f"{cfg.name}: {cfg.L} layers x (Hq {Hq}, Hkv {Hkv}, D {D}), "
+                               f"ctx {T}, gen {S}, c={B}, {cfg.kv_dtype} compact KV, W={W}",
                    "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
-                   "kv_storage": cfg.kv_dtype, "split_tokens": args.split or 256,
+                   "kv_storage": cfg.kv_dtype, "split_tokens": args.split or "library default",
                    "parallelism": "single GPU"},
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "attn_call_us_mean": round(mean_launch_us, 3),
-        "attn_call_us_p10_p90": [round(float(np.percentile(attn_us, 10)), 3),
-                                 round(float(np.percentile(attn_us, 90)), 3)],
+        "attn_kernel_us": round(kernel_us, 3),
+        "prefill_compaction_ms": round(prefill_ms, 3),
+        "decode_layer_step_us": round((ms - prefill_ms) * 1e3 / (S * L), 3),
         "kv_bytes_per_decode_step": round(float(attn_bytes.sum(axis=1).mean())),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

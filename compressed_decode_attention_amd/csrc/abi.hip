@@ -8,7 +8,10 @@
 
 namespace {
 
-constexpr int kDefaultSplit = 256;   // rows per attention work unit
+// Default rows per attention work unit: 512 for large pools (fewer units
+// and partials per segment), 256 otherwise (enough units to fill the chip).
+constexpr int kDefaultSplitLarge = 512, kDefaultSplitSmall = 256;
+constexpr int64_t kLargePoolRows = 1 << 16;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -42,8 +45,10 @@ int32_t check_bf16_rows(const void* k, const void* v, int64_t sb, int64_t st, in
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? CDA_OK : CDA_ERR_HIP; }
 
-int tiles_per_unit(int32_t split_tokens) {
-  const int s = split_tokens > 0 ? split_tokens : kDefaultSplit;
+int tiles_per_unit(const cda_kv_cache* c, int32_t split_tokens) {
+  const int s = split_tokens > 0
+                    ? split_tokens
+                    : (c->pool_rows >= kLargePoolRows ? kDefaultSplitLarge : kDefaultSplitSmall);
   return (s + CDA_SEG_ALIGN - 1) / CDA_SEG_ALIGN;
 }
 
@@ -88,7 +93,7 @@ int32_t kv_compact(const cda_kv_cache* c, const cda_compact_args* a, void* strea
 
 size_t cda_attn_workspace_bytes(const cda_kv_cache* c, int32_t Hq, int32_t split_tokens) {
   if (check_cache(c) != CDA_OK || Hq <= 0 || Hq % c->Hkv != 0 || split_tokens < 0) return 0;
-  return cda::attn_workspace_bytes(*c, Hq / c->Hkv, tiles_per_unit(split_tokens));
+  return cda::attn_workspace_bytes(*c, Hq / c->Hkv, tiles_per_unit(c, split_tokens));
 }
 
 int32_t decode_attn_compact(const cda_kv_cache* c, const void* q, int32_t Hq, float sm_scale,
@@ -104,7 +109,7 @@ int32_t decode_attn_compact(const cda_kv_cache* c, const void* q, int32_t Hq, fl
     if (!q || !out || !aligned(q, 16) || !aligned(out, 4)) return CDA_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return CDA_ERR_INVALID_ARG;
   }
-  const int tpu = tiles_per_unit(split_tokens);
+  const int tpu = tiles_per_unit(c, split_tokens);
   const size_t need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, tpu);
   if (workspace_bytes < need) return CDA_ERR_WORKSPACE;
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return CDA_ERR_INVALID_ARG;

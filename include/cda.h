@@ -172,8 +172,9 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  *   out          [B, Hq, D] contiguous, BF16 or F32 per out_dtype
  *   lse          optional F32 [B, Hq] (natural log), may be NULL
  *   split_tokens rows per work unit (one workgroup), rounded up to a
- *                multiple of 64; 0 = default (256).  Heads longer than one
- *                unit are split and their partials merged.
+ *                multiple of 64; 0 = default (512 when pool_rows >= 65536,
+ *                else 256).  Heads longer than one unit are split and their
+ *                partials merged.
  *   The call reads the device's XCD count (hipDeviceGetAttribute) on the
  *   current device; the attention may set CDA_DEVERR_XCD in cache->err.
  *   workspace    device scratch of at least cda_attn_workspace_bytes()

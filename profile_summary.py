@@ -1,0 +1,84 @@
+"""Turn rocprofv3 output of the benchmark into the short text summaries kept
+under profiles/.
+
+  python profile_summary.py trace <kernel_stats.csv> <command> > profiles/X.md
+  python profile_summary.py traffic <copy FETCH csv> <copy WRITE csv>
+         <bench FETCH csv> <bench WRITE csv> <commands...>
+
+The traffic mode scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
+dispatch) by what the same counter reads for the plain 64 MiB copy of
+`bench.py --copy-calibration`, and writes profiles/attn_qwen_c8_traffic.json
+(read by bench.py while it matches the attention kernel source) plus a
+markdown table on stdout.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "attn.hip")
+COPY_KIB = 64 * 1024
+
+
+def short(name: str) -> str:
+    ours = "cda::" in name
+    name = name.replace("cda::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0] if ours else name[:60]
+
+
+def trace(stats_csv: str, command: str) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    print(f"# rocprofv3 kernel trace summary\n\nCommand (from the repository root):\n\n"
+          f"```\n{command}\n```\n")
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for r in rows[:12]:
+        print(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+              f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
+              f"{float(r['Percentage']):.1f}% |")
+
+
+def _mean(path: str, pat: str) -> dict:
+    v = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if pat in r["Kernel_Name"]:
+            v[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(x) / len(x) for k, x in v.items()}
+
+
+def traffic(cf: str, cw: str, bf: str, bw: str, commands: list[str]) -> None:
+    fcal = COPY_KIB / list(_mean(cf, "direct_copy").values())[0]
+    wcal = COPY_KIB / list(_mean(cw, "direct_copy").values())[0]
+    fetch, write = _mean(bf, "cda"), _mean(bw, "cda")
+    print("# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)\n")
+    print("Commands (from the repository root), one counter per run:\n\n```")
+    for c in commands:
+        print(c)
+    print("```\n")
+    print(f"Calibration: a plain 64 MiB copy reads as FETCH_SIZE x{fcal:.4f} and "
+          f"WRITE_SIZE x{wcal:.4f} of the true KiB; the figures below are scaled by them.\n")
+    print("| kernel | fetched MB | written MB |")
+    print("|---|---:|---:|")
+    for k in fetch:
+        print(f"| `{k}` | {fetch[k] * fcal * 1024 / 1e6:.3f} | {write.get(k, 0) * wcal * 1024 / 1e6:.3f} |")
+    attn = [k for k in fetch if k.startswith("attn_kernel")][0]
+    rec = {"attn_src_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+           "kernel": attn,
+           "fetch_bytes_per_launch": fetch[attn] * fcal * 1024,
+           "write_bytes_per_launch": write[attn] * wcal * 1024,
+           "hbm_bytes_per_launch": (fetch[attn] * fcal + write[attn] * wcal) * 1024,
+           "fetch_scale": fcal, "write_scale": wcal}
+    with open(os.path.join(ROOT, "profiles", "attn_qwen_c8_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3])
+    else:
+        traffic(*sys.argv[2:6], sys.argv[6:])
