@@ -1,7 +1,8 @@
 """Compact (DMS-style) decode attention for MI355X (gfx950).
 
-Python face of libcda_hip.so.  The two calls of the C ABI are exposed under
-their own names (:func:`kv_compact`, :func:`decode_attn_compact`); the class
+Python face of libcda_hip.so.  The calls of the C ABI are exposed under
+their own names (:func:`kv_compact`, :func:`decode_attn_compact`,
+:func:`decode_step_compact`); the class
 :class:`CompactKVCache` holds one layer's device buffers (torch tensors) and
 forwards to them.  All arithmetic runs in the library's HIP kernels; this
 module only checks shapes and passes pointers.  There is no CPU path: if the
@@ -18,7 +19,7 @@ from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD, CDA_KV_
                    CDA_OP_APPEND, CDA_OP_COUNT, CDA_OP_PACK, CDA_OUT_BF16, CDA_OUT_F32,
                    CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
-__all__ = ["CompactKVCache", "kv_compact", "decode_attn_compact", "CdaError",
+__all__ = ["CompactKVCache", "kv_compact", "decode_attn_compact", "decode_step_compact", "CdaError",
            "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY", "CDA_DEVERR_POOL", "CDA_DEVERR_XCD"]
 
 _DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3}
@@ -32,9 +33,8 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-def kv_compact(cache: "CompactKVCache", op: int, *, T: int = 0, reserve: int = 0,
-               scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None) -> None:
-    """One kv_compact call (COUNT, PACK or APPEND) on ``cache``'s stream."""
+def _compact_args(cache: "CompactKVCache", op: int, T: int = 0, reserve: int = 0,
+                  scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None) -> CdaCompactArgs:
     a = CdaCompactArgs()
     a.op, a.T, a.reserve, a.scale_mode = op, T, reserve, scale_mode
     if keep is not None:
@@ -66,15 +66,19 @@ def kv_compact(cache: "CompactKVCache", op: int, *, T: int = 0, reserve: int = 0
         if dst_out.dtype != torch.int32 or not dst_out.is_contiguous() or dst_out.numel() < cache.B * cache.Hkv * T:
             raise ValueError("dst_out must be a contiguous int32 tensor of B*Hkv*T elements")
         a.dst_out = _ptr(dst_out)
+    return a
+
+
+def kv_compact(cache: "CompactKVCache", op: int, *, T: int = 0, reserve: int = 0,
+               scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None) -> None:
+    """One kv_compact call (COUNT, PACK or APPEND) on ``cache``'s stream."""
+    a = _compact_args(cache, op, T, reserve, scale_mode, keep, k, v, dst_out)
     st = _lib.kv_compact(cache.struct, a, _stream(cache.device))
     if st != 0:
         raise CdaError(st, "kv_compact")
 
 
-def decode_attn_compact(cache: "CompactKVCache", q: torch.Tensor, out: torch.Tensor,
-                        lse: torch.Tensor | None = None, sm_scale: float = 0.0,
-                        split_tokens: int = 0, workspace: torch.Tensor | None = None) -> None:
-    """One decode_attn_compact call: q [B, Hq, D] bf16 -> out [B, Hq, D]."""
+def _check_attention(cache: "CompactKVCache", q, out, lse) -> None:
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3:
         raise ValueError("q must be a contiguous bfloat16 [B, Hq, D] tensor")
     B, Hq, D = q.shape
@@ -84,6 +88,14 @@ def decode_attn_compact(cache: "CompactKVCache", q: torch.Tensor, out: torch.Ten
         raise ValueError("out must be a contiguous [B, Hq, D] bfloat16 or float32 tensor")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq):
         raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+
+
+def decode_attn_compact(cache: "CompactKVCache", q: torch.Tensor, out: torch.Tensor,
+                        lse: torch.Tensor | None = None, sm_scale: float = 0.0,
+                        split_tokens: int = 0, workspace: torch.Tensor | None = None) -> None:
+    """One decode_attn_compact call: q [B, Hq, D] bf16 -> out [B, Hq, D]."""
+    _check_attention(cache, q, out, lse)
+    Hq = q.shape[1]
     if workspace is None:
         workspace = cache.workspace(Hq, split_tokens)
     out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
@@ -93,6 +105,27 @@ def decode_attn_compact(cache: "CompactKVCache", q: torch.Tensor, out: torch.Ten
                                   _stream(cache.device))
     if st != 0:
         raise CdaError(st, "decode_attn_compact")
+
+
+def decode_step_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: torch.Tensor,
+                        keep_new: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                        lse: torch.Tensor | None = None, sm_scale: float = 0.0,
+                        split_tokens: int = 0, workspace: torch.Tensor | None = None) -> None:
+    """One decode_step_compact call: append (k_new, v_new [B, Hkv, D] bf16,
+    keep_new [B, Hkv] uint8), then attention of q [B, Hq, D] -> out, in one
+    launch."""
+    _check_attention(cache, q, out, lse)
+    Hq = q.shape[1]
+    a = _compact_args(cache, CDA_OP_APPEND, keep=keep_new, k=k_new, v=v_new)
+    if workspace is None:
+        workspace = cache.workspace(Hq, split_tokens)
+    out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
+    st = _lib.decode_step_compact(cache.struct, a, _ptr(q), Hq, sm_scale, _ptr(out), out_dtype,
+                                  _ptr(lse), split_tokens, _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0,
+                                  _stream(cache.device))
+    if st != 0:
+        raise CdaError(st, "decode_step_compact")
 
 
 class CompactKVCache:
@@ -182,6 +215,16 @@ class CompactKVCache:
         if out is None:
             out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
         decode_attn_compact(self, q, out, lse, sm_scale, split_tokens, workspace)
+        return out
+
+    def decode_step(self, k_new, v_new, keep_new, q, out=None, out_dtype=torch.bfloat16,
+                    lse=None, sm_scale: float = 0.0, split_tokens: int = 0,
+                    workspace=None) -> torch.Tensor:
+        """append(k_new, v_new, keep_new) then attention(q), in one launch."""
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
+        decode_step_compact(self, k_new, v_new, keep_new, q, out, lse, sm_scale, split_tokens,
+                            workspace)
         return out
 
     # ---- inspection (synchronise)

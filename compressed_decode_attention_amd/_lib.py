@@ -21,8 +21,8 @@ CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16
 
 # every symbol include/cda.h declares
-EXPORTS = ("kv_compact", "decode_attn_compact", "cda_attn_workspace_bytes",
-           "cda_status_string", "cda_version")
+EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact",
+           "cda_attn_workspace_bytes", "cda_status_string", "cda_version")
 
 
 class CdaKvCache(C.Structure):
@@ -72,6 +72,10 @@ def load(path: str = LIB_PATH):
                                       C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
                                       C.c_void_p, C.c_size_t, C.c_void_p]
     L.decode_attn_compact.restype = C.c_int32
+    L.decode_step_compact.argtypes = [C.POINTER(CdaKvCache), C.POINTER(CdaCompactArgs), C.c_void_p,
+                                      C.c_int32, C.c_float, C.c_void_p, C.c_int32, C.c_void_p,
+                                      C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
+    L.decode_step_compact.restype = C.c_int32
     L.cda_attn_workspace_bytes.argtypes = [C.POINTER(CdaKvCache), C.c_int32, C.c_int32]
     L.cda_attn_workspace_bytes.restype = C.c_size_t
     L.cda_status_string.argtypes = [C.c_int32]
@@ -101,6 +105,16 @@ def decode_attn_compact(cache: CdaKvCache, q_ptr: int, Hq: int, sm_scale: float,
         C.byref(cache), C.c_void_p(q_ptr), int(Hq), float(sm_scale), C.c_void_p(out_ptr),
         int(out_dtype), C.c_void_p(lse_ptr or 0), int(split_tokens), C.c_void_p(ws_ptr or 0),
         C.c_size_t(ws_bytes), C.c_void_p(stream or 0)))
+
+
+def decode_step_compact(cache: CdaKvCache, args: CdaCompactArgs, q_ptr: int, Hq: int,
+                        sm_scale: float, out_ptr: int, out_dtype: int, lse_ptr: int | None,
+                        split_tokens: int, ws_ptr: int | None, ws_bytes: int,
+                        stream: int | None) -> int:
+    return int(load().decode_step_compact(
+        C.byref(cache), C.byref(args), C.c_void_p(q_ptr), int(Hq), float(sm_scale),
+        C.c_void_p(out_ptr), int(out_dtype), C.c_void_p(lse_ptr or 0), int(split_tokens),
+        C.c_void_p(ws_ptr or 0), C.c_size_t(ws_bytes), C.c_void_p(stream or 0)))
 
 
 def attn_workspace_bytes(cache: CdaKvCache, Hq: int, split_tokens: int) -> int:

@@ -96,9 +96,15 @@ size_t cda_attn_workspace_bytes(const cda_kv_cache* c, int32_t Hq, int32_t split
   return cda::attn_workspace_bytes(*c, Hq / c->Hkv, tiles_per_unit(c, split_tokens));
 }
 
-int32_t decode_attn_compact(const cda_kv_cache* c, const void* q, int32_t Hq, float sm_scale,
-                            void* out, int32_t out_dtype, float* lse, int32_t split_tokens,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two attention entry points; on success *tpu is the
+// work-unit size in tiles.
+int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* out,
+                        int32_t out_dtype, float* lse, int32_t split_tokens, void* workspace,
+                        size_t workspace_bytes, int* tpu) {
   int32_t st = check_cache(c);
   if (st != CDA_OK) return st;
   if ((st = check_pools(c)) != CDA_OK) return st;
@@ -109,14 +115,46 @@ int32_t decode_attn_compact(const cda_kv_cache* c, const void* q, int32_t Hq, fl
     if (!q || !out || !aligned(q, 16) || !aligned(out, 4)) return CDA_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return CDA_ERR_INVALID_ARG;
   }
-  const int tpu = tiles_per_unit(c, split_tokens);
-  const size_t need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, tpu);
+  *tpu = tiles_per_unit(c, split_tokens);
+  const size_t need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, *tpu);
   if (workspace_bytes < need) return CDA_ERR_WORKSPACE;
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return CDA_ERR_INVALID_ARG;
-  if (cda::attn_max_units(*c, tpu) > 0x7FFFFFFF) return CDA_ERR_INVALID_ARG;
+  if (cda::attn_max_units(*c, *tpu) > 0x7FFFFFFF) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t decode_attn_compact(const cda_kv_cache* c, const void* q, int32_t Hq, float sm_scale,
+                            void* out, int32_t out_dtype, float* lse, int32_t split_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int tpu = 0;
+  const int32_t st = check_attention(c, q, Hq, out, out_dtype, lse, split_tokens, workspace,
+                                     workspace_bytes, &tpu);
+  if (st != CDA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(cda::launch_attn(*c, q, Hq, sm_scale, out, out_dtype == CDA_OUT_F32, lse,
-                                     tpu, workspace, s));
+                                     tpu, workspace, s, nullptr));
+}
+
+int32_t decode_step_compact(const cda_kv_cache* c, const cda_compact_args* a, const void* q,
+                            int32_t Hq, float sm_scale, void* out, int32_t out_dtype, float* lse,
+                            int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  int tpu = 0;
+  int32_t st = check_attention(c, q, Hq, out, out_dtype, lse, split_tokens, workspace,
+                               workspace_bytes, &tpu);
+  if (st != CDA_OK) return st;
+  if (!a || a->op != CDA_OP_APPEND) return CDA_ERR_INVALID_ARG;
+  if (c->B > 0) {
+    if (!a->keep) return CDA_ERR_INVALID_ARG;
+    if ((st = check_bf16_rows(a->k, a->v, a->stride_b, 0, a->stride_h)) != CDA_OK) return st;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(cda::launch_attn(*c, q, Hq, sm_scale, out, out_dtype == CDA_OUT_F32, lse,
+                                     tpu, workspace, s, a));
 }
 
 const char* cda_status_string(int32_t status) {

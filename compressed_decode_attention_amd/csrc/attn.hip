@@ -1,4 +1,5 @@
-// Single-token GQA decode attention over the compact KV store, for gfx950.
+// Single-token GQA decode attention over the compact KV store, for gfx950,
+// alone or fused with the decode-time append of the new token.
 //
 // What is computed (FastDMS page, release and benchmark paragraphs: decode
 // over the compact store; PackKV abstract: decompression fused into the
@@ -6,12 +7,12 @@
 // attention of q[b, j] over the n_i stored rows of its KV head's segment.
 //
 // Work split.  Each segment's rows [0, n_i) are cut into 64-row tiles, and
-// tiles into work units of `tpu` tiles; one workgroup (4 waves) takes one
-// unit at a time and each wave one tile at a time.  Every wave derives the
-// unit -> (segment, tiles) map itself from pos / comp_len / seg_cap (lane l
-// looks at one segment, a wave-wide scan of unit counts finds the segment
-// holding the unit), so the host needs no copy of the lengths and no
-// workgroup barrier delays the K/V loads.  A segment with one unit writes
+// tiles into work units of `tpu` tiles; one workgroup (4 or 8 waves) takes
+// one unit at a time and each wave one tile at a time.  Every wave derives
+// the unit -> (segment, tiles) map itself from pos / comp_len / seg_cap
+// (lane l looks at one segment, a wave-wide scan of unit counts finds the
+// segment holding the unit), so the host needs no copy of the lengths and
+// no workgroup barrier delays the K/V loads.  A segment with one unit writes
 // its output directly; otherwise each unit writes an unnormalised partial
 // (m, l, o) and counts itself in with an atomic, and the last unit of the
 // segment to finish combines all of them with a log-sum-exp merge and resets
@@ -36,11 +37,33 @@
 // each lane holds exactly the 16 tokens that lane needs for its P operand,
 // so P never moves between lanes.  FP8 codes are converted to bf16 (K) or
 // f16 (V) in registers, exactly; the K scale is folded into the logit scale
-// and the V scale into the output.  P is split into a high and a low 16-bit
-// part (p = hi + lo to ~2^-17) so that the 16-bit P operand adds no visible
-// rounding.  All K/V loads of a tile are unconditional (a tile never leaves
-// its 64-row-padded segment); rows past the end of the segment are masked
-// out of the logits and the values.
+// and the V scale into the output.  With FP8 values P enters the product as
+// f16 (relative rounding <= 2^-11 per weight; V codes and the products are
+// exact in the f16 x f16 -> f32 MFMA).  With BF16 values P is split into a
+// high and a low bf16 part (p = hi + lo to ~2^-17), since one bf16 would
+// round each weight by up to 2^-9.  All K/V loads of a tile are
+// unconditional (a tile never leaves its 64-row-padded segment); rows past
+// the end of the segment are masked out of the logits and the values.
+//
+// Decode step (append fused in; FastDMS memory-table paragraph, "cache +
+// staging": the token leaving the W-row ring moves to the compact tail if
+// kept, the new token takes its ring row).  The result equals an append
+// followed by attention, computed from the state before the append:
+//   - the rows before the step are attended as they are, except that the
+//     ring row of the token leaving the window is masked when that token is
+//     not kept (it is the same row either way: if it moves, its values are
+//     the ones now in the ring row);
+//   - the new token is one more (logit, value) pair, formed in registers
+//     from the BF16 input with the frozen scales, added to the running
+//     softmax state of the wave that reads the tile of the new token's row;
+//   - that wave, after its loads of the tile, copies the leaving token from
+//     its registers to the compact tail and writes the new token's row.  No
+//     other workgroup reads those rows as data (the compact tail is past
+//     the attended rows of its segment);
+//   - pos, comp_len and ring_keep are read by every workgroup while it
+//     plans its units, so they change only after all of them are done
+//     planning: each workgroup counts itself in on a grid counter after its
+//     last plan, and the last to count in writes the new metadata.
 #include "cda_device.h"
 #include "cda_launch.h"
 
@@ -50,17 +73,16 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMergeBatch = 8;   // partials loaded per round trip in the merge
-constexpr int kMergeElems = 2;   // outputs per thread merged together
 constexpr int kXcdGroups = 8;    // segment groups of the XCD-local mode
 
 struct AttnParams {
-  const uint8_t* k_pool;
-  const uint8_t* v_pool;
+  uint8_t* k_pool;
+  uint8_t* v_pool;
   int64_t pool_rows;
   const int64_t* seg_base;
   const int32_t* seg_cap;
-  const int32_t* comp_len;
-  const int32_t* pos;
+  int32_t* comp_len;
+  int32_t* pos;
   const float* k_amax;
   const float* v_amax;
   const uint16_t* q;
@@ -70,6 +92,13 @@ struct AttnParams {
   float* part_o;       // [slots][G][D]
   float* part_ml;      // [slots][G][2]
   int32_t* sem;        // [nh]: units of the segment finished so far (0 between calls)
+  // decode step only
+  int32_t* gcount;     // workgroups done planning (0 between calls)
+  uint8_t* ring_keep;
+  const uint16_t* k_new;   // BF16 (b, h, d) at b * new_sb + h * new_sh + d
+  const uint16_t* v_new;
+  int64_t new_sb, new_sh;
+  const uint8_t* keep_new; // [nh]
   int Hkv, G, Hq, W, nh, tpu, out_f32;
   int per_xcd;         // XCD-local mode: workgroups per segment group
   int nxcc;            // XCD-local mode: XCDs of the device (divides 8)
@@ -85,13 +114,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ void store_out(const AttnParams& p, int64_t idx, float v) {
-  if (p.out_f32)
-    static_cast<float*>(p.out)[idx] = v;
-  else
-    static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16_rne(v);
 }
 
 // Final output of 4 consecutive d of query row gg of segment (b, h).
@@ -145,35 +167,84 @@ __device__ __forceinline__ f32x4 load_part4(const float* a) {
                load_part1<XL>(a + 3)};
 }
 
+// Wave-uniform copies of lane `src`'s value.
+__device__ __forceinline__ int lane_i(int x, int src) { return __builtin_amdgcn_readlane(x, src); }
+__device__ __forceinline__ float lane_f(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+__device__ __forceinline__ long long lane_l(long long x, int src) {
+  const int lo = __builtin_amdgcn_readlane((int)(x & 0xFFFFFFFF), src);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), src);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Reductions across the 16-lane rows of a wave: partner lanes l ^ 16 and
+// l ^ 32 via the row-swap permutes (no LDS round trip).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Rows of a segment in a decode step, from its state before the append
+// (P = pos >= 0, 0 <= cl <= cap, kn = keep byte of the new token != 0).
+struct StepRows {
+  int n_pre;     // rows holding data before the append
+  int new_row;   // segment row that receives the new token, -1 if it is dropped
+  int n_plan;    // rows the work units cover (n_pre, or up to new_row)
+};
+__device__ __forceinline__ StepRows step_rows(int W, int P, int cl, int cap, int kn) {
+  StepRows s;
+  s.n_pre = min(W, P) + cl;
+  s.new_row = W > 0 ? P % W : ((kn && cl < cap) ? cl : -1);
+  s.n_plan = s.new_row >= 0 ? max(s.n_pre, s.new_row + 1) : s.n_pre;
+  return s;
+}
+
 // The unit a workgroup works on: its segment and that segment's metadata.
 struct Unit {
-  int i, first, U, n;
+  int i, first, U, n;      // n: rows planned
   long long sb;
-  float ks, vs;
+  float ka, va;            // absmax of K and V (FP8)
+  int P, cl, cap, kn;      // decode step: state before the append
 };
 
 // Unit k among the segments x0, x0 + xs, x0 + 2xs, ... (in that order, each
-// with units_of(n_i) units).  Wave-level: every wave of a workgroup calls it
-// with the same arguments and gets the same answer.
-template <bool FP8>
+// with units_of(rows) units).  Wave-level: every wave of a workgroup calls it
+// with the same arguments and gets the same answer.  With APP it scans all
+// the segments and returns their unit count in `total`.
+template <bool FP8, bool APP>
 __device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, int k, int lane,
-                                          Unit& un) {
+                                          Unit& un, int& total) {
   int carry = 0;
+  bool found = false;
   for (int base = 0; x0 + xs * base < p.nh; base += 64) {
     const int hi = x0 + xs * (base + lane);
-    int Ui = 0, ni = 0;
+    int Ui = 0, ni = 0, Pi = 0, cli = 0, capi = 0, kni = 0;
     long long sbi = 0;
-    float ka = 1.0f, va = 1.0f;
+    float ka = 0.0f, va = 0.0f;
     if (hi < p.nh) {
-      const int P = p.pos[hi / p.Hkv];
-      const int cap = max(p.seg_cap[hi], 0);
-      const int cl = p.comp_len[hi];
+      Pi = max(p.pos[hi / p.Hkv], 0);
+      capi = max(p.seg_cap[hi], 0);
+      cli = min(max(p.comp_len[hi], 0), capi);
       sbi = p.seg_base[hi];
       if (FP8) {
         ka = p.k_amax[hi];
         va = p.v_amax[hi];
       }
-      ni = min(p.W, max(P, 0)) + min(max(cl, 0), cap);
+      if (APP && p.W == 0) kni = p.keep_new[hi] != 0;
+      ni = APP ? step_rows(p.W, Pi, cli, capi, kni).n_plan : min(p.W, Pi) + cli;
       Ui = units_of(ni, p.tpu);
     }
     int x = Ui;
@@ -183,21 +254,78 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, i
       if (lane >= o) x += y;
     }
     const int ex = carry + x - Ui;
-    const unsigned long long mine = __ballot(hi < p.nh && k >= ex && k < ex + Ui);
+    const unsigned long long mine = __ballot(!found && hi < p.nh && k >= ex && k < ex + Ui);
     if (mine) {
       const int src = __ffsll((long long)mine) - 1;
       un.i = x0 + xs * (base + src);
-      un.first = __shfl(ex, src, 64);
-      un.U = __shfl(Ui, src, 64);
-      un.n = __shfl(ni, src, 64);
-      un.sb = __shfl(sbi, src, 64);
-      un.ks = fp8_scale(__shfl(ka, src, 64));
-      un.vs = fp8_scale(__shfl(va, src, 64));
-      return true;
+      un.first = lane_i(ex, src);
+      un.U = lane_i(Ui, src);
+      un.n = lane_i(ni, src);
+      un.sb = lane_l(sbi, src);
+      un.ka = lane_f(ka, src);
+      un.va = lane_f(va, src);
+      if (APP) {
+        un.P = lane_i(Pi, src);
+        un.cl = lane_i(cli, src);
+        un.cap = lane_i(capi, src);
+        un.kn = lane_i(kni, src);
+      }
+      found = true;
+      if (!APP) return true;
     }
-    carry += __shfl(x, 63, 64);
+    carry += lane_i(x, 63);
   }
-  return false;
+  total = carry;
+  return found;
+}
+
+// Metadata of segment i after the append, from its state before it, with
+// the error bits the append raises (the same rules as the APPEND operation
+// of kv_compact).
+struct StepMeta {
+  int cl_new;      // comp_len after the append
+  int slot;        // ring row written (W > 0), else -1
+  int kn;          // keep bit stored for that ring row
+  int errbits;
+};
+__device__ __forceinline__ StepMeta step_meta(const AttnParams& p, int64_t i) {
+  StepMeta s;
+  const int P = max(p.pos[i / p.Hkv], 0);
+  const int cap = max(p.seg_cap[i], 0);
+  const int cl = min(max(p.comp_len[i], 0), cap);
+  const int64_t sb = p.seg_base[i];
+  const int kn = p.keep_new[i] != 0;
+  const int W = p.W;
+  s.cl_new = cl;
+  s.slot = -1;
+  s.kn = kn;
+  s.errbits = 0;
+  if (W > 0) {
+    s.slot = P % W;
+    const int rk = P >= W ? p.ring_keep[i * W + s.slot] : 0;
+    if (rk) {
+      if (cl < cap) {
+        if (sb + s.slot >= p.pool_rows || sb + W + cl >= p.pool_rows) s.errbits |= CDA_DEVERR_POOL;
+        s.cl_new = cl + 1;
+      } else {
+        s.errbits |= CDA_DEVERR_CAPACITY;
+      }
+    }
+    if (sb + s.slot >= p.pool_rows) s.errbits |= CDA_DEVERR_POOL;
+  } else if (kn) {
+    if (cl < cap) {
+      if (sb + cl >= p.pool_rows) s.errbits |= CDA_DEVERR_POOL;
+      s.cl_new = cl + 1;
+    } else {
+      s.errbits |= CDA_DEVERR_CAPACITY;
+    }
+  }
+  return s;
+}
+__device__ __forceinline__ void commit_meta(const AttnParams& p, int64_t i, const StepMeta& s) {
+  p.comp_len[i] = s.cl_new;
+  if (s.slot >= 0) p.ring_keep[i * p.W + s.slot] = (uint8_t)s.kn;
+  if (s.errbits) atomicOr(p.err, s.errbits);
 }
 
 // Mask of the bytes of dword w (bytes 4w .. 4w+3) that lie below `lim`.
@@ -206,18 +334,21 @@ __device__ __forceinline__ uint32_t bytes_below(int lim, int w) {
   return k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
 }
 
-template <bool FP8, int D, bool XL, int NW>
+template <bool FP8, int D, bool XL, int NW, bool APP>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   constexpr int NTH = 64 * NW;              // threads of the workgroup
   constexpr int E = FP8 ? 1 : 2;            // bytes per stored element
+  constexpr int RB = D * E;                 // bytes per row
   constexpr int NK = D / 32;                // MFMA k-steps of q.K
   constexpr int NT = D / 16;                // 16-wide d tiles of the output
   constexpr int KL = FP8 ? D / 64 : D / 32; // 16-byte K loads per (lane, token group)
   constexpr int VL = FP8 ? 1 : 2;           // 16-byte V loads per (lane, d tile)
+  constexpr int EPL = D / 64;               // new-token elements per lane
 
-  __shared__ int s_last;
+  __shared__ int s_last, s_lastg;
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ f32x4 s_o[NW][16][D / 4];
+  __shared__ f32x4 s_new[APP ? D / 2 : 1];  // decoded new token: K values, then V values
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 15, kg = lane >> 4;
@@ -229,18 +360,72 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     if (xcc != w % p.nxcc) atomicOr(p.err, CDA_DEVERR_XCD);
   }
 
+  // Decode step: this workgroup's count-in on the grid counter (tid 0), and
+  // the new metadata of segment `lane`, prepared by wave 0 into LDS when
+  // nh <= 64.
+  __shared__ StepMeta s_meta[APP ? 64 : 1];
+  bool counted = false;
+  int gprev = -1;
+  const bool meta_fast = p.nh <= 64;
+  auto count_in = [&]() {
+    if (APP && !counted) {
+      counted = true;
+      if (meta_fast && wave == 0 && lane < p.nh) {
+        s_meta[lane] = step_meta(p, lane);
+        // the values have been read before the count-in is issued
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      if (tid == 0)
+        gprev = __hip_atomic_fetch_add(p.gcount, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
   for (int k = XL ? (w / kXcdGroups) : w;; k += p.per_xcd) {
     Unit un;
-    if (!find_unit<FP8>(p, grp, XL ? kXcdGroups : 1, k, lane, un)) return;
-    const int i = un.i, U = un.U, n = un.n;
+    int total = 0;
+    if (!find_unit<FP8, APP>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
+    // decode step: whether this is the workgroup's last unit (its group has
+    // `total` units; workgroups take every per_xcd-th of them)
+    const bool last_unit = APP && (!XL || k + p.per_xcd >= total);
+    const int i = un.i, U = un.U;
     const int b = i / p.Hkv, h = i - b * p.Hkv;
     const int G = p.G;
     const int64_t sb = un.sb;
     const int64_t in_pool = p.pool_rows - sb;
-    const int ntiles = (n + kTile - 1) / kTile;
+    const int ntiles = (un.n + kTile - 1) / kTile;
     const int t_begin = (k - un.first) * p.tpu;
     const int t_end = min(t_begin + p.tpu, ntiles);
     const int slot = XL ? k * kXcdGroups + grp : k;   // this unit's partial
+    const float ks = FP8 ? fp8_scale(un.ka) : 1.0f;
+    const float vs = FP8 ? fp8_scale(un.va) : 1.0f;
+
+    // ---- decode step: rows with data, the new token's row and its tile
+    int n = un.n, new_row = -1, t_own = -1;
+    if (APP) {
+      const StepRows st = step_rows(p.W, un.P, un.cl, un.cap, un.kn);
+      n = st.n_pre;
+      if (st.new_row >= 0 && st.new_row < in_pool) {
+        new_row = st.new_row;
+        t_own = new_row / kTile;
+      }
+    }
+    const bool owner = APP && t_own >= t_begin && t_own < t_end && (t_own - t_begin) % NW == wave;
+    // owner wave: the leaving token's keep bit and its slice of the new token
+    bool leaving = false, moved = false;
+    uint32_t nk = 0, nv = 0;
+    if (owner) {
+      leaving = p.W > 0 && un.P >= p.W;
+      const int rk = leaving ? p.ring_keep[(int64_t)i * p.W + new_row] : 0;
+      moved = rk && un.cl < un.cap && sb + p.W + un.cl < p.pool_rows;
+      const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
+      if (EPL == 2) {
+        nk = *reinterpret_cast<const uint32_t*>(p.k_new + off);
+        nv = *reinterpret_cast<const uint32_t*>(p.v_new + off);
+      } else {
+        nk = p.k_new[off];
+        nv = p.v_new[off];
+      }
+    }
 
     // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per k-step
     bf16x8 qop[NK];
@@ -254,7 +439,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         qop[s] = as_bf16x8(v);
       }
     }
-    const float c1 = p.sm_scale * kLog2e * (FP8 ? un.ks : 1.0f);
+    const float c1 = p.sm_scale * kLog2e * ks;
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x4 acc[NT];
@@ -265,141 +450,259 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     for (int t = t_begin + wave; t < t_end; t += NW) {
       const int r0 = t * kTile;
       const int valid = (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
-      if (valid <= 0) break;
-      const bool full = valid == kTile;
-      const uint8_t* ktile = p.k_pool + (sb + r0) * (int64_t)(D * E);
-      const uint8_t* vtile = p.v_pool + (sb + r0) * (int64_t)(D * E);
+      const bool own = APP && t == t_own;
+      if (valid <= 0 && !own) break;
+      if (valid > 0) {
+        const bool full = valid == kTile;
+        // the leaving token's row is masked unless it moves to the compact tail
+        const int mrow = (own && leaving && !moved) ? (new_row & (kTile - 1)) : -1;
+        const uint8_t* ktile = p.k_pool + (sb + r0) * (int64_t)RB;
+        const uint8_t* vtile = p.v_pool + (sb + r0) * (int64_t)RB;
 
-      // -- loads: K rows for the 4 token groups (each instruction 1 KB of the
-      //    permuted K tile), V columns for the NT d tiles
-      u32x4 kr[4][KL];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int j = 0; j < KL; ++j)
-          kr[m][j] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16));
-      u32x4 vr[NT][VL];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < VL; ++j)
-          vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
-
-      // -- S^T = K . Q^T, 16 tokens per MFMA row block
-      f32x4 s[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        s[m] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int st = 0; st < NK; ++st) {
-          bf16x8 a;
-          if (FP8) {
-            const u32x4 v = kr[m][st >> 1];
-            a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
-          } else {
-            a = as_bf16x8(kr[m][st]);
-          }
-          s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], s[m], 0, 0, 0);
-        }
-      }
-
-      // -- online softmax over this tile; lane (g, kg) owns tokens 16kg + 4m + r
-      float z[4][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[m][r] = s[m][r] * c1;
-      if (!full) {
+        // -- loads: K rows for the 4 token groups (each instruction 1 KB of the
+        //    permuted K tile), V columns for the NT d tiles
+        u32x4 kr[4][KL];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (16 * kg + 4 * m + r >= valid) z[m][r] = -INFINITY;
-      }
+          for (int j = 0; j < KL; ++j)
+            kr[m][j] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16));
+        u32x4 vr[NT][VL];
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, z[m][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      if (!first_tile) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
-      }
-      float psum = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_new);
-          psum += z[m][r];
-        }
-      l_run += psum;
-      m_run = m_new;
+          for (int j = 0; j < VL; ++j)
+            vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
 
-      // -- rows past the segment end: zero their V bytes (P is 0 there, but
-      //    the bytes may not be finite values)
-      if (!full) {
+        // -- decode step, owner wave: copy the leaving token's row from the
+        //    registers of this tile to the compact tail (segment row W + cl).
+        //    Stores are predicated per register so that no array is indexed
+        //    at run time.
+        if (own && moved) {
+          const int to = p.W + un.cl, rt = to & (kTile - 1);
+          uint8_t* kt = p.k_pool + (sb + (to - rt)) * (int64_t)RB;
+          uint8_t* vt = p.v_pool + (sb + (to - rt)) * (int64_t)RB;
+          const int rs = new_row & (kTile - 1);
+          const int m_r = (rs >> 2) & 3, g_r = ((rs >> 4) << 2) | (rs & 3);
 #pragma unroll
-        for (int j = 0; j < VL; ++j) {
-          const int lim = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;  // valid bytes
+          for (int m = 0; m < 4; ++m)   // lane kg holds chunks kg + 4j of row rs
+            if (m == m_r && g == g_r) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t msk = bytes_below(lim, q);
+              for (int j = 0; j < KL; ++j)
+                *reinterpret_cast<u32x4*>(kt + k_chunk_offset(rt, kg + 4 * j, RB)) = kr[m][j];
+            }
+          if (kg == (rs >> 4)) {        // lane g holds column 16nt + g of rows 16kg..16kg+15
+            const int jv = VL == 1 ? 0 : (rs & 15) >> 3;          // which 16-byte load
+            const int bi = (rs & (16 / VL - 1)) * E;              // byte inside it
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) vr[nt][j][q] &= msk;
+            for (int j = 0; j < VL; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (j == jv && q == (bi >> 2)) {
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) {
+                    const uint32_t wd = vr[nt][j][q] >> (8 * (bi & 3));
+                    const int64_t o = (int64_t)((16 * nt + g) * kTile + rt) * E;
+                    if (FP8)
+                      vt[o] = (uint8_t)wd;
+                    else
+                      *reinterpret_cast<uint16_t*>(vt + o) = (uint16_t)wd;
+                  }
+                }
           }
         }
+
+        // -- S^T = K . Q^T, 16 tokens per MFMA row block
+        f32x4 s[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s[m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int st = 0; st < NK; ++st) {
+            bf16x8 a;
+            if (FP8) {
+              const u32x4 v = kr[m][st >> 1];
+              a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
+            } else {
+              a = as_bf16x8(kr[m][st]);
+            }
+            s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], s[m], 0, 0, 0);
+          }
+        }
+
+        // -- online softmax over this tile; lane (g, kg) owns tokens 16kg + 4m + r
+        float z[4][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) z[m][r] = s[m][r] * c1;
+        if (!full || mrow >= 0) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int tok = 16 * kg + 4 * m + r;
+              if (tok >= valid || tok == mrow) z[m][r] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, z[m][r]);
+        tmax = max_xor32(max_xor16(tmax));
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // every logit masked so far
+        if (!first_tile) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+          l_run *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+        }
+        float psum = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
+            psum += z[m][r];
+          }
+        l_run += psum;
+        m_run = m_new;
+
+        // -- rows past the segment end: zero their V bytes (P is 0 there, but
+        //    the bytes may not be finite values)
+        if (!full) {
+#pragma unroll
+          for (int j = 0; j < VL; ++j) {
+            const int lim = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;  // valid bytes
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t msk = bytes_below(lim, q);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) vr[nt][j][q] &= msk;
+            }
+          }
+        }
+
+        // -- O^T += V^T . P^T, per d tile one MFMA (FP8) or two (BF16: hi, lo)
+        //    per 8 tokens of each lane
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (FP8) {
+            f16x8 pf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[e] = (_Float16)z[2 * hh + (e >> 2)][e & 3];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const u32x4 v = vr[nt][0];
+              const f16x8 a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, acc[nt], 0, 0, 0);
+            }
+          } else {
+            bf16x8 phi, plo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pv = z[2 * hh + (e >> 2)][e & 3];
+              const __bf16 hi = (__bf16)pv;
+              phi[e] = hi;
+              plo[e] = (__bf16)(pv - (float)hi);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const bf16x8 a = as_bf16x8(vr[nt][hh]);
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[nt], 0, 0, 0);
+              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[nt], 0, 0, 0);
+            }
+          }
+        }
+        first_tile = false;
+
       }
 
-      // -- O^T += V^T . P^T, two MFMAs (8 tokens per lane each) per d tile
+      // -- decode step, owner wave: the new token's (logit, value) pair joins
+      //    the running softmax state, then its row is written
+      if (own) {
+        const int d0n = EPL * lane;
+        float kd[EPL], vd[EPL];
+        uint32_t kc = 0, vc = 0;   // stored bytes of this lane's elements
+        const float kinv = FP8 ? fp8_inv_scale(un.ka) : 1.0f;
+        const float vinv = FP8 ? fp8_inv_scale(un.va) : 1.0f;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        if (FP8) {
-          f16x8 phi, plo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = z[2 * hh + (e >> 2)][e & 3];
-            const _Float16 hi = (_Float16)pv;
-            phi[e] = hi;
-            plo[e] = (_Float16)(pv - (float)hi);
-          }
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const u32x4 v = vr[nt][0];
-            const f16x8 a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, phi, acc[nt], 0, 0, 0);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, plo, acc[nt], 0, 0, 0);
-          }
-        } else {
-          bf16x8 phi, plo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = z[2 * hh + (e >> 2)][e & 3];
-            const __bf16 hi = (__bf16)pv;
-            phi[e] = hi;
-            plo[e] = (__bf16)(pv - (float)hi);
-          }
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const bf16x8 a = as_bf16x8(vr[nt][hh]);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[nt], 0, 0, 0);
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[nt], 0, 0, 0);
+        for (int e = 0; e < EPL; ++e) {
+          const uint32_t kb = (nk >> (16 * e)) & 0xFFFFu, vb = (nv >> (16 * e)) & 0xFFFFu;
+          if (FP8) {
+            const uint32_t kq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv));
+            const uint32_t vq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+            kd[e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kq, 1.0f, false)[0];
+            vd[e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vq, 1.0f, false)[0];
+            kc |= kq << (8 * e);
+            vc |= vq << (8 * e);
+          } else {
+            kd[e] = bf16_bits_to_f32(kb);
+            vd[e] = bf16_bits_to_f32(vb);
+            kc |= kb << (16 * e);
+            vc |= vb << (16 * e);
           }
         }
+        float* sn = reinterpret_cast<float*>(s_new);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          sn[d0n + e] = kd[e];
+          sn[D + d0n + e] = vd[e];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float dot = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
+          const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dot = fmaf((float)qop[s][e], a[e], dot);
+            dot = fmaf((float)qop[s][4 + e], c[e], dot);
+          }
+        }
+        dot = sum_xor32(sum_xor16(dot));
+        const float zn = dot * c1;
+        const float m_new = fmaxf(m_run, zn);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const float pn = __builtin_amdgcn_exp2f(zn - m_use);
+        l_run = l_run * alpha + (kg == 0 ? pn : 0.0f);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = acc[nt] * alpha + pn * s_new[D / 4 + 4 * nt + kg];
+        m_run = m_new;
+        first_tile = false;
+
+        // every load of this wave (the ring row included) has completed
+        __builtin_amdgcn_s_waitcnt(0);
+        const int rn = new_row & (kTile - 1);
+        uint8_t* kt = p.k_pool + (sb + (new_row - rn)) * (int64_t)RB;
+        uint8_t* vt = p.v_pool + (sb + (new_row - rn)) * (int64_t)RB;
+        const int kb0 = d0n * E;   // byte of this lane's first element in the row
+        uint8_t* kdst = kt + k_chunk_offset(rn, kb0 >> 4, RB) + (kb0 & 15);
+        if (EPL * E == 4)
+          *reinterpret_cast<uint32_t*>(kdst) = kc;
+        else if (EPL * E == 2)
+          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
+        else
+          *kdst = (uint8_t)kc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (FP8)
+            vt[(d0n + e) * kTile + rn] = (uint8_t)(vc >> (8 * e));
+          else
+            reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rn] = (uint16_t)(vc >> (16 * e));
+        }
       }
-      first_tile = false;
     }
 
-    // ---- combine the 4 waves of the workgroup
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
+    // ---- combine the waves of the workgroup
+    l_run = sum_xor32(sum_xor16(l_run));
     if (kg == 0) {
       s_m[wave][g] = m_run;
       s_l[wave][g] = l_run;
@@ -407,8 +710,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
     __syncthreads();
+    if (last_unit) count_in();   // every wave is past its plan and its owner reads
 
-    const float sv = FP8 ? un.vs : 1.0f;
+    const float sv = vs;
     for (int e = tid; e < G * (D / 4); e += NTH) {     // (query row, 4 consecutive d)
       const int gg = e / (D / 4), d4 = e - gg * (D / 4);
       float M = -INFINITY;
@@ -487,8 +791,33 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         }
       }
     }
-    if (!XL) return;
+    // after its last unit a workgroup plans nothing more: with the decode
+    // step, the metadata may already have changed
+    if (!XL || last_unit) break;
     __syncthreads();   // the LDS of this unit is reused by the next one
+  }
+
+  if (APP) {
+    // ---- decode step: the last workgroup to count itself in writes the
+    // new metadata (every other workgroup is done reading it)
+    count_in();
+    if (tid == 0) {
+      const bool last = gprev == (int)gridDim.x - 1;
+      s_lastg = last;
+      if (last) __hip_atomic_store(p.gcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (s_lastg) {
+      const int B = p.nh / p.Hkv;
+      if (meta_fast) {
+        if (wave == 0 && lane < p.nh) commit_meta(p, lane, s_meta[lane]);
+        __syncthreads();
+      } else {
+        for (int i = tid; i < p.nh; i += NTH) commit_meta(p, i, step_meta(p, i));
+        __syncthreads();   // every pos[b] has been read
+      }
+      for (int bb = tid; bb < B; bb += NTH) p.pos[bb] = max(p.pos[bb], 0) + 1;
+    }
   }
 }
 
@@ -502,6 +831,27 @@ int device_xcds() {
   return nx;
 }
 
+template <bool APP>
+void launch_variant(bool fp8, int D, bool xl, int nw, dim3 grid, hipStream_t s, const AttnParams& p) {
+#define CDA_LAUNCH_ATTN(F, DD, X)                                                      \
+  (nw == 8 ? attn_kernel<F, DD, X, 8, APP><<<grid, 512, 0, s>>>(p)                     \
+           : attn_kernel<F, DD, X, 4, APP><<<grid, 256, 0, s>>>(p))
+  if (fp8) {
+    if (D == 64) {
+      if (xl) CDA_LAUNCH_ATTN(true, 64, true); else CDA_LAUNCH_ATTN(true, 64, false);
+    } else {
+      if (xl) CDA_LAUNCH_ATTN(true, 128, true); else CDA_LAUNCH_ATTN(true, 128, false);
+    }
+  } else {
+    if (D == 64) {
+      if (xl) CDA_LAUNCH_ATTN(false, 64, true); else CDA_LAUNCH_ATTN(false, 64, false);
+    } else {
+      if (xl) CDA_LAUNCH_ATTN(false, 128, true); else CDA_LAUNCH_ATTN(false, 128, false);
+    }
+  }
+#undef CDA_LAUNCH_ATTN
+}
+
 }  // namespace
 
 int64_t attn_max_units(const cda_kv_cache& c, int tpu) {
@@ -509,25 +859,27 @@ int64_t attn_max_units(const cda_kv_cache& c, int tpu) {
   return nh + c.pool_rows / ((int64_t)kTile * tpu);
 }
 
+// Workspace: [grid counter][per-segment counters][partial (m, l)][partial o].
 // Partial slots: an XCD-local slot is 8k + group with k below the units of
 // the group (at most all units), so 8 x the unit bound covers both modes.
 size_t attn_workspace_bytes(const cda_kv_cache& c, int G, int tpu) {
   const int64_t slots = kXcdGroups * attn_max_units(c, tpu);
   const int64_t nh = (int64_t)c.B * c.Hkv;
-  return align256((size_t)nh * 4) + align256((size_t)slots * G * 2 * 4) +
+  return 256 + align256((size_t)nh * 4) + align256((size_t)slots * G * 2 * 4) +
          align256((size_t)slots * G * c.D * 4);
 }
 
 hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_scale, void* out,
-                       int out_f32, float* lse, int tpu, void* workspace, hipStream_t s) {
+                       int out_f32, float* lse, int tpu, void* workspace, hipStream_t s,
+                       const cda_compact_args* step) {
   const int nh = c.B * c.Hkv;
   if (nh == 0) return hipGetLastError();
   const int G = Hq / c.Hkv;
   const int64_t units = attn_max_units(c, tpu);
   const int64_t slots = kXcdGroups * units;
   AttnParams p;
-  p.k_pool = static_cast<const uint8_t*>(c.k_pool);
-  p.v_pool = static_cast<const uint8_t*>(c.v_pool);
+  p.k_pool = static_cast<uint8_t*>(c.k_pool);
+  p.v_pool = static_cast<uint8_t*>(c.v_pool);
   p.pool_rows = c.pool_rows;
   p.seg_base = c.seg_base;
   p.seg_cap = c.seg_cap;
@@ -539,13 +891,20 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.out = out;
   p.lse = lse;
   p.err = c.err;
-  // workspace: [sem: nh int32][part_ml: slots*G*2 f32][part_o: slots*G*D f32]
   char* ws = static_cast<char*>(workspace);
+  p.gcount = reinterpret_cast<int32_t*>(ws);
+  ws += 256;
   p.sem = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)nh * 4);
   p.part_ml = reinterpret_cast<float*>(ws);
   ws += align256((size_t)slots * G * 2 * 4);
   p.part_o = reinterpret_cast<float*>(ws);
+  p.ring_keep = c.ring_keep;
+  p.k_new = step ? static_cast<const uint16_t*>(step->k) : nullptr;
+  p.v_new = step ? static_cast<const uint16_t*>(step->v) : nullptr;
+  p.new_sb = step ? step->stride_b : 0;
+  p.new_sh = step ? step->stride_h : 0;
+  p.keep_new = step ? step->keep : nullptr;
   p.Hkv = c.Hkv;
   p.G = G;
   p.Hq = Hq;
@@ -563,23 +922,10 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   const dim3 grid((unsigned)(xl ? (int64_t)p.per_xcd * kXcdGroups : units));
   const bool fp8 = c.kv_dtype == CDA_KV_FP8_E4M3;
   const int nw = tpu >= 8 ? 8 : 4;   // waves per workgroup: one tile each per pass
-#define CDA_LAUNCH_ATTN(F, DD, X)                                                   \
-  (nw == 8 ? attn_kernel<F, DD, X, 8><<<grid, 512, 0, s>>>(p)                       \
-           : attn_kernel<F, DD, X, 4><<<grid, 256, 0, s>>>(p))
-  if (fp8) {
-    if (c.D == 64) {
-      if (xl) CDA_LAUNCH_ATTN(true, 64, true); else CDA_LAUNCH_ATTN(true, 64, false);
-    } else {
-      if (xl) CDA_LAUNCH_ATTN(true, 128, true); else CDA_LAUNCH_ATTN(true, 128, false);
-    }
-  } else {
-    if (c.D == 64) {
-      if (xl) CDA_LAUNCH_ATTN(false, 64, true); else CDA_LAUNCH_ATTN(false, 64, false);
-    } else {
-      if (xl) CDA_LAUNCH_ATTN(false, 128, true); else CDA_LAUNCH_ATTN(false, 128, false);
-    }
-  }
-#undef CDA_LAUNCH_ATTN
+  if (step)
+    launch_variant<true>(fp8, c.D, xl, nw, grid, s, p);
+  else
+    launch_variant<false>(fp8, c.D, xl, nw, grid, s, p);
   return hipGetLastError();
 }
 

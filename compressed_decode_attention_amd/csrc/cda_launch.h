@@ -18,8 +18,10 @@ hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipSt
 // workgroups it launches (one per unit) for this cache and split.
 int64_t attn_max_units(const cda_kv_cache& c, int tiles_per_unit);
 size_t attn_workspace_bytes(const cda_kv_cache& c, int G, int tiles_per_unit);
+// step == NULL: attention only; otherwise the APPEND arguments of the new
+// token, appended in the same launch (decode step).
 hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_scale,
                        void* out, int out_f32, float* lse, int tiles_per_unit,
-                       void* workspace, hipStream_t s);
+                       void* workspace, hipStream_t s, const cda_compact_args* step);
 
 }  // namespace cda

@@ -178,8 +178,8 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  *   The call reads the device's XCD count (hipDeviceGetAttribute) on the
  *   current device; the attention may set CDA_DEVERR_XCD in cache->err.
  *   workspace    device scratch of at least cda_attn_workspace_bytes()
- *                bytes: one completion counter per segment, then the
- *                partial states of split segments.  It must be zero-filled
+ *                bytes: a grid counter and one completion counter per
+ *                segment, then the partial states of split segments.  It must be zero-filled
  *                before its first use; every completed call leaves the
  *                counters at zero again, so one workspace can serve any
  *                later call (any cache, any split) ordered after it on a
@@ -191,7 +191,31 @@ int32_t decode_attn_compact(const cda_kv_cache *cache, const void *q, int32_t Hq
                             int32_t split_tokens, void *workspace,
                             size_t workspace_bytes, void *stream);
 
-/* Workspace bytes decode_attn_compact needs for this cache, Hq and split. */
+/*
+ * decode_step_compact -- one decode step of one layer in a single launch:
+ * the APPEND operation of kv_compact followed by decode_attn_compact over
+ * the appended store (FastDMS memory-table paragraph, "cache + staging",
+ * for the append; decode over the compact store as above).
+ *
+ *   args         the APPEND arguments of kv_compact (op must be
+ *                CDA_OP_APPEND): the new token's BF16 K and V rows and its
+ *                keep byte per (sequence, KV head)
+ *   other arguments as for decode_attn_compact, with the same workspace.
+ *
+ * Afterwards the cache (pools, comp_len, ring_keep, pos, err) is bit for bit
+ * what kv_compact(APPEND) leaves, and out / lse are the attention of q over
+ * the stored rows after the append.  The attention is computed from the
+ * rows as they were before the append plus the new token in registers, so
+ * the kernel never reads a row that the append writes in the same launch.
+ * Errors as for the two calls it replaces.
+ */
+int32_t decode_step_compact(const cda_kv_cache *cache, const cda_compact_args *args,
+                            const void *q, int32_t Hq, float sm_scale, void *out,
+                            int32_t out_dtype, float *lse, int32_t split_tokens,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes decode_attn_compact and decode_step_compact need for this
+ * cache, Hq and split. */
 size_t cda_attn_workspace_bytes(const cda_kv_cache *cache, int32_t Hq, int32_t split_tokens);
 
 /* Static text for a cda_status value. */

@@ -85,9 +85,11 @@ def compare_state(c: CompactKVCache, o: oracle.OracleCache, what: str = ""):
 def check_close(got, ref, what="", atol=ATOL, rtol=RTOL):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
-    err = np.abs(got - ref)
+    same = got == ref                       # equal infinities (lse of an empty set)
+    with np.errstate(invalid="ignore"):
+        err = np.where(same, 0.0, np.abs(got - ref))
     bound = atol + rtol * np.abs(ref)
-    bad = ~(err <= bound)
+    bad = ~(same | (err <= bound))
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; "

@@ -113,3 +113,28 @@ def test_attention_validation(lib):
     # a bigger split never needs more workspace
     assert L.cda_attn_workspace_bytes(C.byref(c), 8, 4096) <= need
     assert L.cda_attn_workspace_bytes(C.byref(c), 7, 0) == 0
+
+
+def test_decode_step_validation(lib):
+    L = lib.load()
+    c = _cache(lib)
+    q = out = ws = C.c_void_p(0x100000)
+    need = L.cda_attn_workspace_bytes(C.byref(c), 8, 0)
+    a = lib.CdaCompactArgs()
+    a.op, a.keep, a.k, a.v = lib.CDA_OP_APPEND, 0x100000, 0x100000, 0x100000
+    a.stride_b, a.stride_h = 128, 64
+    f = L.decode_step_compact
+    # attention checks come first, as for decode_attn_compact
+    assert f(C.byref(c), C.byref(a), q, 7, 0.0, out, 0, None, 0, ws, need, None) == 2
+    assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need - 1, None) == 3
+    assert f(None, C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    # then the APPEND arguments
+    assert f(C.byref(c), None, q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    a.op = lib.CDA_OP_PACK
+    assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    a.op, a.keep = lib.CDA_OP_APPEND, 0
+    assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    a.keep, a.k = 0x100000, 0x100008                                   # misaligned k
+    assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+    a.k, a.stride_h = 0x100000, 12                                     # stride not a multiple of 8
+    assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1

@@ -2,7 +2,9 @@
 Llama-3.2-1B and Qwen3-8B attention shapes, plus the tiny case), in the
 launch configuration the benchmark times: prefill compaction of a layer
 bit-exact, all 128 decode appends bit-exact, and the attention output of
-every query head at several decode steps against the oracle."""
+every query head at several decode steps against the oracle.  Each decode
+step runs either as one decode_step_compact launch (what the benchmark
+times) or as kv_compact APPEND followed by decode_attn_compact."""
 import numpy as np
 import pytest
 import torch
@@ -16,11 +18,12 @@ pytestmark = pytest.mark.gpu
 RESERVE_EXTRA = 0   # the benchmark reserves exactly gen_len rows per segment
 
 
+@pytest.mark.parametrize("mode", ["step", "append"])
 @pytest.mark.parametrize("name,layer", [("tiny", 0), ("llama_c1", 3), ("llama_c8", 0),
                                         ("qwen_c1", 35), ("qwen_c8", 0)])
-def test_config_layer(name, layer):
+def test_config_layer(name, layer, mode):
     cfg = workload.CONFIGS[name]
-    log(f"config {name} layer {layer}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} "
+    log(f"config {name} layer {layer} ({mode}): B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} "
         f"T={cfg.T} S={cfg.S} W={cfg.W} {cfg.kv_dtype}")
     lay = workload.make_layer(cfg, layer)
     T, S, W = cfg.T, cfg.S, cfg.W
@@ -35,9 +38,13 @@ def test_config_layer(name, layer):
     check_steps = {0, S // 2, S - 1}
     worst = 0.0
     for s in range(S):
-        c.append(kd[:, T + s], vd[:, T + s], keep_new[s])
+        if mode == "step":
+            out = c.decode_step(kd[:, T + s], vd[:, T + s], keep_new[s], qd[s],
+                                out_dtype=torch.float32)
+        else:
+            c.append(kd[:, T + s], vd[:, T + s], keep_new[s])
+            out = c.attention(qd[s], out_dtype=torch.float32)
         o.append(lay.k[:, T + s], lay.v[:, T + s], lay.keep[:, :, T + s])
-        out = c.attention(qd[s], out_dtype=torch.float32)
         if s in check_steps:
             torch.cuda.synchronize()
             ref, _ = oracle.attention(lay.q[s], lay.k, lay.v, lay.keep, T + s, W,
