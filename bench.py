@@ -9,15 +9,20 @@ memory-table row, on synthetic inputs (no weights, no dataset).
 One step = one pass of the whole path over the batch, everything already
 resident in HBM:
   prefill compaction of every layer (kv_compact COUNT + PACK), then
-  128 decode steps x 36 layers of kv_compact APPEND + decode_attn_compact,
+  128 decode steps x 36 layers of decode_step_compact (the append of the
+  new token and the attention over the compact store, one launch each),
 all enqueued on one stream with no host synchronisation inside the step.
+The prefill and the decode launches are captured once into two HIP graphs
+(no memset or allocation inside; every replay starts from COUNT, so it
+redoes the same work) and replayed each step; --eager issues every call
+from Python instead, --unfused uses kv_compact APPEND + decode_attn_compact.
 
 Reported: value = decode-attention KV bytes moved per second over the whole
 step (algorithmic bytes: every stored row's K and V read once per decode
 step and layer, divided by the step's wall time); the roofline of the
-attention kernel, its per-launch duration measured with HIP events on its
-stream around back-to-back launches over all layers right after the timed
-steps; the CPU oracle timed on a bounded sample; and parity of that sample.
+decode-step kernel, its per-launch duration measured with HIP events on its
+stream around the decode part of each timed step; the CPU oracle timed on a
+bounded sample; and parity of that sample.
 """
 from __future__ import annotations
 
@@ -114,6 +119,9 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="0 = all layers of the config")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="issue every call from Python (no graphs)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode steps as kv_compact APPEND + decode_attn_compact")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 64 MiB device copy 3 times (the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -168,69 +176,92 @@ def main():
                            for s in range(S)], np.float64)          # [S, L]
     step_attn_bytes = float(attn_bytes.sum())
 
-    stream = torch.cuda.current_stream(dev)
-
-    def run_step():
+    def prefill_all():
         for l in range(L):
             c = caches[l]
             c.count(keepd[l], T, reserve=S)
             c.pack(kd[l], vd[l], keepd[l], T)
+
+    def decode_all():
         for s in range(S):
             for l in range(L):
                 c = caches[l]
-                c.append(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s])
-                c.attention(qd[l][s], out=outs[l], split_tokens=args.split)
+                if args.unfused:
+                    c.append(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s])
+                    c.attention(qd[l][s], out=outs[l], split_tokens=args.split)
+                else:
+                    c.decode_step(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s], qd[l][s],
+                                  out=outs[l], split_tokens=args.split)
+
+    # one eager pass first: loads the library, sizes the workspaces
+    prefill_all()
+    decode_all()
+    torch.cuda.synchronize()
+    graphs = None
+    if not args.eager:
+        g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pre):
+            prefill_all()
+        with torch.cuda.graph(g_dec):
+            decode_all()
+        torch.cuda.synchronize()
+        graphs = (g_pre, g_dec)
+        log(f"captured {2 * L} prefill and {S * L * (2 if args.unfused else 1)} decode launches "
+            f"in two graphs")
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def run_step():
+        ev[0].record(stream)
+        if graphs:
+            graphs[0].replay()
+        else:
+            prefill_all()
+        ev[1].record(stream)
+        if graphs:
+            graphs[1].replay()
+        else:
+            decode_all()
+        ev[2].record(stream)
 
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    for c in caches:
-        if c.error_word() != 0:
-            raise RuntimeError("device error word set during warm-up")
+    words = [c.error_word() for c in caches]
+    if any(words):
+        raise RuntimeError(f"device error words set during warm-up: {words} "
+                           f"(1 capacity, 2 pool, 4 workgroup-to-XCD mapping)")
     log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
 
-    step_ms = []
+    step_ms, prefill_ms_l, decode_ms_l = [], [], []
     for k in range(args.steps):
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         run_step()
         torch.cuda.synchronize()
         step_ms.append((time.perf_counter() - t_start) * 1e3)
-        log(f"step {k}: {step_ms[-1]:.2f} ms")
+        prefill_ms_l.append(ev[0].elapsed_time(ev[1]))
+        decode_ms_l.append(ev[1].elapsed_time(ev[2]))
+        log(f"step {k}: {step_ms[-1]:.2f} ms (prefill {prefill_ms_l[-1]:.2f} ms, "
+            f"decode {decode_ms_l[-1]:.2f} ms)")
 
     # the device state after the last step must match the host accounting
     for l in range(L):
         got = caches[l].stored_rows().cpu().numpy().reshape(B, Hkv)
         if not np.array_equal(got, nrows[l][S - 1]):
             raise RuntimeError(f"layer {l}: device stored-row counts differ from the keep mask")
+        if caches[l].error_word() != 0:
+            raise RuntimeError(f"layer {l}: device error word set")
 
-    # Per-launch duration of the attention kernel: HIP events on the kernel's
-    # stream around back-to-back launches over all layers, at the decode
-    # state the timed steps ended in (last step).  One event pair per layer
-    # sweep, so event overhead does not land inside the average.
-    reps = 5
-    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for l in range(L):
-        caches[l].attention(qd[l][S - 1], out=outs[l], split_tokens=args.split)
-    ev_a.record(stream)
-    for _ in range(reps):
-        for l in range(L):
-            caches[l].attention(qd[l][S - 1], out=outs[l], split_tokens=args.split)
-    ev_b.record(stream)
-    torch.cuda.synchronize()
-    kernel_us = ev_a.elapsed_time(ev_b) * 1e3 / (reps * L)
-    bytes_per_launch = float(attn_bytes[S - 1].mean())
-
-    # prefill compaction alone (COUNT + PACK of every layer), for the split
-    # of the step time; this leaves the caches in their prefill state
-    ev_a.record(stream)
-    for _ in range(reps):
-        for l in range(L):
-            caches[l].count(keepd[l], T, reserve=S)
-            caches[l].pack(kd[l], vd[l], keepd[l], T)
-    ev_b.record(stream)
-    torch.cuda.synchronize()
-    prefill_ms = ev_a.elapsed_time(ev_b) / reps
+    # Per-launch duration of the decode-step kernel: the decode part of each
+    # timed step (S x L back-to-back launches on this stream, between two HIP
+    # events, gaps between launches included) divided by the launches; the
+    # algorithmic bytes per launch are the mean over the same launches.  With
+    # --unfused this is the time of one layer step (APPEND + attention).
+    kernel_us = float(np.mean(decode_ms_l)) * 1e3 / (S * L)
+    bytes_per_launch = float(attn_bytes.mean())
+    prefill_ms = float(np.mean(prefill_ms_l))
 
     ms = float(np.mean(step_ms))
     value = step_attn_bytes / (ms * 1e-3) / 1e9
@@ -264,9 +295,11 @@ def main():
                    "parallelism": "single GPU"},
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "attn_kernel_us": round(kernel_us, 3),
+        "decode_step_kernel_us": round(kernel_us, 3),
         "prefill_compaction_ms": round(prefill_ms, 3),
-        "decode_layer_step_us": round((ms - prefill_ms) * 1e3 / (S * L), 3),
+        "decode_ms_per_step": round(float(np.mean(decode_ms_l)), 3),
+        "launch": ("eager" if args.eager else "hip graphs") +
+                  (", append + attention" if args.unfused else ", fused decode step"),
         "kv_bytes_per_decode_step": round(float(attn_bytes.sum(axis=1).mean())),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

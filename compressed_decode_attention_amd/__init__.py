@@ -150,6 +150,7 @@ class CompactKVCache:
         self.k_amax = torch.zeros(max(nh, 1), dtype=torch.float32, device=dev)
         self.v_amax = torch.zeros(max(nh, 1), dtype=torch.float32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.seg_group = torch.zeros(max(nh, 1), dtype=torch.uint8, device=dev)
         self.k_pool = None
         self.v_pool = None
         self.pool_rows = 0
@@ -169,6 +170,7 @@ class CompactKVCache:
         s.ring_keep = _ptr(self.ring_keep)
         s.k_amax, s.v_amax = _ptr(self.k_amax), _ptr(self.v_amax)
         s.err = _ptr(self.err)
+        s.seg_group = _ptr(self.seg_group)
 
     # ---- prefill
     def count(self, keep, T: int, reserve: int, dst_out=None) -> None:

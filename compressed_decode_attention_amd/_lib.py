@@ -34,6 +34,7 @@ class CdaKvCache(C.Structure):
         ("seg_base", C.c_void_p), ("seg_cap", C.c_void_p), ("comp_len", C.c_void_p),
         ("pos", C.c_void_p), ("ring_keep", C.c_void_p),
         ("k_amax", C.c_void_p), ("v_amax", C.c_void_p), ("err", C.c_void_p),
+        ("seg_group", C.c_void_p),
     ]
 
 

@@ -18,13 +18,22 @@
 // segment to finish combines all of them with a log-sum-exp merge and resets
 // the counter (so the counters are zero between calls).
 //
-// XCD-local mode.  Workgroup w runs on XCD w mod (number of XCDs) on this
-// chip.  When that number divides 8, the units of segment i are given only
-// to workgroups w = 8k + (i mod 8), so all of them share one L2: partials
-// are plain stores and the merge reads them from that L2.  Workgroup w then
-// walks units k = w/8, w/8 + P, ... of its group's segments.  Otherwise
-// every workgroup takes one unit of the global list and partials go through
-// agent-scope (device-coherent) stores and loads.
+// XCD-local mode.  The dispatcher hands consecutive workgroups to the XCDs
+// round robin: workgroup w runs on XCD (w + c) mod (number of XCDs), with a
+// start c fixed for the dispatch (0 for a direct launch; graph replays have
+// shown other values).  When that number divides 8, the workgroups
+// w = 8k + r of one residue r share one XCD and so one L2, whatever c is.
+// The units of segment i are given only to the workgroups of one residue,
+// its group (seg_group[i] when COUNT has written the map, which evens out
+// the rows per group, else i mod 8): partials are plain stores and the
+// merge reads them from that L2.  An XCD keeps one 8-wave workgroup per CU
+// resident (32 at a time), so a group with more units than that finishes
+// its last ones a whole unit later; the balanced map keeps groups under it.
+// Workgroup w walks units k = w/8, w/8 + P, ... of its group's segments.
+// Each partial carries the XCD it was written on; the merging workgroup
+// sets CDA_DEVERR_XCD if one differs from its own.  Otherwise (XCD count not
+// a divisor of 8) every workgroup takes one unit of the global list and
+// partials go through agent-scope (device-coherent) stores and loads.
 //
 // Inside a wave, the G query rows of the KV head (G <= 16) are the N = 16
 // columns of two MFMA products per tile:
@@ -60,10 +69,15 @@
 //     its registers to the compact tail and writes the new token's row.  No
 //     other workgroup reads those rows as data (the compact tail is past
 //     the attended rows of its segment);
-//   - pos, comp_len and ring_keep are read by every workgroup while it
-//     plans its units, so they change only after all of them are done
-//     planning: each workgroup counts itself in on a grid counter after its
-//     last plan, and the last to count in writes the new metadata.
+//   - the work units of a decode step are planned from the segment
+//     capacities W + seg_cap, which do not change during decode, so no
+//     plan depends on another segment's length; rows past the data are
+//     masked like any segment end;
+//   - comp_len and ring_keep of a segment are written by its last unit to
+//     finish (the one that merges, or the only one), after every unit of
+//     the segment has read them; that unit then counts the segment in on a
+//     per-sequence counter, and the last of the Hkv segments of sequence b
+//     writes pos[b] (read by the units of all of them).
 #include "cda_device.h"
 #include "cda_launch.h"
 
@@ -90,10 +104,11 @@ struct AttnParams {
   float* lse;
   int32_t* err;
   float* part_o;       // [slots][G][D]
-  float* part_ml;      // [slots][G][2]
+  float* part_ml;      // [slots][G][4]: m, l, XCD of the writer, unused
   int32_t* sem;        // [nh]: units of the segment finished so far (0 between calls)
+  const uint8_t* seg_group;   // XCD-local mode: group of each segment, or NULL (i mod 8)
   // decode step only
-  int32_t* gcount;     // workgroups done planning (0 between calls)
+  int32_t* seqcnt;     // [B]: segments of the sequence done (0 between calls)
   uint8_t* ring_keep;
   const uint16_t* k_new;   // BF16 (b, h, d) at b * new_sb + h * new_sh + d
   const uint16_t* v_new;
@@ -101,7 +116,6 @@ struct AttnParams {
   const uint8_t* keep_new; // [nh]
   int Hkv, G, Hq, W, nh, tpu, out_f32;
   int per_xcd;         // XCD-local mode: workgroups per segment group
-  int nxcc;            // XCD-local mode: XCDs of the device (divides 8)
   float sm_scale;
 };
 
@@ -144,22 +158,9 @@ __device__ __forceinline__ void store_part4(float* a, f32x4 v) {
   }
 }
 template <bool XL>
-__device__ __forceinline__ void store_part2(float* a, float x, float y) {
-  if (XL) {
-    *reinterpret_cast<float2*>(a) = make_float2(x, y);
-  } else {
-    __hip_atomic_store(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a + 1, y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-template <bool XL>
 __device__ __forceinline__ float load_part1(const float* a) {
   return XL ? __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
             : __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <bool XL>
-__device__ __forceinline__ float2 load_part2(const float* a) {
-  return make_float2(load_part1<XL>(a), load_part1<XL>(a + 1));
 }
 template <bool XL>
 __device__ __forceinline__ f32x4 load_part4(const float* a) {
@@ -201,14 +202,12 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // (P = pos >= 0, 0 <= cl <= cap, kn = keep byte of the new token != 0).
 struct StepRows {
   int n_pre;     // rows holding data before the append
-  int new_row;   // segment row that receives the new token, -1 if it is dropped
-  int n_plan;    // rows the work units cover (n_pre, or up to new_row)
+  int new_row;   // segment row that receives the new token (< W + cap), -1 if dropped
 };
 __device__ __forceinline__ StepRows step_rows(int W, int P, int cl, int cap, int kn) {
   StepRows s;
   s.n_pre = min(W, P) + cl;
   s.new_row = W > 0 ? P % W : ((kn && cl < cap) ? cl : -1);
-  s.n_plan = s.new_row >= 0 ? max(s.n_pre, s.new_row + 1) : s.n_pre;
   return s;
 }
 
@@ -220,21 +219,26 @@ struct Unit {
   int P, cl, cap, kn;      // decode step: state before the append
 };
 
-// Unit k among the segments x0, x0 + xs, x0 + 2xs, ... (in that order, each
-// with units_of(rows) units).  Wave-level: every wave of a workgroup calls it
-// with the same arguments and gets the same answer.  With APP it scans all
-// the segments and returns their unit count in `total`.
+// Unit k of group grp: its segments in index order, each with
+// units_of(rows) units (rows = n_i, or W + seg_cap with APP).  With a group
+// map the group's segments are those mapped to it; otherwise they are grp,
+// grp + xs, grp + 2xs, ...  Wave-level: every wave of a workgroup calls it
+// with the same arguments and gets the same answer.  It scans all of the
+// group's segments and returns their unit count in `total`.
 template <bool FP8, bool APP>
-__device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, int k, int lane,
+__device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, int k, int lane,
                                           Unit& un, int& total) {
+  const bool mapped = p.seg_group != nullptr;
+  const int x0 = mapped ? 0 : grp, st = mapped ? 1 : xs;
   int carry = 0;
   bool found = false;
-  for (int base = 0; x0 + xs * base < p.nh; base += 64) {
-    const int hi = x0 + xs * (base + lane);
+  for (int base = 0; x0 + st * base < p.nh; base += 64) {
+    const int hi = x0 + st * (base + lane);
     int Ui = 0, ni = 0, Pi = 0, cli = 0, capi = 0, kni = 0;
     long long sbi = 0;
     float ka = 0.0f, va = 0.0f;
     if (hi < p.nh) {
+      const bool in_group = !mapped || (p.seg_group[hi] & 7) == grp;
       Pi = max(p.pos[hi / p.Hkv], 0);
       capi = max(p.seg_cap[hi], 0);
       cli = min(max(p.comp_len[hi], 0), capi);
@@ -243,9 +247,9 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, i
         ka = p.k_amax[hi];
         va = p.v_amax[hi];
       }
-      if (APP && p.W == 0) kni = p.keep_new[hi] != 0;
-      ni = APP ? step_rows(p.W, Pi, cli, capi, kni).n_plan : min(p.W, Pi) + cli;
-      Ui = units_of(ni, p.tpu);
+      if (APP) kni = p.keep_new[hi] != 0;
+      ni = APP ? p.W + capi : min(p.W, Pi) + cli;
+      Ui = in_group ? units_of(ni, p.tpu) : 0;
     }
     int x = Ui;
 #pragma unroll
@@ -257,7 +261,7 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, i
     const unsigned long long mine = __ballot(!found && hi < p.nh && k >= ex && k < ex + Ui);
     if (mine) {
       const int src = __ffsll((long long)mine) - 1;
-      un.i = x0 + xs * (base + src);
+      un.i = x0 + st * (base + src);
       un.first = lane_i(ex, src);
       un.U = lane_i(Ui, src);
       un.n = lane_i(ni, src);
@@ -271,7 +275,6 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, i
         un.kn = lane_i(kni, src);
       }
       found = true;
-      if (!APP) return true;
     }
     carry += lane_i(x, 63);
   }
@@ -279,53 +282,37 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int x0, int xs, i
   return found;
 }
 
-// Metadata of segment i after the append, from its state before it, with
-// the error bits the append raises (the same rules as the APPEND operation
-// of kv_compact).
-struct StepMeta {
-  int cl_new;      // comp_len after the append
-  int slot;        // ring row written (W > 0), else -1
-  int kn;          // keep bit stored for that ring row
-  int errbits;
-};
-__device__ __forceinline__ StepMeta step_meta(const AttnParams& p, int64_t i) {
-  StepMeta s;
-  const int P = max(p.pos[i / p.Hkv], 0);
-  const int cap = max(p.seg_cap[i], 0);
-  const int cl = min(max(p.comp_len[i], 0), cap);
-  const int64_t sb = p.seg_base[i];
-  const int kn = p.keep_new[i] != 0;
+// Decode step: the metadata of segment i after the append, from its state
+// before it (the unit's P, cl, cap, kn and the keep bit rk of the ring row
+// the new token takes), with the error bits the append raises -- the rules
+// of the APPEND operation of kv_compact.  Written by the last unit of the
+// segment.
+__device__ __forceinline__ void commit_segment(const AttnParams& p, int i, const Unit& un, int rk) {
   const int W = p.W;
-  s.cl_new = cl;
-  s.slot = -1;
-  s.kn = kn;
-  s.errbits = 0;
+  const int64_t sb = un.sb;
+  int cl_new = un.cl, errbits = 0;
   if (W > 0) {
-    s.slot = P % W;
-    const int rk = P >= W ? p.ring_keep[i * W + s.slot] : 0;
-    if (rk) {
-      if (cl < cap) {
-        if (sb + s.slot >= p.pool_rows || sb + W + cl >= p.pool_rows) s.errbits |= CDA_DEVERR_POOL;
-        s.cl_new = cl + 1;
+    const int slot = un.P % W;
+    if (un.P >= W && rk) {
+      if (un.cl < un.cap) {
+        if (sb + slot >= p.pool_rows || sb + W + un.cl >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
+        cl_new = un.cl + 1;
       } else {
-        s.errbits |= CDA_DEVERR_CAPACITY;
+        errbits |= CDA_DEVERR_CAPACITY;
       }
     }
-    if (sb + s.slot >= p.pool_rows) s.errbits |= CDA_DEVERR_POOL;
-  } else if (kn) {
-    if (cl < cap) {
-      if (sb + cl >= p.pool_rows) s.errbits |= CDA_DEVERR_POOL;
-      s.cl_new = cl + 1;
+    if (sb + slot >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
+    p.ring_keep[(int64_t)i * W + slot] = (uint8_t)un.kn;
+  } else if (un.kn) {
+    if (un.cl < un.cap) {
+      if (sb + un.cl >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
+      cl_new = un.cl + 1;
     } else {
-      s.errbits |= CDA_DEVERR_CAPACITY;
+      errbits |= CDA_DEVERR_CAPACITY;
     }
   }
-  return s;
-}
-__device__ __forceinline__ void commit_meta(const AttnParams& p, int64_t i, const StepMeta& s) {
-  p.comp_len[i] = s.cl_new;
-  if (s.slot >= 0) p.ring_keep[i * p.W + s.slot] = (uint8_t)s.kn;
-  if (s.errbits) atomicOr(p.err, s.errbits);
+  p.comp_len[i] = cl_new;
+  if (errbits) atomicOr(p.err, errbits);
 }
 
 // Mask of the bytes of dword w (bytes 4w .. 4w+3) that lie below `lim`.
@@ -345,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   constexpr int VL = FP8 ? 1 : 2;           // 16-byte V loads per (lane, d tile)
   constexpr int EPL = D / 64;               // new-token elements per lane
 
-  __shared__ int s_last, s_lastg;
+  __shared__ int s_last;
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ f32x4 s_o[NW][16][D / 4];
   __shared__ f32x4 s_new[APP ? D / 2 : 1];  // decoded new token: K values, then V values
@@ -354,39 +341,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   const int g = lane & 15, kg = lane >> 4;
   const int w = blockIdx.x;
   const int grp = XL ? (w & (kXcdGroups - 1)) : 0;
-  if (XL && tid == 0) {
-    // the XCD-local merge relies on workgroup w running on XCD w mod nxcc
-    const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;   // HW_REG_XCC_ID
-    if (xcc != w % p.nxcc) atomicOr(p.err, CDA_DEVERR_XCD);
-  }
-
-  // Decode step: this workgroup's count-in on the grid counter (tid 0), and
-  // the new metadata of segment `lane`, prepared by wave 0 into LDS when
-  // nh <= 64.
-  __shared__ StepMeta s_meta[APP ? 64 : 1];
-  bool counted = false;
-  int gprev = -1;
-  const bool meta_fast = p.nh <= 64;
-  auto count_in = [&]() {
-    if (APP && !counted) {
-      counted = true;
-      if (meta_fast && wave == 0 && lane < p.nh) {
-        s_meta[lane] = step_meta(p, lane);
-        // the values have been read before the count-in is issued
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      if (tid == 0)
-        gprev = __hip_atomic_fetch_add(p.gcount, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
+  const int xcc = XL ? (__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) : 0;   // HW_REG_XCC_ID
 
   for (int k = XL ? (w / kXcdGroups) : w;; k += p.per_xcd) {
     Unit un;
     int total = 0;
     if (!find_unit<FP8, APP>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
-    // decode step: whether this is the workgroup's last unit (its group has
-    // `total` units; workgroups take every per_xcd-th of them)
-    const bool last_unit = APP && (!XL || k + p.per_xcd >= total);
+    // whether this is the workgroup's last unit (its group has `total`
+    // units; workgroups take every per_xcd-th of them)
+    const bool last_unit = !XL || k + p.per_xcd >= total;
     const int i = un.i, U = un.U;
     const int b = i / p.Hkv, h = i - b * p.Hkv;
     const int G = p.G;
@@ -410,6 +373,11 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       }
     }
     const bool owner = APP && t_own >= t_begin && t_own < t_end && (t_own - t_begin) % NW == wave;
+    // wave 0: the keep bit of the ring row the new token takes, for the
+    // segment's metadata if this unit ends up writing it
+    int rk_seg = 0;
+    if (APP && wave == 0 && p.W > 0 && un.P >= p.W)
+      rk_seg = p.ring_keep[(int64_t)i * p.W + un.P % p.W];
     // owner wave: the leaving token's keep bit and its slice of the new token
     bool leaving = false, moved = false;
     uint32_t nk = 0, nv = 0;
@@ -710,7 +678,13 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
     __syncthreads();
-    if (last_unit) count_in();   // every wave is past its plan and its owner reads
+    // decode step, single-unit segment: every wave of the workgroup has read
+    // the segment's metadata (the owner's keep bit included)
+    int seq_prev = -1;
+    if (APP && U == 1 && tid == 0) {
+      commit_segment(p, i, un, rk_seg);
+      seq_prev = __hip_atomic_fetch_add(p.seqcnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     const float sv = vs;
     for (int e = tid; e < G * (D / 4); e += NTH) {     // (query row, 4 consecutive d)
@@ -734,7 +708,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         write_final4(p, b, h, gg, d4, D, M, L, O, sv);
       } else {
         store_part4<XL>(p.part_o + ((int64_t)slot * G + gg) * D + 4 * d4, O);
-        if (d4 == 0) store_part2<XL>(p.part_ml + ((int64_t)slot * G + gg) * 2, M, L);
+        if (d4 == 0)   // (m, l, XCD of this workgroup)
+          store_part4<XL>(p.part_ml + ((int64_t)slot * G + gg) * 4,
+                          f32x4{M, L, __int_as_float(xcc), 0.0f});
       }
     }
 
@@ -753,72 +729,64 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       }
       __syncthreads();
       if (s_last) {
+        // decode step: every unit of the segment has read its metadata
+        if (APP && tid == 0) {
+          commit_segment(p, i, un, rk_seg);
+          seq_prev = __hip_atomic_fetch_add(p.seqcnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         // each thread merges 4 consecutive outputs of one query row; the
-        // (m, l) and o loads of a batch of kMergeBatch units go out together
+        // (m, l) and o loads of a batch of kMergeBatch units go out together.
+        // XCD-local mode: a partial written on another XCD than this one
+        // (the workgroups of a residue not sharing an L2) sets CDA_DEVERR_XCD.
+        bool xcd_clash = false;
         for (int e = tid; e < G * (D / 4); e += NTH) {
           const int gg = e / (D / 4), d4 = e - gg * (D / 4);
           float M = -INFINITY, L = 0.0f;
           f32x4 O = f32x4{0, 0, 0, 0};
           for (int k0 = 0; k0 < U; k0 += kMergeBatch) {
-            float2 ml[kMergeBatch];
+            f32x4 ml[kMergeBatch];
             f32x4 ov[kMergeBatch];
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {   // unconditional loads, clamped index
               const int ku = un.first + min(k0 + j, U - 1);
               const int64_t sl = (int64_t)(XL ? ku * kXcdGroups + grp : ku) * G + gg;
-              ml[j] = load_part2<XL>(p.part_ml + sl * 2);
+              ml[j] = load_part4<XL>(p.part_ml + sl * 4);
               ov[j] = load_part4<XL>(p.part_o + sl * D + 4 * d4);
             }
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j)
-              if (k0 + j >= U) ml[j].x = -INFINITY;
+            for (int j = 0; j < kMergeBatch; ++j) {
+              if (XL && __float_as_int(ml[j][2]) != xcc) xcd_clash = true;
+              if (k0 + j >= U) ml[j][0] = -INFINITY;
+            }
             float Mb = M;
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, ml[j].x);
+            for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, ml[j][0]);
             if (Mb == -INFINITY) continue;
             const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
             O *= a;
             L *= a;
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
-              const float f = (ml[j].x == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml[j].x - Mb);
+              const float f = (ml[j][0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml[j][0] - Mb);
               O += f * ov[j];
-              L += f * ml[j].y;
+              L += f * ml[j][1];
             }
             M = Mb;
           }
           write_final4(p, b, h, gg, d4, D, M, L, O, sv);
         }
+        if (xcd_clash) atomicOr(p.err, CDA_DEVERR_XCD);
       }
     }
-    // after its last unit a workgroup plans nothing more: with the decode
-    // step, the metadata may already have changed
-    if (!XL || last_unit) break;
+    // decode step: the last segment of sequence b to be done writes pos[b]
+    if (APP && tid == 0 && seq_prev == p.Hkv - 1) {
+      p.pos[b] = un.P + 1;
+      __hip_atomic_store(p.seqcnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (last_unit) break;
     __syncthreads();   // the LDS of this unit is reused by the next one
   }
 
-  if (APP) {
-    // ---- decode step: the last workgroup to count itself in writes the
-    // new metadata (every other workgroup is done reading it)
-    count_in();
-    if (tid == 0) {
-      const bool last = gprev == (int)gridDim.x - 1;
-      s_lastg = last;
-      if (last) __hip_atomic_store(p.gcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (s_lastg) {
-      const int B = p.nh / p.Hkv;
-      if (meta_fast) {
-        if (wave == 0 && lane < p.nh) commit_meta(p, lane, s_meta[lane]);
-        __syncthreads();
-      } else {
-        for (int i = tid; i < p.nh; i += NTH) commit_meta(p, i, step_meta(p, i));
-        __syncthreads();   // every pos[b] has been read
-      }
-      for (int bb = tid; bb < B; bb += NTH) p.pos[bb] = max(p.pos[bb], 0) + 1;
-    }
-  }
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -859,13 +827,14 @@ int64_t attn_max_units(const cda_kv_cache& c, int tpu) {
   return nh + c.pool_rows / ((int64_t)kTile * tpu);
 }
 
-// Workspace: [grid counter][per-segment counters][partial (m, l)][partial o].
+// Workspace: [per-segment counters][per-sequence counters]
+// [partial (m, l, XCD)][partial o].
 // Partial slots: an XCD-local slot is 8k + group with k below the units of
 // the group (at most all units), so 8 x the unit bound covers both modes.
 size_t attn_workspace_bytes(const cda_kv_cache& c, int G, int tpu) {
   const int64_t slots = kXcdGroups * attn_max_units(c, tpu);
   const int64_t nh = (int64_t)c.B * c.Hkv;
-  return 256 + align256((size_t)nh * 4) + align256((size_t)slots * G * 2 * 4) +
+  return align256((size_t)nh * 4) + align256((size_t)c.B * 4) + align256((size_t)slots * G * 4 * 4) +
          align256((size_t)slots * G * c.D * 4);
 }
 
@@ -892,12 +861,12 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.lse = lse;
   p.err = c.err;
   char* ws = static_cast<char*>(workspace);
-  p.gcount = reinterpret_cast<int32_t*>(ws);
-  ws += 256;
   p.sem = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)nh * 4);
+  p.seqcnt = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)c.B * 4);
   p.part_ml = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)slots * G * 2 * 4);
+  ws += align256((size_t)slots * G * 4 * 4);
   p.part_o = reinterpret_cast<float*>(ws);
   p.ring_keep = c.ring_keep;
   p.k_new = step ? static_cast<const uint16_t*>(step->k) : nullptr;
@@ -915,7 +884,9 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c.D);
   const int nx = device_xcds();
   const bool xl = nx > 0 && kXcdGroups % nx == 0;
-  p.nxcc = xl ? nx : 1;
+  // the group map (written by COUNT) is used for up to 512 segments; past
+  // that it is the identity i mod 8 and scanning it would only cost time
+  p.seg_group = (xl && nh <= 512) ? c.seg_group : nullptr;
   // XCD-local: 8 groups of per_xcd workgroups, a quarter more than an even
   // share of the unit bound; a group with more units loops over them.
   p.per_xcd = xl ? (int)((units * 5 / 4 + kXcdGroups - 1) / kXcdGroups) : 0;

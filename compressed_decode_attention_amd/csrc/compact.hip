@@ -89,10 +89,18 @@ __device__ __forceinline__ long long block_exclusive_scan64(long long v, long lo
   return before + x - v;
 }
 
+// Segments whose attention work is spread over the 8 XCD groups by size.
+constexpr int kBalanceMax = 512;
+
+// seg_base by a prefix sum of the aligned segment sizes; then, if asked, the
+// group map: segments ranked by size in 64-row tiles (larger first, ties by
+// index) and dealt to the 8 groups in snake order (0..7, 7..0, ...), so
+// that every group gets a near-equal share of rows.
 __global__ __launch_bounds__(kBlock) void seg_scan_kernel(
     int nh, int W, const int32_t* __restrict__ seg_cap, int64_t* __restrict__ seg_base,
-    int32_t* __restrict__ err) {
+    int32_t* __restrict__ err, uint8_t* __restrict__ seg_group) {
   __shared__ long long smem[4];
+  __shared__ int s_tiles[kBalanceMax];
   long long carry = 0;
   for (int base = 0; base < nh; base += kBlock) {
     const int i = base + threadIdx.x;
@@ -106,6 +114,25 @@ __global__ __launch_bounds__(kBlock) void seg_scan_kernel(
   if (threadIdx.x == 0) {
     seg_base[nh] = carry;
     err[0] = 0;
+  }
+  if (seg_group) {
+    if (nh <= kBalanceMax) {
+      for (int i = threadIdx.x; i < nh; i += kBlock)
+        s_tiles[i] = (int)(((long long)W + seg_cap[i] + kTile - 1) / kTile);
+      __syncthreads();
+      for (int i = threadIdx.x; i < nh; i += kBlock) {
+        const int wi = s_tiles[i];
+        int rank = 0;
+        for (int j = 0; j < nh; ++j) {
+          const int wj = s_tiles[j];
+          rank += (wj > wi) || (wj == wi && j < i);
+        }
+        const int round = rank >> 3, slot = rank & 7;
+        seg_group[i] = (uint8_t)((round & 1) ? 7 - slot : slot);
+      }
+    } else {
+      for (int i = threadIdx.x; i < nh; i += kBlock) seg_group[i] = (uint8_t)(i & 7);
+    }
   }
 }
 
@@ -462,7 +489,7 @@ hipError_t launch_count(const cda_kv_cache& c, const cda_compact_args& a, hipStr
     count_kernel<<<nh, kBlock, 0, s>>>(a.keep, a.keep_ld, a.T, c.W, a.reserve, c.comp_len,
                                        c.seg_cap, a.dst_out);
   }
-  seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err);
+  seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err, c.seg_group);
   return hipGetLastError();
 }
 

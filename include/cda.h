@@ -81,9 +81,10 @@ enum cda_status {
  * the host sees them only after it synchronises and copies the word). */
 #define CDA_DEVERR_CAPACITY 1   /* APPEND: a segment's compact region was full; that token was dropped */
 #define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written */
-#define CDA_DEVERR_XCD 4        /* attention: a workgroup ran on an XCD other than the one the
-                                   XCD-local merge assumes (workgroup w on XCD w mod #XCDs);
-                                   that call's outputs are not reliable */
+#define CDA_DEVERR_XCD 4        /* attention: the workgroups w of one residue w mod 8 did not all
+                                   run on one XCD, which the XCD-local merge of split heads
+                                   needs (the dispatcher deals workgroups to the XCDs round
+                                   robin); that call's outputs are not reliable */
 
 enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1 };
 enum cda_out_dtype { CDA_OUT_BF16 = 0, CDA_OUT_F32 = 1 };
@@ -112,6 +113,11 @@ typedef struct cda_kv_cache {
     float *k_amax;      /* [B*Hkv]; FP8 absmax of K (PACK computes or takes it) */
     float *v_amax;      /* [B*Hkv]; FP8 absmax of V */
     int32_t *err;       /* [1]; device error word, CDA_DEVERR_* bits; COUNT clears it */
+    uint8_t *seg_group; /* optional [B*Hkv] (may be NULL); written by COUNT: the group (0..7)
+                           of workgroups, one XCD's worth, that takes the attention work of
+                           each segment, chosen to even out the capacity W + seg_cap per group.
+                           NULL, or more than 512 segments: segment i goes to group i mod 8.
+                           Scheduling only: results do not depend on it */
 } cda_kv_cache;
 
 /*
@@ -140,7 +146,8 @@ typedef struct cda_compact_args {
  * CDA_OP_COUNT: per segment, counts kept positions p <= T-1-W (comp_len),
  *   sets seg_cap = comp_len + reserve, and writes seg_base by an exclusive
  *   prefix sum of the aligned segment sizes; seg_base[B*Hkv] is the number
- *   of pool rows to allocate.  Optionally writes dst_out.  Clears *err.
+ *   of pool rows to allocate.  Optionally writes dst_out and seg_group.
+ *   Clears *err.
  *   Reads keep; needs seg_base, seg_cap, comp_len, err (pools may be NULL).
  * CDA_OP_PACK: after COUNT (same keep, T), writes every stored prefill row
  *   (the W most recent positions and every kept older one) to its pool row,

@@ -156,3 +156,41 @@ def test_decode_loop_matches_oracle(kv_dtype, D, W):
             worst = max(worst, check_close(out.cpu().numpy(), ref, f"step {s}"))
     assert c.error_word() == 0
     log(f"  worst abs err {worst:.2e}")
+
+
+def test_group_map_from_count_is_balanced_and_changes_nothing():
+    # COUNT deals the segments to the 8 XCD groups by size (snake order over
+    # the capacities); attention and decode steps give the same bits with
+    # the map as with the plain i mod 8 grouping (map pointer NULL)
+    B, Hq, Hkv, D, T, W, S = 8, 32, 8, 128, 2500, 256, 4
+    rates = torch.rand((B, Hkv, 1), generator=torch.Generator().manual_seed(102)) * 0.3
+    keep = (torch.rand((B, Hkv, T + S), generator=torch.Generator().manual_seed(103)) < rates)
+    keep = keep.to(torch.uint8)
+    k = workload.random_bf16((B, T + S, Hkv, D), seed=104)
+    v = workload.random_bf16((B, T + S, Hkv, D), seed=105)
+    q = workload.random_bf16((S, B, Hq, D), seed=106)
+    c1, _ = gpu_prefill(k, v, keep, T, W, S, "fp8", with_dst=False)
+    c2, _ = gpu_prefill(k, v, keep, T, W, S, "fp8", with_dst=False)
+    gm = c1.seg_group.cpu().numpy().astype(np.int64)
+    tiles = -(-(W + c1.seg_cap.cpu().numpy().astype(np.int64)) // 64)
+    nh = B * Hkv
+    assert gm.min() >= 0 and gm.max() < 8
+    assert np.all(np.bincount(gm, minlength=8) == nh // 8)
+    sums = np.bincount(gm, weights=tiles, minlength=8)
+    assert sums.max() - sums.min() <= tiles.max(), sums
+    c2.struct.seg_group = 0          # plain i mod 8 grouping
+    kd, vd, qd = k.to(dev()), v.to(dev()), q.to(dev())
+    kn = keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev())
+    for split in (256, 512):
+        o1 = c1.attention(qd[0], out_dtype=torch.float32, split_tokens=split)
+        o2 = c2.attention(qd[0], out_dtype=torch.float32, split_tokens=split)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"attention, split {split}"
+    for s in range(S):
+        o1 = c1.decode_step(kd[:, T + s], vd[:, T + s], kn[s], qd[s], out_dtype=torch.float32)
+        o2 = c2.decode_step(kd[:, T + s], vd[:, T + s], kn[s], qd[s], out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"decode step {s}"
+    assert torch.equal(c1.comp_len, c2.comp_len) and torch.equal(c1.pos, c2.pos)
+    assert torch.equal(c1.k_pool, c2.k_pool) and torch.equal(c1.v_pool, c2.v_pool)
+    assert c1.error_word() == 0 and c2.error_word() == 0
