@@ -78,6 +78,8 @@
 //     the segment has read them; that unit then counts the segment in on a
 //     per-sequence counter, and the last of the Hkv segments of sequence b
 //     writes pos[b] (read by the units of all of them).
+//   - every counter sits on a 128-byte line of its own: atomics on one line
+//     are performed one after another.
 #include "cda_device.h"
 #include "cda_launch.h"
 
@@ -88,6 +90,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMergeBatch = 8;   // partials loaded per round trip in the merge
 constexpr int kXcdGroups = 8;    // segment groups of the XCD-local mode
+constexpr int kCounterStride = 32;   // ints between counters: one 128-byte line each
 
 struct AttnParams {
   uint8_t* k_pool;
@@ -105,10 +108,11 @@ struct AttnParams {
   int32_t* err;
   float* part_o;       // [slots][G][D]
   float* part_ml;      // [slots][G][4]: m, l, XCD of the writer, unused
-  int32_t* sem;        // [nh]: units of the segment finished so far (0 between calls)
+  int32_t* sem;        // [nh] (stride kCounterStride): units of the segment finished so
+                       // far (0 between calls)
   const uint8_t* seg_group;   // XCD-local mode: group of each segment, or NULL (i mod 8)
   // decode step only
-  int32_t* seqcnt;     // [B]: segments of the sequence done (0 between calls)
+  int32_t* seqcnt;     // [B] (stride kCounterStride): segments of the sequence done
   uint8_t* ring_keep;
   const uint16_t* k_new;   // BF16 (b, h, d) at b * new_sb + h * new_sh + d
   const uint16_t* v_new;
@@ -238,7 +242,6 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
     long long sbi = 0;
     float ka = 0.0f, va = 0.0f;
     if (hi < p.nh) {
-      const bool in_group = !mapped || (p.seg_group[hi] & 7) == grp;
       Pi = max(p.pos[hi / p.Hkv], 0);
       capi = max(p.seg_cap[hi], 0);
       cli = min(max(p.comp_len[hi], 0), capi);
@@ -248,6 +251,10 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
         va = p.v_amax[hi];
       }
       if (APP) kni = p.keep_new[hi] != 0;
+      // the map byte last, through a valid address either way, so that no
+      // load of this round trip waits behind it or behind a branch
+      const uint8_t gb = *(mapped ? p.seg_group + hi : reinterpret_cast<const uint8_t*>(p.seg_cap + hi));
+      const bool in_group = !mapped || (gb & 7) == grp;
       ni = APP ? p.W + capi : min(p.W, Pi) + cli;
       Ui = in_group ? units_of(ni, p.tpu) : 0;
     }
@@ -347,6 +354,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     Unit un;
     int total = 0;
     if (!find_unit<FP8, APP>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
+    // every load of the plan has been used: say so, so that no later write to
+    // a register it used waits for the loads issued after this point
+    __builtin_amdgcn_s_waitcnt(0);
     // whether this is the workgroup's last unit (its group has `total`
     // units; workgroups take every per_xcd-th of them)
     const bool last_unit = !XL || k + p.per_xcd >= total;
@@ -373,18 +383,37 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       }
     }
     const bool owner = APP && t_own >= t_begin && t_own < t_end && (t_own - t_begin) % NW == wave;
-    // wave 0: the keep bit of the ring row the new token takes, for the
-    // segment's metadata if this unit ends up writing it
-    int rk_seg = 0;
-    if (APP && wave == 0 && p.W > 0 && un.P >= p.W)
-      rk_seg = p.ring_keep[(int64_t)i * p.W + un.P % p.W];
-    // owner wave: the leaving token's keep bit and its slice of the new token
-    bool leaving = false, moved = false;
+    // decode step: where the keep bit of the token leaving the ring (ring
+    // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
+    // needed, and tested only after the loads that must not wait for it.
+    const bool leaving = APP && p.W > 0 && un.P >= p.W;
+    const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + un.P % max(p.W, 1)
+                                        : p.keep_new + i)
+                             : nullptr;
+    // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per
+    // k-step.  Columns g >= G repeat row 0: their results land in rows of the
+    // product nobody reads, and the loads stay free of any condition (nothing
+    // waits for them before the first MFMA).
+    bf16x8 qop[NK];
+    {
+      const uint16_t* qrow = p.q + (int64_t)(b * p.Hq + h * G + (g < G ? g : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
+        qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + d0));
+      }
+    }
+    const float c1 = p.sm_scale * kLog2e * ks;
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+
+    // owner wave: its slice of the new token (issued after the accumulators
+    // are set up, so that nothing before the tile loads waits for it)
     uint32_t nk = 0, nv = 0;
     if (owner) {
-      leaving = p.W > 0 && un.P >= p.W;
-      const int rk = leaving ? p.ring_keep[(int64_t)i * p.W + new_row] : 0;
-      moved = rk && un.cl < un.cap && sb + p.W + un.cl < p.pool_rows;
       const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
       if (EPL == 2) {
         nk = *reinterpret_cast<const uint32_t*>(p.k_new + off);
@@ -395,25 +424,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       }
     }
 
-    // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per k-step
-    bf16x8 qop[NK];
-    {
-      const bool have = g < G;
-      const uint16_t* qrow = p.q + (int64_t)(b * p.Hq + h * G + (have ? g : 0)) * D;
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
-        u32x4 v = have ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
-        qop[s] = as_bf16x8(v);
-      }
-    }
-    const float c1 = p.sm_scale * kLog2e * ks;
-
-    float m_run = -INFINITY, l_run = 0.0f;
-    f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-
     bool first_tile = true;
     for (int t = t_begin + wave; t < t_end; t += NW) {
       const int r0 = t * kTile;
@@ -422,8 +432,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       if (valid <= 0 && !own) break;
       if (valid > 0) {
         const bool full = valid == kTile;
-        // the leaving token's row is masked unless it moves to the compact tail
-        const int mrow = (own && leaving && !moved) ? (new_row & (kTile - 1)) : -1;
+        // decode step: the leaving token's keep bit, issued ahead of the tile
+        int rko = 0;
+        if (APP) rko = *rkp;
         const uint8_t* ktile = p.k_pool + (sb + r0) * (int64_t)RB;
         const uint8_t* vtile = p.v_pool + (sb + r0) * (int64_t)RB;
 
@@ -443,6 +454,32 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
           for (int j = 0; j < VL; ++j)
             vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
                 vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
+
+        // -- S^T = K . Q^T, 16 tokens per MFMA row block
+        f32x4 s[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          s[m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int st = 0; st < NK; ++st) {
+            bf16x8 a;
+            if (FP8) {
+              const u32x4 v = kr[m][st >> 1];
+              a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
+            } else {
+              a = as_bf16x8(kr[m][st]);
+            }
+            s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], s[m], 0, 0, 0);
+          }
+        }
+
+        // -- decode step, owner wave: whether the leaving token moves to the
+        //    compact tail (else its row is masked); tested here, after QK,
+        //    so that nothing before the tile loads waits for the keep bit
+        __asm__ volatile("" : "+v"(rko));   // keeps the test from moving up
+        const bool moved = own && leaving && rko != 0 && un.cl < un.cap &&
+                           sb + p.W + un.cl < p.pool_rows;
+        const int mrow = (own && leaving && !moved) ? (new_row & (kTile - 1)) : -1;
 
         // -- decode step, owner wave: copy the leaving token's row from the
         //    registers of this tile to the compact tail (segment row W + cl).
@@ -479,24 +516,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
                       *reinterpret_cast<uint16_t*>(vt + o) = (uint16_t)wd;
                   }
                 }
-          }
-        }
-
-        // -- S^T = K . Q^T, 16 tokens per MFMA row block
-        f32x4 s[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          s[m] = f32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int st = 0; st < NK; ++st) {
-            bf16x8 a;
-            if (FP8) {
-              const u32x4 v = kr[m][st >> 1];
-              a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
-            } else {
-              a = as_bf16x8(kr[m][st]);
-            }
-            s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], s[m], 0, 0, 0);
           }
         }
 
@@ -593,6 +612,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       // -- decode step, owner wave: the new token's (logit, value) pair joins
       //    the running softmax state, then its row is written
       if (own) {
+        // keeps the work on the new token (loop-invariant) from being hoisted
+        // above the tile loads, where it would wait for k_new / v_new
+        __asm__ volatile("" : "+v"(nk), "+v"(nv));
         const int d0n = EPL * lane;
         float kd[EPL], vd[EPL];
         uint32_t kc = 0, vc = 0;   // stored bytes of this lane's elements
@@ -669,6 +691,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       }
     }
 
+    // decode step: the keep bit again, for the segment's metadata (back
+    // before it is needed, after the combine or the merge)
+    const int rkc = APP ? *rkp : 0;
+
     // ---- combine the waves of the workgroup
     l_run = sum_xor32(sum_xor16(l_run));
     if (kg == 0) {
@@ -682,8 +708,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     // the segment's metadata (the owner's keep bit included)
     int seq_prev = -1;
     if (APP && U == 1 && tid == 0) {
-      commit_segment(p, i, un, rk_seg);
-      seq_prev = __hip_atomic_fetch_add(p.seqcnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      commit_segment(p, i, un, leaving && rkc != 0);
+      seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     const float sv = vs;
@@ -721,18 +748,18 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) {
-        const int prev =
-            __hip_atomic_fetch_add(p.sem + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int32_t* cnt = p.sem + (int64_t)i * kCounterStride;
+        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = prev == U - 1;
-        if (prev == U - 1)
-          __hip_atomic_store(p.sem + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == U - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
       if (s_last) {
         // decode step: every unit of the segment has read its metadata
         if (APP && tid == 0) {
-          commit_segment(p, i, un, rk_seg);
-          seq_prev = __hip_atomic_fetch_add(p.seqcnt + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          commit_segment(p, i, un, leaving && rkc != 0);
+          seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // each thread merges 4 consecutive outputs of one query row; the
         // (m, l) and o loads of a batch of kMergeBatch units go out together.
@@ -753,6 +780,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
               ml[j] = load_part4<XL>(p.part_ml + sl * 4);
               ov[j] = load_part4<XL>(p.part_o + sl * D + 4 * d4);
             }
+
 #pragma unroll
             for (int j = 0; j < kMergeBatch; ++j) {
               if (XL && __float_as_int(ml[j][2]) != xcc) xcd_clash = true;
@@ -781,10 +809,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     // decode step: the last segment of sequence b to be done writes pos[b]
     if (APP && tid == 0 && seq_prev == p.Hkv - 1) {
       p.pos[b] = un.P + 1;
-      __hip_atomic_store(p.seqcnt + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.seqcnt + (int64_t)b * kCounterStride, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
     if (last_unit) break;
-    __syncthreads();   // the LDS of this unit is reused by the next one
+    // the next unit starts with nothing in flight (its first loads then wait
+    // for nothing of this one), and reuses this unit's LDS
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
 }
@@ -827,14 +859,15 @@ int64_t attn_max_units(const cda_kv_cache& c, int tpu) {
   return nh + c.pool_rows / ((int64_t)kTile * tpu);
 }
 
-// Workspace: [per-segment counters][per-sequence counters]
-// [partial (m, l, XCD)][partial o].
+// Workspace: [per-segment counters][per-sequence counters] (one 128-byte
+// line each) [partial (m, l, XCD)][partial o].
 // Partial slots: an XCD-local slot is 8k + group with k below the units of
 // the group (at most all units), so 8 x the unit bound covers both modes.
 size_t attn_workspace_bytes(const cda_kv_cache& c, int G, int tpu) {
   const int64_t slots = kXcdGroups * attn_max_units(c, tpu);
   const int64_t nh = (int64_t)c.B * c.Hkv;
-  return align256((size_t)nh * 4) + align256((size_t)c.B * 4) + align256((size_t)slots * G * 4 * 4) +
+  return align256((size_t)nh * 4 * kCounterStride) + align256((size_t)c.B * 4 * kCounterStride) +
+         align256((size_t)slots * G * 4 * 4) +
          align256((size_t)slots * G * c.D * 4);
 }
 
@@ -862,9 +895,9 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.err = c.err;
   char* ws = static_cast<char*>(workspace);
   p.sem = reinterpret_cast<int32_t*>(ws);
-  ws += align256((size_t)nh * 4);
+  ws += align256((size_t)nh * 4 * kCounterStride);
   p.seqcnt = reinterpret_cast<int32_t*>(ws);
-  ws += align256((size_t)c.B * 4);
+  ws += align256((size_t)c.B * 4 * kCounterStride);
   p.part_ml = reinterpret_cast<float*>(ws);
   ws += align256((size_t)slots * G * 4 * 4);
   p.part_o = reinterpret_cast<float*>(ws);

@@ -82,6 +82,14 @@ def compare_state(c: CompactKVCache, o: oracle.OracleCache, what: str = ""):
             raise AssertionError(f"{what} V rows differ in segment {i}: rows {bad[:8]}")
 
 
+def counter_bytes(B: int, Hkv: int) -> int:
+    """Bytes at the start of an attention workspace that hold the
+    completion counters (one 128-byte line per segment, then one per
+    sequence, each region 256-byte aligned); zero between calls."""
+    a = lambda x: -(-x // 256) * 256
+    return a(B * Hkv * 128) + a(B * 128)
+
+
 def check_close(got, ref, what="", atol=ATOL, rtol=RTOL):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)

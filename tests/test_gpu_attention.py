@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workload
-from _cda_testlib import (check_close, dev, gpu_prefill, log, odt, oracle_prefill)
+from _cda_testlib import (check_close, counter_bytes, dev, gpu_prefill, log, odt, oracle_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,8 +91,7 @@ def test_one_workspace_reused_across_splits_and_caches():
             for c in caches:
                 out = c.attention(qd, out_dtype=torch.float32, split_tokens=split, workspace=ws)
                 check_close(out.cpu().numpy(), refs[c.kv_dtype], f"{c.kv_dtype} split {split} rep {rep}")
-    nh = B * Hkv
-    assert torch.count_nonzero(ws[: 4 * nh]) == 0
+    assert torch.count_nonzero(ws[: counter_bytes(B, Hkv)]) == 0
 
 
 def test_outliers_and_custom_scale():

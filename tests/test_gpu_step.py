@@ -11,7 +11,8 @@ import torch
 
 import oracle
 import workload
-from _cda_testlib import check_close, compare_state, dev, gpu_prefill, log, odt, oracle_prefill
+from _cda_testlib import (check_close, compare_state, counter_bytes, dev, gpu_prefill, log, odt,
+                          oracle_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,10 +112,7 @@ def test_counters_zero_and_workspace_shared_with_attention():
         ref, _ = oracle.attention(q[s], k, v, keep, P, W, oracle.FP8, ka, va)
         check_close(out.cpu().numpy(), ref, f"step {s} split {split}")
         check_close(again.cpu().numpy(), ref, f"step {s} attention after the step")
-        # per-segment counters, then per-sequence counters (256-byte aligned)
-        seq0 = -(-4 * B * Hkv // 256) * 256
-        assert torch.count_nonzero(ws[: 4 * B * Hkv]) == 0
-        assert torch.count_nonzero(ws[seq0: seq0 + 4 * B]) == 0
+        assert torch.count_nonzero(ws[: counter_bytes(B, Hkv)]) == 0
     assert c.error_word() == 0
 
 
