@@ -62,13 +62,14 @@
 //     ring row of the token leaving the window is masked when that token is
 //     not kept (it is the same row either way: if it moves, its values are
 //     the ones now in the ring row);
-//   - the new token is one more (logit, value) pair, formed in registers
-//     from the BF16 input with the frozen scales, added to the running
-//     softmax state of the wave that reads the tile of the new token's row;
-//   - that wave, after its loads of the tile, copies the leaving token from
-//     its registers to the compact tail and writes the new token's row.  No
-//     other workgroup reads those rows as data (the compact tail is past
-//     the attended rows of its segment);
+//   - the new token is one more (logit, value) pair, formed from the BF16
+//     input with the frozen scales by wave 0 of the unit that holds the
+//     tile of its row, after that unit's tiles are done; the workgroup's
+//     combine folds it in with the waves' partial states;
+//   - the same wave then copies the leaving token's row to the compact tail
+//     (if it moves) and writes the new token's row; every load of the tile
+//     has completed by then.  No other workgroup reads those rows as data
+//     (the compact tail is past the attended rows of its segment);
 //   - the work units of a decode step are planned from the segment
 //     capacities W + seg_cap, which do not change during decode, so no
 //     plan depends on another segment's length; rows past the data are
@@ -343,6 +344,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   __shared__ float s_m[NW][16], s_l[NW][16];
   __shared__ f32x4 s_o[NW][16][D / 4];
   __shared__ f32x4 s_new[APP ? D / 2 : 1];  // decoded new token: K values, then V values
+  __shared__ float s_zn[APP ? 16 : 1];        // its logit per query row (log2 units)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 15, kg = lane >> 4;
@@ -382,7 +384,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         t_own = new_row / kTile;
       }
     }
-    const bool owner = APP && t_own >= t_begin && t_own < t_end && (t_own - t_begin) % NW == wave;
+    // the unit that holds the new token's tile adds it to the segment
+    const bool owner_unit = APP && t_own >= t_begin && t_own < t_end;
     // decode step: where the keep bit of the token leaving the ring (ring
     // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
     // needed, and tested only after the loads that must not wait for it.
@@ -410,10 +413,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
 
-    // owner wave: its slice of the new token (issued after the accumulators
-    // are set up, so that nothing before the tile loads waits for it)
-    uint32_t nk = 0, nv = 0;
-    if (owner) {
+    // owner unit, wave 0: its slice of the new token (issued after the
+    // accumulators are set up, so that nothing before the tile loads waits
+    // for it)
+    // It also reads the ring row the new token replaces (the leaving
+    // token's row: 16-byte K chunk `lane`, V elements EPL*lane..), in case
+    // it moves to the compact tail.
+    uint32_t nk = 0, nv = 0, ox = 0;
+    u32x4 okx = u32x4{0, 0, 0, 0};
+    if (owner_unit && wave == 0) {
       const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
       if (EPL == 2) {
         nk = *reinterpret_cast<const uint32_t*>(p.k_new + off);
@@ -422,15 +430,73 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         nk = p.k_new[off];
         nv = p.v_new[off];
       }
+      const int rs = new_row & (kTile - 1);
+      const uint8_t* kt = p.k_pool + (sb + (new_row - rs)) * (int64_t)RB;
+      const uint8_t* vt = p.v_pool + (sb + (new_row - rs)) * (int64_t)RB;
+      okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        ox |= (FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
+                   : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs])
+              << (16 * e);
     }
 
     bool first_tile = true;
+    // decode step, wave 0 of the unit holding the new token's tile: forms
+    // the new token from its BF16 input with the frozen scales -- its values
+    // and one logit per query row (from the q operand) into LDS, for the
+    // combine -- and returns its stored bytes.  It runs during wave 0's
+    // first tile, while that tile is in flight.
+    auto new_token = [&](uint32_t& kc, uint32_t& vc) {
+      __asm__ volatile("" : "+v"(nk), "+v"(nv));   // keeps this work below the tile loads
+      const int d0n = EPL * lane;
+      const float kinv = FP8 ? fp8_inv_scale(un.ka) : 1.0f;
+      const float vinv = FP8 ? fp8_inv_scale(un.va) : 1.0f;
+      kc = 0;
+      vc = 0;
+      float* sn = reinterpret_cast<float*>(s_new);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const uint32_t kb = (nk >> (16 * e)) & 0xFFFFu, vb = (nv >> (16 * e)) & 0xFFFFu;
+        if (FP8) {
+          const uint32_t kq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv));
+          const uint32_t vq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+          sn[d0n + e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kq, 1.0f, false)[0];
+          sn[D + d0n + e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vq, 1.0f, false)[0];
+          kc |= kq << (8 * e);
+          vc |= vq << (8 * e);
+        } else {
+          sn[d0n + e] = bf16_bits_to_f32(kb);
+          sn[D + d0n + e] = bf16_bits_to_f32(vb);
+          kc |= kb << (16 * e);
+          vc |= vb << (16 * e);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      float dot = 0.0f;   // lane (g, kg): its quarter of q[g] . k^
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
+        const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dot = fmaf((float)qop[s][e], a[e], dot);
+          dot = fmaf((float)qop[s][4 + e], c[e], dot);
+        }
+      }
+      dot = sum_xor32(sum_xor16(dot));
+      if (kg == 0) s_zn[g] = dot * c1;
+    };
+    uint32_t kc = 0, vc = 0;   // wave 0 of the owner unit: the new row's stored bytes
+    bool nt_done = false;
+
     for (int t = t_begin + wave; t < t_end; t += NW) {
       const int r0 = t * kTile;
       const int valid = (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
-      const bool own = APP && t == t_own;
-      if (valid <= 0 && !own) break;
-      if (valid > 0) {
+      const bool own = APP && t == t_own;   // the tile of the leaving token's row
+      if (valid <= 0) break;
+      {
         const bool full = valid == kTile;
         // decode step: the leaving token's keep bit, issued ahead of the tile
         int rko = 0;
@@ -473,51 +539,18 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
           }
         }
 
-        // -- decode step, owner wave: whether the leaving token moves to the
-        //    compact tail (else its row is masked); tested here, after QK,
-        //    so that nothing before the tile loads waits for the keep bit
-        __asm__ volatile("" : "+v"(rko));   // keeps the test from moving up
-        const bool moved = own && leaving && rko != 0 && un.cl < un.cap &&
-                           sb + p.W + un.cl < p.pool_rows;
-        const int mrow = (own && leaving && !moved) ? (new_row & (kTile - 1)) : -1;
-
-        // -- decode step, owner wave: copy the leaving token's row from the
-        //    registers of this tile to the compact tail (segment row W + cl).
-        //    Stores are predicated per register so that no array is indexed
-        //    at run time.
-        if (own && moved) {
-          const int to = p.W + un.cl, rt = to & (kTile - 1);
-          uint8_t* kt = p.k_pool + (sb + (to - rt)) * (int64_t)RB;
-          uint8_t* vt = p.v_pool + (sb + (to - rt)) * (int64_t)RB;
-          const int rs = new_row & (kTile - 1);
-          const int m_r = (rs >> 2) & 3, g_r = ((rs >> 4) << 2) | (rs & 3);
-#pragma unroll
-          for (int m = 0; m < 4; ++m)   // lane kg holds chunks kg + 4j of row rs
-            if (m == m_r && g == g_r) {
-#pragma unroll
-              for (int j = 0; j < KL; ++j)
-                *reinterpret_cast<u32x4*>(kt + k_chunk_offset(rt, kg + 4 * j, RB)) = kr[m][j];
-            }
-          if (kg == (rs >> 4)) {        // lane g holds column 16nt + g of rows 16kg..16kg+15
-            const int jv = VL == 1 ? 0 : (rs & 15) >> 3;          // which 16-byte load
-            const int bi = (rs & (16 / VL - 1)) * E;              // byte inside it
-#pragma unroll
-            for (int j = 0; j < VL; ++j)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (j == jv && q == (bi >> 2)) {
-#pragma unroll
-                  for (int nt = 0; nt < NT; ++nt) {
-                    const uint32_t wd = vr[nt][j][q] >> (8 * (bi & 3));
-                    const int64_t o = (int64_t)((16 * nt + g) * kTile + rt) * E;
-                    if (FP8)
-                      vt[o] = (uint8_t)wd;
-                    else
-                      *reinterpret_cast<uint16_t*>(vt + o) = (uint16_t)wd;
-                  }
-                }
-          }
+        if (owner_unit && wave == 0 && first_tile) {   // while V is still in flight
+          new_token(kc, vc);
+          nt_done = true;
         }
+
+        // -- decode step: the leaving token's row is masked unless it moves
+        //    to the compact tail; tested after QK, so that nothing before the
+        //    tile loads waits for the keep bit
+        __asm__ volatile("" : "+v"(rko));   // keeps the test from moving up
+        const bool moved_t = own && leaving && rko != 0 && un.cl < un.cap &&
+                             sb + p.W + un.cl < p.pool_rows;
+        const int mrow = (own && leaving && !moved_t) ? (new_row & (kTile - 1)) : -1;
 
         // -- online softmax over this tile; lane (g, kg) owns tokens 16kg + 4m + r
         float z[4][4];
@@ -606,90 +639,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
           }
         }
         first_tile = false;
-
-      }
-
-      // -- decode step, owner wave: the new token's (logit, value) pair joins
-      //    the running softmax state, then its row is written
-      if (own) {
-        // keeps the work on the new token (loop-invariant) from being hoisted
-        // above the tile loads, where it would wait for k_new / v_new
-        __asm__ volatile("" : "+v"(nk), "+v"(nv));
-        const int d0n = EPL * lane;
-        float kd[EPL], vd[EPL];
-        uint32_t kc = 0, vc = 0;   // stored bytes of this lane's elements
-        const float kinv = FP8 ? fp8_inv_scale(un.ka) : 1.0f;
-        const float vinv = FP8 ? fp8_inv_scale(un.va) : 1.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const uint32_t kb = (nk >> (16 * e)) & 0xFFFFu, vb = (nv >> (16 * e)) & 0xFFFFu;
-          if (FP8) {
-            const uint32_t kq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv));
-            const uint32_t vq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
-            kd[e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kq, 1.0f, false)[0];
-            vd[e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vq, 1.0f, false)[0];
-            kc |= kq << (8 * e);
-            vc |= vq << (8 * e);
-          } else {
-            kd[e] = bf16_bits_to_f32(kb);
-            vd[e] = bf16_bits_to_f32(vb);
-            kc |= kb << (16 * e);
-            vc |= vb << (16 * e);
-          }
-        }
-        float* sn = reinterpret_cast<float*>(s_new);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          sn[d0n + e] = kd[e];
-          sn[D + d0n + e] = vd[e];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        float dot = 0.0f;
-#pragma unroll
-        for (int s = 0; s < NK; ++s) {
-          const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
-          const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dot = fmaf((float)qop[s][e], a[e], dot);
-            dot = fmaf((float)qop[s][4 + e], c[e], dot);
-          }
-        }
-        dot = sum_xor32(sum_xor16(dot));
-        const float zn = dot * c1;
-        const float m_new = fmaxf(m_run, zn);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        const float pn = __builtin_amdgcn_exp2f(zn - m_use);
-        l_run = l_run * alpha + (kg == 0 ? pn : 0.0f);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = acc[nt] * alpha + pn * s_new[D / 4 + 4 * nt + kg];
-        m_run = m_new;
-        first_tile = false;
-
-        // every load of this wave (the ring row included) has completed
-        __builtin_amdgcn_s_waitcnt(0);
-        const int rn = new_row & (kTile - 1);
-        uint8_t* kt = p.k_pool + (sb + (new_row - rn)) * (int64_t)RB;
-        uint8_t* vt = p.v_pool + (sb + (new_row - rn)) * (int64_t)RB;
-        const int kb0 = d0n * E;   // byte of this lane's first element in the row
-        uint8_t* kdst = kt + k_chunk_offset(rn, kb0 >> 4, RB) + (kb0 & 15);
-        if (EPL * E == 4)
-          *reinterpret_cast<uint32_t*>(kdst) = kc;
-        else if (EPL * E == 2)
-          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
-        else
-          *kdst = (uint8_t)kc;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          if (FP8)
-            vt[(d0n + e) * kTile + rn] = (uint8_t)(vc >> (8 * e));
-          else
-            reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rn] = (uint16_t)(vc >> (16 * e));
-        }
       }
     }
+
+    if (owner_unit && wave == 0 && !nt_done) new_token(kc, vc);   // wave 0 had no tile
 
     // decode step: the keep bit again, for the segment's metadata (back
     // before it is needed, after the combine or the merge)
@@ -704,6 +657,55 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
     __syncthreads();
+
+    // ---- decode step, the unit holding the new token's tile: wave 0
+    // copies the leaving token's row to the compact tail if it moves and
+    // writes the new row; every tile load of the workgroup has completed
+    // (barrier above)
+    if (owner_unit && wave == 0) {
+      {
+        const int d0n = EPL * lane;
+        // the leaving token's row (ring row P mod W) moves to compact row
+        // W + cl if it is kept; read back from the pool (this wave's reads
+        // finish before the new row is written over it)
+        const int rs = new_row & (kTile - 1);
+        uint8_t* kt = p.k_pool + (sb + (new_row - rs)) * (int64_t)RB;
+        uint8_t* vt = p.v_pool + (sb + (new_row - rs)) * (int64_t)RB;
+        const bool moved = leaving && rkc != 0 && un.cl < un.cap && sb + p.W + un.cl < p.pool_rows;
+        if (moved) {   // from the copy read at the start of the unit
+          const int to = p.W + un.cl, rt = to & (kTile - 1);
+          uint8_t* kd = p.k_pool + (sb + (to - rt)) * (int64_t)RB;
+          uint8_t* vd = p.v_pool + (sb + (to - rt)) * (int64_t)RB;
+          constexpr int KC = RB / 16;   // 16-byte chunks per K row
+          if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            if (FP8)
+              vd[(d0n + e) * kTile + rt] = (uint8_t)(ox >> (16 * e));
+            else
+              reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)(ox >> (16 * e));
+          }
+        }
+        // the new row goes over the ring row: the tiles read its old bytes
+        // before the barrier above, and the copy above used the ones read at
+        // the start of the unit (unused, and harmless, if it did not move)
+        const int kb0 = d0n * E;   // byte of this lane's first element in the row
+        uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
+        if (EPL * E == 4)
+          *reinterpret_cast<uint32_t*>(kdst) = kc;
+        else if (EPL * E == 2)
+          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
+        else
+          *kdst = (uint8_t)kc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (FP8)
+            vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
+          else
+            reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
+        }
+      }
+    }
     // decode step, single-unit segment: every wave of the workgroup has read
     // the segment's metadata (the owner's keep bit included)
     int seq_prev = -1;
@@ -730,6 +732,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
           O += f * s_o[ww][gg][d4];
           L += f * s_l[ww][gg];
         }
+      }
+      if (owner_unit) {   // decode step: the new token's (logit, value) pair
+        const float zn = s_zn[gg];
+        const float M2 = fmaxf(M, zn);
+        const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - M2);
+        const float pn = __builtin_amdgcn_exp2f(zn - M2);
+        O = O * a + pn * s_new[D / 4 + d4];
+        L = L * a + pn;
+        M = M2;
       }
       if (U == 1) {
         write_final4(p, b, h, gg, d4, D, M, L, O, sv);
