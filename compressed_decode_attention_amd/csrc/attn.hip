@@ -655,7 +655,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       s_l[wave][g] = l_run;
     }
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
+    for (int nt = 0; nt < NT; ++nt)   // columns g >= G hold no query row
+      if (g < G) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
     __syncthreads();
 
     // ---- decode step, the unit holding the new token's tile: wave 0
