@@ -43,18 +43,23 @@ def trace(stats_csv: str, command: str) -> None:
               f"{float(r['Percentage']):.1f}% |")
 
 
-def _mean(path: str, pat: str) -> dict:
+def _mean(path: str, pats: tuple) -> dict:
     v = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
-        if pat in r["Kernel_Name"]:
+        if any(q in r["Kernel_Name"] for q in pats):
             v[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return {k: sum(x) / len(x) for k, x in v.items()}
 
 
+# the device-to-device copy of `bench.py --copy-calibration` (the runtime's
+# blit kernel, or torch's elementwise copy, depending on the build)
+COPY_KERNELS = ("copyBuffer", "direct_copy")
+
+
 def traffic(cf: str, cw: str, bf: str, bw: str, commands: list[str]) -> None:
-    fcal = COPY_KIB / list(_mean(cf, "direct_copy").values())[0]
-    wcal = COPY_KIB / list(_mean(cw, "direct_copy").values())[0]
-    fetch, write = _mean(bf, "cda"), _mean(bw, "cda")
+    fcal = COPY_KIB / list(_mean(cf, COPY_KERNELS).values())[0]
+    wcal = COPY_KIB / list(_mean(cw, COPY_KERNELS).values())[0]
+    fetch, write = _mean(bf, ("cda",)), _mean(bw, ("cda",))
     print("# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)\n")
     print("Commands (from the repository root), one counter per run:\n\n```")
     for c in commands:
