@@ -89,7 +89,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMergeBatch = 8;   // partials loaded per round trip in the merge
+constexpr int kMergeBatch = 4;   // partials loaded per round trip in the merge
 constexpr int kXcdGroups = 8;    // segment groups of the XCD-local mode
 constexpr int kCounterStride = 32;   // ints between counters: one 128-byte line each
 
@@ -151,7 +151,7 @@ __device__ __forceinline__ void write_final4(const AttnParams& p, int b, int h, 
 }
 
 // Partials: XCD-local mode keeps them in the shared L2 of the XCD (plain
-// stores; loads that skip the CU's L1); otherwise they are device-coherent
+// 16-byte stores and loads); otherwise they are device-coherent
 // (agent-scope stores and loads, one per dword).
 template <bool XL>
 __device__ __forceinline__ void store_part4(float* a, f32x4 v) {
@@ -169,6 +169,9 @@ __device__ __forceinline__ float load_part1(const float* a) {
 }
 template <bool XL>
 __device__ __forceinline__ f32x4 load_part4(const float* a) {
+  // XCD-local: one 16-byte load (the merging CU has not read these lines
+  // before in this kernel, so its L1 holds no stale copy)
+  if (XL) return *reinterpret_cast<const f32x4*>(a);
   return f32x4{load_part1<XL>(a), load_part1<XL>(a + 1), load_part1<XL>(a + 2),
                load_part1<XL>(a + 3)};
 }
