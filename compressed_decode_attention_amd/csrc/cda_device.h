@@ -71,6 +71,21 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
   return sign | q;
 }
 
+// The same encode of two values (codes in bits 0-7 and 8-15) with the
+// gfx950 conversion instruction: inputs clamped to [-448, 448] first (the
+// instruction alone gives NaN for magnitudes that round past 448), NaN
+// mapped to 0x7F with its sign after it (the instruction does not keep the
+// sign of every NaN).  Equal to e4m3_from_f32 on every binary32 input, in
+// the default round-to-nearest-even mode.
+__device__ __forceinline__ uint32_t e4m3x2_from_f32(float a, float b) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                                                         __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f),
+                                                         0, false) & 0xFFFFu;
+  if (__builtin_isnan(a)) w = (w & 0xFF00u) | 0x7Fu | ((__float_as_uint(a) >> 24) & 0x80u);
+  if (__builtin_isnan(b)) w = (w & 0x00FFu) | ((0x7Fu | ((__float_as_uint(b) >> 24) & 0x80u)) << 8);
+  return w;
+}
+
 // Dequantisation and quantisation factors from a per-head absmax.
 __device__ __forceinline__ float fp8_scale(float amax) {
   return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(amax, 448.0f) : 1.0f;

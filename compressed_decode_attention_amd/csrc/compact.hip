@@ -5,11 +5,12 @@
 //   count_kernel     keep mask -> per-segment kept count, optional dst map
 //   seg_scan_kernel  aligned segment sizes -> seg_base (exclusive prefix sum)
 //   amax_kernel      per-segment absmax of the stored prefill K and V (FP8)
-//   pack_kernel      stored prefill rows -> pool rows (BF16 copy / FP8 encode)
+//   pack_kernel      stored prefill rows -> pool tiles (BF16 copy / FP8 encode)
 //   append_kernel    one decode step: ring exit -> compact tail, new token -> ring
 //
 // All of these run once per prefill or move at most one row per segment per
 // step; the decode hot loop is the attention kernel.
+#include <algorithm>
 #include <type_traits>
 
 #include "cda_device.h"
@@ -225,6 +226,7 @@ struct PackParams {
   int64_t keep_ld;
   int T, W, Hkv, D;
   const int64_t* seg_base;
+  const int32_t* comp_len;
   int64_t pool_rows;
   uint8_t* k_pool;
   uint8_t* v_pool;
@@ -240,112 +242,194 @@ __device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
   return (row / kTile) * kTile * D + (int64_t)d * kTile + (row % kTile);
 }
 
-// Store 8 consecutive elements (d0 .. d0+7) of one row: K row-major, V into
-// its column-major tile; FP8 encodes x * inv.
-template <bool FP8>
-__device__ __forceinline__ void store_row8(uint8_t* k_pool, uint8_t* v_pool, int64_t r, int d0,
-                                           int D, u32x4 kin, u32x4 vin, float kinv, float vinv) {
-  if (FP8) {
-    uint32_t kc[2] = {0, 0};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t kb = (kin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t vb = (vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      kc[j >> 2] |= e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv)) << (8 * (j & 3));
-      v_pool[v_elem(r, d0 + j, D)] = (uint8_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
-    }
-    *reinterpret_cast<u32x2*>(k_pool + k_elem8(r, d0, D, 1)) = u32x2{kc[0], kc[1]};
-  } else {
-    *reinterpret_cast<u32x4*>(k_pool + k_elem8(r, d0, D, 2)) = kin;
-    uint16_t* vp = reinterpret_cast<uint16_t*>(v_pool);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      vp[v_elem(r, d0 + j, D)] = (uint16_t)((vin[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
-  }
+// Row (inside its 64-row tile) of the 16-byte K pool chunk at byte offset
+// `off` of the tile: the inverse of k_chunk_offset.
+__device__ __forceinline__ int k_chunk_row(int off, int rb) {
+  const int blk = off >> 10, m = blk / (rb >> 6), g = (off >> 4) & 15;
+  return ((g >> 2) << 4) | (m << 2) | (g & 3);
 }
 
-// Workgroup (segment i, chunk c) handles prefill positions [256c, 256c+256).
-template <bool FP8>
+// Workgroup (segment i, y) writes the 64-row pool tiles j = y, y + gridDim.y,
+// ... of segment i that hold ring rows or stored rows, one whole tile at a
+// time: it finds the source position of each row of the tile (ring row r:
+// the position p of the window with p mod W = r; compact row W + c: the
+// c-th kept older position, by a scan of the keep row), loads the BF16 rows
+// (each 64-lane load is whole rows), encodes them into LDS images of the
+// K tile (chunk-permuted rows) and the V tile (column-major), and stores
+// both with 16-byte writes.  Rows of the tile with no source are zero.
+template <bool FP8, int D>
 __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
-  constexpr int kPre = 32;   // keep bytes per thread of the prefix count
+  constexpr int E = FP8 ? 1 : 2;            // bytes per stored element
+  constexpr int RB = D * E;                 // pool bytes per row
+  constexpr int CPR = D / 8;                // 8-element input chunks per row
+  constexpr int RPI = 64 / CPR;             // rows per 64-lane load
+  constexpr int NI = kTile / (RPI * (kBlock / 64));   // loads per wave and tensor
+  constexpr int VS = FP8 ? 68 : 132;        // LDS bytes per V column: 64 rows + pad
+  constexpr int kScan = 32;                 // keep bytes per thread per scan pass
+  __shared__ int s_src[kTile];
   __shared__ int smem[4];
-  __shared__ int s_pos[kBlock], s_dst[kBlock];
-  const int i = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kTile * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[D * VS];
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
-  const int T = p.T, W = p.W, D = p.D;
-  const uint8_t* row = p.keep + (int64_t)i * p.keep_ld;
-  const int ncand = T - W > 0 ? T - W : 0;
-  const int pp = c * kBlock + tid;
-
-  // kept older positions before this chunk (up to 8192 bytes per pass, one
-  // round trip), and this thread's own keep byte
-  const int lim = min(c * kBlock, ncand);
-  const int own = (pp < ncand) ? row[pp] : 0;
-  int before = 0;
-  for (int q0 = tid * kPre; q0 < lim; q0 += kBlock * kPre) {
-    uint8_t kb[kPre];
-#pragma unroll
-    for (int j = 0; j < kPre; ++j) kb[j] = row[min(q0 + j, lim - 1)];
-#pragma unroll
-    for (int j = 0; j < kPre; ++j) before += (q0 + j < lim) && kb[j] != 0;
+  const int T = p.T, W = p.W;
+  const int ncand = T - W > 0 ? T - W : 0;  // positions older than the window
+  const int nring = min(W, T);
+  const uint8_t* krow = p.keep + (int64_t)i * p.keep_ld;
+  const bool row16 = (reinterpret_cast<uintptr_t>(krow) & 15) == 0;   // 16-byte keep loads
+  // this thread's keep bytes of the first scan pass of the first tile, read
+  // before the segment's metadata (one round trip for both)
+  u32x4 pre0 = u32x4{0, 0, 0, 0}, pre1 = u32x4{0, 0, 0, 0};
+  const bool pre = row16 && (int)blockIdx.y * kTile + kTile > W && tid * kScan + kScan <= ncand;
+  if (pre) {
+    pre0 = *reinterpret_cast<const u32x4*>(krow + tid * kScan);
+    pre1 = *reinterpret_cast<const u32x4*>(krow + tid * kScan + 16);
   }
-  before = block_sum(before, smem);
-
-  const int flag = (pp < ncand) && own != 0;
-  int dummy;
-  const int rank = block_exclusive_scan(flag, &dummy, smem);
-  int stored = 0, dst = -1;
-  if (pp < T) {
-    if (pp >= ncand) {
-      dst = pp % W;
-      stored = 1;
-    } else if (flag) {
-      dst = W + before + rank;
-      stored = 1;
-    }
-  }
-  if (stored && dst < W) p.ring_keep[(int64_t)i * W + dst] = row[pp] != 0;
-  if (c == 0) {
-    for (int r = T + tid; r < W; r += kBlock) p.ring_keep[(int64_t)i * W + r] = 0;
-    if (h == 0 && tid == 0) p.pos[b] = T;
-  }
-  int nst;
-  const int slot = block_exclusive_scan(stored, &nst, smem);
-  if (stored) {
-    s_pos[slot] = pp;
-    s_dst[slot] = dst;
-  }
-  __syncthreads();
-
+  const int64_t sb = p.seg_base[i];
+  const int64_t alloc = p.seg_base[i + 1] - sb;
+  const int cl = min(max(p.comp_len[i], 0), ncand);   // from COUNT
+  // tiles holding ring rows or stored rows, inside the segment's rows
+  const int64_t rows = min((int64_t)max(nring + cl, W), alloc);
+  const int ntiles = (int)((rows + kTile - 1) / kTile);
   float kinv = 1.0f, vinv = 1.0f;
   if (FP8) {
     kinv = fp8_inv_scale(p.k_amax[i]);
     vinv = fp8_inv_scale(p.v_amax[i]);
   }
-  const int64_t base = p.seg_base[i];
-  const int lpr = D / 8;
-  const int rows_per_pass = kBlock / lpr;
-  const int d0 = (tid % lpr) * 8;
-  for (int e0 = tid / lpr; e0 < nst; e0 += 4 * rows_per_pass) {
-    u32x4 kin[4], vin[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = min(e0 + j * rows_per_pass, nst - 1);
-      const int64_t off = (int64_t)b * p.sb + (int64_t)s_pos[e] * p.st + (int64_t)h * p.sh + d0;
-      kin[j] = *reinterpret_cast<const u32x4*>(p.k + off);
-      vin[j] = *reinterpret_cast<const u32x4*>(p.v + off);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + j * rows_per_pass;
-      if (e >= nst) continue;
-      const int64_t r = base + s_dst[e];
-      if (r < 0 || r >= p.pool_rows) {
-        if (d0 == 0) atomicOr(p.err, CDA_DEVERR_POOL);
-        continue;
+  if (blockIdx.y == 0 && h == 0 && tid == 0) p.pos[b] = T;
+
+  for (int j = blockIdx.y; j < ntiles; j += gridDim.y) {
+    const int r0 = j * kTile;
+    // ---- source position of each row: ring rows here, compact rows below
+    if (tid < kTile) {
+      const int r = r0 + tid;
+      int src = -1;
+      if (r < W) {
+        if (T >= W) {
+          const int base = T - W;             // window: positions base .. T-1
+          src = base + (r - base % W + W) % W;
+        } else if (r < T) {
+          src = r;
+        }
+        p.ring_keep[(int64_t)i * W + r] = (uint8_t)(src >= 0 && krow[src] != 0);
       }
-      store_row8<FP8>(p.k_pool, p.v_pool, r, d0, D, kin[j], vin[j], kinv, vinv);
+      s_src[tid] = src;
     }
+    const int c_lo = max(r0 - W, 0), c_hi = r0 + kTile - W;   // compact ranks of the tile
+    if (c_hi > 0 && cl > c_lo) {
+      // the kept older positions of ranks [c_lo, c_hi), by a running scan of
+      // the keep row (its barriers also order the ring entries above)
+      int carry = 0;
+      for (int q0 = 0; q0 < ncand && carry < c_hi; q0 += kBlock * kScan) {
+        const int pp = q0 + tid * kScan;
+        uint32_t flags = 0;   // bit e: position pp + e is kept
+        if (row16 && pp + kScan <= ncand) {
+          const bool use_pre = pre && q0 == 0 && j == (int)blockIdx.y;
+          const u32x4 x0 = use_pre ? pre0 : *reinterpret_cast<const u32x4*>(krow + pp);
+          const u32x4 x1 = use_pre ? pre1 : *reinterpret_cast<const u32x4*>(krow + pp + 16);
+#pragma unroll
+          for (int e = 0; e < kScan; ++e) {
+            const uint32_t wd = e < 16 ? x0[e >> 2] : x1[(e - 16) >> 2];
+            flags |= (uint32_t)(((wd >> (8 * (e & 3))) & 0xFFu) != 0u) << e;
+          }
+        } else {
+          uint8_t kb[kScan];
+#pragma unroll
+          for (int e = 0; e < kScan; ++e) kb[e] = krow[min(pp + e, ncand - 1)];
+#pragma unroll
+          for (int e = 0; e < kScan; ++e) flags |= (uint32_t)((pp + e < ncand) && kb[e] != 0) << e;
+        }
+        const int cnt = __builtin_popcount(flags);
+        int total;
+        int rank = block_exclusive_scan(cnt, &total, smem) + carry;
+        if (rank < c_hi && rank + cnt > c_lo) {
+          for (uint32_t f = flags; f != 0u; f &= f - 1u, ++rank)
+            if (rank >= c_lo && rank < c_hi) s_src[W + rank - r0] = pp + __builtin_ctz(f);
+        }
+        carry += total;
+      }
+    }
+    __syncthreads();
+    // the rows with a source are a prefix of the tile (ring rows fill from
+    // row 0, compact rows follow them in rank order), so row 0 has one if
+    // any row does
+    const int any = s_src[0];
+
+    // ---- loads: wave w, load k covers rows (w NI + k) RPI .. + RPI - 1,
+    // lane = (row, 8-element chunk); rows with no source read the tile's
+    // source row `any` (no extra HBM traffic) and are zeroed below
+    const int cc = lane % CPR, d0 = 8 * cc;
+    u32x4 kin[NI], vin[NI];
+    int rr[NI];
+    bool has[NI];
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      rr[k] = (wave * NI + k) * RPI + lane / CPR;
+      const int src = s_src[rr[k]];
+      has[k] = src >= 0;
+      kin[k] = u32x4{0, 0, 0, 0};
+      vin[k] = u32x4{0, 0, 0, 0};
+      if (any >= 0) {
+        const int64_t off = (int64_t)b * p.sb + (int64_t)(has[k] ? src : any) * p.st +
+                            (int64_t)h * p.sh + d0;
+        kin[k] = *reinterpret_cast<const u32x4*>(p.k + off);
+        vin[k] = *reinterpret_cast<const u32x4*>(p.v + off);
+      }
+    }
+    // ---- encode into the LDS tile images
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int r = rr[k];
+      const u32x4 kx = has[k] ? kin[k] : u32x4{0, 0, 0, 0};
+      const u32x4 vx = has[k] ? vin[k] : u32x4{0, 0, 0, 0};
+      if (FP8) {
+        uint32_t kc[2] = {0, 0}, vc[2] = {0, 0};
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {   // elements 2 w2, 2 w2 + 1
+          const float k0 = __fmul_rn(__uint_as_float(kx[w2] << 16), kinv);
+          const float k1 = __fmul_rn(__uint_as_float(kx[w2] & 0xFFFF0000u), kinv);
+          const float v0 = __fmul_rn(__uint_as_float(vx[w2] << 16), vinv);
+          const float v1 = __fmul_rn(__uint_as_float(vx[w2] & 0xFFFF0000u), vinv);
+          kc[w2 >> 1] |= e4m3x2_from_f32(k0, k1) << (16 * (w2 & 1));
+          vc[w2 >> 1] |= e4m3x2_from_f32(v0, v1) << (16 * (w2 & 1));
+        }
+        *reinterpret_cast<u32x2*>(s_k + k_chunk_offset(r, d0 >> 4, RB) + (d0 & 15)) = u32x2{kc[0], kc[1]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s_v[(d0 + e) * VS + r] = (uint8_t)(vc[e >> 2] >> (8 * (e & 3)));
+      } else {
+        *reinterpret_cast<u32x4*>(s_k + k_chunk_offset(r, cc, RB)) = kx;
+        uint16_t* v16 = reinterpret_cast<uint16_t*>(s_v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v16[(d0 + e) * (VS / 2) + r] = (uint16_t)((vx[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      }
+    }
+    __syncthreads();
+
+    // ---- stores: both tiles as 16-byte chunks; a tile that reaches past
+    // pool_rows (a pool smaller than seg_base[B*Hkv]) keeps to the rows
+    // inside it and flags the rows with data outside it
+    const int64_t in_pool = p.pool_rows - (sb + r0);   // rows of the tile inside the pool
+    uint8_t* kt = p.k_pool + (sb + r0) * (int64_t)RB;
+    uint8_t* vt = p.v_pool + (sb + r0) * (int64_t)RB;
+    for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
+      if (in_pool >= kTile || k_chunk_row(ch * 16, RB) < in_pool)
+        *reinterpret_cast<u32x4*>(kt + ch * 16) = *reinterpret_cast<const u32x4*>(s_k + ch * 16);
+      // V: chunk ch is rows r .. r + 16/E - 1 of column d
+      const int d = ch / (4 * E), r = (ch % (4 * E)) * (16 / E);
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * VS + r * E);
+      const u32x4 vv = u32x4{src[0], src[1], src[2], src[3]};
+      if (in_pool >= kTile || r + 16 / E <= in_pool) {
+        *reinterpret_cast<u32x4*>(vt + ch * 16) = vv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((r * E + e) / E < in_pool) vt[ch * 16 + e] = (uint8_t)(vv[e >> 2] >> (8 * (e & 3)));
+      }
+    }
+    if (in_pool < kTile && tid < kTile && tid >= in_pool && s_src[tid] >= 0)
+      atomicOr(p.err, CDA_DEVERR_POOL);
+    __syncthreads();   // the next tile reuses s_src and the LDS images
   }
 }
 
@@ -493,6 +577,8 @@ hipError_t launch_count(const cda_kv_cache& c, const cda_compact_args& a, hipStr
   return hipGetLastError();
 }
 
+constexpr int kPackY = 32;   // workgroups per segment of the pack kernel
+
 hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
   const int nh = c.B * c.Hkv;
   if (nh == 0) return hipGetLastError();
@@ -518,6 +604,7 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   p.Hkv = c.Hkv;
   p.D = c.D;
   p.seg_base = c.seg_base;
+  p.comp_len = c.comp_len;
   p.pool_rows = c.pool_rows;
   p.k_pool = static_cast<uint8_t*>(c.k_pool);
   p.v_pool = static_cast<uint8_t*>(c.v_pool);
@@ -526,10 +613,17 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   p.k_amax = c.k_amax;
   p.v_amax = c.v_amax;
   p.err = c.err;
-  if (fp8)
-    pack_kernel<true><<<grid, kBlock, 0, s>>>(p);
-  else
-    pack_kernel<false><<<grid, kBlock, 0, s>>>(p);
+  // tiles of a segment: at most ceil(max(T, W) / 64); workgroups take every
+  // kPackY-th of them
+  const int max_tiles = (int)((std::max<int64_t>(a.T, c.W) + kTile - 1) / kTile);
+  const dim3 pgrid(nh, std::max(1, std::min(max_tiles, kPackY)));
+  if (fp8) {
+    if (c.D == 64) pack_kernel<true, 64><<<pgrid, kBlock, 0, s>>>(p);
+    else pack_kernel<true, 128><<<pgrid, kBlock, 0, s>>>(p);
+  } else {
+    if (c.D == 64) pack_kernel<false, 64><<<pgrid, kBlock, 0, s>>>(p);
+    else pack_kernel<false, 128><<<pgrid, kBlock, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
