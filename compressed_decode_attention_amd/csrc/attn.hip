@@ -212,10 +212,11 @@ struct StepRows {
   int n_pre;     // rows holding data before the append
   int new_row;   // segment row that receives the new token (< W + cap), -1 if dropped
 };
-__device__ __forceinline__ StepRows step_rows(int W, int P, int cl, int cap, int kn) {
+// ring_slot = P mod W (W > 0).
+__device__ __forceinline__ StepRows step_rows(int W, int P, int ring_slot, int cl, int cap, int kn) {
   StepRows s;
   s.n_pre = min(W, P) + cl;
-  s.new_row = W > 0 ? P % W : ((kn && cl < cap) ? cl : -1);
+  s.new_row = W > 0 ? ring_slot : ((kn && cl < cap) ? cl : -1);
   return s;
 }
 
@@ -379,8 +380,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 
     // ---- decode step: rows with data, the new token's row and its tile
     int n = un.n, new_row = -1, t_own = -1;
+    const int ring_slot = (APP && p.W > 0) ? un.P % p.W : 0;   // ring row of P
     if (APP) {
-      const StepRows st = step_rows(p.W, un.P, un.cl, un.cap, un.kn);
+      const StepRows st = step_rows(p.W, un.P, ring_slot, un.cl, un.cap, un.kn);
       n = st.n_pre;
       if (st.new_row >= 0 && st.new_row < in_pool) {
         new_row = st.new_row;
@@ -393,8 +395,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
     // needed, and tested only after the loads that must not wait for it.
     const bool leaving = APP && p.W > 0 && un.P >= p.W;
-    const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + un.P % max(p.W, 1)
-                                        : p.keep_new + i)
+    const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + ring_slot : p.keep_new + i)
                              : nullptr;
     // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per
     // k-step.  Columns g >= G repeat row 0: their results land in rows of the
@@ -422,7 +423,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     // It also reads the ring row the new token replaces (the leaving
     // token's row: 16-byte K chunk `lane`, V elements EPL*lane..), in case
     // it moves to the compact tail.
-    uint32_t nk = 0, nv = 0, ox = 0;
+    uint32_t nk = 0, nv = 0;
+    uint32_t ox[EPL];   // kept apart: combining them would wait for the loads here
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ox[e] = 0;
     u32x4 okx = u32x4{0, 0, 0, 0};
     if (owner_unit && wave == 0) {
       const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
@@ -439,9 +443,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
-        ox |= (FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
-                   : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs])
-              << (16 * e);
+        ox[e] = FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
+                    : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs];
     }
 
     bool first_tile = true;
@@ -453,8 +456,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     auto new_token = [&](uint32_t& kc, uint32_t& vc) {
       __asm__ volatile("" : "+v"(nk), "+v"(nv));   // keeps this work below the tile loads
       const int d0n = EPL * lane;
-      const float kinv = FP8 ? fp8_inv_scale(un.ka) : 1.0f;
-      const float vinv = FP8 ? fp8_inv_scale(un.va) : 1.0f;
+      float ka = un.ka, va = un.va;
+      __asm__ volatile("" : "+v"(ka), "+v"(va));   // the divisions stay here too
+      const float kinv = FP8 ? fp8_inv_scale(ka) : 1.0f;
+      const float vinv = FP8 ? fp8_inv_scale(va) : 1.0f;
       kc = 0;
       vc = 0;
       float* sn = reinterpret_cast<float*>(s_new);
@@ -482,10 +487,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       for (int s = 0; s < NK; ++s) {
         const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
         const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
+        // an opaque copy: converted here, not hoisted above the tile loads
+        // (where converting it would wait for the q loads)
+        bf16x8 qs = qop[s];
+        __asm__ volatile("" : "+v"(qs));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          dot = fmaf((float)qop[s][e], a[e], dot);
-          dot = fmaf((float)qop[s][4 + e], c[e], dot);
+          dot = fmaf((float)qs[e], a[e], dot);
+          dot = fmaf((float)qs[4 + e], c[e], dot);
         }
       }
       dot = sum_xor32(sum_xor16(dot));
@@ -685,9 +694,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
             if (FP8)
-              vd[(d0n + e) * kTile + rt] = (uint8_t)(ox >> (16 * e));
+              vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
             else
-              reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)(ox >> (16 * e));
+              reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
           }
         }
         // the new row goes over the ring row: the tiles read its old bytes
