@@ -152,8 +152,9 @@ typedef struct cda_compact_args {
  * CDA_OP_PACK: after COUNT (same keep, T), writes every stored prefill row
  *   (the W most recent positions and every kept older one) to its pool row,
  *   fills ring_keep, sets pos[b] = T and, for FP8 with scale_mode 0,
- *   computes k_amax/v_amax first.  Rows the layout leaves unused are not
- *   written.
+ *   computes k_amax/v_amax first.  Pools are written in whole 64-row
+ *   tiles: unused rows inside a tile that holds ring or stored rows are set
+ *   to zero; tiles past them are not written.
  * CDA_OP_APPEND: one decode step: for each sequence b (P = pos[b]) and head,
  *   the token at P-W leaves the ring and, if its keep bit is set, is copied
  *   to compact row W + comp_len (comp_len += 1; CDA_DEVERR_CAPACITY if
