@@ -25,8 +25,9 @@ _LIB = os.path.join(_HERE, "liboracle_cda.so")
 _lock = threading.Lock()
 _lib = None
 
-BF16, FP8 = 0, 1
+BF16, FP8, FP4 = 0, 1, 2
 FP8_MAX = 448.0
+FP4_MAX = 6.0
 
 
 def build(force: bool = False) -> str:
@@ -53,6 +54,11 @@ def lib():
             L.orc_e4m3_decode.argtypes = [C.c_uint8]
             L.orc_e4m3_decode.restype = f64
             L.orc_scales_from_amax.argtypes = [f32, P, P]
+            L.orc_e2m1_encode.argtypes = [f32]
+            L.orc_e2m1_encode.restype = C.c_uint8
+            L.orc_e2m1_decode.argtypes = [C.c_uint8]
+            L.orc_e2m1_decode.restype = f64
+            L.orc_fp4_scales_from_amax.argtypes = [f32, P, P]
             L.orc_stored_count.argtypes = [P, i32, i32]
             L.orc_stored_count.restype = i64
             L.orc_prefill_layout.argtypes = [i32, i32, i32, i32, i32, i32, P, i64, P, P, P, P]
@@ -111,6 +117,21 @@ def scales_from_amax(amax: float):
     return s.value, inv.value
 
 
+def e2m1_encode(y: float) -> int:
+    """4-bit code (0..15) of the OCP MX FP4 E2M1 encoding of y."""
+    return int(lib().orc_e2m1_encode(float(y)))
+
+
+def e2m1_decode(code: int) -> float:
+    return float(lib().orc_e2m1_decode(int(code)))
+
+
+def fp4_scales_from_amax(amax: float):
+    s, inv = C.c_float(), C.c_float()
+    lib().orc_fp4_scales_from_amax(float(amax), C.byref(s), C.byref(inv))
+    return s.value, inv.value
+
+
 def stored_count(keep_row: np.ndarray, P: int, W: int) -> int:
     k = _u8(keep_row)
     return int(lib().orc_stored_count(_p(k), int(P), int(W)))
@@ -140,9 +161,9 @@ class OracleCache:
 
     def __init__(self, B, Hkv, D, W, kv_dtype, rows):
         self.B, self.Hkv, self.D, self.W, self.kv_dtype = B, Hkv, D, W, kv_dtype
-        esz = 2 if kv_dtype == BF16 else 1
-        self.k_pool = np.zeros((rows, D * esz), np.uint8)
-        self.v_pool = np.zeros((rows, D * esz), np.uint8)
+        rb = row_bytes(D, kv_dtype)
+        self.k_pool = np.zeros((rows, rb), np.uint8)
+        self.v_pool = np.zeros((rows, rb), np.uint8)
         nh = B * Hkv
         self.seg_base = np.zeros(nh + 1, np.int64)
         self.seg_cap = np.zeros(nh, np.int32)
@@ -186,7 +207,7 @@ def prefill_pack(k, v, keep, T: int, W: int, reserve: int, kv_dtype: int,
                  amax=None, align: int = 1) -> OracleCache:
     """Prefill compaction of one layer.  k, v: bf16 [B, >=T, Hkv, D] (only the
     first T positions are read); keep: [B, Hkv, >=T].  amax: optional
-    (k_amax, v_amax) to use instead of computing them (FP8)."""
+    (k_amax, v_amax) to use instead of computing them (FP8, FP4)."""
     kb, vb, kp = _bits(k), _bits(v), _u8(keep)
     B, Tt, Hkv, D = kb.shape
     lay = prefill_layout(kp, T, W, reserve, align)
@@ -252,8 +273,13 @@ def attention_head(q_row, k, v, keep, b: int, j: int, G: int, P: int, W: int,
 
 # ---------------------------------------------------------------- accounting
 
-def bytes_per_elem(kv_dtype: int) -> int:
-    return 2 if kv_dtype == BF16 else 1
+def bytes_per_elem(kv_dtype: int) -> float:
+    return {BF16: 2, FP8: 1, FP4: 0.5}[kv_dtype]
+
+
+def row_bytes(D: int, kv_dtype: int) -> int:
+    """Bytes of one stored row of D elements (FP4: two elements per byte)."""
+    return {BF16: 2 * D, FP8: D, FP4: D // 2}[kv_dtype]
 
 
 def dense_kv_bytes(layers: int, Hkv: int, D: int, tokens: int, elem_bytes: float) -> float:
@@ -264,8 +290,8 @@ def dense_kv_bytes(layers: int, Hkv: int, D: int, tokens: int, elem_bytes: float
 
 def compact_kv_bytes(stored_tokens: int, D: int, kv_dtype: int, heads: int) -> int:
     """Bytes the compact store holds: every stored token keeps K and V rows of
-    D elements, plus two f32 scales per head for FP8."""
-    b = int(stored_tokens) * 2 * D * bytes_per_elem(kv_dtype)
-    if kv_dtype == FP8:
+    D elements, plus two f32 scales per head for FP8 and FP4."""
+    b = int(stored_tokens) * 2 * row_bytes(D, kv_dtype)
+    if kv_dtype != BF16:
         b += 8 * int(heads)
     return b

@@ -21,6 +21,12 @@
  *   - Same page, summary bullets: FastDMS runs in BF16 and FP8.  FP8 is OCP
  *     E4M3FN (OCP 8-bit Floating Point specification, E4M3 encoding table),
  *     with one absmax scale per (sequence, KV head) for K and one for V.
+ *   - A 4-bit store (same page, memory table, the 4-bit vLLM row; PackKV
+ *     page, abstract: compressed KV decoded inside the products): the page
+ *     does not define its format.  Reading: the OCP Microscaling FP4 element
+ *     type E2M1 with the same per-(sequence, KV head) absmax scales as FP8,
+ *     two elements per byte (element d in the low nibble of byte d/2 when d
+ *     is even, the high nibble when odd).
  *   - Attention: plain scaled-dot-product softmax attention of one query
  *     token over the stored set, in fp64, in position order; no blocking,
  *     no split, no reordering.
@@ -37,6 +43,13 @@
 
 #define ORC_BF16 0
 #define ORC_FP8 1
+#define ORC_FP4 2
+
+/* Bytes of one stored row of D elements. */
+static int64_t row_bytes(int D, int kv_dtype)
+{
+    return kv_dtype == ORC_BF16 ? 2 * (int64_t)D : kv_dtype == ORC_FP8 ? D : D / 2;
+}
 
 /* ------------------------------------------------------------------ */
 /* Scalars                                                             */
@@ -100,6 +113,48 @@ double orc_e4m3_decode(uint8_t c)
 }
 
 /*
+ * OCP MX FP4 E2M1 encode, round-to-nearest-even, saturating.  Codes are
+ * sign | E(2 bits, bias 1) | M(1 bit); E = 1..3 stands for 2^(E-1) * (1 + M/2)
+ * (1, 1.5, 2, 3, 4, 6), E = 0 for M * 0.5 (0, 0.5).  The format has no
+ * infinity and no NaN.  Readings: magnitudes that round past 6 (and
+ * infinity) give +-6; NaN gives +-6 with the input's sign; the sign of zero
+ * and of values that round to zero is kept.  Returns the 4-bit code.
+ */
+uint8_t orc_e2m1_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x8 : 0x0;
+    if (isnan(y))
+        return sign | 0x7;
+    double a = fabs((double)y);
+    if (a >= 6.0)                     /* 6 and above (infinity too): +-6 */
+        return sign | 0x7;
+    if (a < 1.0) {
+        /* multiples of 0.5, rounded half to even: 2 is the code of 1.0 */
+        return sign | (uint8_t)rint(a * 2.0);
+    }
+    int k;
+    double f = frexp(a, &k);          /* a = f * 2^k, f in [0.5, 1) */
+    int e = k - 1;                    /* a = (2f) * 2^e, 2f in [1, 2) */
+    double m = rint((2.0 * f - 1.0) * 2.0);
+    if (m == 2.0) {                   /* rounded up to the next binade */
+        m = 0.0;
+        e += 1;
+    }
+    int code = ((e + 1) << 1) | (int)m;
+    if (code > 0x7)
+        code = 0x7;
+    return sign | (uint8_t)code;
+}
+
+/* OCP MX FP4 E2M1 decode of a 4-bit code (exact). */
+double orc_e2m1_decode(uint8_t c)
+{
+    int s = (c >> 3) & 1, E = (c >> 1) & 3, M = c & 1;
+    double v = (E == 0) ? 0.5 * M : ldexp(1.0 + 0.5 * M, E - 1);
+    return s ? -v : v;
+}
+
+/*
  * Per-head FP8 scales from an absmax a.  s dequantises (x ~ s * code), inv
  * quantises (code = enc(x * inv)).  Reading: both are single f32 divisions of
  * a and the format's largest finite value 448; a head whose absmax is zero
@@ -114,6 +169,29 @@ void orc_scales_from_amax(float amax, float *s, float *inv)
         *s = 1.0f;
         *inv = 1.0f;
     }
+}
+
+/* The same for the 4-bit store, whose largest magnitude is 6. */
+void orc_fp4_scales_from_amax(float amax, float *s, float *inv)
+{
+    if (amax > 0.0f && isfinite(amax)) {
+        *s = amax / 6.0f;
+        *inv = 6.0f / amax;
+    } else {
+        *s = 1.0f;
+        *inv = 1.0f;
+    }
+}
+
+/* Scales of a head for a quantised store (FP8 or FP4); 1 for BF16. */
+static void head_scales(int kv_dtype, float amax, float *s, float *inv)
+{
+    *s = 1.0f;
+    *inv = 1.0f;
+    if (kv_dtype == ORC_FP8)
+        orc_scales_from_amax(amax, s, inv);
+    else if (kv_dtype == ORC_FP4)
+        orc_fp4_scales_from_amax(amax, s, inv);
 }
 
 /*
@@ -220,7 +298,8 @@ void orc_prefill_amax(int B, int Hkv, int D, int T, int W,
         }
 }
 
-/* Store one D-element row: BF16 bits verbatim, or FP8 codes of x * inv. */
+/* Store one D-element row: BF16 bits verbatim, or FP8 / FP4 codes of
+ * x * inv (FP4: two codes per byte, even element in the low nibble). */
 static int64_t store_row(int D, int kv_dtype, const uint16_t *src, float inv,
                          uint8_t *dst_row)
 {
@@ -229,11 +308,20 @@ static int64_t store_row(int D, int kv_dtype, const uint16_t *src, float inv,
         if (kv_dtype == ORC_BF16) {
             dst_row[2 * d] = (uint8_t)(src[d] & 0xFF);
             dst_row[2 * d + 1] = (uint8_t)(src[d] >> 8);
-        } else {
+        } else if (kv_dtype == ORC_FP8) {
             float y = bf16_to_f32(src[d]) * inv;
             if (fabsf(y) > 448.0f)
                 ++sat;
             dst_row[d] = orc_e4m3_encode(y);
+        } else {
+            float y = bf16_to_f32(src[d]) * inv;
+            if (fabsf(y) > 6.0f)
+                ++sat;
+            uint8_t c = orc_e2m1_encode(y);
+            if (d % 2 == 0)
+                dst_row[d / 2] = c;
+            else
+                dst_row[d / 2] |= (uint8_t)(c << 4);
         }
     }
     return sat;
@@ -245,7 +333,8 @@ static int64_t store_row(int D, int kv_dtype, const uint16_t *src, float inv,
  * every stored row written to its pool row seg_base[i] + dst.  Rows the
  * layout leaves unused are not touched.  ring_keep[i*W + r] = keep bit (0/1)
  * of the position held in ring row r, 0 for a ring row not yet filled.
- * pos[b] = T.  Pools are [rows, D] elements of 2 (BF16) or 1 (FP8) bytes.
+ * pos[b] = T.  Pools are [rows, D] elements of 2 (BF16) or 1 (FP8) bytes,
+ * or half a byte (FP4, two per byte).
  * The caller passes pools of at least seg_base[B*Hkv] rows, obtained from
  * orc_prefill_layout with the same arguments.
  */
@@ -261,19 +350,17 @@ void orc_prefill_pack(int B, int Hkv, int D, int T, int W, int reserve,
     int32_t *dst = (int32_t *)malloc(sizeof(int32_t) * (size_t)nh * (size_t)(T > 0 ? T : 1));
     orc_prefill_layout(B, Hkv, T, W, reserve, align, keep, keep_ld, comp_len,
                        seg_cap, seg_base, dst);
-    if (kv_dtype == ORC_FP8 && scale_mode == 0)
+    if (kv_dtype != ORC_BF16 && scale_mode == 0)
         orc_prefill_amax(B, Hkv, D, T, W, k, v, sb, st, sh, keep, keep_ld,
                          k_amax, v_amax);
-    int esz = kv_dtype == ORC_BF16 ? 2 : 1;
+    int64_t rowb = row_bytes(D, kv_dtype);
     for (int b = 0; b < B; ++b) {
         pos[b] = T;
         for (int h = 0; h < Hkv; ++h) {
             int i = b * Hkv + h;
-            float ks = 1.0f, kinv = 1.0f, vs = 1.0f, vinv = 1.0f;
-            if (kv_dtype == ORC_FP8) {
-                orc_scales_from_amax(k_amax[i], &ks, &kinv);
-                orc_scales_from_amax(v_amax[i], &vs, &vinv);
-            }
+            float ks, kinv, vs, vinv;
+            head_scales(kv_dtype, kv_dtype == ORC_BF16 ? 0.0f : k_amax[i], &ks, &kinv);
+            head_scales(kv_dtype, kv_dtype == ORC_BF16 ? 0.0f : v_amax[i], &vs, &vinv);
             for (int r = 0; r < W; ++r)
                 ring_keep[(int64_t)i * W + r] = 0;
             const uint8_t *krow = keep + (int64_t)i * keep_ld;
@@ -285,8 +372,8 @@ void orc_prefill_pack(int B, int Hkv, int D, int T, int W, int reserve,
                     ring_keep[(int64_t)i * W + d] = krow[p] != 0;
                 int64_t row = seg_base[i] + d;
                 int64_t off = b * sb + p * st + h * sh;
-                store_row(D, kv_dtype, k + off, kinv, k_pool + row * D * esz);
-                store_row(D, kv_dtype, v + off, vinv, v_pool + row * D * esz);
+                store_row(D, kv_dtype, k + off, kinv, k_pool + row * rowb);
+                store_row(D, kv_dtype, v + off, vinv, v_pool + row * rowb);
             }
         }
     }
@@ -320,18 +407,15 @@ int64_t orc_append(int B, int Hkv, int D, int W, int kv_dtype,
                    int32_t *comp_len, int32_t *pos, uint8_t *ring_keep,
                    uint8_t *k_pool, uint8_t *v_pool, int32_t *err)
 {
-    int esz = kv_dtype == ORC_BF16 ? 2 : 1;
-    int64_t rowb = (int64_t)D * esz;
+    int64_t rowb = row_bytes(D, kv_dtype);
     int64_t sat = 0;
     for (int b = 0; b < B; ++b) {
         int P = pos[b];
         for (int h = 0; h < Hkv; ++h) {
             int i = b * Hkv + h;
-            float ks = 1.0f, kinv = 1.0f, vs = 1.0f, vinv = 1.0f;
-            if (kv_dtype == ORC_FP8) {
-                orc_scales_from_amax(k_amax[i], &ks, &kinv);
-                orc_scales_from_amax(v_amax[i], &vs, &vinv);
-            }
+            float ks, kinv, vs, vinv;
+            head_scales(kv_dtype, kv_dtype == ORC_BF16 ? 0.0f : k_amax[i], &ks, &kinv);
+            head_scales(kv_dtype, kv_dtype == ORC_BF16 ? 0.0f : v_amax[i], &vs, &vinv);
             int kept = keep_new[i] != 0;
             const uint16_t *kn = k_new + b * sb + h * sh;
             const uint16_t *vn = v_new + b * sb + h * sh;
@@ -373,12 +457,14 @@ int64_t orc_append(int B, int Hkv, int D, int W, int kv_dtype,
 /* ------------------------------------------------------------------ */
 
 /* The value a stored element stands for: the BF16 input itself, or the FP8
- * code of x * inv decoded and multiplied by s (in fp64). */
+ * or FP4 code of x * inv decoded and multiplied by s (in fp64). */
 static double stored_value(int kv_dtype, uint16_t x, float s, float inv)
 {
     if (kv_dtype == ORC_BF16)
         return (double)bf16_to_f32(x);
-    return orc_e4m3_decode(orc_e4m3_encode(bf16_to_f32(x) * inv)) * (double)s;
+    if (kv_dtype == ORC_FP8)
+        return orc_e4m3_decode(orc_e4m3_encode(bf16_to_f32(x) * inv)) * (double)s;
+    return orc_e2m1_decode(orc_e2m1_encode(bf16_to_f32(x) * inv)) * (double)s;
 }
 
 /*
@@ -397,11 +483,9 @@ void orc_attention_head(int D, int W, int kv_dtype, int P,
                         const uint16_t *q, double sm_scale, double *out,
                         double *lse)
 {
-    float ks = 1.0f, kinv = 1.0f, vs = 1.0f, vinv = 1.0f;
-    if (kv_dtype == ORC_FP8) {
-        orc_scales_from_amax(k_amax, &ks, &kinv);
-        orc_scales_from_amax(v_amax, &vs, &vinv);
-    }
+    float ks, kinv, vs, vinv;
+    head_scales(kv_dtype, k_amax, &ks, &kinv);
+    head_scales(kv_dtype, v_amax, &vs, &vinv);
     if (sm_scale <= 0.0)
         sm_scale = 1.0 / sqrt((double)D);
     double *z = (double *)malloc(sizeof(double) * (size_t)(P + 1 > 0 ? P + 1 : 1));
@@ -458,8 +542,8 @@ void orc_attention(int B, int Hq, int Hkv, int D, int W, int kv_dtype,
             orc_attention_head(D, W, kv_dtype, P[b], k + b * sb + h * sh,
                                v + b * sb + h * sh, st,
                                keep + (int64_t)i * keep_ld,
-                               kv_dtype == ORC_FP8 ? k_amax[i] : 0.0f,
-                               kv_dtype == ORC_FP8 ? v_amax[i] : 0.0f,
+                               kv_dtype != ORC_BF16 ? k_amax[i] : 0.0f,
+                               kv_dtype != ORC_BF16 ? v_amax[i] : 0.0f,
                                q + ((int64_t)b * Hq + j) * D, sm_scale,
                                out + ((int64_t)b * Hq + j) * D,
                                lse + (int64_t)b * Hq + j);

@@ -70,6 +70,21 @@ def test_fp8_encode_every_bf16_value():
     compare_state(c, o, "bf16 exhaustive")
 
 
+def test_fp8_encode_every_bf16_value_scaled():
+    # given scales far from 1: x * inv runs past +-448 (saturation), through
+    # the subnormal codes and into zero, and carries inf and NaN of both signs
+    B, Hkv, D, T = 1, 1, 128, 512
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    k = bits.view(torch.bfloat16).reshape(B, T, Hkv, D)
+    v = bits.flip(0).view(torch.bfloat16).reshape(B, T, Hkv, D)
+    keep = torch.ones((B, Hkv, T), dtype=torch.uint8)
+    for ka, va in ((0.37, 3.1e4), (1.0e-3, 0.75)):
+        amax = (np.full(1, ka, np.float32), np.full(1, va, np.float32))
+        c, _ = gpu_prefill(k, v, keep, T, 0, 0, "fp8", amax=amax)
+        o = oracle_prefill(k, v, keep, T, 0, 0, "fp8", amax=amax)
+        compare_state(c, o, f"fp8 scaled k_amax {ka} v_amax {va}")
+
+
 def test_fp8_scale_edge_cases():
     # heads whose stored values are all zero (amax 0 -> scale 1), or hold an inf
     B, Hkv, D, T, W = 1, 3, 64, 100, 8
