@@ -15,14 +15,16 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD, CDA_KV_BF16, CDA_KV_FP8_E4M3,
+from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD, CDA_KV_BF16, CDA_KV_FP4_E2M1,
+                   CDA_KV_FP8_E4M3,
                    CDA_OP_APPEND, CDA_OP_COUNT, CDA_OP_PACK, CDA_OUT_BF16, CDA_OUT_F32,
                    CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
 __all__ = ["CompactKVCache", "kv_compact", "decode_attn_compact", "decode_step_compact", "CdaError",
            "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY", "CDA_DEVERR_POOL", "CDA_DEVERR_XCD"]
 
-_DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3}
+_DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3, "fp4": CDA_KV_FP4_E2M1}
+_ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
 
 
 def _stream(device) -> int:
@@ -134,11 +136,11 @@ class CompactKVCache:
     def __init__(self, B: int, Hkv: int, D: int, W: int, kv_dtype: str = "bf16",
                  device="cuda"):
         if kv_dtype not in _DTYPES:
-            raise ValueError("kv_dtype must be 'bf16' or 'fp8'")
+            raise ValueError("kv_dtype must be 'bf16', 'fp8' or 'fp4'")
         _lib.load()
         self.B, self.Hkv, self.D, self.W = B, Hkv, D, W
         self.kv_dtype = kv_dtype
-        self.elem_bytes = 2 if kv_dtype == "bf16" else 1
+        self.row_bytes = _ROW_BYTES[kv_dtype](D)   # bytes of one stored row
         self.device = torch.device(device)
         nh = B * Hkv
         dev = self.device
@@ -183,7 +185,7 @@ class CompactKVCache:
     def allocate(self, rows: int | None = None) -> None:
         rows = self.rows_needed() if rows is None else rows
         rows = -(-rows // CDA_SEG_ALIGN) * CDA_SEG_ALIGN
-        nbytes = max(rows, 1) * self.D * self.elem_bytes
+        nbytes = max(rows, 1) * self.row_bytes
         self.k_pool = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.v_pool = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.pool_rows = rows
@@ -238,16 +240,23 @@ class CompactKVCache:
         return ring.repeat_interleave(self.Hkv) + self.comp_len.to(torch.int64)
 
     def v_rows(self) -> torch.Tensor:
-        """The V pool as [pool_rows, D * elem_bytes] bytes in row order (a
-        gather of the column-major tiles, for inspection and tests)."""
-        e, D = self.elem_bytes, self.D
-        t = self.v_pool[: self.pool_rows * D * e].view(-1, D, CDA_SEG_ALIGN, e)
-        return t.permute(0, 2, 1, 3).reshape(self.pool_rows, D * e)
+        """The V pool as [pool_rows, row_bytes] bytes in row order (a gather
+        of the column-major tiles, for inspection and tests; FP4 rows hold
+        element d in the low nibble of byte d / 2 for even d)."""
+        D, rows = self.D, self.pool_rows
+        if self.kv_dtype == "fp4":
+            t = self.v_pool[: rows * D // 2].view(-1, D, CDA_SEG_ALIGN // 2)   # [tile, d, byte]
+            codes = torch.stack([t & 15, t >> 4], dim=-1).reshape(-1, D, CDA_SEG_ALIGN)
+            codes = codes.permute(0, 2, 1)                                     # [tile, r, d]
+            return (codes[..., 0::2] | (codes[..., 1::2] << 4)).reshape(rows, D // 2)
+        e = self.row_bytes // D
+        t = self.v_pool[: rows * D * e].view(-1, D, CDA_SEG_ALIGN, e)
+        return t.permute(0, 2, 1, 3).reshape(rows, D * e)
 
     def k_rows(self) -> torch.Tensor:
-        """The K pool as [pool_rows, D * elem_bytes] bytes in row order (undoes
+        """The K pool as [pool_rows, row_bytes] bytes in row order (undoes
         the in-tile chunk permutation described in include/cda.h)."""
-        rb = self.D * self.elem_bytes
+        rb = self.row_bytes
         kl = rb // 64
         t = self.k_pool[: self.pool_rows * rb].view(-1, 4, kl, 4, 4, 4, 16)
         # [tile, m, j, kg, gh, gl, byte] -> [tile, gh, m, gl, j, kg, byte]

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libcda_hip.so")
 
 CDA_OK, CDA_ERR_INVALID_ARG, CDA_ERR_UNSUPPORTED, CDA_ERR_WORKSPACE, CDA_ERR_HIP = range(5)
 CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD = 1, 2, 4
-CDA_KV_BF16, CDA_KV_FP8_E4M3 = 0, 1
+CDA_KV_BF16, CDA_KV_FP8_E4M3, CDA_KV_FP4_E2M1 = 0, 1, 2
 CDA_OUT_BF16, CDA_OUT_F32 = 0, 1
 CDA_OP_COUNT, CDA_OP_PACK, CDA_OP_APPEND = 0, 1, 2
 CDA_SEG_ALIGN = 64

@@ -20,7 +20,10 @@ int32_t check_cache(const cda_kv_cache* c) {
   if (c->B < 0 || c->Hkv < 1 || c->W < 0 || c->reserved0 != 0) return CDA_ERR_INVALID_ARG;
   if (c->W > (1 << 28)) return CDA_ERR_INVALID_ARG;
   if (c->D != 64 && c->D != 128) return CDA_ERR_UNSUPPORTED;
-  if (c->kv_dtype != CDA_KV_BF16 && c->kv_dtype != CDA_KV_FP8_E4M3) return CDA_ERR_UNSUPPORTED;
+  if (c->kv_dtype != CDA_KV_BF16 && c->kv_dtype != CDA_KV_FP8_E4M3 &&
+      c->kv_dtype != CDA_KV_FP4_E2M1)
+    return CDA_ERR_UNSUPPORTED;
+  if (c->kv_dtype == CDA_KV_FP4_E2M1 && c->D != 128) return CDA_ERR_UNSUPPORTED;
   if ((int64_t)c->B * c->Hkv > (1 << 24)) return CDA_ERR_INVALID_ARG;
   if (!c->seg_base || !c->seg_cap || !c->comp_len || !c->err) return CDA_ERR_INVALID_ARG;
   return CDA_OK;
@@ -32,7 +35,7 @@ int32_t check_pools(const cda_kv_cache* c) {
   if (c->pool_rows > 0 && (!c->k_pool || !c->v_pool)) return CDA_ERR_INVALID_ARG;
   if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16)) return CDA_ERR_INVALID_ARG;
   if (!c->pos || (c->W > 0 && !c->ring_keep)) return CDA_ERR_INVALID_ARG;
-  if (c->kv_dtype == CDA_KV_FP8_E4M3 && (!c->k_amax || !c->v_amax)) return CDA_ERR_INVALID_ARG;
+  if (c->kv_dtype != CDA_KV_BF16 && (!c->k_amax || !c->v_amax)) return CDA_ERR_INVALID_ARG;
   return CDA_OK;
 }
 
@@ -109,6 +112,7 @@ int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* 
   if (st != CDA_OK) return st;
   if ((st = check_pools(c)) != CDA_OK) return st;
   if (Hq <= 0 || split_tokens < 0) return CDA_ERR_INVALID_ARG;
+  if (c->kv_dtype == CDA_KV_FP4_E2M1) return CDA_ERR_UNSUPPORTED;   // no 4-bit attention kernel yet
   if (Hq % c->Hkv != 0 || Hq / c->Hkv > CDA_MAX_GQA) return CDA_ERR_UNSUPPORTED;
   if (out_dtype != CDA_OUT_BF16 && out_dtype != CDA_OUT_F32) return CDA_ERR_UNSUPPORTED;
   if (c->B > 0) {

@@ -20,6 +20,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr int kTile = CDA_SEG_ALIGN;   // rows per V tile and per segment granule
 constexpr int kBlock = 256;            // threads per workgroup of every kernel
 
+// Stored formats (the cda_kv_dtype values), as template arguments.
+constexpr int kKvBF16 = CDA_KV_BF16, kKvFP8 = CDA_KV_FP8_E4M3, kKvFP4 = CDA_KV_FP4_E2M1;
+// Bytes of one stored row of D elements (FP4: two elements per byte).
+__host__ __device__ constexpr int kv_row_bytes(int kv, int D) {
+  return kv == kKvBF16 ? 2 * D : kv == kKvFP8 ? D : D / 2;
+}
+
 // Byte offset, inside its 64-row tile, of the 16-byte chunk c of row r of a
 // K pool whose rows are rb = D * e bytes.  The permutation puts the data one
 // 64-lane load instruction of the attention kernel needs (16 rows x 64 bytes,
@@ -36,6 +43,17 @@ __host__ __device__ __forceinline__ int k_chunk_offset(int r, int c, int rb) {
 __device__ __forceinline__ int64_t k_elem8(int64_t row, int d0, int D, int e) {
   const int rb = D * e, b = d0 * e;
   return (row / kTile) * kTile * rb + k_chunk_offset((int)(row % kTile), b >> 4, rb) + (b & 15);
+}
+
+// Byte offset of byte `byte` of pool row `row` in a K pool of rb-byte rows.
+__device__ __forceinline__ int64_t k_byte(int64_t row, int byte, int rb) {
+  return (row / kTile) * kTile * rb + k_chunk_offset((int)(row % kTile), byte >> 4, rb) + (byte & 15);
+}
+
+// FP4 V pool: 64-row tiles, column-major, two rows per byte: element
+// (row, d) is nibble row & 1 (low for even rows) of this byte.
+__device__ __forceinline__ int64_t v_nib_byte(int64_t row, int d, int D) {
+  return (row / kTile) * kTile * (D / 2) + (int64_t)d * (kTile / 2) + (row % kTile) / 2;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -86,12 +104,33 @@ __device__ __forceinline__ uint32_t e4m3x2_from_f32(float a, float b) {
   return w;
 }
 
+// OCP MX FP4 E2M1 encode of two values into one byte (a in the low nibble):
+// round-to-nearest-even, saturating at +-6, NaN -> +-6 with its sign -- what
+// the gfx950 conversion instruction computes for every binary32 input at
+// scale 1 (checked exhaustively on the device against the definition).
+__device__ __forceinline__ uint32_t e2m1x2_from_f32(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
 // Dequantisation and quantisation factors from a per-head absmax.
 __device__ __forceinline__ float fp8_scale(float amax) {
   return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(amax, 448.0f) : 1.0f;
 }
 __device__ __forceinline__ float fp8_inv_scale(float amax) {
   return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(448.0f, amax) : 1.0f;
+}
+// The same for the 4-bit store (largest magnitude 6); 1 for BF16.
+template <int KV>
+__device__ __forceinline__ float kv_scale(float amax) {
+  if (KV == kKvFP8) return fp8_scale(amax);
+  if (KV == kKvFP4) return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(amax, 6.0f) : 1.0f;
+  return 1.0f;
+}
+template <int KV>
+__device__ __forceinline__ float kv_inv_scale(float amax) {
+  if (KV == kKvFP8) return fp8_inv_scale(amax);
+  if (KV == kKvFP4) return (amax > 0.0f && amax <= 3.402823466e38f) ? __fdiv_rn(6.0f, amax) : 1.0f;
+  return 1.0f;
 }
 
 // Four FP8 codes (one dword) -> four bf16 / f16 values, exact.

@@ -242,13 +242,6 @@ __device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
   return (row / kTile) * kTile * D + (int64_t)d * kTile + (row % kTile);
 }
 
-// Row (inside its 64-row tile) of the 16-byte K pool chunk at byte offset
-// `off` of the tile: the inverse of k_chunk_offset.
-__device__ __forceinline__ int k_chunk_row(int off, int rb) {
-  const int blk = off >> 10, m = blk / (rb >> 6), g = (off >> 4) & 15;
-  return ((g >> 2) << 4) | (m << 2) | (g & 3);
-}
-
 // Workgroup (segment i, y) writes the 64-row pool tiles j = y, y + gridDim.y,
 // ... of segment i that hold ring rows or stored rows, one whole tile at a
 // time: it finds the source position of each row of the tile (ring row r:
@@ -257,14 +250,16 @@ __device__ __forceinline__ int k_chunk_row(int off, int rb) {
 // (each 64-lane load is whole rows), encodes them into LDS images of the
 // K tile (chunk-permuted rows) and the V tile (column-major), and stores
 // both with 16-byte writes.  Rows of the tile with no source are zero.
-template <bool FP8, int D>
+// The V image holds one byte per element (an FP4 code in its low nibble);
+// FP4 tiles are packed two rows per byte on the way out.
+template <int KV, int D>
 __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
-  constexpr int E = FP8 ? 1 : 2;            // bytes per stored element
-  constexpr int RB = D * E;                 // pool bytes per row
+  constexpr bool Q = KV != kKvBF16;         // quantised store
+  constexpr int RB = kv_row_bytes(KV, D);   // pool bytes per row
   constexpr int CPR = D / 8;                // 8-element input chunks per row
   constexpr int RPI = 64 / CPR;             // rows per 64-lane load
   constexpr int NI = kTile / (RPI * (kBlock / 64));   // loads per wave and tensor
-  constexpr int VS = FP8 ? 68 : 132;        // LDS bytes per V column: 64 rows + pad
+  constexpr int VS = Q ? 68 : 132;          // LDS bytes per V column: 64 rows + pad
   constexpr int kScan = 32;                 // keep bytes per thread per scan pass
   __shared__ int s_src[kTile];
   __shared__ int smem[4];
@@ -292,9 +287,9 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
   const int64_t rows = min((int64_t)max(nring + cl, W), alloc);
   const int ntiles = (int)((rows + kTile - 1) / kTile);
   float kinv = 1.0f, vinv = 1.0f;
-  if (FP8) {
-    kinv = fp8_inv_scale(p.k_amax[i]);
-    vinv = fp8_inv_scale(p.v_amax[i]);
+  if (Q) {
+    kinv = kv_inv_scale<KV>(p.k_amax[i]);
+    vinv = kv_inv_scale<KV>(p.v_amax[i]);
   }
   if (blockIdx.y == 0 && h == 0 && tid == 0) p.pos[b] = T;
 
@@ -382,7 +377,21 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
       const int r = rr[k];
       const u32x4 kx = has[k] ? kin[k] : u32x4{0, 0, 0, 0};
       const u32x4 vx = has[k] ? vin[k] : u32x4{0, 0, 0, 0};
-      if (FP8) {
+      if (KV == kKvFP4) {
+        uint32_t kc = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {   // elements 2 w2 (low nibble), 2 w2 + 1
+          const float k0 = __fmul_rn(__uint_as_float(kx[w2] << 16), kinv);
+          const float k1 = __fmul_rn(__uint_as_float(kx[w2] & 0xFFFF0000u), kinv);
+          const float v0 = __fmul_rn(__uint_as_float(vx[w2] << 16), vinv);
+          const float v1 = __fmul_rn(__uint_as_float(vx[w2] & 0xFFFF0000u), vinv);
+          kc |= e2m1x2_from_f32(k0, k1) << (8 * w2);
+          const uint32_t vb = e2m1x2_from_f32(v0, v1);
+          s_v[(d0 + 2 * w2) * VS + r] = (uint8_t)(vb & 15u);
+          s_v[(d0 + 2 * w2 + 1) * VS + r] = (uint8_t)(vb >> 4);
+        }
+        *reinterpret_cast<uint32_t*>(s_k + k_chunk_offset(r, (d0 / 2) >> 4, RB) + ((d0 / 2) & 15)) = kc;
+      } else if (KV == kKvFP8) {
         uint32_t kc[2] = {0, 0}, vc[2] = {0, 0};
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {   // elements 2 w2, 2 w2 + 1
@@ -406,29 +415,37 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
     }
     __syncthreads();
 
-    // ---- stores: both tiles as 16-byte chunks; a tile that reaches past
-    // pool_rows (a pool smaller than seg_base[B*Hkv]) keeps to the rows
-    // inside it and flags the rows with data outside it
-    const int64_t in_pool = p.pool_rows - (sb + r0);   // rows of the tile inside the pool
-    uint8_t* kt = p.k_pool + (sb + r0) * (int64_t)RB;
-    uint8_t* vt = p.v_pool + (sb + r0) * (int64_t)RB;
-    for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
-      if (in_pool >= kTile || k_chunk_row(ch * 16, RB) < in_pool)
+    // ---- stores: both tiles as 16-byte chunks.  Tiles and pool_rows are
+    // multiples of 64 rows, so a tile is wholly inside the pool or wholly
+    // outside it (a pool smaller than seg_base[B*Hkv]); outside, the rows
+    // with data are flagged and nothing is written.
+    if (p.pool_rows - (sb + r0) >= kTile) {
+      uint8_t* kt = p.k_pool + (sb + r0) * (int64_t)RB;
+      uint8_t* vt = p.v_pool + (sb + r0) * (int64_t)RB;
+      for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
         *reinterpret_cast<u32x4*>(kt + ch * 16) = *reinterpret_cast<const u32x4*>(s_k + ch * 16);
-      // V: chunk ch is rows r .. r + 16/E - 1 of column d
-      const int d = ch / (4 * E), r = (ch % (4 * E)) * (16 / E);
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * VS + r * E);
-      const u32x4 vv = u32x4{src[0], src[1], src[2], src[3]};
-      if (in_pool >= kTile || r + 16 / E <= in_pool) {
-        *reinterpret_cast<u32x4*>(vt + ch * 16) = vv;
-      } else {
+        u32x4 vv;
+        if (KV == kKvFP4) {   // chunk ch: rows r .. r + 31 of column d, two per byte
+          const int d = ch >> 1, r = (ch & 1) * 32;
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * VS + r);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if ((r * E + e) / E < in_pool) vt[ch * 16 + e] = (uint8_t)(vv[e >> 2] >> (8 * (e & 3)));
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t a = src[2 * q], c = src[2 * q + 1];   // one code per byte
+            const uint32_t lo = (a & 0xFu) | ((a >> 4) & 0xF0u) | ((a >> 8) & 0xF00u) | ((a >> 12) & 0xF000u);
+            const uint32_t hi = (c & 0xFu) | ((c >> 4) & 0xF0u) | ((c >> 8) & 0xF00u) | ((c >> 12) & 0xF000u);
+            vv[q] = lo | (hi << 16);
+          }
+        } else {              // chunk ch: rows r .. r + 16/E - 1 of column d
+          constexpr int E = KV == kKvFP8 ? 1 : 2;
+          const int d = ch / (4 * E), r = (ch % (4 * E)) * (16 / E);
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * VS + r * E);
+          vv = u32x4{src[0], src[1], src[2], src[3]};
+        }
+        *reinterpret_cast<u32x4*>(vt + ch * 16) = vv;
       }
-    }
-    if (in_pool < kTile && tid < kTile && tid >= in_pool && s_src[tid] >= 0)
+    } else if (tid < kTile && s_src[tid] >= 0) {
       atomicOr(p.err, CDA_DEVERR_POOL);
+    }
     __syncthreads();   // the next tile reuses s_src and the LDS images
   }
 }
@@ -454,25 +471,38 @@ struct AppendParams {
   int32_t* err;
 };
 
-// 8 consecutive K elements of a row (8 FP8 bytes or 8 bf16 = 16 bytes).
-template <bool FP8>
+// 8 consecutive K elements of a row: 4 FP4 bytes, 8 FP8 bytes or 8 bf16
+// (16 bytes).
+template <int KV>
 struct Row8 {
-  typedef typename std::conditional<FP8, u32x2, u32x4>::type type;
+  typedef typename std::conditional<KV == kKvFP4, uint32_t,
+                                    typename std::conditional<KV == kKvFP8, u32x2, u32x4>::type>::type type;
 };
+
+// Nibble `odd` of the FP4 V byte at q set to code c, the other kept.
+__device__ __forceinline__ void nib_store(uint8_t* q, int odd, uint32_t c) {
+  const uint32_t cur = *q;
+  *q = (uint8_t)(odd ? ((cur & 0x0Fu) | (c << 4)) : ((cur & 0xF0u) | c));
+}
 
 // Workgroup b handles sequence b.  Thread t owns elements [8c, 8c+8) of one
 // head's K and V rows (c = t mod D/8).  Straight-line code, two dependent
 // round trips: (1) position, segment metadata and its slice of the new
 // token; (2) the exiting ring row's keep bit and its slice of that row.
 // Then it writes the moved slice (if kept) and the new token's slice into
-// the ring row; the old slice was read by the same thread, before.
-template <bool FP8>
+// the ring row; the old slice was read by the same thread, before.  FP4 V
+// elements share bytes with the neighbouring row, so they are written as
+// read-modify-writes of their nibble (no other thread writes those bytes:
+// a byte's two rows are the moved row or the new row and a row nobody
+// writes in this step).
+template <int KV>
 __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
-  typedef typename std::conditional<FP8, uint8_t, uint16_t>::type elem_t;
-  typedef typename Row8<FP8>::type krow_t;
-  constexpr int E = FP8 ? 1 : 2;
+  typedef typename std::conditional<KV == kKvBF16, uint16_t, uint8_t>::type elem_t;
+  typedef typename Row8<KV>::type krow_t;
+  constexpr bool Q = KV != kKvBF16;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int W = p.W, D = p.D;
+  const int RB = kv_row_bytes(KV, D);
   const int cpr = D / 8;                       // 8-element chunks per row
   const int P = p.pos[b];
   elem_t* vp = reinterpret_cast<elem_t*>(p.v_pool);
@@ -484,11 +514,13 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
     const int cl0 = p.comp_len[i];
     const int cap = p.seg_cap[i];
     const int kept = p.keep[i] != 0;
-    const float kinv = FP8 ? fp8_inv_scale(p.k_amax[i]) : 1.0f;
-    const float vinv = FP8 ? fp8_inv_scale(p.v_amax[i]) : 1.0f;
+    const float kinv = Q ? kv_inv_scale<KV>(p.k_amax[i]) : 1.0f;
+    const float vinv = Q ? kv_inv_scale<KV>(p.v_amax[i]) : 1.0f;
     const int64_t off = (int64_t)b * p.sb + (int64_t)h * p.sh + d0;
     const u32x4 kn = *reinterpret_cast<const u32x4*>(p.k + off);
     const u32x4 vn = *reinterpret_cast<const u32x4*>(p.v + off);
+    // byte of this thread's K slice in a row
+    const int kb0 = KV == kKvFP4 ? d0 / 2 : d0 * (KV == kKvFP8 ? 1 : 2);
 
     int64_t from = -1, to = -1, nw = -1;
     int cl = cl0, full = 0, bad = 0;
@@ -501,10 +533,15 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
       const bool readable = slot < p.pool_rows;
       const int64_t rslot = readable ? slot : 0;
       const int rk = p.ring_keep[i * W + eslot];
-      const krow_t ok = *reinterpret_cast<const krow_t*>(p.k_pool + k_elem8(rslot, d0, D, E));
+      const krow_t ok = *reinterpret_cast<const krow_t*>(p.k_pool + k_byte(rslot, kb0, RB));
       elem_t ov[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ov[j] = vp[v_elem(rslot, d0 + j, D)];
+      for (int j = 0; j < 8; ++j) {
+        if (KV == kKvFP4)
+          ov[j] = (uint8_t)((p.v_pool[v_nib_byte(rslot, d0 + j, D)] >> (4 * (rslot & 1))) & 15u);
+        else
+          ov[j] = vp[v_elem(rslot, d0 + j, D)];
+      }
       if (exit_pos >= 0 && rk) {
         if (cl < cap) {
           from = slot;
@@ -520,9 +557,14 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
         bad = 1;
       }
       if (from >= 0) {
-        *reinterpret_cast<krow_t*>(p.k_pool + k_elem8(to, d0, D, E)) = ok;
+        *reinterpret_cast<krow_t*>(p.k_pool + k_byte(to, kb0, RB)) = ok;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) vp[v_elem(to, d0 + j, D)] = ov[j];
+        for (int j = 0; j < 8; ++j) {
+          if (KV == kKvFP4)
+            nib_store(p.v_pool + v_nib_byte(to, d0 + j, D), (int)(to & 1), ov[j]);
+          else
+            vp[v_elem(to, d0 + j, D)] = ov[j];
+        }
       }
     } else if (kept) {
       if (cl < cap) {
@@ -537,7 +579,19 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
       bad = 1;
     }
     if (nw >= 0) {
-      if (FP8) {
+      if (KV == kKvFP4) {
+        uint32_t kc = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {   // elements 2 w2 (low nibble), 2 w2 + 1
+          kc |= e2m1x2_from_f32(__fmul_rn(__uint_as_float(kn[w2] << 16), kinv),
+                                __fmul_rn(__uint_as_float(kn[w2] & 0xFFFF0000u), kinv)) << (8 * w2);
+          const uint32_t vb = e2m1x2_from_f32(__fmul_rn(__uint_as_float(vn[w2] << 16), vinv),
+                                              __fmul_rn(__uint_as_float(vn[w2] & 0xFFFF0000u), vinv));
+          nib_store(p.v_pool + v_nib_byte(nw, d0 + 2 * w2, D), (int)(nw & 1), vb & 15u);
+          nib_store(p.v_pool + v_nib_byte(nw, d0 + 2 * w2 + 1, D), (int)(nw & 1), vb >> 4);
+        }
+        *reinterpret_cast<uint32_t*>(p.k_pool + k_byte(nw, kb0, RB)) = kc;
+      } else if (KV == kKvFP8) {
         uint32_t kc[2] = {0, 0};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -546,9 +600,9 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
           kc[j >> 2] |= e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv)) << (8 * (j & 3));
           vp[v_elem(nw, d0 + j, D)] = (elem_t)e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
         }
-        *reinterpret_cast<u32x2*>(p.k_pool + k_elem8(nw, d0, D, 1)) = u32x2{kc[0], kc[1]};
+        *reinterpret_cast<u32x2*>(p.k_pool + k_byte(nw, kb0, RB)) = u32x2{kc[0], kc[1]};
       } else {
-        *reinterpret_cast<u32x4*>(p.k_pool + k_elem8(nw, d0, D, 2)) = kn;
+        *reinterpret_cast<u32x4*>(p.k_pool + k_byte(nw, kb0, RB)) = kn;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           vp[v_elem(nw, d0 + j, D)] = (elem_t)((vn[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
@@ -582,9 +636,8 @@ constexpr int kPackY = 32;   // workgroups per segment of the pack kernel
 hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
   const int nh = c.B * c.Hkv;
   if (nh == 0) return hipGetLastError();
-  const bool fp8 = c.kv_dtype == CDA_KV_FP8_E4M3;
   const dim3 grid(nh, a.T > 0 ? (a.T + kBlock - 1) / kBlock : 1);
-  if (fp8 && a.scale_mode == 0) {
+  if (c.kv_dtype != CDA_KV_BF16 && a.scale_mode == 0) {
     amax_zero_kernel<<<(nh + kBlock - 1) / kBlock, kBlock, 0, s>>>(nh, c.k_amax, c.v_amax);
     amax_kernel<<<grid, kBlock, 0, s>>>(static_cast<const uint16_t*>(a.k),
                                       static_cast<const uint16_t*>(a.v), a.stride_b, a.stride_t,
@@ -617,12 +670,14 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   // kPackY-th of them
   const int max_tiles = (int)((std::max<int64_t>(a.T, c.W) + kTile - 1) / kTile);
   const dim3 pgrid(nh, std::max(1, std::min(max_tiles, kPackY)));
-  if (fp8) {
-    if (c.D == 64) pack_kernel<true, 64><<<pgrid, kBlock, 0, s>>>(p);
-    else pack_kernel<true, 128><<<pgrid, kBlock, 0, s>>>(p);
+  if (c.kv_dtype == CDA_KV_FP4_E2M1) {
+    pack_kernel<kKvFP4, 128><<<pgrid, kBlock, 0, s>>>(p);   // FP4 needs D = 128
+  } else if (c.kv_dtype == CDA_KV_FP8_E4M3) {
+    if (c.D == 64) pack_kernel<kKvFP8, 64><<<pgrid, kBlock, 0, s>>>(p);
+    else pack_kernel<kKvFP8, 128><<<pgrid, kBlock, 0, s>>>(p);
   } else {
-    if (c.D == 64) pack_kernel<false, 64><<<pgrid, kBlock, 0, s>>>(p);
-    else pack_kernel<false, 128><<<pgrid, kBlock, 0, s>>>(p);
+    if (c.D == 64) pack_kernel<kKvBF16, 64><<<pgrid, kBlock, 0, s>>>(p);
+    else pack_kernel<kKvBF16, 128><<<pgrid, kBlock, 0, s>>>(p);
   }
   return hipGetLastError();
 }
@@ -649,10 +704,12 @@ hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipSt
   p.k_pool = static_cast<uint8_t*>(c.k_pool);
   p.v_pool = static_cast<uint8_t*>(c.v_pool);
   p.err = c.err;
-  if (c.kv_dtype == CDA_KV_FP8_E4M3)
-    append_kernel<true><<<c.B, kBlock, 0, s>>>(p);
+  if (c.kv_dtype == CDA_KV_FP4_E2M1)
+    append_kernel<kKvFP4><<<c.B, kBlock, 0, s>>>(p);
+  else if (c.kv_dtype == CDA_KV_FP8_E4M3)
+    append_kernel<kKvFP8><<<c.B, kBlock, 0, s>>>(p);
   else
-    append_kernel<false><<<c.B, kBlock, 0, s>>>(p);
+    append_kernel<kKvBF16><<<c.B, kBlock, 0, s>>>(p);
   return hipGetLastError();
 }
 

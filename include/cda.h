@@ -16,6 +16,9 @@
  *   - Summary bullets, FP8 and BF16: rows are stored as BF16 or as OCP
  *     E4M3FN FP8 with one absmax scale per (sequence, KV head) for K and one
  *     for V.
+ *   - Memory table, the 4-bit vLLM row (a format the page leaves undefined):
+ *     a 4-bit store, read here as the OCP MX FP4 element type E2M1 with the
+ *     same per-(sequence, KV head) absmax scales, two elements per byte.
  *   - decode_attn_compact: single-token GQA decode attention over the
  *     variable-length compact segments, split into work units whose partial
  *     softmax states are combined by a log-sum-exp merge.  With FP8 the
@@ -38,7 +41,8 @@
  *   The rows holding data are always the contiguous run [0, n_i) with
  *   n_i = min(W, pos[b]) + comp_len[i].
  *   Both pools are split into tiles of CDA_SEG_ALIGN = 64 rows (tile t =
- *   pool rows [64t, 64t+64), 64 * D * e bytes, e = 2 for BF16, 1 for FP8).
+ *   pool rows [64t, 64t+64), 64 * D * e bytes, e = 2 for BF16, 1 for FP8,
+ *   1/2 for FP4).
  *   k_pool: rows are cut into 16-byte chunks; chunk c of row r (r taken
  *     inside its tile) is at tile byte
  *       ((m * (D*e/64) + c / 4) * 1024) + (c % 4) * 256 + g * 16,
@@ -47,12 +51,18 @@
  *     kernel needs (the rows of a tile are a permutation of its bytes).
  *   v_pool: tiles stored column-major: element (r, d) at byte
  *     ((r / 64) * 64 * D + d * 64 + r % 64) * e, so that the 64 values of one
- *     column of a tile are contiguous.
+ *     column of a tile are contiguous (FP4: the low nibble of that byte for
+ *     even r, the high nibble for odd r).
+ *   FP4 elements of a K row: element d is the low nibble of row byte d / 2
+ *     when d is even, the high nibble when odd.
  *   FP8: code = E4M3FN_RNE_SATURATE(f32(x) * inv), inv = 448 / amax and
  *   value = code * s, s = amax / 448 (both single f32 divisions; s = inv = 1
  *   when amax is 0 or not finite).  amax is the largest |x| over the
  *   stored prefill tokens, per (sequence, KV head), for K and V separately;
  *   decode-time tokens use these frozen scales and saturate at +-448.
+ *   FP4: code = E2M1_RNE_SATURATE(f32(x) * inv), inv = 6 / amax, value =
+ *   code * s, s = amax / 6; NaN encodes as +-6 with its sign (E2M1 has no
+ *   NaN).  FP4 needs D = 128 (a K row must fill 64 bytes).
  */
 #ifndef CDA_H
 #define CDA_H
@@ -86,7 +96,7 @@ enum cda_status {
                                    needs (the dispatcher deals workgroups to the XCDs round
                                    robin); that call's outputs are not reliable */
 
-enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1 };
+enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1, CDA_KV_FP4_E2M1 = 2 };
 enum cda_out_dtype { CDA_OUT_BF16 = 0, CDA_OUT_F32 = 1 };
 enum cda_compact_op { CDA_OP_COUNT = 0, CDA_OP_PACK = 1, CDA_OP_APPEND = 2 };
 
@@ -110,8 +120,8 @@ typedef struct cda_kv_cache {
     int32_t *comp_len;  /* [B*Hkv]; written by COUNT, grown by APPEND */
     int32_t *pos;       /* [B]; tokens seen so far (next position); PACK sets T */
     uint8_t *ring_keep; /* [B*Hkv*W]; keep bit of the token each ring row holds */
-    float *k_amax;      /* [B*Hkv]; FP8 absmax of K (PACK computes or takes it) */
-    float *v_amax;      /* [B*Hkv]; FP8 absmax of V */
+    float *k_amax;      /* [B*Hkv]; FP8/FP4 absmax of K (PACK computes or takes it) */
+    float *v_amax;      /* [B*Hkv]; FP8/FP4 absmax of V */
     int32_t *err;       /* [1]; device error word, CDA_DEVERR_* bits; COUNT clears it */
     uint8_t *seg_group; /* optional [B*Hkv] (may be NULL); written by COUNT: the group (0..7)
                            of workgroups, one XCD's worth, that takes the attention work of
@@ -128,7 +138,7 @@ typedef struct cda_compact_args {
     int32_t op;         /* enum cda_compact_op */
     int32_t T;          /* COUNT, PACK: prefill length, 0 <= T <= 2^24 */
     int32_t reserve;    /* COUNT: spare compact rows per segment for decode growth (>= 0) */
-    int32_t scale_mode; /* PACK with FP8: 0 = compute k_amax/v_amax, 1 = use them as given */
+    int32_t scale_mode; /* PACK with FP8/FP4: 0 = compute k_amax/v_amax, 1 = use them as given */
     const uint8_t *keep;/* COUNT, PACK: row i = b*Hkv+h at keep + i*keep_ld, first T bytes used;
                            APPEND: [B*Hkv] bytes, one per head for the new token */
     int64_t keep_ld;    /* COUNT, PACK: bytes between keep rows (>= T) */
@@ -151,7 +161,7 @@ typedef struct cda_compact_args {
  *   Reads keep; needs seg_base, seg_cap, comp_len, err (pools may be NULL).
  * CDA_OP_PACK: after COUNT (same keep, T), writes every stored prefill row
  *   (the W most recent positions and every kept older one) to its pool row,
- *   fills ring_keep, sets pos[b] = T and, for FP8 with scale_mode 0,
+ *   fills ring_keep, sets pos[b] = T and, for FP8/FP4 with scale_mode 0,
  *   computes k_amax/v_amax first.  Pools are written in whole 64-row
  *   tiles: unused rows inside a tile that holds ring or stored rows are set
  *   to zero; tiles past them are not written.
@@ -172,7 +182,7 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  * For sequence b and query head j (KV head h = j / (Hq / Hkv)):
  *   z_p = sm_scale * q[b,j,:] . k^_p    over the n_i stored rows of segment i
  *   out[b,j,:] = sum_p softmax(z)_p v^_p,   lse[b,j] = log sum_p exp(z_p)
- * where k^, v^ are the stored values (BF16, or FP8 code * scale).  A segment
+ * where k^, v^ are the stored values (BF16, or FP8/FP4 code * scale).  A segment
  * with no stored rows gives out = 0 and lse = -inf.
  *
  *   q            BF16 [B, Hq, D] contiguous, 16-byte aligned

@@ -16,7 +16,7 @@ def dev():
 
 
 def odt(kv_dtype: str) -> int:
-    return oracle.BF16 if kv_dtype == "bf16" else oracle.FP8
+    return {"bf16": oracle.BF16, "fp8": oracle.FP8, "fp4": oracle.FP4}[kv_dtype]
 
 
 def log(msg: str):
@@ -62,7 +62,7 @@ def compare_state(c: CompactKVCache, o: oracle.OracleCache, what: str = ""):
     if c.W:
         assert np.array_equal(c.ring_keep.cpu().numpy()[: nh * c.W], o.ring_keep[: nh * c.W]), \
             what + " ring_keep"
-    if c.kv_dtype == "fp8":
+    if c.kv_dtype in ("fp8", "fp4"):
         ga, oa = c.k_amax.cpu().numpy()[:nh], o.k_amax
         assert np.array_equal(np.isnan(ga), np.isnan(oa)) and np.array_equal(ga[~np.isnan(ga)], oa[~np.isnan(oa)]), what + " k_amax"
         ga, oa = c.v_amax.cpu().numpy()[:nh], o.v_amax

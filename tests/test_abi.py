@@ -66,6 +66,18 @@ def test_cache_validation(lib, field, value, status):
     assert L.kv_compact(C.byref(c), C.byref(a), None) == status
 
 
+def test_fp4_needs_head_dim_128(lib):
+    # the 4-bit store needs K rows of 64 bytes: D = 64 is unsupported
+    L = lib.load()
+    a = lib.CdaCompactArgs()
+    a.op = lib.CDA_OP_PACK
+    a.T, a.keep_ld, a.keep = 4, 4, 0x100000
+    c = _cache(lib, kv_dtype=lib.CDA_KV_FP4_E2M1, D=64)
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 2
+    c = _cache(lib, kv_dtype=lib.CDA_KV_FP4_E2M1, D=128, k_amax=0)   # scales needed
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+
+
 def test_compact_args_validation(lib):
     L = lib.load()
     c = _cache(lib)

@@ -21,6 +21,10 @@ CASES = [
     (2, 2, 64, 257, 16, 0, 1.0, "bf16", 11),     # keep all
     (2, 2, 128, 257, 16, 0, 0.0, "fp8", 13),     # keep none
     (1, 1, 64, 0, 8, 4, 0.5, "bf16", 15),        # empty prefill
+    (2, 3, 128, 700, 64, 5, 0.2, "fp4", 17),     # 4-bit store
+    (1, 4, 128, 40, 64, 2, 0.5, "fp4", 19),      # FP4, T < W
+    (3, 1, 128, 1000, 1, 0, 0.1, "fp4", 21),     # FP4, W = 1 (ring row pairs with row 1)
+    (2, 2, 128, 257, 17, 0, 1.0, "fp4", 23),     # FP4, odd W, keep all
 ]
 
 
@@ -47,7 +51,7 @@ def test_strided_inputs_and_nonbinary_keep():
     v = workload.random_bf16((B, T + 10, Hkv + 2, D), seed=42)[:, :, 1:Hkv + 1]
     keep = workload.random_keep((B, Hkv, T + 10), 0.3, seed=43)         # bytes 1..255 kept
     assert keep.max() > 1
-    for kv_dtype in ("bf16", "fp8"):
+    for kv_dtype in ("bf16", "fp8", "fp4"):
         c, _ = gpu_prefill(k, v, keep, T, W, 4, kv_dtype)
         o = oracle_prefill(k.contiguous(), v.contiguous(), keep, T, W, 4, kv_dtype)
         compare_state(c, o, kv_dtype)
@@ -85,6 +89,21 @@ def test_fp8_encode_every_bf16_value_scaled():
         compare_state(c, o, f"fp8 scaled k_amax {ka} v_amax {va}")
 
 
+def test_fp4_encode_every_bf16_value():
+    # amax 6 gives inv = 1, so each code is the E2M1 encoding of the input;
+    # then given scales far from 1 (saturation, zero, inf and NaN of both signs)
+    B, Hkv, D, T = 1, 1, 128, 512
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    k = bits.view(torch.bfloat16).reshape(B, T, Hkv, D)
+    v = bits.flip(0).view(torch.bfloat16).reshape(B, T, Hkv, D)
+    keep = torch.ones((B, Hkv, T), dtype=torch.uint8)
+    for ka, va in ((6.0, 6.0), (0.37, 3.1e4)):
+        amax = (np.full(1, ka, np.float32), np.full(1, va, np.float32))
+        c, _ = gpu_prefill(k, v, keep, T, 0, 0, "fp4", amax=amax)
+        o = oracle_prefill(k, v, keep, T, 0, 0, "fp4", amax=amax)
+        compare_state(c, o, f"fp4 k_amax {ka} v_amax {va}")
+
+
 def test_fp8_scale_edge_cases():
     # heads whose stored values are all zero (amax 0 -> scale 1), or hold an inf
     B, Hkv, D, T, W = 1, 3, 64, 100, 8
@@ -102,7 +121,9 @@ def test_fp8_scale_edge_cases():
 
 @pytest.mark.parametrize("kv_dtype,D,W,reserve", [("bf16", 64, 16, 40), ("fp8", 128, 16, 40),
                                                   ("fp8", 64, 0, 40), ("bf16", 128, 1, 40),
-                                                  ("fp8", 128, 100, 40)])
+                                                  ("fp8", 128, 100, 40), ("fp4", 128, 16, 40),
+                                                  ("fp4", 128, 0, 40), ("fp4", 128, 7, 40),
+                                                  ("fp4", 128, 1, 40)])
 def test_append_steps_bit_exact(kv_dtype, D, W, reserve):
     B, Hkv, T, S = 3, 2, 150, 40
     log(f"append {kv_dtype} D={D} W={W}")
