@@ -112,7 +112,6 @@ int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* 
   if (st != CDA_OK) return st;
   if ((st = check_pools(c)) != CDA_OK) return st;
   if (Hq <= 0 || split_tokens < 0) return CDA_ERR_INVALID_ARG;
-  if (c->kv_dtype == CDA_KV_FP4_E2M1) return CDA_ERR_UNSUPPORTED;   // no 4-bit attention kernel yet
   if (Hq % c->Hkv != 0 || Hq / c->Hkv > CDA_MAX_GQA) return CDA_ERR_UNSUPPORTED;
   if (out_dtype != CDA_OUT_BF16 && out_dtype != CDA_OUT_F32) return CDA_ERR_UNSUPPORTED;
   if (c->B > 0) {

@@ -224,7 +224,7 @@ __device__ __forceinline__ StepRows step_rows(int W, int P, int ring_slot, int c
 struct Unit {
   int i, first, U, n;      // n: rows planned
   long long sb;
-  float ka, va;            // absmax of K and V (FP8)
+  float ka, va;            // absmax of K and V (FP8, FP4)
   int P, cl, cap, kn;      // decode step: state before the append
 };
 
@@ -234,7 +234,7 @@ struct Unit {
 // grp + xs, grp + 2xs, ...  Wave-level: every wave of a workgroup calls it
 // with the same arguments and gets the same answer.  It scans all of the
 // group's segments and returns their unit count in `total`.
-template <bool FP8, bool APP>
+template <bool Q, bool APP>
 __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, int k, int lane,
                                           Unit& un, int& total) {
   const bool mapped = p.seg_group != nullptr;
@@ -251,7 +251,7 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
       capi = max(p.seg_cap[hi], 0);
       cli = min(max(p.comp_len[hi], 0), capi);
       sbi = p.seg_base[hi];
-      if (FP8) {
+      if (Q) {
         ka = p.k_amax[hi];
         va = p.v_amax[hi];
       }
@@ -327,22 +327,34 @@ __device__ __forceinline__ void commit_segment(const AttnParams& p, int i, const
   if (errbits) atomicOr(p.err, errbits);
 }
 
+// d of the first of the 8 q values lane (g, kg) supplies at k-step s: the d
+// the K operand of that lane holds there (the order of the bytes of its K
+// chunk: 16 FP8 elements = 2 k-steps, 32 FP4 elements = 4, 8 bf16 = 1).
+template <int KV>
+__device__ __forceinline__ int q_d0(int s, int kg) {
+  if (KV == kKvFP8) return 64 * (s >> 1) + 16 * kg + 8 * (s & 1);
+  if (KV == kKvFP4) return 32 * kg + 8 * s;
+  return 32 * s + 8 * kg;
+}
+
 // Mask of the bytes of dword w (bytes 4w .. 4w+3) that lie below `lim`.
 __device__ __forceinline__ uint32_t bytes_below(int lim, int w) {
   const int k = lim - 4 * w;
   return k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
 }
 
-template <bool FP8, int D, bool XL, int NW, bool APP>
+template <int KV, int D, bool XL, int NW, bool APP>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
+  constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
   constexpr int NTH = 64 * NW;              // threads of the workgroup
-  constexpr int E = FP8 ? 1 : 2;            // bytes per stored element
-  constexpr int RB = D * E;                 // bytes per row
+  constexpr int E = FP8 ? 1 : 2;            // bytes per element (FP8, BF16)
+  constexpr int RB = kv_row_bytes(KV, D);   // bytes per row
   constexpr int NK = D / 32;                // MFMA k-steps of q.K
   constexpr int NT = D / 16;                // 16-wide d tiles of the output
-  constexpr int KL = FP8 ? D / 64 : D / 32; // 16-byte K loads per (lane, token group)
-  constexpr int VL = FP8 ? 1 : 2;           // 16-byte V loads per (lane, d tile)
+  constexpr int KL = RB / 64;               // 16-byte K loads per (lane, token group)
+  constexpr int VL = FP8 ? 1 : 2;           // 16-byte V loads per (lane, d tile); FP4: one 8-byte
   constexpr int EPL = D / 64;               // new-token elements per lane
+  static_assert(!FP4 || D == 128, "the 4-bit store needs 64-byte K rows");
 
   __shared__ int s_last;
   __shared__ float s_m[NW][16], s_l[NW][16];
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   for (int k = XL ? (w / kXcdGroups) : w;; k += p.per_xcd) {
     Unit un;
     int total = 0;
-    if (!find_unit<FP8, APP>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
+    if (!find_unit<Q, APP>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
     // every load of the plan has been used: say so, so that no later write to
     // a register it used waits for the loads issued after this point
     __builtin_amdgcn_s_waitcnt(0);
@@ -375,8 +387,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     const int t_begin = (k - un.first) * p.tpu;
     const int t_end = min(t_begin + p.tpu, ntiles);
     const int slot = XL ? k * kXcdGroups + grp : k;   // this unit's partial
-    const float ks = FP8 ? fp8_scale(un.ka) : 1.0f;
-    const float vs = FP8 ? fp8_scale(un.va) : 1.0f;
+    const float ks = kv_scale<KV>(un.ka);
+    const float vs = kv_scale<KV>(un.va);
 
     // ---- decode step: rows with data, the new token's row and its tile
     int n = un.n, new_row = -1, t_own = -1;
@@ -406,8 +418,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       const uint16_t* qrow = p.q + (int64_t)(b * p.Hq + h * G + (g < G ? g : 0)) * D;
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
-        qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + d0));
+        qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + q_d0<KV>(s, kg)));
       }
     }
     const float c1 = p.sm_scale * kLog2e * ks;
@@ -443,7 +454,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
-        ox[e] = FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
+        ox[e] = FP4 ? ((uint32_t)vt[(EPL * lane + e) * (kTile / 2) + rs / 2] >> (4 * (rs & 1))) & 15u
+              : FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
                     : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs];
     }
 
@@ -458,13 +470,25 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       const int d0n = EPL * lane;
       float ka = un.ka, va = un.va;
       __asm__ volatile("" : "+v"(ka), "+v"(va));   // the divisions stay here too
-      const float kinv = FP8 ? fp8_inv_scale(ka) : 1.0f;
-      const float vinv = FP8 ? fp8_inv_scale(va) : 1.0f;
+      const float kinv = kv_inv_scale<KV>(ka);
+      const float vinv = kv_inv_scale<KV>(va);
       kc = 0;
       vc = 0;
       float* sn = reinterpret_cast<float*>(s_new);
+      if (FP4) {   // the lane's two elements: one K byte, two V codes (low: d0n)
+        kc = e2m1x2_from_f32(__fmul_rn(__uint_as_float(nk << 16), kinv),
+                             __fmul_rn(__uint_as_float(nk & 0xFFFF0000u), kinv));
+        vc = e2m1x2_from_f32(__fmul_rn(__uint_as_float(nv << 16), vinv),
+                             __fmul_rn(__uint_as_float(nv & 0xFFFF0000u), vinv));
+        const auto kf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(kc, 1.0f, 0);
+        const auto vf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc, 1.0f, 0);
+        sn[d0n] = kf[0];
+        sn[d0n + 1] = kf[1];
+        sn[D + d0n] = vf[0];
+        sn[D + d0n + 1] = vf[1];
+      }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
+      for (int e = 0; e < (FP4 ? 0 : EPL); ++e) {
         const uint32_t kb = (nk >> (16 * e)) & 0xFFFFu, vb = (nv >> (16 * e)) & 0xFFFFu;
         if (FP8) {
           const uint32_t kq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv));
@@ -485,7 +509,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       float dot = 0.0f;   // lane (g, kg): its quarter of q[g] . k^
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
-        const int d0 = FP8 ? (64 * (s >> 1) + 16 * kg + 8 * (s & 1)) : (32 * s + 8 * kg);
+        const int d0 = q_d0<KV>(s, kg);
         const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
         // an opaque copy: converted here, not hoisted above the tile loads
         // (where converting it would wait for the q loads)
@@ -526,12 +550,20 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
             kr[m][j] = __builtin_nontemporal_load(
                 reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16));
         u32x4 vr[NT][VL];
+        u32x2 vq[FP4 ? NT : 1];   // FP4: tokens 16 kg .. 16 kg + 15 of column 16 nt + g
+        if (FP4) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+          for (int nt = 0; nt < NT; ++nt)
+            vq[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+                vtile + (16 * nt + g) * (kTile / 2) + 8 * kg));
+        } else {
 #pragma unroll
-          for (int j = 0; j < VL; ++j)
-            vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < VL; ++j)
+              vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                  vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
+        }
 
         // -- S^T = K . Q^T, 16 tokens per MFMA row block
         f32x4 s[4];
@@ -541,7 +573,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
 #pragma unroll
           for (int st = 0; st < NK; ++st) {
             bf16x8 a;
-            if (FP8) {
+            if (FP4) {
+              a = fp4x8_to_bf16x8(kr[m][0][st]);
+            } else if (FP8) {
               const u32x4 v = kr[m][st >> 1];
               a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
             } else {
@@ -605,8 +639,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         m_run = m_new;
 
         // -- rows past the segment end: zero their V bytes (P is 0 there, but
-        //    the bytes may not be finite values)
-        if (!full) {
+        //    the bytes may not be finite values; every FP4 code is finite)
+        if (!FP4 && !full) {
 #pragma unroll
           for (int j = 0; j < VL; ++j) {
             const int lim = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;  // valid bytes
@@ -619,18 +653,23 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
           }
         }
 
-        // -- O^T += V^T . P^T, per d tile one MFMA (FP8) or two (BF16: hi, lo)
-        //    per 8 tokens of each lane
+        // -- O^T += V^T . P^T, per d tile one MFMA (FP8, FP4) or two (BF16:
+        //    hi, lo) per 8 tokens of each lane
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          if (FP8) {
+          if (Q) {
             f16x8 pf;
 #pragma unroll
             for (int e = 0; e < 8; ++e) pf[e] = (_Float16)z[2 * hh + (e >> 2)][e & 3];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-              const u32x4 v = vr[nt][0];
-              const f16x8 a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
+              f16x8 a;
+              if (FP4) {
+                a = fp4x8_to_f16x8(vq[nt][hh]);
+              } else {
+                const u32x4 v = vr[nt][0];
+                a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
+              }
               acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, acc[nt], 0, 0, 0);
             }
           } else {
@@ -693,7 +732,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
           if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
-            if (FP8)
+            if (FP4)
+              nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
+            else if (FP8)
               vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
             else
               reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
@@ -702,17 +743,21 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         // the new row goes over the ring row: the tiles read its old bytes
         // before the barrier above, and the copy above used the ones read at
         // the start of the unit (unused, and harmless, if it did not move)
-        const int kb0 = d0n * E;   // byte of this lane's first element in the row
+        // byte of this lane's first element in the row, and the lane's bytes
+        constexpr int LB = FP4 ? EPL / 2 : EPL * E;
+        const int kb0 = FP4 ? d0n / 2 : d0n * E;
         uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
-        if (EPL * E == 4)
+        if (LB == 4)
           *reinterpret_cast<uint32_t*>(kdst) = kc;
-        else if (EPL * E == 2)
+        else if (LB == 2)
           *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
         else
           *kdst = (uint8_t)kc;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          if (FP8)
+          if (FP4)   // after the moved row's write, which may share the byte
+            nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
+          else if (FP8)
             vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
           else
             reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
@@ -856,21 +901,23 @@ int device_xcds() {
 }
 
 template <bool APP>
-void launch_variant(bool fp8, int D, bool xl, int nw, dim3 grid, hipStream_t s, const AttnParams& p) {
+void launch_variant(int kv, int D, bool xl, int nw, dim3 grid, hipStream_t s, const AttnParams& p) {
 #define CDA_LAUNCH_ATTN(F, DD, X)                                                      \
   (nw == 8 ? attn_kernel<F, DD, X, 8, APP><<<grid, 512, 0, s>>>(p)                     \
            : attn_kernel<F, DD, X, 4, APP><<<grid, 256, 0, s>>>(p))
-  if (fp8) {
+  if (kv == kKvFP4) {   // D = 128 only
+    if (xl) CDA_LAUNCH_ATTN(kKvFP4, 128, true); else CDA_LAUNCH_ATTN(kKvFP4, 128, false);
+  } else if (kv == kKvFP8) {
     if (D == 64) {
-      if (xl) CDA_LAUNCH_ATTN(true, 64, true); else CDA_LAUNCH_ATTN(true, 64, false);
+      if (xl) CDA_LAUNCH_ATTN(kKvFP8, 64, true); else CDA_LAUNCH_ATTN(kKvFP8, 64, false);
     } else {
-      if (xl) CDA_LAUNCH_ATTN(true, 128, true); else CDA_LAUNCH_ATTN(true, 128, false);
+      if (xl) CDA_LAUNCH_ATTN(kKvFP8, 128, true); else CDA_LAUNCH_ATTN(kKvFP8, 128, false);
     }
   } else {
     if (D == 64) {
-      if (xl) CDA_LAUNCH_ATTN(false, 64, true); else CDA_LAUNCH_ATTN(false, 64, false);
+      if (xl) CDA_LAUNCH_ATTN(kKvBF16, 64, true); else CDA_LAUNCH_ATTN(kKvBF16, 64, false);
     } else {
-      if (xl) CDA_LAUNCH_ATTN(false, 128, true); else CDA_LAUNCH_ATTN(false, 128, false);
+      if (xl) CDA_LAUNCH_ATTN(kKvBF16, 128, true); else CDA_LAUNCH_ATTN(kKvBF16, 128, false);
     }
   }
 #undef CDA_LAUNCH_ATTN
@@ -948,12 +995,12 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   // share of the unit bound; a group with more units loops over them.
   p.per_xcd = xl ? (int)((units * 5 / 4 + kXcdGroups - 1) / kXcdGroups) : 0;
   const dim3 grid((unsigned)(xl ? (int64_t)p.per_xcd * kXcdGroups : units));
-  const bool fp8 = c.kv_dtype == CDA_KV_FP8_E4M3;
+  const int kv = c.kv_dtype;
   const int nw = tpu >= 8 ? 8 : 4;   // waves per workgroup: one tile each per pass
   if (step)
-    launch_variant<true>(fp8, c.D, xl, nw, grid, s, p);
+    launch_variant<true>(kv, c.D, xl, nw, grid, s, p);
   else
-    launch_variant<false>(fp8, c.D, xl, nw, grid, s, p);
+    launch_variant<false>(kv, c.D, xl, nw, grid, s, p);
   return hipGetLastError();
 }
 

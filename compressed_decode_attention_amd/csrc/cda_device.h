@@ -104,6 +104,14 @@ __device__ __forceinline__ uint32_t e4m3x2_from_f32(float a, float b) {
   return w;
 }
 
+// Nibble `odd` of the FP4 V byte at q set to code c, the other kept (a
+// read-modify-write of the byte; its other row must not be written at the
+// same time).
+__device__ __forceinline__ void nib_store(uint8_t* q, int odd, uint32_t c) {
+  const uint32_t cur = *q;
+  *q = (uint8_t)(odd ? ((cur & 0x0Fu) | (c << 4)) : ((cur & 0xF0u) | c));
+}
+
 // OCP MX FP4 E2M1 encode of two values into one byte (a in the low nibble):
 // round-to-nearest-even, saturating at +-6, NaN -> +-6 with its sign -- what
 // the gfx950 conversion instruction computes for every binary32 input at
@@ -149,6 +157,23 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t w0, uint32_t w1) {
   f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
   f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
   f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight FP4 codes (one dword, element 2j in the low nibble of byte j) ->
+// eight bf16 / f16 values, exact.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+__device__ __forceinline__ f16x8 fp4x8_to_f16x8(uint32_t w) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 

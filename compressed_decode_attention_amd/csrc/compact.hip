@@ -479,12 +479,6 @@ struct Row8 {
                                     typename std::conditional<KV == kKvFP8, u32x2, u32x4>::type>::type type;
 };
 
-// Nibble `odd` of the FP4 V byte at q set to code c, the other kept.
-__device__ __forceinline__ void nib_store(uint8_t* q, int odd, uint32_t c) {
-  const uint32_t cur = *q;
-  *q = (uint8_t)(odd ? ((cur & 0x0Fu) | (c << 4)) : ((cur & 0xF0u) | c));
-}
-
 // Workgroup b handles sequence b.  Thread t owns elements [8c, 8c+8) of one
 // head's K and V rows (c = t mod D/8).  Straight-line code, two dependent
 // round trips: (1) position, segment metadata and its slice of the new

@@ -26,9 +26,10 @@ def _run(B, Hq, Hkv, D, T, W, rate, kv_dtype, seed, split=0, sm_scale=0.0, reser
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev())
     c.attention(q.to(dev()), out=out, lse=lse, sm_scale=sm_scale, split_tokens=split)
     torch.cuda.synchronize()
-    ka = c.k_amax.cpu().numpy() if kv_dtype == "fp8" else None
-    va = c.v_amax.cpu().numpy() if kv_dtype == "fp8" else None
-    if kv_dtype == "fp8":   # the scales themselves are pinned bit-exact elsewhere
+    quant = kv_dtype in ("fp8", "fp4")
+    ka = c.k_amax.cpu().numpy() if quant else None
+    va = c.v_amax.cpu().numpy() if quant else None
+    if quant:   # the scales themselves are pinned bit-exact elsewhere
         oa = oracle.prefill_amax(k, v, keep, T, W)
         assert np.array_equal(ka[: B * Hkv], oa[0]) and np.array_equal(va[: B * Hkv], oa[1])
     ref, rlse = oracle.attention(q, k, v, keep, T - 1, W, odt(kv_dtype), ka, va, sm_scale)
@@ -48,6 +49,10 @@ CASES = [
     (2, 12, 4, 64, 333, 7, 0.2, "fp8", 8),         # G = 3
     (1, 8, 2, 128, 50, 64, 0.5, "fp8", 9),         # T < W
     (2, 8, 4, 64, 4100, 1, 0.02, "bf16", 10),      # W = 1, very sparse
+    (2, 32, 8, 128, 1500, 256, 0.15, "fp4", 31),   # 4-bit store
+    (1, 8, 2, 128, 50, 64, 0.5, "fp4", 32),        # FP4, T < W
+    (1, 32, 2, 128, 650, 33, 0.5, "fp4", 33),      # FP4, G = 16, odd W
+    (1, 16, 16, 128, 777, 20, 0.4, "fp4", 34),     # FP4, G = 1
 ]
 
 
@@ -62,8 +67,9 @@ def test_attention_matches_oracle(case):
 
 
 @pytest.mark.parametrize("split", [64, 128, 192, 256, 1024, 100000])
-def test_split_invariance(split):
-    case = (2, 32, 8, 128, 3000, 256, 0.2, "fp8", 21)
+@pytest.mark.parametrize("kv_dtype", ["fp8", "fp4"])
+def test_split_invariance(split, kv_dtype):
+    case = (2, 32, 8, 128, 3000, 256, 0.2, kv_dtype, 21)
     c, out, lse, ref, rlse = _run(*case, split=split)
     check_close(out, ref, f"split {split}")
     check_close(lse, rlse, f"split {split} lse", atol=1e-4, rtol=1e-5)
@@ -133,7 +139,8 @@ def test_bf16_output_is_rounded_f32_output():
     assert torch.equal(o16, o32.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("kv_dtype,D,W", [("fp8", 128, 64), ("bf16", 64, 64), ("fp8", 64, 0)])
+@pytest.mark.parametrize("kv_dtype,D,W", [("fp8", 128, 64), ("bf16", 64, 64), ("fp8", 64, 0),
+                                          ("fp4", 128, 64), ("fp4", 128, 0)])
 def test_decode_loop_matches_oracle(kv_dtype, D, W):
     B, Hq, Hkv, T, S = 2, 16, 4, 700, 80
     log(f"decode loop {kv_dtype} D={D} W={W}")
@@ -143,8 +150,8 @@ def test_decode_loop_matches_oracle(kv_dtype, D, W):
     q = workload.random_bf16((S, B, Hq, D), seed=54)
     c, _ = gpu_prefill(k, v, keep, T, W, S, kv_dtype, with_dst=False)
     kd, vd, keepd, qd = k.to(dev()), v.to(dev()), keep.to(dev()), q.to(dev())
-    ka = c.k_amax.cpu().numpy() if kv_dtype == "fp8" else None
-    va = c.v_amax.cpu().numpy() if kv_dtype == "fp8" else None
+    ka = c.k_amax.cpu().numpy() if kv_dtype != "bf16" else None
+    va = c.v_amax.cpu().numpy() if kv_dtype != "bf16" else None
     worst = 0.0
     for s in range(S):
         c.append(kd[:, T + s], vd[:, T + s], keepd[:, :, T + s].contiguous())

@@ -28,6 +28,11 @@ CASES = [
     (2, 16, 2, 64, 200, 30, 16, 0.9, "fp8", 8, 3, 0),        # compact region fills: CAPACITY
     (3, 8, 1, 128, 0, 70, 64, 0.5, "bf16", 9, 70, 0),        # empty prefill
     (2, 8, 2, 64, 0, 20, 0, 0.5, "bf16", 10, 8, 0),          # W = 0, empty prefill, region fills
+    (2, 16, 4, 128, 700, 40, 64, 0.2, "fp4", 11, 40, 0),     # 4-bit store
+    (1, 8, 8, 128, 30, 60, 64, 0.5, "fp4", 12, 60, 0),       # FP4: ring fills, tokens leave
+    (2, 24, 8, 128, 400, 30, 1, 0.4, "fp4", 13, 30, 0),      # FP4, W = 1: moved row pairs with the ring row
+    (2, 16, 2, 128, 300, 40, 7, 0.6, "fp4", 14, 40, 64),     # FP4, odd W
+    (2, 8, 2, 128, 200, 40, 0, 0.5, "fp4", 15, 40, 0),       # FP4, W = 0
 ]
 
 
@@ -61,8 +66,8 @@ def test_decode_step_matches_oracle(case):
     compare_state(ca, o, "prefill")
     kd, vd, qd = k.to(dev()), v.to(dev()), q.to(dev())
     keep_new = keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev())        # [S, B, Hkv]
-    ka = ca.k_amax.cpu().numpy() if kv_dtype == "fp8" else None
-    va = ca.v_amax.cpu().numpy() if kv_dtype == "fp8" else None
+    ka = ca.k_amax.cpu().numpy() if kv_dtype != "bf16" else None
+    va = ca.v_amax.cpu().numpy() if kv_dtype != "bf16" else None
     keep_eff = keep.clone()
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev())
     worst = 0.0
