@@ -62,6 +62,9 @@ def stored_rows_host(keep_np, T, W, S):
     return out
 
 
+ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
+
+
 def traffic_from_profile():
     """HBM bytes per attention launch from the committed counter summary, if
     it was taken on the current attention kernel source."""
@@ -82,7 +85,7 @@ def cpu_baseline(cfg, layers, outs, kv_dtype, budget_s=12.0):
     worst parity error of the GPU outputs of those layers."""
     import oracle
     from workload import make_layer
-    od = oracle.FP8 if kv_dtype == "fp8" else oracle.BF16
+    od = {"bf16": oracle.BF16, "fp8": oracle.FP8, "fp4": oracle.FP4}[kv_dtype]
     T, S, W = cfg.T, cfg.S, cfg.W
     nbytes, t_used, worst, done = 0, 0.0, 0.0, 0
     for l in layers:
@@ -93,7 +96,7 @@ def cpu_baseline(cfg, layers, outs, kv_dtype, budget_s=12.0):
                                   ka, va)
         t_used += time.perf_counter() - t0
         n = stored_rows_host(lay.keep.numpy(), T, W, S)[S - 1]
-        nbytes += int(n.sum()) * 2 * cfg.D * (1 if kv_dtype == "fp8" else 2)
+        nbytes += int(n.sum()) * 2 * ROW_BYTES[kv_dtype](cfg.D)
         got = outs[l].float().cpu().numpy()
         err = np.abs(got - ref)
         tol = 2e-3 + 1e-2 * np.abs(ref) + np.abs(ref) * 2.0 ** -8   # bf16 output rounding
@@ -116,6 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="qwen_c8")
+    ap.add_argument("--kv", choices=["bf16", "fp8", "fp4"], default=None,
+                    help="stored format (default: the config's; fp4 is the 4-bit variant)")
     ap.add_argument("--layers", type=int, default=0, help="0 = all layers of the config")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -146,11 +151,12 @@ def main():
         log("copied 64 MiB three times")
         return
     cfg = workload.CONFIGS[args.config]
+    kv = args.kv or cfg.kv_dtype
     L = args.layers or cfg.L
     B, Hq, Hkv, D, T, S, W = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.T, cfg.S, cfg.W
-    ebytes = 1 if cfg.kv_dtype == "fp8" else 2
+    row_bytes = ROW_BYTES[kv](D)
     log(f"config {cfg.name}: L={L} B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} S={S} W={W} "
-        f"{cfg.kv_dtype}; generating inputs")
+        f"{kv}; generating inputs")
 
     t0 = time.perf_counter()
     kd, vd, keepd, keep_new, qd, caches, nrows = [], [], [], [], [], [], []
@@ -162,7 +168,7 @@ def main():
         keep_new.append(lay.keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev))
         qd.append(lay.q.to(dev))
         nrows.append(stored_rows_host(lay.keep.numpy(), T, W, S))
-        c = CompactKVCache(B, Hkv, D, W, cfg.kv_dtype, dev)
+        c = CompactKVCache(B, Hkv, D, W, kv, dev)
         c.count(keepd[l], T, reserve=S)
         c.allocate()
         c.workspace(Hq, args.split)
@@ -172,7 +178,7 @@ def main():
     log(f"inputs resident in {time.perf_counter() - t0:.1f} s")
 
     # algorithmic bytes of every attention call: stored rows x 2 x D x e
-    attn_bytes = np.array([[int(nrows[l][s].sum()) * 2 * D * ebytes for l in range(L)]
+    attn_bytes = np.array([[int(nrows[l][s].sum()) * 2 * row_bytes for l in range(L)]
                            for s in range(S)], np.float64)          # [S, L]
     step_attn_bytes = float(attn_bytes.sum())
 
@@ -267,12 +273,13 @@ def main():
     value = step_attn_bytes / (ms * 1e-3) / 1e9
     tokens_per_s = B * S / (ms * 1e-3)
     achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
-    traffic = traffic_from_profile()
+    # the committed counters are those of the default run (this config, FP8)
+    traffic = traffic_from_profile() if (args.config, kv) == ("qwen_c8", "fp8") else None
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        cpu, worst, nl = cpu_baseline(cfg, list(range(L)), outs, cfg.kv_dtype)
+        cpu, worst, nl = cpu_baseline(cfg, list(range(L)), outs, kv)
         log(f"oracle sample: {nl} layers, GPU max abs err {worst:.2e}")
 
     rec = {
@@ -289,9 +296,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.L} layers x (Hq {Hq}, Hkv {Hkv}, D {D}), "
-                               f"ctx {T}, gen {S}, c={B}, {cfg.kv_dtype} compact KV, W={W}",
+                               f"ctx {T}, gen {S}, c={B}, {kv} compact KV, W={W}",
                    "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
-                   "kv_storage": cfg.kv_dtype, "split_tokens": args.split or "library default",
+                   "kv_storage": kv, "split_tokens": args.split or "library default",
                    "parallelism": "single GPU"},
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
