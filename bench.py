@@ -296,9 +296,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.L} layers x (Hq {Hq}, Hkv {Hkv}, D {D}), "
-                               f"ctx {T}, gen {S}, c={B}, {kv} compact KV, W={W}",
+                               f"ctx {T}, gen {S}, c={B}, {kv} compact KV, W={W}" +
+                               (", keep rate x1.5 at layer 0 falling linearly to x0.5 "
+                                "at the last layer" if cfg.budget == "pyramid" else ""),
                    "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
-                   "kv_storage": kv, "split_tokens": args.split or "library default",
+                   "kv_storage": kv, "budget": cfg.budget, "split_tokens": args.split or "library default",
                    "parallelism": "single GPU"},
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),

@@ -10,8 +10,9 @@ namespace {
 
 // Default rows per attention work unit: 512 for large pools (fewer units
 // and partials per segment), 256 otherwise (enough units to fill the chip).
-constexpr int kDefaultSplitLarge = 512, kDefaultSplitSmall = 256;
 constexpr int64_t kLargePoolRows = 1 << 16;
+constexpr int kGroups = 8;           // XCD groups of the attention's work map
+constexpr int kResidentPerGroup = 32;  // 8-wave workgroups one XCD keeps resident (one per CU)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -48,11 +49,30 @@ int32_t check_bf16_rows(const void* k, const void* v, int64_t sb, int64_t st, in
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? CDA_OK : CDA_ERR_HIP; }
 
+// Default work-unit size in 64-row tiles.  One unit is one workgroup, and
+// the units of a group all run on one XCD, which keeps one 8-wave workgroup
+// per CU resident: a group with more than 32 units starts its last ones a
+// whole unit late, which costs about half again the layer's time.  The
+// estimate of the units per group is the pool's tiles / tpu plus half a unit
+// of rounding per segment, spread over the 8 groups, plus one for the
+// unevenness of the group map (pool_rows counts capacity, so it errs high).
+// Small pools that fit at 4 tiles keep 4-tile units (4-wave workgroups, more
+// of them in flight); otherwise the smallest 8-wave unit that fits.  When
+// none fits (hundreds of segments) the extra rounds are unavoidable and
+// 8-tile units do the least work per round.
+int default_tpu(const cda_kv_cache* c) {
+  const double tiles = (double)c->pool_rows / CDA_SEG_ALIGN;
+  const double nh = (double)c->B * c->Hkv;
+  const auto fits = [&](int t) { return (tiles / t + nh / 2) / kGroups + 1 <= kResidentPerGroup; };
+  if (c->pool_rows < kLargePoolRows && fits(4)) return 4;
+  for (const int t : {8, 12, 16, 24, 32, 48, 64})
+    if (fits(t)) return t;
+  return 8;
+}
+
 int tiles_per_unit(const cda_kv_cache* c, int32_t split_tokens) {
-  const int s = split_tokens > 0
-                    ? split_tokens
-                    : (c->pool_rows >= kLargePoolRows ? kDefaultSplitLarge : kDefaultSplitSmall);
-  return (s + CDA_SEG_ALIGN - 1) / CDA_SEG_ALIGN;
+  if (split_tokens <= 0) return default_tpu(c);
+  return (split_tokens + CDA_SEG_ALIGN - 1) / CDA_SEG_ALIGN;
 }
 
 }  // namespace

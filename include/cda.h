@@ -190,9 +190,13 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  *   out          [B, Hq, D] contiguous, BF16 or F32 per out_dtype
  *   lse          optional F32 [B, Hq] (natural log), may be NULL
  *   split_tokens rows per work unit (one workgroup), rounded up to a
- *                multiple of 64; 0 = default (512 when pool_rows >= 65536,
- *                else 256).  Heads longer than one unit are split and their
- *                partials merged.
+ *                multiple of 64; 0 = default, chosen from pool_rows and
+ *                B*Hkv: the smallest of 256 (pools under 65536 rows only),
+ *                512, 768, 1024, 1536, ... 4096 for which the estimated
+ *                units per XCD group, (pool_rows/split + B*Hkv/2)/8 + 1,
+ *                stay at or below 32 (one resident workgroup per CU of an
+ *                XCD); 512 when none does.  Heads longer than one unit are
+ *                split and their partials merged.
  *   The call reads the device's XCD count (hipDeviceGetAttribute) on the
  *   current device; the attention may set CDA_DEVERR_XCD in cache->err.
  *   workspace    device scratch of at least cda_attn_workspace_bytes()

@@ -150,3 +150,35 @@ def test_decode_step_validation(lib):
     assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
     a.k, a.stride_h = 0x100000, 12                                     # stride not a multiple of 8
     assert f(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need, None) == 1
+
+
+def _default_split_rule(pool_rows, nh):
+    """The documented default: smallest unit (in 64-row tiles) whose estimated
+    units per XCD group, (pool_rows/64/t + nh/2)/8 + 1, stay <= 32."""
+    fits = lambda t: (pool_rows / 64 / t + nh / 2) / 8 + 1 <= 32
+    if pool_rows < 65536 and fits(4):
+        return 4
+    return next((t for t in (8, 12, 16, 24, 32, 48, 64) if fits(t)), 8)
+
+
+@pytest.mark.parametrize("B,Hkv,pool_rows", [
+    (1, 8, 11776),       # c = 1, ctx 8192: 256-row units
+    (8, 8, 98304),       # c = 8, 24 tiles a segment: 512
+    (8, 8, 126976),      # c = 8, 31 tiles a segment: 768
+    (8, 8, 61440),       # a small pool that does not fit at 4 tiles: 512
+    (8, 8, 262144),      # long segments (64 tiles): 1536
+    (64, 8, 1 << 22),    # 512 segments: nothing fits, 512
+    (1, 1, 64),
+])
+def test_default_split(lib, B, Hkv, pool_rows):
+    # the default shows in the workspace size, which falls with the unit size
+    L = lib.load()
+    c = _cache(lib, B=B, Hkv=Hkv, pool_rows=pool_rows)
+    t = _default_split_rule(pool_rows, B * Hkv)
+    assert L.cda_attn_workspace_bytes(C.byref(c), 4 * Hkv, 0) == \
+        L.cda_attn_workspace_bytes(C.byref(c), 4 * Hkv, 64 * t)
+    if pool_rows // (64 * t) != pool_rows // 512:     # the unit bound differs from 512's
+        assert L.cda_attn_workspace_bytes(C.byref(c), 4 * Hkv, 0) != \
+            L.cda_attn_workspace_bytes(C.byref(c), 4 * Hkv, 512)
+    expect = {11776: 4, 98304: 8, 126976: 12, 61440: 8, 262144: 24, 1 << 22: 8, 64: 4}
+    assert t == expect[pool_rows]

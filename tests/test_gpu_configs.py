@@ -1,5 +1,6 @@
 """Parity at the five workload shapes (ctx 8192, gen 128, c = 1 / 8 for the
-Llama-3.2-1B and Qwen3-8B attention shapes, plus the tiny case), in the
+Llama-3.2-1B and Qwen3-8B attention shapes, plus the tiny case, and the
+c = 8 shapes with the per-layer pyramid budget), in the
 launch configuration the benchmark times: prefill compaction of a layer
 bit-exact, all 128 decode appends bit-exact, and the attention output of
 every query head at several decode steps against the oracle.  Each decode
@@ -29,6 +30,13 @@ def test_config_layer(name, layer, mode):
 def test_config_layer_fp4(name, layer):
     # the Qwen3-8B shapes with the 4-bit store, as the benchmark's --kv fp4 runs them
     _run_config(name, layer, "step", "fp4")
+
+
+@pytest.mark.parametrize("name,layer", [("qwen_c8_pyramid", 0), ("qwen_c8_pyramid", 35),
+                                        ("llama_c8_pyramid", 15)])
+def test_config_layer_pyramid(name, layer):
+    # per-layer budget: layer 0 keeps 1.5x the flat rate, the last layer 0.5x
+    _run_config(name, layer, "step", workload.CONFIGS[name].kv_dtype)
 
 
 def _run_config(name, layer, mode, kv_dtype):

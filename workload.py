@@ -13,7 +13,9 @@ eviction predictor (page's DMS paragraph), which needs trained weights.
 
 Recipe per (config, layer), all on the CPU with one torch.Generator seeded
 ``seed * 1000 + layer``, drawn in this order:
-  1. keep rates r[B, Hkv]: a fixed rate, or U[lo, hi] per (sequence, head)
+  1. keep rates r[B, Hkv]: a fixed rate, or U[lo, hi] per (sequence, head),
+     times the layer's budget factor (1 for a flat budget; see
+     ``layer_budget``), capped at 1
   2. keep bits [B, Hkv, T + S] ~ Bernoulli(r)          (uint8 0/1)
   3. K [B, T + S, Hkv, D] ~ N(0, 1) in float32, then V likewise
   4. outlier channels (optional): a fraction of the layer's Hkv*D channels,
@@ -45,6 +47,7 @@ class Config:
     keep_hi: float
     outlier_frac: float
     seed: int
+    budget: str = "flat"   # "flat" or "pyramid" (keep rate falling with depth)
 
     @property
     def G(self) -> int:
@@ -74,10 +77,39 @@ CONFIGS = {
 
 def custom(name="custom", *, L=1, B=1, Hq=8, Hkv=2, D=64, T=256, S=1, W=16,
            kv_dtype="bf16", keep_lo=0.2, keep_hi=0.2, outlier_frac=0.0,
-           seed=12345) -> Config:
+           seed=12345, budget="flat") -> Config:
     """A free-form config for property and edge-case tests."""
     return Config(name, L, B, Hq, Hkv, D, T, S, W, kv_dtype, keep_lo, keep_hi,
-                  outlier_frac, seed)
+                  outlier_frac, seed, budget)
+
+
+def pyramid(cfg: Config) -> Config:
+    """The same workload with a per-layer budget that shrinks with depth.
+
+    PyramidInfer page ("PyramidInfer: Pyramid KV Cache Compression for
+    High-throughput LLM Inference"), abstract and technical-approach list:
+    the number of keys and values that matter falls layer by layer, so
+    deeper layers keep a shorter pivotal context.  The pages give no
+    schedule; the reading here is a linear one that keeps the model's mean
+    keep rate, so the flat and pyramid workloads store about the same bytes
+    and differ only in how the rows are spread over the layers.
+    """
+    return dataclasses.replace(cfg, name=cfg.name + "_pyramid", budget="pyramid")
+
+
+def layer_budget(cfg: Config, layer: int) -> float:
+    """Factor on the keep rates of one layer: 1 for a flat budget; for the
+    pyramid budget 1.5 at layer 0 falling linearly to 0.5 at layer L-1
+    (mean 1 over the layers)."""
+    if cfg.budget == "flat" or cfg.L == 1:
+        return 1.0
+    if cfg.budget != "pyramid":
+        raise ValueError(f"unknown budget {cfg.budget!r}")
+    return 1.5 - layer / (cfg.L - 1)
+
+
+# The two c = 8 workloads with the pyramid budget.
+CONFIGS.update({c.name: c for c in (pyramid(CONFIGS["llama_c8"]), pyramid(CONFIGS["qwen_c8"]))})
 
 
 @dataclasses.dataclass
@@ -104,6 +136,7 @@ def make_layer(cfg: Config, layer: int) -> Layer:
     else:
         rate = cfg.keep_lo + (cfg.keep_hi - cfg.keep_lo) * torch.rand(
             (B, Hkv), generator=g, dtype=torch.float32)
+    rate = (rate * layer_budget(cfg, layer)).clamp(max=1.0)
     keep = (torch.rand((B, Hkv, T + S), generator=g) < rate[..., None]).to(torch.uint8)
     k = torch.randn((B, T + S, Hkv, D), generator=g, dtype=torch.float32)
     v = torch.randn((B, T + S, Hkv, D), generator=g, dtype=torch.float32)
