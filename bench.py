@@ -44,6 +44,9 @@ HBM_PEAK_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "attn.hip")
 
 
+REFILL = 64   # --paged: rows of headroom a refill leaves, and steps between refills
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -125,6 +128,9 @@ def main():
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue every call from Python (no graphs)")
+    ap.add_argument("--paged", action="store_true",
+                    help="paged store: 64-row pages, no prefill reserve, a refill every 64 "
+                         "steps (inside the timed step)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode steps as kv_compact APPEND + decode_attn_compact")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -139,7 +145,7 @@ def main():
     import torch
 
     import workload
-    from compressed_decode_attention_amd import CompactKVCache, _lib
+    from compressed_decode_attention_amd import CompactKVCache, PagedKVCache, _lib
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -168,9 +174,14 @@ def main():
         keep_new.append(lay.keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev))
         qd.append(lay.q.to(dev))
         nrows.append(stored_rows_host(lay.keep.numpy(), T, W, S))
-        c = CompactKVCache(B, Hkv, D, W, kv, dev)
-        c.count(keepd[l], T, reserve=S)
-        c.allocate()
+        if args.paged:
+            # pages for each segment's last rows plus one refill's headroom
+            pages = -(-(nrows[l][S - 1].astype(np.int64) + REFILL) // 64)
+            c = PagedKVCache(B, Hkv, D, W, int(pages.sum()), int(pages.max()), kv, dev)
+        else:
+            c = CompactKVCache(B, Hkv, D, W, kv, dev)
+            c.count(keepd[l], T, reserve=S)
+            c.allocate()
         c.workspace(Hq, args.split)
         caches.append(c)
     outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
@@ -185,13 +196,19 @@ def main():
     def prefill_all():
         for l in range(L):
             c = caches[l]
-            c.count(keepd[l], T, reserve=S)
-            c.pack(kd[l], vd[l], keepd[l], T)
+            if args.paged:
+                c.init()
+                c.admit(0, kd[l], vd[l], keepd[l], T, reserve=0)
+            else:
+                c.count(keepd[l], T, reserve=S)
+                c.pack(kd[l], vd[l], keepd[l], T)
 
     def decode_all():
         for s in range(S):
             for l in range(L):
                 c = caches[l]
+                if args.paged and s % REFILL == 0:
+                    c.refill(REFILL)
                 if args.unfused:
                     c.append(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s])
                     c.attention(qd[l][s], out=outs[l], split_tokens=args.split)
@@ -274,7 +291,8 @@ def main():
     tokens_per_s = B * S / (ms * 1e-3)
     achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
     # the committed counters are those of the default run (this config, FP8)
-    traffic = traffic_from_profile() if (args.config, kv) == ("qwen_c8", "fp8") else None
+    traffic = (traffic_from_profile() if (args.config, kv) == ("qwen_c8", "fp8") and
+               not args.paged else None)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -300,7 +318,9 @@ def main():
                                (", keep rate x1.5 at layer 0 falling linearly to x0.5 "
                                 "at the last layer" if cfg.budget == "pyramid" else ""),
                    "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
-                   "kv_storage": kv, "budget": cfg.budget, "split_tokens": args.split or "library default",
+                   "kv_storage": kv, "budget": cfg.budget,
+                   "store": (f"paged: 64-row pages, no prefill reserve, refill every {REFILL} steps"
+                             if args.paged else f"contiguous segments, reserve {S} rows"), "split_tokens": args.split or "library default",
                    "parallelism": "single GPU"},
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -310,6 +330,7 @@ def main():
         "launch": ("eager" if args.eager else "hip graphs") +
                   (", append + attention" if args.unfused else ", fused decode step"),
         "kv_bytes_per_decode_step": round(float(attn_bytes.sum(axis=1).mean())),
+        "kv_pool_mb": round(sum(2 * c.pool_rows * row_bytes for c in caches) / 1e6, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -15,13 +15,14 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD, CDA_KV_BF16, CDA_KV_FP4_E2M1,
-                   CDA_KV_FP8_E4M3,
-                   CDA_OP_APPEND, CDA_OP_COUNT, CDA_OP_PACK, CDA_OUT_BF16, CDA_OUT_F32,
-                   CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
+from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_PAGES, CDA_DEVERR_POOL, CDA_DEVERR_XCD,
+                   CDA_KV_BF16, CDA_KV_FP4_E2M1, CDA_KV_FP8_E4M3, CDA_OP_APPEND, CDA_OP_COUNT,
+                   CDA_OP_PACK, CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE, CDA_OUT_BF16,
+                   CDA_OUT_F32, CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
-__all__ = ["CompactKVCache", "kv_compact", "decode_attn_compact", "decode_step_compact", "CdaError",
-           "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY", "CDA_DEVERR_POOL", "CDA_DEVERR_XCD"]
+__all__ = ["CompactKVCache", "PagedKVCache", "kv_compact", "decode_attn_compact",
+           "decode_step_compact", "CdaError", "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY",
+           "CDA_DEVERR_POOL", "CDA_DEVERR_XCD", "CDA_DEVERR_PAGES"]
 
 _DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3, "fp4": CDA_KV_FP4_E2M1}
 _ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
@@ -36,9 +37,12 @@ def _ptr(t) -> int:
 
 
 def _compact_args(cache: "CompactKVCache", op: int, T: int = 0, reserve: int = 0,
-                  scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None) -> CdaCompactArgs:
+                  scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None,
+                  seq_begin: int = 0, seq_count: int = 0) -> CdaCompactArgs:
     a = CdaCompactArgs()
     a.op, a.T, a.reserve, a.scale_mode = op, T, reserve, scale_mode
+    a.seq_begin, a.seq_count = seq_begin, seq_count
+    nb = seq_count if seq_count > 0 else cache.B     # sequences the inputs hold
     if keep is not None:
         if keep.dtype != torch.uint8:
             raise TypeError("keep must be uint8")
@@ -47,8 +51,8 @@ def _compact_args(cache: "CompactKVCache", op: int, T: int = 0, reserve: int = 0
                 raise ValueError("APPEND keep must be a contiguous [B, Hkv] uint8 tensor")
             a.keep_ld = 1
         else:
-            if keep.dim() != 3 or keep.shape[0] != cache.B or keep.shape[1] != cache.Hkv:
-                raise ValueError("keep must be [B, Hkv, >=T]")
+            if keep.dim() != 3 or keep.shape[0] != nb or keep.shape[1] != cache.Hkv:
+                raise ValueError("keep must be [sequences, Hkv, >=T]")
             if keep.shape[2] < T or keep.stride(2) != 1 or keep.stride(0) != cache.Hkv * keep.stride(1):
                 raise ValueError("keep rows must be contiguous with a uniform pitch")
             a.keep_ld = keep.stride(1)
@@ -59,22 +63,27 @@ def _compact_args(cache: "CompactKVCache", op: int, T: int = 0, reserve: int = 0
                 raise ValueError("k, v must be bfloat16 with contiguous rows of D elements")
         if k.stride() != v.stride():
             raise ValueError("k and v must share strides")
-        if op == CDA_OP_PACK:      # [B, >=T, Hkv, D]
+        if op == CDA_OP_PACK:      # [sequences, >=T, Hkv, D]
+            if k.shape[0] != nb or k.shape[2] != cache.Hkv or v.shape != k.shape:
+                raise ValueError("k, v must be [sequences, >=T, Hkv, D]")
             a.stride_b, a.stride_t, a.stride_h = k.stride(0), k.stride(1), k.stride(2)
         else:                      # [B, Hkv, D]
             a.stride_b, a.stride_t, a.stride_h = k.stride(0), 0, k.stride(1)
         a.k, a.v = _ptr(k), _ptr(v)
     if dst_out is not None:
-        if dst_out.dtype != torch.int32 or not dst_out.is_contiguous() or dst_out.numel() < cache.B * cache.Hkv * T:
-            raise ValueError("dst_out must be a contiguous int32 tensor of B*Hkv*T elements")
+        if dst_out.dtype != torch.int32 or not dst_out.is_contiguous() or dst_out.numel() < nb * cache.Hkv * T:
+            raise ValueError("dst_out must be a contiguous int32 tensor of sequences*Hkv*T elements")
         a.dst_out = _ptr(dst_out)
     return a
 
 
 def kv_compact(cache: "CompactKVCache", op: int, *, T: int = 0, reserve: int = 0,
-               scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None) -> None:
-    """One kv_compact call (COUNT, PACK or APPEND) on ``cache``'s stream."""
-    a = _compact_args(cache, op, T, reserve, scale_mode, keep, k, v, dst_out)
+               scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None,
+               seq_begin: int = 0, seq_count: int = 0) -> None:
+    """One kv_compact call (COUNT, PACK, APPEND, or PAGE_INIT / REFILL /
+    RELEASE of a paged store) on ``cache``'s stream."""
+    a = _compact_args(cache, op, T, reserve, scale_mode, keep, k, v, dst_out, seq_begin,
+                      seq_count)
     st = _lib.kv_compact(cache.struct, a, _stream(cache.device))
     if st != 0:
         raise CdaError(st, "kv_compact")
@@ -159,6 +168,8 @@ class CompactKVCache:
         self._ws = {}
         self.struct = CdaKvCache()
         self._refresh()
+
+    paged = False
 
     def _refresh(self):
         s = self.struct
@@ -261,3 +272,92 @@ class CompactKVCache:
         t = self.k_pool[: self.pool_rows * rb].view(-1, 4, kl, 4, 4, 4, 16)
         # [tile, m, j, kg, gh, gl, byte] -> [tile, gh, m, gl, j, kg, byte]
         return t.permute(0, 4, 1, 5, 2, 3, 6).reshape(self.pool_rows, rb)
+
+
+class PagedKVCache(CompactKVCache):
+    """One layer's paged compact store: a pool of ``n_pages`` 64-row pages
+    shared by all B*Hkv segments, a page table of ``max_pages`` entries per
+    segment and a device stack of free pages.  Sequences are admitted
+    (COUNT + PACK of a range) and released one range at a time; REFILL keeps
+    every live segment ``reserve`` compact rows ahead of its data."""
+
+    paged = True
+
+    def __init__(self, B: int, Hkv: int, D: int, W: int, n_pages: int, max_pages: int,
+                 kv_dtype: str = "bf16", device="cuda"):
+        super().__init__(B, Hkv, D, W, kv_dtype, device)
+        if n_pages < 1 or max_pages < 1:
+            raise ValueError("n_pages >= 1 and max_pages >= 1 are required")
+        dev = self.device
+        nh = B * Hkv
+        self.n_pages, self.max_pages = n_pages, max_pages
+        self.page_table = torch.full((max(nh * max_pages, 1),), -1, dtype=torch.int32, device=dev)
+        self.free_pages = torch.zeros(max(n_pages, 1), dtype=torch.int32, device=dev)
+        self.free_top = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.pool_rows = n_pages * CDA_SEG_ALIGN
+        nbytes = max(self.pool_rows, 1) * self.row_bytes
+        self.k_pool = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.v_pool = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self._refresh()
+        self.init()
+
+    def _refresh(self):
+        super()._refresh()
+        s = self.struct
+        if getattr(self, "page_table", None) is None:   # during the base constructor
+            return
+        s.seg_base = 0
+        s.page_table = _ptr(self.page_table)
+        s.max_pages = self.max_pages
+        s.reserved1 = 0
+        s.free_pages, s.free_top = _ptr(self.free_pages), _ptr(self.free_top)
+
+    def init(self) -> None:
+        """Every page free, every sequence idle (PAGE_INIT)."""
+        kv_compact(self, CDA_OP_PAGE_INIT)
+
+    def admit(self, b0: int, k, v, keep, T: int, reserve: int = 0, scale_mode: int = 0,
+              dst_out=None) -> None:
+        """Prefill of sequences [b0, b0 + n) from k, v [n, >=T, Hkv, D] bf16 and
+        keep [n, Hkv, >=T]: COUNT (takes the pages) then PACK.  With too few
+        free pages the range stays idle and CDA_DEVERR_PAGES is set."""
+        n = keep.shape[0]
+        kv_compact(self, CDA_OP_COUNT, T=T, reserve=reserve, keep=keep, dst_out=dst_out,
+                   seq_begin=b0, seq_count=n)
+        kv_compact(self, CDA_OP_PACK, T=T, scale_mode=scale_mode, keep=keep, k=k, v=v,
+                   seq_begin=b0, seq_count=n)
+
+    def refill(self, reserve: int = CDA_SEG_ALIGN) -> None:
+        """Tops every live segment up to ``reserve`` free compact rows."""
+        kv_compact(self, CDA_OP_REFILL, reserve=reserve)
+
+    def release(self, b0: int, n: int = 1) -> None:
+        """Returns the pages of sequences [b0, b0 + n) and makes them idle."""
+        kv_compact(self, CDA_OP_RELEASE, seq_begin=b0, seq_count=n)
+
+    def count(self, *a, **kw):
+        raise TypeError("a paged store admits sequences with admit()")
+
+    def allocate(self, *a, **kw):
+        raise TypeError("a paged store's pool is sized by n_pages")
+
+    def compact(self, *a, **kw):
+        raise TypeError("a paged store admits sequences with admit()")
+
+    # ---- inspection (synchronise)
+    def free_count(self) -> int:
+        return int(self.free_top.item())
+
+    def pages(self) -> torch.Tensor:
+        """Page tables as [B*Hkv, max_pages] (CPU)."""
+        return self.page_table[: self.B * self.Hkv * self.max_pages].view(
+            self.B * self.Hkv, self.max_pages).cpu()
+
+    def segment_rows(self, i: int, rows: int):
+        """Rows [0, rows) of segment i as (K bytes, V bytes), each
+        [rows, row_bytes], gathered through its page table."""
+        pt = self.pages()[i]
+        idx = torch.arange(rows)
+        pool_row = (pt[idx // CDA_SEG_ALIGN].to(torch.int64) * CDA_SEG_ALIGN +
+                    idx % CDA_SEG_ALIGN).to(self.device)
+        return self.k_rows()[pool_row], self.v_rows()[pool_row]

@@ -8,8 +8,6 @@
 
 namespace {
 
-// Default rows per attention work unit: 512 for large pools (fewer units
-// and partials per segment), 256 otherwise (enough units to fill the chip).
 constexpr int64_t kLargePoolRows = 1 << 16;
 constexpr int kGroups = 8;           // XCD groups of the attention's work map
 constexpr int kResidentPerGroup = 32;  // 8-wave workgroups one XCD keeps resident (one per CU)
@@ -26,7 +24,27 @@ int32_t check_cache(const cda_kv_cache* c) {
     return CDA_ERR_UNSUPPORTED;
   if (c->kv_dtype == CDA_KV_FP4_E2M1 && c->D != 128) return CDA_ERR_UNSUPPORTED;
   if ((int64_t)c->B * c->Hkv > (1 << 24)) return CDA_ERR_INVALID_ARG;
-  if (!c->seg_base || !c->seg_cap || !c->comp_len || !c->err) return CDA_ERR_INVALID_ARG;
+  if (!c->seg_cap || !c->comp_len || !c->err || c->reserved1 != 0) return CDA_ERR_INVALID_ARG;
+  if (c->page_table) {   // paged store
+    if (c->max_pages < 1 || (int64_t)c->B * c->Hkv * c->max_pages > INT32_MAX)
+      return CDA_ERR_INVALID_ARG;
+    if (!c->free_pages || !c->free_top || !c->pos) return CDA_ERR_INVALID_ARG;
+    if (c->W > 0 && !c->ring_keep) return CDA_ERR_INVALID_ARG;
+    if (c->pool_rows < CDA_SEG_ALIGN || c->pool_rows / CDA_SEG_ALIGN > INT32_MAX)
+      return CDA_ERR_INVALID_ARG;   // at least one page
+  } else if (!c->seg_base) {
+    return CDA_ERR_INVALID_ARG;
+  }
+  return CDA_OK;
+}
+
+// The sequence range of COUNT, PACK and RELEASE: paged store only (both 0
+// for contiguous segments); seq_count 0 = the whole batch.
+int32_t check_range(const cda_kv_cache* c, const cda_compact_args* a) {
+  if (!c->page_table) return (a->seq_begin == 0 && a->seq_count == 0) ? CDA_OK : CDA_ERR_INVALID_ARG;
+  if (a->seq_count == 0) return a->seq_begin == 0 ? CDA_OK : CDA_ERR_INVALID_ARG;
+  if (a->seq_count < 0 || a->seq_begin < 0 || a->seq_begin > c->B - a->seq_count)
+    return CDA_ERR_INVALID_ARG;
   return CDA_OK;
 }
 
@@ -84,8 +102,17 @@ int32_t kv_compact(const cda_kv_cache* c, const cda_compact_args* a, void* strea
   if (st != CDA_OK) return st;
   if (!a) return CDA_ERR_INVALID_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t nh = (int64_t)c->B * c->Hkv;
+  if ((st = check_range(c, a)) != CDA_OK) return st;
+  // segments the call covers (the range's, or the batch's)
+  const int64_t nh = (int64_t)(a->seq_count > 0 ? a->seq_count : c->B) * c->Hkv;
   switch (a->op) {
+    case CDA_OP_PAGE_INIT:
+    case CDA_OP_REFILL:
+    case CDA_OP_RELEASE:
+      if (!c->page_table) return CDA_ERR_INVALID_ARG;
+      if (a->op == CDA_OP_REFILL && (a->reserve < 0 || a->reserve > (1 << 28)))
+        return CDA_ERR_INVALID_ARG;
+      return hip_status(cda::launch_page_op(*c, *a, s));
     case CDA_OP_COUNT:
     case CDA_OP_PACK: {
       if (a->T < 0 || a->T > (1 << 24) || a->keep_ld < a->T) return CDA_ERR_INVALID_ARG;
@@ -103,6 +130,7 @@ int32_t kv_compact(const cda_kv_cache* c, const cda_compact_args* a, void* strea
     }
     case CDA_OP_APPEND: {
       if ((st = check_pools(c)) != CDA_OK) return st;
+      if (a->seq_count != 0) return CDA_ERR_INVALID_ARG;   // always the whole batch
       if (nh > 0) {
         if (!a->keep) return CDA_ERR_INVALID_ARG;
         if ((st = check_bf16_rows(a->k, a->v, a->stride_b, 0, a->stride_h)) != CDA_OK) return st;
@@ -170,7 +198,8 @@ int32_t decode_step_compact(const cda_kv_cache* c, const cda_compact_args* a, co
   int32_t st = check_attention(c, q, Hq, out, out_dtype, lse, split_tokens, workspace,
                                workspace_bytes, &tpu);
   if (st != CDA_OK) return st;
-  if (!a || a->op != CDA_OP_APPEND) return CDA_ERR_INVALID_ARG;
+  if (!a || a->op != CDA_OP_APPEND || a->seq_begin != 0 || a->seq_count != 0)
+    return CDA_ERR_INVALID_ARG;
   if (c->B > 0) {
     if (!a->keep) return CDA_ERR_INVALID_ARG;
     if ((st = check_bf16_rows(a->k, a->v, a->stride_b, 0, a->stride_h)) != CDA_OK) return st;

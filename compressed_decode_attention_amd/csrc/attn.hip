@@ -97,7 +97,7 @@ struct AttnParams {
   uint8_t* k_pool;
   uint8_t* v_pool;
   int64_t pool_rows;
-  const int64_t* seg_base;
+  const int64_t* seg_base;     // contiguous segments
   const int32_t* seg_cap;
   int32_t* comp_len;
   int32_t* pos;
@@ -122,6 +122,9 @@ struct AttnParams {
   int Hkv, G, Hq, W, nh, tpu, out_f32;
   int per_xcd;         // XCD-local mode: workgroups per segment group
   float sm_scale;
+  // paged store only (last, so that the other fields keep their offsets)
+  const int32_t* page_table;   // [nh][max_pages]
+  int max_pages, n_pages;
 };
 
 __device__ __forceinline__ int units_of(int n, int tpu) {
@@ -234,7 +237,9 @@ struct Unit {
 // grp + xs, grp + 2xs, ...  Wave-level: every wave of a workgroup calls it
 // with the same arguments and gets the same answer.  It scans all of the
 // group's segments and returns their unit count in `total`.
-template <bool Q, bool APP>
+// Paged store (PG): no seg_base; P keeps its sign (an idle sequence, pos <
+// 0, plans no rows in a decode step).
+template <bool Q, bool APP, bool PG>
 __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, int k, int lane,
                                           Unit& un, int& total) {
   const bool mapped = p.seg_group != nullptr;
@@ -247,10 +252,10 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
     long long sbi = 0;
     float ka = 0.0f, va = 0.0f;
     if (hi < p.nh) {
-      Pi = max(p.pos[hi / p.Hkv], 0);
+      Pi = PG ? p.pos[hi / p.Hkv] : max(p.pos[hi / p.Hkv], 0);
       capi = max(p.seg_cap[hi], 0);
       cli = min(max(p.comp_len[hi], 0), capi);
-      sbi = p.seg_base[hi];
+      if (!PG) sbi = p.seg_base[hi];
       if (Q) {
         ka = p.k_amax[hi];
         va = p.v_amax[hi];
@@ -260,7 +265,7 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
       // load of this round trip waits behind it or behind a branch
       const uint8_t gb = *(mapped ? p.seg_group + hi : reinterpret_cast<const uint8_t*>(p.seg_cap + hi));
       const bool in_group = !mapped || (gb & 7) == grp;
-      ni = APP ? p.W + capi : min(p.W, Pi) + cli;
+      ni = APP ? ((PG && Pi < 0) ? 0 : p.W + capi) : min(p.W, max(Pi, 0)) + cli;
       Ui = in_group ? units_of(ni, p.tpu) : 0;
     }
     int x = Ui;
@@ -299,6 +304,9 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
 // the new token takes), with the error bits the append raises -- the rules
 // of the APPEND operation of kv_compact.  Written by the last unit of the
 // segment.
+// Paged store (PG): rows are checked against their pages where they are
+// written, not here.
+template <bool PG>
 __device__ __forceinline__ void commit_segment(const AttnParams& p, int i, const Unit& un, int rk) {
   const int W = p.W;
   const int64_t sb = un.sb;
@@ -307,17 +315,18 @@ __device__ __forceinline__ void commit_segment(const AttnParams& p, int i, const
     const int slot = un.P % W;
     if (un.P >= W && rk) {
       if (un.cl < un.cap) {
-        if (sb + slot >= p.pool_rows || sb + W + un.cl >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
+        if (!PG && (sb + slot >= p.pool_rows || sb + W + un.cl >= p.pool_rows))
+          errbits |= CDA_DEVERR_POOL;
         cl_new = un.cl + 1;
       } else {
         errbits |= CDA_DEVERR_CAPACITY;
       }
     }
-    if (sb + slot >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
+    if (!PG && sb + slot >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
     p.ring_keep[(int64_t)i * W + slot] = (uint8_t)un.kn;
   } else if (un.kn) {
     if (un.cl < un.cap) {
-      if (sb + un.cl >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
+      if (!PG && sb + un.cl >= p.pool_rows) errbits |= CDA_DEVERR_POOL;
       cl_new = un.cl + 1;
     } else {
       errbits |= CDA_DEVERR_CAPACITY;
@@ -337,13 +346,24 @@ __device__ __forceinline__ int q_d0(int s, int kg) {
   return 32 * s + 8 * kg;
 }
 
+// Paged store: page of tile t of segment i (the index is clamped into the
+// segment's page-table row, so the load never leaves the table; -1 past it).
+__device__ __forceinline__ int page_of(const AttnParams& p, int i, int t) {
+  const int pg = p.page_table[(int64_t)i * p.max_pages + min(max(t, 0), p.max_pages - 1)];
+  return t < p.max_pages ? pg : -1;
+}
+__device__ __forceinline__ bool page_ok(const AttnParams& p, int pg) {
+  return (unsigned)pg < (unsigned)p.n_pages;
+}
+
 // Mask of the bytes of dword w (bytes 4w .. 4w+3) that lie below `lim`.
 __device__ __forceinline__ uint32_t bytes_below(int lim, int w) {
   const int k = lim - 4 * w;
   return k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
 }
 
-template <int KV, int D, bool XL, int NW, bool APP>
+// PG: the paged store (tiles through the page table; idle sequences).
+template <int KV, int D, bool XL, int NW, bool APP, bool PG>
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
   constexpr int NTH = 64 * NW;              // threads of the workgroup
@@ -371,7 +391,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   for (int k = XL ? (w / kXcdGroups) : w;; k += p.per_xcd) {
     Unit un;
     int total = 0;
-    if (!find_unit<Q, APP>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
+    if (!find_unit<Q, APP, PG>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
     // every load of the plan has been used: say so, so that no later write to
     // a register it used waits for the loads issued after this point
     __builtin_amdgcn_s_waitcnt(0);
@@ -382,21 +402,27 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     const int b = i / p.Hkv, h = i - b * p.Hkv;
     const int G = p.G;
     const int64_t sb = un.sb;
-    const int64_t in_pool = p.pool_rows - sb;
+    // rows of the segment inside the pool (paged: every page is checked)
+    const int64_t in_pool = PG ? INT64_MAX : p.pool_rows - sb;
     const int ntiles = (un.n + kTile - 1) / kTile;
     const int t_begin = (k - un.first) * p.tpu;
     const int t_end = min(t_begin + p.tpu, ntiles);
     const int slot = XL ? k * kXcdGroups + grp : k;   // this unit's partial
     const float ks = kv_scale<KV>(un.ka);
     const float vs = kv_scale<KV>(un.va);
+    // paged store: the page of this wave's first tile, loaded before anything
+    // else so that one round trip covers it
+    int pg_next = PG ? page_of(p, i, t_begin + wave) : 0;
+    const bool idle = PG && APP && un.P < 0;   // paged: a sequence not in use
+    const int P = APP ? (PG ? max(un.P, 0) : un.P) : 0;   // contiguous: already >= 0
 
     // ---- decode step: rows with data, the new token's row and its tile
     int n = un.n, new_row = -1, t_own = -1;
-    const int ring_slot = (APP && p.W > 0) ? un.P % p.W : 0;   // ring row of P
+    const int ring_slot = (APP && p.W > 0) ? P % p.W : 0;   // ring row of P
     if (APP) {
-      const StepRows st = step_rows(p.W, un.P, ring_slot, un.cl, un.cap, un.kn);
-      n = st.n_pre;
-      if (st.new_row >= 0 && st.new_row < in_pool) {
+      const StepRows st = step_rows(p.W, P, ring_slot, un.cl, un.cap, un.kn);
+      n = idle ? 0 : st.n_pre;
+      if (!idle && st.new_row >= 0 && st.new_row < in_pool) {
         new_row = st.new_row;
         t_own = new_row / kTile;
       }
@@ -406,7 +432,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
     // decode step: where the keep bit of the token leaving the ring (ring
     // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
     // needed, and tested only after the loads that must not wait for it.
-    const bool leaving = APP && p.W > 0 && un.P >= p.W;
+    const bool leaving = APP && !idle && p.W > 0 && P >= p.W;
+    // paged store, wave 0 of the owner unit: pages of the new token's row and
+    // of the compact row the leaving token may move to (same round trip as
+    // the tile's page)
+    int pg_own = -1, pg_dst = -1;
+    if (PG && owner_unit && wave == 0) {
+      pg_own = page_of(p, i, t_own);
+      pg_dst = page_of(p, i, (p.W + un.cl) / kTile);
+    }
     const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + ring_slot : p.keep_new + i)
                              : nullptr;
     // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per
@@ -449,8 +483,11 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         nv = p.v_new[off];
       }
       const int rs = new_row & (kTile - 1);
-      const uint8_t* kt = p.k_pool + (sb + (new_row - rs)) * (int64_t)RB;
-      const uint8_t* vt = p.v_pool + (sb + (new_row - rs)) * (int64_t)RB;
+      // paged: a missing page reads tile 0 (unused: nothing is written then)
+      const int64_t trow = PG ? (page_ok(p, pg_own) ? (int64_t)pg_own * kTile : 0)
+                              : sb + (new_row - rs);
+      const uint8_t* kt = p.k_pool + trow * (int64_t)RB;
+      const uint8_t* vt = p.v_pool + trow * (int64_t)RB;
       okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
@@ -532,13 +569,22 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       const int valid = (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
       const bool own = APP && t == t_own;   // the tile of the leaving token's row
       if (valid <= 0) break;
+      int64_t trow = sb + r0;   // pool row of the tile
+      if (PG) {
+        const int pg = __builtin_amdgcn_readfirstlane(pg_next);
+        if (!page_ok(p, pg)) {   // a tile with data and no page: inconsistent store
+          if (lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+          break;
+        }
+        trow = (int64_t)pg * kTile;
+      }
       {
         const bool full = valid == kTile;
         // decode step: the leaving token's keep bit, issued ahead of the tile
         int rko = 0;
         if (APP) rko = *rkp;
-        const uint8_t* ktile = p.k_pool + (sb + r0) * (int64_t)RB;
-        const uint8_t* vtile = p.v_pool + (sb + r0) * (int64_t)RB;
+        const uint8_t* ktile = p.k_pool + trow * (int64_t)RB;
+        const uint8_t* vtile = p.v_pool + trow * (int64_t)RB;
 
         // -- loads: K rows for the 4 token groups (each instruction 1 KB of the
         //    permuted K tile), V columns for the NT d tiles
@@ -564,6 +610,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
               vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
                   vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
         }
+        // paged: the page of this wave's next tile, in flight with this one
+        if (PG) pg_next = page_of(p, i, t + NW);
 
         // -- S^T = K . Q^T, 16 tokens per MFMA row block
         f32x4 s[4];
@@ -595,7 +643,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         //    tile loads waits for the keep bit
         __asm__ volatile("" : "+v"(rko));   // keeps the test from moving up
         const bool moved_t = own && leaving && rko != 0 && un.cl < un.cap &&
-                             sb + p.W + un.cl < p.pool_rows;
+                             (PG || sb + p.W + un.cl < p.pool_rows);
         const int mrow = (own && leaving && !moved_t) ? (new_row & (kTile - 1)) : -1;
 
         // -- online softmax over this tile; lane (g, kg) owns tokens 16kg + 4m + r
@@ -721,13 +769,21 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         // W + cl if it is kept; read back from the pool (this wave's reads
         // finish before the new row is written over it)
         const int rs = new_row & (kTile - 1);
-        uint8_t* kt = p.k_pool + (sb + (new_row - rs)) * (int64_t)RB;
-        uint8_t* vt = p.v_pool + (sb + (new_row - rs)) * (int64_t)RB;
-        const bool moved = leaving && rkc != 0 && un.cl < un.cap && sb + p.W + un.cl < p.pool_rows;
+        // paged: rows whose page is missing are not written (CDA_DEVERR_POOL)
+        const bool own_ok = !PG || page_ok(p, pg_own);
+        const bool dst_ok = !PG || page_ok(p, pg_dst);
+        const int64_t trow = PG ? (int64_t)pg_own * kTile : sb + (new_row - rs);
+        uint8_t* kt = p.k_pool + trow * (int64_t)RB;
+        uint8_t* vt = p.v_pool + trow * (int64_t)RB;
+        const bool wants_move = leaving && rkc != 0 && un.cl < un.cap;
+        const bool moved = wants_move && own_ok && dst_ok &&
+                           (PG || sb + p.W + un.cl < p.pool_rows);
+        if (PG && lane == 0 && ((wants_move && !moved) || !own_ok)) atomicOr(p.err, CDA_DEVERR_POOL);
         if (moved) {   // from the copy read at the start of the unit
           const int to = p.W + un.cl, rt = to & (kTile - 1);
-          uint8_t* kd = p.k_pool + (sb + (to - rt)) * (int64_t)RB;
-          uint8_t* vd = p.v_pool + (sb + (to - rt)) * (int64_t)RB;
+          const int64_t drow = PG ? (int64_t)pg_dst * kTile : sb + (to - rt);
+          uint8_t* kd = p.k_pool + drow * (int64_t)RB;
+          uint8_t* vd = p.v_pool + drow * (int64_t)RB;
           constexpr int KC = RB / 16;   // 16-byte chunks per K row
           if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
 #pragma unroll
@@ -746,29 +802,31 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
         // byte of this lane's first element in the row, and the lane's bytes
         constexpr int LB = FP4 ? EPL / 2 : EPL * E;
         const int kb0 = FP4 ? d0n / 2 : d0n * E;
-        uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
-        if (LB == 4)
-          *reinterpret_cast<uint32_t*>(kdst) = kc;
-        else if (LB == 2)
-          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
-        else
-          *kdst = (uint8_t)kc;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          if (FP4)   // after the moved row's write, which may share the byte
-            nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
-          else if (FP8)
-            vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
+        if (own_ok) {
+          uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
+          if (LB == 4)
+            *reinterpret_cast<uint32_t*>(kdst) = kc;
+          else if (LB == 2)
+            *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
           else
-            reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
+            *kdst = (uint8_t)kc;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            if (FP4)   // after the moved row's write, which may share the byte
+              nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
+            else if (FP8)
+              vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
+            else
+              reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
+          }
         }
       }
     }
     // decode step, single-unit segment: every wave of the workgroup has read
     // the segment's metadata (the owner's keep bit included)
     int seq_prev = -1;
-    if (APP && U == 1 && tid == 0) {
-      commit_segment(p, i, un, leaving && rkc != 0);
+    if (APP && !idle && U == 1 && tid == 0) {
+      commit_segment<PG>(p, i, un, leaving && rkc != 0);
       seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -825,8 +883,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
       __syncthreads();
       if (s_last) {
         // decode step: every unit of the segment has read its metadata
-        if (APP && tid == 0) {
-          commit_segment(p, i, un, leaving && rkc != 0);
+        if (APP && !idle && tid == 0) {
+          commit_segment<PG>(p, i, un, leaving && rkc != 0);
           seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -900,11 +958,11 @@ int device_xcds() {
   return nx;
 }
 
-template <bool APP>
+template <bool APP, bool PG>
 void launch_variant(int kv, int D, bool xl, int nw, dim3 grid, hipStream_t s, const AttnParams& p) {
 #define CDA_LAUNCH_ATTN(F, DD, X)                                                      \
-  (nw == 8 ? attn_kernel<F, DD, X, 8, APP><<<grid, 512, 0, s>>>(p)                     \
-           : attn_kernel<F, DD, X, 4, APP><<<grid, 256, 0, s>>>(p))
+  (nw == 8 ? attn_kernel<F, DD, X, 8, APP, PG><<<grid, 512, 0, s>>>(p)                 \
+           : attn_kernel<F, DD, X, 4, APP, PG><<<grid, 256, 0, s>>>(p))
   if (kv == kKvFP4) {   // D = 128 only
     if (xl) CDA_LAUNCH_ATTN(kKvFP4, 128, true); else CDA_LAUNCH_ATTN(kKvFP4, 128, false);
   } else if (kv == kKvFP8) {
@@ -955,6 +1013,9 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.v_pool = static_cast<uint8_t*>(c.v_pool);
   p.pool_rows = c.pool_rows;
   p.seg_base = c.seg_base;
+  p.page_table = c.page_table;
+  p.max_pages = c.max_pages;
+  p.n_pages = (int)(c.pool_rows / kTile);
   p.seg_cap = c.seg_cap;
   p.comp_len = c.comp_len;
   p.pos = c.pos;
@@ -997,10 +1058,14 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   const dim3 grid((unsigned)(xl ? (int64_t)p.per_xcd * kXcdGroups : units));
   const int kv = c.kv_dtype;
   const int nw = tpu >= 8 ? 8 : 4;   // waves per workgroup: one tile each per pass
-  if (step)
-    launch_variant<true>(kv, c.D, xl, nw, grid, s, p);
-  else
-    launch_variant<false>(kv, c.D, xl, nw, grid, s, p);
+  const bool pg = c.page_table != nullptr;
+  if (step) {
+    if (pg) launch_variant<true, true>(kv, c.D, xl, nw, grid, s, p);
+    else launch_variant<true, false>(kv, c.D, xl, nw, grid, s, p);
+  } else {
+    if (pg) launch_variant<false, true>(kv, c.D, xl, nw, grid, s, p);
+    else launch_variant<false, false>(kv, c.D, xl, nw, grid, s, p);
+  }
   return hipGetLastError();
 }
 

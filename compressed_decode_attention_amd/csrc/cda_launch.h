@@ -13,6 +13,8 @@ namespace cda {
 hipError_t launch_count(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s);
 hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s);
 hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s);
+// Paged store: PAGE_INIT, REFILL and RELEASE.
+hipError_t launch_page_op(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s);
 
 // Work units of the attention kernel: an upper bound on the number of
 // workgroups it launches (one per unit) for this cache and split.

@@ -7,6 +7,12 @@
 //   amax_kernel      per-segment absmax of the stored prefill K and V (FP8)
 //   pack_kernel      stored prefill rows -> pool tiles (BF16 copy / FP8 encode)
 //   append_kernel    one decode step: ring exit -> compact tail, new token -> ring
+//   page_init_kernel / page_kernel   the paged store's page bookkeeping
+//
+// Paged store: the pool's 64-row tiles are pages; a segment's tile t is page
+// page_table[i * max_pages + t].  COUNT, PACK and RELEASE then act on a range
+// of sequences (their inputs indexed from the range's first sequence), and
+// sequences with pos < 0 are idle: the append leaves them alone.
 //
 // All of these run once per prefill or move at most one row per segment per
 // step; the decode hot loop is the attention kernel.
@@ -21,13 +27,14 @@ namespace {
 
 // ---------------------------------------------------------------- COUNT
 
+// Workgroup x: segment i0 + x, whose keep row (and dst_out row) is row x.
 __global__ __launch_bounds__(kBlock) void count_kernel(
-    const uint8_t* __restrict__ keep, int64_t keep_ld, int T, int W, int reserve,
+    const uint8_t* __restrict__ keep, int64_t keep_ld, int T, int W, int reserve, int i0,
     int32_t* __restrict__ comp_len, int32_t* __restrict__ seg_cap,
     int32_t* __restrict__ dst_out) {
   __shared__ int smem[4];
-  const int i = blockIdx.x, tid = threadIdx.x;
-  const uint8_t* row = keep + (int64_t)i * keep_ld;
+  const int x = blockIdx.x, i = i0 + x, tid = threadIdx.x;
+  const uint8_t* row = keep + (int64_t)x * keep_ld;
   const int ncand = T - W > 0 ? T - W : 0;       // positions older than the window
   const int limit = dst_out ? T : ncand;
   int running = 0;
@@ -47,7 +54,7 @@ __global__ __launch_bounds__(kBlock) void count_kernel(
     int total;
     int rank = block_exclusive_scan(cnt, &total, smem) + running;
     if (dst_out) {
-      int32_t* d = dst_out + (int64_t)i * T;
+      int32_t* d = dst_out + (int64_t)x * T;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int p = p0 + j;
@@ -145,27 +152,30 @@ __device__ __forceinline__ uint32_t abs_bits(uint32_t word, int half) {
   return ((word >> (16 * half)) & 0x7FFFu) << 16;
 }
 
-__global__ void amax_zero_kernel(int nh, float* __restrict__ k_amax, float* __restrict__ v_amax) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+__global__ void amax_zero_kernel(int i0, int nh, float* __restrict__ k_amax,
+                                 float* __restrict__ v_amax) {
+  const int i = i0 + blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nh) {
     k_amax[i] = 0.0f;
     v_amax[i] = 0.0f;
   }
 }
 
-// Workgroup (segment i, chunk c): absmax of K and V over the stored prefill
-// rows of positions [256c, 256c+256), folded into k_amax / v_amax with an
-// unsigned atomic max on the magnitude bit patterns.
+// Workgroup (x, chunk c): absmax of K and V of segment i0 + x over the
+// stored prefill rows of positions [256c, 256c+256), folded into k_amax /
+// v_amax with an unsigned atomic max on the magnitude bit patterns.  Its
+// inputs are row x of keep and sequence x / Hkv of k and v.
 __global__ __launch_bounds__(kBlock) void amax_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t sb, int64_t st,
     int64_t sh, const uint8_t* __restrict__ keep, int64_t keep_ld, int T, int W, int Hkv,
-    int D, float* __restrict__ k_amax, float* __restrict__ v_amax) {
+    int D, int i0, float* __restrict__ k_amax, float* __restrict__ v_amax) {
   __shared__ int smem[4];
   __shared__ int s_pos[kBlock];
   __shared__ uint32_t red[2][kBlock / 64];
-  const int i = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const int b = i / Hkv, h = i - b * Hkv;
-  const uint8_t* krow = keep + (int64_t)i * keep_ld;
+  const int x = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int i = i0 + x;
+  const int b = x / Hkv, h = x - b * Hkv;
+  const uint8_t* krow = keep + (int64_t)x * keep_ld;
   const int pp = c * kBlock + tid;
   const int stored = pp < T && (pp >= T - W || krow[pp] != 0);
   int nst;
@@ -225,7 +235,11 @@ struct PackParams {
   const uint8_t* keep;
   int64_t keep_ld;
   int T, W, Hkv, D;
-  const int64_t* seg_base;
+  int i0;                    // first segment of the range (paged store)
+  const int64_t* seg_base;   // contiguous segments
+  const int32_t* page_table; // paged store: [nh][max_pages], or NULL
+  const int32_t* seg_cap;
+  int max_pages, n_pages;
   const int32_t* comp_len;
   int64_t pool_rows;
   uint8_t* k_pool;
@@ -265,12 +279,18 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
   __shared__ int smem[4];
   __shared__ __attribute__((aligned(16))) uint8_t s_k[kTile * RB];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[D * VS];
-  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int x = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = p.i0 + x;                     // segment; x indexes the inputs
   const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int bx = x / p.Hkv;                   // sequence index in the inputs
+  const bool paged = p.page_table != nullptr;
   const int T = p.T, W = p.W;
   const int ncand = T - W > 0 ? T - W : 0;  // positions older than the window
   const int nring = min(W, T);
-  const uint8_t* krow = p.keep + (int64_t)i * p.keep_ld;
+  const uint8_t* krow = p.keep + (int64_t)x * p.keep_ld;
+  // paged: a sequence COUNT left idle (no pages) is skipped (pos stays -1;
+  // once admitted it reads 0 or T, never below 0)
+  if (paged && p.pos[b] < 0) return;
   const bool row16 = (reinterpret_cast<uintptr_t>(krow) & 15) == 0;   // 16-byte keep loads
   // this thread's keep bytes of the first scan pass of the first tile, read
   // before the segment's metadata (one round trip for both)
@@ -280,8 +300,9 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
     pre0 = *reinterpret_cast<const u32x4*>(krow + tid * kScan);
     pre1 = *reinterpret_cast<const u32x4*>(krow + tid * kScan + 16);
   }
-  const int64_t sb = p.seg_base[i];
-  const int64_t alloc = p.seg_base[i + 1] - sb;
+  // rows the segment has room for: its pages, or its aligned contiguous size
+  const int64_t sb = paged ? 0 : p.seg_base[i];
+  const int64_t alloc = paged ? (int64_t)W + max(p.seg_cap[i], 0) : p.seg_base[i + 1] - sb;
   const int cl = min(max(p.comp_len[i], 0), ncand);   // from COUNT
   // tiles holding ring rows or stored rows, inside the segment's rows
   const int64_t rows = min((int64_t)max(nring + cl, W), alloc);
@@ -365,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
       kin[k] = u32x4{0, 0, 0, 0};
       vin[k] = u32x4{0, 0, 0, 0};
       if (any >= 0) {
-        const int64_t off = (int64_t)b * p.sb + (int64_t)(has[k] ? src : any) * p.st +
+        const int64_t off = (int64_t)bx * p.sb + (int64_t)(has[k] ? src : any) * p.st +
                             (int64_t)h * p.sh + d0;
         kin[k] = *reinterpret_cast<const u32x4*>(p.k + off);
         vin[k] = *reinterpret_cast<const u32x4*>(p.v + off);
@@ -417,11 +438,17 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
 
     // ---- stores: both tiles as 16-byte chunks.  Tiles and pool_rows are
     // multiples of 64 rows, so a tile is wholly inside the pool or wholly
-    // outside it (a pool smaller than seg_base[B*Hkv]); outside, the rows
-    // with data are flagged and nothing is written.
-    if (p.pool_rows - (sb + r0) >= kTile) {
-      uint8_t* kt = p.k_pool + (sb + r0) * (int64_t)RB;
-      uint8_t* vt = p.v_pool + (sb + r0) * (int64_t)RB;
+    // outside it (a pool smaller than seg_base[B*Hkv], or a page-table entry
+    // that is not a page); outside, the rows with data are flagged and
+    // nothing is written.
+    int64_t tr = sb + r0;   // pool row of the tile
+    if (paged) {
+      const int pg = p.page_table[(int64_t)i * p.max_pages + min(j, p.max_pages - 1)];
+      tr = (j < p.max_pages && pg >= 0 && pg < p.n_pages) ? (int64_t)pg * kTile : p.pool_rows;
+    }
+    if (p.pool_rows - tr >= kTile) {
+      uint8_t* kt = p.k_pool + tr * (int64_t)RB;
+      uint8_t* vt = p.v_pool + tr * (int64_t)RB;
       for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
         *reinterpret_cast<u32x4*>(kt + ch * 16) = *reinterpret_cast<const u32x4*>(s_k + ch * 16);
         u32x4 vv;
@@ -458,7 +485,9 @@ struct AppendParams {
   int64_t sb, sh;
   const uint8_t* keep;
   int W, Hkv, D;
-  const int64_t* seg_base;
+  const int64_t* seg_base;   // contiguous segments
+  const int32_t* page_table; // paged store: [nh][max_pages], or NULL
+  int max_pages, n_pages;
   const int32_t* seg_cap;
   int32_t* comp_len;
   int32_t* pos;
@@ -488,7 +517,9 @@ struct Row8 {
 // elements share bytes with the neighbouring row, so they are written as
 // read-modify-writes of their nibble (no other thread writes those bytes:
 // a byte's two rows are the moved row or the new row and a row nobody
-// writes in this step).
+// writes in this step).  Paged store: the three rows' pages come from the
+// page table first (one more round trip); an idle sequence (pos < 0) is
+// left as it is.
 template <int KV>
 __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
   typedef typename std::conditional<KV == kKvBF16, uint16_t, uint8_t>::type elem_t;
@@ -499,12 +530,25 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
   const int RB = kv_row_bytes(KV, D);
   const int cpr = D / 8;                       // 8-element chunks per row
   const int P = p.pos[b];
+  const bool paged = p.page_table != nullptr;
+  if (paged && P < 0) return;       // idle sequence (uniform over the workgroup)
   elem_t* vp = reinterpret_cast<elem_t*>(p.v_pool);
   for (int h0 = 0; h0 < p.Hkv; h0 += kBlock / cpr) {
     const int h = h0 + tid / cpr, d0 = (tid % cpr) * 8;
     if (h >= p.Hkv) continue;
     const int64_t i = (int64_t)b * p.Hkv + h;
-    const int64_t base = p.seg_base[i];
+    const int64_t base = paged ? 0 : p.seg_base[i];
+    // pool row of segment row r (paged: through the page table; a missing
+    // page gives the out-of-pool row pool_rows)
+    const int32_t* pt = paged ? p.page_table + i * p.max_pages : nullptr;
+    auto prow = [&](int r) -> int64_t {
+      if (!paged) return base + r;
+      if (r < 0) return p.pool_rows;
+      const int t = r / kTile;
+      const int pg = pt[min(t, p.max_pages - 1)];
+      return (t < p.max_pages && pg >= 0 && pg < p.n_pages) ? (int64_t)pg * kTile + r % kTile
+                                                             : p.pool_rows;
+    };
     const int cl0 = p.comp_len[i];
     const int cap = p.seg_cap[i];
     const int kept = p.keep[i] != 0;
@@ -521,7 +565,7 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
     if (W > 0) {
       const int exit_pos = P - W;
       const int eslot = exit_pos >= 0 ? exit_pos % W : 0;
-      const int64_t slot = base + eslot;
+      const int64_t slot = prow(eslot);
       // the exiting row's keep bit and slice are read whether or not it moves
       // (unconditional loads, clamped into the pool, so they share one trip)
       const bool readable = slot < p.pool_rows;
@@ -539,13 +583,13 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
       if (exit_pos >= 0 && rk) {
         if (cl < cap) {
           from = slot;
-          to = base + W + cl;
+          to = prow(W + cl);
           ++cl;
         } else {
           full = 1;
         }
       }
-      nw = base + P % W;
+      nw = prow(P % W);
       if (from >= 0 && (!readable || to >= p.pool_rows)) {
         from = -1;
         bad = 1;
@@ -562,7 +606,7 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
       }
     } else if (kept) {
       if (cl < cap) {
-        nw = base + cl;
+        nw = prow(cl);
         ++cl;
       } else {
         full = 1;
@@ -613,29 +657,282 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
   if (tid == 0) p.pos[b] = P + 1;
 }
 
+// ---------------------------------------------------------------- PAGES
+
+// Every page free (stacked so that page 0 is on top), every page-table entry
+// -1, every sequence idle with empty segments.  Grid-stride over the largest
+// of the arrays.
+__global__ __launch_bounds__(kBlock) void page_init_kernel(
+    int n_pages, int nh, int max_pages, int B, int W, int32_t* __restrict__ free_pages,
+    int32_t* __restrict__ free_top, int32_t* __restrict__ page_table,
+    int32_t* __restrict__ comp_len, int32_t* __restrict__ seg_cap, int32_t* __restrict__ pos,
+    uint8_t* __restrict__ ring_keep, uint8_t* __restrict__ seg_group, int32_t* __restrict__ err) {
+  const int64_t n_pt = (int64_t)nh * max_pages, n_rk = (int64_t)nh * W;
+  const int64_t n = max(max((int64_t)n_pages, n_pt), max(n_rk, (int64_t)max(nh, B)));
+  for (int64_t x = (int64_t)blockIdx.x * kBlock + threadIdx.x; x < n;
+       x += (int64_t)gridDim.x * kBlock) {
+    if (x < n_pages) free_pages[x] = n_pages - 1 - (int32_t)x;
+    if (x < n_pt) page_table[x] = -1;
+    if (x < n_rk) ring_keep[x] = 0;
+    if (x < nh) {
+      comp_len[x] = 0;
+      seg_cap[x] = 0;
+      if (seg_group) seg_group[x] = (uint8_t)(x & 7);
+    }
+    if (x < B) pos[x] = -1;
+    if (x == 0) {
+      *free_top = n_pages;
+      *err = 0;
+    }
+  }
+}
+
+enum PageOp { kPageAdmit = 0, kPageRefill = 1, kPageRelease = 2 };
+
+struct PageParams {
+  int op;
+  int nh, Hkv, W, max_pages, n_pages;
+  int i0, i1;          // admit, release: segments [i0, i1) (whole sequences)
+  int reserve;         // admit, refill: spare compact rows
+  int32_t* page_table;
+  int32_t* free_pages;
+  int32_t* free_top;
+  int32_t* seg_cap;
+  int32_t* comp_len;
+  int32_t* pos;
+  uint8_t* ring_keep;
+  uint8_t* seg_group;
+  int32_t* err;
+};
+
+__device__ __forceinline__ int pages_for(int64_t rows) { return (int)((rows + kTile - 1) / kTile); }
+
+// Pages held by segment i of a live sequence: seg_cap = 64 * pages - W, and
+// a live segment's pages always cover the W ring rows.
+__device__ __forceinline__ int pages_held(const PageParams& p, int i) {
+  return p.pos[i / p.Hkv] >= 0 ? (p.W + max(p.seg_cap[i], 0)) / kTile : 0;
+}
+
+// One workgroup: the page bookkeeping of one operation, then the group map
+// over the pages every segment holds afterwards.  Pages are taken from the
+// top of the stack (the k-th taken is free_pages[top - 1 - k]) and returned
+// on top of it, in segment order and then row order, by prefix sums over
+// the segments: the result does not depend on thread timing.
+//   admit   segments [i0, i1) of idle sequences, comp_len from COUNT: each
+//           gets pages_for(W + comp_len + reserve) pages, all segments or
+//           none (CDA_DEVERR_PAGES: stack short, or a segment over
+//           max_pages); its sequences become live with pos = 0.
+//   refill  every live segment is topped up to pages_for(W + comp_len +
+//           reserve) pages (at most max_pages); a short stack serves the
+//           earlier segments first and sets CDA_DEVERR_PAGES.
+//   release segments [i0, i1): their pages go back on the stack, the
+//           segments are emptied and their sequences become idle (pos = -1).
+__global__ __launch_bounds__(kBlock) void page_kernel(PageParams p) {
+  __shared__ int smem[4];
+  __shared__ int s_top, s_over;
+  __shared__ int s_tiles[kBalanceMax];
+  const int tid = threadIdx.x, mp = p.max_pages, W = p.W;
+  const bool balance = p.seg_group != nullptr && p.nh <= kBalanceMax;
+  if (tid == 0) {
+    s_top = min(max(*p.free_top, 0), p.n_pages);   // every stack index stays inside
+    s_over = 0;
+  }
+  // pages held before the operation (the group map's weights)
+  if (balance)
+    for (int i = tid; i < p.nh; i += kBlock) s_tiles[i] = pages_held(p, i);
+  __syncthreads();
+  const int top = s_top;
+  int taken = 0, given = 0;   // pages taken from / returned to the stack (block totals)
+
+  if (p.op == kPageAdmit) {
+    // pass 1: the total, and whether a segment needs more than max_pages
+    for (int base = p.i0; base < p.i1; base += kBlock) {
+      const int i = base + tid;
+      int need = 0;
+      if (i < p.i1) {
+        need = pages_for((int64_t)W + max(p.comp_len[i], 0) + p.reserve);
+        if (need > mp) s_over = 1;
+      }
+      int total;
+      block_exclusive_scan(need, &total, smem);
+      taken += total;
+    }
+    __syncthreads();
+    const bool ok = s_over == 0 && taken <= top;
+    if (!ok) taken = 0;
+    // pass 2: the pages, or the idle state
+    int k0 = 0;
+    for (int base = p.i0; base < p.i1; base += kBlock) {
+      const int i = base + tid;
+      int need = 0;
+      if (i < p.i1) need = pages_for((int64_t)W + max(p.comp_len[i], 0) + p.reserve);
+      int total;
+      const int ex = block_exclusive_scan(need, &total, smem) + k0;
+      k0 += total;
+      if (i < p.i1) {
+        int32_t* row = p.page_table + (int64_t)i * mp;
+        const int got = ok ? need : 0;
+        for (int j = 0; j < got; ++j) row[j] = p.free_pages[top - 1 - (ex + j)];
+        for (int j = got; j < mp; ++j) row[j] = -1;
+        p.seg_cap[i] = ok ? got * kTile - W : 0;
+        if (!ok) p.comp_len[i] = 0;
+        if (balance) s_tiles[i] = got;
+      }
+    }
+    for (int b = p.i0 / p.Hkv + tid; b < p.i1 / p.Hkv; b += kBlock) p.pos[b] = ok ? 0 : -1;
+    if (tid == 0 && !ok) atomicOr(p.err, CDA_DEVERR_PAGES);
+  } else if (p.op == kPageRefill) {
+    int k0 = 0;
+    for (int base = 0; base < p.nh; base += kBlock) {
+      const int i = base + tid;
+      int cur = 0, add = 0;
+      if (i < p.nh && p.pos[i / p.Hkv] >= 0) {
+        cur = pages_held(p, i);
+        const int want = min(pages_for((int64_t)W + max(p.comp_len[i], 0) + p.reserve), mp);
+        add = max(want - cur, 0);
+      }
+      int total;
+      const int ex = block_exclusive_scan(add, &total, smem) + k0;
+      k0 += total;
+      if (add > 0) {
+        const int got = max(0, min(add, top - ex));   // what is left on the stack
+        int32_t* row = p.page_table + (int64_t)i * mp;
+        for (int j = 0; j < got; ++j) row[cur + j] = p.free_pages[top - 1 - (ex + j)];
+        p.seg_cap[i] = (cur + got) * kTile - W;
+        if (balance) s_tiles[i] = cur + got;
+      }
+    }
+    taken = min(k0, top);
+    if (tid == 0 && k0 > top) atomicOr(p.err, CDA_DEVERR_PAGES);
+  } else {   // kPageRelease
+    int k0 = 0;
+    for (int base = p.i0; base < p.i1; base += kBlock) {
+      const int i = base + tid;
+      const int cur = i < p.i1 ? min(pages_held(p, i), mp) : 0;
+      int total;
+      const int ex = block_exclusive_scan(cur, &total, smem) + k0;
+      k0 += total;
+      if (i < p.i1) {
+        int32_t* row = p.page_table + (int64_t)i * mp;
+        for (int j = 0; j < cur; ++j) {
+          if (top + ex + j < p.n_pages) p.free_pages[top + ex + j] = row[j];
+          row[j] = -1;
+        }
+        p.seg_cap[i] = 0;
+        p.comp_len[i] = 0;
+        for (int r = 0; r < W; ++r) p.ring_keep[(int64_t)i * W + r] = 0;
+        if (balance) s_tiles[i] = 0;
+      }
+    }
+    __syncthreads();   // every thread has read pos (pages_held) of the range
+    for (int b = p.i0 / p.Hkv + tid; b < p.i1 / p.Hkv; b += kBlock) p.pos[b] = -1;
+    given = k0;
+  }
+  if (tid == 0) *p.free_top = min(top - taken + given, p.n_pages);
+
+  // ---- group map: segments ranked by pages held, dealt in snake order
+  __syncthreads();
+  if (p.seg_group) {
+    if (balance) {
+      for (int i = tid; i < p.nh; i += kBlock) {
+        const int wi = s_tiles[i];
+        int rank = 0;
+        for (int j = 0; j < p.nh; ++j) {
+          const int wj = s_tiles[j];
+          rank += (wj > wi) || (wj == wi && j < i);
+        }
+        const int round = rank >> 3, slot = rank & 7;
+        p.seg_group[i] = (uint8_t)((round & 1) ? 7 - slot : slot);
+      }
+    } else {
+      for (int i = tid; i < p.nh; i += kBlock) p.seg_group[i] = (uint8_t)(i & 7);
+    }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+// The sequences a COUNT / PACK / RELEASE call covers: [b0, b0 + nb).
+void seq_range(const cda_kv_cache& c, const cda_compact_args& a, int& b0, int& nb) {
+  b0 = a.seq_count > 0 ? a.seq_begin : 0;
+  nb = a.seq_count > 0 ? a.seq_count : c.B;
+}
+
+PageParams page_params(const cda_kv_cache& c, int op, int b0, int nb, int reserve) {
+  PageParams p;
+  p.op = op;
+  p.nh = c.B * c.Hkv;
+  p.Hkv = c.Hkv;
+  p.W = c.W;
+  p.max_pages = c.max_pages;
+  p.n_pages = (int)(c.pool_rows / kTile);
+  p.i0 = b0 * c.Hkv;
+  p.i1 = (b0 + nb) * c.Hkv;
+  p.reserve = reserve;
+  p.page_table = c.page_table;
+  p.free_pages = c.free_pages;
+  p.free_top = c.free_top;
+  p.seg_cap = c.seg_cap;
+  p.comp_len = c.comp_len;
+  p.pos = c.pos;
+  p.ring_keep = c.ring_keep;
+  p.seg_group = c.seg_group;
+  p.err = c.err;
+  return p;
+}
+
 }  // namespace
 
 hipError_t launch_count(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
-  const int nh = c.B * c.Hkv;
-  if (nh > 0) {
-    count_kernel<<<nh, kBlock, 0, s>>>(a.keep, a.keep_ld, a.T, c.W, a.reserve, c.comp_len,
-                                       c.seg_cap, a.dst_out);
+  int b0, nb;
+  seq_range(c, a, b0, nb);
+  const int nh = c.B * c.Hkv, nr = nb * c.Hkv;
+  if (nr > 0) {
+    count_kernel<<<nr, kBlock, 0, s>>>(a.keep, a.keep_ld, a.T, c.W, a.reserve, b0 * c.Hkv,
+                                       c.comp_len, c.seg_cap, a.dst_out);
   }
-  seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err, c.seg_group);
+  if (c.page_table)
+    page_kernel<<<1, kBlock, 0, s>>>(page_params(c, kPageAdmit, b0, nb, a.reserve));
+  else
+    seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err, c.seg_group);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_op(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
+  if (a.op == CDA_OP_PAGE_INIT) {
+    const int nh = c.B * c.Hkv;
+    const int64_t n = std::max(std::max(c.pool_rows / kTile, (int64_t)nh * c.max_pages),
+                               std::max((int64_t)nh * c.W, (int64_t)std::max(nh, c.B)));
+    const int grid = (int)std::min<int64_t>(std::max<int64_t>((n + kBlock - 1) / kBlock, 1), 1024);
+    page_init_kernel<<<grid, kBlock, 0, s>>>((int)(c.pool_rows / kTile), nh, c.max_pages, c.B,
+                                             c.W, c.free_pages, c.free_top, c.page_table,
+                                             c.comp_len, c.seg_cap, c.pos, c.ring_keep,
+                                             c.seg_group, c.err);
+  } else {
+    int b0, nb;
+    seq_range(c, a, b0, nb);
+    const int op = a.op == CDA_OP_REFILL ? kPageRefill : kPageRelease;
+    page_kernel<<<1, kBlock, 0, s>>>(page_params(c, op, b0, nb, a.reserve));
+  }
   return hipGetLastError();
 }
 
 constexpr int kPackY = 32;   // workgroups per segment of the pack kernel
 
 hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
-  const int nh = c.B * c.Hkv;
-  if (nh == 0) return hipGetLastError();
-  const dim3 grid(nh, a.T > 0 ? (a.T + kBlock - 1) / kBlock : 1);
+  int b0, nb;
+  seq_range(c, a, b0, nb);
+  const int nr = nb * c.Hkv, i0 = b0 * c.Hkv;   // the range's segments
+  if (nr == 0) return hipGetLastError();
+  const dim3 grid(nr, a.T > 0 ? (a.T + kBlock - 1) / kBlock : 1);
   if (c.kv_dtype != CDA_KV_BF16 && a.scale_mode == 0) {
-    amax_zero_kernel<<<(nh + kBlock - 1) / kBlock, kBlock, 0, s>>>(nh, c.k_amax, c.v_amax);
+    amax_zero_kernel<<<(nr + kBlock - 1) / kBlock, kBlock, 0, s>>>(i0, i0 + nr, c.k_amax,
+                                                                  c.v_amax);
     amax_kernel<<<grid, kBlock, 0, s>>>(static_cast<const uint16_t*>(a.k),
                                       static_cast<const uint16_t*>(a.v), a.stride_b, a.stride_t,
-                                      a.stride_h, a.keep, a.keep_ld, a.T, c.W, c.Hkv, c.D,
+                                      a.stride_h, a.keep, a.keep_ld, a.T, c.W, c.Hkv, c.D, i0,
                                       c.k_amax, c.v_amax);
   }
   PackParams p;
@@ -650,7 +947,12 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   p.W = c.W;
   p.Hkv = c.Hkv;
   p.D = c.D;
+  p.i0 = i0;
   p.seg_base = c.seg_base;
+  p.page_table = c.page_table;
+  p.seg_cap = c.seg_cap;
+  p.max_pages = c.max_pages;
+  p.n_pages = (int)(c.pool_rows / kTile);
   p.comp_len = c.comp_len;
   p.pool_rows = c.pool_rows;
   p.k_pool = static_cast<uint8_t*>(c.k_pool);
@@ -663,7 +965,7 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   // tiles of a segment: at most ceil(max(T, W) / 64); workgroups take every
   // kPackY-th of them
   const int max_tiles = (int)((std::max<int64_t>(a.T, c.W) + kTile - 1) / kTile);
-  const dim3 pgrid(nh, std::max(1, std::min(max_tiles, kPackY)));
+  const dim3 pgrid(nr, std::max(1, std::min(max_tiles, kPackY)));
   if (c.kv_dtype == CDA_KV_FP4_E2M1) {
     pack_kernel<kKvFP4, 128><<<pgrid, kBlock, 0, s>>>(p);   // FP4 needs D = 128
   } else if (c.kv_dtype == CDA_KV_FP8_E4M3) {
@@ -688,6 +990,9 @@ hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipSt
   p.Hkv = c.Hkv;
   p.D = c.D;
   p.seg_base = c.seg_base;
+  p.page_table = c.page_table;
+  p.max_pages = c.max_pages;
+  p.n_pages = (int)(c.pool_rows / kTile);
   p.seg_cap = c.seg_cap;
   p.comp_len = c.comp_len;
   p.pos = c.pos;

@@ -63,6 +63,42 @@
  *   FP4: code = E2M1_RNE_SATURATE(f32(x) * inv), inv = 6 / amax, value =
  *   code * s, s = amax / 6; NaN encodes as +-6 with its sign (E2M1 has no
  *   NaN).  FP4 needs D = 128 (a K row must fill 64 bytes).
+ *
+ * Paged store (optional; cache->page_table != NULL).  The release
+ * paragraph's point, that the compact store hands evicted memory back to
+ * the allocator, carried across requests: the pools are pool_rows / 64
+ * pages, a page being one 64-row tile in the formats above, and segment
+ * row r (ring and compact rows numbered as above) is row r mod 64 of page
+ * page_table[i * max_pages + r / 64].  A segment's pages are the leading
+ * entries of its page-table row that are not -1 (the rest are -1), and
+ * seg_cap = max(64 * pages - W, 0); seg_base is not used.  Free pages are a
+ * stack: free_pages[0 .. *free_top), taken from the top.  Sequences are
+ * admitted and released one range at a time (seq_begin, seq_count of
+ * cda_compact_args), so requests of different lengths come and go without
+ * moving any other sequence's rows:
+ *   PAGE_INIT  every page free (free_pages[j] = n - 1 - j, so pages are
+ *              first taken in ascending order), page tables -1, pos = -1
+ *              (idle), comp_len = seg_cap = 0, err = 0.
+ *   COUNT      as for contiguous segments, for the range's sequences, then
+ *              takes ceil((W + comp_len + reserve) / 64) pages per segment
+ *              (segments in index order, pages in row order, each the top
+ *              of the stack), all or nothing: CDA_DEVERR_PAGES if the stack
+ *              is short or a segment needs more than max_pages.
+ *   PACK       as for contiguous segments, for the range (pos[b] = T);
+ *              sequences that COUNT left idle are skipped.
+ *   APPEND, decode_step_compact: as for contiguous segments, over all B
+ *              sequences; idle ones (pos[b] < 0) are left untouched.
+ *   REFILL     for every live segment (pos >= 0), in index order, takes
+ *              pages until 64 * pages >= W + comp_len + reserve (at most
+ *              max_pages); a short stack serves earlier segments first and
+ *              sets CDA_DEVERR_PAGES.  An append uses at most one compact
+ *              row per segment, so REFILL with reserve R once every R
+ *              steps means no append finds its segment full.
+ *   RELEASE    returns the pages of the range's segments to the stack
+ *              (segments in index order, pages in row order, so the last
+ *              page released is the next taken) and makes them idle.
+ * With one range covering the batch right after PAGE_INIT, the pages are
+ * laid out exactly as the contiguous segments of the same capacities.
  */
 #ifndef CDA_H
 #define CDA_H
@@ -74,7 +110,7 @@
 extern "C" {
 #endif
 
-#define CDA_VERSION 1
+#define CDA_VERSION 2
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
 
@@ -91,6 +127,8 @@ enum cda_status {
  * the host sees them only after it synchronises and copies the word). */
 #define CDA_DEVERR_CAPACITY 1   /* APPEND: a segment's compact region was full; that token was dropped */
 #define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written */
+#define CDA_DEVERR_PAGES 8      /* paged COUNT / REFILL: not enough free pages, or a segment
+                                   would need more than max_pages (see the paged store) */
 #define CDA_DEVERR_XCD 4        /* attention: the workgroups w of one residue w mod 8 did not all
                                    run on one XCD, which the XCD-local merge of split heads
                                    needs (the dispatcher deals workgroups to the XCDs round
@@ -98,7 +136,8 @@ enum cda_status {
 
 enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1, CDA_KV_FP4_E2M1 = 2 };
 enum cda_out_dtype { CDA_OUT_BF16 = 0, CDA_OUT_F32 = 1 };
-enum cda_compact_op { CDA_OP_COUNT = 0, CDA_OP_PACK = 1, CDA_OP_APPEND = 2 };
+enum cda_compact_op { CDA_OP_COUNT = 0, CDA_OP_PACK = 1, CDA_OP_APPEND = 2,
+                      CDA_OP_PAGE_INIT = 3, CDA_OP_REFILL = 4, CDA_OP_RELEASE = 5 };
 
 /*
  * One layer's compact store.  The struct itself is host memory read by
@@ -127,7 +166,14 @@ typedef struct cda_kv_cache {
                            of workgroups, one XCD's worth, that takes the attention work of
                            each segment, chosen to even out the capacity W + seg_cap per group.
                            NULL, or more than 512 segments: segment i goes to group i mod 8.
-                           Scheduling only: results do not depend on it */
+                           Scheduling only: results do not depend on it.  Paged store:
+                           rewritten by COUNT, REFILL and RELEASE, over the pages held */
+    int32_t *page_table;   /* NULL: contiguous segments.  Else the paged store:
+                              [B*Hkv*max_pages] page ids, -1 = none */
+    int32_t max_pages;     /* paged: page-table entries per segment, >= 1 */
+    int32_t reserved1;     /* must be 0 */
+    int32_t *free_pages;   /* paged: [pool_rows/64] stack of free page ids (pool_rows >= 64) */
+    int32_t *free_top;     /* paged: [1] number of free pages */
 } cda_kv_cache;
 
 /*
@@ -148,6 +194,11 @@ typedef struct cda_compact_args {
     int64_t stride_b, stride_t, stride_h;
     int32_t *dst_out;   /* COUNT, optional (may be NULL): [B*Hkv*T] int32, the segment row
                            each position is stored in (ring p mod W or W + rank), -1 if evicted */
+    int32_t seq_begin;  /* paged COUNT, PACK, RELEASE: sequences [seq_begin, seq_begin +
+                           seq_count); keep, k, v and dst_out then start at sequence seq_begin
+                           (their sequence index is b - seq_begin).  seq_count = 0: all B
+                           (seq_begin 0).  Contiguous segments: both 0 */
+    int32_t seq_count;
 } cda_compact_args;
 
 /*
@@ -165,6 +216,8 @@ typedef struct cda_compact_args {
  *   computes k_amax/v_amax first.  Pools are written in whole 64-row
  *   tiles: unused rows inside a tile that holds ring or stored rows are set
  *   to zero; tiles past them are not written.
+ * CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE: paged store only (see
+ *   the paged store above; REFILL reads reserve, RELEASE the range).
  * CDA_OP_APPEND: one decode step: for each sequence b (P = pos[b]) and head,
  *   the token at P-W leaves the ring and, if its keep bit is set, is copied
  *   to compact row W + comp_len (comp_len += 1; CDA_DEVERR_CAPACITY if

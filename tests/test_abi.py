@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.version() == 1
+    assert lib.version() == lib.CDA_VERSION == 2
     assert lib.status_string(0) == "ok"
     assert lib.status_string(3) == "workspace too small"
     assert lib.status_string(99) == "unknown status"
@@ -182,3 +182,52 @@ def test_default_split(lib, B, Hkv, pool_rows):
             L.cda_attn_workspace_bytes(C.byref(c), 4 * Hkv, 512)
     expect = {11776: 4, 98304: 8, 126976: 12, 61440: 8, 262144: 24, 1 << 22: 8, 64: 4}
     assert t == expect[pool_rows]
+
+
+def _paged(lib, **kw):
+    c = _cache(lib, **kw)
+    fake = 0x100000
+    c.page_table = c.free_pages = c.free_top = fake
+    c.max_pages = 4
+    c.seg_base = 0          # not used by a paged store
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value", [("max_pages", 0), ("reserved1", 1), ("free_pages", 0),
+                                         ("free_top", 0), ("pos", 0), ("ring_keep", 0)])
+def test_paged_cache_validation(lib, field, value):
+    L = lib.load()
+    c = _paged(lib, **{field: value})
+    a = lib.CdaCompactArgs()
+    a.op = lib.CDA_OP_REFILL
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+
+
+def test_paged_ranges_and_ops(lib):
+    L = lib.load()
+    a = lib.CdaCompactArgs()
+    # page operations need a paged store; ranges need one too
+    c = _cache(lib)
+    for op in (lib.CDA_OP_PAGE_INIT, lib.CDA_OP_REFILL, lib.CDA_OP_RELEASE):
+        a.op = op
+        assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    a.op, a.seq_count = lib.CDA_OP_COUNT, 1
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == 1
+    # a paged store: ranges inside the batch only
+    p = _paged(lib, B=2)
+    a.op, a.T, a.keep, a.keep_ld = lib.CDA_OP_COUNT, 0, 0, 0
+    for b0, n in ((0, -1), (-1, 1), (2, 1), (1, 2), (1, 0)):
+        a.seq_begin, a.seq_count = b0, n
+        assert L.kv_compact(C.byref(p), C.byref(a), None) == 1, (b0, n)
+    a.op, a.seq_begin, a.seq_count, a.reserve = lib.CDA_OP_REFILL, 0, 0, -1
+    assert L.kv_compact(C.byref(p), C.byref(a), None) == 1
+    # the append and the decode step always cover the whole batch
+    a.op, a.seq_count, a.reserve = lib.CDA_OP_APPEND, 1, 0
+    a.keep = a.k = a.v = 0x100000
+    assert L.kv_compact(C.byref(p), C.byref(a), None) == 1
+    q = out = ws = C.c_void_p(0x100000)
+    need = L.cda_attn_workspace_bytes(C.byref(p), 8, 0)
+    assert L.decode_step_compact(C.byref(p), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need,
+                                 None) == 1
