@@ -1,15 +1,16 @@
 """Turn rocprofv3 output of the benchmark into the short text summaries kept
 under profiles/.
 
-  python profile_summary.py trace <kernel_stats.csv> <command> > profiles/X.md
+  python profile_summary.py trace <kernel_stats.csv> <command> [note] > profiles/X.md
   python profile_summary.py traffic <copy FETCH csv> <copy WRITE csv>
-         <bench FETCH csv> <bench WRITE csv> <commands...>
+         <bench FETCH csv> <bench WRITE csv> <json path or -> <commands...>
 
 The traffic mode scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
 dispatch) by what the same counter reads for the plain 64 MiB copy of
-`bench.py --copy-calibration`, and writes profiles/attn_qwen_c8_traffic.json
-(read by bench.py while it matches the attention kernel source) plus a
-markdown table on stdout.
+`bench.py --copy-calibration`, prints a markdown table, and writes the
+attention kernel's bytes per launch to the JSON path (bench.py reads
+profiles/attn_qwen_c8_traffic.json while it matches the attention kernel
+source); "-" writes no JSON.
 """
 from __future__ import annotations
 
@@ -31,10 +32,12 @@ def short(name: str) -> str:
     return name.split("(")[0] if ours else name[:60]
 
 
-def trace(stats_csv: str, command: str) -> None:
+def trace(stats_csv: str, command: str, note: str = "") -> None:
     rows = list(csv.DictReader(open(stats_csv)))
     print(f"# rocprofv3 kernel trace summary\n\nCommand (from the repository root):\n\n"
           f"```\n{command}\n```\n")
+    if note:
+        print(note + "\n")
     print("| kernel | calls | avg us | min us | max us | share |")
     print("|---|---:|---:|---:|---:|---:|")
     for r in rows[:12]:
@@ -56,7 +59,7 @@ def _mean(path: str, pats: tuple) -> dict:
 COPY_KERNELS = ("copyBuffer", "direct_copy")
 
 
-def traffic(cf: str, cw: str, bf: str, bw: str, commands: list[str]) -> None:
+def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[str]) -> None:
     fcal = COPY_KIB / list(_mean(cf, COPY_KERNELS).values())[0]
     wcal = COPY_KIB / list(_mean(cw, COPY_KERNELS).values())[0]
     fetch, write = _mean(bf, ("cda",)), _mean(bw, ("cda",))
@@ -65,8 +68,9 @@ def traffic(cf: str, cw: str, bf: str, bw: str, commands: list[str]) -> None:
     for c in commands:
         print(c)
     print("```\n")
-    print(f"Calibration: a plain 64 MiB copy reads as FETCH_SIZE x{fcal:.4f} and "
-          f"WRITE_SIZE x{wcal:.4f} of the true KiB; the figures below are scaled by them.\n")
+    print(f"Calibration: a plain 64 MiB copy reads as FETCH_SIZE x{1 / fcal:.4f} and "
+          f"WRITE_SIZE x{1 / wcal:.4f} of its true KiB, so the counters below are multiplied "
+          f"by {fcal:.4f} and {wcal:.4f}.\n")
     print("| kernel | fetched MB | written MB |")
     print("|---|---:|---:|")
     for k in fetch:
@@ -78,12 +82,13 @@ def traffic(cf: str, cw: str, bf: str, bw: str, commands: list[str]) -> None:
            "write_bytes_per_launch": write[attn] * wcal * 1024,
            "hbm_bytes_per_launch": (fetch[attn] * fcal + write[attn] * wcal) * 1024,
            "fetch_scale": fcal, "write_scale": wcal}
-    with open(os.path.join(ROOT, "profiles", "attn_qwen_c8_traffic.json"), "w") as f:
-        json.dump(rec, f, indent=1)
+    if json_path != "-":
+        with open(json_path, "w") as f:
+            json.dump(rec, f, indent=1)
 
 
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
-        trace(sys.argv[2], sys.argv[3])
+        trace(*sys.argv[2:5])
     else:
-        traffic(*sys.argv[2:6], sys.argv[6:])
+        traffic(*sys.argv[2:7], sys.argv[7:])
