@@ -65,7 +65,17 @@ def stored_rows_host(keep_np, T, W, S):
     return out
 
 
+def rows_before_host(keep_np, T, W, s0):
+    """n[b, h]: stored rows of every segment before the token at T + s0 is
+    appended (after prefill when s0 = 0) -- byte accounting only."""
+    kept = (keep_np != 0).astype(np.int64)
+    P = T + s0 - 1                          # newest stored position
+    older = max(P - W + 1, 0)
+    return min(W, P + 1) + kept[:, :, :older].sum(axis=2)
+
+
 ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / f16 MFMA of the MI355X
 
 
 def traffic_from_profile():
@@ -131,6 +141,10 @@ def main():
     ap.add_argument("--paged", action="store_true",
                     help="paged store: 64-row pages, no prefill reserve, a refill every 64 "
                          "steps (inside the timed step)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="M > 0: the gen_len tokens of each layer arrive as chunks of M "
+                         "(chunk_attn_compact: multi-query attention, then the append) "
+                         "instead of one decode step each")
     ap.add_argument("--unfused", action="store_true",
                     help="decode steps as kv_compact APPEND + decode_attn_compact")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,6 +199,17 @@ def main():
         c.workspace(Hq, args.split)
         caches.append(c)
     outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    # --chunk: per layer and chunk, (start, tokens, keep [B, m, Hkv], q [B, m, Hq, D], out)
+    chunks = []
+    if args.chunk > 0:
+        for l in range(L):
+            lc = []
+            for s0 in range(0, S, args.chunk):
+                m = min(args.chunk, S - s0)
+                lc.append((s0, m, keepd[l][:, :, T + s0:T + s0 + m].permute(0, 2, 1).contiguous(),
+                           qd[l][s0:s0 + m].permute(1, 0, 2, 3).contiguous(),
+                           torch.empty((B, m, Hq, D), dtype=torch.bfloat16, device=dev)))
+            chunks.append(lc)
     torch.cuda.synchronize()
     log(f"inputs resident in {time.perf_counter() - t0:.1f} s")
 
@@ -204,6 +229,16 @@ def main():
                 c.pack(kd[l], vd[l], keepd[l], T)
 
     def decode_all():
+        if args.chunk > 0:
+            for j in range(len(chunks[0])):
+                for l in range(L):
+                    s0, m, kp, qc, oc = chunks[l][j]
+                    c = caches[l]
+                    if args.paged:
+                        c.refill(max(REFILL, m))
+                    c.chunk(kd[l][:, T + s0:T + s0 + m], vd[l][:, T + s0:T + s0 + m], kp, qc,
+                            out=oc)
+            return
         for s in range(S):
             for l in range(L):
                 c = caches[l]
@@ -282,14 +317,37 @@ def main():
     # events, gaps between launches included) divided by the launches; the
     # algorithmic bytes per launch are the mean over the same launches.  With
     # --unfused this is the time of one layer step (APPEND + attention).
-    kernel_us = float(np.mean(decode_ms_l)) * 1e3 / (S * L)
+    n_calls = (len(chunks[0]) if args.chunk > 0 else S) * L
+    kernel_us = float(np.mean(decode_ms_l)) * 1e3 / n_calls
     bytes_per_launch = float(attn_bytes.mean())
+    flops_per_call = None
+    if args.chunk > 0:
+        # each chunk call reads the rows stored before it once (algorithmic
+        # bytes), and its queries t see those rows plus chunk tokens <= t:
+        # 2 x 2 x D flops per (visible row, query row), for QK and PV
+        cb, cf = [], []
+        for l in range(L):
+            keep_np = keepd[l].cpu().numpy()
+            for s0, m, *_ in chunks[l]:
+                n0 = rows_before_host(keep_np, T, W, s0).astype(np.float64)
+                cb.append(float(n0.sum()) * 2 * row_bytes)
+                cf.append(4.0 * D * (Hq // Hkv) * float((m * n0 + m * (m + 1) / 2).sum()))
+        step_attn_bytes = float(np.sum(cb))
+        bytes_per_launch = float(np.mean(cb))
+        flops_per_call = float(np.mean(cf))
     prefill_ms = float(np.mean(prefill_ms_l))
 
     ms = float(np.mean(step_ms))
     value = step_attn_bytes / (ms * 1e-3) / 1e9
     tokens_per_s = B * S / (ms * 1e-3)
     achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
+    if flops_per_call is not None:
+        tflops = flops_per_call / (kernel_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                    "traffic": None}
+    else:
+        roofline = None
     # the committed counters are those of the default run (this config, FP8)
     traffic = (traffic_from_profile() if (args.config, kv) == ("qwen_c8", "fp8") and
                not args.paged else None)
@@ -297,7 +355,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        cpu, worst, nl = cpu_baseline(cfg, list(range(L)), outs, kv)
+        # the answers at the last position: the decode step's output, or the
+        # last query of the last chunk
+        last = outs if args.chunk <= 0 else [chunks[l][-1][4][:, -1] for l in range(L)]
+        cpu, worst, nl = cpu_baseline(cfg, list(range(L)), last, kv)
         log(f"oracle sample: {nl} layers, GPU max abs err {worst:.2e}")
 
     rec = {
@@ -320,20 +381,22 @@ def main():
                    "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
                    "kv_storage": kv, "budget": cfg.budget,
                    "store": (f"paged: 64-row pages, no prefill reserve, refill every {REFILL} steps"
-                             if args.paged else f"contiguous segments, reserve {S} rows"), "split_tokens": args.split or "library default",
+                             if args.paged else f"contiguous segments, reserve {S} rows"),
+                   "split_tokens": args.split or "library default",
                    "parallelism": "single GPU"},
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "decode_step_kernel_us": round(kernel_us, 3),
+        ("chunk_call_us" if args.chunk > 0 else "decode_step_kernel_us"): round(kernel_us, 3),
         "prefill_compaction_ms": round(prefill_ms, 3),
         "decode_ms_per_step": round(float(np.mean(decode_ms_l)), 3),
         "launch": ("eager" if args.eager else "hip graphs") +
-                  (", append + attention" if args.unfused else ", fused decode step"),
+                  (f", chunks of {args.chunk} tokens (chunk_attn_compact)" if args.chunk > 0 else
+                   ", append + attention" if args.unfused else ", fused decode step"),
         "kv_bytes_per_decode_step": round(float(attn_bytes.sum(axis=1).mean())),
         "kv_pool_mb": round(sum(2 * c.pool_rows * row_bytes for c in caches) / 1e6, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+        "roofline": roofline or {"bound": "hbm", "achieved": round(achieved, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

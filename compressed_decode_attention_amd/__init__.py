@@ -21,7 +21,7 @@ from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_PAGES, CDA_DEVERR_POOL, CDA_D
                    CDA_OUT_F32, CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
 __all__ = ["CompactKVCache", "PagedKVCache", "kv_compact", "decode_attn_compact",
-           "decode_step_compact", "CdaError", "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY",
+           "decode_step_compact", "chunk_attn_compact", "CdaError", "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY",
            "CDA_DEVERR_POOL", "CDA_DEVERR_XCD", "CDA_DEVERR_PAGES"]
 
 _DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3, "fp4": CDA_KV_FP4_E2M1}
@@ -139,6 +139,45 @@ def decode_step_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: tor
         raise CdaError(st, "decode_step_compact")
 
 
+def chunk_attn_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: torch.Tensor,
+                       keep_new: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor | None = None, sm_scale: float = 0.0,
+                       workspace: torch.Tensor | None = None) -> None:
+    """One chunk_attn_compact call: M new tokens per sequence (k_new, v_new
+    [B, M, Hkv, D] bf16, keep_new [B, M, Hkv] uint8, q [B, M, Hq, D] bf16):
+    query t answered as the decode step at position pos + t, out [B, M, Hq, D],
+    then the M tokens appended."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be a contiguous bfloat16 [B, M, Hq, D] tensor")
+    B, M, Hq, D = q.shape
+    if B != cache.B or D != cache.D:
+        raise ValueError("q shape does not match the cache")
+    if out.shape != q.shape or not out.is_contiguous() or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be a contiguous [B, M, Hq, D] bfloat16 or float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * M * Hq):
+        raise ValueError("lse must be a contiguous float32 [B, M, Hq] tensor")
+    for x in (k_new, v_new):
+        if x.dtype != torch.bfloat16 or tuple(x.shape) != (B, M, cache.Hkv, D) or x.stride(-1) != 1:
+            raise ValueError("k_new, v_new must be bfloat16 [B, M, Hkv, D] with contiguous rows")
+    if k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must share strides")
+    if keep_new.dtype != torch.uint8 or not keep_new.is_contiguous() or keep_new.numel() != B * M * cache.Hkv:
+        raise ValueError("keep_new must be a contiguous uint8 [B, M, Hkv] tensor")
+    a = CdaCompactArgs()
+    a.op = CDA_OP_APPEND
+    a.keep, a.keep_ld = _ptr(keep_new), cache.Hkv
+    a.k, a.v = _ptr(k_new), _ptr(v_new)
+    a.stride_b, a.stride_t, a.stride_h = k_new.stride(0), k_new.stride(1), k_new.stride(2)
+    if workspace is None:
+        workspace = cache.chunk_workspace(Hq, M)
+    out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
+    st = _lib.chunk_attn_compact(cache.struct, a, M, _ptr(q), Hq, sm_scale, _ptr(out), out_dtype,
+                                 _ptr(lse), _ptr(workspace), workspace.numel(),
+                                 _stream(cache.device))
+    if st != 0:
+        raise CdaError(st, "chunk_attn_compact")
+
+
 class CompactKVCache:
     """One layer's compact KV store: metadata and pools as device tensors."""
 
@@ -224,6 +263,23 @@ class CompactKVCache:
             # zero-filled once; the library keeps its counters at zero
             self._ws[key] = torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
         return self._ws[key]
+
+    def chunk_workspace(self, Hq: int, M: int) -> torch.Tensor:
+        key = ("chunk", Hq, M)
+        if key not in self._ws:
+            n = _lib.chunk_workspace_bytes(self.struct, Hq, M)
+            self._ws[key] = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self._ws[key]
+
+    def chunk(self, k_new, v_new, keep_new, q, out=None, out_dtype=torch.bfloat16, lse=None,
+              sm_scale: float = 0.0, workspace=None) -> torch.Tensor:
+        """chunk_attn_compact: q [B, M, Hq, D] over the store plus the chunk,
+        then the chunk (k_new, v_new [B, M, Hkv, D], keep_new [B, M, Hkv])
+        appended."""
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
+        chunk_attn_compact(self, k_new, v_new, keep_new, q, out, lse, sm_scale, workspace)
+        return out
 
     def attention(self, q, out=None, out_dtype=torch.bfloat16, lse=None, sm_scale: float = 0.0,
                   split_tokens: int = 0, workspace=None) -> torch.Tensor:

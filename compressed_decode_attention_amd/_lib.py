@@ -21,10 +21,12 @@ CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE = 3, 4, 5
 CDA_VERSION = 2       # the struct layouts below are those of this version
 CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16
+CDA_MAX_CHUNK = 64
 
 # every symbol include/cda.h declares
-EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact",
-           "cda_attn_workspace_bytes", "cda_status_string", "cda_version")
+EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact", "chunk_attn_compact",
+           "cda_attn_workspace_bytes", "cda_chunk_workspace_bytes", "cda_status_string",
+           "cda_version")
 
 
 class CdaKvCache(C.Structure):
@@ -84,6 +86,12 @@ def load(path: str = LIB_PATH):
     L.decode_step_compact.restype = C.c_int32
     L.cda_attn_workspace_bytes.argtypes = [C.POINTER(CdaKvCache), C.c_int32, C.c_int32]
     L.cda_attn_workspace_bytes.restype = C.c_size_t
+    L.chunk_attn_compact.argtypes = [C.POINTER(CdaKvCache), C.POINTER(CdaCompactArgs), C.c_int32,
+                                     C.c_void_p, C.c_int32, C.c_float, C.c_void_p, C.c_int32,
+                                     C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    L.chunk_attn_compact.restype = C.c_int32
+    L.cda_chunk_workspace_bytes.argtypes = [C.POINTER(CdaKvCache), C.c_int32, C.c_int32]
+    L.cda_chunk_workspace_bytes.restype = C.c_size_t
     L.cda_status_string.argtypes = [C.c_int32]
     L.cda_status_string.restype = C.c_char_p
     L.cda_version.argtypes = []
@@ -124,6 +132,19 @@ def decode_step_compact(cache: CdaKvCache, args: CdaCompactArgs, q_ptr: int, Hq:
         C.byref(cache), C.byref(args), C.c_void_p(q_ptr), int(Hq), float(sm_scale),
         C.c_void_p(out_ptr), int(out_dtype), C.c_void_p(lse_ptr or 0), int(split_tokens),
         C.c_void_p(ws_ptr or 0), C.c_size_t(ws_bytes), C.c_void_p(stream or 0)))
+
+
+def chunk_attn_compact(cache: CdaKvCache, args: CdaCompactArgs, M: int, q_ptr: int, Hq: int,
+                       sm_scale: float, out_ptr: int, out_dtype: int, lse_ptr: int,
+                       ws_ptr: int, ws_bytes: int, stream: int | None) -> int:
+    return int(load().chunk_attn_compact(
+        C.byref(cache), C.byref(args), int(M), C.c_void_p(q_ptr), int(Hq), float(sm_scale),
+        C.c_void_p(out_ptr), int(out_dtype), C.c_void_p(lse_ptr or 0), C.c_void_p(ws_ptr or 0),
+        C.c_size_t(ws_bytes), C.c_void_p(stream or 0)))
+
+
+def chunk_workspace_bytes(cache: CdaKvCache, Hq: int, M: int) -> int:
+    return int(load().cda_chunk_workspace_bytes(C.byref(cache), Hq, M))
 
 
 def attn_workspace_bytes(cache: CdaKvCache, Hq: int, split_tokens: int) -> int:

@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["compact.hip", "attn.hip", "abi.hip"]
+SOURCES = ["compact.hip", "attn.hip", "chunk.hip", "abi.hip"]
 OUT = os.path.join(HERE, "libcda_hip.so")
 ARCH = os.environ.get("CDA_OFFLOAD_ARCH", "gfx950")
 

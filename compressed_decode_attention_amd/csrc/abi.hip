@@ -209,6 +209,39 @@ int32_t decode_step_compact(const cda_kv_cache* c, const cda_compact_args* a, co
                                      tpu, workspace, s, a));
 }
 
+size_t cda_chunk_workspace_bytes(const cda_kv_cache* c, int32_t Hq, int32_t M) {
+  if (check_cache(c) != CDA_OK || Hq <= 0 || Hq % c->Hkv != 0 || M < 1 || M > CDA_MAX_CHUNK)
+    return 0;
+  return cda::chunk_workspace_bytes(*c, Hq / c->Hkv, M);
+}
+
+int32_t chunk_attn_compact(const cda_kv_cache* c, const cda_compact_args* a, int32_t M,
+                           const void* q, int32_t Hq, float sm_scale, void* out,
+                           int32_t out_dtype, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int32_t st = check_cache(c);
+  if (st != CDA_OK) return st;
+  if ((st = check_pools(c)) != CDA_OK) return st;
+  if (M < 1 || M > CDA_MAX_CHUNK || Hq <= 0) return CDA_ERR_INVALID_ARG;
+  if (Hq % c->Hkv != 0 || Hq / c->Hkv > CDA_MAX_GQA) return CDA_ERR_UNSUPPORTED;
+  if (out_dtype != CDA_OUT_BF16 && out_dtype != CDA_OUT_F32) return CDA_ERR_UNSUPPORTED;
+  if (!a || a->op != CDA_OP_APPEND || a->seq_begin != 0 || a->seq_count != 0)
+    return CDA_ERR_INVALID_ARG;
+  if (c->B > 0) {
+    if (!a->keep) return CDA_ERR_INVALID_ARG;
+    if ((st = check_bf16_rows(a->k, a->v, a->stride_b, a->stride_t, a->stride_h)) != CDA_OK)
+      return st;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return CDA_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return CDA_ERR_INVALID_ARG;
+  }
+  const size_t need = cda::chunk_workspace_bytes(*c, Hq / c->Hkv, M);
+  if (workspace_bytes < need) return CDA_ERR_WORKSPACE;
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return CDA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(cda::launch_chunk(*c, *a, M, q, Hq, sm_scale, out, out_dtype == CDA_OUT_F32,
+                                      lse, workspace, s));
+}
+
 const char* cda_status_string(int32_t status) {
   switch (status) {
     case CDA_OK: return "ok";

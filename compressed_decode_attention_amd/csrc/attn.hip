@@ -81,14 +81,13 @@
 //     writes pos[b] (read by the units of all of them).
 //   - every counter sits on a 128-byte line of its own: atomics on one line
 //     are performed one after another.
+#include "attn_common.h"
 #include "cda_device.h"
 #include "cda_launch.h"
 
 namespace cda {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMergeBatch = 4;   // partials loaded per round trip in the merge
 constexpr int kXcdGroups = 8;    // segment groups of the XCD-local mode
 constexpr int kCounterStride = 32;   // ints between counters: one 128-byte line each
@@ -132,11 +131,6 @@ __device__ __forceinline__ int units_of(int n, int tpu) {
   return max(1, (tiles + tpu - 1) / tpu);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
 
 // Final output of 4 consecutive d of query row gg of segment (b, h).
 __device__ __forceinline__ void write_final4(const AttnParams& p, int b, int h, int gg, int d4,
@@ -190,24 +184,6 @@ __device__ __forceinline__ long long lane_l(long long x, int src) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
-// Reductions across the 16-lane rows of a wave: partner lanes l ^ 16 and
-// l ^ 32 via the row-swap permutes (no LDS round trip).
-__device__ __forceinline__ float max_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Rows of a segment in a decode step, from its state before the append
 // (P = pos >= 0, 0 <= cl <= cap, kn = keep byte of the new token != 0).
@@ -336,15 +312,6 @@ __device__ __forceinline__ void commit_segment(const AttnParams& p, int i, const
   if (errbits) atomicOr(p.err, errbits);
 }
 
-// d of the first of the 8 q values lane (g, kg) supplies at k-step s: the d
-// the K operand of that lane holds there (the order of the bytes of its K
-// chunk: 16 FP8 elements = 2 k-steps, 32 FP4 elements = 4, 8 bf16 = 1).
-template <int KV>
-__device__ __forceinline__ int q_d0(int s, int kg) {
-  if (KV == kKvFP8) return 64 * (s >> 1) + 16 * kg + 8 * (s & 1);
-  if (KV == kKvFP4) return 32 * kg + 8 * s;
-  return 32 * s + 8 * kg;
-}
 
 // Paged store: page of tile t of segment i (the index is clamped into the
 // segment's page-table row, so the load never leaves the table; -1 past it).
@@ -356,11 +323,6 @@ __device__ __forceinline__ bool page_ok(const AttnParams& p, int pg) {
   return (unsigned)pg < (unsigned)p.n_pages;
 }
 
-// Mask of the bytes of dword w (bytes 4w .. 4w+3) that lie below `lim`.
-__device__ __forceinline__ uint32_t bytes_below(int lim, int w) {
-  const int k = lim - 4 * w;
-  return k >= 4 ? 0xFFFFFFFFu : (k <= 0 ? 0u : (1u << (8 * k)) - 1u);
-}
 
 // PG: the paged store (tiles through the page table; idle sequences).
 template <int KV, int D, bool XL, int NW, bool APP, bool PG>

@@ -1,0 +1,808 @@
+// Multi-query attention of a chunk of new tokens over the compact KV store,
+// for gfx950: a prefill continued chunk by chunk on top of a compacted
+// context, or several draft tokens at once.
+//
+// What is computed (FastDMS page, memory-table paragraph: the compact cache
+// plus the W-token staging window; PyramidInfer page: compressing the cache
+// already while the prompt is processed): sequence b receives M <= 64 new
+// tokens at positions P .. P+M-1 (P = pos[b]) with queries q[b, t], keys and
+// values k[b, t], v[b, t] and keep bytes keep[b, t].  Query t gets exactly
+// the decode attention at position P + t, i.e. attention over the rows the
+// store would hold after the tokens P .. P+t were appended one at a time:
+//   - every compact row of the store (kept tokens older than the window);
+//   - the store's ring rows, except a token that has left query t's window
+//     (position <= P + t - W) without being kept;
+//   - the chunk's tokens t' <= t, except one that has left the window
+//     without being kept (only when M > W).
+// Chunk tokens take part with the values the store would hold for them
+// (BF16, or encoded with the segment's frozen FP8/FP4 scales).  Attending
+// first and appending afterwards is what makes this exact: appending the
+// chunk first would overwrite ring rows that the chunk's earlier queries
+// still see.
+//
+// Launches: (1) encode: each segment's chunk becomes one 64-row tile in the
+// store's formats, in the workspace; (2) attention: workgroup (segment,
+// block of 16 query columns, split) walks every split-th tile of the
+// segment, the chunk tile being the last; the 16 columns of a block are
+// (token, query head) pairs, column c = t * G + g; (3) merge of the
+// splits' partial states per column; (4) the commit: the store becomes what
+// M APPEND operations leave, computed for all M tokens at once.
+//
+// The MFMA layout is the decode kernel's: per 64-row tile and wave,
+//   S^T[token][c] = K_tile[token][:] . Q^T[:][c]      (16 x 16 x 32 bf16)
+//   O^T[d][c]    += V^T[d][token] . P^T[token][c]     (16 x 16 x 32 f16/bf16)
+// with the K tile chunk-permuted and the V tile column-major, and every
+// lane holding, in its S accumulator, the 16 tokens of its P operand.
+#include <algorithm>
+
+#include "attn_common.h"
+#include "cda_device.h"
+#include "cda_launch.h"
+
+namespace cda {
+namespace {
+
+constexpr int kChunkWaves = 4;       // waves per attention workgroup
+constexpr int kChunkTarget = 512;    // workgroups the split count aims at
+
+struct ChunkParams {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  int64_t pool_rows;
+  const int64_t* seg_base;     // contiguous segments
+  const int32_t* page_table;   // paged store
+  int max_pages, n_pages;
+  const int32_t* seg_cap;
+  const int32_t* comp_len;
+  const int32_t* pos;
+  const uint8_t* ring_keep;
+  const float* k_amax;
+  const float* v_amax;
+  const uint16_t* q;           // [B, M, Hq, D]
+  void* out;                   // [B, M, Hq, D]
+  float* lse;                  // [B, M, Hq] or NULL
+  const uint16_t* k_new;       // chunk: (b, t, h, d) at b*nsb + t*nst + h*nsh + d
+  const uint16_t* v_new;
+  int64_t nsb, nst, nsh;
+  const uint8_t* keep_new;     // [B, M, Hkv]
+  uint8_t* chunk_k;            // workspace: [nh] tiles in the K pool format
+  uint8_t* chunk_v;            // workspace: [nh] tiles in the V pool format
+  float* part_o;               // workspace: [nh][NB][SP][16][D]
+  float* part_ml;              // workspace: [nh][NB][SP][16][2]
+  int32_t* seqcnt;             // workspace: [B] segments of the sequence committed
+  int B, Hkv, Hq, G, M, W, nh, NB, SP, out_f32;
+  float sm_scale;
+  int32_t* err;
+};
+
+// ---------------------------------------------------------------- encode
+
+// Workgroup i: segment i's chunk tokens as one 64-row tile, encoded as the
+// append would encode them; rows M .. 63 are zero.
+template <int KV, int D>
+__global__ __launch_bounds__(kBlock) void chunk_encode_kernel(ChunkParams p) {
+  constexpr bool Q = KV != kKvBF16;
+  constexpr int RB = kv_row_bytes(KV, D);
+  constexpr int CPR = D / 8;                 // 8-element input chunks per row
+  constexpr int VB = KV == kKvBF16 ? 2 : 1;  // LDS bytes per V element (FP4: one code a byte)
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[kTile * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[D * kTile * VB];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  if (h == 0 && tid == 0) p.seqcnt[b] = 0;   // the commit's counter of sequence b
+  const float kinv = Q ? kv_inv_scale<KV>(p.k_amax[i]) : 1.0f;
+  const float vinv = Q ? kv_inv_scale<KV>(p.v_amax[i]) : 1.0f;
+  for (int e = tid; e < kTile * CPR; e += kBlock) {
+    const int r = e / CPR, c = e - r * CPR, d0 = 8 * c;
+    u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
+    if (r < p.M) {
+      const int64_t off = (int64_t)b * p.nsb + (int64_t)r * p.nst + (int64_t)h * p.nsh + d0;
+      kx = *reinterpret_cast<const u32x4*>(p.k_new + off);
+      vx = *reinterpret_cast<const u32x4*>(p.v_new + off);
+    }
+    if (KV == kKvFP4) {
+      uint32_t kc = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {   // elements 2 w2 (low nibble), 2 w2 + 1
+        kc |= e2m1x2_from_f32(__fmul_rn(__uint_as_float(kx[w2] << 16), kinv),
+                              __fmul_rn(__uint_as_float(kx[w2] & 0xFFFF0000u), kinv)) << (8 * w2);
+        const uint32_t vb = e2m1x2_from_f32(__fmul_rn(__uint_as_float(vx[w2] << 16), vinv),
+                                            __fmul_rn(__uint_as_float(vx[w2] & 0xFFFF0000u), vinv));
+        s_v[(d0 + 2 * w2) * kTile + r] = (uint8_t)(vb & 15u);
+        s_v[(d0 + 2 * w2 + 1) * kTile + r] = (uint8_t)(vb >> 4);
+      }
+      *reinterpret_cast<uint32_t*>(s_k + k_chunk_offset(r, (d0 / 2) >> 4, RB) + ((d0 / 2) & 15)) = kc;
+    } else if (KV == kKvFP8) {
+      uint32_t kc[2] = {0, 0}, vc[2] = {0, 0};
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        kc[w2 >> 1] |= e4m3x2_from_f32(__fmul_rn(__uint_as_float(kx[w2] << 16), kinv),
+                                       __fmul_rn(__uint_as_float(kx[w2] & 0xFFFF0000u), kinv))
+                       << (16 * (w2 & 1));
+        vc[w2 >> 1] |= e4m3x2_from_f32(__fmul_rn(__uint_as_float(vx[w2] << 16), vinv),
+                                       __fmul_rn(__uint_as_float(vx[w2] & 0xFFFF0000u), vinv))
+                       << (16 * (w2 & 1));
+      }
+      *reinterpret_cast<u32x2*>(s_k + k_chunk_offset(r, d0 >> 4, RB) + (d0 & 15)) = u32x2{kc[0], kc[1]};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s_v[(d0 + q) * kTile + r] = (uint8_t)(vc[q >> 2] >> (8 * (q & 3)));
+    } else {
+      *reinterpret_cast<u32x4*>(s_k + k_chunk_offset(r, c, RB)) = kx;
+      uint16_t* v16 = reinterpret_cast<uint16_t*>(s_v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v16[(d0 + q) * kTile + r] = (uint16_t)((vx[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+    }
+  }
+  __syncthreads();
+  uint8_t* kt = p.chunk_k + (int64_t)i * kTile * RB;
+  uint8_t* vt = p.chunk_v + (int64_t)i * kTile * RB;
+  for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
+    *reinterpret_cast<u32x4*>(kt + 16 * ch) = *reinterpret_cast<const u32x4*>(s_k + 16 * ch);
+    u32x4 vv;
+    if (KV == kKvFP4) {   // chunk ch: rows r .. r + 31 of column d, two per byte
+      const int d = ch >> 1, r = (ch & 1) * 32;
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * kTile + r);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = src[2 * q], c = src[2 * q + 1];   // one code per byte
+        const uint32_t lo = (a & 0xFu) | ((a >> 4) & 0xF0u) | ((a >> 8) & 0xF00u) | ((a >> 12) & 0xF000u);
+        const uint32_t hi = (c & 0xFu) | ((c >> 4) & 0xF0u) | ((c >> 8) & 0xF00u) | ((c >> 12) & 0xF000u);
+        vv[q] = lo | (hi << 16);
+      }
+    } else {              // the LDS image is the tile itself
+      vv = *reinterpret_cast<const u32x4*>(s_v + 16 * ch);
+    }
+    *reinterpret_cast<u32x4*>(vt + 16 * ch) = vv;
+  }
+}
+
+// ---------------------------------------------------------------- attention
+
+// Workgroup w: XCD group w mod 8 takes the segments i = group + 8 l, so that
+// every workgroup reading a segment's tiles shares one L2; within the group,
+// work item w / 8 = (l, column block cb, split s).  Wave v of the workgroup
+// walks the tiles s + SP v, s + SP (v + NW), ... of the segment's n rows,
+// then the chunk tile (tile index ceil(n / 64)).
+template <int KV, int D, bool PG>
+__global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParams p) {
+  constexpr int NW = kChunkWaves;
+  constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
+  constexpr int E = FP8 ? 1 : 2;
+  constexpr int RB = kv_row_bytes(KV, D);
+  constexpr int NK = D / 32, NT = D / 16, KL = RB / 64, VL = FP8 ? 1 : 2;
+
+  __shared__ float s_m[NW][16], s_l[NW][16];
+  __shared__ f32x4 s_o[NW][16][D / 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane & 15, kg = lane >> 4;
+  int work = blockIdx.x >> 3;
+  const int s = work % p.SP;
+  work /= p.SP;
+  const int cb = work % p.NB;
+  const int i = (blockIdx.x & 7) + 8 * (work / p.NB);
+  if (i >= p.nh) return;                       // the whole workgroup
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int W = p.W, G = p.G, M = p.M;
+
+  // the segment before the chunk; an idle sequence of a paged store (pos <
+  // 0) attends to nothing
+  const int Praw = p.pos[b];
+  const bool idle = Praw < 0;
+  const int P = max(Praw, 0);
+  const int cap = max(p.seg_cap[i], 0);
+  const int cl = min(max(p.comp_len[i], 0), cap);
+  const int n = idle ? 0 : min(W, P) + cl;
+  const int ntiles = (n + kTile - 1) / kTile;
+  const int64_t sb = PG ? 0 : p.seg_base[i];
+  const int64_t in_pool = PG ? INT64_MAX : p.pool_rows - sb;
+  const float ks = Q ? kv_scale<KV>(p.k_amax[i]) : 1.0f;
+  const float vs = Q ? kv_scale<KV>(p.v_amax[i]) : 1.0f;
+
+  // this lane's query column: chunk token tq, query head hq of KV head h
+  const int col = cb * 16 + g;
+  const int tq = col / G, hq = col - tq * G;
+  const bool col_ok = tq < M;
+  bf16x8 qop[NK];
+  {
+    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + hq)
+                                : ((int64_t)b * M * p.Hq + h * G);
+    const uint16_t* qr = p.q + qrow * D;
+#pragma unroll
+    for (int st = 0; st < NK; ++st)
+      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + q_d0<KV>(st, kg)));
+  }
+  const float c1 = p.sm_scale * kLog2e * ks;
+  // ring row r holds position P - W + ((r - P mod W) mod W) once P >= W, else
+  // position r; positions <= lim have left query tq's window
+  const int pmw = W > 0 ? P % W : 0;
+  const int lim = P + tq - W;
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+  bool first_tile = true;
+
+  for (int tt = s + p.SP * wave; tt <= ntiles; tt += p.SP * NW) {
+    const bool ctile = tt == ntiles;           // the chunk tile
+    const int r0 = tt * kTile;
+    const int valid = ctile ? (idle ? 0 : M) : (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
+    if (valid <= 0) continue;
+    const uint8_t* ktile;
+    const uint8_t* vtile;
+    if (ctile) {
+      ktile = p.chunk_k + (int64_t)i * kTile * RB;
+      vtile = p.chunk_v + (int64_t)i * kTile * RB;
+    } else {
+      int64_t trow = sb + r0;
+      if (PG) {
+        const int pg = p.page_table[(int64_t)i * p.max_pages + min(tt, p.max_pages - 1)];
+        if (tt >= p.max_pages || pg < 0 || pg >= p.n_pages) {   // inconsistent store
+          if (lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+          continue;
+        }
+        trow = (int64_t)pg * kTile;
+      }
+      ktile = p.k_pool + trow * RB;
+      vtile = p.v_pool + trow * RB;
+    }
+    // keep bytes of this lane's 16 rows: ring rows of the store, or chunk
+    // tokens (clamped indices: every load stays inside its array)
+    uint32_t kb = 0;   // bit j: row 16 kg + j is kept
+    const bool ring = !ctile && r0 < W;
+    if (ctile || ring) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rr = 16 * kg + j;
+        const uint8_t byte = ctile ? p.keep_new[((int64_t)b * M + min(rr, M - 1)) * p.Hkv + h]
+                                   : p.ring_keep[(int64_t)i * W + min(r0 + rr, W - 1)];
+        kb |= (uint32_t)(byte != 0) << j;
+      }
+    }
+
+    u32x4 kr[4][KL];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < KL; ++j)
+        kr[m][j] = *reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16);
+    u32x4 vr[NT][VL];
+    u32x2 vq[FP4 ? NT : 1];
+    if (FP4) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        vq[nt] = *reinterpret_cast<const u32x2*>(vtile + (16 * nt + g) * (kTile / 2) + 8 * kg);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int j = 0; j < VL; ++j)
+          vr[nt][j] = *reinterpret_cast<const u32x4*>(vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E);
+    }
+
+    f32x4 sc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      sc[m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < NK; ++st) {
+        bf16x8 a;
+        if (FP4) {
+          a = fp4x8_to_bf16x8(kr[m][0][st]);
+        } else if (FP8) {
+          const u32x4 v = kr[m][st >> 1];
+          a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
+        } else {
+          a = as_bf16x8(kr[m][st]);
+        }
+        sc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], sc[m], 0, 0, 0);
+      }
+    }
+
+    // visibility of this lane's tokens to query tq
+    float z[4][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 16 * kg + 4 * m + r;       // row inside the tile
+        bool vis = col_ok && rr < valid;
+        if (ctile) {                              // chunk token rr
+          vis = vis && rr <= tq && (tq - rr < W || ((kb >> (4 * m + r)) & 1u));
+        } else if (ring && r0 + rr < W) {         // ring row of the store
+          int d = r0 + rr - pmw;
+          if (d < 0) d += W;
+          const int pr = P >= W ? P - W + d : r0 + rr;
+          vis = vis && (pr > lim || ((kb >> (4 * m + r)) & 1u));
+        }
+        z[m][r] = vis ? sc[m][r] * c1 : -INFINITY;
+        tmax = fmaxf(tmax, z[m][r]);
+      }
+    tmax = max_xor32(max_xor16(tmax));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    if (!first_tile) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
+        psum += z[m][r];
+      }
+    l_run += psum;
+    m_run = m_new;
+
+    // rows past the data: their V bytes may not be finite values
+    if (!FP4 && valid < kTile) {
+#pragma unroll
+      for (int j = 0; j < VL; ++j) {
+        const int lb = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t msk = bytes_below(lb, q);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) vr[nt][j][q] &= msk;
+        }
+      }
+    }
+
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (Q) {
+        f16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (_Float16)z[2 * hh + (e >> 2)][e & 3];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f16x8 a;
+          if (FP4) {
+            a = fp4x8_to_f16x8(vq[nt][hh]);
+          } else {
+            const u32x4 v = vr[nt][0];
+            a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
+          }
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, acc[nt], 0, 0, 0);
+        }
+      } else {
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = z[2 * hh + (e >> 2)][e & 3];
+          const __bf16 hi = (__bf16)pv;
+          phi[e] = hi;
+          plo[e] = (__bf16)(pv - (float)hi);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 a = as_bf16x8(vr[nt][hh]);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    first_tile = false;
+  }
+
+  // ---- combine the waves; one partial state per column
+  l_run = sum_xor32(sum_xor16(l_run));
+  if (kg == 0) {
+    s_m[wave][g] = m_run;
+    s_l[wave][g] = l_run;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
+  __syncthreads();
+  const int64_t slot = ((int64_t)i * p.NB + cb) * p.SP + s;
+  for (int e = tid; e < 16 * (D / 4); e += 64 * NW) {
+    const int c = e / (D / 4), d4 = e - c * (D / 4);
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, s_m[ww][c]);
+    f32x4 O = f32x4{0, 0, 0, 0};
+    float L = 0.0f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = s_m[ww][c];
+        if (mw == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(mw - Mx);
+        O += f * s_o[ww][c][d4];
+        L += f * s_l[ww][c];
+      }
+    }
+    *reinterpret_cast<f32x4*>(p.part_o + (slot * 16 + c) * D + 4 * d4) = O * vs;
+    if (d4 == 0) {
+      p.part_ml[(slot * 16 + c) * 2] = Mx;
+      p.part_ml[(slot * 16 + c) * 2 + 1] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- commit
+
+// Workgroup i: the chunk's M tokens appended to segment i, with the result of
+// M APPEND operations but without their M sequential round trips.  At step
+// t the token at position lp = P + t - W leaves the window (W = 0: the new
+// token itself); if it is kept it goes to compact row W + cl0 + (its rank
+// among the kept leaving tokens) while there is room (the rest are dropped
+// with CDA_DEVERR_CAPACITY).  Its bytes are those of old ring row lp mod W
+// (lp < P) or of chunk row lp - P (encoded in the workspace tile).  Ring row
+// r then takes the last chunk token that maps to it.  Every source row is
+// first copied into LDS (all loads in flight together, every old ring row
+// read before any is overwritten), then written out.  FP4 V elements share
+// a byte between two rows: each byte is written by one thread, keeping the
+// nibble of a row it does not write; the compact and the ring writes go in
+// two rounds because rows W - 1 and W can share a byte.  The last segment of
+// a sequence to finish advances pos (a counter per sequence, zeroed by the
+// encode launch).
+template <int KV, int D, bool PG>
+__global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uint8_t* k_pool,
+                                                              uint8_t* v_pool, int32_t* comp_len,
+                                                              uint8_t* ring_keep, int32_t* pos) {
+  constexpr int RB = kv_row_bytes(KV, D);
+  constexpr int KC = RB / 16;                  // 16-byte K chunks per row
+  constexpr bool FP4 = KV == kKvFP4;
+  constexpr int E = KV == kKvBF16 ? 2 : 1;     // bytes per V element (FP4: one code per LDS byte)
+  __shared__ int s_src[kTile];                 // k-th moved token: ring row -1 - r, or chunk row
+  __shared__ int s_nmove, s_full;
+  __shared__ __attribute__((aligned(16))) uint8_t s_mk[kTile * RB];   // moved rows, K
+  __shared__ __attribute__((aligned(16))) uint8_t s_rk[kTile * RB];   // new ring rows, K
+  __shared__ __attribute__((aligned(16))) uint8_t s_mv[D * kTile * E];   // [d][row]
+  __shared__ __attribute__((aligned(16))) uint8_t s_rv[D * kTile * E];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int P = pos[b];
+  if (P < 0) return;                           // idle (paged store): every segment of b
+  const int W = p.W, M = p.M;
+  const int cap = max(p.seg_cap[i], 0);
+  const int cl0 = min(max(comp_len[i], 0), cap);
+  const uint8_t* ck = p.chunk_k + (int64_t)i * kTile * RB;   // the chunk's encoded rows
+  const uint8_t* cv = p.chunk_v + (int64_t)i * kTile * RB;
+  // pool row of segment row r: -1 if it has no page or leaves the pool
+  auto prow = [&](int r) -> int64_t {
+    int64_t x;
+    if (PG) {
+      const int t = r / kTile;
+      const int pg = p.page_table[(int64_t)i * p.max_pages + min(t, p.max_pages - 1)];
+      x = (t < p.max_pages && pg >= 0 && pg < p.n_pages) ? (int64_t)pg * kTile + r % kTile : -1;
+    } else {
+      x = p.seg_base[i] + r;
+    }
+    return x >= 0 && x < p.pool_rows ? x : -1;
+  };
+  auto kaddr = [&](uint8_t* pool, int64_t row, int c) {   // 16-byte K chunk c of a pool row
+    return pool + (row - row % kTile) * RB + k_chunk_offset((int)(row % kTile), c, RB);
+  };
+  auto vaddr = [&](uint8_t* pool, int64_t row, int d) {   // V element (row, d); FP4: its byte
+    return FP4 ? pool + (row - row % kTile) * RB + d * (kTile / 2) + (row % kTile) / 2
+               : pool + ((row - row % kTile) * D + d * kTile + row % kTile) * E;
+  };
+  auto cnib = [&](int j, int d) -> uint32_t {            // FP4 code of chunk row j, column d
+    return (cv[d * (kTile / 2) + j / 2] >> (4 * (j & 1))) & 15u;
+  };
+
+  // 1. the tokens that move, ranked (one wave: M <= 64)
+  if (tid < 64) {
+    const int t = tid;
+    bool kept = false;
+    int src = 0;
+    if (t < M) {
+      const int lp = P + t - W;
+      if (lp >= 0) {
+        if (lp < P) {   // in the ring before the chunk (so W > t)
+          const int r = lp % W;
+          kept = ring_keep[(int64_t)i * W + r] != 0;
+          src = -1 - r;
+        } else {
+          kept = p.keep_new[((int64_t)b * M + (lp - P)) * p.Hkv + h] != 0;
+          src = lp - P;
+        }
+      }
+    }
+    const uint64_t bal = __ballot(kept);
+    const int rank = __popcll(bal & ((1ull << t) - 1ull));
+    if (kept && cl0 + rank < cap) s_src[rank] = src;
+    if (t == 0) {
+      const int nk = __popcll(bal);
+      s_nmove = min(nk, cap - cl0);
+      s_full = nk > cap - cl0;
+    }
+  }
+  __syncthreads();
+  const int nmove = s_nmove;
+  const int nr = W > 0 ? min(M, W) : 0, j0 = M - nr;   // chunk tokens that end in the ring
+  const int rs = W > 0 ? (P + j0) % W : 0;              // ring row of chunk token j0
+  int bad = 0;
+
+  // 2. every source row into LDS
+  for (int e = tid; e < nmove * KC; e += kBlock) {
+    const int k = e / KC, c = e - k * KC;
+    const int src = s_src[k];
+    u32x4 x = u32x4{0, 0, 0, 0};
+    if (src < 0) {
+      const int64_t from = prow(-1 - src);
+      if (from >= 0) x = *reinterpret_cast<const u32x4*>(kaddr(k_pool, from, c));
+      else bad = 1;
+    } else {
+      x = *reinterpret_cast<const u32x4*>(ck + k_chunk_offset(src, c, RB));
+    }
+    *reinterpret_cast<u32x4*>(s_mk + k * RB + 16 * c) = x;
+  }
+  for (int e = tid; e < nmove * D; e += kBlock) {
+    const int k = e / D, d = e - k * D;
+    const int src = s_src[k];
+    uint32_t x = 0;
+    if (src < 0) {
+      const int64_t from = prow(-1 - src);
+      if (from >= 0) {
+        const uint8_t* a = vaddr(v_pool, from, d);
+        x = FP4 ? ((uint32_t)*a >> (4 * (from & 1))) & 15u
+                : (E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(a) : (uint32_t)*a);
+      }
+    } else {
+      x = FP4 ? cnib(src, d)
+              : (E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(cv + (d * kTile + src) * E)
+                        : (uint32_t)cv[d * kTile + src]);
+    }
+    if (E == 2) *reinterpret_cast<uint16_t*>(s_mv + (d * kTile + k) * 2) = (uint16_t)x;
+    else s_mv[d * kTile + k] = (uint8_t)x;
+  }
+  for (int e = tid; e < nr * KC; e += kBlock) {
+    const int j = e / KC, c = e - j * KC;
+    *reinterpret_cast<u32x4*>(s_rk + j * RB + 16 * c) =
+        *reinterpret_cast<const u32x4*>(ck + k_chunk_offset(j0 + j, c, RB));
+  }
+  for (int e = tid; e < nr * D; e += kBlock) {
+    const int j = e / D, d = e - j * D;
+    if (FP4) s_rv[d * kTile + j] = (uint8_t)cnib(j0 + j, d);
+    else if (E == 2)
+      *reinterpret_cast<uint16_t*>(s_rv + (d * kTile + j) * 2) =
+          *reinterpret_cast<const uint16_t*>(cv + (d * kTile + j0 + j) * 2);
+    else s_rv[d * kTile + j] = cv[d * kTile + j0 + j];
+  }
+  __syncthreads();   // every old ring row has been read
+
+  // 3. moved rows -> compact rows [R0, R1)
+  const int R0 = W + cl0, R1 = R0 + nmove;
+  for (int e = tid; e < nmove * KC; e += kBlock) {
+    const int k = e / KC, c = e - k * KC;
+    const int64_t to = prow(R0 + k);
+    if (to < 0) { bad = 1; continue; }
+    *reinterpret_cast<u32x4*>(kaddr(k_pool, to, c)) = *reinterpret_cast<const u32x4*>(s_mk + k * RB + 16 * c);
+  }
+  if (FP4) {
+    const int q0 = R0 / 2, nq = nmove > 0 ? (R1 - 1) / 2 - q0 + 1 : 0;
+    for (int e = tid; e < nq * D; e += kBlock) {
+      const int q = q0 + e / D, d = e - (e / D) * D;
+      const int64_t base = prow(2 * q);        // both rows of a byte share a page
+      if (base < 0) { bad = 1; continue; }
+      uint8_t* dst = vaddr(v_pool, base, d);
+      const bool lo_in = 2 * q >= R0, hi_in = 2 * q + 1 < R1;
+      uint32_t byte = (lo_in && hi_in) ? 0u : *dst;
+      if (lo_in) byte = (byte & 0xF0u) | s_mv[d * kTile + (2 * q - R0)];
+      if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_mv[d * kTile + (2 * q + 1 - R0)] << 4);
+      *dst = (uint8_t)byte;
+    }
+  } else {
+    for (int e = tid; e < nmove * D; e += kBlock) {
+      const int k = e / D, d = e - k * D;
+      const int64_t to = prow(R0 + k);
+      if (to < 0) { bad = 1; continue; }
+      uint8_t* dp = vaddr(v_pool, to, d);
+      if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + k) * 2);
+      else *dp = s_mv[d * kTile + k];
+    }
+  }
+  __syncthreads();   // rows W - 1 and W may share an FP4 byte
+
+  // 4. the last nr chunk tokens -> ring rows (P + j) mod W
+  if (nr > 0) {
+    for (int e = tid; e < nr * KC; e += kBlock) {
+      const int j = e / KC, c = e - j * KC;
+      const int64_t to = prow((P + j0 + j) % W);
+      if (to < 0) { bad = 1; continue; }
+      *reinterpret_cast<u32x4*>(kaddr(k_pool, to, c)) = *reinterpret_cast<const u32x4*>(s_rk + j * RB + 16 * c);
+    }
+    if (FP4) {
+      for (int e = tid; e < ((W + 1) / 2) * D; e += kBlock) {
+        const int q = e / D, d = e - q * D;
+        // ring row r holds chunk token j0 + off, off = (r - rs) mod W, when off < nr
+        const int off0 = (2 * q - rs + W) % W, off1 = (2 * q + 1 - rs + W) % W;
+        const bool lo_in = off0 < nr, hi_in = 2 * q + 1 < W && off1 < nr;
+        if (!lo_in && !hi_in) continue;
+        const int64_t base = prow(2 * q);
+        if (base < 0) { bad = 1; continue; }
+        uint8_t* dst = vaddr(v_pool, base, d);
+        uint32_t byte = (lo_in && hi_in) ? 0u : *dst;
+        if (lo_in) byte = (byte & 0xF0u) | s_rv[d * kTile + off0];
+        if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_rv[d * kTile + off1] << 4);
+        *dst = (uint8_t)byte;
+      }
+    } else {
+      for (int e = tid; e < nr * D; e += kBlock) {
+        const int j = e / D, d = e - j * D;
+        const int64_t to = prow((P + j0 + j) % W);
+        if (to < 0) { bad = 1; continue; }
+        uint8_t* dp = vaddr(v_pool, to, d);
+        if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_rv + (d * kTile + j) * 2);
+        else *dp = s_rv[d * kTile + j];
+      }
+    }
+    for (int j = tid; j < nr; j += kBlock)
+      ring_keep[(int64_t)i * W + (P + j0 + j) % W] = p.keep_new[((int64_t)b * M + j0 + j) * p.Hkv + h] != 0;
+  }
+  if (bad) atomicOr(p.err, CDA_DEVERR_POOL);
+  if (tid == 0) {
+    comp_len[i] = cl0 + nmove;
+    if (s_full) atomicOr(p.err, CDA_DEVERR_CAPACITY);
+    // every segment of b has read pos[b] before it counts itself in
+    const int prev = atomicAdd(p.seqcnt + b, 1);
+    if (prev == p.Hkv - 1) {
+      pos[b] = P + M;
+      p.seqcnt[b] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- merge
+
+// Workgroup (segment i, column block cb): the log-sum-exp merge of the SP
+// split states of each of its 16 columns (their o already carries the V
+// scale), normalised, into out and lse.
+template <int D>
+__global__ __launch_bounds__(kBlock) void chunk_merge_kernel(ChunkParams p) {
+  const int i = blockIdx.x / p.NB, cb = blockIdx.x - i * p.NB;
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int64_t slot0 = ((int64_t)i * p.NB + cb) * p.SP;
+  for (int e = threadIdx.x; e < 16 * (D / 4); e += kBlock) {
+    const int c = e / (D / 4), d4 = e - c * (D / 4);
+    const int col = cb * 16 + c, tq = col / p.G, hq = col - tq * p.G;
+    if (tq >= p.M) continue;
+    float Mx = -INFINITY;
+    for (int s = 0; s < p.SP; ++s) Mx = fmaxf(Mx, p.part_ml[((slot0 + s) * 16 + c) * 2]);
+    f32x4 O = f32x4{0, 0, 0, 0};
+    float L = 0.0f;
+    if (Mx != -INFINITY) {
+      for (int s = 0; s < p.SP; ++s) {
+        const int64_t sl = (slot0 + s) * 16 + c;
+        const float ms = p.part_ml[sl * 2];
+        if (ms == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(ms - Mx);
+        O += f * *reinterpret_cast<const f32x4*>(p.part_o + sl * D + 4 * d4);
+        L += f * p.part_ml[sl * 2 + 1];
+      }
+    }
+    const int64_t row = ((int64_t)b * p.M + tq) * p.Hq + h * p.G + hq;
+    const f32x4 v = L > 0.0f ? O * (1.0f / L) : f32x4{0, 0, 0, 0};
+    if (p.out_f32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row * D + 4 * d4) = v;
+    } else {
+      const uint32_t lo = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * D + 4 * d4) = u32x2{lo, hi};
+    }
+    if (d4 == 0 && p.lse) p.lse[row] = L > 0.0f ? (Mx + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Column blocks and splits of a chunk call: NB blocks of 16 (token, query
+// head) columns; splits so that the grid holds about kChunkTarget
+// workgroups (at most 16).
+void chunk_shape(int nh, int G, int M, int& NB, int& SP) {
+  NB = (G * M + 15) / 16;
+  const int64_t per = (int64_t)std::max(nh, 1) * NB;
+  SP = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kChunkTarget + per - 1) / per));
+}
+
+template <bool PG>
+void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
+                          const ChunkParams& p, uint8_t* k_pool, uint8_t* v_pool,
+                          int32_t* comp_len, uint8_t* ring_keep, int32_t* pos) {
+  const int groups = (nh + 7) / 8;
+  const dim3 grid((unsigned)(8 * groups * NB * SP));
+#define CDA_CHUNK(F, DD)                                                        \
+  do {                                                                          \
+    chunk_encode_kernel<F, DD><<<nh, kBlock, 0, s>>>(p);                        \
+    chunk_attn_kernel<F, DD, PG><<<grid, 64 * kChunkWaves, 0, s>>>(p);          \
+    chunk_merge_kernel<DD><<<nh * NB, kBlock, 0, s>>>(p);                       \
+    chunk_commit_kernel<F, DD, PG><<<nh, kBlock, 0, s>>>(p, k_pool, v_pool,     \
+                                                         comp_len, ring_keep, pos); \
+  } while (0)
+  if (kv == kKvFP4) {
+    CDA_CHUNK(kKvFP4, 128);
+  } else if (kv == kKvFP8) {
+    if (D == 64) CDA_CHUNK(kKvFP8, 64); else CDA_CHUNK(kKvFP8, 128);
+  } else {
+    if (D == 64) CDA_CHUNK(kKvBF16, 64); else CDA_CHUNK(kKvBF16, 128);
+  }
+#undef CDA_CHUNK
+}
+
+}  // namespace
+
+// Workspace: [chunk K tiles][chunk V tiles][commit counters][partial (m, l)][partial o].
+size_t chunk_workspace_bytes(const cda_kv_cache& c, int G, int M) {
+  const int nh = c.B * c.Hkv;
+  int NB, SP;
+  chunk_shape(nh, G, M, NB, SP);
+  const size_t tile = (size_t)kTile * kv_row_bytes(c.kv_dtype, c.D);
+  const size_t cols = (size_t)nh * NB * SP * 16;
+  return 2 * align256((size_t)nh * tile) + align256((size_t)c.B * 4) + align256(cols * 2 * 4) +
+         align256(cols * c.D * 4);
+}
+
+hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M, const void* q,
+                        int Hq, float sm_scale, void* out, int out_f32, float* lse,
+                        void* workspace, hipStream_t s) {
+  const int nh = c.B * c.Hkv;
+  if (nh == 0 || M <= 0) return hipGetLastError();
+  const int G = Hq / c.Hkv;
+  ChunkParams p;
+  p.k_pool = static_cast<const uint8_t*>(c.k_pool);
+  p.v_pool = static_cast<const uint8_t*>(c.v_pool);
+  p.pool_rows = c.pool_rows;
+  p.seg_base = c.seg_base;
+  p.page_table = c.page_table;
+  p.max_pages = c.max_pages;
+  p.n_pages = (int)(c.pool_rows / kTile);
+  p.seg_cap = c.seg_cap;
+  p.comp_len = c.comp_len;
+  p.pos = c.pos;
+  p.ring_keep = c.ring_keep;
+  p.k_amax = c.k_amax;
+  p.v_amax = c.v_amax;
+  p.q = static_cast<const uint16_t*>(q);
+  p.out = out;
+  p.lse = lse;
+  p.k_new = static_cast<const uint16_t*>(a.k);
+  p.v_new = static_cast<const uint16_t*>(a.v);
+  p.nsb = a.stride_b;
+  p.nst = a.stride_t;
+  p.nsh = a.stride_h;
+  p.keep_new = a.keep;
+  p.B = c.B;
+  p.Hkv = c.Hkv;
+  p.Hq = Hq;
+  p.G = G;
+  p.M = M;
+  p.W = c.W;
+  p.nh = nh;
+  chunk_shape(nh, G, M, p.NB, p.SP);
+  p.out_f32 = out_f32;
+  p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c.D);
+  p.err = c.err;
+  const size_t tile = (size_t)kTile * kv_row_bytes(c.kv_dtype, c.D);
+  const size_t cols = (size_t)nh * p.NB * p.SP * 16;
+  char* ws = static_cast<char*>(workspace);
+  p.chunk_k = reinterpret_cast<uint8_t*>(ws);
+  ws += align256((size_t)nh * tile);
+  p.chunk_v = reinterpret_cast<uint8_t*>(ws);
+  ws += align256((size_t)nh * tile);
+  p.seqcnt = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)c.B * 4);
+  p.part_ml = reinterpret_cast<float*>(ws);
+  ws += align256(cols * 2 * 4);
+  p.part_o = reinterpret_cast<float*>(ws);
+  uint8_t* kp = static_cast<uint8_t*>(c.k_pool);
+  uint8_t* vp = static_cast<uint8_t*>(c.v_pool);
+  if (c.page_table)
+    launch_chunk_kernels<true>(c.kv_dtype, c.D, nh, p.NB, p.SP, s, p, kp, vp, c.comp_len,
+                               c.ring_keep, c.pos);
+  else
+    launch_chunk_kernels<false>(c.kv_dtype, c.D, nh, p.NB, p.SP, s, p, kp, vp, c.comp_len,
+                                c.ring_keep, c.pos);
+  return hipGetLastError();
+}
+
+}  // namespace cda

@@ -482,8 +482,9 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
 struct AppendParams {
   const uint16_t* k;
   const uint16_t* v;
-  int64_t sb, sh;
-  const uint8_t* keep;
+  int64_t sb, st, sh;        // token t of a chunk at t * st
+  const uint8_t* keep;       // [B, M, Hkv]
+  int M;                     // tokens appended, one after another
   int W, Hkv, D;
   const int64_t* seg_base;   // contiguous segments
   const int32_t* page_table; // paged store: [nh][max_pages], or NULL
@@ -519,7 +520,9 @@ struct Row8 {
 // a byte's two rows are the moved row or the new row and a row nobody
 // writes in this step).  Paged store: the three rows' pages come from the
 // page table first (one more round trip); an idle sequence (pos < 0) is
-// left as it is.
+// left as it is.  A chunk of M tokens is appended one token after another,
+// with a barrier between them: a later token reads ring rows, ring keep
+// bytes and comp_len that an earlier one wrote (same workgroup).
 template <int KV>
 __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
   typedef typename std::conditional<KV == kKvBF16, uint16_t, uint8_t>::type elem_t;
@@ -529,10 +532,12 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
   const int W = p.W, D = p.D;
   const int RB = kv_row_bytes(KV, D);
   const int cpr = D / 8;                       // 8-element chunks per row
-  const int P = p.pos[b];
+  const int P0 = p.pos[b];
   const bool paged = p.page_table != nullptr;
-  if (paged && P < 0) return;       // idle sequence (uniform over the workgroup)
+  if (paged && P0 < 0) return;      // idle sequence (uniform over the workgroup)
   elem_t* vp = reinterpret_cast<elem_t*>(p.v_pool);
+  for (int tk = 0; tk < p.M; ++tk) {
+  const int P = P0 + tk;
   for (int h0 = 0; h0 < p.Hkv; h0 += kBlock / cpr) {
     const int h = h0 + tid / cpr, d0 = (tid % cpr) * 8;
     if (h >= p.Hkv) continue;
@@ -551,10 +556,10 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
     };
     const int cl0 = p.comp_len[i];
     const int cap = p.seg_cap[i];
-    const int kept = p.keep[i] != 0;
+    const int kept = p.keep[((int64_t)b * p.M + tk) * p.Hkv + h] != 0;
     const float kinv = Q ? kv_inv_scale<KV>(p.k_amax[i]) : 1.0f;
     const float vinv = Q ? kv_inv_scale<KV>(p.v_amax[i]) : 1.0f;
-    const int64_t off = (int64_t)b * p.sb + (int64_t)h * p.sh + d0;
+    const int64_t off = (int64_t)b * p.sb + (int64_t)tk * p.st + (int64_t)h * p.sh + d0;
     const u32x4 kn = *reinterpret_cast<const u32x4*>(p.k + off);
     const u32x4 vn = *reinterpret_cast<const u32x4*>(p.v + off);
     // byte of this thread's K slice in a row
@@ -653,8 +658,9 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p) {
       if (bad) atomicOr(p.err, CDA_DEVERR_POOL);
     }
   }
-  __syncthreads();                  // every thread has read pos[b]
-  if (tid == 0) p.pos[b] = P + 1;
+  __syncthreads();                  // this token's writes before the next token's reads
+  }
+  if (tid == 0) p.pos[b] = P0 + p.M;   // every thread read pos[b] before the first barrier
 }
 
 // ---------------------------------------------------------------- PAGES
@@ -978,14 +984,16 @@ hipError_t launch_pack(const cda_kv_cache& c, const cda_compact_args& a, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s) {
-  if (c.B * c.Hkv == 0) return hipGetLastError();
+hipError_t launch_append(const cda_kv_cache& c, const cda_compact_args& a, hipStream_t s, int M) {
+  if (c.B * c.Hkv == 0 || M <= 0) return hipGetLastError();
   AppendParams p;
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
   p.sb = a.stride_b;
+  p.st = a.stride_t;
   p.sh = a.stride_h;
   p.keep = a.keep;
+  p.M = M;
   p.W = c.W;
   p.Hkv = c.Hkv;
   p.D = c.D;

@@ -113,6 +113,7 @@ extern "C" {
 #define CDA_VERSION 2
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
+#define CDA_MAX_CHUNK 64        /* largest chunk of chunk_attn_compact */
 
 /* Return codes of every call. */
 enum cda_status {
@@ -292,6 +293,47 @@ int32_t decode_step_compact(const cda_kv_cache *cache, const cda_compact_args *a
 /* Workspace bytes decode_attn_compact and decode_step_compact need for this
  * cache, Hq and split. */
 size_t cda_attn_workspace_bytes(const cda_kv_cache *cache, int32_t Hq, int32_t split_tokens);
+
+/*
+ * chunk_attn_compact -- a chunk of M new tokens per sequence: multi-query
+ * attention over the compact store, then their append.
+ *
+ * The step around the decode path, given by PyramidInfer's point that the
+ * cache is compressed already while the prompt is processed, on the FastDMS
+ * store (memory-table paragraph: compact cache plus W-token staging): the
+ * prompt continues chunk by chunk on top of a compacted context (or several
+ * draft tokens are scored at once).  Sequence b receives tokens at positions
+ * P .. P+M-1 (P = pos[b]); query t is answered exactly as decode_step_compact
+ * would answer it at position P + t after appending tokens P .. P+t one at a
+ * time:
+ *   out[b,t,j,:] = sum_p softmax(z)_p v^_p over the rows stored after token
+ *   P + t, z_p = sm_scale * q[b,t,j,:] . k^_p, lse[b,t,j] = log sum_p exp(z_p)
+ * (the compact rows; ring rows and chunk tokens t' <= t that are still in
+ * query t's window or kept).  Afterwards the cache is bit for bit what M
+ * successive kv_compact(APPEND) calls leave (pos[b] += M).
+ *
+ *   args       APPEND arguments: k, v BF16, token t of head h of sequence b
+ *              at b*stride_b + t*stride_t + h*stride_h + d (16-byte aligned
+ *              rows); keep [B, M, Hkv] bytes at keep + (b*M + t)*Hkv + h
+ *   M          1 .. CDA_MAX_CHUNK
+ *   q          BF16 [B, M, Hq, D] contiguous, 16-byte aligned
+ *   out        [B, M, Hq, D] contiguous, BF16 or F32 per out_dtype, 16-byte aligned
+ *   lse        optional F32 [B, M, Hq]
+ *   workspace  at least cda_chunk_workspace_bytes() bytes, 256-byte aligned,
+ *              any contents (the chunk's encoded rows and the partial states)
+ * Every sequence of a contiguous store takes part; with a paged store, idle
+ * sequences (pos < 0) give out = 0, lse = -inf and are not appended to.
+ * Errors as for kv_compact and decode_attn_compact; the compact region must
+ * have room for the chunk (CDA_DEVERR_CAPACITY otherwise, as for APPEND).
+ */
+int32_t chunk_attn_compact(const cda_kv_cache *cache, const cda_compact_args *args, int32_t M,
+                           const void *q, int32_t Hq, float sm_scale, void *out,
+                           int32_t out_dtype, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Workspace bytes chunk_attn_compact needs for this cache, Hq and M (0 if
+ * they are invalid). */
+size_t cda_chunk_workspace_bytes(const cda_kv_cache *cache, int32_t Hq, int32_t M);
 
 /* Static text for a cda_status value. */
 const char *cda_status_string(int32_t status);

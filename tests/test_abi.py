@@ -231,3 +231,30 @@ def test_paged_ranges_and_ops(lib):
     need = L.cda_attn_workspace_bytes(C.byref(p), 8, 0)
     assert L.decode_step_compact(C.byref(p), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws, need,
                                  None) == 1
+
+
+def test_chunk_validation(lib):
+    L = lib.load()
+    c = _cache(lib)
+    a = lib.CdaCompactArgs()
+    a.op, a.keep, a.k, a.v = lib.CDA_OP_APPEND, 0x100000, 0x100000, 0x100000
+    a.stride_b, a.stride_t, a.stride_h = 512, 128, 64
+    q = out = ws = C.c_void_p(0x100000)
+    f = L.chunk_attn_compact
+    need = L.cda_chunk_workspace_bytes(C.byref(c), 8, 4)
+    assert need > 0
+    assert L.cda_chunk_workspace_bytes(C.byref(c), 8, 0) == 0
+    assert L.cda_chunk_workspace_bytes(C.byref(c), 8, lib.CDA_MAX_CHUNK + 1) == 0
+    assert f(C.byref(c), C.byref(a), 0, q, 8, 0.0, out, 0, None, ws, need, None) == 1     # M = 0
+    assert f(C.byref(c), C.byref(a), 65, q, 8, 0.0, out, 0, None, ws, need, None) == 1    # M > 64
+    assert f(C.byref(c), C.byref(a), 4, q, 7, 0.0, out, 0, None, ws, need, None) == 2     # Hq % Hkv
+    assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 3, None, ws, need, None) == 2     # out dtype
+    assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws, need - 1, None) == 3  # workspace
+    assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 0, None, C.c_void_p(0x100010), need,
+             None) == 1                                                                   # ws alignment
+    a.stride_t = 12
+    assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws, need, None) == 1     # stride
+    a.stride_t, a.op = 128, lib.CDA_OP_PACK
+    assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws, need, None) == 1     # not APPEND
+    # the workspace grows with the chunk
+    assert L.cda_chunk_workspace_bytes(C.byref(c), 8, 64) > need
