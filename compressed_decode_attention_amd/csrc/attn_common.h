@@ -46,6 +46,8 @@ __device__ __forceinline__ int q_d0(int s, int kg) {
   return 32 * s + 8 * kg;
 }
 
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+
 // Mask of the bytes of dword w (bytes 4w .. 4w+3) that lie below `lim`.
 __device__ __forceinline__ uint32_t bytes_below(int lim, int w) {
   const int k = lim - 4 * w;

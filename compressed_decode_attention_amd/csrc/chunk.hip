@@ -43,7 +43,8 @@ namespace cda {
 namespace {
 
 constexpr int kChunkWaves = 4;       // waves per attention workgroup
-constexpr int kChunkTarget = 512;    // workgroups the split count aims at
+constexpr int kChunkTarget = 512;    // workgroups the split count aims at (narrow kernel)
+constexpr int kWideTarget = 256;     // ... and for the wide kernel: one per CU
 
 struct ChunkParams {
   const uint8_t* k_pool;
@@ -427,6 +428,344 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
   }
 }
 
+// ---------------------------------------------------------------- attention, wide
+
+// For chunks with many columns (at least 4 blocks of 16): workgroup (segment,
+// split s, group of up to 16 column blocks), 8 waves.  The workgroup walks
+// the tiles s, s + SP, ... and the chunk tile together.  For each tile the
+// 8 waves stage it in LDS -- the next tile's bytes already in flight in
+// registers -- converting FP8/FP4 codes once, exactly, to the MFMA operand
+// types (K to bf16 in the order the q operand expects, V to a [d][row] f16
+// image like a BF16 V tile), zeroing V rows past the data, and copying the
+// tile's 64 keep bytes.  Wave w owns column blocks 2w and 2w + 1 over every
+// tile: each K and V operand is read from LDS once and used for both.
+// Masks are 16-bit row masks per lane: rows past the data; ring rows that
+// left the query's window unkept (one circular interval of ring rows);
+// chunk tokens after the query or out of its window unkept.
+constexpr int kWideWaves = 8, kWideBlocks = 2;   // waves, column blocks per wave
+constexpr int kWideGroup = kWideWaves * kWideBlocks;
+
+// Bits of rows [a, b] (inclusive) among the 16 rows base .. base + 15.
+__device__ __forceinline__ uint32_t range_bits(int a, int b, int base) {
+  const int lo = max(a - base, 0), hi = min(b - base, 15);
+  return lo > hi ? 0u : (((2u << hi) - 1u) & ~((1u << lo) - 1u));
+}
+
+template <int KV, int D, bool PG>
+__global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkParams p) {
+  constexpr int NW = kWideWaves, BPW = kWideBlocks;
+  constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
+  constexpr int RB = kv_row_bytes(KV, D);
+  constexpr int NK = D / 32, NT = D / 16, KL = RB / 64;
+  constexpr int TB = kTile * RB;                  // bytes of a stored K (or V) tile
+  constexpr int CPT = 2 * TB / 16 / (64 * NW);    // 16-byte chunks per thread
+  constexpr int SPC = FP4 ? 4 : FP8 ? 2 : 1;      // MFMA k-steps per stored 16-byte K chunk
+  constexpr int TX = kTile * D * 2;               // bytes of a staged (16-bit) K tile
+  constexpr int VP = kTile * 2 + 16;              // bytes per staged V column (padded)
+  static_assert(CPT >= 1 && 2 * TB % (16 * 64 * NW) == 0, "tile copy shape");
+
+  // K as bf16 MFMA operands, operand-major: operand (m, st) of lane l at
+  // ((m * NK + st) * 64 + l) * 16; V as [d][row] 16-bit values, VP bytes a column
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[TX];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[D * VP];
+  __shared__ uint8_t s_keep[kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane & 15, kg = lane >> 4;
+  const int NCG = (p.NB + kWideGroup - 1) / kWideGroup;
+  int work = blockIdx.x >> 3;
+  const int s = work % p.SP;
+  work /= p.SP;
+  const int cgi = work % NCG;
+  const int i = (blockIdx.x & 7) + 8 * (work / NCG);
+  if (i >= p.nh) return;                          // the whole workgroup
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int W = p.W, G = p.G, M = p.M;
+
+  const int Praw = p.pos[b];
+  const bool idle = Praw < 0;
+  const int P = max(Praw, 0);
+  const int cap = max(p.seg_cap[i], 0);
+  const int cl = min(max(p.comp_len[i], 0), cap);
+  const int n = idle ? 0 : min(W, P) + cl;
+  const int ntiles = (n + kTile - 1) / kTile;
+  const int last = idle ? ntiles - 1 : ntiles;   // the chunk tile is tile ntiles
+  const int64_t sb = PG ? 0 : p.seg_base[i];
+  const float ks = Q ? kv_scale<KV>(p.k_amax[i]) : 1.0f;
+  const float vs = Q ? kv_scale<KV>(p.v_amax[i]) : 1.0f;
+  const float c1 = p.sm_scale * kLog2e * ks;
+  const int pmw = W > 0 ? P % W : 0;
+
+  // this wave's columns: blocks cb0 + bb, column cb * 16 + g -> (token, head)
+  const int cb0 = cgi * kWideGroup + wave * BPW;
+  int tq[BPW];
+  bool col_ok[BPW];   // per lane: the column is a query of the chunk
+  bool blk_ok[BPW];   // per wave: the block exists
+  bf16x8 qop[BPW][NK];
+#pragma unroll
+  for (int bb = 0; bb < BPW; ++bb) {
+    const int col = (cb0 + bb) * 16 + g;
+    tq[bb] = col / G;
+    blk_ok[bb] = cb0 + bb < p.NB;
+    col_ok[bb] = blk_ok[bb] && tq[bb] < M;
+    const int hq = col - tq[bb] * G;
+    const int64_t qrow = col_ok[bb] ? ((int64_t)(b * M + tq[bb]) * p.Hq + h * G + hq)
+                                    : ((int64_t)b * M * p.Hq + h * G);
+    const uint16_t* qr = p.q + qrow * D;
+#pragma unroll
+    for (int st = 0; st < NK; ++st)
+      qop[bb][st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + q_d0<KV>(st, kg)));
+  }
+  const bool busy = blk_ok[0];
+
+  // stored bytes of tile tt (and its keep bytes) -> registers
+  auto fetch = [&](int tt, u32x4 (&rg)[CPT], uint32_t& kb, bool& ok) {
+    const bool ctile = tt == ntiles;
+    const uint8_t* kt;
+    const uint8_t* vt;
+    ok = true;
+    if (ctile) {
+      kt = p.chunk_k + (int64_t)i * TB;
+      vt = p.chunk_v + (int64_t)i * TB;
+    } else {
+      int64_t trow = sb + (int64_t)tt * kTile;
+      if (PG) {
+        const int pg = p.page_table[(int64_t)i * p.max_pages + min(tt, p.max_pages - 1)];
+        ok = tt < p.max_pages && pg >= 0 && pg < p.n_pages;
+        trow = ok ? (int64_t)pg * kTile : 0;
+      }
+      kt = p.k_pool + trow * RB;
+      vt = p.v_pool + trow * RB;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = c * 64 * NW + tid;          // chunk of the K+V image
+      const uint8_t* src = ch * 16 < TB ? kt + ch * 16 : vt + (ch * 16 - TB);
+      rg[c] = *reinterpret_cast<const u32x4*>(src);
+    }
+    kb = 0;
+    if (tid < kTile) {
+      const int r0 = tt * kTile;
+      if (ctile) kb = p.keep_new[((int64_t)b * M + min(tid, M - 1)) * p.Hkv + h];
+      else if (r0 < W) kb = p.ring_keep[(int64_t)i * W + min(r0 + tid, W - 1)];
+    }
+  };
+
+  float m_run[BPW], l_run[BPW];
+  f32x4 acc[BPW][NT];
+#pragma unroll
+  for (int bb = 0; bb < BPW; ++bb) {
+    m_run[bb] = -INFINITY;
+    l_run[bb] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[bb][t] = f32x4{0, 0, 0, 0};
+  }
+  bool first_tile = true;
+
+  u32x4 rg[CPT];
+  uint32_t kbyte = 0;
+  bool ok = true;
+  if (s <= last) fetch(s, rg, kbyte, ok);
+  for (int tt = s; tt <= last; tt += p.SP) {
+    const bool ctile = tt == ntiles;
+    const int r0 = tt * kTile;
+    const int valid = ctile ? M : min(kTile, n - r0);
+    // ---- this tile -> LDS (converted), then the next one's bytes into the registers
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = c * 64 * NW + tid;
+      const u32x4 x = rg[c];
+      if (ch * 16 < TB) {                        // K chunk ch: SPC k-steps of one lane
+        const int kl = ch & 63, kj = (ch >> 6) % KL, km = (ch >> 6) / KL;
+        uint8_t* dst = s_k + ((km * NK + kj * SPC) * 64 + kl) * 16;   // operand (km, kj SPC + q)
+        if (FP4) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<bf16x8*>(dst + 1024 * q) = fp4x8_to_bf16x8(x[q]);
+        } else if (FP8) {
+          *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16x8(x[0], x[1]);
+          *reinterpret_cast<bf16x8*>(dst + 1024) = fp8x8_to_bf16x8(x[2], x[3]);
+        } else {
+          *reinterpret_cast<u32x4*>(dst) = x;
+        }
+      } else {                                   // V: rows row0 .. of column d
+        const int vb = ch * 16 - TB;             // byte of the stored V tile
+        if (FP4) {                               // 32 rows
+          const int d = vb / 32, row0 = (vb % 32) * 2;
+          uint8_t* dst = s_v + d * VP + row0 * 2;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f16x8 y = fp4x8_to_f16x8(x[q]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (row0 + 8 * q + e >= valid) y[e] = (_Float16)0.0f;
+            *reinterpret_cast<f16x8*>(dst + 16 * q) = y;
+          }
+        } else if (FP8) {                        // 16 rows
+          const int d = vb / kTile, row0 = vb % kTile;
+          uint8_t* dst = s_v + d * VP + row0 * 2;
+          f16x8 y0 = fp8x8_to_f16x8(x[0], x[1]), y1 = fp8x8_to_f16x8(x[2], x[3]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (row0 + e >= valid) y0[e] = (_Float16)0.0f;
+            if (row0 + 8 + e >= valid) y1[e] = (_Float16)0.0f;
+          }
+          *reinterpret_cast<f16x8*>(dst) = y0;
+          *reinterpret_cast<f16x8*>(dst + 16) = y1;
+        } else {                                 // 8 rows, as stored
+          const int d = (vb / 2) / kTile, row0 = (vb / 2) % kTile;
+          u32x4 y = x;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = row0 + 2 * q;
+            y[q] &= (r >= valid ? 0u : 0xFFFFu) | (r + 1 >= valid ? 0u : 0xFFFF0000u);
+          }
+          *reinterpret_cast<u32x4*>(s_v + d * VP + row0 * 2) = y;
+        }
+      }
+    }
+    if (tid < kTile) s_keep[tid] = (uint8_t)(kbyte != 0);
+    const bool tile_ok = ok;
+    if (!tile_ok && tid == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+    __syncthreads();
+    if (tt + p.SP <= last) fetch(tt + p.SP, rg, kbyte, ok);
+
+    if (busy && tile_ok) {
+      // ---- row masks of this lane's 16 rows (bit j: row 16 kg + j of the tile)
+      const int base = r0 + 16 * kg;
+      uint32_t kb = 0;
+      const bool ring = !ctile && r0 < W;
+      if (ctile || ring) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) kb |= (uint32_t)s_keep[16 * kg + j] << j;
+      }
+      const uint32_t vbits = range_bits(ctile ? 0 : r0, (ctile ? 0 : r0) + valid - 1,
+                                        ctile ? 16 * kg : base);
+      uint32_t vis[BPW];
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb) {
+        uint32_t v = col_ok[bb] ? vbits : 0u;
+        const int t = tq[bb];
+        if (ctile) {   // chunk tokens rr <= t, in the window or kept
+          v &= range_bits(t - W + 1, t, 16 * kg) | (kb & range_bits(0, t, 16 * kg));
+        } else if (ring) {
+          // ring rows whose token left query t's window: P >= W: the t + 1
+          // rows from pmw on (circularly); P < W: rows 0 .. P + t - W
+          uint32_t hid;
+          if (P >= W) {
+            const int len = min(t + 1, W);
+            hid = range_bits(pmw, min(pmw + len, W) - 1, base) |
+                  range_bits(0, pmw + len - W - 1, base);
+          } else {
+            hid = range_bits(0, min(P + t - W, W - 1), base);
+          }
+          v &= ~(hid & ~kb);
+        }
+        vis[bb] = v;
+      }
+
+      // ---- S = K . Q^T for both blocks, each K operand read once
+      f32x4 sc[BPW][4];
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sc[bb][m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int st = 0; st < NK; ++st) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(s_k + ((m * NK + st) * 64 + lane) * 16);
+#pragma unroll
+          for (int bb = 0; bb < BPW; ++bb)
+            if (blk_ok[bb]) sc[bb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[bb][st], sc[bb][m], 0, 0, 0);
+        }
+
+      // ---- per block: online softmax -> P operand, then O^T += V^T . P^T.
+      // Block 1's softmax (VALU) is independent of block 0's PV products
+      // (MFMA), so the two overlap; V operands are read again for block 1.
+#pragma unroll
+      for (int bb = 0; bb < BPW; ++bb) {
+        if (!blk_ok[bb]) continue;
+        float z[4][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            z[m][r] = ((vis[bb] >> (4 * m + r)) & 1u) ? sc[bb][m][r] * c1 : -INFINITY;
+            tmax = fmaxf(tmax, z[m][r]);
+          }
+        tmax = max_xor32(max_xor16(tmax));
+        const float m_new = fmaxf(m_run[bb], tmax);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        if (!first_tile) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run[bb] - m_use);
+          l_run[bb] *= alpha;
+          if (__ballot(alpha != 1.0f)) {   // once the maxima settle, most tiles skip this
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[bb][nt] *= alpha;
+          }
+        }
+        float psum = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
+            psum += z[m][r];
+          }
+        l_run[bb] += psum;
+        m_run[bb] = m_new;
+        f16x8 pf[2];
+        bf16x8 phi[2], plo[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pv = z[2 * hh + (e >> 2)][e & 3];
+            if (Q) {
+              pf[hh][e] = (_Float16)pv;
+            } else {
+              const __bf16 hi = (__bf16)pv;
+              phi[hh][e] = hi;
+              plo[hh][e] = (__bf16)(pv - (float)hi);
+            }
+          }
+        __asm__ volatile("" ::: "memory");   // V operands are read again for each block
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 vv = *reinterpret_cast<const u32x4*>(s_v + (16 * nt + g) * VP + (16 * kg + 8 * hh) * 2);
+            if (Q) {
+              acc[bb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(vv), pf[hh], acc[bb][nt], 0, 0, 0);
+            } else {
+              acc[bb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), phi[hh], acc[bb][nt], 0, 0, 0);
+              acc[bb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), plo[hh], acc[bb][nt], 0, 0, 0);
+            }
+          }
+      }
+      first_tile = false;
+    }
+    __syncthreads();   // the tile in LDS is read by every wave before the next one lands
+  }
+
+  // ---- this wave's partial states
+#pragma unroll
+  for (int bb = 0; bb < BPW; ++bb) {
+    const int cb = cb0 + bb;
+    const float l = sum_xor32(sum_xor16(l_run[bb]));
+    if (cb >= p.NB) continue;
+    const int64_t slot = ((int64_t)i * p.NB + cb) * p.SP + s;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(p.part_o + (slot * 16 + g) * D + 16 * nt + 4 * kg) = acc[bb][nt] * vs;
+    if (kg == 0) {
+      p.part_ml[(slot * 16 + g) * 2] = m_run[bb];
+      p.part_ml[(slot * 16 + g) * 2 + 1] = l;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- commit
 
 // Workgroup i: the chunk's M tokens appended to segment i, with the result of
@@ -699,10 +1038,16 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Column blocks and splits of a chunk call: NB blocks of 16 (token, query
 // head) columns; splits so that the grid holds about kChunkTarget
 // workgroups (at most 16).
+// With at least 4 blocks the wide kernel runs (one 8-wave workgroup per
+// segment, split and group of 16 blocks; about one workgroup per CU), else
+// the narrow one (one workgroup per segment, block and split).
 void chunk_shape(int nh, int G, int M, int& NB, int& SP) {
   NB = (G * M + 15) / 16;
-  const int64_t per = (int64_t)std::max(nh, 1) * NB;
-  SP = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kChunkTarget + per - 1) / per));
+  const bool wide = NB >= 4;
+  const int64_t per = (int64_t)std::max(nh, 1) *
+                      (wide ? (NB + kWideGroup - 1) / kWideGroup : NB);
+  const int64_t target = wide ? kWideTarget : kChunkTarget;
+  SP = (int)std::min<int64_t>(16, std::max<int64_t>(1, (target + per - 1) / per));
 }
 
 template <bool PG>
@@ -710,11 +1055,16 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
                           const ChunkParams& p, uint8_t* k_pool, uint8_t* v_pool,
                           int32_t* comp_len, uint8_t* ring_keep, int32_t* pos) {
   const int groups = (nh + 7) / 8;
-  const dim3 grid((unsigned)(8 * groups * NB * SP));
+  const bool wide = NB >= 4;
+  const int ncg = (NB + kWideGroup - 1) / kWideGroup;
+  const dim3 grid((unsigned)(8 * groups * NB * SP)), wgrid((unsigned)(8 * groups * ncg * SP));
 #define CDA_CHUNK(F, DD)                                                        \
   do {                                                                          \
     chunk_encode_kernel<F, DD><<<nh, kBlock, 0, s>>>(p);                        \
-    chunk_attn_kernel<F, DD, PG><<<grid, 64 * kChunkWaves, 0, s>>>(p);          \
+    if (wide)                                                                   \
+      chunk_attn_wide_kernel<F, DD, PG><<<wgrid, 64 * kWideWaves, 0, s>>>(p);   \
+    else                                                                        \
+      chunk_attn_kernel<F, DD, PG><<<grid, 64 * kChunkWaves, 0, s>>>(p);        \
     chunk_merge_kernel<DD><<<nh * NB, kBlock, 0, s>>>(p);                       \
     chunk_commit_kernel<F, DD, PG><<<nh, kBlock, 0, s>>>(p, k_pool, v_pool,     \
                                                          comp_len, ring_keep, pos); \
