@@ -431,18 +431,19 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // ---------------------------------------------------------------- attention, wide
 
 // For chunks with many columns (at least 4 blocks of 16): workgroup (segment,
-// split s, group of up to 16 column blocks), 8 waves.  The workgroup walks
+// split s, group of up to 16 column blocks), 16 waves.  The workgroup walks
 // the tiles s, s + SP, ... and the chunk tile together.  For each tile the
-// 8 waves stage it in LDS -- the next tile's bytes already in flight in
+// waves stage it in LDS -- the next tile's bytes already in flight in
 // registers -- converting FP8/FP4 codes once, exactly, to the MFMA operand
 // types (K to bf16 in the order the q operand expects, V to a [d][row] f16
-// image like a BF16 V tile), zeroing V rows past the data, and copying the
-// tile's 64 keep bytes.  Wave w owns column blocks 2w and 2w + 1 over every
-// tile: each K and V operand is read from LDS once and used for both.
-// Masks are 16-bit row masks per lane: rows past the data; ring rows that
-// left the query's window unkept (one circular interval of ring rows);
-// chunk tokens after the query or out of its window unkept.
-constexpr int kWideWaves = 8, kWideBlocks = 2;   // waves, column blocks per wave
+// image like a BF16 V tile), zeroing V rows past the data, and publishing
+// the rows' keep bits as one ballot.  Wave w owns column block w over every
+// tile.  Masks are 16-bit row masks per lane: rows past the data; ring rows
+// that left the query's window unkept (one circular interval of ring rows);
+// chunk tokens after the query or out of its window unkept.  (Two blocks
+// per wave with 8 waves read each operand once for both, but at 2 waves per
+// SIMD ran 44 us against 39 us for this shape on the Qwen c = 8 layer.)
+constexpr int kWideWaves = 16, kWideBlocks = 1;  // waves, column blocks per wave
 constexpr int kWideGroup = kWideWaves * kWideBlocks;
 
 // Bits of rows [a, b] (inclusive) among the 16 rows base .. base + 15.
@@ -458,17 +459,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   constexpr int RB = kv_row_bytes(KV, D);
   constexpr int NK = D / 32, NT = D / 16, KL = RB / 64;
   constexpr int TB = kTile * RB;                  // bytes of a stored K (or V) tile
-  constexpr int CPT = 2 * TB / 16 / (64 * NW);    // 16-byte chunks per thread
+  constexpr int NCH = 2 * TB / 16;                // 16-byte chunks of a stored K + V tile
+  constexpr int CPT = (NCH + 64 * NW - 1) / (64 * NW);   // per thread
   constexpr int SPC = FP4 ? 4 : FP8 ? 2 : 1;      // MFMA k-steps per stored 16-byte K chunk
   constexpr int TX = kTile * D * 2;               // bytes of a staged (16-bit) K tile
   constexpr int VP = kTile * 2 + 16;              // bytes per staged V column (padded)
-  static_assert(CPT >= 1 && 2 * TB % (16 * 64 * NW) == 0, "tile copy shape");
+  static_assert(NCH % 64 == 0, "tile copy shape");
 
   // K as bf16 MFMA operands, operand-major: operand (m, st) of lane l at
   // ((m * NK + st) * 64 + l) * 16; V as [d][row] 16-bit values, VP bytes a column
   __shared__ __attribute__((aligned(16))) uint8_t s_k[TX];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[D * VP];
-  __shared__ uint8_t s_keep[kTile];
+  __shared__ uint64_t s_keep;   // keep bits of the staged tile's rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 15, kg = lane >> 4;
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = c * 64 * NW + tid;          // chunk of the K+V image
+      const int ch = min(c * 64 * NW + tid, NCH - 1);   // chunk of the K+V image
       const uint8_t* src = ch * 16 < TB ? kt + ch * 16 : vt + (ch * 16 - TB);
       rg[c] = *reinterpret_cast<const u32x4*>(src);
     }
@@ -567,6 +569,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   bool ok = true;
   if (s <= last) fetch(s, rg, kbyte, ok);
   for (int tt = s; tt <= last; tt += p.SP) {
+
     const bool ctile = tt == ntiles;
     const int r0 = tt * kTile;
     const int valid = ctile ? M : min(kTile, n - r0);
@@ -575,6 +578,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     for (int c = 0; c < CPT; ++c) {
       const int ch = c * 64 * NW + tid;
       const u32x4 x = rg[c];
+      if (ch >= NCH) continue;                   // wave-uniform (NCH is a multiple of 64)
       if (ch * 16 < TB) {                        // K chunk ch: SPC k-steps of one lane
         const int kl = ch & 63, kj = (ch >> 6) % KL, km = (ch >> 6) / KL;
         uint8_t* dst = s_k + ((km * NK + kj * SPC) * 64 + kl) * 16;   // operand (km, kj SPC + q)
@@ -595,19 +599,23 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             f16x8 y = fp4x8_to_f16x8(x[q]);
+            if (row0 + 8 * q + 8 > valid) {       // rows past the data
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (row0 + 8 * q + e >= valid) y[e] = (_Float16)0.0f;
+              for (int e = 0; e < 8; ++e)
+                if (row0 + 8 * q + e >= valid) y[e] = (_Float16)0.0f;
+            }
             *reinterpret_cast<f16x8*>(dst + 16 * q) = y;
           }
         } else if (FP8) {                        // 16 rows
           const int d = vb / kTile, row0 = vb % kTile;
           uint8_t* dst = s_v + d * VP + row0 * 2;
           f16x8 y0 = fp8x8_to_f16x8(x[0], x[1]), y1 = fp8x8_to_f16x8(x[2], x[3]);
+          if (row0 + 16 > valid) {                // rows past the data
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            if (row0 + e >= valid) y0[e] = (_Float16)0.0f;
-            if (row0 + 8 + e >= valid) y1[e] = (_Float16)0.0f;
+            for (int e = 0; e < 8; ++e) {
+              if (row0 + e >= valid) y0[e] = (_Float16)0.0f;
+              if (row0 + 8 + e >= valid) y1[e] = (_Float16)0.0f;
+            }
           }
           *reinterpret_cast<f16x8*>(dst) = y0;
           *reinterpret_cast<f16x8*>(dst + 16) = y1;
@@ -623,7 +631,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
         }
       }
     }
-    if (tid < kTile) s_keep[tid] = (uint8_t)(kbyte != 0);
+    if (wave == 0) {   // the tile's keep bits, one per row
+      const uint64_t km = __ballot(kbyte != 0);
+      if (lane == 0) s_keep = km;
+    }
     const bool tile_ok = ok;
     if (!tile_ok && tid == 0) atomicOr(p.err, CDA_DEVERR_POOL);
     __syncthreads();
@@ -635,8 +646,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       uint32_t kb = 0;
       const bool ring = !ctile && r0 < W;
       if (ctile || ring) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) kb |= (uint32_t)s_keep[16 * kg + j] << j;
+        kb = (uint32_t)(s_keep >> (16 * kg)) & 0xFFFFu;
       }
       const uint32_t vbits = range_bits(ctile ? 0 : r0, (ctile ? 0 : r0) + valid - 1,
                                         ctile ? 16 * kg : base);
@@ -687,11 +697,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
         if (!blk_ok[bb]) continue;
         float z[4][4];
         float tmax = -INFINITY;
+        const bool all_vis = __ballot(vis[bb] != 0xFFFFu) == 0;   // wave-uniform
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            z[m][r] = ((vis[bb] >> (4 * m + r)) & 1u) ? sc[bb][m][r] * c1 : -INFINITY;
+            z[m][r] = sc[bb][m][r] * c1;
+            if (!all_vis && !((vis[bb] >> (4 * m + r)) & 1u)) z[m][r] = -INFINITY;
             tmax = fmaxf(tmax, z[m][r]);
           }
         tmax = max_xor32(max_xor16(tmax));
