@@ -58,6 +58,10 @@ def _oracle_append(o, lay, T, s0, M):
     ("fp8", 128, 64, 10, 20, 2, 2, 4),        # P < W: the ring is not full yet
     ("bf16", 64, 16, 1, 150, 2, 4, 2),        # a one-token chunk
     ("fp4", 128, 64, 33, 1000, 2, 2, 16),     # GQA 16
+    ("bf16", 128, 32, 64, 300, 1, 2, 4),      # BF16 through the wide kernel
+    ("bf16", 64, 16, 40, 200, 2, 2, 8),
+    ("fp4", 128, 33, 64, 20, 2, 2, 4),        # odd W, P < W: rows 32 and 33 share V bytes
+    ("fp4", 128, 33, 50, 400, 2, 2, 4),       # odd W, full ring
 ])
 def test_chunk_matches_sequential_decode(kv, D, W, M, T, B, Hkv, G):
     S = M + 8
@@ -156,3 +160,24 @@ def test_chunk_on_the_paged_store():
         assert int(c.pos[1].item()) == -1
         s0 += M
     assert c.error_word() == 0
+
+
+@pytest.mark.parametrize("kv", ["fp8", "fp4"])
+def test_chunk_past_the_capacity(kv):
+    """A chunk whose kept tokens overflow the compact region: the surplus is
+    dropped with CDA_DEVERR_CAPACITY, as M APPENDs would drop it (the oracle
+    drops the same tokens)."""
+    B, Hkv, G, D, W, T, M, reserve = 2, 2, 4, 128, 16, 300, 64, 5
+    cfg = workload.custom(B=B, Hq=G * Hkv, Hkv=Hkv, D=D, T=T, S=M, W=W, kv_dtype=kv,
+                          keep_lo=0.8, keep_hi=0.95, seed=31)
+    lay = workload.make_layer(cfg, 0)
+    c, _ = gpu_prefill(lay.k, lay.v, lay.keep, T, W, reserve, kv, with_dst=False)
+    o = oracle_prefill(lay.k, lay.v, lay.keep, T, W, reserve, kv)
+    d = dev()
+    k, v, keep, q = (x.to(d) for x in _chunk_inputs(lay, T, 0, M))
+    c.chunk(k, v, keep, q, out_dtype=torch.float32)
+    _oracle_append(o, lay, T, 0, M)
+    compare_state(c, o, "after the chunk")
+    from compressed_decode_attention_amd import CDA_DEVERR_CAPACITY
+    assert c.error_word() & CDA_DEVERR_CAPACITY
+    assert int(o.err[0]) & CDA_DEVERR_CAPACITY
