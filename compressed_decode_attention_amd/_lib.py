@@ -22,6 +22,7 @@ CDA_VERSION = 2       # the struct layouts below are those of this version
 CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16
 CDA_MAX_CHUNK = 64
+CDA_MAX_CHUNK_WINDOW = 4096
 
 # every symbol include/cda.h declares
 EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact", "chunk_attn_compact",

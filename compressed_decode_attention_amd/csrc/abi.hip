@@ -224,6 +224,7 @@ int32_t chunk_attn_compact(const cda_kv_cache* c, const cda_compact_args* a, int
   if ((st = check_pools(c)) != CDA_OK) return st;
   if (M < 1 || M > CDA_MAX_CHUNK || Hq <= 0) return CDA_ERR_INVALID_ARG;
   if (Hq % c->Hkv != 0 || Hq / c->Hkv > CDA_MAX_GQA) return CDA_ERR_UNSUPPORTED;
+  if (c->W > CDA_MAX_CHUNK_WINDOW) return CDA_ERR_UNSUPPORTED;
   if (out_dtype != CDA_OUT_BF16 && out_dtype != CDA_OUT_F32) return CDA_ERR_UNSUPPORTED;
   if (!a || a->op != CDA_OP_APPEND || a->seq_begin != 0 || a->seq_count != 0)
     return CDA_ERR_INVALID_ARG;

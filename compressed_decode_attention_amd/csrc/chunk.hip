@@ -45,6 +45,7 @@ namespace {
 constexpr int kChunkWaves = 4;       // waves per attention workgroup
 constexpr int kChunkTarget = 512;    // workgroups the split count aims at (narrow kernel)
 constexpr int kWideTarget = 256;     // ... and for the wide kernel: one per CU
+constexpr int kMaxRingTiles = CDA_MAX_CHUNK_WINDOW / kTile;   // chunk commit: ring tiles
 
 struct ChunkParams {
   const uint8_t* k_pool;
@@ -818,16 +819,28 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
   const int cl0 = min(max(comp_len[i], 0), cap);
   const uint8_t* ck = p.chunk_k + (int64_t)i * kTile * RB;   // the chunk's encoded rows
   const uint8_t* cv = p.chunk_v + (int64_t)i * kTile * RB;
+  // The rows this commit touches lie in the ring tiles [0, nrt) and the two
+  // tiles from the first compact row written on.  Their pool rows are looked
+  // up once here: inside the copy loops a load of the page table (or of
+  // seg_base) would be repeated after every byte store, which may alias it.
+  const int nrt = (W + kTile - 1) / kTile, dt0 = (W + cl0) / kTile;
+  __shared__ int64_t s_tile[kMaxRingTiles + 2];
+  const int64_t sbase = PG ? 0 : p.seg_base[i];
+  for (int t = tid; t < nrt + 2; t += kBlock) {
+    const int tt = t < nrt ? t : dt0 + (t - nrt);
+    int64_t x = sbase + (int64_t)tt * kTile;
+    if (PG) {
+      const int pg = p.page_table[(int64_t)i * p.max_pages + min(tt, p.max_pages - 1)];
+      x = (tt < p.max_pages && pg >= 0 && pg < p.n_pages) ? (int64_t)pg * kTile : -1;
+    }
+    s_tile[t] = x;
+  }
   // pool row of segment row r: -1 if it has no page or leaves the pool
   auto prow = [&](int r) -> int64_t {
-    int64_t x;
-    if (PG) {
-      const int t = r / kTile;
-      const int pg = p.page_table[(int64_t)i * p.max_pages + min(t, p.max_pages - 1)];
-      x = (t < p.max_pages && pg >= 0 && pg < p.n_pages) ? (int64_t)pg * kTile + r % kTile : -1;
-    } else {
-      x = p.seg_base[i] + r;
-    }
+    const int tt = r / kTile;
+    const int slot = tt < nrt ? tt : nrt + (tt - dt0);
+    const int64_t x0 = (slot >= 0 && slot < nrt + 2) ? s_tile[slot] : -1;
+    const int64_t x = x0 < 0 ? -1 : x0 + r % kTile;
     return x >= 0 && x < p.pool_rows ? x : -1;
   };
   auto kaddr = [&](uint8_t* pool, int64_t row, int c) {   // 16-byte K chunk c of a pool row

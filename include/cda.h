@@ -114,6 +114,7 @@ extern "C" {
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
 #define CDA_MAX_CHUNK 64        /* largest chunk of chunk_attn_compact */
+#define CDA_MAX_CHUNK_WINDOW 4096   /* largest W chunk_attn_compact takes */
 
 /* Return codes of every call. */
 enum cda_status {
@@ -323,8 +324,9 @@ size_t cda_attn_workspace_bytes(const cda_kv_cache *cache, int32_t Hq, int32_t s
  *              any contents (the chunk's encoded rows and the partial states)
  * Every sequence of a contiguous store takes part; with a paged store, idle
  * sequences (pos < 0) give out = 0, lse = -inf and are not appended to.
- * Errors as for kv_compact and decode_attn_compact; the compact region must
- * have room for the chunk (CDA_DEVERR_CAPACITY otherwise, as for APPEND).
+ * Errors as for kv_compact and decode_attn_compact; W above
+ * CDA_MAX_CHUNK_WINDOW is CDA_ERR_UNSUPPORTED; the compact region must have
+ * room for the chunk (CDA_DEVERR_CAPACITY otherwise, as for APPEND).
  */
 int32_t chunk_attn_compact(const cda_kv_cache *cache, const cda_compact_args *args, int32_t M,
                            const void *q, int32_t Hq, float sm_scale, void *out,

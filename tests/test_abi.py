@@ -256,5 +256,8 @@ def test_chunk_validation(lib):
     assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws, need, None) == 1     # stride
     a.stride_t, a.op = 128, lib.CDA_OP_PACK
     assert f(C.byref(c), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws, need, None) == 1     # not APPEND
+    c2 = _cache(lib, W=lib.CDA_MAX_CHUNK_WINDOW + 1)
+    assert f(C.byref(c2), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws,
+             L.cda_chunk_workspace_bytes(C.byref(c2), 8, 4), None) == 2                 # W too large
     # the workspace grows with the chunk
     assert L.cda_chunk_workspace_bytes(C.byref(c), 8, 64) > need
