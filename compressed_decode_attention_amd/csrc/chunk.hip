@@ -696,18 +696,26 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 #pragma unroll
       for (int bb = 0; bb < BPW; ++bb) {
         if (!blk_ok[bb]) continue;
+        // raw logits; masked ones -> -inf (a real branch: most tiles need none).
+        // The scale c1 > 0 goes into the max and the exponent, not each logit.
         float z[4][4];
-        float tmax = -INFINITY;
-        const bool all_vis = __ballot(vis[bb] != 0xFFFFu) == 0;   // wave-uniform
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[m][r] = sc[bb][m][r] * c1;
-            if (!all_vis && !((vis[bb] >> (4 * m + r)) & 1u)) z[m][r] = -INFINITY;
-            tmax = fmaxf(tmax, z[m][r]);
-          }
-        tmax = max_xor32(max_xor16(tmax));
+          for (int r = 0; r < 4; ++r) z[m][r] = sc[bb][m][r];
+        if (__ballot(vis[bb] != 0xFFFFu) != 0) {   // wave-uniform
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (!((vis[bb] >> (4 * m + r)) & 1u)) z[m][r] = -INFINITY;
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, z[m][r]);
+        tmax = max_xor32(max_xor16(tmax)) * c1;
         const float m_new = fmaxf(m_run[bb], tmax);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         if (!first_tile) {
@@ -723,7 +731,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
+            z[m][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[m][r], c1, -m_use));
             psum += z[m][r];
           }
         l_run[bb] += psum;
