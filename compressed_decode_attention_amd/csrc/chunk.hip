@@ -94,14 +94,26 @@ __global__ __launch_bounds__(kBlock) void chunk_encode_kernel(ChunkParams p) {
   if (h == 0 && tid == 0) p.seqcnt[b] = 0;   // the commit's counter of sequence b
   const float kinv = Q ? kv_inv_scale<KV>(p.k_amax[i]) : 1.0f;
   const float vinv = Q ? kv_inv_scale<KV>(p.v_amax[i]) : 1.0f;
-  for (int e = tid; e < kTile * CPR; e += kBlock) {
+  // every pass's input first (unconditional loads of a clamped row, zeroed
+  // past M), then the encoding
+  constexpr int EPT = kTile * CPR / kBlock;
+  static_assert(kTile * CPR % kBlock == 0, "encode shape");
+  u32x4 kin[EPT], vin[EPT];
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = u * kBlock + tid, r = e / CPR, d0 = 8 * (e - r * CPR);
+    const int64_t off =
+        (int64_t)b * p.nsb + (int64_t)min(r, p.M - 1) * p.nst + (int64_t)h * p.nsh + d0;
+    kin[u] = *reinterpret_cast<const u32x4*>(p.k_new + off);
+    vin[u] = *reinterpret_cast<const u32x4*>(p.v_new + off);
+  }
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int e = u * kBlock + tid;
     const int r = e / CPR, c = e - r * CPR, d0 = 8 * c;
-    u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
-    if (r < p.M) {
-      const int64_t off = (int64_t)b * p.nsb + (int64_t)r * p.nst + (int64_t)h * p.nsh + d0;
-      kx = *reinterpret_cast<const u32x4*>(p.k_new + off);
-      vx = *reinterpret_cast<const u32x4*>(p.v_new + off);
-    }
+    const bool live = r < p.M;
+    const u32x4 kx = live ? kin[u] : u32x4{0, 0, 0, 0};
+    const u32x4 vx = live ? vin[u] : u32x4{0, 0, 0, 0};
     if (KV == kKvFP4) {
       uint32_t kc = 0;
 #pragma unroll
@@ -796,9 +808,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 // among the kept leaving tokens) while there is room (the rest are dropped
 // with CDA_DEVERR_CAPACITY).  Its bytes are those of old ring row lp mod W
 // (lp < P) or of chunk row lp - P (encoded in the workspace tile).  Ring row
-// r then takes the last chunk token that maps to it.  Every source row is
-// first copied into LDS (all loads in flight together, every old ring row
-// read before any is overwritten), then written out.  FP4 V elements share
+// r then takes the last chunk token that maps to it.  All reads come first,
+// issued together: the chunk's encoded tile whole (16-byte copies) and the
+// moved rows (a lane per row for V), into LDS, so every old ring row is read
+// before any is overwritten.  The writes go a lane per row, so that a wave's
+// V stores fall in one column run of a [d][row] tile.  FP4 V elements share
 // a byte between two rows: each byte is written by one thread, keeping the
 // nibble of a row it does not write; the compact and the ring writes go in
 // two rounds because rows W - 1 and W can share a byte.  The last segment of
@@ -812,13 +826,19 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
   constexpr int KC = RB / 16;                  // 16-byte K chunks per row
   constexpr bool FP4 = KV == kKvFP4;
   constexpr int E = KV == kKvBF16 ? 2 : 1;     // bytes per V element (FP4: one code per LDS byte)
+  constexpr int NWV = kBlock / 64;             // waves
+  constexpr int TCH = kTile * RB / 16;         // 16-byte chunks of one stored tile
+  constexpr int TPT = TCH / kBlock;            // chunk tile copy (K, and V), per thread
+  static_assert(TCH % kBlock == 0, "tile copy shape");
+  constexpr int MPT = (kTile * KC + kBlock - 1) / kBlock;     // moved K chunks, per thread
+  constexpr int DPW = D / NWV;                 // V columns per wave
+  static_assert(D % NWV == 0, "V columns per wave");
   __shared__ int s_src[kTile];                 // k-th moved token: ring row -1 - r, or chunk row
   __shared__ int s_nmove, s_full;
   __shared__ __attribute__((aligned(16))) uint8_t s_mk[kTile * RB];   // moved rows, K
-  __shared__ __attribute__((aligned(16))) uint8_t s_rk[kTile * RB];   // new ring rows, K
-  __shared__ __attribute__((aligned(16))) uint8_t s_mv[D * kTile * E];   // [d][row]
-  __shared__ __attribute__((aligned(16))) uint8_t s_rv[D * kTile * E];
-  const int i = blockIdx.x, tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint8_t s_mv[D * kTile * E];   // moved rows, V [d][row]
+  __shared__ __attribute__((aligned(16))) uint8_t s_ct[2 * kTile * RB];  // the chunk tile, K then V
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
   const int P = pos[b];
   if (P < 0) return;                           // idle (paged store): every segment of b
@@ -827,6 +847,8 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
   const int cl0 = min(max(comp_len[i], 0), cap);
   const uint8_t* ck = p.chunk_k + (int64_t)i * kTile * RB;   // the chunk's encoded rows
   const uint8_t* cv = p.chunk_v + (int64_t)i * kTile * RB;
+  const uint8_t* s_ck = s_ct;
+  const uint8_t* s_cv = s_ct + kTile * RB;
   // The rows this commit touches lie in the ring tiles [0, nrt) and the two
   // tiles from the first compact row written on.  Their pool rows are looked
   // up once here: inside the copy loops a load of the page table (or of
@@ -858,8 +880,11 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
     return FP4 ? pool + (row - row % kTile) * RB + d * (kTile / 2) + (row % kTile) / 2
                : pool + ((row - row % kTile) * D + d * kTile + row % kTile) * E;
   };
-  auto cnib = [&](int j, int d) -> uint32_t {            // FP4 code of chunk row j, column d
-    return (cv[d * (kTile / 2) + j / 2] >> (4 * (j & 1))) & 15u;
+  // V element (row j, column d) of the chunk tile in LDS (FP4: its code)
+  auto cvel = [&](int j, int d) -> uint32_t {
+    if (FP4) return ((uint32_t)s_cv[d * (kTile / 2) + j / 2] >> (4 * (j & 1))) & 15u;
+    if (E == 2) return *reinterpret_cast<const uint16_t*>(s_cv + (d * kTile + j) * 2);
+    return s_cv[d * kTile + j];
   };
 
   // 1. the tokens that move, ranked (one wave: M <= 64)
@@ -895,51 +920,78 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
   const int rs = W > 0 ? (P + j0) % W : 0;              // ring row of chunk token j0
   int bad = 0;
 
-  // 2. every source row into LDS
-  for (int e = tid; e < nmove * KC; e += kBlock) {
+  // 2. every source into registers, then LDS.  Lane `lane` of each wave owns
+  // moved row k = lane for V, over the wave's DPW columns.
+  u32x4 tck[TPT], tcv[TPT], mk[MPT];
+  uint32_t mv[DPW];
+  const bool vrow = lane < nmove;
+  int64_t vfrom = -1;
+  int vsrc = 0;
+  if (vrow) {
+    vsrc = min(s_src[lane], kTile - 1);
+    if (vsrc < 0) {
+      vfrom = prow(-1 - vsrc);
+      if (vfrom < 0) bad = 1;
+    }
+  }
+  // (loads are unconditional, from a valid address, and zeroed after where
+  // not wanted: a load under a branch would be waited for at the join)
+  if (nr > 0) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      tck[u] = *reinterpret_cast<const u32x4*>(ck + 16 * (u * kBlock + tid));
+      tcv[u] = *reinterpret_cast<const u32x4*>(cv + 16 * (u * kBlock + tid));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < MPT; ++u) {
+    // s_src holds only nmove entries: the others are not read
+    const bool in = u * kBlock + tid < nmove * KC;
+    const int e = in ? u * kBlock + tid : 0;
     const int k = e / KC, c = e - k * KC;
-    const int src = s_src[k];
-    u32x4 x = u32x4{0, 0, 0, 0};
-    if (src < 0) {
-      const int64_t from = prow(-1 - src);
-      if (from >= 0) x = *reinterpret_cast<const u32x4*>(kaddr(k_pool, from, c));
-      else bad = 1;
-    } else {
-      x = *reinterpret_cast<const u32x4*>(ck + k_chunk_offset(src, c, RB));
+    const int src = in ? s_src[k] : 0;
+    const int64_t from = src < 0 ? prow(-1 - src) : -1;
+    const bool want = in && (src >= 0 || from >= 0);
+    const uint8_t* a = (src < 0 && from >= 0) ? kaddr(k_pool, from, c)
+                                              : ck + k_chunk_offset(min(max(src, 0), kTile - 1), c, RB);
+    mk[u] = *reinterpret_cast<const u32x4*>(a);
+    if (!want) mk[u] = u32x4{0, 0, 0, 0};
+  }
+  if (nmove > 0) {
+    // this lane's row: column d at va + d * VS (FP4: the code at bit vsh)
+    constexpr int VS = FP4 ? kTile / 2 : kTile * E;
+    const bool vok = vrow && (vsrc >= 0 || vfrom >= 0);
+    const int vr = vsrc >= 0 ? vsrc : (int)(max(vfrom, (int64_t)0) % kTile);
+    const uint8_t* va = (vrow && vsrc < 0 && vfrom >= 0) ? vaddr(v_pool, vfrom, 0)
+                                                         : cv + (FP4 ? vr / 2 : vr * E);
+    const int vsh = FP4 ? 4 * (vr & 1) : 0;
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const uint8_t* a = va + (wave * DPW + u) * VS;
+      uint32_t x = E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(a) : (uint32_t)*a;
+      if (FP4) x = (x >> vsh) & 15u;
+      mv[u] = vok ? x : 0u;
     }
-    *reinterpret_cast<u32x4*>(s_mk + k * RB + 16 * c) = x;
   }
-  for (int e = tid; e < nmove * D; e += kBlock) {
-    const int k = e / D, d = e - k * D;
-    const int src = s_src[k];
-    uint32_t x = 0;
-    if (src < 0) {
-      const int64_t from = prow(-1 - src);
-      if (from >= 0) {
-        const uint8_t* a = vaddr(v_pool, from, d);
-        x = FP4 ? ((uint32_t)*a >> (4 * (from & 1))) & 15u
-                : (E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(a) : (uint32_t)*a);
-      }
-    } else {
-      x = FP4 ? cnib(src, d)
-              : (E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(cv + (d * kTile + src) * E)
-                        : (uint32_t)cv[d * kTile + src]);
+  if (nr > 0) {
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      *reinterpret_cast<u32x4*>(s_ct + 16 * (u * kBlock + tid)) = tck[u];
+      *reinterpret_cast<u32x4*>(s_ct + kTile * RB + 16 * (u * kBlock + tid)) = tcv[u];
     }
-    if (E == 2) *reinterpret_cast<uint16_t*>(s_mv + (d * kTile + k) * 2) = (uint16_t)x;
-    else s_mv[d * kTile + k] = (uint8_t)x;
   }
-  for (int e = tid; e < nr * KC; e += kBlock) {
-    const int j = e / KC, c = e - j * KC;
-    *reinterpret_cast<u32x4*>(s_rk + j * RB + 16 * c) =
-        *reinterpret_cast<const u32x4*>(ck + k_chunk_offset(j0 + j, c, RB));
+#pragma unroll
+  for (int u = 0; u < MPT; ++u) {
+    const int e = u * kBlock + tid;
+    if (e < nmove * KC) *reinterpret_cast<u32x4*>(s_mk + 16 * e) = mk[u];   // row e / KC, chunk e % KC
   }
-  for (int e = tid; e < nr * D; e += kBlock) {
-    const int j = e / D, d = e - j * D;
-    if (FP4) s_rv[d * kTile + j] = (uint8_t)cnib(j0 + j, d);
-    else if (E == 2)
-      *reinterpret_cast<uint16_t*>(s_rv + (d * kTile + j) * 2) =
-          *reinterpret_cast<const uint16_t*>(cv + (d * kTile + j0 + j) * 2);
-    else s_rv[d * kTile + j] = cv[d * kTile + j0 + j];
+  if (nmove > 0 && vrow) {
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int d = wave * DPW + u;
+      if (E == 2) *reinterpret_cast<uint16_t*>(s_mv + (d * kTile + lane) * 2) = (uint16_t)mv[u];
+      else s_mv[d * kTile + lane] = (uint8_t)mv[u];
+    }
   }
   __syncthreads();   // every old ring row has been read
 
@@ -952,26 +1004,39 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
     *reinterpret_cast<u32x4*>(kaddr(k_pool, to, c)) = *reinterpret_cast<const u32x4*>(s_mk + k * RB + 16 * c);
   }
   if (FP4) {
+    // byte q0 + lane (rows 2q, 2q + 1), one per lane
     const int q0 = R0 / 2, nq = nmove > 0 ? (R1 - 1) / 2 - q0 + 1 : 0;
-    for (int e = tid; e < nq * D; e += kBlock) {
-      const int q = q0 + e / D, d = e - (e / D) * D;
+    if (lane < nq) {
+      const int q = q0 + lane;
       const int64_t base = prow(2 * q);        // both rows of a byte share a page
-      if (base < 0) { bad = 1; continue; }
-      uint8_t* dst = vaddr(v_pool, base, d);
       const bool lo_in = 2 * q >= R0, hi_in = 2 * q + 1 < R1;
-      uint32_t byte = (lo_in && hi_in) ? 0u : *dst;
-      if (lo_in) byte = (byte & 0xF0u) | s_mv[d * kTile + (2 * q - R0)];
-      if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_mv[d * kTile + (2 * q + 1 - R0)] << 4);
-      *dst = (uint8_t)byte;
+      if (base < 0) {
+        bad = 1;
+      } else {
+        uint32_t old[DPW];   // the bytes first, all loads together
+#pragma unroll
+        for (int u = 0; u < DPW; ++u) old[u] = *vaddr(v_pool, base, wave * DPW + u);
+#pragma unroll
+        for (int u = 0; u < DPW; ++u) {
+          const int d = wave * DPW + u;
+          uint32_t byte = (lo_in && hi_in) ? 0u : old[u];
+          if (lo_in) byte = (byte & 0xF0u) | s_mv[d * kTile + (2 * q - R0)];
+          if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_mv[d * kTile + (2 * q + 1 - R0)] << 4);
+          *vaddr(v_pool, base, d) = (uint8_t)byte;
+        }
+      }
     }
-  } else {
-    for (int e = tid; e < nmove * D; e += kBlock) {
-      const int k = e / D, d = e - k * D;
-      const int64_t to = prow(R0 + k);
-      if (to < 0) { bad = 1; continue; }
-      uint8_t* dp = vaddr(v_pool, to, d);
-      if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + k) * 2);
-      else *dp = s_mv[d * kTile + k];
+  } else if (vrow) {
+    const int64_t to = prow(R0 + lane);
+    if (to < 0) {
+      bad = 1;
+    } else {
+      for (int u = 0; u < DPW; ++u) {
+        const int d = wave * DPW + u;
+        uint8_t* dp = vaddr(v_pool, to, d);
+        if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + lane) * 2);
+        else *dp = s_mv[d * kTile + lane];
+      }
     }
   }
   __syncthreads();   // rows W - 1 and W may share an FP4 byte
@@ -982,31 +1047,49 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
       const int j = e / KC, c = e - j * KC;
       const int64_t to = prow((P + j0 + j) % W);
       if (to < 0) { bad = 1; continue; }
-      *reinterpret_cast<u32x4*>(kaddr(k_pool, to, c)) = *reinterpret_cast<const u32x4*>(s_rk + j * RB + 16 * c);
+      *reinterpret_cast<u32x4*>(kaddr(k_pool, to, c)) =
+          *reinterpret_cast<const u32x4*>(s_ck + k_chunk_offset(j0 + j, c, RB));
     }
     if (FP4) {
-      for (int e = tid; e < ((W + 1) / 2) * D; e += kBlock) {
-        const int q = e / D, d = e - q * D;
-        // ring row r holds chunk token j0 + off, off = (r - rs) mod W, when off < nr
+      // ring row r holds chunk token j0 + off, off = (r - rs) mod W, when
+      // off < nr: rows [rs, rs + n1) and [0, nr - n1).  The bytes of the
+      // second run come first; the first run's first byte is skipped when the
+      // second run already ends in it (odd rs, nr = W).
+      const int n1 = min(nr, W - rs), n2 = nr - n1;
+      const int nq2 = n2 > 0 ? (n2 - 1) / 2 + 1 : 0;
+      int qa = rs / 2;
+      if (nq2 > 0 && (n2 - 1) / 2 == qa) ++qa;
+      const int nq1 = (rs + n1 - 1) / 2 - qa + 1;
+      for (int x = lane; x < nq2 + nq1; x += 64) {
+        const int q = x < nq2 ? x : qa + (x - nq2);
         const int off0 = (2 * q - rs + W) % W, off1 = (2 * q + 1 - rs + W) % W;
         const bool lo_in = off0 < nr, hi_in = 2 * q + 1 < W && off1 < nr;
         if (!lo_in && !hi_in) continue;
         const int64_t base = prow(2 * q);
         if (base < 0) { bad = 1; continue; }
-        uint8_t* dst = vaddr(v_pool, base, d);
-        uint32_t byte = (lo_in && hi_in) ? 0u : *dst;
-        if (lo_in) byte = (byte & 0xF0u) | s_rv[d * kTile + off0];
-        if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_rv[d * kTile + off1] << 4);
-        *dst = (uint8_t)byte;
+        uint32_t old[DPW];   // the bytes first, all loads together
+#pragma unroll
+        for (int u = 0; u < DPW; ++u) old[u] = *vaddr(v_pool, base, wave * DPW + u);
+#pragma unroll
+        for (int u = 0; u < DPW; ++u) {
+          const int d = wave * DPW + u;
+          uint32_t byte = (lo_in && hi_in) ? 0u : old[u];
+          if (lo_in) byte = (byte & 0xF0u) | cvel(j0 + off0, d);
+          if (hi_in) byte = (byte & 0x0Fu) | (cvel(j0 + off1, d) << 4);
+          *vaddr(v_pool, base, d) = (uint8_t)byte;
+        }
       }
-    } else {
-      for (int e = tid; e < nr * D; e += kBlock) {
-        const int j = e / D, d = e - j * D;
-        const int64_t to = prow((P + j0 + j) % W);
-        if (to < 0) { bad = 1; continue; }
-        uint8_t* dp = vaddr(v_pool, to, d);
-        if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_rv + (d * kTile + j) * 2);
-        else *dp = s_rv[d * kTile + j];
+    } else if (lane < nr) {
+      const int64_t to = prow((P + j0 + lane) % W);
+      if (to < 0) {
+        bad = 1;
+      } else {
+        for (int u = 0; u < DPW; ++u) {
+          const int d = wave * DPW + u;
+          uint8_t* dp = vaddr(v_pool, to, d);
+          if (E == 2) *reinterpret_cast<uint16_t*>(dp) = (uint16_t)cvel(j0 + lane, d);
+          else *dp = (uint8_t)cvel(j0 + lane, d);
+        }
       }
     }
     for (int j = tid; j < nr; j += kBlock)
