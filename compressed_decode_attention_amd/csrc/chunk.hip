@@ -1113,31 +1113,70 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
 // Workgroup (segment i, column block cb): the log-sum-exp merge of the SP
 // split states of each of its 16 columns (their o already carries the V
 // scale), normalised, into out and lse.
+// (nh NB workgroups of 4 waves leave about 4 waves per SIMD: the kernel may
+// use the registers of that occupancy to keep every load in flight)
 template <int D>
-__global__ __launch_bounds__(kBlock) void chunk_merge_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void chunk_merge_kernel(ChunkParams p) {
+  // each thread merges IPT items (4 consecutive outputs of one column); the
+  // (m, l) and o loads of kMB splits of every item go out together, merged
+  // online (a batch's max, then the running sums rescaled to it)
+  constexpr int IPT = 16 * (D / 4) / kBlock, kMB = 4;
+  static_assert(16 * (D / 4) % kBlock == 0, "merge items per thread");
   const int i = blockIdx.x / p.NB, cb = blockIdx.x - i * p.NB;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
   const int64_t slot0 = ((int64_t)i * p.NB + cb) * p.SP;
-  for (int e = threadIdx.x; e < 16 * (D / 4); e += kBlock) {
-    const int c = e / (D / 4), d4 = e - c * (D / 4);
-    const int col = cb * 16 + c, tq = col / p.G, hq = col - tq * p.G;
-    if (tq >= p.M) continue;
-    float Mx = -INFINITY;
-    for (int s = 0; s < p.SP; ++s) Mx = fmaxf(Mx, p.part_ml[((slot0 + s) * 16 + c) * 2]);
-    f32x4 O = f32x4{0, 0, 0, 0};
-    float L = 0.0f;
-    if (Mx != -INFINITY) {
-      for (int s = 0; s < p.SP; ++s) {
-        const int64_t sl = (slot0 + s) * 16 + c;
-        const float ms = p.part_ml[sl * 2];
-        if (ms == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(ms - Mx);
-        O += f * *reinterpret_cast<const f32x4*>(p.part_o + sl * D + 4 * d4);
-        L += f * p.part_ml[sl * 2 + 1];
+  float Mx[IPT], L[IPT];
+  f32x4 O[IPT];
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    Mx[it] = -INFINITY;
+    L[it] = 0.0f;
+    O[it] = f32x4{0, 0, 0, 0};
+  }
+  for (int k0 = 0; k0 < p.SP; k0 += kMB) {
+    float2 ml[IPT][kMB];
+    f32x4 ov[IPT][kMB];
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      const int e = it * kBlock + threadIdx.x, c = e / (D / 4), d4 = e - c * (D / 4);
+#pragma unroll
+      for (int j = 0; j < kMB; ++j) {   // unconditional loads, clamped split
+        const int64_t sl = (slot0 + min(k0 + j, p.SP - 1)) * 16 + c;
+        ml[it][j] = *reinterpret_cast<const float2*>(p.part_ml + sl * 2);
+        ov[it][j] = *reinterpret_cast<const f32x4*>(p.part_o + sl * D + 4 * d4);
       }
     }
+#pragma unroll
+    for (int it = 0; it < IPT; ++it) {
+      float Mb = Mx[it];
+#pragma unroll
+      for (int j = 0; j < kMB; ++j) {
+        if (k0 + j >= p.SP) ml[it][j].x = -INFINITY;
+        Mb = fmaxf(Mb, ml[it][j].x);
+      }
+      // branch-free (a branch here would let the compiler sink the loads
+      // behind it): with no state yet every weight is 0 and Mx stays -inf
+      const float Ms = Mb == -INFINITY ? 0.0f : Mb;
+      const float a = Mx[it] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(Mx[it] - Ms);
+      O[it] *= a;
+      L[it] *= a;
+#pragma unroll
+      for (int j = 0; j < kMB; ++j) {
+        const float f = ml[it][j].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[it][j].x - Ms);
+        O[it] += f * ov[it][j];
+        L[it] += f * ml[it][j].y;
+      }
+      Mx[it] = Mb;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int e = it * kBlock + threadIdx.x, c = e / (D / 4), d4 = e - c * (D / 4);
+    const int col = cb * 16 + c, tq = col / p.G, hq = col - tq * p.G;
+    if (tq >= p.M) continue;
     const int64_t row = ((int64_t)b * p.M + tq) * p.Hq + h * p.G + hq;
-    const f32x4 v = L > 0.0f ? O * (1.0f / L) : f32x4{0, 0, 0, 0};
+    const f32x4 v = L[it] > 0.0f ? O[it] * (1.0f / L[it]) : f32x4{0, 0, 0, 0};
     if (p.out_f32) {
       *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row * D + 4 * d4) = v;
     } else {
@@ -1145,7 +1184,7 @@ __global__ __launch_bounds__(kBlock) void chunk_merge_kernel(ChunkParams p) {
       const uint32_t hi = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
       *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row * D + 4 * d4) = u32x2{lo, hi};
     }
-    if (d4 == 0 && p.lse) p.lse[row] = L > 0.0f ? (Mx + log2f(L)) * kLn2 : -INFINITY;
+    if (d4 == 0 && p.lse) p.lse[row] = L[it] > 0.0f ? (Mx[it] + log2f(L[it])) * kLn2 : -INFINITY;
   }
 }
 
