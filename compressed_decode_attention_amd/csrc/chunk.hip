@@ -69,10 +69,13 @@ struct ChunkParams {
   const uint8_t* keep_new;     // [B, M, Hkv]
   uint8_t* chunk_k;            // workspace: [nh] tiles in the K pool format
   uint8_t* chunk_v;            // workspace: [nh] tiles in the V pool format
-  float* part_o;               // workspace: [nh][NB][SP][16][D]
-  float* part_ml;              // workspace: [nh][NB][SP][16][2]
+  float* part_o;               // workspace: [slots][16][D]
+  float* part_ml;              // workspace: [slots][16][2]
+  // slots: narrow kernel [nh][NB][SP]; wide kernel [column group][Gw][16 blocks]
+  int32_t* plan;               // workspace: [nh][2] wide kernel: first workgroup, splits
   int32_t* seqcnt;             // workspace: [B] segments of the sequence committed
   int B, Hkv, Hq, G, M, W, nh, NB, SP, out_f32;
+  int Gw;                      // wide kernel: workgroups per column group (0: narrow)
   float sm_scale;
   int32_t* err;
 };
@@ -443,9 +446,13 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 
 // ---------------------------------------------------------------- attention, wide
 
-// For chunks with many columns (at least 4 blocks of 16): workgroup (segment,
-// split s, group of up to 16 column blocks), 16 waves.  The workgroup walks
-// the tiles s, s + SP, ... and the chunk tile together.  For each tile the
+// For chunks with many columns (at least 4 blocks of 16): workgroup (split
+// s of a segment, group of up to 16 column blocks), 16 waves, with splits
+// given out in proportion to the segments' tile counts (segment lengths
+// differ with their keep rates: equal splits per segment left workgroups
+// between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
+// kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
+// segment, the chunk tile among them.  For each tile the
 // waves stage it in LDS -- the next tile's bytes already in flight in
 // registers -- converting FP8/FP4 codes once, exactly, to the MFMA operand
 // types (K to bf16 in the order the q operand expects, V to a [d][row] f16
@@ -458,6 +465,19 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // SIMD ran 44 us against 39 us for this shape on the Qwen c = 8 layer.)
 constexpr int kWideWaves = 16, kWideBlocks = 1;  // waves, column blocks per wave
 constexpr int kWideGroup = kWideWaves * kWideBlocks;
+
+// Sum over the 64 lanes of a wave, in every lane: DPP within rows of 16
+// (quad swaps, then rotations by 4 and 8), then the 16- and 32-lane swaps.
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);    // quad_perm [1, 0, 3, 2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);    // quad_perm [2, 3, 0, 1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false);   // row_ror:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);   // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)(r[0] + r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)(r[0] + r[1]);
+}
 
 // Bits of rows [a, b] (inclusive) among the 16 rows base .. base + 15.
 __device__ __forceinline__ uint32_t range_bits(int a, int b, int base) {
@@ -488,26 +508,111 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 15, kg = lane >> 4;
   const int NCG = (p.NB + kWideGroup - 1) / kWideGroup;
-  int work = blockIdx.x >> 3;
-  const int s = work % p.SP;
-  work /= p.SP;
-  const int cgi = work % NCG;
-  const int i = (blockIdx.x & 7) + 8 * (work / NCG);
-  if (i >= p.nh) return;                          // the whole workgroup
-  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int cgi = blockIdx.x % NCG, w = blockIdx.x / NCG;
   const int W = p.W, G = p.G, M = p.M;
 
-  const int Praw = p.pos[b];
+  // ---- the plan.  Segment j has nt_j tiles to attend (its stored tiles and
+  // the chunk tile; none when idle) and gets SP_j = ceil(nt_j / t) of the Gw
+  // workgroups of each column group, t the least tile count per workgroup
+  // for which they fit (ceil(total / (Gw - nh)) always does; the 8 counts
+  // from ceil(total / Gw) up, below which none can, are tried together);
+  // workgroup w takes split w - PS_j of the segment j with PS_j <= w <
+  // PS_j + SP_j.  Every wave computes the same plan on its own, lane l
+  // taking segments l, l + 64, ... (cross-lane sums and a scan; no LDS, no
+  // barrier), and takes its segment's metadata from the lane that loaded it.
+  auto seg_meta = [&](int j, int& P_, int& cl_, int& nt_) {
+    P_ = p.pos[j / p.Hkv];
+    const int cap_ = max(p.seg_cap[j], 0);
+    cl_ = min(max(p.comp_len[j], 0), cap_);
+    nt_ = P_ < 0 ? 0 : (min(W, P_) + cl_ + kTile - 1) / kTile + 1;
+  };
+  const int j0 = min(lane, p.nh - 1);   // segment `lane` (of the first 64)
+  int P0, cl0, nt0;
+  seg_meta(j0, P0, cl0, nt0);
+  if (lane >= p.nh) nt0 = 0;
+  const int64_t sb0 = PG ? 0 : p.seg_base[j0];
+  const float ka0 = Q ? p.k_amax[j0] : 1.0f;
+  const float va0 = Q ? p.v_amax[j0] : 1.0f;
+  auto tiles_of = [&](int j) {
+    if (j < 64) return nt0;
+    int a, c, e;
+    seg_meta(j, a, c, e);
+    return e;
+  };
+  int total = 0;
+  for (int j = lane; j < p.nh; j += 64) total += tiles_of(j);
+  total = wave_sum_i(total);
+  const int room = max(p.Gw - p.nh, 1);
+  int tpw = max(1, (total + room - 1) / room);          // fits
+  const int t_lo = max(1, (total + p.Gw - 1) / p.Gw);   // smaller cannot
+  if (t_lo < tpw) {   // the splits for t_lo .. t_lo + 7 together; the least that fits
+    constexpr int NCAND = 8;
+    int c[NCAND];
+#pragma unroll
+    for (int k = 0; k < NCAND; ++k) c[k] = 0;
+    for (int j = lane; j < p.nh; j += 64) {
+      const int nt = tiles_of(j);
+#pragma unroll
+      for (int k = 0; k < NCAND; ++k) c[k] += (nt + t_lo + k - 1) / (t_lo + k);
+    }
+    int best = tpw;
+#pragma unroll
+    for (int k = NCAND - 1; k >= 0; --k)
+      if (t_lo + k < tpw && wave_sum_i(c[k]) <= p.Gw) best = t_lo + k;
+    tpw = best;
+  }
+  int i = -1, s = 0, SPi = 0, Praw = -1, cl = 0;
+  int64_t sb = 0;
+  float ka = 1.0f, va = 1.0f;
+  {
+    int base = 0;   // splits of the segments before this chunk of 64
+    for (int c0 = 0; c0 < p.nh; c0 += 64) {
+      const int j = c0 + lane;
+      const int sp = j < p.nh ? (tiles_of(j) + tpw - 1) / tpw : 0;
+      int x = sp;   // inclusive scan over the wave
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      const int ps = base + x - sp;   // PS_j
+      if (j < p.nh && w == 0 && cgi == 0 && wave == 0) {
+        p.plan[2 * j] = ps;
+        p.plan[2 * j + 1] = sp;
+      }
+      const uint64_t hit = __ballot(j < p.nh && w >= ps && w < ps + sp);
+      if (hit != 0 && i < 0) {
+        const int src = __builtin_ctzll(hit);   // wave-uniform
+        i = __builtin_amdgcn_readlane(j, src);
+        s = w - __builtin_amdgcn_readlane(ps, src);
+        SPi = __builtin_amdgcn_readlane(sp, src);
+        if (c0 == 0) {
+          Praw = __builtin_amdgcn_readlane(P0, src);
+          cl = __builtin_amdgcn_readlane(cl0, src);
+          sb = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)sb0, src) |
+               ((int64_t)__builtin_amdgcn_readlane((int)(sb0 >> 32), src) << 32);
+          ka = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ka0), src));
+          va = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va0), src));
+        } else {
+          int nt_;
+          seg_meta(i, Praw, cl, nt_);
+          sb = PG ? 0 : p.seg_base[i];
+          ka = Q ? p.k_amax[i] : 1.0f;
+          va = Q ? p.v_amax[i] : 1.0f;
+        }
+      }
+      base += __builtin_amdgcn_readlane(x, 63);
+    }
+  }
+  if (i < 0) return;                              // the whole workgroup: no split left
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
   const bool idle = Praw < 0;
   const int P = max(Praw, 0);
-  const int cap = max(p.seg_cap[i], 0);
-  const int cl = min(max(p.comp_len[i], 0), cap);
   const int n = idle ? 0 : min(W, P) + cl;
   const int ntiles = (n + kTile - 1) / kTile;
   const int last = idle ? ntiles - 1 : ntiles;   // the chunk tile is tile ntiles
-  const int64_t sb = PG ? 0 : p.seg_base[i];
-  const float ks = Q ? kv_scale<KV>(p.k_amax[i]) : 1.0f;
-  const float vs = Q ? kv_scale<KV>(p.v_amax[i]) : 1.0f;
+  const float ks = Q ? kv_scale<KV>(ka) : 1.0f;
+  const float vs = Q ? kv_scale<KV>(va) : 1.0f;
   const float c1 = p.sm_scale * kLog2e * ks;
   const int pmw = W > 0 ? P % W : 0;
 
@@ -581,7 +686,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   uint32_t kbyte = 0;
   bool ok = true;
   if (s <= last) fetch(s, rg, kbyte, ok);
-  for (int tt = s; tt <= last; tt += p.SP) {
+  for (int tt = s; tt <= last; tt += SPi) {
 
     const bool ctile = tt == ntiles;
     const int r0 = tt * kTile;
@@ -651,7 +756,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     const bool tile_ok = ok;
     if (!tile_ok && tid == 0) atomicOr(p.err, CDA_DEVERR_POOL);
     __syncthreads();
-    if (tt + p.SP <= last) fetch(tt + p.SP, rg, kbyte, ok);
+    if (tt + SPi <= last) fetch(tt + SPi, rg, kbyte, ok);
 
     if (busy && tile_ok) {
       // ---- row masks of this lane's 16 rows (bit j: row 16 kg + j of the tile)
@@ -788,7 +893,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     const int cb = cb0 + bb;
     const float l = sum_xor32(sum_xor16(l_run[bb]));
     if (cb >= p.NB) continue;
-    const int64_t slot = ((int64_t)i * p.NB + cb) * p.SP + s;
+    const int64_t slot = ((int64_t)cgi * p.Gw + w) * kWideGroup + (cb - cgi * kWideGroup);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       *reinterpret_cast<f32x4*>(p.part_o + (slot * 16 + g) * D + 16 * nt + 4 * kg) = acc[bb][nt] * vs;
@@ -1121,11 +1226,19 @@ void chunk_merge_kernel(ChunkParams p) {
   // each thread merges IPT items (4 consecutive outputs of one column); the
   // (m, l) and o loads of kMB splits of every item go out together, merged
   // online (a batch's max, then the running sums rescaled to it)
-  constexpr int IPT = 16 * (D / 4) / kBlock, kMB = 4;
+  constexpr int IPT = 16 * (D / 4) / kBlock, kMB = 8;
   static_assert(16 * (D / 4) % kBlock == 0, "merge items per thread");
   const int i = blockIdx.x / p.NB, cb = blockIdx.x - i * p.NB;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
-  const int64_t slot0 = ((int64_t)i * p.NB + cb) * p.SP;
+  // the segment's splits: wide kernel, from its plan (slots of consecutive
+  // workgroups); narrow kernel, SP slots of its own
+  const bool wide = p.Gw > 0;
+  const int first = wide ? min(max(p.plan[2 * i], 0), p.Gw) : 0;   // (within the slots)
+  const int nsp = wide ? min(max(p.plan[2 * i + 1], 0), p.Gw - first) : p.SP;
+  const int64_t slot0 = wide ? ((int64_t)(cb / kWideGroup) * p.Gw + first) * kWideGroup +
+                                   cb % kWideGroup
+                             : ((int64_t)i * p.NB + cb) * p.SP;
+  const int64_t sstep = wide ? kWideGroup : 1;   // slot stride between splits
   float Mx[IPT], L[IPT];
   f32x4 O[IPT];
 #pragma unroll
@@ -1134,7 +1247,7 @@ void chunk_merge_kernel(ChunkParams p) {
     L[it] = 0.0f;
     O[it] = f32x4{0, 0, 0, 0};
   }
-  for (int k0 = 0; k0 < p.SP; k0 += kMB) {
+  for (int k0 = 0; k0 < nsp; k0 += kMB) {
     float2 ml[IPT][kMB];
     f32x4 ov[IPT][kMB];
 #pragma unroll
@@ -1142,7 +1255,7 @@ void chunk_merge_kernel(ChunkParams p) {
       const int e = it * kBlock + threadIdx.x, c = e / (D / 4), d4 = e - c * (D / 4);
 #pragma unroll
       for (int j = 0; j < kMB; ++j) {   // unconditional loads, clamped split
-        const int64_t sl = (slot0 + min(k0 + j, p.SP - 1)) * 16 + c;
+        const int64_t sl = (slot0 + min(k0 + j, nsp - 1) * sstep) * 16 + c;
         ml[it][j] = *reinterpret_cast<const float2*>(p.part_ml + sl * 2);
         ov[it][j] = *reinterpret_cast<const f32x4*>(p.part_o + sl * D + 4 * d4);
       }
@@ -1152,7 +1265,7 @@ void chunk_merge_kernel(ChunkParams p) {
       float Mb = Mx[it];
 #pragma unroll
       for (int j = 0; j < kMB; ++j) {
-        if (k0 + j >= p.SP) ml[it][j].x = -INFINITY;
+        if (k0 + j >= nsp) ml[it][j].x = -INFINITY;
         Mb = fmaxf(Mb, ml[it][j].x);
       }
       // branch-free (a branch here would let the compiler sink the loads
@@ -1191,18 +1304,26 @@ void chunk_merge_kernel(ChunkParams p) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Column blocks and splits of a chunk call: NB blocks of 16 (token, query
-// head) columns; splits so that the grid holds about kChunkTarget
-// workgroups (at most 16).
-// With at least 4 blocks the wide kernel runs (one 8-wave workgroup per
-// segment, split and group of 16 blocks; about one workgroup per CU), else
-// the narrow one (one workgroup per segment, block and split).
-void chunk_shape(int nh, int G, int M, int& NB, int& SP) {
+// head) columns.  With at least 4 blocks the wide kernel runs: Gw 16-wave
+// workgroups per group of 16 blocks (about one per CU in all, at least one
+// per segment), shared out among the segments by the kernel's own plan.
+// Else the narrow one: one workgroup per segment, block and split, with SP
+// splits so that the grid holds about kChunkTarget workgroups (at most 16).
+// Slots: the partial states the merge reads, 16 columns each.
+void chunk_shape(int nh, int G, int M, int& NB, int& SP, int& Gw, int64_t& slots) {
   NB = (G * M + 15) / 16;
   const bool wide = NB >= 4;
-  const int64_t per = (int64_t)std::max(nh, 1) *
-                      (wide ? (NB + kWideGroup - 1) / kWideGroup : NB);
-  const int64_t target = wide ? kWideTarget : kChunkTarget;
-  SP = (int)std::min<int64_t>(16, std::max<int64_t>(1, (target + per - 1) / per));
+  const int ncg = (NB + kWideGroup - 1) / kWideGroup;
+  if (wide) {
+    Gw = std::max((kWideTarget + ncg - 1) / ncg, nh);
+    SP = 0;
+    slots = (int64_t)ncg * Gw * kWideGroup;
+  } else {
+    Gw = 0;
+    const int64_t per = (int64_t)std::max(nh, 1) * NB;
+    SP = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kChunkTarget + per - 1) / per));
+    slots = (int64_t)nh * NB * SP;
+  }
 }
 
 template <bool PG>
@@ -1210,9 +1331,9 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
                           const ChunkParams& p, uint8_t* k_pool, uint8_t* v_pool,
                           int32_t* comp_len, uint8_t* ring_keep, int32_t* pos) {
   const int groups = (nh + 7) / 8;
-  const bool wide = NB >= 4;
+  const bool wide = p.Gw > 0;
   const int ncg = (NB + kWideGroup - 1) / kWideGroup;
-  const dim3 grid((unsigned)(8 * groups * NB * SP)), wgrid((unsigned)(8 * groups * ncg * SP));
+  const dim3 grid((unsigned)(8 * groups * NB * std::max(SP, 1))), wgrid((unsigned)(ncg * p.Gw));
 #define CDA_CHUNK(F, DD)                                                        \
   do {                                                                          \
     chunk_encode_kernel<F, DD><<<nh, kBlock, 0, s>>>(p);                        \
@@ -1236,15 +1357,17 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
 
 }  // namespace
 
-// Workspace: [chunk K tiles][chunk V tiles][commit counters][partial (m, l)][partial o].
+// Workspace: [chunk K tiles][chunk V tiles][commit counters][plan]
+// [partial (m, l)][partial o].
 size_t chunk_workspace_bytes(const cda_kv_cache& c, int G, int M) {
   const int nh = c.B * c.Hkv;
-  int NB, SP;
-  chunk_shape(nh, G, M, NB, SP);
+  int NB, SP, Gw;
+  int64_t slots;
+  chunk_shape(nh, G, M, NB, SP, Gw, slots);
   const size_t tile = (size_t)kTile * kv_row_bytes(c.kv_dtype, c.D);
-  const size_t cols = (size_t)nh * NB * SP * 16;
-  return 2 * align256((size_t)nh * tile) + align256((size_t)c.B * 4) + align256(cols * 2 * 4) +
-         align256(cols * c.D * 4);
+  const size_t cols = (size_t)slots * 16;
+  return 2 * align256((size_t)nh * tile) + align256((size_t)c.B * 4) +
+         align256((size_t)nh * 2 * 4) + align256(cols * 2 * 4) + align256(cols * c.D * 4);
 }
 
 hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M, const void* q,
@@ -1283,12 +1406,13 @@ hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M,
   p.M = M;
   p.W = c.W;
   p.nh = nh;
-  chunk_shape(nh, G, M, p.NB, p.SP);
+  int64_t slots;
+  chunk_shape(nh, G, M, p.NB, p.SP, p.Gw, slots);
   p.out_f32 = out_f32;
   p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c.D);
   p.err = c.err;
   const size_t tile = (size_t)kTile * kv_row_bytes(c.kv_dtype, c.D);
-  const size_t cols = (size_t)nh * p.NB * p.SP * 16;
+  const size_t cols = (size_t)slots * 16;
   char* ws = static_cast<char*>(workspace);
   p.chunk_k = reinterpret_cast<uint8_t*>(ws);
   ws += align256((size_t)nh * tile);
@@ -1296,6 +1420,8 @@ hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M,
   ws += align256((size_t)nh * tile);
   p.seqcnt = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)c.B * 4);
+  p.plan = reinterpret_cast<int32_t*>(ws);
+  ws += align256((size_t)nh * 2 * 4);
   p.part_ml = reinterpret_cast<float*>(ws);
   ws += align256(cols * 2 * 4);
   p.part_o = reinterpret_cast<float*>(ws);
