@@ -181,3 +181,27 @@ def test_chunk_past_the_capacity(kv):
     from compressed_decode_attention_amd import CDA_DEVERR_CAPACITY
     assert c.error_word() & CDA_DEVERR_CAPACITY
     assert int(o.err[0]) & CDA_DEVERR_CAPACITY
+
+
+@pytest.mark.parametrize("kv,B,Hkv", [
+    ("fp8", 40, 2),      # 80 segments: the wide kernel's plan takes two passes of 64
+    ("bf16", 130, 2),    # 260 segments: more than 256 workgroups, one split each
+])
+def test_chunk_many_segments(kv, B, Hkv):
+    """Chunks over more segments than one wave's lanes, and more than the
+    workgroups a chunk call starts by default, through the wide kernel."""
+    G, D, W, T, M = 4, 64, 16, 90, 16
+    cfg = workload.custom(B=B, Hq=G * Hkv, Hkv=Hkv, D=D, T=T, S=M + 1, W=W, kv_dtype=kv,
+                          keep_lo=0.05, keep_hi=0.9, seed=900 + B)
+    lay = workload.make_layer(cfg, 0)
+    log(f"chunk many segments {kv} B={B} Hkv={Hkv}")
+    c, _ = gpu_prefill(lay.k, lay.v, lay.keep, T, W, M + 1, kv, with_dst=False)
+    o = oracle_prefill(lay.k, lay.v, lay.keep, T, W, M + 1, kv)
+    d = dev()
+    k, v, keep, q = (x.to(d) for x in _chunk_inputs(lay, T, 0, M))
+    lse = torch.empty(B, M, G * Hkv, dtype=torch.float32, device=d)
+    out = c.chunk(k, v, keep, q, out_dtype=torch.float32, lse=lse)
+    _check_chunk(out, lse, lay, T, 0, M, W, kv, o, "chunk")
+    _oracle_append(o, lay, T, 0, M)
+    compare_state(c, o, "after the chunk")
+    assert c.error_word() == 0
