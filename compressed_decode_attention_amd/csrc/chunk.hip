@@ -39,6 +39,8 @@
 #include "cda_device.h"
 #include "cda_launch.h"
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));   // a 32x32 MFMA accumulator
+
 namespace cda {
 namespace {
 
@@ -447,23 +449,25 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // ---------------------------------------------------------------- attention, wide
 
 // For chunks with many columns (at least 4 blocks of 16): workgroup (split
-// s of a segment, group of up to 16 column blocks), 16 waves, with splits
+// s of a segment, group of up to 16 column blocks), 8 waves, with splits
 // given out in proportion to the segments' tile counts (segment lengths
 // differ with their keep rates: equal splits per segment left workgroups
 // between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
 // kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
-// segment, the chunk tile among them.  For each tile the
-// waves stage it in LDS -- the next tile's bytes already in flight in
-// registers -- converting FP8/FP4 codes once, exactly, to the MFMA operand
-// types (K to bf16 in the order the q operand expects, V to a [d][row] f16
-// image like a BF16 V tile), zeroing V rows past the data, and publishing
-// the rows' keep bits as one ballot.  Wave w owns column block w over every
-// tile.  Masks are 16-bit row masks per lane: rows past the data; ring rows
-// that left the query's window unkept (one circular interval of ring rows);
-// chunk tokens after the query or out of its window unkept.  (Two blocks
-// per wave with 8 waves read each operand once for both, but at 2 waves per
-// SIMD ran 44 us against 39 us for this shape on the Qwen c = 8 layer.)
-constexpr int kWideWaves = 16, kWideBlocks = 1;  // waves, column blocks per wave
+// segment, the chunk tile among them.  For each tile the waves stage it in
+// LDS -- the next tile's bytes already in flight in registers -- converting
+// FP8/FP4 codes once, exactly, to the MFMA operand types (K to bf16 operands
+// of the 32x32x16 products, its rows in the order that makes each lane's S
+// values its own P operand; V to a [d][row] f16 image like a BF16 V tile),
+// zeroing V rows past the data, and publishing the rows' keep bits as one
+// ballot.  Wave w owns 32 columns (blocks 2w and 2w + 1) over every tile:
+// each K and V operand read from LDS serves 32 columns (with 16x16 products
+// and 16 waves, 39 us against 32 us on that layer: the 512 KB of operand
+// reads per tile bounded it).  Masks: a 64-bit row mask per column (rows
+// past the data; ring rows that left the query's window unkept, one
+// circular interval; chunk tokens after the query or out of its window
+// unkept), of which each lane takes its 32 rows.
+constexpr int kWideWaves = 8, kWideBlocks = 2;   // waves, column blocks per wave
 constexpr int kWideGroup = kWideWaves * kWideBlocks;
 
 // Sum over the 64 lanes of a wave, in every lane: DPP within rows of 16
@@ -479,18 +483,22 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return (int)(r[0] + r[1]);
 }
 
-// Bits of rows [a, b] (inclusive) among the 16 rows base .. base + 15.
-__device__ __forceinline__ uint32_t range_bits(int a, int b, int base) {
-  const int lo = max(a - base, 0), hi = min(b - base, 15);
-  return lo > hi ? 0u : (((2u << hi) - 1u) & ~((1u << lo) - 1u));
+// Bits a .. b of a 64-bit row mask (none when a > b), a and b clamped to 0 .. 63.
+__device__ __forceinline__ uint64_t rows64(int a, int b) {
+  a = max(a, 0);
+  b = min(b, 63);
+  return a > b ? 0ull : ((~0ull >> (63 - b)) & (~0ull << a));
 }
+
+// Bits 2 and 3 of x exchanged (the K row order of the 32x32 S products).
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 template <int KV, int D, bool PG>
 __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkParams p) {
-  constexpr int NW = kWideWaves, BPW = kWideBlocks;
+  constexpr int NW = kWideWaves;
   constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
   constexpr int RB = kv_row_bytes(KV, D);
-  constexpr int NK = D / 32, NT = D / 16, KL = RB / 64;
+  constexpr int NKS = D / 16, ND = D / 32, KL = RB / 64;   // 32x32x16 k-steps, d blocks
   constexpr int TB = kTile * RB;                  // bytes of a stored K (or V) tile
   constexpr int NCH = 2 * TB / 16;                // 16-byte chunks of a stored K + V tile
   constexpr int CPT = (NCH + 64 * NW - 1) / (64 * NW);   // per thread
@@ -499,8 +507,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   constexpr int VP = kTile * 2 + 16;              // bytes per staged V column (padded)
   static_assert(NCH % 64 == 0, "tile copy shape");
 
-  // K as bf16 MFMA operands, operand-major: operand (m, st) of lane l at
-  // ((m * NK + st) * 64 + l) * 16; V as [d][row] 16-bit values, VP bytes a column
+  // K as bf16 MFMA operands, operand-major: operand (mu, st) of lane l at
+  // ((mu * NKS + st) * 64 + l) * 16 holds row 32 mu + swap23(l % 32), d
+  // 16 st + 8 (l / 32) .. + 7; V as [d][row] 16-bit values, VP bytes a column
   __shared__ __attribute__((aligned(16))) uint8_t s_k[TX];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[D * VP];
   __shared__ uint64_t s_keep;   // keep bits of the staged tile's rows
@@ -616,27 +625,22 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   const float c1 = p.sm_scale * kLog2e * ks;
   const int pmw = W > 0 ? P % W : 0;
 
-  // this wave's columns: blocks cb0 + bb, column cb * 16 + g -> (token, head)
-  const int cb0 = cgi * kWideGroup + wave * BPW;
-  int tq[BPW];
-  bool col_ok[BPW];   // per lane: the column is a query of the chunk
-  bool blk_ok[BPW];   // per wave: the block exists
-  bf16x8 qop[BPW][NK];
+  // this wave's 32 columns: blocks cb0 and cb0 + 1, column cb0 * 16 + cq
+  // -> (token, head); lanes l and l + 32 share column l % 32
+  const int hi = lane >> 5, cq = lane & 31;
+  const int cb0 = cgi * kWideGroup + wave * kWideBlocks;
+  const int col = cb0 * 16 + cq, tq = col / G;
+  const bool busy = cb0 < p.NB;                              // per wave
+  const bool col_ok = cb0 + (cq >> 4) < p.NB && tq < M;      // per lane
+  bf16x8 qop[NKS];
+  {
+    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + (col - tq * G))
+                                : ((int64_t)b * M * p.Hq + h * G);
+    const uint16_t* qr = p.q + qrow * D + 8 * hi;
 #pragma unroll
-  for (int bb = 0; bb < BPW; ++bb) {
-    const int col = (cb0 + bb) * 16 + g;
-    tq[bb] = col / G;
-    blk_ok[bb] = cb0 + bb < p.NB;
-    col_ok[bb] = blk_ok[bb] && tq[bb] < M;
-    const int hq = col - tq[bb] * G;
-    const int64_t qrow = col_ok[bb] ? ((int64_t)(b * M + tq[bb]) * p.Hq + h * G + hq)
-                                    : ((int64_t)b * M * p.Hq + h * G);
-    const uint16_t* qr = p.q + qrow * D;
-#pragma unroll
-    for (int st = 0; st < NK; ++st)
-      qop[bb][st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + q_d0<KV>(st, kg)));
+    for (int st = 0; st < NKS; ++st)
+      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * st));
   }
-  const bool busy = blk_ok[0];
 
   // stored bytes of tile tt (and its keep bytes) -> registers
   auto fetch = [&](int tt, u32x4 (&rg)[CPT], uint32_t& kb, bool& ok) {
@@ -671,15 +675,12 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     }
   };
 
-  float m_run[BPW], l_run[BPW];
-  f32x4 acc[BPW][NT];
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 acc[ND];   // O^T: register v of lane l: d 32 dl + 8 (v / 4) + 4 hi + v % 4
 #pragma unroll
-  for (int bb = 0; bb < BPW; ++bb) {
-    m_run[bb] = -INFINITY;
-    l_run[bb] = 0.0f;
+  for (int dl = 0; dl < ND; ++dl)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[bb][t] = f32x4{0, 0, 0, 0};
-  }
+    for (int v = 0; v < 16; ++v) acc[dl][v] = 0.0f;
   bool first_tile = true;
 
   u32x4 rg[CPT];
@@ -697,17 +698,23 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       const int ch = c * 64 * NW + tid;
       const u32x4 x = rg[c];
       if (ch >= NCH) continue;                   // wave-uniform (NCH is a multiple of 64)
-      if (ch * 16 < TB) {                        // K chunk ch: SPC k-steps of one lane
+      if (ch * 16 < TB) {                        // K chunk ch: row r, SPC groups of 8 d from d0
         const int kl = ch & 63, kj = (ch >> 6) % KL, km = (ch >> 6) / KL;
-        uint8_t* dst = s_k + ((km * NK + kj * SPC) * 64 + kl) * 16;   // operand (km, kj SPC + q)
+        const int g = kl & 15, kc = kl >> 4;   // the stored tile interleaves rows (k_chunk_offset)
+        const int r = 16 * (g >> 2) + 4 * km + (g & 3);
+        const int d0 = FP8 ? 64 * kj + 16 * kc : FP4 ? 32 * kc : 32 * kj + 8 * kc;
+        uint8_t* rowb = s_k + ((r >> 5) * NKS * 64 + swap23(r & 31)) * 16;
+        auto dst = [&](int dd) {   // operand slot of d dd .. dd + 7 of row r
+          return reinterpret_cast<bf16x8*>(rowb + ((dd >> 4) * 64 + 32 * ((dd >> 3) & 1)) * 16);
+        };
         if (FP4) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) *reinterpret_cast<bf16x8*>(dst + 1024 * q) = fp4x8_to_bf16x8(x[q]);
+          for (int q = 0; q < 4; ++q) *dst(d0 + 8 * q) = fp4x8_to_bf16x8(x[q]);
         } else if (FP8) {
-          *reinterpret_cast<bf16x8*>(dst) = fp8x8_to_bf16x8(x[0], x[1]);
-          *reinterpret_cast<bf16x8*>(dst + 1024) = fp8x8_to_bf16x8(x[2], x[3]);
+          *dst(d0) = fp8x8_to_bf16x8(x[0], x[1]);
+          *dst(d0 + 8) = fp8x8_to_bf16x8(x[2], x[3]);
         } else {
-          *reinterpret_cast<u32x4*>(dst) = x;
+          *reinterpret_cast<u32x4*>(dst(d0)) = x;
         }
       } else {                                   // V: rows row0 .. of column d
         const int vb = ch * 16 - TB;             // byte of the stored V tile
@@ -759,147 +766,134 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     if (tt + SPi <= last) fetch(tt + SPi, rg, kbyte, ok);
 
     if (busy && tile_ok) {
-      // ---- row masks of this lane's 16 rows (bit j: row 16 kg + j of the tile)
-      const int base = r0 + 16 * kg;
-      uint32_t kb = 0;
-      const bool ring = !ctile && r0 < W;
-      if (ctile || ring) {
-        kb = (uint32_t)(s_keep >> (16 * kg)) & 0xFFFFu;
+      // ---- visible rows of the tile for this lane's query, as a 64-bit mask,
+      // then this lane's 32 rows: bit 8 k + e of vl is row 16 k + 8 hi + e
+      const uint64_t keep64 = s_keep;
+      uint64_t vis = col_ok ? rows64(0, valid - 1) : 0ull;
+      if (ctile) {   // chunk tokens rr <= t, in the window or kept
+        vis &= rows64(tq - W + 1, tq) | (keep64 & rows64(0, tq));
+      } else if (r0 < W) {
+        // ring rows whose token left query t's window: P >= W: the t + 1
+        // rows from pmw on (circularly); P < W: rows 0 .. P + t - W
+        uint64_t hid;
+        if (P >= W) {
+          const int len = min(tq + 1, W);
+          hid = rows64(pmw - r0, min(pmw + len, W) - 1 - r0) | rows64(-r0, pmw + len - W - 1 - r0);
+        } else {
+          hid = rows64(-r0, min(P + tq - W, W - 1) - r0);
+        }
+        vis &= ~(hid & ~keep64);
       }
-      const uint32_t vbits = range_bits(ctile ? 0 : r0, (ctile ? 0 : r0) + valid - 1,
-                                        ctile ? 16 * kg : base);
-      uint32_t vis[BPW];
+      uint32_t vl = 0;
 #pragma unroll
-      for (int bb = 0; bb < BPW; ++bb) {
-        uint32_t v = col_ok[bb] ? vbits : 0u;
-        const int t = tq[bb];
-        if (ctile) {   // chunk tokens rr <= t, in the window or kept
-          v &= range_bits(t - W + 1, t, 16 * kg) | (kb & range_bits(0, t, 16 * kg));
-        } else if (ring) {
-          // ring rows whose token left query t's window: P >= W: the t + 1
-          // rows from pmw on (circularly); P < W: rows 0 .. P + t - W
-          uint32_t hid;
-          if (P >= W) {
-            const int len = min(t + 1, W);
-            hid = range_bits(pmw, min(pmw + len, W) - 1, base) |
-                  range_bits(0, pmw + len - W - 1, base);
+      for (int k = 0; k < 4; ++k) vl |= (uint32_t)((vis >> (16 * k + 8 * hi)) & 0xFFu) << (8 * k);
+
+      // ---- S = K . Q^T: two 32-row blocks; register v of block mu is row
+      // 32 mu + 16 (v / 8) + 8 hi + v % 8 (the K rows were staged in that order)
+      f32x16 sc[2];
+#pragma unroll
+      for (int mu = 0; mu < 2; ++mu)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sc[mu][v] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < NKS; ++st)
+#pragma unroll
+        for (int mu = 0; mu < 2; ++mu) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(s_k + ((mu * NKS + st) * 64 + lane) * 16);
+          sc[mu] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sc[mu], 0, 0, 0);
+        }
+
+      // ---- online softmax over the column (this lane's 32 rows and lane l ^ 32's);
+      // z[k][e] is row 16 k + 8 hi + e.  Masked logits -> -inf (a real
+      // branch: most tiles need none); the scale c1 > 0 goes into the max and
+      // the exponent.
+      float z[4][8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[k][e] = sc[k >> 1][8 * (k & 1) + e];
+      if (__ballot(vl != 0xFFFFFFFFu) != 0) {   // wave-uniform
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (!((vl >> (8 * k + e)) & 1u)) z[k][e] = -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[k][e]);
+      tmax = max_xor32(tmax) * c1;
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      if (!first_tile) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+        if (__ballot(alpha != 1.0f)) {   // once the maxima settle, most tiles skip this
+#pragma unroll
+          for (int dl = 0; dl < ND; ++dl) acc[dl] *= alpha;
+        }
+      }
+      float psum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          z[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k][e], c1, -m_use));
+          psum += z[k][e];
+        }
+      l_run += psum;
+      m_run = m_new;
+
+      // ---- O^T += V^T . P^T over the 4 row blocks of 16: this lane's P
+      // operand for block k is z[k] (rows 16 k + 8 hi + e), V^T's the d
+      // column 32 dl + cq at the same rows
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f16x8 pf;
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (Q) {
+            pf[e] = (_Float16)z[k][e];
           } else {
-            hid = range_bits(0, min(P + t - W, W - 1), base);
-          }
-          v &= ~(hid & ~kb);
-        }
-        vis[bb] = v;
-      }
-
-      // ---- S = K . Q^T for both blocks, each K operand read once
-      f32x4 sc[BPW][4];
-#pragma unroll
-      for (int bb = 0; bb < BPW; ++bb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sc[bb][m] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int st = 0; st < NK; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(s_k + ((m * NK + st) * 64 + lane) * 16);
-#pragma unroll
-          for (int bb = 0; bb < BPW; ++bb)
-            if (blk_ok[bb]) sc[bb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[bb][st], sc[bb][m], 0, 0, 0);
-        }
-
-      // ---- per block: online softmax -> P operand, then O^T += V^T . P^T.
-      // Block 1's softmax (VALU) is independent of block 0's PV products
-      // (MFMA), so the two overlap; V operands are read again for block 1.
-#pragma unroll
-      for (int bb = 0; bb < BPW; ++bb) {
-        if (!blk_ok[bb]) continue;
-        // raw logits; masked ones -> -inf (a real branch: most tiles need none).
-        // The scale c1 > 0 goes into the max and the exponent, not each logit.
-        float z[4][4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) z[m][r] = sc[bb][m][r];
-        if (__ballot(vis[bb] != 0xFFFFu) != 0) {   // wave-uniform
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (!((vis[bb] >> (4 * m + r)) & 1u)) z[m][r] = -INFINITY;
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, z[m][r]);
-        tmax = max_xor32(max_xor16(tmax)) * c1;
-        const float m_new = fmaxf(m_run[bb], tmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        if (!first_tile) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run[bb] - m_use);
-          l_run[bb] *= alpha;
-          if (__ballot(alpha != 1.0f)) {   // once the maxima settle, most tiles skip this
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[bb][nt] *= alpha;
+            const __bf16 hb = (__bf16)z[k][e];
+            phi[e] = hb;
+            plo[e] = (__bf16)(z[k][e] - (float)hb);
           }
         }
-        float psum = 0.0f;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[m][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[m][r], c1, -m_use));
-            psum += z[m][r];
+        for (int dl = 0; dl < ND; ++dl) {
+          const u32x4 vv = *reinterpret_cast<const u32x4*>(s_v + (32 * dl + cq) * VP + (16 * k + 8 * hi) * 2);
+          if (Q) {
+            acc[dl] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), pf, acc[dl], 0, 0, 0);
+          } else {
+            acc[dl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), phi, acc[dl], 0, 0, 0);
+            acc[dl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), plo, acc[dl], 0, 0, 0);
           }
-        l_run[bb] += psum;
-        m_run[bb] = m_new;
-        f16x8 pf[2];
-        bf16x8 phi[2], plo[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = z[2 * hh + (e >> 2)][e & 3];
-            if (Q) {
-              pf[hh][e] = (_Float16)pv;
-            } else {
-              const __bf16 hi = (__bf16)pv;
-              phi[hh][e] = hi;
-              plo[hh][e] = (__bf16)(pv - (float)hi);
-            }
-          }
-        __asm__ volatile("" ::: "memory");   // V operands are read again for each block
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 vv = *reinterpret_cast<const u32x4*>(s_v + (16 * nt + g) * VP + (16 * kg + 8 * hh) * 2);
-            if (Q) {
-              acc[bb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(vv), pf[hh], acc[bb][nt], 0, 0, 0);
-            } else {
-              acc[bb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), phi[hh], acc[bb][nt], 0, 0, 0);
-              acc[bb][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vv), plo[hh], acc[bb][nt], 0, 0, 0);
-            }
-          }
+        }
       }
       first_tile = false;
     }
     __syncthreads();   // the tile in LDS is read by every wave before the next one lands
   }
 
-  // ---- this wave's partial states
-#pragma unroll
-  for (int bb = 0; bb < BPW; ++bb) {
-    const int cb = cb0 + bb;
-    const float l = sum_xor32(sum_xor16(l_run[bb]));
-    if (cb >= p.NB) continue;
+  // ---- this lane's partial state (column cq: block cb0 + cq / 16)
+  const float lsum = sum_xor32(l_run);
+  const int cb = cb0 + (cq >> 4);
+  if (busy && cb < p.NB) {
     const int64_t slot = ((int64_t)cgi * p.Gw + w) * kWideGroup + (cb - cgi * kWideGroup);
+    const int64_t row = slot * 16 + (cq & 15);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      *reinterpret_cast<f32x4*>(p.part_o + (slot * 16 + g) * D + 16 * nt + 4 * kg) = acc[bb][nt] * vs;
-    if (kg == 0) {
-      p.part_ml[(slot * 16 + g) * 2] = m_run[bb];
-      p.part_ml[(slot * 16 + g) * 2 + 1] = l;
+    for (int dl = 0; dl < ND; ++dl)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        *reinterpret_cast<f32x4*>(p.part_o + row * D + 32 * dl + 8 * a4 + 4 * hi) =
+            f32x4{acc[dl][4 * a4], acc[dl][4 * a4 + 1], acc[dl][4 * a4 + 2], acc[dl][4 * a4 + 3]} * vs;
+    if (hi == 0) {
+      p.part_ml[row * 2] = m_run;
+      p.part_ml[row * 2 + 1] = lsum;
     }
   }
 }
