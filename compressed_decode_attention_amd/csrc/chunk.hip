@@ -535,13 +535,14 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     cl_ = min(max(p.comp_len[j], 0), cap_);
     nt_ = P_ < 0 ? 0 : (min(W, P_) + cl_ + kTile - 1) / kTile + 1;
   };
-  const int j0 = min(lane, p.nh - 1);   // segment `lane` (of the first 64)
-  int P0, cl0, nt0;
-  seg_meta(j0, P0, cl0, nt0);
-  if (lane >= p.nh) nt0 = 0;
+  const int j0 = min(lane, p.nh - 1);   // segment `lane` (of the first 64): its six
+  const int P0 = p.pos[j0 / p.Hkv];      // loads in one round trip
+  const int cap0 = p.seg_cap[j0], clr0 = p.comp_len[j0];
   const int64_t sb0 = PG ? 0 : p.seg_base[j0];
   const float ka0 = Q ? p.k_amax[j0] : 1.0f;
   const float va0 = Q ? p.v_amax[j0] : 1.0f;
+  const int cl0 = min(max(clr0, 0), max(cap0, 0));
+  const int nt0 = (lane >= p.nh || P0 < 0) ? 0 : (min(W, P0) + cl0 + kTile - 1) / kTile + 1;
   auto tiles_of = [&](int j) {
     if (j < 64) return nt0;
     int a, c, e;
@@ -632,16 +633,6 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   const int col = cb0 * 16 + cq, tq = col / G;
   const bool busy = cb0 < p.NB;                              // per wave
   const bool col_ok = cb0 + (cq >> 4) < p.NB && tq < M;      // per lane
-  bf16x8 qop[NKS];
-  {
-    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + (col - tq * G))
-                                : ((int64_t)b * M * p.Hq + h * G);
-    const uint16_t* qr = p.q + qrow * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < NKS; ++st)
-      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * st));
-  }
-
   // stored bytes of tile tt (and its keep bytes) -> registers
   auto fetch = [&](int tt, u32x4 (&rg)[CPT], uint32_t& kb, bool& ok) {
     const bool ctile = tt == ntiles;
@@ -687,6 +678,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   uint32_t kbyte = 0;
   bool ok = true;
   if (s <= last) fetch(s, rg, kbyte, ok);
+  // the q operands after the first tile's loads (the compiler waits for them
+  // where they are first moved, which would otherwise hold the tile back)
+  bf16x8 qop[NKS];
+  {
+    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + (col - tq * G))
+                                : ((int64_t)b * M * p.Hq + h * G);
+    const uint16_t* qr = p.q + qrow * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st)
+      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * st));
+  }
+
   for (int tt = s; tt <= last; tt += SPi) {
 
     const bool ctile = tt == ntiles;
