@@ -454,8 +454,9 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // differ with their keep rates: equal splits per segment left workgroups
 // between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
 // kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
-// segment, the chunk tile among them.  For each tile the waves stage it in
-// LDS -- the next tile's bytes already in flight in registers -- converting
+// segment, the chunk tile among them.  The waves stage each tile in one of
+// two LDS buffers while computing on the other -- the tile after it already
+// in flight in registers -- converting
 // FP8/FP4 codes once, exactly, to the MFMA operand types (K to bf16 operands
 // of the 32x32x16 products, its rows in the order that makes each lane's S
 // values its own P operand; V to a [d][row] f16 image like a BF16 V tile),
@@ -510,9 +511,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   // K as bf16 MFMA operands, operand-major: operand (mu, st) of lane l at
   // ((mu * NKS + st) * 64 + l) * 16 holds row 32 mu + swap23(l % 32), d
   // 16 st + 8 (l / 32) .. + 7; V as [d][row] 16-bit values, VP bytes a column
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[TX];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[D * VP];
-  __shared__ uint64_t s_keep;   // keep bits of the staged tile's rows
+  // Two buffers: the next tile is staged into one while the waves compute
+  // on the other.
+  __shared__ __attribute__((aligned(16))) uint8_t s_kb[2][TX];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vb[2][D * VP];
+  __shared__ uint64_t s_keepb[2];   // keep bits of the staged tiles' rows
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 15, kg = lane >> 4;
@@ -674,28 +677,16 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     for (int v = 0; v < 16; ++v) acc[dl][v] = 0.0f;
   bool first_tile = true;
 
-  u32x4 rg[CPT];
-  uint32_t kbyte = 0;
-  bool ok = true;
-  if (s <= last) fetch(s, rg, kbyte, ok);
-  // the q operands after the first tile's loads (the compiler waits for them
-  // where they are first moved, which would otherwise hold the tile back)
-  bf16x8 qop[NKS];
-  {
-    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + (col - tq * G))
-                                : ((int64_t)b * M * p.Hq + h * G);
-    const uint16_t* qr = p.q + qrow * D + 8 * hi;
-#pragma unroll
-    for (int st = 0; st < NKS; ++st)
-      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * st));
-  }
-
-  for (int tt = s; tt <= last; tt += SPi) {
-
+  u32x4 rg[CPT];          // the fetched tile's bytes
+  uint32_t kbyte = 0;     // its keep bytes
+  bool ok = true, ok_cur = true;   // it (the tile being computed) has a page
+  // ---- tile tt (its bytes in rg, keep bytes in kbyte) -> LDS buffer buf, converted
+  auto stage = [&](int tt, int buf) {
+    uint8_t* s_k = s_kb[buf];
+    uint8_t* s_v = s_vb[buf];
     const bool ctile = tt == ntiles;
     const int r0 = tt * kTile;
     const int valid = ctile ? M : min(kTile, n - r0);
-    // ---- this tile -> LDS (converted), then the next one's bytes into the registers
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = c * 64 * NW + tid;
@@ -761,14 +752,48 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     }
     if (wave == 0) {   // the tile's keep bits, one per row
       const uint64_t km = __ballot(kbyte != 0);
-      if (lane == 0) s_keep = km;
+      if (lane == 0) s_keepb[buf] = km;
     }
-    const bool tile_ok = ok;
-    if (!tile_ok && tid == 0) atomicOr(p.err, CDA_DEVERR_POOL);
-    __syncthreads();
-    if (tt + SPi <= last) fetch(tt + SPi, rg, kbyte, ok);
+    if (!ok && tid == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+  };
 
-    if (busy && tile_ok) {
+  // Tile s + SP k: fetched two tiles ahead into registers, staged one tile
+  // ahead into the other buffer, so each tile costs one barrier and its
+  // staging overlaps the other waves' products.
+  int cur = 0;
+  if (s <= last) fetch(s, rg, kbyte, ok);
+  // the q operands after the first tile's loads (the compiler waits for them
+  // where they are first moved, which would otherwise hold the tile back)
+  bf16x8 qop[NKS];
+  {
+    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + (col - tq * G))
+                                : ((int64_t)b * M * p.Hq + h * G);
+    const uint16_t* qr = p.q + qrow * D + 8 * hi;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st)
+      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * st));
+  }
+
+  if (s <= last) {
+    stage(s, 0);
+    ok_cur = ok;
+    if (s + SPi <= last) fetch(s + SPi, rg, kbyte, ok);
+  }
+  __syncthreads();
+  for (int tt = s; tt <= last; tt += SPi) {
+    const int tn = tt + SPi;
+    const bool ok_next = ok;
+    if (tn <= last) {
+      stage(tn, cur ^ 1);
+      if (tn + SPi <= last) fetch(tn + SPi, rg, kbyte, ok);
+    }
+    if (busy && ok_cur) {
+      const bool ctile = tt == ntiles;
+      const int r0 = tt * kTile;
+      const int valid = ctile ? M : min(kTile, n - r0);
+      const uint8_t* s_k = s_kb[cur];
+      const uint8_t* s_v = s_vb[cur];
+      const uint64_t s_keep = s_keepb[cur];
       // ---- visible rows of the tile for this lane's query, as a 64-bit mask,
       // then this lane's 32 rows: bit 8 k + e of vl is row 16 k + 8 hi + e
       const uint64_t keep64 = s_keep;
@@ -879,7 +904,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       }
       first_tile = false;
     }
-    __syncthreads();   // the tile in LDS is read by every wave before the next one lands
+    __syncthreads();   // buffer cur is read by every wave before it is staged again
+    ok_cur = ok_next;
+    cur ^= 1;
   }
 
   // ---- this lane's partial state (column cq: block cb0 + cq / 16)
