@@ -1328,7 +1328,7 @@ void chunk_merge_kernel(ChunkParams p) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Column blocks and splits of a chunk call: NB blocks of 16 (token, query
-// head) columns.  With at least 4 blocks the wide kernel runs: Gw 16-wave
+// head) columns.  With at least 4 blocks the wide kernel runs: Gw 8-wave
 // workgroups per group of 16 blocks (about one per CU in all, at least one
 // per segment), shared out among the segments by the kernel's own plan.
 // Else the narrow one: one workgroup per segment, block and split, with SP
