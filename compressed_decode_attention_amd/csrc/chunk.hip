@@ -463,7 +463,7 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // zeroing V rows past the data, and publishing the rows' keep bits as one
 // ballot.  Wave w owns 32 columns (blocks 2w and 2w + 1) over every tile:
 // each K and V operand read from LDS serves 32 columns (with 16x16 products
-// and 16 waves, 39 us against 32 us on that layer: the 512 KB of operand
+// and 16 waves, 35 us against 32 us on that layer: the 512 KB of operand
 // reads per tile bounded it).  Masks: a 64-bit row mask per column (rows
 // past the data; ring rows that left the query's window unkept, one
 // circular interval; chunk tokens after the query or out of its window
