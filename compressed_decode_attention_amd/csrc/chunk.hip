@@ -930,7 +930,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 
 // ---------------------------------------------------------------- commit
 
-// Workgroup i: the chunk's M tokens appended to segment i, with the result of
+// Segment i's commit (one workgroup): the chunk's M tokens appended to it, with the result of
 // M APPEND operations but without their M sequential round trips.  At step
 // t the token at position lp = P + t - W leaves the window (W = 0: the new
 // token itself); if it is kept it goes to compact row W + cl0 + (its rank
@@ -948,9 +948,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 // a sequence to finish advances pos (a counter per sequence, zeroed by the
 // encode launch).
 template <int KV, int D, bool PG>
-__global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uint8_t* k_pool,
-                                                              uint8_t* v_pool, int32_t* comp_len,
-                                                              uint8_t* ring_keep, int32_t* pos) {
+__device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_t* k_pool,
+                                             uint8_t* v_pool, int32_t* comp_len,
+                                             uint8_t* ring_keep, int32_t* pos) {
   constexpr int RB = kv_row_bytes(KV, D);
   constexpr int KC = RB / 16;                  // 16-byte K chunks per row
   constexpr bool FP4 = KV == kKvFP4;
@@ -967,7 +967,7 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
   __shared__ __attribute__((aligned(16))) uint8_t s_mk[kTile * RB];   // moved rows, K
   __shared__ __attribute__((aligned(16))) uint8_t s_mv[D * kTile * E];   // moved rows, V [d][row]
   __shared__ __attribute__((aligned(16))) uint8_t s_ct[2 * kTile * RB];  // the chunk tile, K then V
-  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
   const int P = pos[b];
   if (P < 0) return;                           // idle (paged store): every segment of b
@@ -1239,20 +1239,28 @@ __global__ __launch_bounds__(kBlock) void chunk_commit_kernel(ChunkParams p, uin
 
 // ---------------------------------------------------------------- merge
 
-// Workgroup (segment i, column block cb): the log-sum-exp merge of the SP
-// split states of each of its 16 columns (their o already carries the V
-// scale), normalised, into out and lse.
-// (nh NB workgroups of 4 waves leave about 4 waves per SIMD: the kernel may
-// use the registers of that occupancy to keep every load in flight)
-template <int D>
+// Workgroups 0 .. nh - 1 commit segment blockIdx.x; workgroup nh + (segment
+// i, column block cb) merges the split states of each of that block's 16
+// columns (their o already carries the V scale), normalised, into out and
+// lse.  The commits read and write none of what the merges use, so the two
+// run side by side in one launch, the commits dispatched first.  (The
+// workgroups of 4 waves leave about 4 waves per SIMD: the kernel may use
+// the registers of that occupancy to keep every load in flight.)
+template <int KV, int D, bool PG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 4)))
-void chunk_merge_kernel(ChunkParams p) {
+void chunk_merge_commit_kernel(ChunkParams p, uint8_t* k_pool, uint8_t* v_pool,
+                               int32_t* comp_len, uint8_t* ring_keep, int32_t* pos) {
   // each thread merges IPT items (4 consecutive outputs of one column); the
   // (m, l) and o loads of kMB splits of every item go out together, merged
   // online (a batch's max, then the running sums rescaled to it)
   constexpr int IPT = 16 * (D / 4) / kBlock, kMB = 8;
   static_assert(16 * (D / 4) % kBlock == 0, "merge items per thread");
-  const int i = blockIdx.x / p.NB, cb = blockIdx.x - i * p.NB;
+  if ((int)blockIdx.x < p.nh) {
+    chunk_commit<KV, D, PG>(p, blockIdx.x, k_pool, v_pool, comp_len, ring_keep, pos);
+    return;
+  }
+  const int wm = blockIdx.x - p.nh;
+  const int i = wm / p.NB, cb = wm - i * p.NB;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
   // the segment's splits: wide kernel, from its plan (slots of consecutive
   // workgroups); narrow kernel, SP slots of its own
@@ -1365,9 +1373,8 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
       chunk_attn_wide_kernel<F, DD, PG><<<wgrid, 64 * kWideWaves, 0, s>>>(p);   \
     else                                                                        \
       chunk_attn_kernel<F, DD, PG><<<grid, 64 * kChunkWaves, 0, s>>>(p);        \
-    chunk_merge_kernel<DD><<<nh * NB, kBlock, 0, s>>>(p);                       \
-    chunk_commit_kernel<F, DD, PG><<<nh, kBlock, 0, s>>>(p, k_pool, v_pool,     \
-                                                         comp_len, ring_keep, pos); \
+    chunk_merge_commit_kernel<F, DD, PG><<<nh * (NB + 1), kBlock, 0, s>>>(      \
+        p, k_pool, v_pool, comp_len, ring_keep, pos);                           \
   } while (0)
   if (kv == kKvFP4) {
     CDA_CHUNK(kKvFP4, 128);
