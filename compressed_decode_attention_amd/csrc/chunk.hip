@@ -454,7 +454,8 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // differ with their keep rates: equal splits per segment left workgroups
 // between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
 // kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
-// segment, the chunk tile among them.  The waves stage each tile in one of
+// segment from the highest down, the chunk tile first where it is among
+// them (encoded here from the new rows).  The waves stage each tile in one of
 // two LDS buffers while computing on the other -- the tile after it already
 // in flight in registers -- converting
 // FP8/FP4 codes once, exactly, to the MFMA operand types (K to bf16 operands
@@ -617,6 +618,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       base += __builtin_amdgcn_readlane(x, 63);
     }
   }
+  // the commit's counters (the encode launch, which zeroes them for the
+  // narrow kernel, does not run with this one)
+  if (w == 0 && cgi == 0)
+    for (int j = tid; j < p.B; j += 64 * NW) p.seqcnt[j] = 0;
   if (i < 0) return;                              // the whole workgroup: no split left
   const int b = i / p.Hkv, h = i - b * p.Hkv;
   const bool idle = Praw < 0;
@@ -667,6 +672,87 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       if (ctile) kb = p.keep_new[((int64_t)b * M + min(tid, M - 1)) * p.Hkv + h];
       else if (r0 < W) kb = p.ring_keep[(int64_t)i * W + min(r0 + tid, W - 1)];
     }
+  };
+
+  // The chunk tile, encoded here from the new rows as the encode launch of
+  // the narrow kernel would (the same conversions of the same products, so
+  // the same bytes), into the registers in the stored tile's byte order and
+  // into the workspace, where the commit reads it.  Rows M .. 63 are zero.
+  auto encode_chunk = [&](u32x4 (&rg)[CPT], uint32_t& kb) {
+    const float kinv = Q ? kv_inv_scale<KV>(ka) : 1.0f;
+    const float vinv = Q ? kv_inv_scale<KV>(va) : 1.0f;
+    const int64_t nb0 = (int64_t)b * p.nsb + (int64_t)h * p.nsh;
+    auto f = [](uint32_t bits16, float inv) { return __fmul_rn(__uint_as_float(bits16 << 16), inv); };
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = min(c * 64 * NW + tid, NCH - 1);
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (ch * 16 < TB) {   // K: 16 bytes of row r from element d0 (the stored tile interleaves rows)
+        const int kl = ch & 63, kj = (ch >> 6) % KL, km = (ch >> 6) / KL;
+        const int g = kl & 15, kc = kl >> 4;
+        const int r = 16 * (g >> 2) + 4 * km + (g & 3);
+        const int d0 = FP8 ? 64 * kj + 16 * kc : FP4 ? 32 * kc : 32 * kj + 8 * kc;
+        const uint16_t* src = p.k_new + nb0 + (int64_t)min(r, M - 1) * p.nst + d0;
+        if (FP8) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(src + 8);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4& a = q < 2 ? a0 : a1;
+            const uint32_t w0 = a[2 * (q & 1)], w1 = a[2 * (q & 1) + 1];
+            x[q] = e4m3x2_from_f32(f(w0 & 0xFFFFu, kinv), f(w0 >> 16, kinv)) |
+                   (e4m3x2_from_f32(f(w1 & 0xFFFFu, kinv), f(w1 >> 16, kinv)) << 16);
+          }
+        } else if (FP4) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(src + 8 * q);
+            uint32_t y = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2)
+              y |= e2m1x2_from_f32(f(a[w2] & 0xFFFFu, kinv), f(a[w2] >> 16, kinv)) << (8 * w2);
+            x[q] = y;
+          }
+        } else {
+          x = *reinterpret_cast<const u32x4*>(src);
+        }
+        if (r >= M) x = u32x4{0, 0, 0, 0};
+      } else {              // V: column d, rows row0 .. (16 FP8, 32 FP4, 8 BF16)
+        const int vb = ch * 16 - TB;
+        constexpr int NR = FP8 ? 16 : FP4 ? 32 : 8;
+        const int d = FP8 ? vb / kTile : FP4 ? vb / 32 : (vb / 2) / kTile;
+        const int row0 = FP8 ? vb % kTile : FP4 ? (vb % 32) * 2 : (vb / 2) % kTile;
+        uint32_t v[NR];
+#pragma unroll
+        for (int e = 0; e < NR; ++e) {
+          const uint32_t raw = p.v_new[nb0 + (int64_t)min(row0 + e, M - 1) * p.nst + d];
+          v[e] = row0 + e < M ? raw : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (FP8) {
+            x[q] = e4m3x2_from_f32(f(v[4 * q], vinv), f(v[4 * q + 1], vinv)) |
+                   (e4m3x2_from_f32(f(v[4 * q + 2], vinv), f(v[4 * q + 3], vinv)) << 16);
+          } else if (FP4) {
+            uint32_t y = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2)
+              y |= e2m1x2_from_f32(f(v[8 * q + 2 * w2], vinv), f(v[8 * q + 2 * w2 + 1], vinv)) << (8 * w2);
+            x[q] = y;
+          } else {
+            x[q] = v[2 * q] | (v[2 * q + 1] << 16);
+          }
+        }
+      }
+      rg[c] = x;
+      if (c * 64 * NW + tid < NCH) {
+        uint8_t* dst = ch * 16 < TB ? p.chunk_k + (int64_t)i * TB + ch * 16
+                                    : p.chunk_v + (int64_t)i * TB + (ch * 16 - TB);
+        *reinterpret_cast<u32x4*>(dst) = x;
+      }
+    }
+    kb = 0;
+    if (tid < kTile) kb = p.keep_new[((int64_t)b * M + min(tid, M - 1)) * p.Hkv + h];
   };
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -760,8 +846,14 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   // Tile s + SP k: fetched two tiles ahead into registers, staged one tile
   // ahead into the other buffer, so each tile costs one barrier and its
   // staging overlaps the other waves' products.
+  // This split's tiles from the highest down: the workgroup holding the chunk
+  // tile (always the highest) encodes it first, its loads beside the q loads.
+  const int t0 = s <= last ? s + SPi * ((last - s) / SPi) : -1;
   int cur = 0;
-  if (s <= last) fetch(s, rg, kbyte, ok);
+  if (t0 >= 0) {
+    if (t0 == ntiles) encode_chunk(rg, kbyte);
+    else fetch(t0, rg, kbyte, ok);
+  }
   // the q operands after the first tile's loads (the compiler waits for them
   // where they are first moved, which would otherwise hold the tile back)
   bf16x8 qop[NKS];
@@ -774,18 +866,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + 16 * st));
   }
 
-  if (s <= last) {
-    stage(s, 0);
+  if (t0 >= 0) {
+    stage(t0, 0);
     ok_cur = ok;
-    if (s + SPi <= last) fetch(s + SPi, rg, kbyte, ok);
+    if (t0 - SPi >= s) fetch(t0 - SPi, rg, kbyte, ok);
   }
   __syncthreads();
-  for (int tt = s; tt <= last; tt += SPi) {
-    const int tn = tt + SPi;
+  for (int tt = t0; tt >= s; tt -= SPi) {
+    const int tn = tt - SPi;
     const bool ok_next = ok;
-    if (tn <= last) {
+    if (tn >= s) {
       stage(tn, cur ^ 1);
-      if (tn + SPi <= last) fetch(tn + SPi, rg, kbyte, ok);
+      if (tn - SPi >= s) fetch(tn - SPi, rg, kbyte, ok);
     }
     if (busy && ok_cur) {
       const bool ctile = tt == ntiles;
@@ -1368,7 +1460,7 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
   const dim3 grid((unsigned)(8 * groups * NB * std::max(SP, 1))), wgrid((unsigned)(ncg * p.Gw));
 #define CDA_CHUNK(F, DD)                                                        \
   do {                                                                          \
-    chunk_encode_kernel<F, DD><<<nh, kBlock, 0, s>>>(p);                        \
+    if (!wide) chunk_encode_kernel<F, DD><<<nh, kBlock, 0, s>>>(p);            \
     if (wide)                                                                   \
       chunk_attn_wide_kernel<F, DD, PG><<<wgrid, 64 * kWideWaves, 0, s>>>(p);   \
     else                                                                        \
