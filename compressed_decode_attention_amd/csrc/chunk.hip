@@ -85,7 +85,8 @@ struct ChunkParams {
 // ---------------------------------------------------------------- encode
 
 // Workgroup i: segment i's chunk tokens as one 64-row tile, encoded as the
-// append would encode them; rows M .. 63 are zero.
+// append would encode them; rows M .. 63 are zero.  (Runs before the narrow
+// attention kernel; the wide one encodes its chunk tiles itself.)
 template <int KV, int D>
 __global__ __launch_bounds__(kBlock) void chunk_encode_kernel(ChunkParams p) {
   constexpr bool Q = KV != kKvBF16;
@@ -455,10 +456,10 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 // between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
 // kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
 // segment from the highest down, the chunk tile first where it is among
-// them (encoded here from the new rows).  The waves stage each tile in one of
-// two LDS buffers while computing on the other -- the tile after it already
-// in flight in registers -- converting
-// FP8/FP4 codes once, exactly, to the MFMA operand types (K to bf16 operands
+// them (encoded here from the new rows).  The waves stage each tile in one
+// of two LDS buffers while computing on the other -- the tile after it
+// already in flight in registers -- converting FP8/FP4 codes once, exactly,
+// to the MFMA operand types (K to bf16 operands
 // of the 32x32x16 products, its rows in the order that makes each lane's S
 // values its own P operand; V to a [d][row] f16 image like a BF16 V tile),
 // zeroing V rows past the data, and publishing the rows' keep bits as one
