@@ -268,20 +268,6 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
       ktile = p.k_pool + trow * RB;
       vtile = p.v_pool + trow * RB;
     }
-    // keep bytes of this lane's 16 rows: ring rows of the store, or chunk
-    // tokens (clamped indices: every load stays inside its array)
-    uint32_t kb = 0;   // bit j: row 16 kg + j is kept
-    const bool ring = !ctile && r0 < W;
-    if (ctile || ring) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int rr = 16 * kg + j;
-        const uint8_t byte = ctile ? p.keep_new[((int64_t)b * M + min(rr, M - 1)) * p.Hkv + h]
-                                   : p.ring_keep[(int64_t)i * W + min(r0 + rr, W - 1)];
-        kb |= (uint32_t)(byte != 0) << j;
-      }
-    }
-
     u32x4 kr[4][KL];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -300,6 +286,22 @@ __global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParam
 #pragma unroll
         for (int j = 0; j < VL; ++j)
           vr[nt][j] = *reinterpret_cast<const u32x4*>(vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E);
+    }
+
+    // keep bytes of this lane's 16 rows: ring rows of the store, or chunk
+    // tokens (clamped indices: every load stays inside its array).  After
+    // the tile's loads: a load under a branch is waited for at its join,
+    // which would otherwise hold the tile's loads back a round trip.
+    uint32_t kb = 0;   // bit j: row 16 kg + j is kept
+    const bool ring = !ctile && r0 < W;
+    if (ctile || ring) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int rr = 16 * kg + j;
+        const uint8_t byte = ctile ? p.keep_new[((int64_t)b * M + min(rr, M - 1)) * p.Hkv + h]
+                                   : p.ring_keep[(int64_t)i * W + min(r0 + rr, W - 1)];
+        kb |= (uint32_t)(byte != 0) << j;
+      }
     }
 
     f32x4 sc[4];
