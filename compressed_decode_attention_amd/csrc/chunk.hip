@@ -20,19 +20,21 @@
 // chunk first would overwrite ring rows that the chunk's earlier queries
 // still see.
 //
-// Launches: (1) encode: each segment's chunk becomes one 64-row tile in the
-// store's formats, in the workspace; (2) attention: workgroup (segment,
-// block of 16 query columns, split) walks every split-th tile of the
-// segment, the chunk tile being the last; the 16 columns of a block are
-// (token, query head) pairs, column c = t * G + g; (3) merge of the
-// splits' partial states per column; (4) the commit: the store becomes what
-// M APPEND operations leave, computed for all M tokens at once.
+// Launches: (1) attention: workgroup (split of a segment, group of 16
+// blocks of 16 query columns) walks its share of the segment's tiles; the
+// columns are (token, query head) pairs, column c = t * G + g; the
+// workgroup holding the chunk tile first encodes the chunk into one 64-row
+// tile in the store's formats (in the workspace); (2) the commit of every
+// segment -- the store becomes what M APPEND operations leave, computed for
+// all M tokens at once -- side by side with the merge of the splits'
+// partial states per column.
 //
-// The MFMA layout is the decode kernel's: per 64-row tile and wave,
-//   S^T[token][c] = K_tile[token][:] . Q^T[:][c]      (16 x 16 x 32 bf16)
-//   O^T[d][c]    += V^T[d][token] . P^T[token][c]     (16 x 16 x 32 f16/bf16)
-// with the K tile chunk-permuted and the V tile column-major, and every
-// lane holding, in its S accumulator, the 16 tokens of its P operand.
+// Per 64-row tile and wave of 32 columns (two 32-row blocks mu, four 32-d
+// blocks of V):
+//   S[row][c]    = K_tile[row][:] . Q^T[:][c]        (32 x 32 x 16 bf16)
+//   O^T[d][c]   += V^T[d][row] . P^T[row][c]          (32 x 32 x 16 f16/bf16)
+// with K staged so that every lane holds, in its S accumulator, the rows
+// of its P operand, and V staged column-major.
 #include <algorithm>
 
 #include "attn_common.h"
@@ -44,9 +46,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));   // a 32x32 MFMA acc
 namespace cda {
 namespace {
 
-constexpr int kChunkWaves = 4;       // waves per attention workgroup
-constexpr int kChunkTarget = 512;    // workgroups the split count aims at (narrow kernel)
-constexpr int kWideTarget = 256;     // ... and for the wide kernel: one per CU
+constexpr int kWideTarget = 256;     // attention workgroups in all: one per CU
 constexpr int kMaxRingTiles = CDA_MAX_CHUNK_WINDOW / kTile;   // chunk commit: ring tiles
 
 struct ChunkParams {
@@ -73,392 +73,25 @@ struct ChunkParams {
   uint8_t* chunk_v;            // workspace: [nh] tiles in the V pool format
   float* part_o;               // workspace: [slots][16][D]
   float* part_ml;              // workspace: [slots][16][2]
-  // slots: narrow kernel [nh][NB][SP]; wide kernel [column group][Gw][16 blocks]
-  int32_t* plan;               // workspace: [nh][2] wide kernel: first workgroup, splits
+  // slots: [column group][Gw][16 blocks]
+  int32_t* plan;               // workspace: [nh][2] first workgroup, splits of each segment
   int32_t* seqcnt;             // workspace: [B] segments of the sequence committed
-  int B, Hkv, Hq, G, M, W, nh, NB, SP, out_f32;
-  int Gw;                      // wide kernel: workgroups per column group (0: narrow)
+  int B, Hkv, Hq, G, M, W, nh, NB, out_f32;
+  int Gw;                      // attention workgroups per column group
   float sm_scale;
   int32_t* err;
 };
 
-// ---------------------------------------------------------------- encode
-
-// Workgroup i: segment i's chunk tokens as one 64-row tile, encoded as the
-// append would encode them; rows M .. 63 are zero.  (Runs before the narrow
-// attention kernel; the wide one encodes its chunk tiles itself.)
-template <int KV, int D>
-__global__ __launch_bounds__(kBlock) void chunk_encode_kernel(ChunkParams p) {
-  constexpr bool Q = KV != kKvBF16;
-  constexpr int RB = kv_row_bytes(KV, D);
-  constexpr int CPR = D / 8;                 // 8-element input chunks per row
-  constexpr int VB = KV == kKvBF16 ? 2 : 1;  // LDS bytes per V element (FP4: one code a byte)
-  __shared__ __attribute__((aligned(16))) uint8_t s_k[kTile * RB];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[D * kTile * VB];
-  const int i = blockIdx.x, tid = threadIdx.x;
-  const int b = i / p.Hkv, h = i - b * p.Hkv;
-  if (h == 0 && tid == 0) p.seqcnt[b] = 0;   // the commit's counter of sequence b
-  const float kinv = Q ? kv_inv_scale<KV>(p.k_amax[i]) : 1.0f;
-  const float vinv = Q ? kv_inv_scale<KV>(p.v_amax[i]) : 1.0f;
-  // every pass's input first (unconditional loads of a clamped row, zeroed
-  // past M), then the encoding
-  constexpr int EPT = kTile * CPR / kBlock;
-  static_assert(kTile * CPR % kBlock == 0, "encode shape");
-  u32x4 kin[EPT], vin[EPT];
-#pragma unroll
-  for (int u = 0; u < EPT; ++u) {
-    const int e = u * kBlock + tid, r = e / CPR, d0 = 8 * (e - r * CPR);
-    const int64_t off =
-        (int64_t)b * p.nsb + (int64_t)min(r, p.M - 1) * p.nst + (int64_t)h * p.nsh + d0;
-    kin[u] = *reinterpret_cast<const u32x4*>(p.k_new + off);
-    vin[u] = *reinterpret_cast<const u32x4*>(p.v_new + off);
-  }
-#pragma unroll
-  for (int u = 0; u < EPT; ++u) {
-    const int e = u * kBlock + tid;
-    const int r = e / CPR, c = e - r * CPR, d0 = 8 * c;
-    const bool live = r < p.M;
-    const u32x4 kx = live ? kin[u] : u32x4{0, 0, 0, 0};
-    const u32x4 vx = live ? vin[u] : u32x4{0, 0, 0, 0};
-    if (KV == kKvFP4) {
-      uint32_t kc = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {   // elements 2 w2 (low nibble), 2 w2 + 1
-        kc |= e2m1x2_from_f32(__fmul_rn(__uint_as_float(kx[w2] << 16), kinv),
-                              __fmul_rn(__uint_as_float(kx[w2] & 0xFFFF0000u), kinv)) << (8 * w2);
-        const uint32_t vb = e2m1x2_from_f32(__fmul_rn(__uint_as_float(vx[w2] << 16), vinv),
-                                            __fmul_rn(__uint_as_float(vx[w2] & 0xFFFF0000u), vinv));
-        s_v[(d0 + 2 * w2) * kTile + r] = (uint8_t)(vb & 15u);
-        s_v[(d0 + 2 * w2 + 1) * kTile + r] = (uint8_t)(vb >> 4);
-      }
-      *reinterpret_cast<uint32_t*>(s_k + k_chunk_offset(r, (d0 / 2) >> 4, RB) + ((d0 / 2) & 15)) = kc;
-    } else if (KV == kKvFP8) {
-      uint32_t kc[2] = {0, 0}, vc[2] = {0, 0};
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        kc[w2 >> 1] |= e4m3x2_from_f32(__fmul_rn(__uint_as_float(kx[w2] << 16), kinv),
-                                       __fmul_rn(__uint_as_float(kx[w2] & 0xFFFF0000u), kinv))
-                       << (16 * (w2 & 1));
-        vc[w2 >> 1] |= e4m3x2_from_f32(__fmul_rn(__uint_as_float(vx[w2] << 16), vinv),
-                                       __fmul_rn(__uint_as_float(vx[w2] & 0xFFFF0000u), vinv))
-                       << (16 * (w2 & 1));
-      }
-      *reinterpret_cast<u32x2*>(s_k + k_chunk_offset(r, d0 >> 4, RB) + (d0 & 15)) = u32x2{kc[0], kc[1]};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) s_v[(d0 + q) * kTile + r] = (uint8_t)(vc[q >> 2] >> (8 * (q & 3)));
-    } else {
-      *reinterpret_cast<u32x4*>(s_k + k_chunk_offset(r, c, RB)) = kx;
-      uint16_t* v16 = reinterpret_cast<uint16_t*>(s_v);
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        v16[(d0 + q) * kTile + r] = (uint16_t)((vx[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
-    }
-  }
-  __syncthreads();
-  uint8_t* kt = p.chunk_k + (int64_t)i * kTile * RB;
-  uint8_t* vt = p.chunk_v + (int64_t)i * kTile * RB;
-  for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
-    *reinterpret_cast<u32x4*>(kt + 16 * ch) = *reinterpret_cast<const u32x4*>(s_k + 16 * ch);
-    u32x4 vv;
-    if (KV == kKvFP4) {   // chunk ch: rows r .. r + 31 of column d, two per byte
-      const int d = ch >> 1, r = (ch & 1) * 32;
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * kTile + r);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t a = src[2 * q], c = src[2 * q + 1];   // one code per byte
-        const uint32_t lo = (a & 0xFu) | ((a >> 4) & 0xF0u) | ((a >> 8) & 0xF00u) | ((a >> 12) & 0xF000u);
-        const uint32_t hi = (c & 0xFu) | ((c >> 4) & 0xF0u) | ((c >> 8) & 0xF00u) | ((c >> 12) & 0xF000u);
-        vv[q] = lo | (hi << 16);
-      }
-    } else {              // the LDS image is the tile itself
-      vv = *reinterpret_cast<const u32x4*>(s_v + 16 * ch);
-    }
-    *reinterpret_cast<u32x4*>(vt + 16 * ch) = vv;
-  }
-}
-
 // ---------------------------------------------------------------- attention
 
-// Workgroup w: XCD group w mod 8 takes the segments i = group + 8 l, so that
-// every workgroup reading a segment's tiles shares one L2; within the group,
-// work item w / 8 = (l, column block cb, split s).  Wave v of the workgroup
-// walks the tiles s + SP v, s + SP (v + NW), ... of the segment's n rows,
-// then the chunk tile (tile index ceil(n / 64)).
-template <int KV, int D, bool PG>
-__global__ __launch_bounds__(64 * kChunkWaves) void chunk_attn_kernel(ChunkParams p) {
-  constexpr int NW = kChunkWaves;
-  constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
-  constexpr int E = FP8 ? 1 : 2;
-  constexpr int RB = kv_row_bytes(KV, D);
-  constexpr int NK = D / 32, NT = D / 16, KL = RB / 64, VL = FP8 ? 1 : 2;
-
-  __shared__ float s_m[NW][16], s_l[NW][16];
-  __shared__ f32x4 s_o[NW][16][D / 4];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane & 15, kg = lane >> 4;
-  int work = blockIdx.x >> 3;
-  const int s = work % p.SP;
-  work /= p.SP;
-  const int cb = work % p.NB;
-  const int i = (blockIdx.x & 7) + 8 * (work / p.NB);
-  if (i >= p.nh) return;                       // the whole workgroup
-  const int b = i / p.Hkv, h = i - b * p.Hkv;
-  const int W = p.W, G = p.G, M = p.M;
-
-  // the segment before the chunk; an idle sequence of a paged store (pos <
-  // 0) attends to nothing
-  const int Praw = p.pos[b];
-  const bool idle = Praw < 0;
-  const int P = max(Praw, 0);
-  const int cap = max(p.seg_cap[i], 0);
-  const int cl = min(max(p.comp_len[i], 0), cap);
-  const int n = idle ? 0 : min(W, P) + cl;
-  const int ntiles = (n + kTile - 1) / kTile;
-  const int64_t sb = PG ? 0 : p.seg_base[i];
-  const int64_t in_pool = PG ? INT64_MAX : p.pool_rows - sb;
-  const float ks = Q ? kv_scale<KV>(p.k_amax[i]) : 1.0f;
-  const float vs = Q ? kv_scale<KV>(p.v_amax[i]) : 1.0f;
-
-  // this lane's query column: chunk token tq, query head hq of KV head h
-  const int col = cb * 16 + g;
-  const int tq = col / G, hq = col - tq * G;
-  const bool col_ok = tq < M;
-  bf16x8 qop[NK];
-  {
-    const int64_t qrow = col_ok ? ((int64_t)(b * M + tq) * p.Hq + h * G + hq)
-                                : ((int64_t)b * M * p.Hq + h * G);
-    const uint16_t* qr = p.q + qrow * D;
-#pragma unroll
-    for (int st = 0; st < NK; ++st)
-      qop[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(qr + q_d0<KV>(st, kg)));
-  }
-  const float c1 = p.sm_scale * kLog2e * ks;
-  // ring row r holds position P - W + ((r - P mod W) mod W) once P >= W, else
-  // position r; positions <= lim have left query tq's window
-  const int pmw = W > 0 ? P % W : 0;
-  const int lim = P + tq - W;
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  bool first_tile = true;
-
-  for (int tt = s + p.SP * wave; tt <= ntiles; tt += p.SP * NW) {
-    const bool ctile = tt == ntiles;           // the chunk tile
-    const int r0 = tt * kTile;
-    const int valid = ctile ? (idle ? 0 : M) : (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
-    if (valid <= 0) continue;
-    const uint8_t* ktile;
-    const uint8_t* vtile;
-    if (ctile) {
-      ktile = p.chunk_k + (int64_t)i * kTile * RB;
-      vtile = p.chunk_v + (int64_t)i * kTile * RB;
-    } else {
-      int64_t trow = sb + r0;
-      if (PG) {
-        const int pg = p.page_table[(int64_t)i * p.max_pages + min(tt, p.max_pages - 1)];
-        if (tt >= p.max_pages || pg < 0 || pg >= p.n_pages) {   // inconsistent store
-          if (lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
-          continue;
-        }
-        trow = (int64_t)pg * kTile;
-      }
-      ktile = p.k_pool + trow * RB;
-      vtile = p.v_pool + trow * RB;
-    }
-    u32x4 kr[4][KL];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int j = 0; j < KL; ++j)
-        kr[m][j] = *reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16);
-    u32x4 vr[NT][VL];
-    u32x2 vq[FP4 ? NT : 1];
-    if (FP4) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        vq[nt] = *reinterpret_cast<const u32x2*>(vtile + (16 * nt + g) * (kTile / 2) + 8 * kg);
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < VL; ++j)
-          vr[nt][j] = *reinterpret_cast<const u32x4*>(vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E);
-    }
-
-    // keep bytes of this lane's 16 rows: ring rows of the store, or chunk
-    // tokens (clamped indices: every load stays inside its array).  After
-    // the tile's loads: a load under a branch is waited for at its join,
-    // which would otherwise hold the tile's loads back a round trip.
-    uint32_t kb = 0;   // bit j: row 16 kg + j is kept
-    const bool ring = !ctile && r0 < W;
-    if (ctile || ring) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int rr = 16 * kg + j;
-        const uint8_t byte = ctile ? p.keep_new[((int64_t)b * M + min(rr, M - 1)) * p.Hkv + h]
-                                   : p.ring_keep[(int64_t)i * W + min(r0 + rr, W - 1)];
-        kb |= (uint32_t)(byte != 0) << j;
-      }
-    }
-
-    f32x4 sc[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      sc[m] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int st = 0; st < NK; ++st) {
-        bf16x8 a;
-        if (FP4) {
-          a = fp4x8_to_bf16x8(kr[m][0][st]);
-        } else if (FP8) {
-          const u32x4 v = kr[m][st >> 1];
-          a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
-        } else {
-          a = as_bf16x8(kr[m][st]);
-        }
-        sc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], sc[m], 0, 0, 0);
-      }
-    }
-
-    // visibility of this lane's tokens to query tq
-    float z[4][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = 16 * kg + 4 * m + r;       // row inside the tile
-        bool vis = col_ok && rr < valid;
-        if (ctile) {                              // chunk token rr
-          vis = vis && rr <= tq && (tq - rr < W || ((kb >> (4 * m + r)) & 1u));
-        } else if (ring && r0 + rr < W) {         // ring row of the store
-          int d = r0 + rr - pmw;
-          if (d < 0) d += W;
-          const int pr = P >= W ? P - W + d : r0 + rr;
-          vis = vis && (pr > lim || ((kb >> (4 * m + r)) & 1u));
-        }
-        z[m][r] = vis ? sc[m][r] * c1 : -INFINITY;
-        tmax = fmaxf(tmax, z[m][r]);
-      }
-    tmax = max_xor32(max_xor16(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    if (!first_tile) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      l_run *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
-    }
-    float psum = 0.0f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
-        psum += z[m][r];
-      }
-    l_run += psum;
-    m_run = m_new;
-
-    // rows past the data: their V bytes may not be finite values
-    if (!FP4 && valid < kTile) {
-#pragma unroll
-      for (int j = 0; j < VL; ++j) {
-        const int lb = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t msk = bytes_below(lb, q);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) vr[nt][j][q] &= msk;
-        }
-      }
-    }
-
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (Q) {
-        f16x8 pf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = (_Float16)z[2 * hh + (e >> 2)][e & 3];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f16x8 a;
-          if (FP4) {
-            a = fp4x8_to_f16x8(vq[nt][hh]);
-          } else {
-            const u32x4 v = vr[nt][0];
-            a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
-          }
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, acc[nt], 0, 0, 0);
-        }
-      } else {
-        bf16x8 phi, plo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = z[2 * hh + (e >> 2)][e & 3];
-          const __bf16 hi = (__bf16)pv;
-          phi[e] = hi;
-          plo[e] = (__bf16)(pv - (float)hi);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 a = as_bf16x8(vr[nt][hh]);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[nt], 0, 0, 0);
-        }
-      }
-    }
-    first_tile = false;
-  }
-
-  // ---- combine the waves; one partial state per column
-  l_run = sum_xor32(sum_xor16(l_run));
-  if (kg == 0) {
-    s_m[wave][g] = m_run;
-    s_l[wave][g] = l_run;
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
-  __syncthreads();
-  const int64_t slot = ((int64_t)i * p.NB + cb) * p.SP + s;
-  for (int e = tid; e < 16 * (D / 4); e += 64 * NW) {
-    const int c = e / (D / 4), d4 = e - c * (D / 4);
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, s_m[ww][c]);
-    f32x4 O = f32x4{0, 0, 0, 0};
-    float L = 0.0f;
-    if (Mx != -INFINITY) {
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float mw = s_m[ww][c];
-        if (mw == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(mw - Mx);
-        O += f * s_o[ww][c][d4];
-        L += f * s_l[ww][c];
-      }
-    }
-    *reinterpret_cast<f32x4*>(p.part_o + (slot * 16 + c) * D + 4 * d4) = O * vs;
-    if (d4 == 0) {
-      p.part_ml[(slot * 16 + c) * 2] = Mx;
-      p.part_ml[(slot * 16 + c) * 2 + 1] = L;
-    }
-  }
-}
-
-// ---------------------------------------------------------------- attention, wide
-
-// For chunks with many columns (at least 4 blocks of 16): workgroup (split
-// s of a segment, group of up to 16 column blocks), 8 waves, with splits
+// Workgroup (split s of a segment, group of up to 16 blocks of 16 (token,
+// query head) columns), 8 waves, with splits
 // given out in proportion to the segments' tile counts (segment lengths
 // differ with their keep rates: equal splits per segment left workgroups
 // between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
 // kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
 // segment from the highest down, the chunk tile first where it is among
-// them (encoded here from the new rows).  The waves stage each tile in one
+// them (encoded here from the new rows, as an APPEND would encode them).  The waves stage each tile in one
 // of two LDS buffers while computing on the other -- the tile after it
 // already in flight in registers -- converting FP8/FP4 codes once, exactly,
 // to the MFMA operand types (K to bf16 operands
@@ -621,8 +254,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       base += __builtin_amdgcn_readlane(x, 63);
     }
   }
-  // the commit's counters (the encode launch, which zeroes them for the
-  // narrow kernel, does not run with this one)
+  // the commit's counters, for the launch after this one
   if (w == 0 && cgi == 0)
     for (int j = tid; j < p.B; j += 64 * NW) p.seqcnt[j] = 0;
   if (i < 0) return;                              // the whole workgroup: no split left
@@ -677,10 +309,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     }
   };
 
-  // The chunk tile, encoded here from the new rows as the encode launch of
-  // the narrow kernel would (the same conversions of the same products, so
-  // the same bytes), into the registers in the stored tile's byte order and
-  // into the workspace, where the commit reads it.  Rows M .. 63 are zero.
+  // The chunk tile, encoded here from the new rows as an APPEND would encode
+  // them (the same conversions of the same products, so the same bytes),
+  // into the registers in the stored tile's byte order and into the
+  // workspace, where the commit reads it.  Rows M .. 63 are zero.
   auto encode_chunk = [&](u32x4 (&rg)[CPT], uint32_t& kb) {
     const float kinv = Q ? kv_inv_scale<KV>(ka) : 1.0f;
     const float vinv = Q ? kv_inv_scale<KV>(va) : 1.0f;
@@ -846,7 +478,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     if (!ok && tid == 0) atomicOr(p.err, CDA_DEVERR_POOL);
   };
 
-  // Tile s + SP k: fetched two tiles ahead into registers, staged one tile
+  // Each tile fetched two tiles ahead into registers and staged one tile
   // ahead into the other buffer, so each tile costs one barrier and its
   // staging overlaps the other waves' products.
   // This split's tiles from the highest down: the workgroup holding the chunk
@@ -1041,7 +673,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 // nibble of a row it does not write; the compact and the ring writes go in
 // two rounds because rows W - 1 and W can share a byte.  The last segment of
 // a sequence to finish advances pos (a counter per sequence, zeroed by the
-// encode launch).
+// attention launch).
 template <int KV, int D, bool PG>
 __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_t* k_pool,
                                              uint8_t* v_pool, int32_t* comp_len,
@@ -1357,15 +989,11 @@ void chunk_merge_commit_kernel(ChunkParams p, uint8_t* k_pool, uint8_t* v_pool,
   const int wm = blockIdx.x - p.nh;
   const int i = wm / p.NB, cb = wm - i * p.NB;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
-  // the segment's splits: wide kernel, from its plan (slots of consecutive
-  // workgroups); narrow kernel, SP slots of its own
-  const bool wide = p.Gw > 0;
-  const int first = wide ? min(max(p.plan[2 * i], 0), p.Gw) : 0;   // (within the slots)
-  const int nsp = wide ? min(max(p.plan[2 * i + 1], 0), p.Gw - first) : p.SP;
-  const int64_t slot0 = wide ? ((int64_t)(cb / kWideGroup) * p.Gw + first) * kWideGroup +
-                                   cb % kWideGroup
-                             : ((int64_t)i * p.NB + cb) * p.SP;
-  const int64_t sstep = wide ? kWideGroup : 1;   // slot stride between splits
+  // the segment's splits, from its plan (slots of consecutive workgroups)
+  const int first = min(max(p.plan[2 * i], 0), p.Gw);   // (within the slots)
+  const int nsp = min(max(p.plan[2 * i + 1], 0), p.Gw - first);
+  const int64_t slot0 = ((int64_t)(cb / kWideGroup) * p.Gw + first) * kWideGroup + cb % kWideGroup;
+  constexpr int64_t sstep = kWideGroup;   // slot stride between splits
   float Mx[IPT], L[IPT];
   f32x4 O[IPT];
 #pragma unroll
@@ -1430,44 +1058,27 @@ void chunk_merge_commit_kernel(ChunkParams p, uint8_t* k_pool, uint8_t* v_pool,
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Column blocks and splits of a chunk call: NB blocks of 16 (token, query
-// head) columns.  With at least 4 blocks the wide kernel runs: Gw 8-wave
-// workgroups per group of 16 blocks (about one per CU in all, at least one
-// per segment), shared out among the segments by the kernel's own plan.
-// Else the narrow one: one workgroup per segment, block and split, with SP
-// splits so that the grid holds about kChunkTarget workgroups (at most 16).
-// Slots: the partial states the merge reads, 16 columns each.
-void chunk_shape(int nh, int G, int M, int& NB, int& SP, int& Gw, int64_t& slots) {
+// Column blocks of a chunk call: NB blocks of 16 (token, query head)
+// columns; Gw 8-wave attention workgroups per group of 16 blocks (about one
+// per CU in all, at least one per segment), shared out among the segments
+// by the kernel's own plan.  Slots: the partial states the merge reads, 16
+// columns each.
+void chunk_shape(int nh, int G, int M, int& NB, int& Gw, int64_t& slots) {
   NB = (G * M + 15) / 16;
-  const bool wide = NB >= 4;
   const int ncg = (NB + kWideGroup - 1) / kWideGroup;
-  if (wide) {
-    Gw = std::max((kWideTarget + ncg - 1) / ncg, nh);
-    SP = 0;
-    slots = (int64_t)ncg * Gw * kWideGroup;
-  } else {
-    Gw = 0;
-    const int64_t per = (int64_t)std::max(nh, 1) * NB;
-    SP = (int)std::min<int64_t>(16, std::max<int64_t>(1, (kChunkTarget + per - 1) / per));
-    slots = (int64_t)nh * NB * SP;
-  }
+  Gw = std::max((kWideTarget + ncg - 1) / ncg, nh);
+  slots = (int64_t)ncg * Gw * kWideGroup;
 }
 
 template <bool PG>
-void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
-                          const ChunkParams& p, uint8_t* k_pool, uint8_t* v_pool,
-                          int32_t* comp_len, uint8_t* ring_keep, int32_t* pos) {
-  const int groups = (nh + 7) / 8;
-  const bool wide = p.Gw > 0;
+void launch_chunk_kernels(int kv, int D, int nh, int NB, hipStream_t s, const ChunkParams& p,
+                          uint8_t* k_pool, uint8_t* v_pool, int32_t* comp_len,
+                          uint8_t* ring_keep, int32_t* pos) {
   const int ncg = (NB + kWideGroup - 1) / kWideGroup;
-  const dim3 grid((unsigned)(8 * groups * NB * std::max(SP, 1))), wgrid((unsigned)(ncg * p.Gw));
+  const dim3 grid((unsigned)(ncg * p.Gw));
 #define CDA_CHUNK(F, DD)                                                        \
   do {                                                                          \
-    if (!wide) chunk_encode_kernel<F, DD><<<nh, kBlock, 0, s>>>(p);            \
-    if (wide)                                                                   \
-      chunk_attn_wide_kernel<F, DD, PG><<<wgrid, 64 * kWideWaves, 0, s>>>(p);   \
-    else                                                                        \
-      chunk_attn_kernel<F, DD, PG><<<grid, 64 * kChunkWaves, 0, s>>>(p);        \
+    chunk_attn_wide_kernel<F, DD, PG><<<grid, 64 * kWideWaves, 0, s>>>(p);      \
     chunk_merge_commit_kernel<F, DD, PG><<<nh * (NB + 1), kBlock, 0, s>>>(      \
         p, k_pool, v_pool, comp_len, ring_keep, pos);                           \
   } while (0)
@@ -1487,9 +1098,9 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, int SP, hipStream_t s,
 // [partial (m, l)][partial o].
 size_t chunk_workspace_bytes(const cda_kv_cache& c, int G, int M) {
   const int nh = c.B * c.Hkv;
-  int NB, SP, Gw;
+  int NB, Gw;
   int64_t slots;
-  chunk_shape(nh, G, M, NB, SP, Gw, slots);
+  chunk_shape(nh, G, M, NB, Gw, slots);
   const size_t tile = (size_t)kTile * kv_row_bytes(c.kv_dtype, c.D);
   const size_t cols = (size_t)slots * 16;
   return 2 * align256((size_t)nh * tile) + align256((size_t)c.B * 4) +
@@ -1533,7 +1144,7 @@ hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M,
   p.W = c.W;
   p.nh = nh;
   int64_t slots;
-  chunk_shape(nh, G, M, p.NB, p.SP, p.Gw, slots);
+  chunk_shape(nh, G, M, p.NB, p.Gw, slots);
   p.out_f32 = out_f32;
   p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c.D);
   p.err = c.err;
@@ -1554,10 +1165,10 @@ hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M,
   uint8_t* kp = static_cast<uint8_t*>(c.k_pool);
   uint8_t* vp = static_cast<uint8_t*>(c.v_pool);
   if (c.page_table)
-    launch_chunk_kernels<true>(c.kv_dtype, c.D, nh, p.NB, p.SP, s, p, kp, vp, c.comp_len,
+    launch_chunk_kernels<true>(c.kv_dtype, c.D, nh, p.NB, s, p, kp, vp, c.comp_len,
                                c.ring_keep, c.pos);
   else
-    launch_chunk_kernels<false>(c.kv_dtype, c.D, nh, p.NB, p.SP, s, p, kp, vp, c.comp_len,
+    launch_chunk_kernels<false>(c.kv_dtype, c.D, nh, p.NB, s, p, kp, vp, c.comp_len,
                                 c.ring_keep, c.pos);
   return hipGetLastError();
 }

@@ -259,5 +259,12 @@ def test_chunk_validation(lib):
     c2 = _cache(lib, W=lib.CDA_MAX_CHUNK_WINDOW + 1)
     assert f(C.byref(c2), C.byref(a), 4, q, 8, 0.0, out, 0, None, ws,
              L.cda_chunk_workspace_bytes(C.byref(c2), 8, 4), None) == 2                 # W too large
-    # the workspace grows with the chunk
-    assert L.cda_chunk_workspace_bytes(C.byref(c), 8, 64) > need
+    # the workspace grows with the segments: their chunk tiles, and the
+    # partial states once segments outnumber the 256 attention workgroups
+    # (the partial states do not grow with M: the workgroups stay ~256)
+    assert L.cda_chunk_workspace_bytes(C.byref(c), 32, 64) == \
+        L.cda_chunk_workspace_bytes(C.byref(c), 32, 16)
+    c3 = _cache(lib, B=300)
+    tile = 64 * 64 * 2   # one BF16 D = 64 tile
+    assert (L.cda_chunk_workspace_bytes(C.byref(c3), 8, 4) - need >
+            2 * tile * (300 * 2 - 2))
