@@ -131,7 +131,11 @@ __device__ __forceinline__ uint64_t rows64(int a, int b) {
 // Bits 2 and 3 of x exchanged (the K row order of the 32x32 S products).
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int KV, int D, bool PG>
+// RS = 2 (chunks of at most 8 blocks, where most waves would have no
+// columns): waves 2c and 2c + 1 share column group c, each taking one
+// 32-row half of every tile with its own softmax state; the pair merges
+// the two states at the end.
+template <int KV, int D, bool PG, int RS>
 __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkParams p) {
   constexpr int NW = kWideWaves;
   constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
@@ -272,7 +276,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   // this wave's 32 columns: blocks cb0 and cb0 + 1, column cb0 * 16 + cq
   // -> (token, head); lanes l and l + 32 share column l % 32
   const int hi = lane >> 5, cq = lane & 31;
-  const int cb0 = cgi * kWideGroup + wave * kWideBlocks;
+  const int wc = wave / RS, mh = RS == 2 ? (wave & 1) : 0;   // column group, row half
+  const int cb0 = cgi * kWideGroup + wc * kWideBlocks;
+  constexpr int NMU = 2 / RS, NKB = 4 / RS;   // 32-row blocks, 16-row blocks of this wave
+  const int kb0 = RS == 2 ? 2 * mh : 0;       // its first 16-row block
   const int col = cb0 * 16 + cq, tq = col / G;
   const bool busy = cb0 < p.NB;                              // per wave
   const bool col_ok = cb0 + (cq >> 4) < p.NB && tq < M;      // per lane
@@ -539,46 +546,49 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
         }
         vis &= ~(hid & ~keep64);
       }
-      uint32_t vl = 0;
+      uint32_t vl = 0;   // bit 8 kk + e: row 16 (kb0 + kk) + 8 hi + e
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vl |= (uint32_t)((vis >> (16 * k + 8 * hi)) & 0xFFu) << (8 * k);
+      for (int kk = 0; kk < NKB; ++kk)
+        vl |= (uint32_t)((vis >> (16 * (kb0 + kk) + 8 * hi)) & 0xFFu) << (8 * kk);
+      constexpr uint32_t kAll = RS == 2 ? 0xFFFFu : 0xFFFFFFFFu;
 
       // ---- S = K . Q^T: two 32-row blocks; register v of block mu is row
       // 32 mu + 16 (v / 8) + 8 hi + v % 8 (the K rows were staged in that order)
-      f32x16 sc[2];
+      f32x16 sc[NMU];
 #pragma unroll
-      for (int mu = 0; mu < 2; ++mu)
+      for (int mm = 0; mm < NMU; ++mm)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sc[mu][v] = 0.0f;
+        for (int v = 0; v < 16; ++v) sc[mm][v] = 0.0f;
 #pragma unroll
       for (int st = 0; st < NKS; ++st)
 #pragma unroll
-        for (int mu = 0; mu < 2; ++mu) {
+        for (int mm = 0; mm < NMU; ++mm) {
+          const int mu = RS == 2 ? mh : mm;
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(s_k + ((mu * NKS + st) * 64 + lane) * 16);
-          sc[mu] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sc[mu], 0, 0, 0);
+          sc[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[st], sc[mm], 0, 0, 0);
         }
 
       // ---- online softmax over the column (this lane's 32 rows and lane l ^ 32's);
       // z[k][e] is row 16 k + 8 hi + e.  Masked logits -> -inf (a real
       // branch: most tiles need none); the scale c1 > 0 goes into the max and
       // the exponent.
-      float z[4][8];
+      float z[NKB][8];   // z[kk]: row block kb0 + kk
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) z[k][e] = sc[k >> 1][8 * (k & 1) + e];
-      if (__ballot(vl != 0xFFFFFFFFu) != 0) {   // wave-uniform
+        for (int e = 0; e < 8; ++e) z[kk][e] = sc[kk >> 1][8 * (kk & 1) + e];
+      if (__ballot(vl != kAll) != 0) {   // wave-uniform
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (!((vl >> (8 * k + e)) & 1u)) z[k][e] = -INFINITY;
+            if (!((vl >> (8 * kk + e)) & 1u)) z[kk][e] = -INFINITY;
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[k][e]);
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, z[kk][e]);
       tmax = max_xor32(tmax) * c1;
       const float m_new = fmaxf(m_run, tmax);
       const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -592,11 +602,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       }
       float psum = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
+      for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          z[k][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k][e], c1, -m_use));
-          psum += z[k][e];
+          z[kk][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[kk][e], c1, -m_use));
+          psum += z[kk][e];
         }
       l_run += psum;
       m_run = m_new;
@@ -605,17 +615,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       // operand for block k is z[k] (rows 16 k + 8 hi + e), V^T's the d
       // column 32 dl + cq at the same rows
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int kk = 0; kk < NKB; ++kk) {
+        const int k = kb0 + kk;
         f16x8 pf;
         bf16x8 phi, plo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (Q) {
-            pf[e] = (_Float16)z[k][e];
+            pf[e] = (_Float16)z[kk][e];
           } else {
-            const __bf16 hb = (__bf16)z[k][e];
+            const __bf16 hb = (__bf16)z[kk][e];
             phi[e] = hb;
-            plo[e] = (__bf16)(z[k][e] - (float)hb);
+            plo[e] = (__bf16)(z[kk][e] - (float)hb);
           }
         }
 #pragma unroll
@@ -637,9 +648,40 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   }
 
   // ---- this lane's partial state (column cq: block cb0 + cq / 16)
-  const float lsum = sum_xor32(l_run);
+  float lsum = sum_xor32(l_run);
+  if (RS == 2) {
+    // the odd wave of each pair hands its state to the even one, through
+    // the staging buffers (free after the loop's last barrier): pairs 0, 1
+    // in the K buffers, 2, 3 in the V buffers, ND * 1024 floats each
+    __shared__ float s_pm[NW / 2][64], s_pl[NW / 2][64];
+    static_assert(2 * TX >= 2 * ND * 4096 && 2 * D * VP >= 2 * ND * 4096, "pair state space");
+    float* pacc = wc < 2 ? reinterpret_cast<float*>(&s_kb[0][0]) + wc * ND * 1024
+                         : reinterpret_cast<float*>(&s_vb[0][0]) + (wc - 2) * ND * 1024;
+    __syncthreads();
+    if (mh == 1) {
+      s_pm[wc][lane] = m_run;
+      s_pl[wc][lane] = lsum;
+#pragma unroll
+      for (int dl = 0; dl < ND; ++dl)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) pacc[(dl * 16 + v) * 64 + lane] = acc[dl][v];
+    }
+    __syncthreads();
+    if (mh == 0) {
+      const float m1 = s_pm[wc][lane], l1 = s_pl[wc][lane];
+      const float mx = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mx);
+      const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+#pragma unroll
+      for (int dl = 0; dl < ND; ++dl)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[dl][v] = acc[dl][v] * a0 + pacc[(dl * 16 + v) * 64 + lane] * a1;
+      lsum = lsum * a0 + l1 * a1;
+      m_run = mx;
+    }
+  }
   const int cb = cb0 + (cq >> 4);
-  if (busy && cb < p.NB) {
+  if (busy && mh == 0 && cb < p.NB) {
     const int64_t slot = ((int64_t)cgi * p.Gw + w) * kWideGroup + (cb - cgi * kWideGroup);
     const int64_t row = slot * 16 + (cq & 15);
 #pragma unroll
@@ -1078,7 +1120,10 @@ void launch_chunk_kernels(int kv, int D, int nh, int NB, hipStream_t s, const Ch
   const dim3 grid((unsigned)(ncg * p.Gw));
 #define CDA_CHUNK(F, DD)                                                        \
   do {                                                                          \
-    chunk_attn_wide_kernel<F, DD, PG><<<grid, 64 * kWideWaves, 0, s>>>(p);      \
+    if (NB <= kWideGroup / 2)                                                   \
+      chunk_attn_wide_kernel<F, DD, PG, 2><<<grid, 64 * kWideWaves, 0, s>>>(p); \
+    else                                                                        \
+      chunk_attn_wide_kernel<F, DD, PG, 1><<<grid, 64 * kWideWaves, 0, s>>>(p); \
     chunk_merge_commit_kernel<F, DD, PG><<<nh * (NB + 1), kBlock, 0, s>>>(      \
         p, k_pool, v_pool, comp_len, ring_keep, pos);                           \
   } while (0)
