@@ -6,7 +6,8 @@ stored after the tokens P .. P+t were appended one by one), and afterwards
 the store must be bit for bit the oracle's after M appends.  Cases cover a
 chunk longer than the window (chunk tokens leave it unkept), a ring not yet
 full (P < W), W = 0, one-token chunks, every storage format, GQA 4 and 8,
-chunks followed by chunks and by decode steps, and the paged store."""
+chunks followed by chunks and by decode steps, the paged store, many
+segments, and full-size layers of the c = 8 workloads in chunks of 64."""
 import numpy as np
 import pytest
 import torch
@@ -204,4 +205,36 @@ def test_chunk_many_segments(kv, B, Hkv):
     _check_chunk(out, lse, lay, T, 0, M, W, kv, o, "chunk")
     _oracle_append(o, lay, T, 0, M)
     compare_state(c, o, "after the chunk")
+    assert c.error_word() == 0
+
+
+@pytest.mark.parametrize("name,layer,kv", [("qwen_c8", 0, "fp8"), ("qwen_c8", 35, "fp4"),
+                                           ("llama_c8", 0, "bf16")])
+def test_chunk_config_layer(name, layer, kv):
+    """A full-size layer of the c = 8 workloads (ctx 8192, 128 new tokens) in
+    chunks of 64, as `bench.py --chunk 64` runs it (reserve = the 128 new
+    tokens): queries 0, 31 and 63 of every chunk against the oracle, the
+    store bit-exact after every chunk."""
+    cfg = workload.CONFIGS[name]
+    T, S, W, M = cfg.T, cfg.S, cfg.W, 64
+    lay = workload.make_layer(cfg, layer)
+    log(f"chunk config {name} layer {layer} {kv}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} T={T}")
+    c, _ = gpu_prefill(lay.k, lay.v, lay.keep, T, W, S, kv, with_dst=False)
+    o = oracle_prefill(lay.k, lay.v, lay.keep, T, W, S, kv)
+    d = dev()
+    ka = o.k_amax if kv != "bf16" else None
+    va = o.v_amax if kv != "bf16" else None
+    for s0 in range(0, S, M):
+        k, v, keep, q = (x.to(d) for x in _chunk_inputs(lay, T, s0, M))
+        lse = torch.empty(cfg.B, M, cfg.Hq, dtype=torch.float32, device=d)
+        out = c.chunk(k, v, keep, q, out_dtype=torch.float32, lse=lse)
+        torch.cuda.synchronize()
+        got, gl = out.cpu().numpy(), lse.cpu().numpy()
+        for t in (0, M // 2 - 1, M - 1):
+            ref, rl = oracle.attention(lay.q[s0 + t], lay.k, lay.v, lay.keep, T + s0 + t, W,
+                                       odt(kv), ka, va)
+            check_close(got[:, t], ref, f"{name} chunk {s0} query {t}")
+            check_close(gl[:, t], rl, f"{name} chunk {s0} query {t} lse", atol=1e-4, rtol=1e-5)
+        _oracle_append(o, lay, T, s0, M)
+        compare_state(c, o, f"after the chunk at {s0}")
     assert c.error_word() == 0
