@@ -75,6 +75,9 @@ def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[s
     print("|---|---:|---:|")
     for k in fetch:
         print(f"| `{k}` | {fetch[k] * fcal * 1024 / 1e6:.3f} | {write.get(k, 0) * wcal * 1024 / 1e6:.3f} |")
+    if json_path == "-":
+        return
+    # the decode attention kernel's bytes per launch, for bench.py
     attn = [k for k in fetch if k.startswith("attn_kernel")][0]
     rec = {"attn_src_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
            "kernel": attn,
@@ -82,9 +85,8 @@ def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[s
            "write_bytes_per_launch": write[attn] * wcal * 1024,
            "hbm_bytes_per_launch": (fetch[attn] * fcal + write[attn] * wcal) * 1024,
            "fetch_scale": fcal, "write_scale": wcal}
-    if json_path != "-":
-        with open(json_path, "w") as f:
-            json.dump(rec, f, indent=1)
+    with open(json_path, "w") as f:
+        json.dump(rec, f, indent=1)
 
 
 if __name__ == "__main__":
