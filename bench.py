@@ -289,7 +289,7 @@ def main():
     words = [c.error_word() for c in caches]
     if any(words):
         raise RuntimeError(f"device error words set during warm-up: {words} "
-                           f"(1 capacity, 2 pool, 4 workgroup-to-XCD mapping)")
+                           f"(1 capacity, 2 pool, 16 merge wait, 32 stale host plan)")
     log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
 
     step_ms, prefill_ms_l, decode_ms_l = [], [], []
@@ -306,7 +306,9 @@ def main():
 
     # the device state after the last step must match the host accounting
     for l in range(L):
-        got = caches[l].stored_rows().cpu().numpy().reshape(B, Hkv)
+        c = caches[l]
+        ring = np.minimum(c.pos[:B].cpu().numpy().astype(np.int64), W)
+        got = ring[:, None] + c.comp_len.cpu().numpy().astype(np.int64).reshape(B, Hkv)
         if not np.array_equal(got, nrows[l][S - 1]):
             raise RuntimeError(f"layer {l}: device stored-row counts differ from the keep mask")
         if caches[l].error_word() != 0:

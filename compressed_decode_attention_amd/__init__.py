@@ -15,14 +15,14 @@ import ctypes as C
 import torch
 
 from . import _lib
-from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_PAGES, CDA_DEVERR_POOL, CDA_DEVERR_XCD,
-                   CDA_KV_BF16, CDA_KV_FP4_E2M1, CDA_KV_FP8_E4M3, CDA_OP_APPEND, CDA_OP_COUNT,
+from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_MERGE, CDA_DEVERR_PAGES, CDA_DEVERR_PLAN,
+                   CDA_DEVERR_POOL, CDA_KV_BF16, CDA_KV_FP4_E2M1, CDA_KV_FP8_E4M3, CDA_OP_APPEND, CDA_OP_COUNT,
                    CDA_OP_PACK, CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE, CDA_OUT_BF16,
                    CDA_OUT_F32, CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
 __all__ = ["CompactKVCache", "PagedKVCache", "kv_compact", "decode_attn_compact",
            "decode_step_compact", "chunk_attn_compact", "CdaError", "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY",
-           "CDA_DEVERR_POOL", "CDA_DEVERR_XCD", "CDA_DEVERR_PAGES"]
+           "CDA_DEVERR_POOL", "CDA_DEVERR_PAGES", "CDA_DEVERR_MERGE", "CDA_DEVERR_PLAN"]
 
 _DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3, "fp4": CDA_KV_FP4_E2M1}
 _ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
@@ -36,9 +36,24 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _on(cache, what: str, *tensors) -> None:
+    """Every tensor argument must live on the cache's device: a host
+    pointer handed to a kernel would be dereferenced on the GPU."""
+    for t in tensors:
+        if t is not None and t.device != cache.device:
+            raise ValueError(f"{what}: tensors must be on {cache.device}, got {t.device}")
+
+
+def _workspace(cache, ws) -> None:
+    _on(cache, "workspace", ws)
+    if ws is not None and (ws.dtype != torch.uint8 or not ws.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor (its numel is its byte size)")
+
+
 def _compact_args(cache: "CompactKVCache", op: int, T: int = 0, reserve: int = 0,
                   scale_mode: int = 0, keep=None, k=None, v=None, dst_out=None,
                   seq_begin: int = 0, seq_count: int = 0) -> CdaCompactArgs:
+    _on(cache, "kv_compact", keep, k, v, dst_out)
     a = CdaCompactArgs()
     a.op, a.T, a.reserve, a.scale_mode = op, T, reserve, scale_mode
     a.seq_begin, a.seq_count = seq_begin, seq_count
@@ -90,6 +105,7 @@ def kv_compact(cache: "CompactKVCache", op: int, *, T: int = 0, reserve: int = 0
 
 
 def _check_attention(cache: "CompactKVCache", q, out, lse) -> None:
+    _on(cache, "attention", q, out, lse)
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3:
         raise ValueError("q must be a contiguous bfloat16 [B, Hq, D] tensor")
     B, Hq, D = q.shape
@@ -109,6 +125,7 @@ def decode_attn_compact(cache: "CompactKVCache", q: torch.Tensor, out: torch.Ten
     Hq = q.shape[1]
     if workspace is None:
         workspace = cache.workspace(Hq, split_tokens)
+    _workspace(cache, workspace)
     out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
     st = _lib.decode_attn_compact(cache.struct, _ptr(q), Hq, sm_scale, _ptr(out), out_dtype,
                                   _ptr(lse), split_tokens, _ptr(workspace),
@@ -130,6 +147,7 @@ def decode_step_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: tor
     a = _compact_args(cache, CDA_OP_APPEND, keep=keep_new, k=k_new, v=v_new)
     if workspace is None:
         workspace = cache.workspace(Hq, split_tokens)
+    _workspace(cache, workspace)
     out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
     st = _lib.decode_step_compact(cache.struct, a, _ptr(q), Hq, sm_scale, _ptr(out), out_dtype,
                                   _ptr(lse), split_tokens, _ptr(workspace),
@@ -147,6 +165,7 @@ def chunk_attn_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: torc
     [B, M, Hkv, D] bf16, keep_new [B, M, Hkv] uint8, q [B, M, Hq, D] bf16):
     query t answered as the decode step at position pos + t, out [B, M, Hq, D],
     then the M tokens appended."""
+    _on(cache, "chunk_attn_compact", k_new, v_new, keep_new, q, out, lse)
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 4:
         raise ValueError("q must be a contiguous bfloat16 [B, M, Hq, D] tensor")
     B, M, Hq, D = q.shape
@@ -170,6 +189,7 @@ def chunk_attn_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: torc
     a.stride_b, a.stride_t, a.stride_h = k_new.stride(0), k_new.stride(1), k_new.stride(2)
     if workspace is None:
         workspace = cache.chunk_workspace(Hq, M)
+    _workspace(cache, workspace)
     out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
     st = _lib.chunk_attn_compact(cache.struct, a, M, _ptr(q), Hq, sm_scale, _ptr(out), out_dtype,
                                  _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -200,7 +220,8 @@ class CompactKVCache:
         self.k_amax = torch.zeros(max(nh, 1), dtype=torch.float32, device=dev)
         self.v_amax = torch.zeros(max(nh, 1), dtype=torch.float32, device=dev)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
-        self.seg_group = torch.zeros(max(nh, 1), dtype=torch.uint8, device=dev)
+        # host copy of seg_base for the host-side work plan (set by allocate)
+        self.seg_base_host = None
         self.k_pool = None
         self.v_pool = None
         self.pool_rows = 0
@@ -222,7 +243,7 @@ class CompactKVCache:
         s.ring_keep = _ptr(self.ring_keep)
         s.k_amax, s.v_amax = _ptr(self.k_amax), _ptr(self.v_amax)
         s.err = _ptr(self.err)
-        s.seg_group = _ptr(self.seg_group)
+        s.seg_base_host = _ptr(self.seg_base_host)
 
     # ---- prefill
     def count(self, keep, T: int, reserve: int, dst_out=None) -> None:
@@ -233,8 +254,17 @@ class CompactKVCache:
         return int(self.seg_base[-1].item())
 
     def allocate(self, rows: int | None = None) -> None:
-        rows = self.rows_needed() if rows is None else rows
+        """Allocates the pools for the layout COUNT wrote (one host
+        synchronisation) and keeps a host copy of seg_base, with which the
+        attention calls plan their work on the host.  A later COUNT must
+        give the same layout (same keep, T and reserve), or allocate must be
+        called again; otherwise the attention calls flag CDA_DEVERR_PLAN."""
+        sbh = self.seg_base.cpu()
+        need = int(sbh[-1])
+        rows = need if rows is None else rows
         rows = -(-rows // CDA_SEG_ALIGN) * CDA_SEG_ALIGN
+        # the host plan describes the layout inside the pool only
+        self.seg_base_host = sbh if rows >= need else None
         nbytes = max(rows, 1) * self.row_bytes
         self.k_pool = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.v_pool = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
@@ -301,33 +331,6 @@ class CompactKVCache:
     # ---- inspection (synchronise)
     def error_word(self) -> int:
         return int(self.err.item())
-
-    def stored_rows(self) -> torch.Tensor:
-        ring = torch.clamp(self.pos[: self.B].to(torch.int64), max=self.W)
-        return ring.repeat_interleave(self.Hkv) + self.comp_len.to(torch.int64)
-
-    def v_rows(self) -> torch.Tensor:
-        """The V pool as [pool_rows, row_bytes] bytes in row order (a gather
-        of the column-major tiles, for inspection and tests; FP4 rows hold
-        element d in the low nibble of byte d / 2 for even d)."""
-        D, rows = self.D, self.pool_rows
-        if self.kv_dtype == "fp4":
-            t = self.v_pool[: rows * D // 2].view(-1, D, CDA_SEG_ALIGN // 2)   # [tile, d, byte]
-            codes = torch.stack([t & 15, t >> 4], dim=-1).reshape(-1, D, CDA_SEG_ALIGN)
-            codes = codes.permute(0, 2, 1)                                     # [tile, r, d]
-            return (codes[..., 0::2] | (codes[..., 1::2] << 4)).reshape(rows, D // 2)
-        e = self.row_bytes // D
-        t = self.v_pool[: rows * D * e].view(-1, D, CDA_SEG_ALIGN, e)
-        return t.permute(0, 2, 1, 3).reshape(rows, D * e)
-
-    def k_rows(self) -> torch.Tensor:
-        """The K pool as [pool_rows, row_bytes] bytes in row order (undoes
-        the in-tile chunk permutation described in include/cda.h)."""
-        rb = self.row_bytes
-        kl = rb // 64
-        t = self.k_pool[: self.pool_rows * rb].view(-1, 4, kl, 4, 4, 4, 16)
-        # [tile, m, j, kg, gh, gl, byte] -> [tile, gh, m, gl, j, kg, byte]
-        return t.permute(0, 4, 1, 5, 2, 3, 6).reshape(self.pool_rows, rb)
 
 
 class PagedKVCache(CompactKVCache):
@@ -408,12 +411,3 @@ class PagedKVCache(CompactKVCache):
         """Page tables as [B*Hkv, max_pages] (CPU)."""
         return self.page_table[: self.B * self.Hkv * self.max_pages].view(
             self.B * self.Hkv, self.max_pages).cpu()
-
-    def segment_rows(self, i: int, rows: int):
-        """Rows [0, rows) of segment i as (K bytes, V bytes), each
-        [rows, row_bytes], gathered through its page table."""
-        pt = self.pages()[i]
-        idx = torch.arange(rows)
-        pool_row = (pt[idx // CDA_SEG_ALIGN].to(torch.int64) * CDA_SEG_ALIGN +
-                    idx % CDA_SEG_ALIGN).to(self.device)
-        return self.k_rows()[pool_row], self.v_rows()[pool_row]

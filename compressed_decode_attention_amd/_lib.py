@@ -13,12 +13,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcda_hip.so")
 
 CDA_OK, CDA_ERR_INVALID_ARG, CDA_ERR_UNSUPPORTED, CDA_ERR_WORKSPACE, CDA_ERR_HIP = range(5)
-CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_XCD, CDA_DEVERR_PAGES = 1, 2, 4, 8
+CDA_DEVERR_CAPACITY, CDA_DEVERR_POOL, CDA_DEVERR_PAGES = 1, 2, 8
+CDA_DEVERR_MERGE, CDA_DEVERR_PLAN = 16, 32
 CDA_KV_BF16, CDA_KV_FP8_E4M3, CDA_KV_FP4_E2M1 = 0, 1, 2
 CDA_OUT_BF16, CDA_OUT_F32 = 0, 1
 CDA_OP_COUNT, CDA_OP_PACK, CDA_OP_APPEND = 0, 1, 2
 CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE = 3, 4, 5
-CDA_VERSION = 2       # the struct layouts below are those of this version
+CDA_VERSION = 3       # the struct layouts below are those of this version
 CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16
 CDA_MAX_CHUNK = 64
@@ -39,7 +40,7 @@ class CdaKvCache(C.Structure):
         ("seg_base", C.c_void_p), ("seg_cap", C.c_void_p), ("comp_len", C.c_void_p),
         ("pos", C.c_void_p), ("ring_keep", C.c_void_p),
         ("k_amax", C.c_void_p), ("v_amax", C.c_void_p), ("err", C.c_void_p),
-        ("seg_group", C.c_void_p),
+        ("seg_base_host", C.c_void_p),
         ("page_table", C.c_void_p), ("max_pages", C.c_int32), ("reserved1", C.c_int32),
         ("free_pages", C.c_void_p), ("free_top", C.c_void_p),
     ]

@@ -9,8 +9,8 @@
 namespace {
 
 constexpr int64_t kLargePoolRows = 1 << 16;
-constexpr int kGroups = 8;           // XCD groups of the attention's work map
-constexpr int kResidentPerGroup = 32;  // 8-wave workgroups one XCD keeps resident (one per CU)
+constexpr double kResidentUnits = 248;  // 8-wave attention workgroups resident at once
+                                        // (one per CU of 256, less a few for unevenness)
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -67,21 +67,31 @@ int32_t check_bf16_rows(const void* k, const void* v, int64_t sb, int64_t st, in
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? CDA_OK : CDA_ERR_HIP; }
 
-// Default work-unit size in 64-row tiles.  One unit is one workgroup, and
-// the units of a group all run on one XCD, which keeps one 8-wave workgroup
-// per CU resident: a group with more than 32 units starts its last ones a
-// whole unit late, which costs about half again the layer's time.  The
-// estimate of the units per group is the pool's tiles / tpu plus half a unit
-// of rounding per segment, spread over the 8 groups, plus one for the
-// unevenness of the group map (pool_rows counts capacity, so it errs high).
-// Small pools that fit at 4 tiles keep 4-tile units (4-wave workgroups, more
-// of them in flight); otherwise the smallest 8-wave unit that fits.  When
-// none fits (hundreds of segments) the extra rounds are unavoidable and
-// 8-tile units do the least work per round.
+// The optional host copy of seg_base (contiguous store): non-decreasing
+// multiples of 64 starting at 0, the last entry inside the pool.
+int32_t check_seg_base_host(const cda_kv_cache* c) {
+  if (!c->seg_base_host || c->page_table) return CDA_OK;
+  const int64_t nh = (int64_t)c->B * c->Hkv;
+  const int64_t* s = c->seg_base_host;
+  if (s[0] != 0 || s[nh] > c->pool_rows) return CDA_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < nh; ++i)
+    if (s[i + 1] < s[i] || s[i + 1] % CDA_SEG_ALIGN != 0) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+// Default work-unit size in 64-row tiles.  One unit is one workgroup; the
+// attention kernels keep one 8-wave workgroup per CU resident, so with more
+// units than that the last ones start a whole unit late, which costs about
+// half again the layer's time.  The estimate of the units is the pool's
+// tiles / tpu plus half a unit of rounding per segment (pool_rows counts
+// capacity, so it errs high).  Small pools that fit at 4 tiles keep 4-tile
+// units (4-wave workgroups, more of them in flight); otherwise the smallest
+// 8-wave unit that fits.  When none fits (hundreds of segments) the extra
+// rounds are unavoidable and 8-tile units do the least work per round.
 int default_tpu(const cda_kv_cache* c) {
   const double tiles = (double)c->pool_rows / CDA_SEG_ALIGN;
   const double nh = (double)c->B * c->Hkv;
-  const auto fits = [&](int t) { return (tiles / t + nh / 2) / kGroups + 1 <= kResidentPerGroup; };
+  const auto fits = [&](int t) { return tiles / t + nh / 2 <= kResidentUnits; };
   if (c->pool_rows < kLargePoolRows && fits(4)) return 4;
   for (const int t : {8, 12, 16, 24, 32, 48, 64})
     if (fits(t)) return t;
@@ -166,6 +176,7 @@ int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* 
     if (!q || !out || !aligned(q, 16) || !aligned(out, 4)) return CDA_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return CDA_ERR_INVALID_ARG;
   }
+  if ((st = check_seg_base_host(c)) != CDA_OK) return st;
   *tpu = tiles_per_unit(c, split_tokens);
   const size_t need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, *tpu);
   if (workspace_bytes < need) return CDA_ERR_WORKSPACE;

@@ -6,34 +6,39 @@
 // matrix-vector products): for every sequence b and query head j, softmax
 // attention of q[b, j] over the n_i stored rows of its KV head's segment.
 //
-// Work split.  Each segment's rows [0, n_i) are cut into 64-row tiles, and
-// tiles into work units of `tpu` tiles; one workgroup (4 or 8 waves) takes
-// one unit at a time and each wave one tile at a time.  Every wave derives
-// the unit -> (segment, tiles) map itself from pos / comp_len / seg_cap
-// (lane l looks at one segment, a wave-wide scan of unit counts finds the
-// segment holding the unit), so the host needs no copy of the lengths and
-// no workgroup barrier delays the K/V loads.  A segment with one unit writes
-// its output directly; otherwise each unit writes an unnormalised partial
-// (m, l, o) and counts itself in with an atomic, and the last unit of the
-// segment to finish combines all of them with a log-sum-exp merge and resets
-// the counter (so the counters are zero between calls).
+// Work split.  Each segment's rows are cut into 64-row tiles, and tiles into
+// work units of `tpu` tiles; one workgroup (4 or 8 waves) takes one unit and
+// each wave one tile at a time.  The unit of workgroup w comes from one of
+// two plans:
+//   - host plan: the caller gave a host copy of seg_base, so the launcher
+//     lists the units of every segment's capacity (its seg_base span) in the
+//     kernel arguments, two words per unit.  A workgroup reads its entry
+//     with its other arguments and issues the loads of its first tiles
+//     before it has read any of the segment's metadata; tiles past the rows
+//     holding data are read too and masked out (they lie inside the
+//     segment's span, hence inside the pool).
+//   - device plan: every wave derives the unit -> (segment, tiles) map from
+//     pos / comp_len / seg_cap (lane l looks at one segment, a wave-wide scan
+//     of unit counts finds the segment holding unit w), one round trip of
+//     metadata loads before the first tile load.  Used for the paged store,
+//     without the host copy, or when the plan does not fit.
+// A segment with one unit writes its output directly.  Otherwise every unit
+// stores an unnormalised partial (m, l, o) and counts itself in with an
+// atomic; the last unit of the segment to do so merges all partials with a
+// log-sum-exp merge and resets the counter and the partial slots.
 //
-// XCD-local mode.  The dispatcher hands consecutive workgroups to the XCDs
-// round robin: workgroup w runs on XCD (w + c) mod (number of XCDs), with a
-// start c fixed for the dispatch (0 for a direct launch; graph replays have
-// shown other values).  When that number divides 8, the workgroups
-// w = 8k + r of one residue r share one XCD and so one L2, whatever c is.
-// The units of segment i are given only to the workgroups of one residue,
-// its group (seg_group[i] when COUNT has written the map, which evens out
-// the rows per group, else i mod 8): partials are plain stores and the
-// merge reads them from that L2.  An XCD keeps one 8-wave workgroup per CU
-// resident (32 at a time), so a group with more units than that finishes
-// its last ones a whole unit later; the balanced map keeps groups under it.
-// Workgroup w walks units k = w/8, w/8 + P, ... of its group's segments.
-// Each partial carries the XCD it was written on; the merging workgroup
-// sets CDA_DEVERR_XCD if one differs from its own.  Otherwise (XCD count not
-// a divisor of 8) every workgroup takes one unit of the global list and
-// partials go through agent-scope (device-coherent) stores and loads.
+// Partials and their merge.  Partial words are stored as the bitwise NOT of
+// their f32 bit patterns (0xFFFFFFFF, a NaN, is first replaced by another
+// NaN), with device-coherent 8-byte stores, so a word of zero means "not yet
+// written" -- the workspace is zero between calls.  A unit does not wait
+// for its stores to complete before it counts itself in: the merging unit
+// polls each word until it is non-zero (every store it waits for has been
+// issued by a running wave, so the wait is short; the number of polls is
+// bounded, CDA_DEVERR_MERGE past it), then writes zeros back.  Nothing
+// depends on which XCD or CU a workgroup runs on.  The merge folds the
+// partials in unit order and the merging unit substitutes its own values
+// from registers at its own position, so the result does not depend on
+// which unit merges.
 //
 // Inside a wave, the G query rows of the KV head (G <= 16) are the N = 16
 // columns of two MFMA products per tile:
@@ -64,7 +69,7 @@
 //     the ones now in the ring row);
 //   - the new token is one more (logit, value) pair, formed from the BF16
 //     input with the frozen scales by wave 0 of the unit that holds the
-//     tile of its row, after that unit's tiles are done; the workgroup's
+//     tile of its row, during that wave's first tile; the workgroup's
 //     combine folds it in with the waves' partial states;
 //   - the same wave then copies the leaving token's row to the compact tail
 //     (if it moves) and writes the new token's row; every load of the tile
@@ -81,6 +86,9 @@
 //     writes pos[b] (read by the units of all of them).
 //   - every counter sits on a 128-byte line of its own: atomics on one line
 //     are performed one after another.
+#include <algorithm>
+#include <type_traits>
+
 #include "attn_common.h"
 #include "cda_device.h"
 #include "cda_launch.h"
@@ -88,9 +96,10 @@
 namespace cda {
 namespace {
 
-constexpr int kMergeBatch = 4;   // partials loaded per round trip in the merge
-constexpr int kXcdGroups = 8;    // segment groups of the XCD-local mode
-constexpr int kCounterStride = 32;   // ints between counters: one 128-byte line each
+constexpr int kMergeBatch = 4;        // partials loaded per round trip in the merge
+constexpr int kCounterStride = 32;    // ints between counters: one 128-byte line each
+constexpr int kMergePolls = 1 << 20;  // polls of one batch of partials before giving up
+constexpr int kMaxPlanUnits = 512;    // units a host plan carries in the kernel arguments (4 KB)
 
 struct AttnParams {
   uint8_t* k_pool;
@@ -106,11 +115,10 @@ struct AttnParams {
   void* out;
   float* lse;
   int32_t* err;
-  float* part_o;       // [slots][G][D]
-  float* part_ml;      // [slots][G][4]: m, l, XCD of the writer, unused
+  uint32_t* part_o;    // [slots][G][D] partial o, each word stored as ~bits
+  uint32_t* part_ml;   // [slots][G][2] partial (m, l), likewise
   int32_t* sem;        // [nh] (stride kCounterStride): units of the segment finished so
                        // far (0 between calls)
-  const uint8_t* seg_group;   // XCD-local mode: group of each segment, or NULL (i mod 8)
   // decode step only
   int32_t* seqcnt;     // [B] (stride kCounterStride): segments of the sequence done
   uint8_t* ring_keep;
@@ -119,18 +127,29 @@ struct AttnParams {
   int64_t new_sb, new_sh;
   const uint8_t* keep_new; // [nh]
   int Hkv, G, Hq, W, nh, tpu, out_f32;
-  int per_xcd;         // XCD-local mode: workgroups per segment group
   float sm_scale;
-  // paged store only (last, so that the other fields keep their offsets)
+  // paged store only
   const int32_t* page_table;   // [nh][max_pages]
   int max_pages, n_pages;
 };
+
+// Host plan: unit w of the launch is the unit of workgroup w.
+//   u[2w]      pool tile of the unit's first tile (0 for a unit without tiles)
+//   u[2w + 1]  segment (bits 0-15) | index of the unit in its segment (16-20)
+//              | units of the segment - 1 (21-25) | tiles of the unit (26-31)
+struct HostPlan {
+  uint32_t u[2 * kMaxPlanUnits];
+};
+struct NoPlan {
+  int unused;
+};
+template <bool HP>
+using PlanArg = typename std::conditional<HP, HostPlan, NoPlan>::type;
 
 __device__ __forceinline__ int units_of(int n, int tpu) {
   const int tiles = (n + kTile - 1) / kTile;
   return max(1, (tiles + tpu - 1) / tpu);
 }
-
 
 // Final output of 4 consecutive d of query row gg of segment (b, h).
 __device__ __forceinline__ void write_final4(const AttnParams& p, int b, int h, int gg, int d4,
@@ -147,30 +166,26 @@ __device__ __forceinline__ void write_final4(const AttnParams& p, int b, int h, 
   if (d4 == 0 && p.lse) p.lse[row] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
-// Partials: XCD-local mode keeps them in the shared L2 of the XCD (plain
-// 16-byte stores and loads); otherwise they are device-coherent
-// (agent-scope stores and loads, one per dword).
-template <bool XL>
-__device__ __forceinline__ void store_part4(float* a, f32x4 v) {
-  if (XL) {
-    *reinterpret_cast<f32x4*>(a) = v;
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) __hip_atomic_store(a + c, v[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+// Partial words: the bitwise NOT of the f32 bit pattern, so that zero means
+// "not written" (the one pattern that would store as zero, 0xFFFFFFFF, is a
+// NaN and is stored as the NaN 0x7FFFFFFF instead).
+__device__ __forceinline__ uint32_t enc_word(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return ~(u == 0xFFFFFFFFu ? 0x7FFFFFFFu : u);
 }
-template <bool XL>
-__device__ __forceinline__ float load_part1(const float* a) {
-  return XL ? __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
-            : __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float dec_word(uint32_t w) { return __uint_as_float(~w); }
+__device__ __forceinline__ uint64_t enc2(float x, float y) {
+  return (uint64_t)enc_word(x) | ((uint64_t)enc_word(y) << 32);
 }
-template <bool XL>
-__device__ __forceinline__ f32x4 load_part4(const float* a) {
-  // XCD-local: one 16-byte load (the merging CU has not read these lines
-  // before in this kernel, so its L1 holds no stale copy)
-  if (XL) return *reinterpret_cast<const f32x4*>(a);
-  return f32x4{load_part1<XL>(a), load_part1<XL>(a + 1), load_part1<XL>(a + 2),
-               load_part1<XL>(a + 3)};
+__device__ __forceinline__ bool written2(uint64_t w) {
+  return (uint32_t)w != 0u && (uint32_t)(w >> 32) != 0u;
+}
+// Device-coherent 8-byte store and load (relaxed, agent scope).
+__device__ __forceinline__ void st_dev64(uint32_t* a, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(a), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(uint32_t* a) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wave-uniform copies of lane `src`'s value.
@@ -184,6 +199,13 @@ __device__ __forceinline__ long long lane_l(long long x, int src) {
   return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
 }
 
+// Workgroup barrier that orders LDS accesses only (no wait for outstanding
+// global memory operations).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Rows of a segment in a decode step, from its state before the append
 // (P = pos >= 0, 0 <= cl <= cap, kn = keep byte of the new token != 0).
@@ -201,29 +223,24 @@ __device__ __forceinline__ StepRows step_rows(int W, int P, int ring_slot, int c
 
 // The unit a workgroup works on: its segment and that segment's metadata.
 struct Unit {
-  int i, first, U, n;      // n: rows planned
+  int i, first, U, n;      // first: index of the segment's first unit; n: rows planned
   long long sb;
   float ka, va;            // absmax of K and V (FP8, FP4)
-  int P, cl, cap, kn;      // decode step: state before the append
+  int P, cl, cap, kn;      // state before the append (P, cl also for attention)
 };
 
-// Unit k of group grp: its segments in index order, each with
-// units_of(rows) units (rows = n_i, or W + seg_cap with APP).  With a group
-// map the group's segments are those mapped to it; otherwise they are grp,
-// grp + xs, grp + 2xs, ...  Wave-level: every wave of a workgroup calls it
-// with the same arguments and gets the same answer.  It scans all of the
-// group's segments and returns their unit count in `total`.
+// Device plan: unit k of the launch -- the segments in index order, each
+// with units_of(rows) units (rows = n_i, or W + seg_cap with APP).
+// Wave-level: every wave of a workgroup calls it with the same arguments
+// and gets the same answer.
 // Paged store (PG): no seg_base; P keeps its sign (an idle sequence, pos <
 // 0, plans no rows in a decode step).
 template <bool Q, bool APP, bool PG>
-__device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, int k, int lane,
-                                          Unit& un, int& total) {
-  const bool mapped = p.seg_group != nullptr;
-  const int x0 = mapped ? 0 : grp, st = mapped ? 1 : xs;
+__device__ __forceinline__ bool find_unit(const AttnParams& p, int k, int lane, Unit& un) {
   int carry = 0;
   bool found = false;
-  for (int base = 0; x0 + st * base < p.nh; base += 64) {
-    const int hi = x0 + st * (base + lane);
+  for (int base = 0; base < p.nh; base += 64) {
+    const int hi = base + lane;
     int Ui = 0, ni = 0, Pi = 0, cli = 0, capi = 0, kni = 0;
     long long sbi = 0;
     float ka = 0.0f, va = 0.0f;
@@ -237,12 +254,8 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
         va = p.v_amax[hi];
       }
       if (APP) kni = p.keep_new[hi] != 0;
-      // the map byte last, through a valid address either way, so that no
-      // load of this round trip waits behind it or behind a branch
-      const uint8_t gb = *(mapped ? p.seg_group + hi : reinterpret_cast<const uint8_t*>(p.seg_cap + hi));
-      const bool in_group = !mapped || (gb & 7) == grp;
       ni = APP ? ((PG && Pi < 0) ? 0 : p.W + capi) : min(p.W, max(Pi, 0)) + cli;
-      Ui = in_group ? units_of(ni, p.tpu) : 0;
+      Ui = units_of(ni, p.tpu);
     }
     int x = Ui;
 #pragma unroll
@@ -254,24 +267,21 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int grp, int xs, 
     const unsigned long long mine = __ballot(!found && hi < p.nh && k >= ex && k < ex + Ui);
     if (mine) {
       const int src = __ffsll((long long)mine) - 1;
-      un.i = x0 + st * (base + src);
+      un.i = base + src;
       un.first = lane_i(ex, src);
       un.U = lane_i(Ui, src);
       un.n = lane_i(ni, src);
       un.sb = lane_l(sbi, src);
       un.ka = lane_f(ka, src);
       un.va = lane_f(va, src);
-      if (APP) {
-        un.P = lane_i(Pi, src);
-        un.cl = lane_i(cli, src);
-        un.cap = lane_i(capi, src);
-        un.kn = lane_i(kni, src);
-      }
+      un.P = lane_i(Pi, src);
+      un.cl = lane_i(cli, src);
+      un.cap = lane_i(capi, src);
+      un.kn = lane_i(kni, src);
       found = true;
     }
     carry += lane_i(x, 63);
   }
-  total = carry;
   return found;
 }
 
@@ -323,10 +333,10 @@ __device__ __forceinline__ bool page_ok(const AttnParams& p, int pg) {
   return (unsigned)pg < (unsigned)p.n_pages;
 }
 
-
 // PG: the paged store (tiles through the page table; idle sequences).
-template <int KV, int D, bool XL, int NW, bool APP, bool PG>
-__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
+// HP: the host plan (contiguous segments only).
+template <int KV, int D, int NW, bool APP, bool PG, bool HP>
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP> plan) {
   constexpr bool FP8 = KV == kKvFP8, FP4 = KV == kKvFP4, Q = KV != kKvBF16;
   constexpr int NTH = 64 * NW;              // threads of the workgroup
   constexpr int E = FP8 ? 1 : 2;            // bytes per element (FP8, BF16)
@@ -337,6 +347,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   constexpr int VL = FP8 ? 1 : 2;           // 16-byte V loads per (lane, d tile); FP4: one 8-byte
   constexpr int EPL = D / 64;               // new-token elements per lane
   static_assert(!FP4 || D == 128, "the 4-bit store needs 64-byte K rows");
+  static_assert(!(HP && PG), "a host plan describes contiguous segments");
 
   __shared__ int s_last;
   __shared__ float s_m[NW][16], s_l[NW][16];
@@ -347,600 +358,696 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 15, kg = lane >> 4;
   const int w = blockIdx.x;
-  const int grp = XL ? (w & (kXcdGroups - 1)) : 0;
-  const int xcc = XL ? (__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15) : 0;   // HW_REG_XCC_ID
 
-  for (int k = XL ? (w / kXcdGroups) : w;; k += p.per_xcd) {
-    Unit un;
-    int total = 0;
-    if (!find_unit<Q, APP, PG>(p, grp, XL ? kXcdGroups : 1, k, lane, un, total)) break;
+  // ---- the unit: its segment, its tiles [t_begin, t_end) and its place
+  // among the units of the segment
+  Unit un;
+  int t_begin, t_end;
+  int64_t pre_row = 0;   // host plan: pool row of this wave's first tile
+  int64_t sb_dev = 0;    // host plan: seg_base[i] as the device holds it
+  int raw_pos = 0, raw_cl = 0, raw_cap = 0, raw_kn = 0;
+  if constexpr (HP) {
+    const uint32_t tile0 = plan.u[2 * w], inf = plan.u[2 * w + 1];
+    const int ui = (int)((inf >> 16) & 31u), nt = (int)(inf >> 26);
+    un.i = (int)(inf & 0xFFFFu);
+    un.U = (int)((inf >> 21) & 31u) + 1;
+    un.first = w - ui;
+    t_begin = ui * p.tpu;
+    t_end = t_begin + nt;
+    un.sb = ((int64_t)tile0 - t_begin) * kTile;
+    // a wave with no tile of its own reads the unit's first again (unused);
+    // a unit without tiles reads pool tile 0 (unused)
+    pre_row = nt > 0 ? ((int64_t)tile0 + min(wave, nt - 1)) * kTile : 0;
+    // the segment's metadata: loaded now, consumed after the first tile's
+    // loads have gone out
+    const int bb = un.i / p.Hkv;
+    raw_pos = p.pos[bb];
+    raw_cl = p.comp_len[un.i];
+    raw_cap = p.seg_cap[un.i];
+    sb_dev = p.seg_base[un.i];
+    if (Q) {
+      un.ka = p.k_amax[un.i];
+      un.va = p.v_amax[un.i];
+    }
+    if (APP) raw_kn = p.keep_new[un.i];
+  } else {
+    if (!find_unit<Q, APP, PG>(p, w, lane, un)) return;
     // every load of the plan has been used: say so, so that no later write to
     // a register it used waits for the loads issued after this point
     __builtin_amdgcn_s_waitcnt(0);
-    // whether this is the workgroup's last unit (its group has `total`
-    // units; workgroups take every per_xcd-th of them)
-    const bool last_unit = !XL || k + p.per_xcd >= total;
-    const int i = un.i, U = un.U;
-    const int b = i / p.Hkv, h = i - b * p.Hkv;
-    const int G = p.G;
-    const int64_t sb = un.sb;
-    // rows of the segment inside the pool (paged: every page is checked)
-    const int64_t in_pool = PG ? INT64_MAX : p.pool_rows - sb;
-    const int ntiles = (un.n + kTile - 1) / kTile;
-    const int t_begin = (k - un.first) * p.tpu;
-    const int t_end = min(t_begin + p.tpu, ntiles);
-    const int slot = XL ? k * kXcdGroups + grp : k;   // this unit's partial
-    const float ks = kv_scale<KV>(un.ka);
-    const float vs = kv_scale<KV>(un.va);
-    // paged store: the page of this wave's first tile, loaded before anything
-    // else so that one round trip covers it
-    int pg_next = PG ? page_of(p, i, t_begin + wave) : 0;
-    const bool idle = PG && APP && un.P < 0;   // paged: a sequence not in use
-    const int P = APP ? (PG ? max(un.P, 0) : un.P) : 0;   // contiguous: already >= 0
+    t_begin = (w - un.first) * p.tpu;
+    t_end = min(t_begin + p.tpu, (un.n + kTile - 1) / kTile);
+  }
+  const int i = un.i, U = un.U;
+  const int b = i / p.Hkv, h = i - b * p.Hkv;
+  const int G = p.G;
+  const int uidx = w - un.first;   // this unit's place among its segment's units
 
-    // ---- decode step: rows with data, the new token's row and its tile
-    int n = un.n, new_row = -1, t_own = -1;
-    const int ring_slot = (APP && p.W > 0) ? P % p.W : 0;   // ring row of P
-    if (APP) {
-      const StepRows st = step_rows(p.W, P, ring_slot, un.cl, un.cap, un.kn);
-      n = idle ? 0 : st.n_pre;
-      if (!idle && st.new_row >= 0 && st.new_row < in_pool) {
-        new_row = st.new_row;
-        t_own = new_row / kTile;
-      }
+  // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per
+  // k-step.  Columns g >= G repeat row 0: their results land in rows of the
+  // product nobody reads, and the loads stay free of any condition (nothing
+  // waits for them before the first MFMA).
+  bf16x8 qop[NK];
+  {
+    const uint16_t* qrow = p.q + (int64_t)(b * p.Hq + h * G + (g < G ? g : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + q_d0<KV>(s, kg)));
     }
-    // the unit that holds the new token's tile adds it to the segment
-    const bool owner_unit = APP && t_own >= t_begin && t_own < t_end;
-    // decode step: where the keep bit of the token leaving the ring (ring
-    // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
-    // needed, and tested only after the loads that must not wait for it.
-    const bool leaving = APP && !idle && p.W > 0 && P >= p.W;
-    // paged store, wave 0 of the owner unit: pages of the new token's row and
-    // of the compact row the leaving token may move to (same round trip as
-    // the tile's page)
-    int pg_own = -1, pg_dst = -1;
-    if (PG && owner_unit && wave == 0) {
-      pg_own = page_of(p, i, t_own);
-      pg_dst = page_of(p, i, (p.W + un.cl) / kTile);
-    }
-    const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + ring_slot : p.keep_new + i)
-                             : nullptr;
-    // ---- Q^T operand: lane (g, kg) holds 8 d-values of query row g per
-    // k-step.  Columns g >= G repeat row 0: their results land in rows of the
-    // product nobody reads, and the loads stay free of any condition (nothing
-    // waits for them before the first MFMA).
-    bf16x8 qop[NK];
-    {
-      const uint16_t* qrow = p.q + (int64_t)(b * p.Hq + h * G + (g < G ? g : 0)) * D;
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        qop[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + q_d0<KV>(s, kg)));
-      }
-    }
-    const float c1 = p.sm_scale * kLog2e * ks;
-
-    float m_run = -INFINITY, l_run = 0.0f;
-    f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-
-    // owner unit, wave 0: its slice of the new token (issued after the
-    // accumulators are set up, so that nothing before the tile loads waits
-    // for it)
-    // It also reads the ring row the new token replaces (the leaving
-    // token's row: 16-byte K chunk `lane`, V elements EPL*lane..), in case
-    // it moves to the compact tail.
-    uint32_t nk = 0, nv = 0;
-    uint32_t ox[EPL];   // kept apart: combining them would wait for the loads here
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) ox[e] = 0;
-    u32x4 okx = u32x4{0, 0, 0, 0};
-    if (owner_unit && wave == 0) {
-      const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
-      if (EPL == 2) {
-        nk = *reinterpret_cast<const uint32_t*>(p.k_new + off);
-        nv = *reinterpret_cast<const uint32_t*>(p.v_new + off);
-      } else {
-        nk = p.k_new[off];
-        nv = p.v_new[off];
-      }
-      const int rs = new_row & (kTile - 1);
-      // paged: a missing page reads tile 0 (unused: nothing is written then)
-      const int64_t trow = PG ? (page_ok(p, pg_own) ? (int64_t)pg_own * kTile : 0)
-                              : sb + (new_row - rs);
-      const uint8_t* kt = p.k_pool + trow * (int64_t)RB;
-      const uint8_t* vt = p.v_pool + trow * (int64_t)RB;
-      okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
-#pragma unroll
-      for (int e = 0; e < EPL; ++e)
-        ox[e] = FP4 ? ((uint32_t)vt[(EPL * lane + e) * (kTile / 2) + rs / 2] >> (4 * (rs & 1))) & 15u
-              : FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
-                    : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs];
-    }
-
-    bool first_tile = true;
-    // decode step, wave 0 of the unit holding the new token's tile: forms
-    // the new token from its BF16 input with the frozen scales -- its values
-    // and one logit per query row (from the q operand) into LDS, for the
-    // combine -- and returns its stored bytes.  It runs during wave 0's
-    // first tile, while that tile is in flight.
-    auto new_token = [&](uint32_t& kc, uint32_t& vc) {
-      __asm__ volatile("" : "+v"(nk), "+v"(nv));   // keeps this work below the tile loads
-      const int d0n = EPL * lane;
-      float ka = un.ka, va = un.va;
-      __asm__ volatile("" : "+v"(ka), "+v"(va));   // the divisions stay here too
-      const float kinv = kv_inv_scale<KV>(ka);
-      const float vinv = kv_inv_scale<KV>(va);
-      kc = 0;
-      vc = 0;
-      float* sn = reinterpret_cast<float*>(s_new);
-      if (FP4) {   // the lane's two elements: one K byte, two V codes (low: d0n)
-        kc = e2m1x2_from_f32(__fmul_rn(__uint_as_float(nk << 16), kinv),
-                             __fmul_rn(__uint_as_float(nk & 0xFFFF0000u), kinv));
-        vc = e2m1x2_from_f32(__fmul_rn(__uint_as_float(nv << 16), vinv),
-                             __fmul_rn(__uint_as_float(nv & 0xFFFF0000u), vinv));
-        const auto kf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(kc, 1.0f, 0);
-        const auto vf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc, 1.0f, 0);
-        sn[d0n] = kf[0];
-        sn[d0n + 1] = kf[1];
-        sn[D + d0n] = vf[0];
-        sn[D + d0n + 1] = vf[1];
-      }
-#pragma unroll
-      for (int e = 0; e < (FP4 ? 0 : EPL); ++e) {
-        const uint32_t kb = (nk >> (16 * e)) & 0xFFFFu, vb = (nv >> (16 * e)) & 0xFFFFu;
-        if (FP8) {
-          const uint32_t kq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv));
-          const uint32_t vq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
-          sn[d0n + e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kq, 1.0f, false)[0];
-          sn[D + d0n + e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vq, 1.0f, false)[0];
-          kc |= kq << (8 * e);
-          vc |= vq << (8 * e);
-        } else {
-          sn[d0n + e] = bf16_bits_to_f32(kb);
-          sn[D + d0n + e] = bf16_bits_to_f32(vb);
-          kc |= kb << (16 * e);
-          vc |= vb << (16 * e);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      float dot = 0.0f;   // lane (g, kg): its quarter of q[g] . k^
-#pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        const int d0 = q_d0<KV>(s, kg);
-        const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
-        // an opaque copy: converted here, not hoisted above the tile loads
-        // (where converting it would wait for the q loads)
-        bf16x8 qs = qop[s];
-        __asm__ volatile("" : "+v"(qs));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dot = fmaf((float)qs[e], a[e], dot);
-          dot = fmaf((float)qs[4 + e], c[e], dot);
-        }
-      }
-      dot = sum_xor32(sum_xor16(dot));
-      if (kg == 0) s_zn[g] = dot * c1;
-    };
-    uint32_t kc = 0, vc = 0;   // wave 0 of the owner unit: the new row's stored bytes
-    bool nt_done = false;
-
-    for (int t = t_begin + wave; t < t_end; t += NW) {
-      const int r0 = t * kTile;
-      const int valid = (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
-      const bool own = APP && t == t_own;   // the tile of the leaving token's row
-      if (valid <= 0) break;
-      int64_t trow = sb + r0;   // pool row of the tile
-      if (PG) {
-        const int pg = __builtin_amdgcn_readfirstlane(pg_next);
-        if (!page_ok(p, pg)) {   // a tile with data and no page: inconsistent store
-          if (lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
-          break;
-        }
-        trow = (int64_t)pg * kTile;
-      }
-      {
-        const bool full = valid == kTile;
-        // decode step: the leaving token's keep bit, issued ahead of the tile
-        int rko = 0;
-        if (APP) rko = *rkp;
-        const uint8_t* ktile = p.k_pool + trow * (int64_t)RB;
-        const uint8_t* vtile = p.v_pool + trow * (int64_t)RB;
-
-        // -- loads: K rows for the 4 token groups (each instruction 1 KB of the
-        //    permuted K tile), V columns for the NT d tiles
-        u32x4 kr[4][KL];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int j = 0; j < KL; ++j)
-            kr[m][j] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16));
-        u32x4 vr[NT][VL];
-        u32x2 vq[FP4 ? NT : 1];   // FP4: tokens 16 kg .. 16 kg + 15 of column 16 nt + g
-        if (FP4) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            vq[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-                vtile + (16 * nt + g) * (kTile / 2) + 8 * kg));
-        } else {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int j = 0; j < VL; ++j)
-              vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                  vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
-        }
-        // paged: the page of this wave's next tile, in flight with this one
-        if (PG) pg_next = page_of(p, i, t + NW);
-
-        // -- S^T = K . Q^T, 16 tokens per MFMA row block
-        f32x4 s[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          s[m] = f32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int st = 0; st < NK; ++st) {
-            bf16x8 a;
-            if (FP4) {
-              a = fp4x8_to_bf16x8(kr[m][0][st]);
-            } else if (FP8) {
-              const u32x4 v = kr[m][st >> 1];
-              a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
-            } else {
-              a = as_bf16x8(kr[m][st]);
-            }
-            s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], s[m], 0, 0, 0);
-          }
-        }
-
-        if (owner_unit && wave == 0 && first_tile) {   // while V is still in flight
-          new_token(kc, vc);
-          nt_done = true;
-        }
-
-        // -- decode step: the leaving token's row is masked unless it moves
-        //    to the compact tail; tested after QK, so that nothing before the
-        //    tile loads waits for the keep bit
-        __asm__ volatile("" : "+v"(rko));   // keeps the test from moving up
-        const bool moved_t = own && leaving && rko != 0 && un.cl < un.cap &&
-                             (PG || sb + p.W + un.cl < p.pool_rows);
-        const int mrow = (own && leaving && !moved_t) ? (new_row & (kTile - 1)) : -1;
-
-        // -- online softmax over this tile; lane (g, kg) owns tokens 16kg + 4m + r
-        float z[4][4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) z[m][r] = s[m][r] * c1;
-        if (!full || mrow >= 0) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int tok = 16 * kg + 4 * m + r;
-              if (tok >= valid || tok == mrow) z[m][r] = -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, z[m][r]);
-        tmax = max_xor32(max_xor16(tmax));
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // every logit masked so far
-        if (!first_tile) {
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-          l_run *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
-        }
-        float psum = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
-            psum += z[m][r];
-          }
-        l_run += psum;
-        m_run = m_new;
-
-        // -- rows past the segment end: zero their V bytes (P is 0 there, but
-        //    the bytes may not be finite values; every FP4 code is finite)
-        if (!FP4 && !full) {
-#pragma unroll
-          for (int j = 0; j < VL; ++j) {
-            const int lim = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;  // valid bytes
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t msk = bytes_below(lim, q);
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) vr[nt][j][q] &= msk;
-            }
-          }
-        }
-
-        // -- O^T += V^T . P^T, per d tile one MFMA (FP8, FP4) or two (BF16:
-        //    hi, lo) per 8 tokens of each lane
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          if (Q) {
-            f16x8 pf;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[e] = (_Float16)z[2 * hh + (e >> 2)][e & 3];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              f16x8 a;
-              if (FP4) {
-                a = fp4x8_to_f16x8(vq[nt][hh]);
-              } else {
-                const u32x4 v = vr[nt][0];
-                a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
-              }
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, acc[nt], 0, 0, 0);
-            }
-          } else {
-            bf16x8 phi, plo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pv = z[2 * hh + (e >> 2)][e & 3];
-              const __bf16 hi = (__bf16)pv;
-              phi[e] = hi;
-              plo[e] = (__bf16)(pv - (float)hi);
-            }
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const bf16x8 a = as_bf16x8(vr[nt][hh]);
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[nt], 0, 0, 0);
-              acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[nt], 0, 0, 0);
-            }
-          }
-        }
-        first_tile = false;
-      }
-    }
-
-    if (owner_unit && wave == 0 && !nt_done) new_token(kc, vc);   // wave 0 had no tile
-
-    // decode step: the keep bit again, for the segment's metadata (back
-    // before it is needed, after the combine or the merge)
-    const int rkc = APP ? *rkp : 0;
-
-    // ---- combine the waves of the workgroup
-    l_run = sum_xor32(sum_xor16(l_run));
-    if (kg == 0) {
-      s_m[wave][g] = m_run;
-      s_l[wave][g] = l_run;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)   // columns g >= G hold no query row
-      if (g < G) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
-    __syncthreads();
-
-    // ---- decode step, the unit holding the new token's tile: wave 0
-    // copies the leaving token's row to the compact tail if it moves and
-    // writes the new row; every tile load of the workgroup has completed
-    // (barrier above)
-    if (owner_unit && wave == 0) {
-      {
-        const int d0n = EPL * lane;
-        // the leaving token's row (ring row P mod W) moves to compact row
-        // W + cl if it is kept; read back from the pool (this wave's reads
-        // finish before the new row is written over it)
-        const int rs = new_row & (kTile - 1);
-        // paged: rows whose page is missing are not written (CDA_DEVERR_POOL)
-        const bool own_ok = !PG || page_ok(p, pg_own);
-        const bool dst_ok = !PG || page_ok(p, pg_dst);
-        const int64_t trow = PG ? (int64_t)pg_own * kTile : sb + (new_row - rs);
-        uint8_t* kt = p.k_pool + trow * (int64_t)RB;
-        uint8_t* vt = p.v_pool + trow * (int64_t)RB;
-        const bool wants_move = leaving && rkc != 0 && un.cl < un.cap;
-        const bool moved = wants_move && own_ok && dst_ok &&
-                           (PG || sb + p.W + un.cl < p.pool_rows);
-        if (PG && lane == 0 && ((wants_move && !moved) || !own_ok)) atomicOr(p.err, CDA_DEVERR_POOL);
-        if (moved) {   // from the copy read at the start of the unit
-          const int to = p.W + un.cl, rt = to & (kTile - 1);
-          const int64_t drow = PG ? (int64_t)pg_dst * kTile : sb + (to - rt);
-          uint8_t* kd = p.k_pool + drow * (int64_t)RB;
-          uint8_t* vd = p.v_pool + drow * (int64_t)RB;
-          constexpr int KC = RB / 16;   // 16-byte chunks per K row
-          if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            if (FP4)
-              nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
-            else if (FP8)
-              vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
-            else
-              reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
-          }
-        }
-        // the new row goes over the ring row: the tiles read its old bytes
-        // before the barrier above, and the copy above used the ones read at
-        // the start of the unit (unused, and harmless, if it did not move)
-        // byte of this lane's first element in the row, and the lane's bytes
-        constexpr int LB = FP4 ? EPL / 2 : EPL * E;
-        const int kb0 = FP4 ? d0n / 2 : d0n * E;
-        if (own_ok) {
-          uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
-          if (LB == 4)
-            *reinterpret_cast<uint32_t*>(kdst) = kc;
-          else if (LB == 2)
-            *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
-          else
-            *kdst = (uint8_t)kc;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) {
-            if (FP4)   // after the moved row's write, which may share the byte
-              nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
-            else if (FP8)
-              vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
-            else
-              reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
-          }
-        }
-      }
-    }
-    // decode step, single-unit segment: every wave of the workgroup has read
-    // the segment's metadata (the owner's keep bit included)
-    int seq_prev = -1;
-    if (APP && !idle && U == 1 && tid == 0) {
-      commit_segment<PG>(p, i, un, leaving && rkc != 0);
-      seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    const float sv = vs;
-    for (int e = tid; e < G * (D / 4); e += NTH) {     // (query row, 4 consecutive d)
-      const int gg = e / (D / 4), d4 = e - gg * (D / 4);
-      float M = -INFINITY;
-#pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][gg]);
-      f32x4 O = f32x4{0, 0, 0, 0};
-      float L = 0.0f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const float mw = s_m[ww][gg];
-          if (mw == -INFINITY) continue;
-          const float f = __builtin_amdgcn_exp2f(mw - M);
-          O += f * s_o[ww][gg][d4];
-          L += f * s_l[ww][gg];
-        }
-      }
-      if (owner_unit) {   // decode step: the new token's (logit, value) pair
-        const float zn = s_zn[gg];
-        const float M2 = fmaxf(M, zn);
-        const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - M2);
-        const float pn = __builtin_amdgcn_exp2f(zn - M2);
-        O = O * a + pn * s_new[D / 4 + d4];
-        L = L * a + pn;
-        M = M2;
-      }
-      if (U == 1) {
-        write_final4(p, b, h, gg, d4, D, M, L, O, sv);
-      } else {
-        store_part4<XL>(p.part_o + ((int64_t)slot * G + gg) * D + 4 * d4, O);
-        if (d4 == 0)   // (m, l, XCD of this workgroup)
-          store_part4<XL>(p.part_ml + ((int64_t)slot * G + gg) * 4,
-                          f32x4{M, L, __int_as_float(xcc), 0.0f});
-      }
-    }
-
-    if (U > 1) {
-      // ---- split segment: the last of its units to get here merges the
-      // partials.  Every wave waits for its partial stores to complete before
-      // the workgroup counts itself in.
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) {
-        int32_t* cnt = p.sem + (int64_t)i * kCounterStride;
-        const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == U - 1;
-        if (prev == U - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      if (s_last) {
-        // decode step: every unit of the segment has read its metadata
-        if (APP && !idle && tid == 0) {
-          commit_segment<PG>(p, i, un, leaving && rkc != 0);
-          seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // each thread merges 4 consecutive outputs of one query row; the
-        // (m, l) and o loads of a batch of kMergeBatch units go out together.
-        // XCD-local mode: a partial written on another XCD than this one
-        // (the workgroups of a residue not sharing an L2) sets CDA_DEVERR_XCD.
-        bool xcd_clash = false;
-        for (int e = tid; e < G * (D / 4); e += NTH) {
-          const int gg = e / (D / 4), d4 = e - gg * (D / 4);
-          float M = -INFINITY, L = 0.0f;
-          f32x4 O = f32x4{0, 0, 0, 0};
-          for (int k0 = 0; k0 < U; k0 += kMergeBatch) {
-            f32x4 ml[kMergeBatch];
-            f32x4 ov[kMergeBatch];
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {   // unconditional loads, clamped index
-              const int ku = un.first + min(k0 + j, U - 1);
-              const int64_t sl = (int64_t)(XL ? ku * kXcdGroups + grp : ku) * G + gg;
-              ml[j] = load_part4<XL>(p.part_ml + sl * 4);
-              ov[j] = load_part4<XL>(p.part_o + sl * D + 4 * d4);
-            }
-
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-              if (XL && __float_as_int(ml[j][2]) != xcc) xcd_clash = true;
-              if (k0 + j >= U) ml[j][0] = -INFINITY;
-            }
-            float Mb = M;
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, ml[j][0]);
-            if (Mb == -INFINITY) continue;
-            const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
-            O *= a;
-            L *= a;
-#pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {
-              const float f = (ml[j][0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ml[j][0] - Mb);
-              O += f * ov[j];
-              L += f * ml[j][1];
-            }
-            M = Mb;
-          }
-          write_final4(p, b, h, gg, d4, D, M, L, O, sv);
-        }
-        if (xcd_clash) atomicOr(p.err, CDA_DEVERR_XCD);
-      }
-    }
-    // decode step: the last segment of sequence b to be done writes pos[b]
-    if (APP && tid == 0 && seq_prev == p.Hkv - 1) {
-      p.pos[b] = un.P + 1;
-      __hip_atomic_store(p.seqcnt + (int64_t)b * kCounterStride, 0, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (last_unit) break;
-    // the next unit starts with nothing in flight (its first loads then wait
-    // for nothing of this one), and reuses this unit's LDS
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
 
+  // ---- one tile's loads: K rows for the 4 token groups (each instruction
+  // 1 KB of the permuted K tile), V columns for the NT d tiles
+  u32x4 kr[4][KL];
+  u32x4 vr[NT][VL];
+  u32x2 vq[FP4 ? NT : 1];   // FP4: tokens 16 kg .. 16 kg + 15 of column 16 nt + g
+  auto load_tile = [&](int64_t trow) {
+    const uint8_t* ktile = p.k_pool + trow * (int64_t)RB;
+    const uint8_t* vtile = p.v_pool + trow * (int64_t)RB;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int j = 0; j < KL; ++j)
+        kr[m][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(ktile + ((m * KL + j) << 10) + lane * 16));
+    if (FP4) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        vq[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+            vtile + (16 * nt + g) * (kTile / 2) + 8 * kg));
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int j = 0; j < VL; ++j)
+          vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
+    }
+  };
+  if (HP) load_tile(pre_row);
+
+  // host plan: the metadata, now that the first tile is in flight; a plan
+  // that does not match the device's seg_base reads nothing and flags it
+  bool plan_ok = true;
+  if (HP) {
+    __asm__ volatile("" : "+v"(raw_pos), "+v"(raw_cl), "+v"(raw_cap), "+v"(raw_kn));
+    plan_ok = sb_dev == un.sb;
+    un.P = max(raw_pos, 0);
+    un.cap = max(raw_cap, 0);
+    un.cl = min(max(raw_cl, 0), un.cap);
+    un.kn = raw_kn != 0;
+    un.n = plan_ok ? (APP ? p.W + un.cap : min(p.W, un.P) + un.cl) : 0;
+    if (!plan_ok && tid == 0) atomicOr(p.err, CDA_DEVERR_PLAN);
+  }
+  const int64_t sb = un.sb;
+  // rows of the segment inside the pool (paged: every page is checked)
+  const int64_t in_pool = PG ? INT64_MAX : (plan_ok ? p.pool_rows - sb : 0);
+  const float ks = kv_scale<KV>(un.ka);
+  const float vs = kv_scale<KV>(un.va);
+  // paged store: the page of this wave's first tile, loaded before anything
+  // else so that one round trip covers it
+  int pg_next = PG ? page_of(p, i, t_begin + wave) : 0;
+  const bool idle = PG && APP && un.P < 0;   // paged: a sequence not in use
+  const int P = (PG ? max(un.P, 0) : un.P);   // contiguous: already >= 0
+
+  // ---- rows with data (decode step: before the append), the new token's
+  // row and its tile
+  int n = HP ? (plan_ok ? min(p.W, P) + un.cl : 0) : un.n, new_row = -1, t_own = -1;
+  const int ring_slot = (APP && p.W > 0) ? P % p.W : 0;   // ring row of P
+  if (APP) {
+    const StepRows st = step_rows(p.W, P, ring_slot, un.cl, un.cap, un.kn);
+    n = (idle || !plan_ok) ? 0 : st.n_pre;
+    if (!idle && plan_ok && st.new_row >= 0 && st.new_row < in_pool) {
+      new_row = st.new_row;
+      t_own = new_row / kTile;
+    }
+  }
+  // the unit that holds the new token's tile adds it to the segment
+  const bool owner_unit = APP && t_own >= t_begin && t_own < t_end;
+  // decode step: where the keep bit of the token leaving the ring (ring
+  // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
+  // needed, and tested only after the loads that must not wait for it.
+  const bool leaving = APP && !idle && p.W > 0 && P >= p.W;
+  // paged store, wave 0 of the owner unit: pages of the new token's row and
+  // of the compact row the leaving token may move to (same round trip as
+  // the tile's page)
+  int pg_own = -1, pg_dst = -1;
+  if (PG && owner_unit && wave == 0) {
+    pg_own = page_of(p, i, t_own);
+    pg_dst = page_of(p, i, (p.W + un.cl) / kTile);
+  }
+  const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + ring_slot : p.keep_new + i)
+                           : nullptr;
+  const float c1 = p.sm_scale * kLog2e * ks;
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+
+  // owner unit, wave 0: its slice of the new token (issued after the
+  // accumulators are set up, so that nothing before the tile loads waits
+  // for it).  It also reads the ring row the new token replaces (the
+  // leaving token's row: 16-byte K chunk `lane`, V elements EPL*lane..), in
+  // case it moves to the compact tail.
+  uint32_t nk = 0, nv = 0;
+  uint32_t ox[EPL];   // kept apart: combining them would wait for the loads here
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ox[e] = 0;
+  u32x4 okx = u32x4{0, 0, 0, 0};
+  if (owner_unit && wave == 0) {
+    const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
+    if (EPL == 2) {
+      nk = *reinterpret_cast<const uint32_t*>(p.k_new + off);
+      nv = *reinterpret_cast<const uint32_t*>(p.v_new + off);
+    } else {
+      nk = p.k_new[off];
+      nv = p.v_new[off];
+    }
+    const int rs = new_row & (kTile - 1);
+    // paged: a missing page reads tile 0 (unused: nothing is written then)
+    const int64_t trow = PG ? (page_ok(p, pg_own) ? (int64_t)pg_own * kTile : 0)
+                            : sb + (new_row - rs);
+    const uint8_t* kt = p.k_pool + trow * (int64_t)RB;
+    const uint8_t* vt = p.v_pool + trow * (int64_t)RB;
+    okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      ox[e] = FP4 ? ((uint32_t)vt[(EPL * lane + e) * (kTile / 2) + rs / 2] >> (4 * (rs & 1))) & 15u
+            : FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
+                  : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs];
+  }
+
+  bool first_tile = true;
+  // decode step, wave 0 of the unit holding the new token's tile: forms
+  // the new token from its BF16 input with the frozen scales -- its values
+  // and one logit per query row (from the q operand) into LDS, for the
+  // combine -- and returns its stored bytes.  It runs during wave 0's
+  // first tile, while that tile is in flight.
+  auto new_token = [&](uint32_t& kc, uint32_t& vc) {
+    __asm__ volatile("" : "+v"(nk), "+v"(nv));   // keeps this work below the tile loads
+    const int d0n = EPL * lane;
+    float ka = un.ka, va = un.va;
+    __asm__ volatile("" : "+v"(ka), "+v"(va));   // the divisions stay here too
+    const float kinv = kv_inv_scale<KV>(ka);
+    const float vinv = kv_inv_scale<KV>(va);
+    kc = 0;
+    vc = 0;
+    float* sn = reinterpret_cast<float*>(s_new);
+    if (FP4) {   // the lane's two elements: one K byte, two V codes (low: d0n)
+      kc = e2m1x2_from_f32(__fmul_rn(__uint_as_float(nk << 16), kinv),
+                           __fmul_rn(__uint_as_float(nk & 0xFFFF0000u), kinv));
+      vc = e2m1x2_from_f32(__fmul_rn(__uint_as_float(nv << 16), vinv),
+                           __fmul_rn(__uint_as_float(nv & 0xFFFF0000u), vinv));
+      const auto kf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(kc, 1.0f, 0);
+      const auto vf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc, 1.0f, 0);
+      sn[d0n] = kf[0];
+      sn[d0n + 1] = kf[1];
+      sn[D + d0n] = vf[0];
+      sn[D + d0n + 1] = vf[1];
+    }
+#pragma unroll
+    for (int e = 0; e < (FP4 ? 0 : EPL); ++e) {
+      const uint32_t kb = (nk >> (16 * e)) & 0xFFFFu, vb = (nv >> (16 * e)) & 0xFFFFu;
+      if (FP8) {
+        const uint32_t kq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(kb), kinv));
+        const uint32_t vq = e4m3_from_f32(__fmul_rn(bf16_bits_to_f32(vb), vinv));
+        sn[d0n + e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(kq, 1.0f, false)[0];
+        sn[D + d0n + e] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(vq, 1.0f, false)[0];
+        kc |= kq << (8 * e);
+        vc |= vq << (8 * e);
+      } else {
+        sn[d0n + e] = bf16_bits_to_f32(kb);
+        sn[D + d0n + e] = bf16_bits_to_f32(vb);
+        kc |= kb << (16 * e);
+        vc |= vb << (16 * e);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    float dot = 0.0f;   // lane (g, kg): its quarter of q[g] . k^
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      const int d0 = q_d0<KV>(s, kg);
+      const f32x4 a = s_new[d0 / 4], c = s_new[d0 / 4 + 1];
+      // an opaque copy: converted here, not hoisted above the tile loads
+      // (where converting it would wait for the q loads)
+      bf16x8 qs = qop[s];
+      __asm__ volatile("" : "+v"(qs));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = fmaf((float)qs[e], a[e], dot);
+        dot = fmaf((float)qs[4 + e], c[e], dot);
+      }
+    }
+    dot = sum_xor32(sum_xor16(dot));
+    if (kg == 0) s_zn[g] = dot * c1;
+  };
+  uint32_t kc = 0, vc = 0;   // wave 0 of the owner unit: the new row's stored bytes
+  bool nt_done = false;
+
+  // ---- one tile: S = K Q^T, online softmax, O += V^T P^T.  valid: rows of
+  // the tile holding data (<= 0: all masked); own: the tile of the new
+  // token's row; rko: keep bit of the token leaving the ring.
+  auto tile_body = [&](int valid, bool own, int rko) {
+    const bool full = valid == kTile;
+    // -- S^T = K . Q^T, 16 tokens per MFMA row block
+    f32x4 s[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s[m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int st = 0; st < NK; ++st) {
+        bf16x8 a;
+        if (FP4) {
+          a = fp4x8_to_bf16x8(kr[m][0][st]);
+        } else if (FP8) {
+          const u32x4 v = kr[m][st >> 1];
+          a = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
+        } else {
+          a = as_bf16x8(kr[m][st]);
+        }
+        s[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[st], s[m], 0, 0, 0);
+      }
+    }
+
+    if (owner_unit && wave == 0 && first_tile) {   // while V is still in flight
+      new_token(kc, vc);
+      nt_done = true;
+    }
+
+    // -- decode step: the leaving token's row is masked unless it moves
+    //    to the compact tail; tested after QK, so that nothing before the
+    //    tile loads waits for the keep bit
+    __asm__ volatile("" : "+v"(rko));   // keeps the test from moving up
+    const bool moved_t = own && leaving && rko != 0 && un.cl < un.cap &&
+                         (PG || sb + p.W + un.cl < p.pool_rows);
+    const int mrow = (own && leaving && !moved_t) ? (new_row & (kTile - 1)) : -1;
+
+    // -- online softmax over this tile; lane (g, kg) owns tokens 16kg + 4m + r
+    float z[4][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[m][r] = s[m][r] * c1;
+    if (!full || mrow >= 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = 16 * kg + 4 * m + r;
+          if (tok >= valid || tok == mrow) z[m][r] = -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, z[m][r]);
+    tmax = max_xor32(max_xor16(tmax));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // every logit masked so far
+    if (!first_tile) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] *= alpha;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[m][r] = __builtin_amdgcn_exp2f(z[m][r] - m_use);
+        psum += z[m][r];
+      }
+    l_run += psum;
+    m_run = m_new;
+
+    // -- rows past the segment end: zero their V bytes (P is 0 there, but
+    //    the bytes may not be finite values; every FP4 code is finite)
+    if (!FP4 && !full) {
+#pragma unroll
+      for (int j = 0; j < VL; ++j) {
+        const int lim = min(max(valid - 16 * kg - 8 * j, 0), 16 / VL) * E;  // valid bytes
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t msk = bytes_below(lim, q);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) vr[nt][j][q] &= msk;
+        }
+      }
+    }
+
+    // -- O^T += V^T . P^T, per d tile one MFMA (FP8, FP4) or two (BF16:
+    //    hi, lo) per 8 tokens of each lane
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (Q) {
+        f16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (_Float16)z[2 * hh + (e >> 2)][e & 3];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          f16x8 a;
+          if (FP4) {
+            a = fp4x8_to_f16x8(vq[nt][hh]);
+          } else {
+            const u32x4 v = vr[nt][0];
+            a = hh ? fp8x8_to_f16x8(v[2], v[3]) : fp8x8_to_f16x8(v[0], v[1]);
+          }
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf, acc[nt], 0, 0, 0);
+        }
+      } else {
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = z[2 * hh + (e >> 2)][e & 3];
+          const __bf16 hi = (__bf16)pv;
+          phi[e] = hi;
+          plo[e] = (__bf16)(pv - (float)hi);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 a = as_bf16x8(vr[nt][hh]);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    first_tile = false;
+  };
+
+  int t = t_begin + wave;
+  if (HP) {
+    // the tile whose loads went out first
+    int rko = 0;
+    if (APP) rko = *rkp;   // issued after that tile's loads
+    const int valid = (int)min((int64_t)min(kTile, n - t * kTile), in_pool - (int64_t)t * kTile);
+    if (t < t_end && valid > 0) tile_body(valid, APP && t == t_own, rko);
+    t += NW;
+  }
+  for (; t < t_end; t += NW) {
+    const int r0 = t * kTile;
+    const int valid = (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
+    if (valid <= 0) break;
+    int64_t trow = sb + r0;   // pool row of the tile
+    if (PG) {
+      const int pg = __builtin_amdgcn_readfirstlane(pg_next);
+      if (!page_ok(p, pg)) {   // a tile with data and no page: inconsistent store
+        if (lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
+        break;
+      }
+      trow = (int64_t)pg * kTile;
+    }
+    // decode step: the leaving token's keep bit, issued ahead of the tile
+    int rko = 0;
+    if (APP) rko = *rkp;
+    load_tile(trow);
+    // paged: the page of this wave's next tile, in flight with this one
+    if (PG) pg_next = page_of(p, i, t + NW);
+    tile_body(valid, APP && t == t_own, rko);
+  }
+
+  if (owner_unit && wave == 0 && !nt_done) new_token(kc, vc);   // wave 0 had no tile
+
+  // decode step: the keep bit again, for the segment's metadata (back
+  // before it is needed, after the combine or the merge)
+  const int rkc = APP ? *rkp : 0;
+
+  // ---- combine the waves of the workgroup
+  l_run = sum_xor32(sum_xor16(l_run));
+  if (kg == 0) {
+    s_m[wave][g] = m_run;
+    s_l[wave][g] = l_run;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)   // columns g >= G hold no query row
+    if (g < G) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
+  lds_barrier();
+
+  // ---- decode step, the unit holding the new token's tile: wave 0
+  // copies the leaving token's row to the compact tail if it moves and
+  // writes the new row; every tile load of the workgroup has completed
+  // (barrier above)
+  if (owner_unit && wave == 0) {
+    {
+      const int d0n = EPL * lane;
+      // the leaving token's row (ring row P mod W) moves to compact row
+      // W + cl if it is kept; read back from the pool (this wave's reads
+      // finish before the new row is written over it)
+      const int rs = new_row & (kTile - 1);
+      // paged: rows whose page is missing are not written (CDA_DEVERR_POOL)
+      const bool own_ok = !PG || page_ok(p, pg_own);
+      const bool dst_ok = !PG || page_ok(p, pg_dst);
+      const int64_t trow = PG ? (int64_t)pg_own * kTile : sb + (new_row - rs);
+      uint8_t* kt = p.k_pool + trow * (int64_t)RB;
+      uint8_t* vt = p.v_pool + trow * (int64_t)RB;
+      const bool wants_move = leaving && rkc != 0 && un.cl < un.cap;
+      const bool moved = wants_move && own_ok && dst_ok &&
+                         (PG || sb + p.W + un.cl < p.pool_rows);
+      if (PG && lane == 0 && ((wants_move && !moved) || !own_ok)) atomicOr(p.err, CDA_DEVERR_POOL);
+      if (moved) {   // from the copy read at the start of the unit
+        const int to = p.W + un.cl, rt = to & (kTile - 1);
+        const int64_t drow = PG ? (int64_t)pg_dst * kTile : sb + (to - rt);
+        uint8_t* kd = p.k_pool + drow * (int64_t)RB;
+        uint8_t* vd = p.v_pool + drow * (int64_t)RB;
+        constexpr int KC = RB / 16;   // 16-byte chunks per K row
+        if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (FP4)
+            nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
+          else if (FP8)
+            vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
+          else
+            reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
+        }
+      }
+      // the new row goes over the ring row: the tiles read its old bytes
+      // before the barrier above, and the copy above used the ones read at
+      // the start of the unit (unused, and harmless, if it did not move)
+      // byte of this lane's first element in the row, and the lane's bytes
+      constexpr int LB = FP4 ? EPL / 2 : EPL * E;
+      const int kb0 = FP4 ? d0n / 2 : d0n * E;
+      if (own_ok) {
+        uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
+        if (LB == 4)
+          *reinterpret_cast<uint32_t*>(kdst) = kc;
+        else if (LB == 2)
+          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
+        else
+          *kdst = (uint8_t)kc;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          if (FP4)   // after the moved row's write, which may share the byte
+            nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
+          else if (FP8)
+            vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
+          else
+            reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
+        }
+      }
+    }
+  }
+  // decode step, single-unit segment: every wave of the workgroup has read
+  // the segment's metadata (the owner's keep bit included)
+  int seq_prev = -1;
+  if (APP && !idle && U == 1 && tid == 0) {
+    if (plan_ok) commit_segment<PG>(p, i, un, leaving && rkc != 0);
+    seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // (m, l, o) of the workgroup for query row gg and d = 4 d4 .. 4 d4 + 3:
+  // the waves' states, and the new token's (logit, value) pair in the unit
+  // that holds it
+  auto combine = [&](int gg, int d4, float& M, float& L, f32x4& O) {
+    M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][gg]);
+    O = f32x4{0, 0, 0, 0};
+    L = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = s_m[ww][gg];
+        if (mw == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(mw - M);
+        O += f * s_o[ww][gg][d4];
+        L += f * s_l[ww][gg];
+      }
+    }
+    if (owner_unit) {   // decode step: the new token's (logit, value) pair
+      const float zn = s_zn[gg];
+      const float M2 = fmaxf(M, zn);
+      const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - M2);
+      const float pn = __builtin_amdgcn_exp2f(zn - M2);
+      O = O * a + pn * s_new[D / 4 + d4];
+      L = L * a + pn;
+      M = M2;
+    }
+  };
+
+  const float sv = vs;
+  if (U == 1) {
+    for (int e = tid; e < G * (D / 4); e += NTH) {   // (query row, 4 consecutive d)
+      const int gg = e / (D / 4), d4 = e - gg * (D / 4);
+      float M, L;
+      f32x4 O;
+      combine(gg, d4, M, L, O);
+      write_final4(p, b, h, gg, d4, D, M, L, O, sv);
+    }
+  } else {
+    // ---- split segment: store this unit's partial (not waited for) and
+    // count the unit in; the last unit of the segment merges.  The partial
+    // is stored by the first threads; the counter, the commit and the merge
+    // are done by the second half of the workgroup when the items fit in
+    // half of it: a wave's wait for a load or an atomic also waits for the
+    // stores it has issued before, and these waves have issued none.
+    const int items = G * (D / 4);
+    const int moff = items <= NTH / 2 ? NTH / 2 : 0;   // first merging thread
+    const int ctid = NTH - 64;                        // counting thread (last wave)
+    for (int e = tid; e < items; e += NTH) {
+      const int gg = e / (D / 4), d4 = e - gg * (D / 4);
+      float M, L;
+      f32x4 O;
+      combine(gg, d4, M, L, O);
+      const int64_t sr = (int64_t)(un.first + uidx) * G + gg;
+      st_dev64(p.part_o + sr * D + 4 * d4, enc2(O[0], O[1]));
+      st_dev64(p.part_o + sr * D + 4 * d4 + 2, enc2(O[2], O[3]));
+      if (d4 == 0) st_dev64(p.part_ml + 2 * sr, enc2(M, L));
+    }
+    if (tid == ctid) {
+      int32_t* cnt = p.sem + (int64_t)i * kCounterStride;
+      const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == U - 1;
+      if (prev == U - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_barrier();
+    if (s_last) {
+      // decode step: every unit of the segment has read its metadata
+      if (APP && !idle && tid == ctid) {
+        if (plan_ok) commit_segment<PG>(p, i, un, leaving && rkc != 0);
+        seq_prev = __hip_atomic_fetch_add(p.seqcnt + (int64_t)b * kCounterStride, 1,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // each thread merges 4 consecutive outputs of one query row, folding
+      // the units' partials in unit order (this unit's own too, as stored,
+      // so that the result does not depend on which unit merges); the loads
+      // of a batch of kMergeBatch units go out together and are repeated
+      // until every word has arrived (the whole wave together, so that no
+      // lane reads a word another lane has already cleared)
+      bool late = false;
+      for (int e = tid - moff; e >= 0 && e < items; e += NTH) {
+        const int gg = e / (D / 4), d4 = e - gg * (D / 4);
+        float M = -INFINITY, L = 0.0f;
+        f32x4 O = f32x4{0, 0, 0, 0};
+        for (int k0 = 0; k0 < U; k0 += kMergeBatch) {
+          uint64_t ml[kMergeBatch], oa[kMergeBatch], ob[kMergeBatch];
+          for (int polls = 0;; ++polls) {
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j) {   // unconditional loads, clamped index
+              const int64_t sr = (int64_t)(un.first + min(k0 + j, U - 1)) * G + gg;
+              ml[j] = ld_dev64(p.part_ml + 2 * sr);
+              oa[j] = ld_dev64(p.part_o + sr * D + 4 * d4);
+              ob[j] = ld_dev64(p.part_o + sr * D + 4 * d4 + 2);
+            }
+            bool ok = true;
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; ++j)
+              if (k0 + j < U) ok = ok && written2(ml[j]) && written2(oa[j]) && written2(ob[j]);
+            if (__all(ok)) break;
+            if (polls >= kMergePolls) {
+              late = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          float mj[kMergeBatch];
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j)
+            mj[j] = k0 + j < U ? dec_word((uint32_t)ml[j]) : -INFINITY;
+          float Mb = M;
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, mj[j]);
+          if (Mb == -INFINITY) continue;
+          const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
+          O *= a;
+          L *= a;
+#pragma unroll
+          for (int j = 0; j < kMergeBatch; ++j) {
+            const float f = (mj[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj[j] - Mb);
+            const f32x4 oj = f32x4{dec_word((uint32_t)oa[j]), dec_word((uint32_t)(oa[j] >> 32)),
+                                   dec_word((uint32_t)ob[j]), dec_word((uint32_t)(ob[j] >> 32))};
+            O += f * oj;
+            L += f * dec_word((uint32_t)(ml[j] >> 32));
+          }
+          M = Mb;
+        }
+        write_final4(p, b, h, gg, d4, D, M, L, O, sv);
+        // the slots back to zero for the next call: every word was read
+        // non-zero above, so its store has landed before these zeros
+        for (int j = 0; j < U; ++j) {
+          const int64_t sr = (int64_t)(un.first + j) * G + gg;
+          st_dev64(p.part_o + sr * D + 4 * d4, 0);
+          st_dev64(p.part_o + sr * D + 4 * d4 + 2, 0);
+          if (d4 == 0) st_dev64(p.part_ml + 2 * sr, 0);
+        }
+      }
+      if (late) atomicOr(p.err, CDA_DEVERR_MERGE);
+    }
+  }
+  // decode step: the last segment of sequence b to be done writes pos[b]
+  if (APP && seq_prev == p.Hkv - 1) {
+    p.pos[b] = un.P + 1;
+    __hip_atomic_store(p.seqcnt + (int64_t)b * kCounterStride, 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// XCD-local mode applies when the XCD count divides the 8 segment groups.
-int device_xcds() {
-  int dev = 0, nx = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&nx, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) return 0;
-  return nx;
-}
-
-template <bool APP, bool PG>
-void launch_variant(int kv, int D, bool xl, int nw, dim3 grid, hipStream_t s, const AttnParams& p) {
-#define CDA_LAUNCH_ATTN(F, DD, X)                                                      \
-  (nw == 8 ? attn_kernel<F, DD, X, 8, APP, PG><<<grid, 512, 0, s>>>(p)                 \
-           : attn_kernel<F, DD, X, 4, APP, PG><<<grid, 256, 0, s>>>(p))
+template <bool APP, bool PG, bool HP>
+void launch_variant(int kv, int D, int nw, dim3 grid, hipStream_t s, const AttnParams& p,
+                    const PlanArg<HP>& plan) {
+#define CDA_LAUNCH_ATTN(F, DD)                                                          \
+  (nw == 8 ? attn_kernel<F, DD, 8, APP, PG, HP><<<grid, 512, 0, s>>>(p, plan)           \
+           : attn_kernel<F, DD, 4, APP, PG, HP><<<grid, 256, 0, s>>>(p, plan))
   if (kv == kKvFP4) {   // D = 128 only
-    if (xl) CDA_LAUNCH_ATTN(kKvFP4, 128, true); else CDA_LAUNCH_ATTN(kKvFP4, 128, false);
+    CDA_LAUNCH_ATTN(kKvFP4, 128);
   } else if (kv == kKvFP8) {
-    if (D == 64) {
-      if (xl) CDA_LAUNCH_ATTN(kKvFP8, 64, true); else CDA_LAUNCH_ATTN(kKvFP8, 64, false);
-    } else {
-      if (xl) CDA_LAUNCH_ATTN(kKvFP8, 128, true); else CDA_LAUNCH_ATTN(kKvFP8, 128, false);
-    }
+    if (D == 64) CDA_LAUNCH_ATTN(kKvFP8, 64); else CDA_LAUNCH_ATTN(kKvFP8, 128);
   } else {
-    if (D == 64) {
-      if (xl) CDA_LAUNCH_ATTN(kKvBF16, 64, true); else CDA_LAUNCH_ATTN(kKvBF16, 64, false);
-    } else {
-      if (xl) CDA_LAUNCH_ATTN(kKvBF16, 128, true); else CDA_LAUNCH_ATTN(kKvBF16, 128, false);
-    }
+    if (D == 64) CDA_LAUNCH_ATTN(kKvBF16, 64); else CDA_LAUNCH_ATTN(kKvBF16, 128);
   }
 #undef CDA_LAUNCH_ATTN
+}
+
+// The host plan of a contiguous store from the host copy of seg_base (its
+// consistency was checked by the caller): every segment's span of W +
+// seg_cap rows rounded to tiles, cut into units of tpu tiles (at least one
+// unit per segment).  False when it does not fit the encoding or the kernel
+// arguments; the device plan is used then.
+bool host_plan(const cda_kv_cache& c, int tpu, HostPlan& plan, int& n) {
+  const int64_t nh = (int64_t)c.B * c.Hkv;
+  if (nh > 65536 || tpu > 63 || c.pool_rows < kTile || c.pool_rows / kTile > 0xFFFFFFFFll)
+    return false;
+  const int64_t* sbh = c.seg_base_host;
+  n = 0;
+  for (int64_t i = 0; i < nh; ++i) {
+    const int64_t tiles = (sbh[i + 1] - sbh[i]) / kTile;
+    const int64_t U = std::max<int64_t>(1, (tiles + tpu - 1) / tpu);
+    if (U > 32 || n + U > kMaxPlanUnits) return false;
+    for (int64_t u = 0; u < U; ++u) {
+      const int64_t nt = std::min<int64_t>(tpu, tiles - u * tpu);
+      plan.u[2 * n] = (uint32_t)(sbh[i] / kTile + u * tpu);
+      plan.u[2 * n + 1] = (uint32_t)i | (uint32_t)(u << 16) | (uint32_t)((U - 1) << 21) |
+                          (uint32_t)(nt << 26);
+      ++n;
+    }
+  }
+  return true;
 }
 
 }  // namespace
@@ -951,15 +1058,13 @@ int64_t attn_max_units(const cda_kv_cache& c, int tpu) {
 }
 
 // Workspace: [per-segment counters][per-sequence counters] (one 128-byte
-// line each) [partial (m, l, XCD)][partial o].
-// Partial slots: an XCD-local slot is 8k + group with k below the units of
-// the group (at most all units), so 8 x the unit bound covers both modes.
+// line each) [partial (m, l) words][partial o words], one partial slot per
+// work unit.
 size_t attn_workspace_bytes(const cda_kv_cache& c, int G, int tpu) {
-  const int64_t slots = kXcdGroups * attn_max_units(c, tpu);
+  const int64_t slots = attn_max_units(c, tpu);
   const int64_t nh = (int64_t)c.B * c.Hkv;
   return align256((size_t)nh * 4 * kCounterStride) + align256((size_t)c.B * 4 * kCounterStride) +
-         align256((size_t)slots * G * 4 * 4) +
-         align256((size_t)slots * G * c.D * 4);
+         align256((size_t)slots * G * 2 * 4) + align256((size_t)slots * G * c.D * 4);
 }
 
 hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_scale, void* out,
@@ -969,7 +1074,6 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   if (nh == 0) return hipGetLastError();
   const int G = Hq / c.Hkv;
   const int64_t units = attn_max_units(c, tpu);
-  const int64_t slots = kXcdGroups * units;
   AttnParams p;
   p.k_pool = static_cast<uint8_t*>(c.k_pool);
   p.v_pool = static_cast<uint8_t*>(c.v_pool);
@@ -992,9 +1096,9 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   ws += align256((size_t)nh * 4 * kCounterStride);
   p.seqcnt = reinterpret_cast<int32_t*>(ws);
   ws += align256((size_t)c.B * 4 * kCounterStride);
-  p.part_ml = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)slots * G * 4 * 4);
-  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_ml = reinterpret_cast<uint32_t*>(ws);
+  ws += align256((size_t)units * G * 2 * 4);
+  p.part_o = reinterpret_cast<uint32_t*>(ws);
   p.ring_keep = c.ring_keep;
   p.k_new = step ? static_cast<const uint16_t*>(step->k) : nullptr;
   p.v_new = step ? static_cast<const uint16_t*>(step->v) : nullptr;
@@ -1009,24 +1113,27 @@ hipError_t launch_attn(const cda_kv_cache& c, const void* q, int Hq, float sm_sc
   p.tpu = tpu;
   p.out_f32 = out_f32;
   p.sm_scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)c.D);
-  const int nx = device_xcds();
-  const bool xl = nx > 0 && kXcdGroups % nx == 0;
-  // the group map (written by COUNT) is used for up to 512 segments; past
-  // that it is the identity i mod 8 and scanning it would only cost time
-  p.seg_group = (xl && nh <= 512) ? c.seg_group : nullptr;
-  // XCD-local: 8 groups of per_xcd workgroups, a quarter more than an even
-  // share of the unit bound; a group with more units loops over them.
-  p.per_xcd = xl ? (int)((units * 5 / 4 + kXcdGroups - 1) / kXcdGroups) : 0;
-  const dim3 grid((unsigned)(xl ? (int64_t)p.per_xcd * kXcdGroups : units));
   const int kv = c.kv_dtype;
   const int nw = tpu >= 8 ? 8 : 4;   // waves per workgroup: one tile each per pass
   const bool pg = c.page_table != nullptr;
+  if (!pg && c.seg_base_host) {
+    HostPlan plan;
+    int n = 0;
+    if (host_plan(c, tpu, plan, n)) {
+      const dim3 grid((unsigned)n);
+      if (step) launch_variant<true, false, true>(kv, c.D, nw, grid, s, p, plan);
+      else launch_variant<false, false, true>(kv, c.D, nw, grid, s, p, plan);
+      return hipGetLastError();
+    }
+  }
+  const dim3 grid((unsigned)units);
+  const NoPlan none{0};
   if (step) {
-    if (pg) launch_variant<true, true>(kv, c.D, xl, nw, grid, s, p);
-    else launch_variant<true, false>(kv, c.D, xl, nw, grid, s, p);
+    if (pg) launch_variant<true, true, false>(kv, c.D, nw, grid, s, p, none);
+    else launch_variant<true, false, false>(kv, c.D, nw, grid, s, p, none);
   } else {
-    if (pg) launch_variant<false, true>(kv, c.D, xl, nw, grid, s, p);
-    else launch_variant<false, false>(kv, c.D, xl, nw, grid, s, p);
+    if (pg) launch_variant<false, true, false>(kv, c.D, nw, grid, s, p, none);
+    else launch_variant<false, false, false>(kv, c.D, nw, grid, s, p, none);
   }
   return hipGetLastError();
 }

@@ -97,18 +97,11 @@ __device__ __forceinline__ long long block_exclusive_scan64(long long v, long lo
   return before + x - v;
 }
 
-// Segments whose attention work is spread over the 8 XCD groups by size.
-constexpr int kBalanceMax = 512;
-
-// seg_base by a prefix sum of the aligned segment sizes; then, if asked, the
-// group map: segments ranked by size in 64-row tiles (larger first, ties by
-// index) and dealt to the 8 groups in snake order (0..7, 7..0, ...), so
-// that every group gets a near-equal share of rows.
+// seg_base by a prefix sum of the aligned segment sizes.
 __global__ __launch_bounds__(kBlock) void seg_scan_kernel(
     int nh, int W, const int32_t* __restrict__ seg_cap, int64_t* __restrict__ seg_base,
-    int32_t* __restrict__ err, uint8_t* __restrict__ seg_group) {
+    int32_t* __restrict__ err) {
   __shared__ long long smem[4];
-  __shared__ int s_tiles[kBalanceMax];
   long long carry = 0;
   for (int base = 0; base < nh; base += kBlock) {
     const int i = base + threadIdx.x;
@@ -122,25 +115,6 @@ __global__ __launch_bounds__(kBlock) void seg_scan_kernel(
   if (threadIdx.x == 0) {
     seg_base[nh] = carry;
     err[0] = 0;
-  }
-  if (seg_group) {
-    if (nh <= kBalanceMax) {
-      for (int i = threadIdx.x; i < nh; i += kBlock)
-        s_tiles[i] = (int)(((long long)W + seg_cap[i] + kTile - 1) / kTile);
-      __syncthreads();
-      for (int i = threadIdx.x; i < nh; i += kBlock) {
-        const int wi = s_tiles[i];
-        int rank = 0;
-        for (int j = 0; j < nh; ++j) {
-          const int wj = s_tiles[j];
-          rank += (wj > wi) || (wj == wi && j < i);
-        }
-        const int round = rank >> 3, slot = rank & 7;
-        seg_group[i] = (uint8_t)((round & 1) ? 7 - slot : slot);
-      }
-    } else {
-      for (int i = threadIdx.x; i < nh; i += kBlock) seg_group[i] = (uint8_t)(i & 7);
-    }
   }
 }
 
@@ -672,7 +646,7 @@ __global__ __launch_bounds__(kBlock) void page_init_kernel(
     int n_pages, int nh, int max_pages, int B, int W, int32_t* __restrict__ free_pages,
     int32_t* __restrict__ free_top, int32_t* __restrict__ page_table,
     int32_t* __restrict__ comp_len, int32_t* __restrict__ seg_cap, int32_t* __restrict__ pos,
-    uint8_t* __restrict__ ring_keep, uint8_t* __restrict__ seg_group, int32_t* __restrict__ err) {
+    uint8_t* __restrict__ ring_keep, int32_t* __restrict__ err) {
   const int64_t n_pt = (int64_t)nh * max_pages, n_rk = (int64_t)nh * W;
   const int64_t n = max(max((int64_t)n_pages, n_pt), max(n_rk, (int64_t)max(nh, B)));
   for (int64_t x = (int64_t)blockIdx.x * kBlock + threadIdx.x; x < n;
@@ -683,7 +657,6 @@ __global__ __launch_bounds__(kBlock) void page_init_kernel(
     if (x < nh) {
       comp_len[x] = 0;
       seg_cap[x] = 0;
-      if (seg_group) seg_group[x] = (uint8_t)(x & 7);
     }
     if (x < B) pos[x] = -1;
     if (x == 0) {
@@ -707,7 +680,6 @@ struct PageParams {
   int32_t* comp_len;
   int32_t* pos;
   uint8_t* ring_keep;
-  uint8_t* seg_group;
   int32_t* err;
 };
 
@@ -719,9 +691,8 @@ __device__ __forceinline__ int pages_held(const PageParams& p, int i) {
   return p.pos[i / p.Hkv] >= 0 ? (p.W + max(p.seg_cap[i], 0)) / kTile : 0;
 }
 
-// One workgroup: the page bookkeeping of one operation, then the group map
-// over the pages every segment holds afterwards.  Pages are taken from the
-// top of the stack (the k-th taken is free_pages[top - 1 - k]) and returned
+// One workgroup: the page bookkeeping of one operation.  Pages are taken
+// from the top of the stack (the k-th taken is free_pages[top - 1 - k]) and returned
 // on top of it, in segment order and then row order, by prefix sums over
 // the segments: the result does not depend on thread timing.
 //   admit   segments [i0, i1) of idle sequences, comp_len from COUNT: each
@@ -736,16 +707,11 @@ __device__ __forceinline__ int pages_held(const PageParams& p, int i) {
 __global__ __launch_bounds__(kBlock) void page_kernel(PageParams p) {
   __shared__ int smem[4];
   __shared__ int s_top, s_over;
-  __shared__ int s_tiles[kBalanceMax];
   const int tid = threadIdx.x, mp = p.max_pages, W = p.W;
-  const bool balance = p.seg_group != nullptr && p.nh <= kBalanceMax;
   if (tid == 0) {
     s_top = min(max(*p.free_top, 0), p.n_pages);   // every stack index stays inside
     s_over = 0;
   }
-  // pages held before the operation (the group map's weights)
-  if (balance)
-    for (int i = tid; i < p.nh; i += kBlock) s_tiles[i] = pages_held(p, i);
   __syncthreads();
   const int top = s_top;
   int taken = 0, given = 0;   // pages taken from / returned to the stack (block totals)
@@ -782,7 +748,6 @@ __global__ __launch_bounds__(kBlock) void page_kernel(PageParams p) {
         for (int j = got; j < mp; ++j) row[j] = -1;
         p.seg_cap[i] = ok ? got * kTile - W : 0;
         if (!ok) p.comp_len[i] = 0;
-        if (balance) s_tiles[i] = got;
       }
     }
     for (int b = p.i0 / p.Hkv + tid; b < p.i1 / p.Hkv; b += kBlock) p.pos[b] = ok ? 0 : -1;
@@ -805,7 +770,6 @@ __global__ __launch_bounds__(kBlock) void page_kernel(PageParams p) {
         int32_t* row = p.page_table + (int64_t)i * mp;
         for (int j = 0; j < got; ++j) row[cur + j] = p.free_pages[top - 1 - (ex + j)];
         p.seg_cap[i] = (cur + got) * kTile - W;
-        if (balance) s_tiles[i] = cur + got;
       }
     }
     taken = min(k0, top);
@@ -827,7 +791,6 @@ __global__ __launch_bounds__(kBlock) void page_kernel(PageParams p) {
         p.seg_cap[i] = 0;
         p.comp_len[i] = 0;
         for (int r = 0; r < W; ++r) p.ring_keep[(int64_t)i * W + r] = 0;
-        if (balance) s_tiles[i] = 0;
       }
     }
     __syncthreads();   // every thread has read pos (pages_held) of the range
@@ -835,25 +798,6 @@ __global__ __launch_bounds__(kBlock) void page_kernel(PageParams p) {
     given = k0;
   }
   if (tid == 0) *p.free_top = min(top - taken + given, p.n_pages);
-
-  // ---- group map: segments ranked by pages held, dealt in snake order
-  __syncthreads();
-  if (p.seg_group) {
-    if (balance) {
-      for (int i = tid; i < p.nh; i += kBlock) {
-        const int wi = s_tiles[i];
-        int rank = 0;
-        for (int j = 0; j < p.nh; ++j) {
-          const int wj = s_tiles[j];
-          rank += (wj > wi) || (wj == wi && j < i);
-        }
-        const int round = rank >> 3, slot = rank & 7;
-        p.seg_group[i] = (uint8_t)((round & 1) ? 7 - slot : slot);
-      }
-    } else {
-      for (int i = tid; i < p.nh; i += kBlock) p.seg_group[i] = (uint8_t)(i & 7);
-    }
-  }
 }
 
 }  // namespace
@@ -884,7 +828,6 @@ PageParams page_params(const cda_kv_cache& c, int op, int b0, int nb, int reserv
   p.comp_len = c.comp_len;
   p.pos = c.pos;
   p.ring_keep = c.ring_keep;
-  p.seg_group = c.seg_group;
   p.err = c.err;
   return p;
 }
@@ -902,7 +845,7 @@ hipError_t launch_count(const cda_kv_cache& c, const cda_compact_args& a, hipStr
   if (c.page_table)
     page_kernel<<<1, kBlock, 0, s>>>(page_params(c, kPageAdmit, b0, nb, a.reserve));
   else
-    seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err, c.seg_group);
+    seg_scan_kernel<<<1, kBlock, 0, s>>>(nh, c.W, c.seg_cap, c.seg_base, c.err);
   return hipGetLastError();
 }
 
@@ -914,8 +857,7 @@ hipError_t launch_page_op(const cda_kv_cache& c, const cda_compact_args& a, hipS
     const int grid = (int)std::min<int64_t>(std::max<int64_t>((n + kBlock - 1) / kBlock, 1), 1024);
     page_init_kernel<<<grid, kBlock, 0, s>>>((int)(c.pool_rows / kTile), nh, c.max_pages, c.B,
                                              c.W, c.free_pages, c.free_top, c.page_table,
-                                             c.comp_len, c.seg_cap, c.pos, c.ring_keep,
-                                             c.seg_group, c.err);
+                                             c.comp_len, c.seg_cap, c.pos, c.ring_keep, c.err);
   } else {
     int b0, nb;
     seq_range(c, a, b0, nb);

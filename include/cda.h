@@ -110,7 +110,7 @@
 extern "C" {
 #endif
 
-#define CDA_VERSION 2
+#define CDA_VERSION 3
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
 #define CDA_MAX_CHUNK 64        /* largest chunk of chunk_attn_compact */
@@ -131,10 +131,13 @@ enum cda_status {
 #define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written */
 #define CDA_DEVERR_PAGES 8      /* paged COUNT / REFILL: not enough free pages, or a segment
                                    would need more than max_pages (see the paged store) */
-#define CDA_DEVERR_XCD 4        /* attention: the workgroups w of one residue w mod 8 did not all
-                                   run on one XCD, which the XCD-local merge of split heads
-                                   needs (the dispatcher deals workgroups to the XCDs round
-                                   robin); that call's outputs are not reliable */
+#define CDA_DEVERR_MERGE 16     /* attention: a split segment's partial results did not all
+                                   arrive within the merge's bounded wait (a bug or a wedged
+                                   device, never expected); that call's outputs are not reliable */
+#define CDA_DEVERR_PLAN 32      /* attention: seg_base_host differs from the device's seg_base
+                                   (a COUNT changed the layout after the host copy was taken);
+                                   the segments concerned read nothing and are not appended to,
+                                   so that call's outputs and the store are not reliable */
 
 enum cda_kv_dtype { CDA_KV_BF16 = 0, CDA_KV_FP8_E4M3 = 1, CDA_KV_FP4_E2M1 = 2 };
 enum cda_out_dtype { CDA_OUT_BF16 = 0, CDA_OUT_F32 = 1 };
@@ -164,12 +167,15 @@ typedef struct cda_kv_cache {
     float *k_amax;      /* [B*Hkv]; FP8/FP4 absmax of K (PACK computes or takes it) */
     float *v_amax;      /* [B*Hkv]; FP8/FP4 absmax of V */
     int32_t *err;       /* [1]; device error word, CDA_DEVERR_* bits; COUNT clears it */
-    uint8_t *seg_group; /* optional [B*Hkv] (may be NULL); written by COUNT: the group (0..7)
-                           of workgroups, one XCD's worth, that takes the attention work of
-                           each segment, chosen to even out the capacity W + seg_cap per group.
-                           NULL, or more than 512 segments: segment i goes to group i mod 8.
-                           Scheduling only: results do not depend on it.  Paged store:
-                           rewritten by COUNT, REFILL and RELEASE, over the pages held */
+    const int64_t *seg_base_host; /* optional HOST memory (may be NULL): a copy of seg_base
+                           [0 .. B*Hkv] as COUNT wrote it, contiguous segments only.  With it,
+                           decode_attn_compact and decode_step_compact plan their work units on
+                           the host and pass the plan with the kernel arguments, so the kernel
+                           reads K and V before the segment metadata has arrived.  Checked on
+                           every call (non-decreasing multiples of 64, last entry <= pool_rows,
+                           CDA_ERR_INVALID_ARG otherwise); a copy that no longer matches the
+                           device's seg_base sets CDA_DEVERR_PLAN.  Ignored by the paged store
+                           and by kv_compact */
     int32_t *page_table;   /* NULL: contiguous segments.  Else the paged store:
                               [B*Hkv*max_pages] page ids, -1 = none */
     int32_t max_pages;     /* paged: page-table entries per segment, >= 1 */
@@ -209,7 +215,7 @@ typedef struct cda_compact_args {
  * CDA_OP_COUNT: per segment, counts kept positions p <= T-1-W (comp_len),
  *   sets seg_cap = comp_len + reserve, and writes seg_base by an exclusive
  *   prefix sum of the aligned segment sizes; seg_base[B*Hkv] is the number
- *   of pool rows to allocate.  Optionally writes dst_out and seg_group.
+ *   of pool rows to allocate.  Optionally writes dst_out.
  *   Clears *err.
  *   Reads keep; needs seg_base, seg_cap, comp_len, err (pools may be NULL).
  * CDA_OP_PACK: after COUNT (same keep, T), writes every stored prefill row
@@ -248,20 +254,21 @@ int32_t kv_compact(const cda_kv_cache *cache, const cda_compact_args *args, void
  *                multiple of 64; 0 = default, chosen from pool_rows and
  *                B*Hkv: the smallest of 256 (pools under 65536 rows only),
  *                512, 768, 1024, 1536, ... 4096 for which the estimated
- *                units per XCD group, (pool_rows/split + B*Hkv/2)/8 + 1,
- *                stay at or below 32 (one resident workgroup per CU of an
- *                XCD); 512 when none does.  Heads longer than one unit are
- *                split and their partials merged.
- *   The call reads the device's XCD count (hipDeviceGetAttribute) on the
- *   current device; the attention may set CDA_DEVERR_XCD in cache->err.
+ *                number of units, pool_rows/split + B*Hkv/2, stays at or
+ *                below 248 (about one resident 8-wave workgroup per compute
+ *                unit); 512 when none does.  Segments longer than one unit
+ *                are split and their partials merged.  With seg_base_host
+ *                the units cover each segment's capacity (W + seg_cap
+ *                rows), otherwise the rows holding data (decode_step: the
+ *                capacity as well).
  *   workspace    device scratch of at least cda_attn_workspace_bytes()
- *                bytes: a grid counter and one completion counter per
- *                segment, then the partial states of split segments.  It must be zero-filled
- *                before its first use; every completed call leaves the
- *                counters at zero again, so one workspace can serve any
- *                later call (any cache, any split) ordered after it on a
- *                stream.  Calls that may run concurrently need separate
- *                workspaces.
+ *                bytes, 16-byte aligned: one completion counter per segment
+ *                and per sequence, then one partial-result slot per work
+ *                unit.  It must be zero-filled before its first use; every
+ *                completed call leaves it zero-filled again, so one
+ *                workspace can serve any later call (any cache, any split)
+ *                ordered after it on a stream.  Calls that may run
+ *                concurrently need separate workspaces.
  */
 int32_t decode_attn_compact(const cda_kv_cache *cache, const void *q, int32_t Hq,
                             float sm_scale, void *out, int32_t out_dtype, float *lse,

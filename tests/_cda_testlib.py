@@ -67,8 +67,8 @@ def compare_state(c: CompactKVCache, o: oracle.OracleCache, what: str = ""):
         assert np.array_equal(np.isnan(ga), np.isnan(oa)) and np.array_equal(ga[~np.isnan(ga)], oa[~np.isnan(oa)]), what + " k_amax"
         ga, oa = c.v_amax.cpu().numpy()[:nh], o.v_amax
         assert np.array_equal(np.isnan(ga), np.isnan(oa)) and np.array_equal(ga[~np.isnan(ga)], oa[~np.isnan(oa)]), what + " v_amax"
-    kr = c.k_rows().cpu().numpy()
-    vr = c.v_rows().cpu().numpy()
+    kr = k_rows(c).cpu().numpy()
+    vr = v_rows(c).cpu().numpy()
     n = o.stored_rows()
     for i in range(nh):
         a = int(o.seg_base[i])
@@ -80,14 +80,6 @@ def compare_state(c: CompactKVCache, o: oracle.OracleCache, what: str = ""):
         if not np.array_equal(vr[a:a + n[i]], o.v_pool[a:a + n[i]]):
             bad = np.nonzero(np.any(vr[a:a + n[i]] != o.v_pool[a:a + n[i]], axis=1))[0]
             raise AssertionError(f"{what} V rows differ in segment {i}: rows {bad[:8]}")
-
-
-def counter_bytes(B: int, Hkv: int) -> int:
-    """Bytes at the start of an attention workspace that hold the
-    completion counters (one 128-byte line per segment, then one per
-    sequence, each region 256-byte aligned); zero between calls."""
-    a = lambda x: -(-x // 256) * 256
-    return a(B * Hkv * 128) + a(B * 128)
 
 
 def check_close(got, ref, what="", atol=ATOL, rtol=RTOL):
@@ -104,3 +96,46 @@ def check_close(got, ref, what="", atol=ATOL, rtol=RTOL):
                              f"max abs err {err.max():.3e}; first {idx.tolist()} "
                              f"got {got[bad][:5]} want {ref[bad][:5]}")
     return float(err.max()) if err.size else 0.0
+
+
+# ---- reading a store back (host-side inspection; synchronises)
+
+def stored_rows(c) -> torch.Tensor:
+    """Rows holding data per segment: min(W, pos) + comp_len."""
+    ring = torch.clamp(c.pos[: c.B].to(torch.int64), max=c.W)
+    return ring.repeat_interleave(c.Hkv) + c.comp_len.to(torch.int64)
+
+
+def v_rows(c) -> torch.Tensor:
+    """The V pool as [pool_rows, row_bytes] bytes in row order (a gather of
+    the column-major tiles; FP4 rows hold element d in the low nibble of
+    byte d / 2 for even d)."""
+    D, rows = c.D, c.pool_rows
+    if c.kv_dtype == "fp4":
+        t = c.v_pool[: rows * D // 2].view(-1, D, CDA_SEG_ALIGN // 2)   # [tile, d, byte]
+        codes = torch.stack([t & 15, t >> 4], dim=-1).reshape(-1, D, CDA_SEG_ALIGN)
+        codes = codes.permute(0, 2, 1)                                  # [tile, r, d]
+        return (codes[..., 0::2] | (codes[..., 1::2] << 4)).reshape(rows, D // 2)
+    e = c.row_bytes // D
+    t = c.v_pool[: rows * D * e].view(-1, D, CDA_SEG_ALIGN, e)
+    return t.permute(0, 2, 1, 3).reshape(rows, D * e)
+
+
+def k_rows(c) -> torch.Tensor:
+    """The K pool as [pool_rows, row_bytes] bytes in row order (undoes the
+    in-tile chunk permutation described in include/cda.h)."""
+    rb = c.row_bytes
+    kl = rb // 64
+    t = c.k_pool[: c.pool_rows * rb].view(-1, 4, kl, 4, 4, 4, 16)
+    # [tile, m, j, kg, gh, gl, byte] -> [tile, gh, m, gl, j, kg, byte]
+    return t.permute(0, 4, 1, 5, 2, 3, 6).reshape(c.pool_rows, rb)
+
+
+def segment_rows(c, i: int, rows: int):
+    """Paged store: rows [0, rows) of segment i as (K bytes, V bytes), each
+    [rows, row_bytes], gathered through its page table."""
+    pt = c.pages()[i]
+    idx = torch.arange(rows)
+    pool_row = (pt[idx // CDA_SEG_ALIGN].to(torch.int64) * CDA_SEG_ALIGN +
+                idx % CDA_SEG_ALIGN).to(c.device)
+    return k_rows(c)[pool_row], v_rows(c)[pool_row]

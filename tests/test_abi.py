@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.version() == lib.CDA_VERSION == 2
+    assert lib.version() == lib.CDA_VERSION == 3
     assert lib.status_string(0) == "ok"
     assert lib.status_string(3) == "workspace too small"
     assert lib.status_string(99) == "unknown status"
@@ -154,8 +154,8 @@ def test_decode_step_validation(lib):
 
 def _default_split_rule(pool_rows, nh):
     """The documented default: smallest unit (in 64-row tiles) whose estimated
-    units per XCD group, (pool_rows/64/t + nh/2)/8 + 1, stay <= 32."""
-    fits = lambda t: (pool_rows / 64 / t + nh / 2) / 8 + 1 <= 32
+    number of units, pool_rows/64/t + nh/2, stays <= 248."""
+    fits = lambda t: pool_rows / 64 / t + nh / 2 <= 248
     if pool_rows < 65536 and fits(4):
         return 4
     return next((t for t in (8, 12, 16, 24, 32, 48, 64) if fits(t)), 8)
@@ -268,3 +268,23 @@ def test_chunk_validation(lib):
     tile = 64 * 64 * 2   # one BF16 D = 64 tile
     assert (L.cda_chunk_workspace_bytes(C.byref(c3), 8, 4) - need >
             2 * tile * (300 * 2 - 2))
+
+
+@pytest.mark.parametrize("table", [
+    [64, 64, 128],        # does not start at 0
+    [0, 128, 64],         # decreasing
+    [0, 100, 192],        # not a multiple of 64
+    [0, 64, 4096],        # past the pool (pool_rows 1024)
+])
+def test_host_seg_base_is_checked(lib, table):
+    # the host copy of seg_base steers which pool rows the kernels read, so
+    # every call checks it before anything is enqueued
+    L = lib.load()
+    c = _cache(lib, B=1, Hkv=2, pool_rows=1024)
+    host = (C.c_int64 * 3)(*table)
+    c.seg_base_host = C.cast(host, C.c_void_p)
+    need = L.cda_attn_workspace_bytes(C.byref(c), 8, 0)
+    ws, q, out = 0x200000, 0x300000, 0x400000
+    st = L.decode_attn_compact(C.byref(c), C.c_void_p(q), 8, 0.0, C.c_void_p(out), 0, None, 0,
+                               C.c_void_p(ws), C.c_size_t(need), None)
+    assert st == lib.CDA_ERR_INVALID_ARG

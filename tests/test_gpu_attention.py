@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workload
-from _cda_testlib import (check_close, counter_bytes, dev, gpu_prefill, log, odt, oracle_prefill)
+from _cda_testlib import (check_close, dev, gpu_prefill, log, odt, oracle_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,7 +76,7 @@ def test_split_invariance(split, kv_dtype):
 
 
 def test_one_workspace_reused_across_splits_and_caches():
-    # the completion counters are left at zero by every call, so a single
+    # the counters and partial slots are left at zero by every call, so a single
     # zero-filled workspace serves calls with different splits and caches
     B, Hq, Hkv, D, T, W = 2, 16, 4, 128, 2000, 64
     keep = workload.random_keep((B, Hkv, T), 0.3, seed=91)
@@ -97,7 +97,7 @@ def test_one_workspace_reused_across_splits_and_caches():
             for c in caches:
                 out = c.attention(qd, out_dtype=torch.float32, split_tokens=split, workspace=ws)
                 check_close(out.cpu().numpy(), refs[c.kv_dtype], f"{c.kv_dtype} split {split} rep {rep}")
-    assert torch.count_nonzero(ws[: counter_bytes(B, Hkv)]) == 0
+    assert torch.count_nonzero(ws) == 0   # counters and partial slots
 
 
 def test_outliers_and_custom_scale():
@@ -164,10 +164,14 @@ def test_decode_loop_matches_oracle(kv_dtype, D, W):
     log(f"  worst abs err {worst:.2e}")
 
 
-def test_group_map_from_count_is_balanced_and_changes_nothing():
-    # COUNT deals the segments to the 8 XCD groups by size (snake order over
-    # the capacities); attention and decode steps give the same bits with
-    # the map as with the plain i mod 8 grouping (map pointer NULL)
+def test_host_plan_and_device_plan_give_the_same_bits():
+    # with the host copy of seg_base the launcher plans the work units over
+    # the segments' capacities; without it every wave plans on the device
+    # (over the rows holding data for attention, over the capacities for a
+    # decode step).  The merge folds the units' partials in unit order, so
+    # the two plans give bit-identical results whenever they cut the
+    # segments the same way (decode steps), and agree within rounding
+    # otherwise (attention)
     B, Hq, Hkv, D, T, W, S = 8, 32, 8, 128, 2500, 256, 4
     rates = torch.rand((B, Hkv, 1), generator=torch.Generator().manual_seed(102)) * 0.3
     keep = (torch.rand((B, Hkv, T + S), generator=torch.Generator().manual_seed(103)) < rates)
@@ -177,21 +181,19 @@ def test_group_map_from_count_is_balanced_and_changes_nothing():
     q = workload.random_bf16((S, B, Hq, D), seed=106)
     c1, _ = gpu_prefill(k, v, keep, T, W, S, "fp8", with_dst=False)
     c2, _ = gpu_prefill(k, v, keep, T, W, S, "fp8", with_dst=False)
-    gm = c1.seg_group.cpu().numpy().astype(np.int64)
-    tiles = -(-(W + c1.seg_cap.cpu().numpy().astype(np.int64)) // 64)
-    nh = B * Hkv
-    assert gm.min() >= 0 and gm.max() < 8
-    assert np.all(np.bincount(gm, minlength=8) == nh // 8)
-    sums = np.bincount(gm, weights=tiles, minlength=8)
-    assert sums.max() - sums.min() <= tiles.max(), sums
-    c2.struct.seg_group = 0          # plain i mod 8 grouping
+    assert c1.seg_base_host is not None
+    c2.seg_base_host = None
+    c2._refresh()                     # device plan
     kd, vd, qd = k.to(dev()), v.to(dev()), q.to(dev())
     kn = keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev())
-    for split in (256, 512):
+    ka, va = c1.k_amax.cpu().numpy(), c1.v_amax.cpu().numpy()
+    for split in (256, 512, 0):
         o1 = c1.attention(qd[0], out_dtype=torch.float32, split_tokens=split)
         o2 = c2.attention(qd[0], out_dtype=torch.float32, split_tokens=split)
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2), f"attention, split {split}"
+        ref, _ = oracle.attention(q[0], k, v, keep, T - 1, W, oracle.FP8, ka, va)
+        check_close(o1.cpu().numpy(), ref, f"host plan, split {split}")
+        check_close(o2.cpu().numpy(), ref, f"device plan, split {split}")
     for s in range(S):
         o1 = c1.decode_step(kd[:, T + s], vd[:, T + s], kn[s], qd[s], out_dtype=torch.float32)
         o2 = c2.decode_step(kd[:, T + s], vd[:, T + s], kn[s], qd[s], out_dtype=torch.float32)
@@ -200,3 +202,26 @@ def test_group_map_from_count_is_balanced_and_changes_nothing():
     assert torch.equal(c1.comp_len, c2.comp_len) and torch.equal(c1.pos, c2.pos)
     assert torch.equal(c1.k_pool, c2.k_pool) and torch.equal(c1.v_pool, c2.v_pool)
     assert c1.error_word() == 0 and c2.error_word() == 0
+
+
+def test_stale_host_plan_is_flagged():
+    # a COUNT that changes the layout after the host copy was taken: the
+    # attention flags CDA_DEVERR_PLAN instead of reading rows of another
+    # layout (the rows it would read stay inside the pool)
+    from compressed_decode_attention_amd import CDA_DEVERR_PLAN
+    B, Hq, Hkv, D, T, W = 2, 8, 2, 128, 900, 64
+    keep = workload.random_keep((B, Hkv, T), 0.3, seed=111)
+    k = workload.random_bf16((B, T, Hkv, D), seed=112)
+    v = workload.random_bf16((B, T, Hkv, D), seed=113)
+    q = workload.random_bf16((B, Hq, D), seed=114).to(dev())
+    c, _ = gpu_prefill(k, v, keep, T, W, 0, "fp8", with_dst=False)
+    out = c.attention(q, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert c.error_word() == 0 and torch.isfinite(out).all()
+    # reserve 64 more rows per segment: every segment after the first moves
+    c.count(keep.to(dev()), T, reserve=64)
+    c.err.zero_()
+    out = c.attention(q, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert c.error_word() & CDA_DEVERR_PLAN
+    assert torch.isfinite(out).all()

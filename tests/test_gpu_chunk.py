@@ -15,7 +15,7 @@ import torch
 import oracle
 import workload
 from _cda_testlib import (CDA_SEG_ALIGN, check_close, compare_state, dev, gpu_prefill, log, odt,
-                          oracle_prefill)
+                          oracle_prefill, segment_rows)
 from compressed_decode_attention_amd import PagedKVCache
 
 pytestmark = pytest.mark.gpu
@@ -154,7 +154,7 @@ def test_chunk_on_the_paged_store():
             _oracle_append(o, lay, T, s0, M)
             n = o.stored_rows()
             for h in range(Hkv):
-                kr, vr = c.segment_rows(slot * Hkv + h, int(n[h]))
+                kr, vr = segment_rows(c, slot * Hkv + h, int(n[h]))
                 a = int(o.seg_base[h])
                 assert np.array_equal(kr.cpu().numpy(), o.k_pool[a:a + n[h]])
                 assert np.array_equal(vr.cpu().numpy(), o.v_pool[a:a + n[h]])

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workload
-from _cda_testlib import compare_state, dev, gpu_prefill, log, oracle_prefill
+from _cda_testlib import compare_state, dev, gpu_prefill, k_rows, log, oracle_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -169,6 +169,6 @@ def test_pack_into_too_small_pool_sets_error_bit():
     assert c.error_word() & 2
     o = oracle_prefill(k, k, keep, T, W, 0, "bf16")
     # the first segment is complete
-    kr = c.k_rows().cpu().numpy()
+    kr = k_rows(c).cpu().numpy()
     n0 = int(o.stored_rows()[0])
     assert np.array_equal(kr[:n0], o.k_pool[:n0])

@@ -1,8 +1,8 @@
 """Decode steps, prefill compaction and attention captured in a HIP graph
 (torch.cuda.CUDAGraph) give, on every replay, exactly the results of the
 same calls issued eagerly: the kernels use no memset and allocate nothing,
-every replay restarts from the prefill, and the XCD-local merge holds under
-the workgroup-to-XCD rotation graph replays use.  Replays are interleaved
+every replay restarts from the prefill, and the split merge gives the same
+bits whichever unit of a segment finishes last.  Replays are interleaved
 with eager work and synchronisations."""
 import pytest
 import torch
@@ -22,7 +22,7 @@ def test_graph_replays_match_eager():
     q = workload.random_bf16((S, B, Hq, D), seed=84)
     kd, vd, keepd, qd = k.to(dev()), v.to(dev()), keep.to(dev()), q.to(dev())
     keep_new = keepd[:, :, T:].permute(2, 0, 1).contiguous()
-    split = 256   # several units per head: the XCD-local merge runs
+    split = 256   # several units per head: the split merge runs
 
     # eager reference
     ce, _ = gpu_prefill(k, v, keep, T, W, S, "fp8", with_dst=False)

@@ -16,7 +16,7 @@ import torch
 import oracle
 import workload
 from _cda_testlib import (CDA_SEG_ALIGN, check_close, dev, gpu_prefill, log, odt,
-                          oracle_prefill)
+                          oracle_prefill, segment_rows)
 from compressed_decode_attention_amd import (CDA_DEVERR_CAPACITY, CDA_DEVERR_PAGES, CompactKVCache,
                                              PagedKVCache)
 from oracle.paged import PagedBook
@@ -81,7 +81,7 @@ def _compare_rows(c: PagedKVCache, slot: int, req: Request, what: str):
     for h in range(Hkv):
         if n[h] == 0:
             continue
-        kr, vr = c.segment_rows(slot * Hkv + h, int(n[h]))
+        kr, vr = segment_rows(c, slot * Hkv + h, int(n[h]))
         a = int(o.seg_base[h])
         assert np.array_equal(kr.cpu().numpy(), o.k_pool[a:a + n[h]]), f"{what} K rows, head {h}"
         assert np.array_equal(vr.cpu().numpy(), o.v_pool[a:a + n[h]]), f"{what} V rows, head {h}"
@@ -269,7 +269,7 @@ def test_growth_beyond_the_prefill_reserve():
     assert cc.error_word() & CDA_DEVERR_CAPACITY       # the contiguous store ran out
     for i in range(B * Hkv):
         n = int(o.stored_rows()[i])
-        kr, vr = pc.segment_rows(i, n)
+        kr, vr = segment_rows(pc, i, n)
         a = int(o.seg_base[i])
         assert np.array_equal(kr.cpu().numpy(), o.k_pool[a:a + n])
         assert np.array_equal(vr.cpu().numpy(), o.v_pool[a:a + n])
