@@ -482,8 +482,11 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
       t_own = new_row / kTile;
     }
   }
-  // the unit that holds the new token's tile adds it to the segment
+  // the unit that holds the new token's tile adds it to the segment, and
+  // the wave that reads that tile (the row wave) forms the new token and
+  // writes the segment's new and moved rows once the tile is consumed
   const bool owner_unit = APP && t_own >= t_begin && t_own < t_end;
+  const bool row_wave = owner_unit && wave == (t_own - t_begin) % NW;
   // decode step: where the keep bit of the token leaving the ring (ring
   // row P mod W) is; W = 0: a valid dummy address.  It is read where it is
   // needed, and tested only after the loads that must not wait for it.
@@ -492,12 +495,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   // of the compact row the leaving token may move to (same round trip as
   // the tile's page)
   int pg_own = -1, pg_dst = -1;
-  if (PG && owner_unit && wave == 0) {
+  if (PG && row_wave) {
     pg_own = page_of(p, i, t_own);
     pg_dst = page_of(p, i, (p.W + un.cl) / kTile);
   }
   const uint8_t* rkp = APP ? (p.W > 0 ? p.ring_keep + (int64_t)i * p.W + ring_slot : p.keep_new + i)
                            : nullptr;
+  // decode step: the keep bit for the segment's metadata, loaded now and
+  // used at the end (commit)
+  const int rkc = APP ? *rkp : 0;
   const float c1 = p.sm_scale * kLog2e * ks;
 
   float m_run = -INFINITY, l_run = 0.0f;
@@ -505,17 +511,17 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
 
-  // owner unit, wave 0: its slice of the new token (issued after the
-  // accumulators are set up, so that nothing before the tile loads waits
-  // for it).  It also reads the ring row the new token replaces (the
-  // leaving token's row: 16-byte K chunk `lane`, V elements EPL*lane..), in
-  // case it moves to the compact tail.
+  // row wave: its slice of the new token (issued after the accumulators are
+  // set up, so that nothing before the tile loads waits for it).  It also
+  // reads the ring row the new token replaces (the leaving token's row:
+  // 16-byte K chunk `lane`, V elements EPL*lane..), in case it moves to the
+  // compact tail.
   uint32_t nk = 0, nv = 0;
   uint32_t ox[EPL];   // kept apart: combining them would wait for the loads here
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ox[e] = 0;
   u32x4 okx = u32x4{0, 0, 0, 0};
-  if (owner_unit && wave == 0) {
+  if (row_wave) {
     const int64_t off = (int64_t)b * p.new_sb + (int64_t)h * p.new_sh + EPL * lane;
     if (EPL == 2) {
       nk = *reinterpret_cast<const uint32_t*>(p.k_new + off);
@@ -539,11 +545,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   }
 
   bool first_tile = true;
-  // decode step, wave 0 of the unit holding the new token's tile: forms
-  // the new token from its BF16 input with the frozen scales -- its values
-  // and one logit per query row (from the q operand) into LDS, for the
-  // combine -- and returns its stored bytes.  It runs during wave 0's
-  // first tile, while that tile is in flight.
+  // decode step, the row wave: forms the new token from its BF16 input with
+  // the frozen scales -- its values and one logit per query row (from the q
+  // operand) into LDS, for the combine -- and returns its stored bytes.  It
+  // runs during the new token's tile, while that tile's V is in flight.
   auto new_token = [&](uint32_t& kc, uint32_t& vc) {
     __asm__ volatile("" : "+v"(nk), "+v"(nv));   // keeps this work below the tile loads
     const int d0n = EPL * lane;
@@ -603,8 +608,71 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     dot = sum_xor32(sum_xor16(dot));
     if (kg == 0) s_zn[g] = dot * c1;
   };
-  uint32_t kc = 0, vc = 0;   // wave 0 of the owner unit: the new row's stored bytes
+  uint32_t kc = 0, vc = 0;   // row wave: the new row's stored bytes
   bool nt_done = false;
+
+  // decode step, the row wave once the new token's tile is consumed:
+  // copies the leaving token's row to the compact tail if it moves
+  // (wants_move: it is kept and the compact region has room) and writes the
+  // new row over its ring row.  No other workgroup reads the new token's
+  // tile, and the compact tail lies past the rows attended in this launch.
+  auto write_rows = [&](bool wants_move) {
+    const int d0n = EPL * lane;
+    // the leaving token's row (ring row P mod W) moves to compact row
+    // W + cl if it is kept; read back from the pool (this wave's reads
+    // finish before the new row is written over it)
+    const int rs = new_row & (kTile - 1);
+    // paged: rows whose page is missing are not written (CDA_DEVERR_POOL)
+    const bool own_ok = !PG || page_ok(p, pg_own);
+    const bool dst_ok = !PG || page_ok(p, pg_dst);
+    const int64_t trow = PG ? (int64_t)pg_own * kTile : sb + (new_row - rs);
+    uint8_t* kt = p.k_pool + trow * (int64_t)RB;
+    uint8_t* vt = p.v_pool + trow * (int64_t)RB;
+    const bool moved = wants_move && own_ok && dst_ok &&
+                       (PG || sb + p.W + un.cl < p.pool_rows);
+    if (PG && lane == 0 && ((wants_move && !moved) || !own_ok)) atomicOr(p.err, CDA_DEVERR_POOL);
+    if (moved) {   // from the copy read at the start of the unit
+      const int to = p.W + un.cl, rt = to & (kTile - 1);
+      const int64_t drow = PG ? (int64_t)pg_dst * kTile : sb + (to - rt);
+      uint8_t* kd = p.k_pool + drow * (int64_t)RB;
+      uint8_t* vd = p.v_pool + drow * (int64_t)RB;
+      constexpr int KC = RB / 16;   // 16-byte chunks per K row
+      if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if (FP4)
+          nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
+        else if (FP8)
+          vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
+        else
+          reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
+      }
+    }
+    // the new row goes over the ring row: this wave has consumed the tile's
+    // old bytes, and the copy above used the ones read at the start of the
+    // unit (unused, and harmless, if it did not move).  Byte of this lane's
+    // first element in the row, and the lane's bytes:
+    constexpr int LB = FP4 ? EPL / 2 : EPL * E;
+    const int kb0 = FP4 ? d0n / 2 : d0n * E;
+    if (own_ok) {
+      uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
+      if (LB == 4)
+        *reinterpret_cast<uint32_t*>(kdst) = kc;
+      else if (LB == 2)
+        *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
+      else
+        *kdst = (uint8_t)kc;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if (FP4)   // after the moved row's write, which may share the byte
+          nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
+        else if (FP8)
+          vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
+        else
+          reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
+      }
+    }
+  };
 
   // ---- one tile: S = K Q^T, online softmax, O += V^T P^T.  valid: rows of
   // the tile holding data (<= 0: all masked); own: the tile of the new
@@ -631,7 +699,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
       }
     }
 
-    if (owner_unit && wave == 0 && first_tile) {   // while V is still in flight
+    if (own) {   // while V is still in flight
       new_token(kc, vc);
       nt_done = true;
     }
@@ -735,6 +803,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
         }
       }
     }
+    // the tile's data is all consumed: the row wave writes the rows now,
+    // while the other waves still stream
+    if (own) write_rows(own && leaving && rko != 0 && un.cl < un.cap);
     first_tile = false;
   };
 
@@ -769,11 +840,12 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     tile_body(valid, APP && t == t_own, rko);
   }
 
-  if (owner_unit && wave == 0 && !nt_done) new_token(kc, vc);   // wave 0 had no tile
-
-  // decode step: the keep bit again, for the segment's metadata (back
-  // before it is needed, after the combine or the merge)
-  const int rkc = APP ? *rkp : 0;
+  // the new token's tile held no data (nothing of it was attended, so no
+  // token leaves the ring here and nothing moves)
+  if (row_wave && !nt_done) {
+    new_token(kc, vc);
+    write_rows(false);
+  }
 
   // ---- combine the waves of the workgroup
   l_run = sum_xor32(sum_xor16(l_run));
@@ -786,70 +858,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     if (g < G) s_o[wave][g][(16 * nt + 4 * kg) / 4] = acc[nt];
   lds_barrier();
 
-  // ---- decode step, the unit holding the new token's tile: wave 0
-  // copies the leaving token's row to the compact tail if it moves and
-  // writes the new row; every tile load of the workgroup has completed
-  // (barrier above)
-  if (owner_unit && wave == 0) {
-    {
-      const int d0n = EPL * lane;
-      // the leaving token's row (ring row P mod W) moves to compact row
-      // W + cl if it is kept; read back from the pool (this wave's reads
-      // finish before the new row is written over it)
-      const int rs = new_row & (kTile - 1);
-      // paged: rows whose page is missing are not written (CDA_DEVERR_POOL)
-      const bool own_ok = !PG || page_ok(p, pg_own);
-      const bool dst_ok = !PG || page_ok(p, pg_dst);
-      const int64_t trow = PG ? (int64_t)pg_own * kTile : sb + (new_row - rs);
-      uint8_t* kt = p.k_pool + trow * (int64_t)RB;
-      uint8_t* vt = p.v_pool + trow * (int64_t)RB;
-      const bool wants_move = leaving && rkc != 0 && un.cl < un.cap;
-      const bool moved = wants_move && own_ok && dst_ok &&
-                         (PG || sb + p.W + un.cl < p.pool_rows);
-      if (PG && lane == 0 && ((wants_move && !moved) || !own_ok)) atomicOr(p.err, CDA_DEVERR_POOL);
-      if (moved) {   // from the copy read at the start of the unit
-        const int to = p.W + un.cl, rt = to & (kTile - 1);
-        const int64_t drow = PG ? (int64_t)pg_dst * kTile : sb + (to - rt);
-        uint8_t* kd = p.k_pool + drow * (int64_t)RB;
-        uint8_t* vd = p.v_pool + drow * (int64_t)RB;
-        constexpr int KC = RB / 16;   // 16-byte chunks per K row
-        if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          if (FP4)
-            nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
-          else if (FP8)
-            vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
-          else
-            reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
-        }
-      }
-      // the new row goes over the ring row: the tiles read its old bytes
-      // before the barrier above, and the copy above used the ones read at
-      // the start of the unit (unused, and harmless, if it did not move)
-      // byte of this lane's first element in the row, and the lane's bytes
-      constexpr int LB = FP4 ? EPL / 2 : EPL * E;
-      const int kb0 = FP4 ? d0n / 2 : d0n * E;
-      if (own_ok) {
-        uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
-        if (LB == 4)
-          *reinterpret_cast<uint32_t*>(kdst) = kc;
-        else if (LB == 2)
-          *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
-        else
-          *kdst = (uint8_t)kc;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          if (FP4)   // after the moved row's write, which may share the byte
-            nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
-          else if (FP8)
-            vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
-          else
-            reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
-        }
-      }
-    }
-  }
   // decode step, single-unit segment: every wave of the workgroup has read
   // the segment's metadata (the owner's keep bit included)
   int seq_prev = -1;
