@@ -96,7 +96,7 @@
 namespace cda {
 namespace {
 
-constexpr int kMergeBatch = 4;        // partials loaded per round trip in the merge
+constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge
 constexpr int kCounterStride = 32;    // ints between counters: one 128-byte line each
 constexpr int kMergePolls = 1 << 20;  // polls of one batch of partials before giving up
 constexpr int kMaxPlanUnits = 512;    // units a host plan carries in the kernel arguments (4 KB)
@@ -871,20 +871,27 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   // the waves' states, and the new token's (logit, value) pair in the unit
   // that holds it
   auto combine = [&](int gg, int d4, float& M, float& L, f32x4& O) {
+    // every LDS read first, then the arithmetic (a wave without rows has
+    // m = -inf and weight exp2(-inf) = 0)
+    float mw[NW], lw[NW];
+    f32x4 ow[NW];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      mw[ww] = s_m[ww][gg];
+      lw[ww] = s_l[ww][gg];
+      ow[ww] = s_o[ww][gg][d4];
+    }
     M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, s_m[ww][gg]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mw[ww]);
+    const float Mu = M == -INFINITY ? 0.0f : M;
     O = f32x4{0, 0, 0, 0};
     L = 0.0f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float mw = s_m[ww][gg];
-        if (mw == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(mw - M);
-        O += f * s_o[ww][gg][d4];
-        L += f * s_l[ww][gg];
-      }
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(mw[ww] - Mu);
+      O += f * ow[ww];
+      L += f * lw[ww];
     }
     if (owner_unit) {   // decode step: the new token's (logit, value) pair
       const float zn = s_zn[gg];
