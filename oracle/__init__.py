@@ -34,7 +34,7 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11",
+        subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-fopenmp",
                                "-ffp-contract=off", "-fno-fast-math",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
@@ -59,6 +59,8 @@ def lib():
             L.orc_e2m1_decode.argtypes = [C.c_uint8]
             L.orc_e2m1_decode.restype = f64
             L.orc_fp4_scales_from_amax.argtypes = [f32, P, P]
+            L.orc_set_threads.argtypes = [i32]
+            L.orc_max_threads.restype = i32
             L.orc_stored_count.argtypes = [P, i32, i32]
             L.orc_stored_count.restype = i64
             L.orc_prefill_layout.argtypes = [i32, i32, i32, i32, i32, i32, P, i64, P, P, P, P]
@@ -93,6 +95,13 @@ def _u8(x) -> np.ndarray:
     if isinstance(x, np.ndarray):
         return np.ascontiguousarray(x, dtype=np.uint8)
     return x.contiguous().numpy().astype(np.uint8, copy=False)
+
+
+def set_threads(n: int) -> int:
+    """Threads the oracle's loops over independent (sequence, head) units
+    use (n < 1: every core); returns the number now in effect."""
+    lib().orc_set_threads(int(n))
+    return int(lib().orc_max_threads())
 
 
 # ---------------------------------------------------------------- scalars

@@ -32,10 +32,14 @@
  *     no split, no reordering.
  *
  * Readings where the pages are silent are listed with each function.
- * Build: gcc -O2 -fPIC -shared -ffp-contract=off -fno-fast-math (x86-64 SSE
- * arithmetic, so every float operation below is a single IEEE rounding).
+ * Build: gcc -O2 -fPIC -shared -fopenmp -ffp-contract=off -fno-fast-math
+ * (x86-64 SSE arithmetic, so every float operation below is a single IEEE
+ * rounding).  Independent (sequence, head) units are spread over OpenMP
+ * threads; the arithmetic of each unit is sequential, so the results do not
+ * depend on the number of threads.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -44,6 +48,17 @@
 #define ORC_BF16 0
 #define ORC_FP8 1
 #define ORC_FP4 2
+
+/* Threads the loops over independent units use (n < 1: all cores). */
+void orc_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+}
+
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* Bytes of one stored row of D elements. */
 static int64_t row_bytes(int D, int kv_dtype)
@@ -275,6 +290,7 @@ void orc_prefill_amax(int B, int Hkv, int D, int T, int W,
                       const uint8_t *keep, int64_t keep_ld,
                       float *k_amax, float *v_amax)
 {
+#pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < Hkv; ++h) {
             int i = b * Hkv + h;
@@ -354,8 +370,10 @@ void orc_prefill_pack(int B, int Hkv, int D, int T, int W, int reserve,
         orc_prefill_amax(B, Hkv, D, T, W, k, v, sb, st, sh, keep, keep_ld,
                          k_amax, v_amax);
     int64_t rowb = row_bytes(D, kv_dtype);
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B; ++b)
         pos[b] = T;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
         for (int h = 0; h < Hkv; ++h) {
             int i = b * Hkv + h;
             float ks, kinv, vs, vinv;
@@ -409,9 +427,11 @@ int64_t orc_append(int B, int Hkv, int D, int W, int kv_dtype,
 {
     int64_t rowb = row_bytes(D, kv_dtype);
     int64_t sat = 0;
+    int32_t errbits = 0;
+#pragma omp parallel for collapse(2) reduction(+ : sat) reduction(| : errbits)
     for (int b = 0; b < B; ++b) {
-        int P = pos[b];
         for (int h = 0; h < Hkv; ++h) {
+            int P = pos[b];
             int i = b * Hkv + h;
             float ks, kinv, vs, vinv;
             head_scales(kv_dtype, kv_dtype == ORC_BF16 ? 0.0f : k_amax[i], &ks, &kinv);
@@ -429,7 +449,7 @@ int64_t orc_append(int B, int Hkv, int D, int W, int kv_dtype,
                         memcpy(v_pool + to * rowb, v_pool + from * rowb, (size_t)rowb);
                         comp_len[i] += 1;
                     } else {
-                        *err |= 1;
+                        errbits |= 1;
                     }
                 }
                 int64_t slot = seg_base[i] + P % W;
@@ -443,12 +463,14 @@ int64_t orc_append(int B, int Hkv, int D, int W, int kv_dtype,
                     sat += store_row(D, kv_dtype, vn, vinv, v_pool + to * rowb);
                     comp_len[i] += 1;
                 } else {
-                    *err |= 1;
+                    errbits |= 1;
                 }
             }
         }
-        pos[b] = P + 1;
     }
+    for (int b = 0; b < B; ++b)
+        pos[b] += 1;
+    *err |= errbits;
     return sat;
 }
 
@@ -536,6 +558,7 @@ void orc_attention(int B, int Hq, int Hkv, int D, int W, int kv_dtype,
                    const uint16_t *q, double sm_scale, double *out, double *lse)
 {
     int G = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < B; ++b)
         for (int j = 0; j < Hq; ++j) {
             int h = j / G, i = b * Hkv + h;

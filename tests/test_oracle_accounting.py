@@ -48,12 +48,6 @@ def test_saved_ratios_match_table():
             assert f"{float(f[col_v]) / fast:.1f}" == f[col_r], (f[0], f[1], col_v)
 
 
-def test_compact_bytes_identity(orc):
-    # stored tokens x 2 x D x bytes/elem (+ 8 B of scales per head for FP8)
-    assert orc.compact_kv_bytes(1000, 128, orc.BF16, 8) == 1000 * 2 * 128 * 2
-    assert orc.compact_kv_bytes(1000, 128, orc.FP8, 8) == 1000 * 2 * 128 + 64
-
-
 def test_fastdms_rows_imply_kept_fraction():
     # FastDMS GiB / (bytes per BF16 token) / 8,320 tokens: a sanity range for
     # the synthetic keep rates, not a parity pin.
