@@ -17,17 +17,27 @@ The prefill and the decode launches are captured once into two HIP graphs
 redoes the same work) and replayed each step; --eager issues every call
 from Python instead, --unfused uses kv_compact APPEND + decode_attn_compact.
 
+Workloads that fit in the 256 MB last-level cache (--config llama_c1,
+qwen_c1, llama_c8) rotate R replicas of every layer's store (--replicas,
+default: enough for 1 GB), so that no launch finds its layer in that cache;
+decode step s then runs on replica s mod R, at that replica's own position.
+
 Reported: value = decode-attention KV bytes moved per second over the whole
 step (algorithmic bytes: every stored row's K and V read once per decode
-step and layer, divided by the step's wall time); the roofline of the
+step and layer, divided by the step's wall time), with the median and
+10th/90th percentiles of the step and launch times; the roofline of the
 decode-step kernel, its per-launch duration measured with HIP events on its
-stream around the decode part of each timed step; the CPU oracle timed on a
-bounded sample; and parity of that sample.
+stream around the decode part of each timed step, beside the measured read
+ceiling of the same access pattern (a plain streaming kernel over 2 GiB and
+over exactly one layer's tiles); the realised compression ratio of the
+store; the CPU oracle timed on one thread and on every core on a bounded
+sample, the FP8 saturations and byte accounting of that sample, and the
+parity of the GPU output there.
 """
 from __future__ import annotations
 
 import argparse
-import glob
+import ctypes as C
 import hashlib
 import json
 import os
@@ -42,9 +52,12 @@ sys.path.insert(0, ROOT)
 METRIC = "compact decode-attn HBM GB/s (% of peak) + attn tokens/s, Qwen3-8B ctx8192"
 HBM_PEAK_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "attn.hip")
-
+STREAM_LIB = os.path.join(ROOT, "compressed_decode_attention_amd", "libcda_stream.so")
+MALL_BYTES = 256 << 20           # last-level (Infinity) cache of the device
+CEILING_BYTES = 2 << 30          # buffer of the read-ceiling measurement
 
 REFILL = 64   # --paged: rows of headroom a refill leaves, and steps between refills
+ORACLE_STEPS = 4                 # decode steps of the timed oracle sample
 
 
 def log(msg):
@@ -75,7 +88,12 @@ def rows_before_host(keep_np, T, W, s0):
 
 
 ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
+ELEM_BYTES = {"bf16": 2.0, "fp8": 1.0, "fp4": 0.5}
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / f16 MFMA of the MI355X
+
+
+def pct(x, q):
+    return round(float(np.percentile(np.asarray(x, np.float64), q)), 3)
 
 
 def traffic_from_profile():
@@ -91,39 +109,126 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, layers, outs, kv_dtype, budget_s=12.0):
-    """The oracle, as it stands, on a bounded sample: for layer 0, 1, ...
-    (until the budget is spent) the prefill absmax and the attention of all
-    B x Hq query heads at the last decode step.  Returns the record and the
-    worst parity error of the GPU outputs of those layers."""
+def stream_lib():
+    if not os.path.exists(STREAM_LIB):
+        raise RuntimeError(f"{STREAM_LIB} is missing: build it with `python -c 'import "
+                           f"__graft_entry__ as g; g.build()'`")
+    L = C.CDLL(STREAM_LIB)
+    L.cda_stream_tiles.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
+                                   C.c_void_p, C.c_void_p]
+    L.cda_stream_tiles.restype = C.c_int32
+    return L
+
+
+def graph_us(torch, fn, calls, reps=5):
+    """Median time of one call of fn, from a HIP graph of `calls` calls."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t = []
+    for _ in range(reps):
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3 / calls)
+    return float(np.median(t))
+
+
+def read_ceiling(torch, dev, tile_bytes, layer_tiles):
+    """The plain streaming read of 64-row tiles (the attention's access
+    pattern, no arithmetic): GB/s over 2 GiB, and the time and GB/s of
+    reading exactly the tiles of one layer's launch."""
+    L = stream_lib()
+    stream = lambda: C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    buf = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
+    half = CEILING_BYTES // 2
+    n_big = half // tile_bytes
+    sink = torch.empty(max(n_big, len(layer_tiles)), dtype=torch.int32, device=dev)
+
+    def big():
+        st = L.cda_stream_tiles(C.c_void_p(buf.data_ptr()), C.c_void_p(buf.data_ptr() + half),
+                                None, n_big, tile_bytes, C.c_void_p(sink.data_ptr()), stream())
+        assert st == 0, st
+    us_big = graph_us(torch, big, 10)
+    gbs_big = 2 * n_big * tile_bytes / (us_big * 1e-6) / 1e9
+    tiles = torch.as_tensor(np.asarray(layer_tiles, np.int32), device=dev)
+    n_layer = len(layer_tiles)
+
+    def layer():
+        st = L.cda_stream_tiles(C.c_void_p(buf.data_ptr()), C.c_void_p(buf.data_ptr() + half),
+                                C.c_void_p(tiles.data_ptr()), n_layer, tile_bytes,
+                                C.c_void_p(sink.data_ptr()), stream())
+        assert st == 0, st
+    # the layer's tile list read from the big buffer: the same tile offsets
+    # and count as the layer's pools, all inside each half
+    assert int(np.max(layer_tiles)) < n_big
+    us_layer = graph_us(torch, layer, 200)
+    gbs_layer = 2 * n_layer * tile_bytes / (us_layer * 1e-6) / 1e9
+    del buf
+    return {"stream_gbs": round(gbs_big, 1), "stream_bytes": CEILING_BYTES,
+            "layer_tiles_us": round(us_layer, 3), "layer_tiles_gbs": round(gbs_layer, 1),
+            "layer_tile_bytes": 2 * n_layer * tile_bytes,
+            "kernel": "cda_stream_tiles: one wave per 64-row tile, 16-byte nontemporal loads "
+                      "of its K then V tile, 8 waves per workgroup"}
+
+
+def cpu_baseline(cfg, kv, dev_rows_l0, out_f32_l0, budget_note=""):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    layer 0 of the full shape, prefill compaction plus the first
+    ORACLE_STEPS decode steps (append, then fp64 attention of all B x Hq
+    query heads), timed on one thread and on every core.  Then the rest of
+    that layer's appends (FP8 saturations, stored rows and byte accounting
+    at the end, checked against the device) and its attention at the last
+    position (parity of the GPU's F32 output there)."""
     import oracle
     from workload import make_layer
-    od = {"bf16": oracle.BF16, "fp8": oracle.FP8, "fp4": oracle.FP4}[kv_dtype]
-    T, S, W = cfg.T, cfg.S, cfg.W
-    nbytes, t_used, worst, done = 0, 0.0, 0.0, 0
-    for l in layers:
-        lay = make_layer(cfg, l)
+    od = {"bf16": oracle.BF16, "fp8": oracle.FP8, "fp4": oracle.FP4}[kv]
+    T, S, W, B, Hkv, D = cfg.T, cfg.S, cfg.W, cfg.B, cfg.Hkv, cfg.D
+    lay = make_layer(cfg, 0)
+    times, threads, nbytes = {}, {}, 0
+    for mode in (1, 0):
+        n = oracle.set_threads(mode)
         t0 = time.perf_counter()
-        ka, va = oracle.prefill_amax(lay.k, lay.v, lay.keep, T, W)
-        ref, _ = oracle.attention(lay.q[S - 1], lay.k, lay.v, lay.keep, T + S - 1, W, od,
-                                  ka, va)
-        t_used += time.perf_counter() - t0
-        n = stored_rows_host(lay.keep.numpy(), T, W, S)[S - 1]
-        nbytes += int(n.sum()) * 2 * ROW_BYTES[kv_dtype](cfg.D)
-        got = outs[l].float().cpu().numpy()
-        err = np.abs(got - ref)
-        tol = 2e-3 + 1e-2 * np.abs(ref) + np.abs(ref) * 2.0 ** -8   # bf16 output rounding
-        if not np.all(err <= tol):
-            raise AssertionError(f"bench parity failed on layer {l}: max err {err.max():.3e}")
-        worst = max(worst, float(err.max()))
-        done += 1
-        if t_used >= budget_s:
-            break
-    rec = {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"layers 0..{done - 1}: prefill absmax + fp64 attention of all "
-                     f"{cfg.B}x{cfg.Hq} query heads at the last decode step "
-                     f"({nbytes / 1e6:.1f} MB of compact KV, {t_used:.1f} s)"}
-    return rec, worst, done
+        c = oracle.prefill_pack(lay.k, lay.v, lay.keep, T, W, S, od, align=64)
+        nbytes = 0
+        for s in range(ORACLE_STEPS):
+            c.append(lay.k[:, T + s], lay.v[:, T + s], lay.keep[:, :, T + s].contiguous())
+            oracle.attention(lay.q[s], lay.k, lay.v, lay.keep, T + s, W, od, c.k_amax, c.v_amax)
+            nbytes += int(c.stored_rows().sum()) * 2 * oracle.row_bytes(D, od)
+        times[mode] = time.perf_counter() - t0
+        threads[mode] = n
+    for s in range(ORACLE_STEPS, S):
+        c.append(lay.k[:, T + s], lay.v[:, T + s], lay.keep[:, :, T + s].contiguous())
+    rows = c.stored_rows().astype(np.int64)
+    if not np.array_equal(rows, dev_rows_l0.reshape(-1)):
+        raise AssertionError("layer 0: device stored rows differ from the oracle's store")
+    ref, _ = oracle.attention(lay.q[S - 1], lay.k, lay.v, lay.keep, T + S - 1, W, od,
+                              c.k_amax, c.v_amax)
+    err = np.abs(out_f32_l0 - ref)
+    tol = 2e-3 + 1e-2 * np.abs(ref)
+    if not np.all(err <= tol):
+        raise AssertionError(f"bench parity failed on layer 0: max err {err.max():.3e}")
+    compact = oracle.compact_kv_bytes(int(rows.sum()), D, od, B * Hkv)
+    rec = {"value": round(nbytes / times[0] / 1e9, 4), "unit": "GB/s", "cores": threads[0],
+           "value_1_thread": round(nbytes / times[1] / 1e9, 4), "kind": "oracle",
+           "sample": f"layer 0 of {cfg.name}: prefill compaction + the first {ORACLE_STEPS} "
+                     f"decode steps (append, then fp64 attention of all {B}x{cfg.Hq} query "
+                     f"heads); {nbytes / 1e6:.1f} MB of compact KV attended; "
+                     f"{times[0]:.2f} s on {threads[0]} threads, {times[1]:.2f} s on 1",
+           "ms_per_decode_step_all_cores": round(times[0] * 1e3 / ORACLE_STEPS, 1)}
+    extra = {"fp8_saturated": int(c.saturated) if od != oracle.BF16 else 0,
+             "oracle_compact_kv_bytes_layer0": int(compact),
+             "max_abs_err_f32_layer0": float(err.max()),
+             "max_rel_err_f32_layer0": float((err / np.maximum(np.abs(ref), 1e-30)).max())}
+    return rec, extra
 
 
 def main():
@@ -136,7 +241,11 @@ def main():
                     help="stored format (default: the config's; fp4 is the 4-bit variant)")
     ap.add_argument("--layers", type=int, default=0, help="0 = all layers of the config")
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="replicas of every layer's store, rotated per decode step; 0 = as "
+                         "many as make the stores at least 1 GB (1 for the c = 8 Qwen shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--eager", action="store_true", help="issue every call from Python (no graphs)")
     ap.add_argument("--paged", action="store_true",
                     help="paged store: 64-row pages, no prefill reserve, a refill every 64 "
@@ -148,8 +257,11 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="decode steps as kv_compact APPEND + decode_attn_compact")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 64 MiB device copy 3 times (the reference kernel "
-                         "for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
+                    help="only run a plain 64 MiB device copy 3 times (the reference for "
+                         "scaling WRITE_SIZE), then exit")
+    ap.add_argument("--stream-calibration", action="store_true",
+                    help="only read 2 GiB with the tile-streaming kernel 3 times (the "
+                         "reference for scaling FETCH_SIZE), then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the compact decode-attention path runs on a "
@@ -159,7 +271,7 @@ def main():
     import torch
 
     import workload
-    from compressed_decode_attention_amd import CompactKVCache, PagedKVCache, _lib
+    from compressed_decode_attention_amd import CompactKVCache, PagedKVCache
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -170,6 +282,19 @@ def main():
         torch.cuda.synchronize()
         log("copied 64 MiB three times")
         return
+    if args.stream_calibration:
+        L_ = stream_lib()
+        buf = torch.zeros(CEILING_BYTES, dtype=torch.uint8, device=dev)
+        sink = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+        half, tb = CEILING_BYTES // 2, 8192
+        for _ in range(3):
+            assert L_.cda_stream_tiles(C.c_void_p(buf.data_ptr()),
+                                       C.c_void_p(buf.data_ptr() + half), None, half // tb, tb,
+                                       C.c_void_p(sink.data_ptr()),
+                                       C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)) == 0
+        torch.cuda.synchronize()
+        log(f"streamed {CEILING_BYTES >> 20} MiB three times ({half // tb} tiles of 2 x {tb} B)")
+        return
     cfg = workload.CONFIGS[args.config]
     kv = args.kv or cfg.kv_dtype
     L = args.layers or cfg.L
@@ -179,7 +304,7 @@ def main():
         f"{kv}; generating inputs")
 
     t0 = time.perf_counter()
-    kd, vd, keepd, keep_new, qd, caches, nrows = [], [], [], [], [], [], []
+    kd, vd, keepd, keep_new, qd, nrows = [], [], [], [], [], []
     for l in range(L):
         lay = workload.make_layer(cfg, l)
         kd.append(lay.k.to(dev))
@@ -188,16 +313,25 @@ def main():
         keep_new.append(lay.keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev))
         qd.append(lay.q.to(dev))
         nrows.append(stored_rows_host(lay.keep.numpy(), T, W, S))
+    # bytes of the stores: one replica unless they fit in the last-level cache
+    est = sum(int(nrows[l][S - 1].sum() + B * Hkv * S) * 2 * row_bytes for l in range(L))
+    R = args.replicas or (1 if est >= 3 * MALL_BYTES else -(-(1 << 30) // est))
+    if args.chunk > 0 or args.paged:
+        R = 1
+    S_r = [len(range(r, S, R)) for r in range(R)]      # decode steps of each replica
+
+    def new_cache(l):
         if args.paged:
             # pages for each segment's last rows plus one refill's headroom
             pages = -(-(nrows[l][S - 1].astype(np.int64) + REFILL) // 64)
             c = PagedKVCache(B, Hkv, D, W, int(pages.sum()), int(pages.max()), kv, dev)
         else:
             c = CompactKVCache(B, Hkv, D, W, kv, dev)
-            c.count(keepd[l], T, reserve=S)
+            c.count(keepd[l], T, reserve=S_r[0])
             c.allocate()
         c.workspace(Hq, args.split)
-        caches.append(c)
+        return c
+    caches = [[new_cache(l) for l in range(L)] for _ in range(R)]     # [replica][layer]
     outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     # --chunk: per layer and chunk, (start, tokens, keep [B, m, Hkv], q [B, m, Hq, D], out)
     chunks = []
@@ -211,44 +345,47 @@ def main():
                            torch.empty((B, m, Hq, D), dtype=torch.bfloat16, device=dev)))
             chunks.append(lc)
     torch.cuda.synchronize()
-    log(f"inputs resident in {time.perf_counter() - t0:.1f} s")
+    log(f"inputs resident in {time.perf_counter() - t0:.1f} s; {R} replica(s) of the stores")
 
-    # algorithmic bytes of every attention call: stored rows x 2 x D x e
-    attn_bytes = np.array([[int(nrows[l][s].sum()) * 2 * row_bytes for l in range(L)]
+    # algorithmic bytes of every attention call: stored rows x 2 x D x e;
+    # decode step s runs on replica s mod R at that replica's step s // R
+    attn_bytes = np.array([[int(nrows[l][s // R].sum()) * 2 * row_bytes for l in range(L)]
                            for s in range(S)], np.float64)          # [S, L]
     step_attn_bytes = float(attn_bytes.sum())
 
     def prefill_all():
-        for l in range(L):
-            c = caches[l]
-            if args.paged:
-                c.init()
-                c.admit(0, kd[l], vd[l], keepd[l], T, reserve=0)
-            else:
-                c.count(keepd[l], T, reserve=S)
-                c.pack(kd[l], vd[l], keepd[l], T)
+        for reps in caches:
+            for l in range(L):
+                c = reps[l]
+                if args.paged:
+                    c.init()
+                    c.admit(0, kd[l], vd[l], keepd[l], T, reserve=0)
+                else:
+                    c.count(keepd[l], T, reserve=S_r[0])
+                    c.pack(kd[l], vd[l], keepd[l], T)
 
     def decode_all():
         if args.chunk > 0:
             for j in range(len(chunks[0])):
                 for l in range(L):
                     s0, m, kp, qc, oc = chunks[l][j]
-                    c = caches[l]
+                    c = caches[0][l]
                     if args.paged:
                         c.refill(max(REFILL, m))
                     c.chunk(kd[l][:, T + s0:T + s0 + m], vd[l][:, T + s0:T + s0 + m], kp, qc,
                             out=oc)
             return
         for s in range(S):
+            k = s // R                        # the replica's own step
             for l in range(L):
-                c = caches[l]
+                c = caches[s % R][l]
                 if args.paged and s % REFILL == 0:
                     c.refill(REFILL)
                 if args.unfused:
-                    c.append(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s])
-                    c.attention(qd[l][s], out=outs[l], split_tokens=args.split)
+                    c.append(kd[l][:, T + k], vd[l][:, T + k], keep_new[l][k])
+                    c.attention(qd[l][k], out=outs[l], split_tokens=args.split)
                 else:
-                    c.decode_step(kd[l][:, T + s], vd[l][:, T + s], keep_new[l][s], qd[l][s],
+                    c.decode_step(kd[l][:, T + k], vd[l][:, T + k], keep_new[l][k], qd[l][k],
                                   out=outs[l], split_tokens=args.split)
 
     # one eager pass first: loads the library, sizes the workspaces
@@ -264,8 +401,8 @@ def main():
             decode_all()
         torch.cuda.synchronize()
         graphs = (g_pre, g_dec)
-        log(f"captured {2 * L} prefill and {S * L * (2 if args.unfused else 1)} decode launches "
-            f"in two graphs")
+        log(f"captured {2 * L * R} prefill and {S * L * (2 if args.unfused else 1)} decode "
+            f"launches in two graphs")
 
     stream = torch.cuda.current_stream(dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -283,10 +420,11 @@ def main():
             decode_all()
         ev[2].record(stream)
 
+    all_caches = [c for reps in caches for c in reps]
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    words = [c.error_word() for c in caches]
+    words = [c.error_word() for c in all_caches]
     if any(words):
         raise RuntimeError(f"device error words set during warm-up: {words} "
                            f"(1 capacity, 2 pool, 16 merge wait, 32 stale host plan)")
@@ -305,14 +443,19 @@ def main():
             f"decode {decode_ms_l[-1]:.2f} ms)")
 
     # the device state after the last step must match the host accounting
-    for l in range(L):
-        c = caches[l]
-        ring = np.minimum(c.pos[:B].cpu().numpy().astype(np.int64), W)
-        got = ring[:, None] + c.comp_len.cpu().numpy().astype(np.int64).reshape(B, Hkv)
-        if not np.array_equal(got, nrows[l][S - 1]):
-            raise RuntimeError(f"layer {l}: device stored-row counts differ from the keep mask")
-        if caches[l].error_word() != 0:
-            raise RuntimeError(f"layer {l}: device error word set")
+    dev_rows = []
+    for r in range(R):
+        dev_rows.append([])
+        for l in range(L):
+            c = caches[r][l]
+            ring = np.minimum(c.pos[:B].cpu().numpy().astype(np.int64), W)
+            got = ring[:, None] + c.comp_len.cpu().numpy().astype(np.int64).reshape(B, Hkv)
+            if args.chunk <= 0 and not np.array_equal(got, nrows[l][S_r[r] - 1]):
+                raise RuntimeError(f"replica {r} layer {l}: device stored-row counts differ "
+                                   f"from the keep mask")
+            if c.error_word() != 0:
+                raise RuntimeError(f"replica {r} layer {l}: device error word set")
+            dev_rows[r].append(got)
 
     # Per-launch duration of the decode-step kernel: the decode part of each
     # timed step (S x L back-to-back launches on this stream, between two HIP
@@ -320,7 +463,8 @@ def main():
     # algorithmic bytes per launch are the mean over the same launches.  With
     # --unfused this is the time of one layer step (APPEND + attention).
     n_calls = (len(chunks[0]) if args.chunk > 0 else S) * L
-    kernel_us = float(np.mean(decode_ms_l)) * 1e3 / n_calls
+    launch_us = [d * 1e3 / n_calls for d in decode_ms_l]
+    kernel_us = float(np.mean(launch_us))
     bytes_per_launch = float(attn_bytes.mean())
     flops_per_call = None
     if args.chunk > 0:
@@ -349,19 +493,49 @@ def main():
                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
                     "traffic": None}
     else:
-        roofline = None
-    # the committed counters are those of the default run (this config, FP8)
-    traffic = (traffic_from_profile() if (args.config, kv) == ("qwen_c8", "fp8") and
-               not args.paged else None)
+        # the committed counters are those of the default run (this config, FP8)
+        traffic = (traffic_from_profile() if (args.config, kv, R) == ("qwen_c8", "fp8", 1) and
+                   not args.paged and not args.unfused else None)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
-    cpu = None
-    if not args.no_cpu_baseline:
+    # the realised compression of the store after the last decode step
+    # (replica 0): stored rows x K and V rows (+ two f32 scales per head for
+    # FP8 / FP4), against dense pools of every position 0 .. T + S - 1
+    stored = sum(int(dev_rows[0][l].sum()) for l in range(L))
+    compact_bytes = stored * 2 * row_bytes + (0 if kv == "bf16" else 8 * B * Hkv * L)
+    tokens_dense = T + S_r[0]
+    dense_bf16 = L * B * Hkv * tokens_dense * 2 * D * 2
+    dense_same = L * B * Hkv * tokens_dense * 2 * D * ELEM_BYTES[kv]
+    compression = {"vs_dense_bf16": round(dense_bf16 / compact_bytes, 3),
+                   "vs_dense_same_dtype": round(dense_same / compact_bytes, 3),
+                   "compact_kv_bytes": int(compact_bytes), "dense_bf16_bytes": int(dense_bf16),
+                   "stored_rows_per_head_mean": round(stored / (L * B * Hkv), 1),
+                   "positions_per_head": tokens_dense}
+
+    ceiling = None
+    if not args.no_ceiling and not args.paged and args.chunk <= 0:
+        log("measuring the read ceiling (tile streaming)")
+        c0 = caches[0][0]
+        sbh = c0.seg_base_host.numpy()
+        rows0 = dev_rows[0][0].reshape(-1)
+        tiles = [int(sbh[i]) // 64 + t for i in range(B * Hkv) for t in range(-(-int(rows0[i]) // 64))]
+        ceiling = read_ceiling(torch, dev, 64 * row_bytes, tiles)
+        ceiling["frac_of_ceiling"] = round(achieved / ceiling["stream_gbs"], 4)
+        ceiling["launch_over_layer_tiles_floor"] = round(kernel_us / ceiling["layer_tiles_us"], 3)
+
+    cpu, cpu_extra = None, {}
+    if not args.no_cpu_baseline and args.chunk <= 0 and R == 1 and not args.paged:
         log("timing the CPU oracle on a sample")
-        # the answers at the last position: the decode step's output, or the
-        # last query of the last chunk
-        last = outs if args.chunk <= 0 else [chunks[l][-1][4][:, -1] for l in range(L)]
-        cpu, worst, nl = cpu_baseline(cfg, list(range(L)), last, kv)
-        log(f"oracle sample: {nl} layers, GPU max abs err {worst:.2e}")
+        # the GPU's F32 answer at the last position of layer 0: attention
+        # over the store as the last decode step left it
+        out32 = caches[0][0].attention(qd[0][S - 1], out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        cpu, cpu_extra = cpu_baseline(cfg, kv, dev_rows[0][0], out32.cpu().double().numpy())
+        layer0_bytes = int(dev_rows[0][0].sum()) * 2 * row_bytes + (0 if kv == "bf16" else 8 * B * Hkv)
+        if cpu_extra["oracle_compact_kv_bytes_layer0"] != layer0_bytes:
+            raise AssertionError("compact KV bytes of layer 0 differ from the oracle's accounting")
+        log(f"oracle sample done: {cpu['sample']}")
 
     rec = {
         "metric": METRIC,
@@ -381,26 +555,34 @@ def main():
                                (", keep rate x1.5 at layer 0 falling linearly to x0.5 "
                                 "at the last layer" if cfg.budget == "pyramid" else ""),
                    "layers": L, "global_batch": B, "seq_len": T, "gen_len": S,
-                   "kv_storage": kv, "budget": cfg.budget,
+                   "kv_storage": kv, "budget": cfg.budget, "replicas": R,
                    "store": (f"paged: 64-row pages, no prefill reserve, refill every {REFILL} steps"
-                             if args.paged else f"contiguous segments, reserve {S} rows"),
+                             if args.paged else f"contiguous segments, reserve {S_r[0]} rows"),
                    "split_tokens": args.split or "library default",
                    "parallelism": "single GPU"},
+        "ms_per_step_median": pct(step_ms, 50),
+        "ms_per_step_p10": pct(step_ms, 10),
+        "ms_per_step_p90": pct(step_ms, 90),
         "attn_tokens_per_s": round(tokens_per_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         ("chunk_call_us" if args.chunk > 0 else "decode_step_kernel_us"): round(kernel_us, 3),
+        "launch_us_median": pct(launch_us, 50),
+        "launch_us_p10": pct(launch_us, 10),
+        "launch_us_p90": pct(launch_us, 90),
+        "decode_only_gbs": round(step_attn_bytes / (float(np.mean(decode_ms_l)) * 1e-3) / 1e9, 1),
         "prefill_compaction_ms": round(prefill_ms, 3),
         "decode_ms_per_step": round(float(np.mean(decode_ms_l)), 3),
         "launch": ("eager" if args.eager else "hip graphs") +
                   (f", chunks of {args.chunk} tokens (chunk_attn_compact)" if args.chunk > 0 else
                    ", append + attention" if args.unfused else ", fused decode step"),
         "kv_bytes_per_decode_step": round(float(attn_bytes.sum(axis=1).mean())),
-        "kv_pool_mb": round(sum(2 * c.pool_rows * row_bytes for c in caches) / 1e6, 1),
-        "roofline": roofline or {"bound": "hbm", "achieved": round(achieved, 1),
-                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kv_pool_mb": round(sum(2 * c.pool_rows * row_bytes for c in all_caches) / 1e6, 1),
+        "compression_ratio": compression,
+        "roofline": roofline,
+        "ceiling": ceiling,
         "cpu_baseline": cpu,
     }
+    rec.update(cpu_extra)
     print(json.dumps(rec), flush=True)
 
 

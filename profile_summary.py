@@ -2,11 +2,13 @@
 under profiles/.
 
   python profile_summary.py trace <kernel_stats.csv> <command> [note] > profiles/X.md
-  python profile_summary.py traffic <copy FETCH csv> <copy WRITE csv>
+  python profile_summary.py traffic <stream FETCH csv> <copy WRITE csv>
          <bench FETCH csv> <bench WRITE csv> <json path or -> <commands...>
 
-The traffic mode scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
-dispatch) by what the same counter reads for the plain 64 MiB copy of
+The traffic mode scales each kernel's FETCH_SIZE by what that counter reads
+for the 2 GiB tile-streaming read of `bench.py --stream-calibration` (the
+attention's own load pattern: 16-byte nontemporal loads of 64-row tiles) and
+WRITE_SIZE by what it reads for the plain 64 MiB copy of
 `bench.py --copy-calibration`, prints a markdown table, and writes the
 attention kernel's bytes per launch to the JSON path (bench.py reads
 profiles/attn_qwen_c8_traffic.json while it matches the attention kernel
@@ -24,6 +26,7 @@ import sys
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "attn.hip")
 COPY_KIB = 64 * 1024
+STREAM_KIB = 2 * 1024 * 1024
 
 
 def short(name: str) -> str:
@@ -57,20 +60,21 @@ def _mean(path: str, pats: tuple) -> dict:
 # the device-to-device copy of `bench.py --copy-calibration` (the runtime's
 # blit kernel, or torch's elementwise copy, depending on the build)
 COPY_KERNELS = ("copyBuffer", "direct_copy")
+STREAM_KERNELS = ("stream_tiles_kernel",)
 
 
 def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[str]) -> None:
-    fcal = COPY_KIB / list(_mean(cf, COPY_KERNELS).values())[0]
+    fcal = STREAM_KIB / list(_mean(cf, STREAM_KERNELS).values())[0]
     wcal = COPY_KIB / list(_mean(cw, COPY_KERNELS).values())[0]
-    fetch, write = _mean(bf, ("cda",)), _mean(bw, ("cda",))
+    fetch, write = _mean(bf, ("cda::",)), _mean(bw, ("cda::",))
     print("# HBM traffic per dispatch (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)\n")
     print("Commands (from the repository root), one counter per run:\n\n```")
     for c in commands:
         print(c)
     print("```\n")
-    print(f"Calibration: a plain 64 MiB copy reads as FETCH_SIZE x{1 / fcal:.4f} and "
-          f"WRITE_SIZE x{1 / wcal:.4f} of its true KiB, so the counters below are multiplied "
-          f"by {fcal:.4f} and {wcal:.4f}.\n")
+    print(f"Calibration: the 2 GiB tile-streaming read reads as FETCH_SIZE x{1 / fcal:.4f} "
+          f"of its true KiB and a plain 64 MiB copy as WRITE_SIZE x{1 / wcal:.4f}, so the "
+          f"counters below are multiplied by {fcal:.4f} and {wcal:.4f}.\n")
     print("| kernel | fetched MB | written MB |")
     print("|---|---:|---:|")
     for k in fetch:
