@@ -114,8 +114,7 @@ def stream_lib():
         raise RuntimeError(f"{STREAM_LIB} is missing: build it with `python -c 'import "
                            f"__graft_entry__ as g; g.build()'`")
     L = C.CDLL(STREAM_LIB)
-    L.cda_stream_tiles.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_int32,
-                                   C.c_void_p, C.c_void_p]
+    L.cda_stream_tiles.argtypes = [C.c_void_p] * 3 + [C.c_int32] * 4 + [C.c_void_p] * 2
     L.cda_stream_tiles.restype = C.c_int32
     return L
 
@@ -142,42 +141,48 @@ def graph_us(torch, fn, calls, reps=5):
     return float(np.median(t))
 
 
+STREAM_SHAPES = [(w, sp) for sp in (0, 1) for w in (1, 2, 4, 8)]   # (waves per group, split)
+
+
 def read_ceiling(torch, dev, tile_bytes, layer_tiles):
     """The plain streaming read of 64-row tiles (the attention's access
-    pattern, no arithmetic): GB/s over 2 GiB, and the time and GB/s of
-    reading exactly the tiles of one layer's launch."""
+    pattern, no arithmetic), in each launch shape: GB/s over 2 GiB, and the
+    time of reading exactly the tiles of one layer's launch; the best shape
+    of each is the ceiling and the load-only floor."""
     L = stream_lib()
     stream = lambda: C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     buf = torch.empty(CEILING_BYTES, dtype=torch.uint8, device=dev)
     half = CEILING_BYTES // 2
     n_big = half // tile_bytes
-    sink = torch.empty(max(n_big, len(layer_tiles)), dtype=torch.int32, device=dev)
-
-    def big():
-        st = L.cda_stream_tiles(C.c_void_p(buf.data_ptr()), C.c_void_p(buf.data_ptr() + half),
-                                None, n_big, tile_bytes, C.c_void_p(sink.data_ptr()), stream())
-        assert st == 0, st
-    us_big = graph_us(torch, big, 10)
-    gbs_big = 2 * n_big * tile_bytes / (us_big * 1e-6) / 1e9
+    sink = torch.empty(2 * max(n_big, len(layer_tiles)), dtype=torch.int32, device=dev)
     tiles = torch.as_tensor(np.asarray(layer_tiles, np.int32), device=dev)
     n_layer = len(layer_tiles)
+    assert int(np.max(layer_tiles)) < n_big     # the layer's tile offsets, inside each half
 
-    def layer():
-        st = L.cda_stream_tiles(C.c_void_p(buf.data_ptr()), C.c_void_p(buf.data_ptr() + half),
-                                C.c_void_p(tiles.data_ptr()), n_layer, tile_bytes,
-                                C.c_void_p(sink.data_ptr()), stream())
-        assert st == 0, st
-    # the layer's tile list read from the big buffer: the same tile offsets
-    # and count as the layer's pools, all inside each half
-    assert int(np.max(layer_tiles)) < n_big
-    us_layer = graph_us(torch, layer, 200)
-    gbs_layer = 2 * n_layer * tile_bytes / (us_layer * 1e-6) / 1e9
+    def call(listed, n, waves, split):
+        def f():
+            st = L.cda_stream_tiles(C.c_void_p(buf.data_ptr()), C.c_void_p(buf.data_ptr() + half),
+                                    C.c_void_p(tiles.data_ptr()) if listed else None, n,
+                                    tile_bytes, waves, split, C.c_void_p(sink.data_ptr()),
+                                    stream())
+            assert st == 0, st
+        return f
+    big, lay = {}, {}
+    for w, sp in STREAM_SHAPES:
+        us = graph_us(torch, call(False, n_big, w, sp), 10)
+        big[f"w{w}s{sp}"] = round(2 * n_big * tile_bytes / (us * 1e-6) / 1e9, 1)
+        lay[f"w{w}s{sp}"] = round(graph_us(torch, call(True, n_layer, w, sp), 200), 3)
     del buf
-    return {"stream_gbs": round(gbs_big, 1), "stream_bytes": CEILING_BYTES,
-            "layer_tiles_us": round(us_layer, 3), "layer_tiles_gbs": round(gbs_layer, 1),
+    best_big = max(big, key=big.get)
+    best_lay = min(lay, key=lay.get)
+    return {"stream_gbs": big[best_big], "stream_shape": best_big, "stream_bytes": CEILING_BYTES,
+            "layer_tiles_us": lay[best_lay], "layer_tiles_shape": best_lay,
+            "layer_tiles_gbs": round(2 * n_layer * tile_bytes / (lay[best_lay] * 1e-6) / 1e9, 1),
             "layer_tile_bytes": 2 * n_layer * tile_bytes,
-            "kernel": "cda_stream_tiles: one wave per 64-row tile, 16-byte nontemporal loads "
-                      "of its K then V tile, 8 waves per workgroup"}
+            "stream_gbs_by_shape": big, "layer_tiles_us_by_shape": lay,
+            "kernel": "cda_stream_tiles: 16-byte nontemporal loads of whole 64-row tiles; shape "
+                      "wXsY = X waves per workgroup, Y = 1: one wave per K or V tile, Y = 0: "
+                      "one wave reads a K tile then its V tile"}
 
 
 def cpu_baseline(cfg, kv, dev_rows_l0, out_f32_l0, budget_note=""):
@@ -290,7 +295,7 @@ def main():
         for _ in range(3):
             assert L_.cda_stream_tiles(C.c_void_p(buf.data_ptr()),
                                        C.c_void_p(buf.data_ptr() + half), None, half // tb, tb,
-                                       C.c_void_p(sink.data_ptr()),
+                                       8, 0, C.c_void_p(sink.data_ptr()),
                                        C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)) == 0
         torch.cuda.synchronize()
         log(f"streamed {CEILING_BYTES >> 20} MiB three times ({half // tb} tiles of 2 x {tb} B)")
