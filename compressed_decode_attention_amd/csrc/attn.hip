@@ -269,7 +269,10 @@ __device__ __forceinline__ bool find_unit(const AttnParams& p, int k, int lane, 
       const int src = __ffsll((long long)mine) - 1;
       un.i = base + src;
       un.first = lane_i(ex, src);
-      un.U = lane_i(Ui, src);
+      // units past the grid do not exist: a store whose segments need more
+      // units than its pool allows (inconsistent pool_rows or seg_cap) has
+      // its last segment cut short here, and the kernel flags it
+      un.U = min(lane_i(Ui, src), (int)gridDim.x - un.first);
       un.n = lane_i(ni, src);
       un.sb = lane_l(sbi, src);
       un.ka = lane_f(ka, src);
@@ -392,6 +395,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     if (APP) raw_kn = p.keep_new[un.i];
   } else {
     if (!find_unit<Q, APP, PG>(p, w, lane, un)) return;
+    if (w == un.first && tid == 0 && un.U < units_of(un.n, p.tpu))
+      atomicOr(p.err, CDA_DEVERR_POOL);
     // every load of the plan has been used: say so, so that no later write to
     // a register it used waits for the loads issued after this point
     __builtin_amdgcn_s_waitcnt(0);
@@ -460,8 +465,11 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     if (!plan_ok && tid == 0) atomicOr(p.err, CDA_DEVERR_PLAN);
   }
   const int64_t sb = un.sb;
-  // rows of the segment inside the pool (paged: every page is checked)
-  const int64_t in_pool = PG ? INT64_MAX : (plan_ok ? p.pool_rows - sb : 0);
+  // rows of the segment inside the pool, in whole tiles (paged: every page is
+  // checked); tiles past them are not read, and flagged (CDA_DEVERR_POOL)
+  const int64_t in_pool =
+      PG ? INT64_MAX
+         : (plan_ok && sb >= 0 && (sb & (kTile - 1)) == 0 ? max(p.pool_rows - sb, (int64_t)0) : 0);
   const float ks = kv_scale<KV>(un.ka);
   const float vs = kv_scale<KV>(un.va);
   // paged store: the page of this wave's first tile, loaded before anything
@@ -814,13 +822,17 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     // the tile whose loads went out first
     int rko = 0;
     if (APP) rko = *rkp;   // issued after that tile's loads
-    const int valid = (int)min((int64_t)min(kTile, n - t * kTile), in_pool - (int64_t)t * kTile);
+    const int want = min(kTile, n - t * kTile);
+    const int valid = (int)min((int64_t)want, in_pool - (int64_t)t * kTile);
+    if (t < t_end && want > 0 && valid < want && lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
     if (t < t_end && valid > 0) tile_body(valid, APP && t == t_own, rko);
     t += NW;
   }
   for (; t < t_end; t += NW) {
     const int r0 = t * kTile;
-    const int valid = (int)min((int64_t)min(kTile, n - r0), in_pool - r0);
+    const int want = min(kTile, n - r0);
+    const int valid = (int)min((int64_t)want, in_pool - r0);
+    if (want > 0 && valid < want && lane == 0) atomicOr(p.err, CDA_DEVERR_POOL);
     if (valid <= 0) break;
     int64_t trow = sb + r0;   // pool row of the tile
     if (PG) {

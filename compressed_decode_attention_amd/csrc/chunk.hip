@@ -297,7 +297,17 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       if (PG) {
         const int pg = p.page_table[(int64_t)i * p.max_pages + min(tt, p.max_pages - 1)];
         ok = tt < p.max_pages && pg >= 0 && pg < p.n_pages;
-        trow = ok ? (int64_t)pg * kTile : 0;
+        trow = (int64_t)pg * kTile;
+      } else {
+        // the whole tile inside the pool (a pool smaller than the segments
+        // COUNT laid out, or a seg_base entry that is not one of its rows)
+        ok = sb >= 0 && (sb & (kTile - 1)) == 0 && trow + kTile <= p.pool_rows;
+      }
+      if (!ok) {   // wave-uniform: nothing read; the tile is not computed (CDA_DEVERR_POOL)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) rg[c] = u32x4{0, 0, 0, 0};
+        kb = 0;
+        return;
       }
       kt = p.k_pool + trow * RB;
       vt = p.v_pool + trow * RB;

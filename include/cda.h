@@ -128,7 +128,9 @@ enum cda_status {
 /* Bits of the device error word cache->err (set with atomic OR on the GPU;
  * the host sees them only after it synchronises and copies the word). */
 #define CDA_DEVERR_CAPACITY 1   /* APPEND: a segment's compact region was full; that token was dropped */
-#define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written */
+#define CDA_DEVERR_POOL 2       /* PACK/APPEND: a row fell outside [0, pool_rows); not written.
+                                   Attention, chunk: a tile of stored rows lies outside the pool
+                                   (pool_rows below seg_base[B*Hkv]); not read */
 #define CDA_DEVERR_PAGES 8      /* paged COUNT / REFILL: not enough free pages, or a segment
                                    would need more than max_pages (see the paged store) */
 #define CDA_DEVERR_MERGE 16     /* attention: a split segment's partial results did not all
