@@ -19,35 +19,54 @@ constexpr int kMaxWaves = 8;
 
 // Job j = blockIdx.x * (blockDim.x / 64) + wave.  Without split, job j reads
 // tile tiles[j] (or j without a list) of both buffers; with split, job j
-// reads tile tiles[j / 2] of k (j even) or of v (j odd).  A tile is
-// tile_kb loads of 16 bytes per lane.
+// reads tile tiles[j / 2] of k (j even) or of v (j odd).  A tile is KB loads
+// of 16 bytes per lane; every load of the job is issued before the first
+// result is used.
+template <int KB>
 __global__ __launch_bounds__(64 * kMaxWaves) void stream_tiles_kernel(
     const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
-    const int32_t* __restrict__ tiles, int n_jobs, int tile_kb, int split,
-    uint32_t* __restrict__ sink) {
+    const int32_t* __restrict__ tiles, int n_jobs, int split, uint32_t* __restrict__ sink) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = blockIdx.x * (blockDim.x >> 6) + wave;
   if (j >= n_jobs) return;
   const int i = split ? j >> 1 : j;
   const int64_t t = tiles ? tiles[i] : i;
-  const int64_t off = t * (int64_t)tile_kb * 1024 + lane * 16;
-  const uint8_t* first = (split && (j & 1)) ? v + off : k + off;
-  u32x4 acc = u32x4{0, 0, 0, 0};
-  for (int c = 0; c < tile_kb; ++c)
-    acc ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(first + c * 1024));
-  if (!split)
-    for (int c = 0; c < tile_kb; ++c)
-      acc ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off + c * 1024));
-  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
-  if (lane == 0) sink[j] = x;
+  const int64_t off = t * (int64_t)KB * 1024 + lane * 16;
+  u32x4 x[2 * KB];
+  if (split) {
+    const uint8_t* src = (j & 1) ? v + off : k + off;
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+      x[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 1024));
+#pragma unroll
+    for (int c = KB; c < 2 * KB; ++c) x[c] = u32x4{0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+      x[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off + c * 1024));
+#pragma unroll
+    for (int c = 0; c < KB; ++c)
+      x[KB + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off + c * 1024));
+  }
+  // every load is in flight before the first result is waited for: no load
+  // moves below the first statement, and the results are all taken (with one
+  // wait for the last) before any is combined
+  __asm__ volatile("" ::: "memory");
+#pragma unroll
+  for (int c = 0; c < 2 * KB; ++c) __asm__ volatile("" : "+v"(x[c]));
+  u32x4 acc = x[0];
+#pragma unroll
+  for (int c = 1; c < 2 * KB; ++c) acc ^= x[c];
+  uint32_t y = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int o = 32; o > 0; o >>= 1) y ^= __shfl_xor(y, o, 64);
+  if (lane == 0) sink[j] = y;
 }
 
 }  // namespace
 
 extern "C" {
 
-// Reads n_tiles tiles of tile_bytes (a multiple of 1024) from k and from v:
+// Reads n_tiles tiles of tile_bytes (4096, 8192 or 16384) from k and from v:
 // tile tiles[j] (or tile j if tiles is NULL) at byte tiles[j] * tile_bytes of
 // each buffer, all of which the caller guarantees to be inside them.
 // waves: waves per workgroup, 1 to 8.  split = 0: one wave reads a tile of k
@@ -58,15 +77,19 @@ extern "C" {
 int32_t cda_stream_tiles(const void* k, const void* v, const int32_t* tiles, int32_t n_tiles,
                          int32_t tile_bytes, int32_t waves, int32_t split, uint32_t* sink,
                          void* stream) {
-  if (n_tiles < 0 || n_tiles > (1 << 29) || tile_bytes <= 0 || tile_bytes % 1024 != 0 ||
-      waves < 1 || waves > kMaxWaves || (split != 0 && split != 1) || !k || !v || !sink)
+  if (n_tiles < 0 || n_tiles > (1 << 29) ||
+      (tile_bytes != 4096 && tile_bytes != 8192 && tile_bytes != 16384) || waves < 1 ||
+      waves > kMaxWaves || (split != 0 && split != 1) || !k || !v || !sink)
     return 1;
   if (n_tiles == 0) return 0;
   const int jobs = split ? 2 * n_tiles : n_tiles;
-  const int grid = (jobs + waves - 1) / waves;
-  stream_tiles_kernel<<<grid, 64 * waves, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), tiles, jobs,
-      tile_bytes / 1024, split, sink);
+  const dim3 grid((jobs + waves - 1) / waves), block(64 * waves);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* kb = static_cast<const uint8_t*>(k);
+  const uint8_t* vb = static_cast<const uint8_t*>(v);
+  if (tile_bytes == 4096) stream_tiles_kernel<4><<<grid, block, 0, s>>>(kb, vb, tiles, jobs, split, sink);
+  else if (tile_bytes == 8192) stream_tiles_kernel<8><<<grid, block, 0, s>>>(kb, vb, tiles, jobs, split, sink);
+  else stream_tiles_kernel<16><<<grid, block, 0, s>>>(kb, vb, tiles, jobs, split, sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
