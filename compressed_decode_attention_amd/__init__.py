@@ -21,7 +21,7 @@ from ._lib import (CDA_DEVERR_CAPACITY, CDA_DEVERR_MERGE, CDA_DEVERR_PAGES, CDA_
                    CDA_OUT_F32, CDA_SEG_ALIGN, CdaCompactArgs, CdaError, CdaKvCache)
 
 __all__ = ["CompactKVCache", "PagedKVCache", "kv_compact", "decode_attn_compact",
-           "decode_step_compact", "chunk_attn_compact", "CdaError", "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY",
+           "decode_step_compact", "decode_step_compact_noalloc", "chunk_attn_compact", "CdaError", "CDA_SEG_ALIGN", "CDA_DEVERR_CAPACITY",
            "CDA_DEVERR_POOL", "CDA_DEVERR_PAGES", "CDA_DEVERR_MERGE", "CDA_DEVERR_PLAN"]
 
 _DTYPES = {"bf16": CDA_KV_BF16, "fp8": CDA_KV_FP8_E4M3, "fp4": CDA_KV_FP4_E2M1}
@@ -155,6 +155,24 @@ def decode_step_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: tor
                                   _stream(cache.device))
     if st != 0:
         raise CdaError(st, "decode_step_compact")
+
+
+def decode_step_compact_noalloc(cache: "CompactKVCache", k_new: torch.Tensor,
+                                v_new: torch.Tensor, keep_new: torch.Tensor, q: torch.Tensor,
+                                out: torch.Tensor, lse: torch.Tensor | None = None,
+                                sm_scale: float = 0.0, split_tokens: int = 0) -> None:
+    """One decode_step_compact_noalloc call: decode_step_compact without a
+    workspace (the library's static per-GPU scratch is used instead; the
+    stream must belong to the current device)."""
+    _check_attention(cache, q, out, lse)
+    Hq = q.shape[1]
+    a = _compact_args(cache, CDA_OP_APPEND, keep=keep_new, k=k_new, v=v_new)
+    out_dtype = CDA_OUT_F32 if out.dtype == torch.float32 else CDA_OUT_BF16
+    st = _lib.decode_step_compact_noalloc(cache.struct, a, _ptr(q), Hq, sm_scale, _ptr(out),
+                                          out_dtype, _ptr(lse), split_tokens,
+                                          _stream(cache.device))
+    if st != 0:
+        raise CdaError(st, "decode_step_compact_noalloc")
 
 
 def chunk_attn_compact(cache: "CompactKVCache", k_new: torch.Tensor, v_new: torch.Tensor,
@@ -326,6 +344,16 @@ class CompactKVCache:
             out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
         decode_step_compact(self, k_new, v_new, keep_new, q, out, lse, sm_scale, split_tokens,
                             workspace)
+        return out
+
+    def decode_step_noalloc(self, k_new, v_new, keep_new, q, out=None,
+                            out_dtype=torch.bfloat16, lse=None, sm_scale: float = 0.0,
+                            split_tokens: int = 0) -> torch.Tensor:
+        """decode_step through decode_step_compact_noalloc (no workspace)."""
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dtype, device=self.device)
+        decode_step_compact_noalloc(self, k_new, v_new, keep_new, q, out, lse, sm_scale,
+                                    split_tokens)
         return out
 
     # ---- inspection (synchronise)

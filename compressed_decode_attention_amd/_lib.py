@@ -19,14 +19,16 @@ CDA_KV_BF16, CDA_KV_FP8_E4M3, CDA_KV_FP4_E2M1 = 0, 1, 2
 CDA_OUT_BF16, CDA_OUT_F32 = 0, 1
 CDA_OP_COUNT, CDA_OP_PACK, CDA_OP_APPEND = 0, 1, 2
 CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE = 3, 4, 5
-CDA_VERSION = 3       # the struct layouts below are those of this version
+CDA_VERSION = 4       # the struct layouts below are those of this version
+CDA_SCRATCH_BYTES = 4 << 20   # device scratch of decode_step_compact_noalloc, per GPU
 CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16
 CDA_MAX_CHUNK = 64
 CDA_MAX_CHUNK_WINDOW = 4096
 
 # every symbol include/cda.h declares
-EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact", "chunk_attn_compact",
+EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact",
+           "decode_step_compact_noalloc", "chunk_attn_compact",
            "cda_attn_workspace_bytes", "cda_chunk_workspace_bytes", "cda_status_string",
            "cda_version")
 
@@ -86,6 +88,10 @@ def load(path: str = LIB_PATH):
                                       C.c_int32, C.c_float, C.c_void_p, C.c_int32, C.c_void_p,
                                       C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]
     L.decode_step_compact.restype = C.c_int32
+    L.decode_step_compact_noalloc.argtypes = [C.POINTER(CdaKvCache), C.POINTER(CdaCompactArgs),
+                                              C.c_void_p, C.c_int32, C.c_float, C.c_void_p,
+                                              C.c_int32, C.c_void_p, C.c_int32, C.c_void_p]
+    L.decode_step_compact_noalloc.restype = C.c_int32
     L.cda_attn_workspace_bytes.argtypes = [C.POINTER(CdaKvCache), C.c_int32, C.c_int32]
     L.cda_attn_workspace_bytes.restype = C.c_size_t
     L.chunk_attn_compact.argtypes = [C.POINTER(CdaKvCache), C.POINTER(CdaCompactArgs), C.c_int32,
@@ -134,6 +140,15 @@ def decode_step_compact(cache: CdaKvCache, args: CdaCompactArgs, q_ptr: int, Hq:
         C.byref(cache), C.byref(args), C.c_void_p(q_ptr), int(Hq), float(sm_scale),
         C.c_void_p(out_ptr), int(out_dtype), C.c_void_p(lse_ptr or 0), int(split_tokens),
         C.c_void_p(ws_ptr or 0), C.c_size_t(ws_bytes), C.c_void_p(stream or 0)))
+
+
+def decode_step_compact_noalloc(cache: CdaKvCache, args: CdaCompactArgs, q_ptr: int, Hq: int,
+                                sm_scale: float, out_ptr: int, out_dtype: int,
+                                lse_ptr: int | None, split_tokens: int, stream: int | None) -> int:
+    return int(load().decode_step_compact_noalloc(
+        C.byref(cache), C.byref(args), C.c_void_p(q_ptr), int(Hq), float(sm_scale),
+        C.c_void_p(out_ptr), int(out_dtype), C.c_void_p(lse_ptr or 0), int(split_tokens),
+        C.c_void_p(stream or 0)))
 
 
 def chunk_attn_compact(cache: CdaKvCache, args: CdaCompactArgs, M: int, q_ptr: int, Hq: int,

@@ -3,8 +3,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/cda.h"
 #include "cda_launch.h"
+
+// Scratch of decode_step_compact_noalloc: the attention workspace (counters
+// and partial slots) as a device array of its own, one per GPU the library
+// runs on, held until the process ends.  Host code uses only the address
+// hipGetSymbolAddress gives for it on each device, never the array's name.
+static __device__ __align__(256) uint8_t scratch[CDA_SCRATCH_BYTES];
 
 namespace {
 
@@ -66,6 +74,47 @@ int32_t check_bf16_rows(const void* k, const void* v, int64_t sb, int64_t st, in
 }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? CDA_OK : CDA_ERR_HIP; }
+
+// Per device: the device address of `scratch` and whether its zero fill has
+// been enqueued.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_zeroed[kMaxDevices] = {};
+
+__global__ void zero_words(uint4* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = uint4{0, 0, 0, 0};
+}
+
+// The scratch address on the current device (which must be the stream's),
+// looked up on the first call on that device; that call also enqueues the
+// array's zero fill on the stream, ahead of the kernel that first uses it
+// (a kernel, not a memset, so that a captured graph replays it as well).
+int32_t device_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CDA_ERR_HIP;
+  if (s) {
+    int sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return CDA_ERR_HIP;
+    if (sdev != dev) return CDA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CDA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  if (!g_scratch_zeroed[dev]) {
+    const int64_t n = CDA_SCRATCH_BYTES / 16;
+    zero_words<<<256, 256, 0, s>>>(static_cast<uint4*>(g_scratch_ptr[dev]), n);
+    if (hipGetLastError() != hipSuccess) return CDA_ERR_HIP;
+    g_scratch_zeroed[dev] = true;
+  }
+  *out = g_scratch_ptr[dev];
+  return CDA_OK;
+}
 
 // The optional host copy of seg_base (contiguous store): non-decreasing
 // multiples of 64 starting at 0, the last entry inside the pool.
@@ -161,11 +210,11 @@ size_t cda_attn_workspace_bytes(const cda_kv_cache* c, int32_t Hq, int32_t split
 
 namespace {
 
-// Checks shared by the two attention entry points; on success *tpu is the
-// work-unit size in tiles.
-int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* out,
-                        int32_t out_dtype, float* lse, int32_t split_tokens, void* workspace,
-                        size_t workspace_bytes, int* tpu) {
+// Checks shared by the attention entry points, all but the workspace's; on
+// success *tpu is the work-unit size in tiles and *need the workspace bytes.
+int32_t check_attention_args(const cda_kv_cache* c, const void* q, int32_t Hq, void* out,
+                             int32_t out_dtype, float* lse, int32_t split_tokens, int* tpu,
+                             size_t* need) {
   int32_t st = check_cache(c);
   if (st != CDA_OK) return st;
   if ((st = check_pools(c)) != CDA_OK) return st;
@@ -178,10 +227,31 @@ int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* 
   }
   if ((st = check_seg_base_host(c)) != CDA_OK) return st;
   *tpu = tiles_per_unit(c, split_tokens);
-  const size_t need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, *tpu);
+  *need = cda::attn_workspace_bytes(*c, Hq / c->Hkv, *tpu);
+  if (cda::attn_max_units(*c, *tpu) > 0x7FFFFFFF) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+// check_attention_args, then the caller's workspace.
+int32_t check_attention(const cda_kv_cache* c, const void* q, int32_t Hq, void* out,
+                        int32_t out_dtype, float* lse, int32_t split_tokens, void* workspace,
+                        size_t workspace_bytes, int* tpu) {
+  size_t need = 0;
+  const int32_t st = check_attention_args(c, q, Hq, out, out_dtype, lse, split_tokens, tpu, &need);
+  if (st != CDA_OK) return st;
   if (workspace_bytes < need) return CDA_ERR_WORKSPACE;
   if (need > 0 && (!workspace || !aligned(workspace, 16))) return CDA_ERR_INVALID_ARG;
-  if (cda::attn_max_units(*c, *tpu) > 0x7FFFFFFF) return CDA_ERR_INVALID_ARG;
+  return CDA_OK;
+}
+
+// The APPEND arguments of a decode step.
+int32_t check_step_args(const cda_kv_cache* c, const cda_compact_args* a) {
+  if (!a || a->op != CDA_OP_APPEND || a->seq_begin != 0 || a->seq_count != 0)
+    return CDA_ERR_INVALID_ARG;
+  if (c->B > 0) {
+    if (!a->keep) return CDA_ERR_INVALID_ARG;
+    return check_bf16_rows(a->k, a->v, a->stride_b, 0, a->stride_h);
+  }
   return CDA_OK;
 }
 
@@ -209,15 +279,29 @@ int32_t decode_step_compact(const cda_kv_cache* c, const cda_compact_args* a, co
   int32_t st = check_attention(c, q, Hq, out, out_dtype, lse, split_tokens, workspace,
                                workspace_bytes, &tpu);
   if (st != CDA_OK) return st;
-  if (!a || a->op != CDA_OP_APPEND || a->seq_begin != 0 || a->seq_count != 0)
-    return CDA_ERR_INVALID_ARG;
-  if (c->B > 0) {
-    if (!a->keep) return CDA_ERR_INVALID_ARG;
-    if ((st = check_bf16_rows(a->k, a->v, a->stride_b, 0, a->stride_h)) != CDA_OK) return st;
-  }
+  if ((st = check_step_args(c, a)) != CDA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(cda::launch_attn(*c, q, Hq, sm_scale, out, out_dtype == CDA_OUT_F32, lse,
                                      tpu, workspace, s, a));
+}
+
+int32_t decode_step_compact_noalloc(const cda_kv_cache* c, const cda_compact_args* a,
+                                    const void* q, int32_t Hq, float sm_scale, void* out,
+                                    int32_t out_dtype, float* lse, int32_t split_tokens,
+                                    void* stream) {
+  // every argument checked, and the scratch the call needs against the
+  // array's size, before any HIP call; the array stands in for the workspace
+  int tpu = 0;
+  size_t need = 0;
+  int32_t st = check_attention_args(c, q, Hq, out, out_dtype, lse, split_tokens, &tpu, &need);
+  if (st != CDA_OK) return st;
+  if (need > CDA_SCRATCH_BYTES) return CDA_ERR_WORKSPACE;
+  if ((st = check_step_args(c, a)) != CDA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ptr = nullptr;
+  if ((st = device_scratch(s, &ptr)) != CDA_OK) return st;
+  return hip_status(cda::launch_attn(*c, q, Hq, sm_scale, out, out_dtype == CDA_OUT_F32, lse,
+                                     tpu, ptr, s, a));
 }
 
 size_t cda_chunk_workspace_bytes(const cda_kv_cache* c, int32_t Hq, int32_t M) {

@@ -110,9 +110,10 @@
 extern "C" {
 #endif
 
-#define CDA_VERSION 3
+#define CDA_VERSION 4
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
+#define CDA_SCRATCH_BYTES (4u << 20) /* device scratch of decode_step_compact_noalloc, per GPU */
 #define CDA_MAX_CHUNK 64        /* largest chunk of chunk_attn_compact */
 #define CDA_MAX_CHUNK_WINDOW 4096   /* largest W chunk_attn_compact takes */
 
@@ -121,7 +122,8 @@ enum cda_status {
     CDA_OK = 0,
     CDA_ERR_INVALID_ARG = 1,    /* NULL or misaligned pointer, bad size/stride */
     CDA_ERR_UNSUPPORTED = 2,    /* head_dim not 64/128, Hq % Hkv != 0, Hq/Hkv > 16, dtype */
-    CDA_ERR_WORKSPACE = 3,      /* workspace smaller than cda_attn_workspace_bytes */
+    CDA_ERR_WORKSPACE = 3,      /* workspace smaller than cda_attn_workspace_bytes (noalloc:
+                                   the call needs more than CDA_SCRATCH_BYTES) */
     CDA_ERR_HIP = 4             /* a kernel launch failed (hipGetLastError) */
 };
 
@@ -299,6 +301,29 @@ int32_t decode_step_compact(const cda_kv_cache *cache, const cda_compact_args *a
                             const void *q, int32_t Hq, float sm_scale, void *out,
                             int32_t out_dtype, float *lse, int32_t split_tokens,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * decode_step_compact_noalloc -- decode_step_compact for callers that cannot
+ * allocate device memory or own a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * and results as decode_step_compact, without the workspace: the library
+ * keeps one static device array of CDA_SCRATCH_BYTES per GPU (allocated
+ * with the code object, held until the process ends) and uses it in its
+ * place.  Nothing is allocated or freed by the call.
+ *
+ *   Returns CDA_ERR_WORKSPACE, before anything is enqueued, when the call
+ *   needs more scratch than CDA_SCRATCH_BYTES (cda_attn_workspace_bytes of
+ *   the same cache, Hq and split_tokens); CDA_ERR_INVALID_ARG when the
+ *   stream does not belong to the current device.  The first call on a GPU
+ *   enqueues the array's zero fill ahead of its kernel; every completed call
+ *   leaves it zero-filled again.  All calls on one GPU share its array:
+ *   calls that may run concurrently on one GPU (different streams without
+ *   ordering between them) race and must not be issued.
+ */
+int32_t decode_step_compact_noalloc(const cda_kv_cache *cache, const cda_compact_args *args,
+                                    const void *q, int32_t Hq, float sm_scale, void *out,
+                                    int32_t out_dtype, float *lse, int32_t split_tokens,
+                                    void *stream);
 
 /* Workspace bytes decode_attn_compact and decode_step_compact need for this
  * cache, Hq and split. */

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.version() == lib.CDA_VERSION == 3
+    assert lib.version() == lib.CDA_VERSION == 4
     assert lib.status_string(0) == "ok"
     assert lib.status_string(3) == "workspace too small"
     assert lib.status_string(99) == "unknown status"
@@ -288,3 +288,26 @@ def test_host_seg_base_is_checked(lib, table):
     st = L.decode_attn_compact(C.byref(c), C.c_void_p(q), 8, 0.0, C.c_void_p(out), 0, None, 0,
                                C.c_void_p(ws), C.c_size_t(need), None)
     assert st == lib.CDA_ERR_INVALID_ARG
+
+
+def test_noalloc_step_validates_before_any_hip_call(lib):
+    """decode_step_compact_noalloc: the scratch the call needs is checked
+    against CDA_SCRATCH_BYTES, and every argument, before anything is
+    enqueued (fake pointers: no call here reaches a kernel)."""
+    L = lib.load()
+    a = lib.CdaCompactArgs()
+    a.op, a.keep, a.k, a.v = lib.CDA_OP_APPEND, 0x100000, 0x100000, 0x100000
+    q = out = C.c_void_p(0x100000)
+    big = _cache(lib, pool_rows=64 * 100000)      # 12502 units of 8 x 64 f32 partials
+    need = L.cda_attn_workspace_bytes(C.byref(big), 16, 0)
+    assert need > lib.CDA_SCRATCH_BYTES
+    assert L.decode_step_compact_noalloc(C.byref(big), C.byref(a), q, 16, 0.0, out, 0, None, 0,
+                                         None) == 3
+    c = _cache(lib)
+    assert L.decode_step_compact_noalloc(C.byref(c), C.byref(a), q, 3, 0.0, out, 0, None, 0,
+                                         None) == 2          # Hq % Hkv
+    assert L.decode_step_compact_noalloc(C.byref(c), C.byref(a), C.c_void_p(0x100001), 8, 0.0,
+                                         out, 0, None, 0, None) == 1   # misaligned q
+    a.op = lib.CDA_OP_COUNT
+    assert L.decode_step_compact_noalloc(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0,
+                                         None) == 1
