@@ -89,6 +89,21 @@ def rows_before_host(keep_np, T, W, s0):
 
 ROW_BYTES = {"bf16": lambda D: 2 * D, "fp8": lambda D: D, "fp4": lambda D: D // 2}
 ELEM_BYTES = {"bf16": 2.0, "fp8": 1.0, "fp4": 0.5}
+
+
+def compression_ratio(stored_rows, layers, B, Hkv, D, tokens, kv):
+    """The store's bytes (stored rows x K and V rows, plus two f32 scales per
+    head for FP8 / FP4) against dense BF16 and dense same-format pools that
+    keep K and V of every position 0 .. tokens - 1 for every layer, sequence
+    and KV head."""
+    compact = stored_rows * 2 * ROW_BYTES[kv](D) + (0 if kv == "bf16" else 8 * B * Hkv * layers)
+    dense_bf16 = layers * B * Hkv * tokens * 2 * D * 2
+    dense_same = layers * B * Hkv * tokens * 2 * D * ELEM_BYTES[kv]
+    return {"vs_dense_bf16": round(dense_bf16 / compact, 3),
+            "vs_dense_same_dtype": round(dense_same / compact, 3),
+            "compact_kv_bytes": int(compact), "dense_bf16_bytes": int(dense_bf16),
+            "stored_rows_per_head_mean": round(stored_rows / (layers * B * Hkv), 1),
+            "positions_per_head": tokens}
 MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 / f16 MFMA of the MI355X
 
 
@@ -243,6 +258,7 @@ def cpu_baseline(cfg, kv, dev_rows_l0, out_f32_l0, budget_note=""):
            "ms_per_decode_step_all_cores": round(times[0] * 1e3 / ORACLE_STEPS, 1)}
     extra = {"fp8_saturated": int(c.saturated) if od != oracle.BF16 else 0,
              "oracle_compact_kv_bytes_layer0": int(compact),
+             "oracle_dense_bf16_bytes_layer0": int(oracle.dense_kv_bytes(1, B * Hkv, D, T + S, 2)),
              "max_abs_err_f32_layer0": float(err.max()),
              "max_rel_err_f32_layer0": float((err / np.maximum(np.abs(ref), 1e-30)).max())}
     return rec, extra
@@ -520,15 +536,7 @@ def main():
     # (replica 0): stored rows x K and V rows (+ two f32 scales per head for
     # FP8 / FP4), against dense pools of every position 0 .. T + S - 1
     stored = sum(int(dev_rows[0][l].sum()) for l in range(L))
-    compact_bytes = stored * 2 * row_bytes + (0 if kv == "bf16" else 8 * B * Hkv * L)
-    tokens_dense = T + S_r[0]
-    dense_bf16 = L * B * Hkv * tokens_dense * 2 * D * 2
-    dense_same = L * B * Hkv * tokens_dense * 2 * D * ELEM_BYTES[kv]
-    compression = {"vs_dense_bf16": round(dense_bf16 / compact_bytes, 3),
-                   "vs_dense_same_dtype": round(dense_same / compact_bytes, 3),
-                   "compact_kv_bytes": int(compact_bytes), "dense_bf16_bytes": int(dense_bf16),
-                   "stored_rows_per_head_mean": round(stored / (L * B * Hkv), 1),
-                   "positions_per_head": tokens_dense}
+    compression = compression_ratio(stored, L, B, Hkv, D, T + S_r[0], kv)
 
     ceiling = None
     if not args.no_ceiling and not args.paged and args.chunk <= 0:
@@ -549,9 +557,11 @@ def main():
         out32 = caches[0][0].attention(qd[0][S - 1], out_dtype=torch.float32)
         torch.cuda.synchronize()
         cpu, cpu_extra = cpu_baseline(cfg, kv, dev_rows[0][0], out32.cpu().double().numpy())
-        layer0_bytes = int(dev_rows[0][0].sum()) * 2 * row_bytes + (0 if kv == "bf16" else 8 * B * Hkv)
-        if cpu_extra["oracle_compact_kv_bytes_layer0"] != layer0_bytes:
+        layer0 = compression_ratio(int(dev_rows[0][0].sum()), 1, B, Hkv, D, T + S_r[0], kv)
+        if cpu_extra["oracle_compact_kv_bytes_layer0"] != layer0["compact_kv_bytes"]:
             raise AssertionError("compact KV bytes of layer 0 differ from the oracle's accounting")
+        if cpu_extra["oracle_dense_bf16_bytes_layer0"] != layer0["dense_bf16_bytes"]:
+            raise AssertionError("dense BF16 bytes of layer 0 differ from the oracle's accounting")
         log(f"oracle sample done: {cpu['sample']}")
 
     rec = {

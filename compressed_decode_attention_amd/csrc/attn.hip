@@ -36,9 +36,8 @@
 // issued by a running wave, so the wait is short; the number of polls is
 // bounded, CDA_DEVERR_MERGE past it), then writes zeros back.  Nothing
 // depends on which XCD or CU a workgroup runs on.  The merge folds the
-// partials in unit order and the merging unit substitutes its own values
-// from registers at its own position, so the result does not depend on
-// which unit merges.
+// partials in unit order, its own read back as stored like the others, so
+// the result does not depend on which unit merges.
 //
 // Inside a wave, the G query rows of the KV head (G <= 16) are the N = 16
 // columns of two MFMA products per tile:
