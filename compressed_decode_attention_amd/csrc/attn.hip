@@ -95,7 +95,7 @@
 namespace cda {
 namespace {
 
-constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge
+constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge (x2 past 8 units)
 constexpr int kCounterStride = 32;    // ints between counters: one 128-byte line each
 constexpr int kMergePolls = 1 << 20;  // polls of one batch of partials before giving up
 constexpr int kMaxPlanUnits = 512;    // units a host plan carries in the kernel arguments (4 KB)
@@ -961,19 +961,23 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
       // each thread merges 4 consecutive outputs of one query row, folding
       // the units' partials in unit order (this unit's own too, as stored,
       // so that the result does not depend on which unit merges); the loads
-      // of a batch of kMergeBatch units go out together and are repeated
-      // until every word has arrived (the whole wave together, so that no
-      // lane reads a word another lane has already cleared)
+      // of a batch of units go out together and are repeated until every
+      // word has arrived (the whole wave together, so that no lane reads a
+      // word another lane has already cleared)
       bool late = false;
+      // batches of 8 units, or of 16 when the segment has more than 8 (one
+      // round trip instead of two; fewer units do not pay for 16 loads)
+      auto merge = [&](auto mb) __attribute__((always_inline)) {
+      constexpr int MB = decltype(mb)::value;
       for (int e = tid - moff; e >= 0 && e < items; e += NTH) {
         const int gg = e / (D / 4), d4 = e - gg * (D / 4);
         float M = -INFINITY, L = 0.0f;
         f32x4 O = f32x4{0, 0, 0, 0};
-        for (int k0 = 0; k0 < U; k0 += kMergeBatch) {
-          uint64_t ml[kMergeBatch], oa[kMergeBatch], ob[kMergeBatch];
+        for (int k0 = 0; k0 < U; k0 += MB) {
+          uint64_t ml[MB], oa[MB], ob[MB];
           for (int polls = 0;; ++polls) {
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j) {   // unconditional loads, clamped index
+            for (int j = 0; j < MB; ++j) {   // unconditional loads, clamped index
               const int64_t sr = (int64_t)(un.first + min(k0 + j, U - 1)) * G + gg;
               ml[j] = ld_dev64(p.part_ml + 2 * sr);
               oa[j] = ld_dev64(p.part_o + sr * D + 4 * d4);
@@ -981,7 +985,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
             }
             bool ok = true;
 #pragma unroll
-            for (int j = 0; j < kMergeBatch; ++j)
+            for (int j = 0; j < MB; ++j)
               if (k0 + j < U) ok = ok && written2(ml[j]) && written2(oa[j]) && written2(ob[j]);
             if (__all(ok)) break;
             if (polls >= kMergePolls) {
@@ -990,19 +994,19 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
             }
             __builtin_amdgcn_s_sleep(1);
           }
-          float mj[kMergeBatch];
+          float mj[MB];
 #pragma unroll
-          for (int j = 0; j < kMergeBatch; ++j)
+          for (int j = 0; j < MB; ++j)
             mj[j] = k0 + j < U ? dec_word((uint32_t)ml[j]) : -INFINITY;
           float Mb = M;
 #pragma unroll
-          for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, mj[j]);
+          for (int j = 0; j < MB; ++j) Mb = fmaxf(Mb, mj[j]);
           if (Mb == -INFINITY) continue;
           const float a = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mb);
           O *= a;
           L *= a;
 #pragma unroll
-          for (int j = 0; j < kMergeBatch; ++j) {
+          for (int j = 0; j < MB; ++j) {
             const float f = (mj[j] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mj[j] - Mb);
             const f32x4 oj = f32x4{dec_word((uint32_t)oa[j]), dec_word((uint32_t)(oa[j] >> 32)),
                                    dec_word((uint32_t)ob[j]), dec_word((uint32_t)(ob[j] >> 32))};
@@ -1021,6 +1025,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
           if (d4 == 0) st_dev64(p.part_ml + 2 * sr, 0);
         }
       }
+      };
+      if (U <= kMergeBatch) merge(std::integral_constant<int, kMergeBatch>{});
+      else merge(std::integral_constant<int, 2 * kMergeBatch>{});
       if (late) atomicOr(p.err, CDA_DEVERR_MERGE);
     }
   }
