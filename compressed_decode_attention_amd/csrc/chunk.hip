@@ -71,7 +71,7 @@ struct ChunkParams {
   const uint8_t* keep_new;     // [B, M, Hkv]
   uint8_t* chunk_k;            // workspace: [nh] tiles in the K pool format
   uint8_t* chunk_v;            // workspace: [nh] tiles in the V pool format
-  float* part_o;               // workspace: [slots][16][D]
+  void* part_o;                // workspace: [slots][16][D] f32 (BF16 store) or f16 (FP8/FP4)
   float* part_ml;              // workspace: [slots][16][2]
   // slots: [column group][Gw][16 blocks]
   int32_t* plan;               // workspace: [nh][2] first workgroup, splits of each segment
@@ -694,12 +694,29 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   if (busy && mh == 0 && cb < p.NB) {
     const int64_t slot = ((int64_t)cgi * p.Gw + w) * kWideGroup + (cb - cgi * kWideGroup);
     const int64_t row = slot * 16 + (cq & 15);
+    if (Q) {
+      // FP8/FP4: o / l, a weighted mean of codes (|code| <= 448, or 6), in
+      // f16; the merge weights it by l and applies the V scale
+      const float il = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+      _Float16* po = static_cast<_Float16*>(p.part_o) + row * D;
 #pragma unroll
-    for (int dl = 0; dl < ND; ++dl)
+      for (int dl = 0; dl < ND; ++dl)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-        *reinterpret_cast<f32x4*>(p.part_o + row * D + 32 * dl + 8 * a4 + 4 * hi) =
-            f32x4{acc[dl][4 * a4], acc[dl][4 * a4 + 1], acc[dl][4 * a4 + 2], acc[dl][4 * a4 + 3]} * vs;
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const f16x2 y0 = {(_Float16)(acc[dl][4 * a4] * il), (_Float16)(acc[dl][4 * a4 + 1] * il)};
+          const f16x2 y1 = {(_Float16)(acc[dl][4 * a4 + 2] * il), (_Float16)(acc[dl][4 * a4 + 3] * il)};
+          *reinterpret_cast<u32x2*>(po + 32 * dl + 8 * a4 + 4 * hi) =
+              u32x2{__builtin_bit_cast(uint32_t, y0), __builtin_bit_cast(uint32_t, y1)};
+        }
+    } else {
+      float* po = static_cast<float*>(p.part_o) + row * D;
+#pragma unroll
+      for (int dl = 0; dl < ND; ++dl)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+          *reinterpret_cast<f32x4*>(po + 32 * dl + 8 * a4 + 4 * hi) =
+              f32x4{acc[dl][4 * a4], acc[dl][4 * a4 + 1], acc[dl][4 * a4 + 2], acc[dl][4 * a4 + 3]} * vs;
+    }
     if (hi == 0) {
       p.part_ml[row * 2] = m_run;
       p.part_ml[row * 2 + 1] = lsum;
@@ -1020,8 +1037,9 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
 
 // Workgroups 0 .. nh - 1 commit segment blockIdx.x; workgroup nh + (segment
 // i, column block cb) merges the split states of each of that block's 16
-// columns (their o already carries the V scale), normalised, into out and
-// lse.  The commits read and write none of what the merges use, so the two
+// columns, normalised, into out and lse: BF16 store, o carrying the V
+// scale (weight 2^(m - M)); FP8/FP4, o / l in f16 (weight 2^(m - M) l, the
+// V scale applied at the end).  The commits read and write none of what the merges use, so the two
 // run side by side in one launch, the commits dispatched first.  (The
 // workgroups of 4 waves leave about 4 waves per SIMD: the kernel may use
 // the registers of that occupancy to keep every load in flight.)
@@ -1046,6 +1064,7 @@ void chunk_merge_commit_kernel(ChunkParams p, uint8_t* k_pool, uint8_t* v_pool,
   const int nsp = min(max(p.plan[2 * i + 1], 0), p.Gw - first);
   const int64_t slot0 = ((int64_t)(cb / kWideGroup) * p.Gw + first) * kWideGroup + cb % kWideGroup;
   constexpr int64_t sstep = kWideGroup;   // slot stride between splits
+  constexpr bool Q = KV != kKvBF16;
   float Mx[IPT], L[IPT];
   f32x4 O[IPT];
 #pragma unroll
@@ -1064,7 +1083,15 @@ void chunk_merge_commit_kernel(ChunkParams p, uint8_t* k_pool, uint8_t* v_pool,
       for (int j = 0; j < kMB; ++j) {   // unconditional loads, clamped split
         const int64_t sl = (slot0 + min(k0 + j, nsp - 1) * sstep) * 16 + c;
         ml[it][j] = *reinterpret_cast<const float2*>(p.part_ml + sl * 2);
-        ov[it][j] = *reinterpret_cast<const f32x4*>(p.part_o + sl * D + 4 * d4);
+        if (Q) {
+          const u32x2 hv = *reinterpret_cast<const u32x2*>(static_cast<const _Float16*>(p.part_o) + sl * D + 4 * d4);
+          // (the words through scalars: a bit cast of a vector element reads element 0 here)
+          const uint32_t w0 = hv.x, w1 = hv.y;
+          const f16x2 y0 = __builtin_bit_cast(f16x2, w0), y1 = __builtin_bit_cast(f16x2, w1);
+          ov[it][j] = f32x4{(float)y0[0], (float)y0[1], (float)y1[0], (float)y1[1]};
+        } else {
+          ov[it][j] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.part_o) + sl * D + 4 * d4);
+        }
       }
     }
 #pragma unroll
@@ -1084,19 +1111,21 @@ void chunk_merge_commit_kernel(ChunkParams p, uint8_t* k_pool, uint8_t* v_pool,
 #pragma unroll
       for (int j = 0; j < kMB; ++j) {
         const float f = ml[it][j].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[it][j].x - Ms);
-        O[it] += f * ov[it][j];
-        L[it] += f * ml[it][j].y;
+        const float fl = f * ml[it][j].y;
+        O[it] += (Q ? fl : f) * ov[it][j];
+        L[it] += fl;
       }
       Mx[it] = Mb;
     }
   }
+  const float sv = Q ? kv_scale<KV>(p.v_amax[i]) : 1.0f;
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int e = it * kBlock + threadIdx.x, c = e / (D / 4), d4 = e - c * (D / 4);
     const int col = cb * 16 + c, tq = col / p.G, hq = col - tq * p.G;
     if (tq >= p.M) continue;
     const int64_t row = ((int64_t)b * p.M + tq) * p.Hq + h * p.G + hq;
-    const f32x4 v = L[it] > 0.0f ? O[it] * (1.0f / L[it]) : f32x4{0, 0, 0, 0};
+    const f32x4 v = L[it] > 0.0f ? O[it] * (sv / L[it]) : f32x4{0, 0, 0, 0};
     if (p.out_f32) {
       *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row * D + 4 * d4) = v;
     } else {
@@ -1158,8 +1187,9 @@ size_t chunk_workspace_bytes(const cda_kv_cache& c, int G, int M) {
   chunk_shape(nh, G, M, NB, Gw, slots);
   const size_t tile = (size_t)kTile * kv_row_bytes(c.kv_dtype, c.D);
   const size_t cols = (size_t)slots * 16;
+  const size_t ob = c.kv_dtype == kKvBF16 ? 4 : 2;   // partial o: f32, or f16 (FP8/FP4)
   return 2 * align256((size_t)nh * tile) + align256((size_t)c.B * 4) +
-         align256((size_t)nh * 2 * 4) + align256(cols * 2 * 4) + align256(cols * c.D * 4);
+         align256((size_t)nh * 2 * 4) + align256(cols * 2 * 4) + align256(cols * c.D * ob);
 }
 
 hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M, const void* q,
@@ -1216,7 +1246,7 @@ hipError_t launch_chunk(const cda_kv_cache& c, const cda_compact_args& a, int M,
   ws += align256((size_t)nh * 2 * 4);
   p.part_ml = reinterpret_cast<float*>(ws);
   ws += align256(cols * 2 * 4);
-  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_o = ws;
   uint8_t* kp = static_cast<uint8_t*>(c.k_pool);
   uint8_t* vp = static_cast<uint8_t*>(c.v_pool);
   if (c.page_table)
