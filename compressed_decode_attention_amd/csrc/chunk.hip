@@ -763,15 +763,39 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   __shared__ __attribute__((aligned(16))) uint8_t s_mk[kTile * RB];   // moved rows, K
   __shared__ __attribute__((aligned(16))) uint8_t s_mv[D * kTile * E];   // moved rows, V [d][row]
   __shared__ __attribute__((aligned(16))) uint8_t s_ct[2 * kTile * RB];  // the chunk tile, K then V
+  __shared__ uint8_t s_rk[CDA_MAX_CHUNK_WINDOW];   // the ring rows' keep bytes
+  constexpr int RKPT = CDA_MAX_CHUNK_WINDOW / kBlock;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
-  const int P = pos[b];
-  if (P < 0) return;                           // idle (paged store): every segment of b
   const int W = p.W, M = p.M;
-  const int cap = max(p.seg_cap[i], 0);
-  const int cl0 = min(max(comp_len[i], 0), cap);
   const uint8_t* ck = p.chunk_k + (int64_t)i * kTile * RB;   // the chunk's encoded rows
   const uint8_t* cv = p.chunk_v + (int64_t)i * kTile * RB;
+  // Every load that does not depend on the metadata goes out beside it: the
+  // ring's keep bytes (the ranking reads those of rows (P + t) mod W), the
+  // chunk tokens' keep bytes, the chunk's encoded tile.  (Loads are
+  // unconditional, from a valid address, and zeroed after where not wanted:
+  // a load under a branch would be waited for at the join.)
+  const int P = pos[b];
+  const int cap_r = p.seg_cap[i], clr = comp_len[i];
+  const int64_t sbase = PG ? 0 : p.seg_base[i];
+  u32x4 tck[TPT], tcv[TPT], mk[MPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    tck[u] = *reinterpret_cast<const u32x4*>(ck + 16 * (u * kBlock + tid));
+    tcv[u] = *reinterpret_cast<const u32x4*>(cv + 16 * (u * kBlock + tid));
+  }
+  uint32_t rkb[RKPT];
+  const uint8_t* rkrow = ring_keep + (int64_t)i * W;
+#pragma unroll
+  for (int u = 0; u < RKPT; ++u) rkb[u] = W > 0 ? rkrow[min(u * kBlock + tid, max(W, 1) - 1)] : 0u;
+  const int tkn = min(max(tid - W, 0), M - 1);   // chunk token t - W of ranking thread t
+  const uint32_t knb = p.keep_new[((int64_t)b * M + tkn) * p.Hkv + h];
+  if (P < 0) return;                           // idle (paged store): every segment of b
+  const int cap = max(cap_r, 0);
+  const int cl0 = min(max(clr, 0), cap);
+#pragma unroll
+  for (int u = 0; u < RKPT; ++u)
+    if (u * kBlock + tid < W) s_rk[u * kBlock + tid] = (uint8_t)rkb[u];
   const uint8_t* s_ck = s_ct;
   const uint8_t* s_cv = s_ct + kTile * RB;
   // The rows this commit touches lie in the ring tiles [0, nrt) and the two
@@ -780,7 +804,6 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   // seg_base) would be repeated after every byte store, which may alias it.
   const int nrt = (W + kTile - 1) / kTile, dt0 = (W + cl0) / kTile;
   __shared__ int64_t s_tile[kMaxRingTiles + 2];
-  const int64_t sbase = PG ? 0 : p.seg_base[i];
   for (int t = tid; t < nrt + 2; t += kBlock) {
     const int tt = t < nrt ? t : dt0 + (t - nrt);
     int64_t x = sbase + (int64_t)tt * kTile;
@@ -812,6 +835,7 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
     return s_cv[d * kTile + j];
   };
 
+  __syncthreads();   // s_rk
   // 1. the tokens that move, ranked (one wave: M <= 64)
   if (tid < 64) {
     const int t = tid;
@@ -822,10 +846,10 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
       if (lp >= 0) {
         if (lp < P) {   // in the ring before the chunk (so W > t)
           const int r = lp % W;
-          kept = ring_keep[(int64_t)i * W + r] != 0;
+          kept = s_rk[r] != 0;
           src = -1 - r;
-        } else {
-          kept = p.keep_new[((int64_t)b * M + (lp - P)) * p.Hkv + h] != 0;
+        } else {        // chunk token lp - P = t - W
+          kept = knb != 0;
           src = lp - P;
         }
       }
@@ -847,7 +871,6 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
 
   // 2. every source into registers, then LDS.  Lane `lane` of each wave owns
   // moved row k = lane for V, over the wave's DPW columns.
-  u32x4 tck[TPT], tcv[TPT], mk[MPT];
   uint32_t mv[DPW];
   const bool vrow = lane < nmove;
   int64_t vfrom = -1;
@@ -857,15 +880,6 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
     if (vsrc < 0) {
       vfrom = prow(-1 - vsrc);
       if (vfrom < 0) bad = 1;
-    }
-  }
-  // (loads are unconditional, from a valid address, and zeroed after where
-  // not wanted: a load under a branch would be waited for at the join)
-  if (nr > 0) {
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      tck[u] = *reinterpret_cast<const u32x4*>(ck + 16 * (u * kBlock + tid));
-      tcv[u] = *reinterpret_cast<const u32x4*>(cv + 16 * (u * kBlock + tid));
     }
   }
 #pragma unroll
