@@ -47,6 +47,11 @@ namespace cda {
 namespace {
 
 constexpr int kWideTarget = 256;     // attention workgroups in all: one per CU
+// The chunk tile counts as 1 + kChunkExtra tiles in the plan: the workgroup
+// that holds it encodes the chunk's rows first (their loads and
+// conversions).  (Extras of 1, 2, 3, 4: 40.5, 40.8-41.1, 41.7, 42.0 us per
+// call at M = 64 on the Qwen c = 8 layer; 1 is also the best at M = 16.)
+constexpr int kChunkExtra = 1;
 constexpr int kMaxRingTiles = CDA_MAX_CHUNK_WINDOW / kTile;   // chunk commit: ring tiles
 
 struct ChunkParams {
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   const int W = p.W, G = p.G, M = p.M;
 
   // ---- the plan.  Segment j has nt_j tiles to attend (its stored tiles and
-  // the chunk tile; none when idle) and gets SP_j = ceil(nt_j / t) of the Gw
+  // the chunk tile, which counts 1 + kChunkExtra; none when idle) and gets SP_j = ceil(nt_j / t) of the Gw
   // workgroups of each column group, t the least tile count per workgroup
   // for which they fit (ceil(total / (Gw - nh)) always does; the 8 counts
   // from ceil(total / Gw) up, below which none can, are tried together);
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     P_ = p.pos[j / p.Hkv];
     const int cap_ = max(p.seg_cap[j], 0);
     cl_ = min(max(p.comp_len[j], 0), cap_);
-    nt_ = P_ < 0 ? 0 : (min(W, P_) + cl_ + kTile - 1) / kTile + 1;
+    nt_ = P_ < 0 ? 0 : (min(W, P_) + cl_ + kTile - 1) / kTile + 1 + kChunkExtra;
   };
   const int j0 = min(lane, p.nh - 1);   // segment `lane` (of the first 64): its six
   const int P0 = p.pos[j0 / p.Hkv];      // loads in one round trip
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   const float ka0 = Q ? p.k_amax[j0] : 1.0f;
   const float va0 = Q ? p.v_amax[j0] : 1.0f;
   const int cl0 = min(max(clr0, 0), max(cap0, 0));
-  const int nt0 = (lane >= p.nh || P0 < 0) ? 0 : (min(W, P0) + cl0 + kTile - 1) / kTile + 1;
+  const int nt0 = (lane >= p.nh || P0 < 0) ? 0 : (min(W, P0) + cl0 + kTile - 1) / kTile + 1 + kChunkExtra;
   auto tiles_of = [&](int j) {
     if (j < 64) return nt0;
     int a, c, e;
@@ -267,7 +272,25 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   const int P = max(Praw, 0);
   const int n = idle ? 0 : min(W, P) + cl;
   const int ntiles = (n + kTile - 1) / kTile;
-  const int last = idle ? ntiles - 1 : ntiles;   // the chunk tile is tile ntiles
+  // this split's tiles: a contiguous range [rlo, rhi) of the segment's tiles,
+  // the splits' shares of the plan's nt tiles taken from the top down; the
+  // top split holds the chunk tile (tile ntiles, worth 1 + kChunkExtra) and
+  // the stored tiles just below it, split 0 the lowest (the ring's)
+  int rlo = 0, rhi = 0;
+  {
+    const int nq = ntiles + 1 + kChunkExtra, qb = nq / SPi, qr = nq - qb * SPi;
+    const int ctop = max(qb + (SPi - 1 < qr ? 1 : 0) - 1 - kChunkExtra, 0);
+    if (s == SPi - 1) {
+      rlo = ntiles - ctop;
+      rhi = ntiles;
+    } else {   // below the top split and the splits s + 1 .. SPi - 2
+      const int above = (SPi - 2 - s) * qb + max(0, min(qr, SPi - 1) - (s + 1));
+      rhi = ntiles - ctop - above;
+      rlo = s == 0 ? 0 : rhi - (qb + (s < qr ? 1 : 0));
+    }
+    rlo = max(rlo, 0);
+    rhi = max(rhi, rlo);
+  }
   const float ks = Q ? kv_scale<KV>(ka) : 1.0f;
   const float vs = Q ? kv_scale<KV>(va) : 1.0f;
   const float c1 = p.sm_scale * kLog2e * ks;
@@ -498,9 +521,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   // Each tile fetched two tiles ahead into registers and staged one tile
   // ahead into the other buffer, so each tile costs one barrier and its
   // staging overlaps the other waves' products.
-  // This split's tiles from the highest down: the workgroup holding the chunk
-  // tile (always the highest) encodes it first, its loads beside the q loads.
-  const int t0 = s <= last ? s + SPi * ((last - s) / SPi) : -1;
+  // This split's tiles from the highest down: the top split encodes the
+  // chunk tile first, its loads beside the q loads.
+  const int t0 = (s == SPi - 1 && !idle) ? ntiles : rhi - 1 >= rlo ? rhi - 1 : -1;
+  auto next_t = [&](int tt) {
+    const int tn_ = tt == ntiles ? rhi - 1 : tt - 1;
+    return tn_ >= rlo ? tn_ : -1;
+  };
   int cur = 0;
   if (t0 >= 0) {
     if (t0 == ntiles) encode_chunk(rg, kbyte);
@@ -521,15 +548,17 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   if (t0 >= 0) {
     stage(t0, 0);
     ok_cur = ok;
-    if (t0 - SPi >= s) fetch(t0 - SPi, rg, kbyte, ok);
+    const int t1 = next_t(t0);
+    if (t1 >= 0) fetch(t1, rg, kbyte, ok);
   }
   __syncthreads();
-  for (int tt = t0; tt >= s; tt -= SPi) {
-    const int tn = tt - SPi;
+  for (int tt = t0; tt >= 0;) {
+    const int tn = next_t(tt);
     const bool ok_next = ok;
-    if (tn >= s) {
+    if (tn >= 0) {
       stage(tn, cur ^ 1);
-      if (tn - SPi >= s) fetch(tn - SPi, rg, kbyte, ok);
+      const int tnn = next_t(tn);
+      if (tnn >= 0) fetch(tnn, rg, kbyte, ok);
     }
     if (busy && ok_cur) {
       const bool ctile = tt == ntiles;
@@ -655,6 +684,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
     __syncthreads();   // buffer cur is read by every wave before it is staged again
     ok_cur = ok_next;
     cur ^= 1;
+    tt = tn;
   }
 
   // ---- this lane's partial state (column cq: block cb0 + cq / 16)
