@@ -94,9 +94,10 @@ struct ChunkParams {
 // given out in proportion to the segments' tile counts (segment lengths
 // differ with their keep rates: equal splits per segment left workgroups
 // between 2 and 10 tiles on the Qwen c = 8 layer, and the longest set the
-// kernel's time).  The workgroup walks the tiles s, s + SP_i, ... of its
-// segment from the highest down, the chunk tile first where it is among
-// them (encoded here from the new rows, as an APPEND would encode them).  The waves stage each tile in one
+// kernel's time).  The workgroup walks a contiguous range of its segment's
+// tiles from the highest down; the top split takes the chunk tile first
+// (encoded here from the new rows, as an APPEND would encode them) and
+// fewer stored tiles.  The waves stage each tile in one
 // of two LDS buffers while computing on the other -- the tile after it
 // already in flight in registers -- converting FP8/FP4 codes once, exactly,
 // to the MFMA operand types (K to bf16 operands
