@@ -124,6 +124,19 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
+def chunk_traffic_from_profile():
+    """HBM bytes per chunk call (M = 64, its two launches) from the committed
+    counter summary, if it was taken on the current chunk kernel source."""
+    path = os.path.join(ROOT, "profiles", "chunk_qwen_c8_chunk64_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "chunk.hip")
+    if rec.get("chunk_src_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
 def stream_lib():
     if not os.path.exists(STREAM_LIB):
         raise RuntimeError(f"{STREAM_LIB} is missing: build it with `python -c 'import "
@@ -522,9 +535,12 @@ def main():
     achieved = bytes_per_launch / (kernel_us * 1e-6) / 1e9
     if flops_per_call is not None:
         tflops = flops_per_call / (kernel_us * 1e-6) / 1e12
+        # the committed counters are those of one M = 64 call of this config (FP8)
+        traffic = (chunk_traffic_from_profile() if (args.config, kv, R, args.chunk) ==
+                   ("qwen_c8", "fp8", 1, 64) and not args.paged else None)
         roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                    "traffic": None}
+                    "traffic": traffic}
     else:
         # the committed counters are those of the default run (this config, FP8)
         traffic = (traffic_from_profile() if (args.config, kv, R) == ("qwen_c8", "fp8", 1) and

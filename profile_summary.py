@@ -4,6 +4,7 @@ under profiles/.
   python profile_summary.py trace <kernel_stats.csv> <command> [note] > profiles/X.md
   python profile_summary.py traffic <stream FETCH csv> <copy WRITE csv>
          <bench FETCH csv> <bench WRITE csv> <json path or -> <commands...>
+  python profile_summary.py traffic-chunk <the same arguments>
 
 The traffic mode scales each kernel's FETCH_SIZE by what that counter reads
 for the 2 GiB tile-streaming read of `bench.py --stream-calibration` (the
@@ -12,7 +13,10 @@ WRITE_SIZE by what it reads for the plain 64 MiB copy of
 `bench.py --copy-calibration`, prints a markdown table, and writes the
 attention kernel's bytes per launch to the JSON path (bench.py reads
 profiles/attn_qwen_c8_traffic.json while it matches the attention kernel
-source); "-" writes no JSON.
+source); "-" writes no JSON.  The traffic-chunk mode writes instead the
+bytes of one chunk_attn_compact call (its attention and merge-and-commit
+launches), which bench.py --chunk 64 reads from
+profiles/chunk_qwen_c8_chunk64_traffic.json while it matches chunk.hip.
 """
 from __future__ import annotations
 
@@ -25,6 +29,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "attn.hip")
+CHUNK_SRC = os.path.join(ROOT, "compressed_decode_attention_amd", "csrc", "chunk.hip")
 COPY_KIB = 64 * 1024
 STREAM_KIB = 2 * 1024 * 1024
 
@@ -63,7 +68,8 @@ COPY_KERNELS = ("copyBuffer", "direct_copy")
 STREAM_KERNELS = ("stream_tiles_kernel",)
 
 
-def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[str]) -> None:
+def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[str],
+            chunk: bool = False) -> None:
     fcal = STREAM_KIB / list(_mean(cf, STREAM_KERNELS).values())[0]
     wcal = COPY_KIB / list(_mean(cw, COPY_KERNELS).values())[0]
     fetch, write = _mean(bf, ("cda::",)), _mean(bw, ("cda::",))
@@ -81,6 +87,17 @@ def traffic(cf: str, cw: str, bf: str, bw: str, json_path: str, commands: list[s
         print(f"| `{k}` | {fetch[k] * fcal * 1024 / 1e6:.3f} | {write.get(k, 0) * wcal * 1024 / 1e6:.3f} |")
     if json_path == "-":
         return
+    if chunk:   # one chunk call: its attention launch and its merge-and-commit launch
+        ks = [k for k in fetch if k.startswith("chunk_")]
+        rec = {"chunk_src_sha256": hashlib.sha256(open(CHUNK_SRC, "rb").read()).hexdigest(),
+               "kernels": ks,
+               "fetch_bytes_per_call": sum(fetch[k] for k in ks) * fcal * 1024,
+               "write_bytes_per_call": sum(write.get(k, 0) for k in ks) * wcal * 1024,
+               "hbm_bytes_per_call": sum(fetch[k] * fcal + write.get(k, 0) * wcal for k in ks) * 1024,
+               "fetch_scale": fcal, "write_scale": wcal}
+        with open(json_path, "w") as f:
+            json.dump(rec, f, indent=1)
+        return
     # the decode attention kernel's bytes per launch, for bench.py
     attn = [k for k in fetch if k.startswith("attn_kernel")][0]
     rec = {"attn_src_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
@@ -97,4 +114,4 @@ if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(*sys.argv[2:5])
     else:
-        traffic(*sys.argv[2:7], sys.argv[7:])
+        traffic(*sys.argv[2:7], sys.argv[7:], chunk=sys.argv[1] == "traffic-chunk")
