@@ -16,7 +16,10 @@
 //     with its other arguments and issues the loads of its first tiles
 //     before it has read any of the segment's metadata; tiles past the rows
 //     holding data are read too and masked out (they lie inside the
-//     segment's span, hence inside the pool).
+//     segment's span, hence inside the pool) -- except the last tile of the
+//     span, which the wave reads only once the metadata shows it holds data
+//     (in a decode step it is the end of the reserve, empty until the
+//     segment has nearly filled its capacity).
 //   - device plan: every wave derives the unit -> (segment, tiles) map from
 //     pos / comp_len / seg_cap (lane l looks at one segment, a wave-wide scan
 //     of unit counts finds the segment holding unit w), one round trip of
@@ -95,7 +98,8 @@
 namespace cda {
 namespace {
 
-constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge (x2 past 8 units)
+constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge (4 for up
+                                      // to 4 units, x2 past 8)
 constexpr int kCounterStride = 32;    // ints between counters: one 128-byte line each
 constexpr int kMergePolls = 1 << 20;  // polls of one batch of partials before giving up
 constexpr int kMaxPlanUnits = 512;    // units a host plan carries in the kernel arguments (4 KB)
@@ -133,7 +137,9 @@ struct AttnParams {
 };
 
 // Host plan: unit w of the launch is the unit of workgroup w.
-//   u[2w]      pool tile of the unit's first tile (0 for a unit without tiles)
+//   u[2w]      pool tile of the unit's first tile (0 for a unit without tiles;
+//              bits 0-25) | tiles of the segment's span from that tile on,
+//              at most 63 (26-31)
 //   u[2w + 1]  segment (bits 0-15) | index of the unit in its segment (16-20)
 //              | units of the segment - 1 (21-25) | tiles of the unit (26-31)
 struct HostPlan {
@@ -179,9 +185,13 @@ __device__ __forceinline__ uint64_t enc2(float x, float y) {
 __device__ __forceinline__ bool written2(uint64_t w) {
   return (uint32_t)w != 0u && (uint32_t)(w >> 32) != 0u;
 }
-// Device-coherent 8-byte store and load (relaxed, agent scope).
+// Device-coherent 8-byte (and 1-byte) store and 8-byte load (relaxed, agent
+// scope).
 __device__ __forceinline__ void st_dev64(uint32_t* a, uint64_t v) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(a), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev8(uint8_t* a, uint8_t v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_dev64(uint32_t* a) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -368,8 +378,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   int64_t pre_row = 0;   // host plan: pool row of this wave's first tile
   int64_t sb_dev = 0;    // host plan: seg_base[i] as the device holds it
   int raw_pos = 0, raw_cl = 0, raw_cap = 0, raw_kn = 0;
+  bool deferred = false;  // host plan: this wave's first tile is read after the metadata
   if constexpr (HP) {
-    const uint32_t tile0 = plan.u[2 * w], inf = plan.u[2 * w + 1];
+    const uint32_t tile0 = plan.u[2 * w] & 0x3FFFFFFu, inf = plan.u[2 * w + 1];
+    const int rem = (int)(plan.u[2 * w] >> 26);
     const int ui = (int)((inf >> 16) & 31u), nt = (int)(inf >> 26);
     un.i = (int)(inf & 0xFFFFu);
     un.U = (int)((inf >> 21) & 31u) + 1;
@@ -379,7 +391,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     un.sb = ((int64_t)tile0 - t_begin) * kTile;
     // a wave with no tile of its own reads the unit's first again (unused);
     // a unit without tiles reads pool tile 0 (unused)
-    pre_row = nt > 0 ? ((int64_t)tile0 + min(wave, nt - 1)) * kTile : 0;
+    // the last tile of the segment's span waits for the metadata: its wave
+    // reads the unit's first tile now instead (unused)
+    deferred = wave >= rem - 1;
+    pre_row = nt > 0 ? ((int64_t)tile0 + (deferred ? 0 : min(wave, nt - 1))) * kTile : 0;
     // the segment's metadata: loaded now, consumed after the first tile's
     // loads have gone out
     const int bb = un.i / p.Hkv;
@@ -623,6 +638,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   // (wants_move: it is kept and the compact region has room) and writes the
   // new row over its ring row.  No other workgroup reads the new token's
   // tile, and the compact tail lies past the rows attended in this launch.
+  // FP8 rows go out through agent-scope stores, which write through the L2:
+  // the end of the launch then has none of their lines left to write back.
   auto write_rows = [&](bool wants_move) {
     const int d0n = EPL * lane;
     // the leaving token's row (ring row P mod W) moves to compact row
@@ -644,13 +661,17 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
       uint8_t* kd = p.k_pool + drow * (int64_t)RB;
       uint8_t* vd = p.v_pool + drow * (int64_t)RB;
       constexpr int KC = RB / 16;   // 16-byte chunks per K row
-      if (lane < KC) *reinterpret_cast<u32x4*>(kd + k_chunk_offset(rt, lane, RB)) = okx;
+      if (lane < KC) {
+        uint32_t* kq = reinterpret_cast<uint32_t*>(kd + k_chunk_offset(rt, lane, RB));
+        st_dev64(kq, (uint64_t)okx[0] | ((uint64_t)okx[1] << 32));
+        st_dev64(kq + 2, (uint64_t)okx[2] | ((uint64_t)okx[3] << 32));
+      }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         if (FP4)
           nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
         else if (FP8)
-          vd[(d0n + e) * kTile + rt] = (uint8_t)ox[e];
+          st_dev8(vd + (d0n + e) * kTile + rt, (uint8_t)ox[e]);
         else
           reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
       }
@@ -664,7 +685,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     if (own_ok) {
       uint8_t* kdst = kt + k_chunk_offset(rs, kb0 >> 4, RB) + (kb0 & 15);
       if (LB == 4)
-        *reinterpret_cast<uint32_t*>(kdst) = kc;
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(kdst), kc, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       else if (LB == 2)
         *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)kc;
       else
@@ -674,7 +696,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
         if (FP4)   // after the moved row's write, which may share the byte
           nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
         else if (FP8)
-          vt[(d0n + e) * kTile + rs] = (uint8_t)(vc >> (8 * e));
+          st_dev8(vt + (d0n + e) * kTile + rs, (uint8_t)(vc >> (8 * e)));
         else
           reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
       }
@@ -817,7 +839,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   };
 
   int t = t_begin + wave;
-  if (HP) {
+  if (HP && !deferred) {
     // the tile whose loads went out first
     int rko = 0;
     if (APP) rko = *rkp;   // issued after that tile's loads
@@ -965,8 +987,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
       // word has arrived (the whole wave together, so that no lane reads a
       // word another lane has already cleared)
       bool late = false;
-      // batches of 8 units, or of 16 when the segment has more than 8 (one
-      // round trip instead of two; fewer units do not pay for 16 loads)
+      // batches of 4 units when the segment has at most 4, of 8 up to 8,
+      // else of 16 (one round trip instead of two; fewer units do not pay
+      // for the loads and the folds of a larger batch)
       auto merge = [&](auto mb) __attribute__((always_inline)) {
       constexpr int MB = decltype(mb)::value;
       for (int e = tid - moff; e >= 0 && e < items; e += NTH) {
@@ -1026,7 +1049,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
         }
       }
       };
-      if (U <= kMergeBatch) merge(std::integral_constant<int, kMergeBatch>{});
+      if (U <= 4) merge(std::integral_constant<int, 4>{});
+      else if (U <= kMergeBatch) merge(std::integral_constant<int, kMergeBatch>{});
       else merge(std::integral_constant<int, 2 * kMergeBatch>{});
       if (late) atomicOr(p.err, CDA_DEVERR_MERGE);
     }
@@ -1064,7 +1088,7 @@ void launch_variant(int kv, int D, int nw, dim3 grid, hipStream_t s, const AttnP
 // arguments; the device plan is used then.
 bool host_plan(const cda_kv_cache& c, int tpu, HostPlan& plan, int& n) {
   const int64_t nh = (int64_t)c.B * c.Hkv;
-  if (nh > 65536 || tpu > 63 || c.pool_rows < kTile || c.pool_rows / kTile > 0xFFFFFFFFll)
+  if (nh > 65536 || tpu > 63 || c.pool_rows < kTile || c.pool_rows / kTile > 0x3FFFFFFll)
     return false;
   const int64_t* sbh = c.seg_base_host;
   n = 0;
@@ -1074,7 +1098,8 @@ bool host_plan(const cda_kv_cache& c, int tpu, HostPlan& plan, int& n) {
     if (U > 32 || n + U > kMaxPlanUnits) return false;
     for (int64_t u = 0; u < U; ++u) {
       const int64_t nt = std::min<int64_t>(tpu, tiles - u * tpu);
-      plan.u[2 * n] = (uint32_t)(sbh[i] / kTile + u * tpu);
+      plan.u[2 * n] = (uint32_t)(sbh[i] / kTile + u * tpu) |
+                      ((uint32_t)std::min<int64_t>(63, tiles - u * tpu) << 26);
       plan.u[2 * n + 1] = (uint32_t)i | (uint32_t)(u << 16) | (uint32_t)((U - 1) << 21) |
                           (uint32_t)(nt << 26);
       ++n;
