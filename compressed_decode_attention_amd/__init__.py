@@ -240,6 +240,8 @@ class CompactKVCache:
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         # host copy of seg_base for the host-side work plan (set by allocate)
         self.seg_base_host = None
+        # rows at each segment's end expected empty (the COUNT reserve): a read hint
+        self.spare_rows = 0
         self.k_pool = None
         self.v_pool = None
         self.pool_rows = 0
@@ -253,7 +255,7 @@ class CompactKVCache:
         s = self.struct
         s.B, s.Hkv, s.D, s.W = self.B, self.Hkv, self.D, self.W
         s.kv_dtype = _DTYPES[self.kv_dtype]
-        s.reserved0 = 0
+        s.spare_rows = self.spare_rows
         s.pool_rows = self.pool_rows
         s.k_pool, s.v_pool = _ptr(self.k_pool), _ptr(self.v_pool)
         s.seg_base, s.seg_cap = _ptr(self.seg_base), _ptr(self.seg_cap)
@@ -266,6 +268,8 @@ class CompactKVCache:
     # ---- prefill
     def count(self, keep, T: int, reserve: int, dst_out=None) -> None:
         kv_compact(self, CDA_OP_COUNT, T=T, reserve=reserve, keep=keep, dst_out=dst_out)
+        self.spare_rows = int(reserve)
+        self.struct.spare_rows = self.spare_rows
 
     def rows_needed(self) -> int:
         """Pool rows the layout needs (reads seg_base[B*Hkv]: synchronises)."""

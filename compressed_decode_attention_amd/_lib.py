@@ -19,7 +19,7 @@ CDA_KV_BF16, CDA_KV_FP8_E4M3, CDA_KV_FP4_E2M1 = 0, 1, 2
 CDA_OUT_BF16, CDA_OUT_F32 = 0, 1
 CDA_OP_COUNT, CDA_OP_PACK, CDA_OP_APPEND = 0, 1, 2
 CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE = 3, 4, 5
-CDA_VERSION = 4       # the struct layouts below are those of this version
+CDA_VERSION = 5       # the struct layouts below are those of this version
 CDA_SCRATCH_BYTES = 4 << 20   # device scratch of decode_step_compact_noalloc, per GPU
 CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16
@@ -36,7 +36,7 @@ EXPORTS = ("kv_compact", "decode_attn_compact", "decode_step_compact",
 class CdaKvCache(C.Structure):
     _fields_ = [
         ("B", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32), ("W", C.c_int32),
-        ("kv_dtype", C.c_int32), ("reserved0", C.c_int32),
+        ("kv_dtype", C.c_int32), ("spare_rows", C.c_int32),
         ("pool_rows", C.c_int64),
         ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
         ("seg_base", C.c_void_p), ("seg_cap", C.c_void_p), ("comp_len", C.c_void_p),

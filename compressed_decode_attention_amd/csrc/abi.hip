@@ -24,7 +24,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int32_t check_cache(const cda_kv_cache* c) {
   if (!c) return CDA_ERR_INVALID_ARG;
-  if (c->B < 0 || c->Hkv < 1 || c->W < 0 || c->reserved0 != 0) return CDA_ERR_INVALID_ARG;
+  if (c->B < 0 || c->Hkv < 1 || c->W < 0 || c->spare_rows < 0) return CDA_ERR_INVALID_ARG;
   if (c->W > (1 << 28)) return CDA_ERR_INVALID_ARG;
   if (c->D != 64 && c->D != 128) return CDA_ERR_UNSUPPORTED;
   if (c->kv_dtype != CDA_KV_BF16 && c->kv_dtype != CDA_KV_FP8_E4M3 &&

@@ -16,10 +16,11 @@
 //     with its other arguments and issues the loads of its first tiles
 //     before it has read any of the segment's metadata; tiles past the rows
 //     holding data are read too and masked out (they lie inside the
-//     segment's span, hence inside the pool) -- except the last tile of the
-//     span, which the wave reads only once the metadata shows it holds data
-//     (in a decode step it is the end of the reserve, empty until the
-//     segment has nearly filled its capacity).
+//     segment's span, hence inside the pool) -- except the tiles the
+//     caller's spare_rows hint puts wholly in the end of the span that is
+//     expected empty (the unfilled decode reserve, less one tile of margin
+//     for its growth): their waves read them only once the metadata shows
+//     data in them.
 //   - device plan: every wave derives the unit -> (segment, tiles) map from
 //     pos / comp_len / seg_cap (lane l looks at one segment, a wave-wide scan
 //     of unit counts finds the segment holding unit w), one round trip of
@@ -138,8 +139,8 @@ struct AttnParams {
 
 // Host plan: unit w of the launch is the unit of workgroup w.
 //   u[2w]      pool tile of the unit's first tile (0 for a unit without tiles;
-//              bits 0-25) | tiles of the segment's span from that tile on,
-//              at most 63 (26-31)
+//              bits 0-25) | the first wave of the unit whose tile is read
+//              only after the metadata, at most 63 (26-31)
 //   u[2w + 1]  segment (bits 0-15) | index of the unit in its segment (16-20)
 //              | units of the segment - 1 (21-25) | tiles of the unit (26-31)
 struct HostPlan {
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   bool deferred = false;  // host plan: this wave's first tile is read after the metadata
   if constexpr (HP) {
     const uint32_t tile0 = plan.u[2 * w] & 0x3FFFFFFu, inf = plan.u[2 * w + 1];
-    const int rem = (int)(plan.u[2 * w] >> 26);
+    const int wdef = (int)(plan.u[2 * w] >> 26);
     const int ui = (int)((inf >> 16) & 31u), nt = (int)(inf >> 26);
     un.i = (int)(inf & 0xFFFFu);
     un.U = (int)((inf >> 21) & 31u) + 1;
@@ -391,9 +392,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     un.sb = ((int64_t)tile0 - t_begin) * kTile;
     // a wave with no tile of its own reads the unit's first again (unused);
     // a unit without tiles reads pool tile 0 (unused)
-    // the last tile of the segment's span waits for the metadata: its wave
-    // reads the unit's first tile now instead (unused)
-    deferred = wave >= rem - 1;
+    // a tile expected empty waits for the metadata: its wave reads the
+    // unit's first tile now instead (unused)
+    deferred = wave >= wdef;
     pre_row = nt > 0 ? ((int64_t)tile0 + (deferred ? 0 : min(wave, nt - 1))) * kTile : 0;
     // the segment's metadata: loaded now, consumed after the first tile's
     // loads have gone out
@@ -1087,6 +1088,9 @@ void launch_variant(int kv, int D, int nw, dim3 grid, hipStream_t s, const AttnP
 // unit per segment).  False when it does not fit the encoding or the kernel
 // arguments; the device plan is used then.
 bool host_plan(const cda_kv_cache& c, int tpu, HostPlan& plan, int& n) {
+  // tiles wholly past span - spare_rows + 64 rows of a segment are expected
+  // empty and read after the metadata (none without the hint)
+  const int64_t spare = c.spare_rows;
   const int64_t nh = (int64_t)c.B * c.Hkv;
   if (nh > 65536 || tpu > 63 || c.pool_rows < kTile || c.pool_rows / kTile > 0x3FFFFFFll)
     return false;
@@ -1098,8 +1102,10 @@ bool host_plan(const cda_kv_cache& c, int tpu, HostPlan& plan, int& n) {
     if (U > 32 || n + U > kMaxPlanUnits) return false;
     for (int64_t u = 0; u < U; ++u) {
       const int64_t nt = std::min<int64_t>(tpu, tiles - u * tpu);
-      plan.u[2 * n] = (uint32_t)(sbh[i] / kTile + u * tpu) |
-                      ((uint32_t)std::min<int64_t>(63, tiles - u * tpu) << 26);
+      const int64_t span = sbh[i + 1] - sbh[i];
+      const int64_t t_def = spare > kTile ? (span - spare + 2 * kTile - 1) / kTile : tiles;
+      const int64_t wdef = std::min<int64_t>(63, std::max<int64_t>(0, t_def - u * tpu));
+      plan.u[2 * n] = (uint32_t)(sbh[i] / kTile + u * tpu) | ((uint32_t)wdef << 26);
       plan.u[2 * n + 1] = (uint32_t)i | (uint32_t)(u << 16) | (uint32_t)((U - 1) << 21) |
                           (uint32_t)(nt << 26);
       ++n;

@@ -110,7 +110,7 @@
 extern "C" {
 #endif
 
-#define CDA_VERSION 4
+#define CDA_VERSION 5
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
 #define CDA_SCRATCH_BYTES (4u << 20) /* device scratch of decode_step_compact_noalloc, per GPU */
@@ -159,7 +159,13 @@ typedef struct cda_kv_cache {
     int32_t D;          /* head_dim: 64 or 128 */
     int32_t W;          /* always-kept recent window (ring rows), >= 0 */
     int32_t kv_dtype;   /* enum cda_kv_dtype */
-    int32_t reserved0;  /* must be 0 */
+    int32_t spare_rows; /* hint, >= 0 (0 = none): rows at the end of every segment's capacity
+                           the caller expects to hold no data in this call, typically the
+                           COUNT reserve not yet filled.  With seg_base_host, the tiles of a
+                           segment's span lying wholly past (span - spare_rows + 64) rows are
+                           read only once the segment's metadata shows data in them, instead
+                           of ahead of it.  Changes no result, only which reads go out early
+                           (a wrong hint costs time, never correctness) */
     int64_t pool_rows;  /* rows allocated in k_pool and v_pool (multiple of 64) */
     void *k_pool;       /* [pool_rows / 64] tiles of 64 x D, chunk-permuted (see above) */
     void *v_pool;       /* [pool_rows / 64][D][64] */

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.version() == lib.CDA_VERSION == 4
+    assert lib.version() == lib.CDA_VERSION == 5
     assert lib.status_string(0) == "ok"
     assert lib.status_string(3) == "workspace too small"
     assert lib.status_string(99) == "unknown status"
@@ -55,7 +55,7 @@ def _cache(lib, **kw):
 
 @pytest.mark.parametrize("field,value,status", [
     ("D", 96, 2), ("D", 256, 2), ("kv_dtype", 7, 2), ("Hkv", 0, 1), ("W", -1, 1),
-    ("B", -1, 1), ("reserved0", 3, 1), ("seg_base", 0, 1), ("err", 0, 1),
+    ("B", -1, 1), ("spare_rows", -1, 1), ("seg_base", 0, 1), ("err", 0, 1),
 ])
 def test_cache_validation(lib, field, value, status):
     L = lib.load()

@@ -225,3 +225,47 @@ def test_stale_host_plan_is_flagged():
     torch.cuda.synchronize()
     assert c.error_word() & CDA_DEVERR_PLAN
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp8", "bf16"])
+def test_spare_rows_hint_changes_no_bit(kv_dtype):
+    # the spare_rows hint (count sets it to the COUNT reserve) makes the host
+    # plan read the tiles it puts wholly in the empty end of a span only once
+    # the metadata has arrived.  The right hint (a reserve of 300 rows:
+    # several empty tiles per span), no hint, a partly wrong hint (tiles
+    # holding data deferred) and one that defers every tile give the same
+    # bits, in attention and in decode steps, and the oracle's result
+    B, Hq, Hkv, D, T, W, S, reserve = 4, 16, 4, 128, 3000, 128, 6, 300
+    rates = torch.rand((B, Hkv, 1), generator=torch.Generator().manual_seed(121)) * 0.4
+    keep = (torch.rand((B, Hkv, T + S), generator=torch.Generator().manual_seed(122)) < rates)
+    keep = keep.to(torch.uint8)
+    k = workload.random_bf16((B, T + S, Hkv, D), seed=123)
+    v = workload.random_bf16((B, T + S, Hkv, D), seed=124)
+    q = workload.random_bf16((S, B, Hq, D), seed=125)
+    caches = [gpu_prefill(k, v, keep, T, W, reserve, kv_dtype, with_dst=False)[0]
+              for _ in range(4)]
+    assert caches[0].spare_rows == reserve and caches[0].seg_base_host is not None
+    for c, hint in zip(caches[1:], (0, 500, 100000)):
+        c.spare_rows = hint
+        c._refresh()
+    kd, vd, qd = k.to(dev()), v.to(dev()), q.to(dev())
+    kn = keep[:, :, T:].permute(2, 0, 1).contiguous().to(dev())
+    quant = kv_dtype != "bf16"
+    ka = caches[0].k_amax.cpu().numpy() if quant else None
+    va = caches[0].v_amax.cpu().numpy() if quant else None
+    o = [c.attention(qd[0], out_dtype=torch.float32) for c in caches]
+    torch.cuda.synchronize()
+    assert all(torch.equal(o[0], x) for x in o[1:]), "attention"
+    ref, _ = oracle.attention(q[0], k, v, keep, T - 1, W, odt(kv_dtype), ka, va)
+    check_close(o[0].cpu().numpy(), ref, "attention, hint = reserve")
+    for s in range(S):
+        o = [c.decode_step(kd[:, T + s], vd[:, T + s], kn[s], qd[s], out_dtype=torch.float32)
+             for c in caches]
+        torch.cuda.synchronize()
+        assert all(torch.equal(o[0], x) for x in o[1:]), f"decode step {s}"
+        ref, _ = oracle.attention(q[s], k, v, keep, T + s, W, odt(kv_dtype), ka, va)
+        check_close(o[0].cpu().numpy(), ref, f"decode step {s}, hint = reserve")
+    for c in caches[1:]:
+        assert torch.equal(c.comp_len, caches[0].comp_len) and torch.equal(c.pos, caches[0].pos)
+        assert torch.equal(c.k_pool, caches[0].k_pool) and torch.equal(c.v_pool, caches[0].v_pool)
+    assert all(c.error_word() == 0 for c in caches)
