@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
 #pragma unroll
         for (int j = 0; j < VL; ++j)
           vr[nt][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-              vtile + ((16 * nt + g) * kTile + 16 * kg + 8 * j) * E));
+              vtile + v_tile_off(16 * kg + 8 * j, 16 * nt + g, D, E)));
     }
   };
   if (HP) load_tile(pre_row);
@@ -563,8 +563,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
       ox[e] = FP4 ? ((uint32_t)vt[(EPL * lane + e) * (kTile / 2) + rs / 2] >> (4 * (rs & 1))) & 15u
-            : FP8 ? (uint32_t)vt[(EPL * lane + e) * kTile + rs]
-                  : (uint32_t)reinterpret_cast<const uint16_t*>(vt)[(EPL * lane + e) * kTile + rs];
+            : FP8 ? (uint32_t)vt[v_tile_off(rs, EPL * lane + e, D, 1)]
+                  : (uint32_t)*reinterpret_cast<const uint16_t*>(vt + v_tile_off(rs, EPL * lane + e, D, 2));
   }
 
   bool first_tile = true;
@@ -672,9 +672,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
         if (FP4)
           nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
         else if (FP8)
-          st_dev8(vd + (d0n + e) * kTile + rt, (uint8_t)ox[e]);
+          st_dev8(vd + v_tile_off(rt, d0n + e, D, 1), (uint8_t)ox[e]);
         else
-          reinterpret_cast<uint16_t*>(vd)[(d0n + e) * kTile + rt] = (uint16_t)ox[e];
+          *reinterpret_cast<uint16_t*>(vd + v_tile_off(rt, d0n + e, D, 2)) = (uint16_t)ox[e];
       }
     }
     // the new row goes over the ring row: this wave has consumed the tile's
@@ -697,9 +697,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
         if (FP4)   // after the moved row's write, which may share the byte
           nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
         else if (FP8)
-          st_dev8(vt + (d0n + e) * kTile + rs, (uint8_t)(vc >> (8 * e)));
+          st_dev8(vt + v_tile_off(rs, d0n + e, D, 1), (uint8_t)(vc >> (8 * e)));
         else
-          reinterpret_cast<uint16_t*>(vt)[(d0n + e) * kTile + rs] = (uint16_t)(vc >> (16 * e));
+          *reinterpret_cast<uint16_t*>(vt + v_tile_off(rs, d0n + e, D, 2)) =
+              (uint16_t)(vc >> (16 * e));
       }
     }
   };

@@ -50,6 +50,23 @@ __device__ __forceinline__ int64_t k_byte(int64_t row, int byte, int rb) {
   return (row / kTile) * kTile * rb + k_chunk_offset((int)(row % kTile), byte >> 4, rb) + (byte & 15);
 }
 
+// BF16 and FP8 V pool: a 64-row tile is four blocks of 16 rows, each block
+// column-major, so element (r, d) of a tile is at byte
+//   ((r / 16) * D + d) * 16 * e + (r % 16) * e.
+// One lane's 16 consecutive rows of one column (a PV operand) stay one run
+// of 16 * e bytes, and the D values of one row fall in D * 16 * e / 128
+// cache lines instead of one line per 128 / (64 * e) columns.
+__host__ __device__ __forceinline__ int v_tile_off(int r, int d, int D, int e) {
+  return (((r >> 4) * D + d) * 16 + (r & 15)) * e;
+}
+// Column d and first row row0 of the 16-byte run at tile byte vb (a multiple
+// of 16) of such a tile: 16 / e rows of one column.
+__host__ __device__ __forceinline__ void v_tile_run(int vb, int D, int e, int& d, int& row0) {
+  const int blk = vb / (16 * D * e), o = vb - blk * 16 * D * e;
+  d = o / (16 * e);
+  row0 = blk * 16 + (o - d * 16 * e) / e;
+}
+
 // FP4 V pool: 64-row tiles, column-major, two rows per byte: element
 // (row, d) is nibble row & 1 (low for even rows) of this byte.
 __device__ __forceinline__ int64_t v_nib_byte(int64_t row, int d, int D) {

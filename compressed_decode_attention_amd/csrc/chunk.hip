@@ -153,6 +153,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
   constexpr int SPC = FP4 ? 4 : FP8 ? 2 : 1;      // MFMA k-steps per stored 16-byte K chunk
   constexpr int TX = kTile * D * 2;               // bytes of a staged (16-bit) K tile
   constexpr int VP = kTile * 2 + 16;              // bytes per staged V column (padded)
+  constexpr int EV = FP8 ? 1 : 2;                 // bytes per BF16 / FP8 V element
   static_assert(NCH % 64 == 0, "tile copy shape");
 
   // K as bf16 MFMA operands, operand-major: operand (mu, st) of lane l at
@@ -396,8 +397,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
       } else {              // V: column d, rows row0 .. (16 FP8, 32 FP4, 8 BF16)
         const int vb = ch * 16 - TB;
         constexpr int NR = FP8 ? 16 : FP4 ? 32 : 8;
-        const int d = FP8 ? vb / kTile : FP4 ? vb / 32 : (vb / 2) / kTile;
-        const int row0 = FP8 ? vb % kTile : FP4 ? (vb % 32) * 2 : (vb / 2) % kTile;
+        int d = vb / 32, row0 = (vb % 32) * 2;   // FP4: column-major nibbles
+        if (!FP4) v_tile_run(vb, D, EV, d, row0);
         uint32_t v[NR];
 #pragma unroll
         for (int e = 0; e < NR; ++e) {
@@ -488,7 +489,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
             *reinterpret_cast<f16x8*>(dst + 16 * q) = y;
           }
         } else if (FP8) {                        // 16 rows
-          const int d = vb / kTile, row0 = vb % kTile;
+          int d, row0;
+          v_tile_run(vb, D, 1, d, row0);
           uint8_t* dst = s_v + d * VP + row0 * 2;
           f16x8 y0 = fp8x8_to_f16x8(x[0], x[1]), y1 = fp8x8_to_f16x8(x[2], x[3]);
           if (row0 + 16 > valid) {                // rows past the data
@@ -501,7 +503,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
           *reinterpret_cast<f16x8*>(dst) = y0;
           *reinterpret_cast<f16x8*>(dst + 16) = y1;
         } else {                                 // 8 rows, as stored
-          const int d = (vb / 2) / kTile, row0 = (vb / 2) % kTile;
+          int d, row0;
+          v_tile_run(vb, D, 2, d, row0);
           u32x4 y = x;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -798,6 +801,12 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   constexpr int RKPT = CDA_MAX_CHUNK_WINDOW / kBlock;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
+  // the u-th V column of this wave: BF16 / FP8 columns taken in an order
+  // that puts consecutive stores in different cache lines (16 rows of
+  // neighbouring columns share a line of the stored tile); FP4 in order
+  auto vcol = [&](int u) {
+    return FP4 ? wave * DPW + u : wave * DPW + (u % 4) * (DPW / 4) + u / 4;
+  };
   const int W = p.W, M = p.M;
   const uint8_t* ck = p.chunk_k + (int64_t)i * kTile * RB;   // the chunk's encoded rows
   const uint8_t* cv = p.chunk_v + (int64_t)i * kTile * RB;
@@ -857,13 +866,13 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   };
   auto vaddr = [&](uint8_t* pool, int64_t row, int d) {   // V element (row, d); FP4: its byte
     return FP4 ? pool + (row - row % kTile) * RB + d * (kTile / 2) + (row % kTile) / 2
-               : pool + ((row - row % kTile) * D + d * kTile + row % kTile) * E;
+               : pool + (row - row % kTile) * D * E + v_tile_off((int)(row % kTile), d, D, E);
   };
   // V element (row j, column d) of the chunk tile in LDS (FP4: its code)
   auto cvel = [&](int j, int d) -> uint32_t {
     if (FP4) return ((uint32_t)s_cv[d * (kTile / 2) + j / 2] >> (4 * (j & 1))) & 15u;
-    if (E == 2) return *reinterpret_cast<const uint16_t*>(s_cv + (d * kTile + j) * 2);
-    return s_cv[d * kTile + j];
+    if (E == 2) return *reinterpret_cast<const uint16_t*>(s_cv + v_tile_off(j, d, D, 2));
+    return s_cv[v_tile_off(j, d, D, 1)];
   };
 
   __syncthreads();   // s_rk
@@ -928,16 +937,18 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
     if (!want) mk[u] = u32x4{0, 0, 0, 0};
   }
   if (nmove > 0) {
-    // this lane's row: column d at va + d * VS (FP4: the code at bit vsh)
-    constexpr int VS = FP4 ? kTile / 2 : kTile * E;
+    // this lane's row vr of a tile at vt: column d at vt + v_tile_off(vr, d)
+    // (FP4: the byte vt + d * 32 + vr / 2, the code at bit vsh)
     const bool vok = vrow && (vsrc >= 0 || vfrom >= 0);
     const int vr = vsrc >= 0 ? vsrc : (int)(max(vfrom, (int64_t)0) % kTile);
-    const uint8_t* va = (vrow && vsrc < 0 && vfrom >= 0) ? vaddr(v_pool, vfrom, 0)
-                                                         : cv + (FP4 ? vr / 2 : vr * E);
+    const uint8_t* vt = (vrow && vsrc < 0 && vfrom >= 0)
+                            ? v_pool + (vfrom - vfrom % kTile) * RB
+                            : cv;
     const int vsh = FP4 ? 4 * (vr & 1) : 0;
 #pragma unroll
     for (int u = 0; u < DPW; ++u) {
-      const uint8_t* a = va + (wave * DPW + u) * VS;
+      const int d = vcol(u);
+      const uint8_t* a = FP4 ? vt + d * (kTile / 2) + vr / 2 : vt + v_tile_off(vr, d, D, E);
       uint32_t x = E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(a) : (uint32_t)*a;
       if (FP4) x = (x >> vsh) & 15u;
       mv[u] = vok ? x : 0u;
@@ -958,7 +969,7 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   if (nmove > 0 && vrow) {
 #pragma unroll
     for (int u = 0; u < DPW; ++u) {
-      const int d = wave * DPW + u;
+      const int d = vcol(u);
       if (E == 2) *reinterpret_cast<uint16_t*>(s_mv + (d * kTile + lane) * 2) = (uint16_t)mv[u];
       else s_mv[d * kTile + lane] = (uint8_t)mv[u];
     }
@@ -1002,7 +1013,7 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
       bad = 1;
     } else {
       for (int u = 0; u < DPW; ++u) {
-        const int d = wave * DPW + u;
+        const int d = vcol(u);
         uint8_t* dp = vaddr(v_pool, to, d);
         if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + lane) * 2);
         else *dp = s_mv[d * kTile + lane];
@@ -1055,7 +1066,7 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
         bad = 1;
       } else {
         for (int u = 0; u < DPW; ++u) {
-          const int d = wave * DPW + u;
+          const int d = vcol(u);
           uint8_t* dp = vaddr(v_pool, to, d);
           if (E == 2) *reinterpret_cast<uint16_t*>(dp) = (uint16_t)cvel(j0 + lane, d);
           else *dp = (uint8_t)cvel(j0 + lane, d);

@@ -225,9 +225,10 @@ struct PackParams {
   int32_t* err;
 };
 
-// Byte offset of element (row, d) in a V pool of column-major 64-row tiles.
+// Element offset of (row, d) in a BF16 or FP8 V pool (16-row blocks of
+// column-major 64-row tiles; v_tile_off in elements).
 __device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
-  return (row / kTile) * kTile * D + (int64_t)d * kTile + (row % kTile);
+  return (row / kTile) * kTile * D + v_tile_off((int)(row % kTile), d, D, 1);
 }
 
 // Workgroup (segment i, y) writes the 64-row pool tiles j = y, y + gridDim.y,
@@ -438,7 +439,8 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
           }
         } else {              // chunk ch: rows r .. r + 16/E - 1 of column d
           constexpr int E = KV == kKvFP8 ? 1 : 2;
-          const int d = ch / (4 * E), r = (ch % (4 * E)) * (16 / E);
+          int d, r;
+          v_tile_run(ch * 16, D, E, d, r);
           const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * VS + r * E);
           vv = u32x4{src[0], src[1], src[2], src[3]};
         }

@@ -108,7 +108,8 @@ def stored_rows(c) -> torch.Tensor:
 
 def v_rows(c) -> torch.Tensor:
     """The V pool as [pool_rows, row_bytes] bytes in row order (a gather of
-    the column-major tiles; FP4 rows hold element d in the low nibble of
+    the tiles: BF16 and FP8 tiles are four column-major blocks of 16 rows,
+    FP4 tiles column-major; FP4 rows hold element d in the low nibble of
     byte d / 2 for even d)."""
     D, rows = c.D, c.pool_rows
     if c.kv_dtype == "fp4":
@@ -117,8 +118,8 @@ def v_rows(c) -> torch.Tensor:
         codes = codes.permute(0, 2, 1)                                  # [tile, r, d]
         return (codes[..., 0::2] | (codes[..., 1::2] << 4)).reshape(rows, D // 2)
     e = c.row_bytes // D
-    t = c.v_pool[: rows * D * e].view(-1, D, CDA_SEG_ALIGN, e)
-    return t.permute(0, 2, 1, 3).reshape(rows, D * e)
+    t = c.v_pool[: rows * D * e].view(-1, CDA_SEG_ALIGN // 16, D, 16, e)   # [tile, blk, d, r, byte]
+    return t.permute(0, 1, 3, 2, 4).reshape(rows, D * e)
 
 
 def k_rows(c) -> torch.Tensor:
