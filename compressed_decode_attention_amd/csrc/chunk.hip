@@ -53,6 +53,9 @@ constexpr int kWideTarget = 256;     // attention workgroups in all: one per CU
 // call at M = 64 on the Qwen c = 8 layer; 1 is also the best at M = 16.)
 constexpr int kChunkExtra = 1;
 constexpr int kMaxRingTiles = CDA_MAX_CHUNK_WINDOW / kTile;   // chunk commit: ring tiles
+// chunk commit, BF16 / FP8: more rows than this are written a lane per row
+// (a column per store), fewer a row per pass and a lane per column
+constexpr int kRowsByLane = 8;
 
 struct ChunkParams {
   const uint8_t* k_pool;
@@ -770,8 +773,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
 // r then takes the last chunk token that maps to it.  All reads come first,
 // issued together: the chunk's encoded tile whole (16-byte copies) and the
 // moved rows (a lane per row for V), into LDS, so every old ring row is read
-// before any is overwritten.  The writes go a lane per row, so that a wave's
-// V stores fall in one column run of a [d][row] tile.  FP4 V elements share
+// before any is overwritten.  V rows are written a lane per row (a column
+// per store, so a wave's stores fall in one column run), except BF16 and
+// FP8 runs of at most kRowsByLane rows: a row per pass of a wave and a lane
+// per column there (one row's values lie 16 * e bytes apart in its 16-row
+// block, so a store covers 8 lines instead of 8 stores one).  FP4 V elements share
 // a byte between two rows: each byte is written by one thread, keeping the
 // nibble of a row it does not write; the compact and the ring writes go in
 // two rounds because rows W - 1 and W can share a byte.  The last segment of
@@ -1007,16 +1013,40 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
         }
       }
     }
-  } else if (vrow) {
-    const int64_t to = prow(R0 + lane);
-    if (to < 0) {
-      bad = 1;
-    } else {
-      for (int u = 0; u < DPW; ++u) {
-        const int d = vcol(u);
+  } else if (nmove > kRowsByLane) {
+    // BF16 / FP8, many rows: a lane per row, a column per store
+    if (vrow) {
+      const int64_t to = prow(R0 + lane);
+      if (to < 0) {
+        bad = 1;
+      } else {
+        for (int u = 0; u < DPW; ++u) {
+          const int d = vcol(u);
+          uint8_t* dp = vaddr(v_pool, to, d);
+          if (E == 2)
+            *reinterpret_cast<uint16_t*>(dp) =
+                *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + lane) * 2);
+          else
+            *dp = s_mv[d * kTile + lane];
+        }
+      }
+    }
+  } else {
+    // BF16 / FP8, few rows: a moved row per pass of a wave, a lane per
+    // column (one row's values lie 16 * E bytes apart in its 16-row block)
+    for (int k = wave; k < nmove; k += NWV) {
+      const int64_t to = prow(R0 + k);
+      if (to < 0) {
+        bad = 1;
+        continue;
+      }
+      for (int d = lane; d < D; d += 64) {
         uint8_t* dp = vaddr(v_pool, to, d);
-        if (E == 2) *reinterpret_cast<uint16_t*>(dp) = *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + lane) * 2);
-        else *dp = s_mv[d * kTile + lane];
+        if (E == 2)
+          *reinterpret_cast<uint16_t*>(dp) =
+              *reinterpret_cast<const uint16_t*>(s_mv + (d * kTile + k) * 2);
+        else
+          *dp = s_mv[d * kTile + k];
       }
     }
   }
@@ -1060,16 +1090,33 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
           *vaddr(v_pool, base, d) = (uint8_t)byte;
         }
       }
-    } else if (lane < nr) {
-      const int64_t to = prow((P + j0 + lane) % W);
-      if (to < 0) {
-        bad = 1;
-      } else {
-        for (int u = 0; u < DPW; ++u) {
-          const int d = vcol(u);
+    } else if (nr > kRowsByLane) {
+      // BF16 / FP8, many rows: a lane per row, a column per store
+      if (lane < nr) {
+        const int64_t to = prow((P + j0 + lane) % W);
+        if (to < 0) {
+          bad = 1;
+        } else {
+          for (int u = 0; u < DPW; ++u) {
+            const int d = vcol(u);
+            uint8_t* dp = vaddr(v_pool, to, d);
+            if (E == 2) *reinterpret_cast<uint16_t*>(dp) = (uint16_t)cvel(j0 + lane, d);
+            else *dp = (uint8_t)cvel(j0 + lane, d);
+          }
+        }
+      }
+    } else {
+      // BF16 / FP8, few rows: a ring row per pass of a wave, a lane per column
+      for (int j = wave; j < nr; j += NWV) {
+        const int64_t to = prow((P + j0 + j) % W);
+        if (to < 0) {
+          bad = 1;
+          continue;
+        }
+        for (int d = lane; d < D; d += 64) {
           uint8_t* dp = vaddr(v_pool, to, d);
-          if (E == 2) *reinterpret_cast<uint16_t*>(dp) = (uint16_t)cvel(j0 + lane, d);
-          else *dp = (uint8_t)cvel(j0 + lane, d);
+          if (E == 2) *reinterpret_cast<uint16_t*>(dp) = (uint16_t)cvel(j0 + j, d);
+          else *dp = (uint8_t)cvel(j0 + j, d);
         }
       }
     }
