@@ -564,7 +564,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     for (int e = 0; e < EPL; ++e)
       ox[e] = FP4 ? ((uint32_t)vt[(EPL * lane + e) * (kTile / 2) + rs / 2] >> (4 * (rs & 1))) & 15u
             : FP8 ? (uint32_t)vt[v_tile_off(rs, EPL * lane + e, D, 1)]
-                  : (uint32_t)*reinterpret_cast<const uint16_t*>(vt + v_tile_off(rs, EPL * lane + e, D, 2));
+                  : (uint32_t)*reinterpret_cast<const uint16_t*>(
+                        vt + v_tile_off(rs, EPL * lane + e, D, 2));
   }
 
   bool first_tile = true;
@@ -639,8 +640,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
   // (wants_move: it is kept and the compact region has room) and writes the
   // new row over its ring row.  No other workgroup reads the new token's
   // tile, and the compact tail lies past the rows attended in this launch.
-  // FP8 rows go out through agent-scope stores, which write through the L2:
-  // the end of the launch then has none of their lines left to write back.
+  // The moved K chunks, 4-byte K slices and FP8 V bytes go out through
+  // agent-scope stores, which write through the L2: the end of the launch
+  // then has none of their lines left to write back (measured faster).
   auto write_rows = [&](bool wants_move) {
     const int d0n = EPL * lane;
     // the leaving token's row (ring row P mod W) moves to compact row
