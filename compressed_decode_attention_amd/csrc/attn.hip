@@ -48,9 +48,9 @@
 //   S^T[token][g] = K_tile[token][:] . Q^T[:][g]     v_mfma_f32_16x16x32_bf16
 //   O^T[d][g]    += V^T[d][token] . P^T[token][g]    v_mfma_f32_16x16x32_{f16,bf16}
 // K is stored in 64-row tiles permuted so that each 64-lane load of the S
-// operand is 1 KB of consecutive bytes; V is stored in 64-row column-major
-// tiles, so the O operand is 16-byte loads of 8 or 16 consecutive tokens of
-// one column.  Tokens are assigned to MFMA rows so that the S accumulator of
+// operand is 1 KB of consecutive bytes; V is stored in 64-row tiles of four
+// column-major 16-row blocks (FP4: column-major tiles), so the O operand is
+// 16-byte loads of 8 or 16 consecutive tokens of one column.  Tokens are assigned to MFMA rows so that the S accumulator of
 // each lane holds exactly the 16 tokens that lane needs for its P operand,
 // so P never moves between lanes.  FP8 codes are converted to bf16 (K) or
 // f16 (V) in registers, exactly; the K scale is folded into the logit scale

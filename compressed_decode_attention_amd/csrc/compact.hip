@@ -225,8 +225,8 @@ struct PackParams {
   int32_t* err;
 };
 
-// Element offset of (row, d) in a BF16 or FP8 V pool (16-row blocks of
-// column-major 64-row tiles; v_tile_off in elements).
+// Element offset of (row, d) in a BF16 or FP8 V pool (64-row tiles of four
+// column-major 16-row blocks; v_tile_off in elements).
 __device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
   return (row / kTile) * kTile * D + v_tile_off((int)(row % kTile), d, D, 1);
 }
@@ -237,7 +237,8 @@ __device__ __forceinline__ int64_t v_elem(int64_t row, int d, int D) {
 // the position p of the window with p mod W = r; compact row W + c: the
 // c-th kept older position, by a scan of the keep row), loads the BF16 rows
 // (each 64-lane load is whole rows), encodes them into LDS images of the
-// K tile (chunk-permuted rows) and the V tile (column-major), and stores
+// K tile (chunk-permuted rows) and the V tile (column-major; stored in the
+// pool's 16-row blocks, FP4 column-major), and stores
 // both with 16-byte writes.  Rows of the tile with no source are zero.
 // The V image holds one byte per element (an FP4 code in its low nibble);
 // FP4 tiles are packed two rows per byte on the way out.
