@@ -19,7 +19,7 @@ CDA_KV_BF16, CDA_KV_FP8_E4M3, CDA_KV_FP4_E2M1 = 0, 1, 2
 CDA_OUT_BF16, CDA_OUT_F32 = 0, 1
 CDA_OP_COUNT, CDA_OP_PACK, CDA_OP_APPEND = 0, 1, 2
 CDA_OP_PAGE_INIT, CDA_OP_REFILL, CDA_OP_RELEASE = 3, 4, 5
-CDA_VERSION = 6       # the struct layouts below are those of this version
+CDA_VERSION = 7       # the struct layouts below are those of this version
 CDA_SCRATCH_BYTES = 4 << 20   # device scratch of decode_step_compact_noalloc, per GPU
 CDA_SEG_ALIGN = 64
 CDA_MAX_GQA = 16

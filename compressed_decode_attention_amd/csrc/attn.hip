@@ -454,7 +454,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         vq[nt] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-            vtile + (16 * nt + g) * (kTile / 2) + 8 * kg));
+            vtile + v_nib_off(16 * kg, 16 * nt + g, D)));
     } else {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
     okx = *reinterpret_cast<const u32x4*>(kt + k_chunk_offset(rs, min(lane, RB / 16 - 1), RB));
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
-      ox[e] = FP4 ? ((uint32_t)vt[(EPL * lane + e) * (kTile / 2) + rs / 2] >> (4 * (rs & 1))) & 15u
+      ox[e] = FP4 ? ((uint32_t)vt[v_nib_off(rs, EPL * lane + e, D)] >> (4 * (rs & 1))) & 15u
             : FP8 ? (uint32_t)vt[v_tile_off(rs, EPL * lane + e, D, 1)]
                   : (uint32_t)*reinterpret_cast<const uint16_t*>(
                         vt + v_tile_off(rs, EPL * lane + e, D, 2));
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         if (FP4)
-          nib_store(vd + (d0n + e) * (kTile / 2) + rt / 2, rt & 1, ox[e]);
+          nib_store(vd + v_nib_off(rt, d0n + e, D), rt & 1, ox[e]);
         else if (FP8)
           st_dev8(vd + v_tile_off(rt, d0n + e, D, 1), (uint8_t)ox[e]);
         else
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         if (FP4)   // after the moved row's write, which may share the byte
-          nib_store(vt + (d0n + e) * (kTile / 2) + rs / 2, rs & 1, (vc >> (4 * e)) & 15u);
+          nib_store(vt + v_nib_off(rs, d0n + e, D), rs & 1, (vc >> (4 * e)) & 15u);
         else if (FP8)
           st_dev8(vt + v_tile_off(rs, d0n + e, D, 1), (uint8_t)(vc >> (8 * e)));
         else

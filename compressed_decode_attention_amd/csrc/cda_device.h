@@ -67,10 +67,15 @@ __host__ __device__ __forceinline__ void v_tile_run(int vb, int D, int e, int& d
   row0 = blk * 16 + (o - d * 16 * e) / e;
 }
 
-// FP4 V pool: 64-row tiles, column-major, two rows per byte: element
-// (row, d) is nibble row & 1 (low for even rows) of this byte.
+// FP4 V pool: the same 16-row blocks, two rows per byte: element (r, d) of
+// a tile is nibble r & 1 (low for even rows) of tile byte
+//   ((r / 16) * D + d) * 8 + (r % 16) / 2.
+__host__ __device__ __forceinline__ int v_nib_off(int r, int d, int D) {
+  return ((r >> 4) * D + d) * 8 + ((r & 15) >> 1);
+}
+// The pool byte of element (row, d).
 __device__ __forceinline__ int64_t v_nib_byte(int64_t row, int d, int D) {
-  return (row / kTile) * kTile * (D / 2) + (int64_t)d * (kTile / 2) + (row % kTile) / 2;
+  return (row / kTile) * kTile * (D / 2) + v_nib_off((int)(row % kTile), d, D);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

@@ -397,16 +397,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
           x = *reinterpret_cast<const u32x4*>(src);
         }
         if (r >= M) x = u32x4{0, 0, 0, 0};
-      } else {              // V: column d, rows row0 .. (16 FP8, 32 FP4, 8 BF16)
+      } else {              // V: column d, rows row0 .. (16 FP8, 8 BF16; FP4 16 of 2 columns)
         const int vb = ch * 16 - TB;
         constexpr int NR = FP8 ? 16 : FP4 ? 32 : 8;
-        int d = vb / 32, row0 = (vb % 32) * 2;   // FP4: column-major nibbles
+        // FP4: rows row0 .. row0 + 15 of columns d and d + 1 (v[16 + e])
+        int d = 2 * ((vb % (8 * D)) / 16), row0 = 16 * (vb / (8 * D));
         if (!FP4) v_tile_run(vb, D, EV, d, row0);
         uint32_t v[NR];
 #pragma unroll
         for (int e = 0; e < NR; ++e) {
-          const uint32_t raw = p.v_new[nb0 + (int64_t)min(row0 + e, M - 1) * p.nst + d];
-          v[e] = row0 + e < M ? raw : 0u;
+          const int re = FP4 ? row0 + (e & 15) : row0 + e, de = FP4 ? d + (e >> 4) : d;
+          const uint32_t raw = p.v_new[nb0 + (int64_t)min(re, M - 1) * p.nst + de];
+          v[e] = re < M ? raw : 0u;
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -478,18 +480,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void chunk_attn_wide_kernel(ChunkP
         }
       } else {                                   // V: rows row0 .. of column d
         const int vb = ch * 16 - TB;             // byte of the stored V tile
-        if (FP4) {                               // 32 rows
-          const int d = vb / 32, row0 = (vb % 32) * 2;
-          uint8_t* dst = s_v + d * VP + row0 * 2;
+        if (FP4) {                               // 16 rows of columns d and d + 1
+          const int d = 2 * ((vb % (8 * D)) / 16), row0 = 16 * (vb / (8 * D));
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            const int r = row0 + 8 * (q & 1);
             f16x8 y = fp4x8_to_f16x8(x[q]);
-            if (row0 + 8 * q + 8 > valid) {       // rows past the data
+            if (r + 8 > valid) {                  // rows past the data
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                if (row0 + 8 * q + e >= valid) y[e] = (_Float16)0.0f;
+                if (r + e >= valid) y[e] = (_Float16)0.0f;
             }
-            *reinterpret_cast<f16x8*>(dst + 16 * q) = y;
+            *reinterpret_cast<f16x8*>(s_v + (d + (q >> 1)) * VP + r * 2) = y;
           }
         } else if (FP8) {                        // 16 rows
           int d, row0;
@@ -871,12 +873,12 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
     return pool + (row - row % kTile) * RB + k_chunk_offset((int)(row % kTile), c, RB);
   };
   auto vaddr = [&](uint8_t* pool, int64_t row, int d) {   // V element (row, d); FP4: its byte
-    return FP4 ? pool + (row - row % kTile) * RB + d * (kTile / 2) + (row % kTile) / 2
+    return FP4 ? pool + (row - row % kTile) * RB + v_nib_off((int)(row % kTile), d, D)
                : pool + (row - row % kTile) * D * E + v_tile_off((int)(row % kTile), d, D, E);
   };
   // V element (row j, column d) of the chunk tile in LDS (FP4: its code)
   auto cvel = [&](int j, int d) -> uint32_t {
-    if (FP4) return ((uint32_t)s_cv[d * (kTile / 2) + j / 2] >> (4 * (j & 1))) & 15u;
+    if (FP4) return ((uint32_t)s_cv[v_nib_off(j, d, D)] >> (4 * (j & 1))) & 15u;
     if (E == 2) return *reinterpret_cast<const uint16_t*>(s_cv + v_tile_off(j, d, D, 2));
     return s_cv[v_tile_off(j, d, D, 1)];
   };
@@ -944,7 +946,7 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   }
   if (nmove > 0) {
     // this lane's row vr of a tile at vt: column d at vt + v_tile_off(vr, d)
-    // (FP4: the byte vt + d * 32 + vr / 2, the code at bit vsh)
+    // (FP4: the byte vt + v_nib_off(vr, d), the code at bit vsh)
     const bool vok = vrow && (vsrc >= 0 || vfrom >= 0);
     const int vr = vsrc >= 0 ? vsrc : (int)(max(vfrom, (int64_t)0) % kTile);
     const uint8_t* vt = (vrow && vsrc < 0 && vfrom >= 0)
@@ -954,7 +956,7 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
 #pragma unroll
     for (int u = 0; u < DPW; ++u) {
       const int d = vcol(u);
-      const uint8_t* a = FP4 ? vt + d * (kTile / 2) + vr / 2 : vt + v_tile_off(vr, d, D, E);
+      const uint8_t* a = FP4 ? vt + v_nib_off(vr, d, D) : vt + v_tile_off(vr, d, D, E);
       uint32_t x = E == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(a) : (uint32_t)*a;
       if (FP4) x = (x >> vsh) & 15u;
       mv[u] = vok ? x : 0u;
@@ -990,7 +992,27 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
     if (to < 0) { bad = 1; continue; }
     *reinterpret_cast<u32x4*>(kaddr(k_pool, to, c)) = *reinterpret_cast<const u32x4*>(s_mk + k * RB + 16 * c);
   }
-  if (FP4) {
+  if (FP4 && W % 2 == 0 && nmove <= kRowsByLane) {
+    // few rows (and no byte shared with a ring row): a byte (rows 2q,
+    // 2q + 1) per pass of a wave, a lane per column
+    const int q0 = R0 / 2, nq = nmove > 0 ? (R1 - 1) / 2 - q0 + 1 : 0;
+    for (int x = wave; x < nq; x += NWV) {
+      const int q = q0 + x;
+      const int64_t base = prow(2 * q);        // both rows of a byte share a page
+      const bool lo_in = 2 * q >= R0, hi_in = 2 * q + 1 < R1;
+      if (base < 0) {
+        bad = 1;
+        continue;
+      }
+      for (int d = lane; d < D; d += 64) {
+        uint8_t* bp = vaddr(v_pool, base, d);
+        uint32_t byte = (lo_in && hi_in) ? 0u : (uint32_t)*bp;
+        if (lo_in) byte = (byte & 0xF0u) | s_mv[d * kTile + (2 * q - R0)];
+        if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_mv[d * kTile + (2 * q + 1 - R0)] << 4);
+        *bp = (uint8_t)byte;
+      }
+    }
+  } else if (FP4) {
     // byte q0 + lane (rows 2q, 2q + 1), one per lane
     const int q0 = R0 / 2, nq = nmove > 0 ? (R1 - 1) / 2 - q0 + 1 : 0;
     if (lane < nq) {
@@ -1071,7 +1093,25 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
       int qa = rs / 2;
       if (nq2 > 0 && (n2 - 1) / 2 == qa) ++qa;
       const int nq1 = (rs + n1 - 1) / 2 - qa + 1;
-      for (int x = lane; x < nq2 + nq1; x += 64) {
+      // few bytes (and none shared with a compact row): a byte per pass of a
+      // wave, a lane per column; else a lane per byte, a column per store
+      const bool by_col = W % 2 == 0 && nq2 + nq1 <= kRowsByLane / 2;
+      for (int x = wave; by_col && x < nq2 + nq1; x += NWV) {
+        const int q = x < nq2 ? x : qa + (x - nq2);
+        const int off0 = (2 * q - rs + W) % W, off1 = (2 * q + 1 - rs + W) % W;
+        const bool lo_in = off0 < nr, hi_in = 2 * q + 1 < W && off1 < nr;
+        if (!lo_in && !hi_in) continue;
+        const int64_t base = prow(2 * q);
+        if (base < 0) { bad = 1; continue; }
+        for (int d = lane; d < D; d += 64) {
+          uint8_t* bp = vaddr(v_pool, base, d);
+          uint32_t byte = (lo_in && hi_in) ? 0u : (uint32_t)*bp;
+          if (lo_in) byte = (byte & 0xF0u) | cvel(j0 + off0, d);
+          if (hi_in) byte = (byte & 0x0Fu) | (cvel(j0 + off1, d) << 4);
+          *bp = (uint8_t)byte;
+        }
+      }
+      for (int x = lane; !by_col && x < nq2 + nq1; x += 64) {
         const int q = x < nq2 ? x : qa + (x - nq2);
         const int off0 = (2 * q - rs + W) % W, off1 = (2 * q + 1 - rs + W) % W;
         const bool lo_in = off0 < nr, hi_in = 2 * q + 1 < W && off1 < nr;

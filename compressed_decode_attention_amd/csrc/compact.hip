@@ -428,12 +428,13 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackParams p) {
       for (int ch = tid; ch < kTile * RB / 16; ch += kBlock) {
         *reinterpret_cast<u32x4*>(kt + ch * 16) = *reinterpret_cast<const u32x4*>(s_k + ch * 16);
         u32x4 vv;
-        if (KV == kKvFP4) {   // chunk ch: rows r .. r + 31 of column d, two per byte
-          const int d = ch >> 1, r = (ch & 1) * 32;
-          const uint32_t* src = reinterpret_cast<const uint32_t*>(s_v + d * VS + r);
+        if (KV == kKvFP4) {   // chunk ch: rows r .. r + 15 of columns d and d + 1, two per byte
+          const int blk = ch / (D / 2), d = 2 * (ch % (D / 2)), r = 16 * blk;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t a = src[2 * q], c = src[2 * q + 1];   // one code per byte
+            const uint32_t* src =
+                reinterpret_cast<const uint32_t*>(s_v + (d + (q >> 1)) * VS + r + 8 * (q & 1));
+            const uint32_t a = src[0], c = src[1];   // one code per byte
             const uint32_t lo = (a & 0xFu) | ((a >> 4) & 0xF0u) | ((a >> 8) & 0xF00u) | ((a >> 12) & 0xF000u);
             const uint32_t hi = (c & 0xFu) | ((c >> 4) & 0xF0u) | ((c >> 8) & 0xF00u) | ((c >> 12) & 0xF000u);
             vv[q] = lo | (hi << 16);

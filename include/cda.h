@@ -49,14 +49,12 @@
  *       m = (r / 4) % 4,  g = (r / 16) * 4 + r % 4,
  *     so that every 1 KB of a tile is what one 64-lane load of the attention
  *     kernel needs (the rows of a tile are a permutation of its bytes).
- *   v_pool (BF16, FP8): a tile is four blocks of 16 rows, each block stored
+ *   v_pool: a tile is four blocks of 16 rows, each block stored
  *     column-major: element (r, d) at byte
  *       (r / 64) * 64 * D * e + (((r % 64) / 16) * D + d) * 16 * e + (r % 16) * e,
  *     so that 16 consecutive rows of one column are contiguous and the D
- *     values of one row lie in D * 16 * e bytes.
- *   v_pool (FP4): tiles stored column-major: element (r, d) in byte
- *     (r / 64) * 32 * D + d * 32 + (r % 64) / 2, the low nibble for even r,
- *     the high nibble for odd r.
+ *     values of one row lie in D * 16 * e bytes (FP4, e = 1/2: the low
+ *     nibble of that byte for even r, the high nibble for odd r).
  *   FP4 elements of a K row: element d is the low nibble of row byte d / 2
  *     when d is even, the high nibble when odd.
  *   FP8: code = E4M3FN_RNE_SATURATE(f32(x) * inv), inv = 448 / amax and
@@ -114,7 +112,7 @@
 extern "C" {
 #endif
 
-#define CDA_VERSION 6
+#define CDA_VERSION 7
 #define CDA_SEG_ALIGN 64        /* rows; segment sizes are rounded up to this */
 #define CDA_MAX_GQA 16          /* largest Hq / Hkv supported */
 #define CDA_SCRATCH_BYTES (4u << 20) /* device scratch of decode_step_compact_noalloc, per GPU */
@@ -172,7 +170,7 @@ typedef struct cda_kv_cache {
                            (a wrong hint costs time, never correctness) */
     int64_t pool_rows;  /* rows allocated in k_pool and v_pool (multiple of 64) */
     void *k_pool;       /* [pool_rows / 64] tiles of 64 x D, chunk-permuted (see above) */
-    void *v_pool;       /* [pool_rows / 64][4][D][16] (FP4: [pool_rows / 64][D][32 bytes]) */
+    void *v_pool;       /* [pool_rows / 64][4][D][16 rows] */
     int64_t *seg_base;  /* [B*Hkv + 1]; written by COUNT; [B*Hkv] = rows needed */
     int32_t *seg_cap;   /* [B*Hkv]; written by COUNT */
     int32_t *comp_len;  /* [B*Hkv]; written by COUNT, grown by APPEND */

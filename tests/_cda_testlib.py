@@ -108,14 +108,14 @@ def stored_rows(c) -> torch.Tensor:
 
 def v_rows(c) -> torch.Tensor:
     """The V pool as [pool_rows, row_bytes] bytes in row order (a gather of
-    the tiles: BF16 and FP8 tiles are four column-major blocks of 16 rows,
-    FP4 tiles column-major; FP4 rows hold element d in the low nibble of
-    byte d / 2 for even d)."""
+    the tiles: four column-major blocks of 16 rows, two rows per byte for
+    FP4; FP4 rows hold element d in the low nibble of byte d / 2 for even
+    d)."""
     D, rows = c.D, c.pool_rows
     if c.kv_dtype == "fp4":
-        t = c.v_pool[: rows * D // 2].view(-1, D, CDA_SEG_ALIGN // 2)   # [tile, d, byte]
-        codes = torch.stack([t & 15, t >> 4], dim=-1).reshape(-1, D, CDA_SEG_ALIGN)
-        codes = codes.permute(0, 2, 1)                                  # [tile, r, d]
+        t = c.v_pool[: rows * D // 2].view(-1, CDA_SEG_ALIGN // 16, D, 8)   # [tile, blk, d, byte]
+        codes = torch.stack([t & 15, t >> 4], dim=-1).reshape(-1, CDA_SEG_ALIGN // 16, D, 16)
+        codes = codes.permute(0, 1, 3, 2).reshape(-1, CDA_SEG_ALIGN, D)   # [tile, r, d]
         return (codes[..., 0::2] | (codes[..., 1::2] << 4)).reshape(rows, D // 2)
     e = c.row_bytes // D
     t = c.v_pool[: rows * D * e].view(-1, CDA_SEG_ALIGN // 16, D, 16, e)   # [tile, blk, d, r, byte]

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.version() == lib.CDA_VERSION == 6
+    assert lib.version() == lib.CDA_VERSION == 7
     assert lib.status_string(0) == "ok"
     assert lib.status_string(3) == "workspace too small"
     assert lib.status_string(99) == "unknown status"
