@@ -809,11 +809,11 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
   constexpr int RKPT = CDA_MAX_CHUNK_WINDOW / kBlock;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = i / p.Hkv, h = i - b * p.Hkv;
-  // the u-th V column of this wave: BF16 / FP8 columns taken in an order
-  // that puts consecutive stores in different cache lines (16 rows of
-  // neighbouring columns share a line of the stored tile); FP4 in order
+  // the u-th V column of this wave, in an order that puts consecutive
+  // stores in different cache lines (the 16-row runs of neighbouring
+  // columns share a line of the stored tile)
   auto vcol = [&](int u) {
-    return FP4 ? wave * DPW + u : wave * DPW + (u % 4) * (DPW / 4) + u / 4;
+    return wave * DPW + (u % 4) * (DPW / 4) + u / 4;
   };
   const int W = p.W, M = p.M;
   const uint8_t* ck = p.chunk_k + (int64_t)i * kTile * RB;   // the chunk's encoded rows
@@ -1024,10 +1024,10 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
       } else {
         uint32_t old[DPW];   // the bytes first, all loads together
 #pragma unroll
-        for (int u = 0; u < DPW; ++u) old[u] = *vaddr(v_pool, base, wave * DPW + u);
+        for (int u = 0; u < DPW; ++u) old[u] = *vaddr(v_pool, base, vcol(u));
 #pragma unroll
         for (int u = 0; u < DPW; ++u) {
-          const int d = wave * DPW + u;
+          const int d = vcol(u);
           uint32_t byte = (lo_in && hi_in) ? 0u : old[u];
           if (lo_in) byte = (byte & 0xF0u) | s_mv[d * kTile + (2 * q - R0)];
           if (hi_in) byte = (byte & 0x0Fu) | ((uint32_t)s_mv[d * kTile + (2 * q + 1 - R0)] << 4);
@@ -1120,10 +1120,10 @@ __device__ __forceinline__ void chunk_commit(const ChunkParams& p, int i, uint8_
         if (base < 0) { bad = 1; continue; }
         uint32_t old[DPW];   // the bytes first, all loads together
 #pragma unroll
-        for (int u = 0; u < DPW; ++u) old[u] = *vaddr(v_pool, base, wave * DPW + u);
+        for (int u = 0; u < DPW; ++u) old[u] = *vaddr(v_pool, base, vcol(u));
 #pragma unroll
         for (int u = 0; u < DPW; ++u) {
-          const int d = wave * DPW + u;
+          const int d = vcol(u);
           uint32_t byte = (lo_in && hi_in) ? 0u : old[u];
           if (lo_in) byte = (byte & 0xF0u) | cvel(j0 + off0, d);
           if (hi_in) byte = (byte & 0x0Fu) | (cvel(j0 + off1, d) << 4);
