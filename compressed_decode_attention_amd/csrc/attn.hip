@@ -99,8 +99,8 @@
 namespace cda {
 namespace {
 
-constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge (4 for up
-                                      // to 4 units, x2 past 8)
+constexpr int kMergeBatch = 8;        // partials loaded per round trip in the merge (2, 4 or 6
+                                      // for up to that many units, x2 past 8)
 constexpr int kCounterStride = 32;    // ints between counters: one 128-byte line each
 constexpr int kMergePolls = 1 << 20;  // polls of one batch of partials before giving up
 constexpr int kMaxPlanUnits = 512;    // units a host plan carries in the kernel arguments (4 KB)
@@ -991,7 +991,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
       // word has arrived (the whole wave together, so that no lane reads a
       // word another lane has already cleared)
       bool late = false;
-      // batches of 4 units when the segment has at most 4, of 8 up to 8,
+      // batches of 2, 4, 6 or 8 units for segments of at most that many,
       // else of 16 (one round trip instead of two; fewer units do not pay
       // for the loads and the folds of a larger batch)
       auto merge = [&](auto mb) __attribute__((always_inline)) {
@@ -1053,7 +1053,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnParams p, PlanArg<HP>
         }
       }
       };
-      if (U <= 4) merge(std::integral_constant<int, 4>{});
+      if (U <= 2) merge(std::integral_constant<int, 2>{});
+      else if (U <= 4) merge(std::integral_constant<int, 4>{});
+      else if (U <= 6) merge(std::integral_constant<int, 6>{});
       else if (U <= kMergeBatch) merge(std::integral_constant<int, kMergeBatch>{});
       else merge(std::integral_constant<int, 2 * kMergeBatch>{});
       if (late) atomicOr(p.err, CDA_DEVERR_MERGE);
