@@ -37,3 +37,19 @@ def test_stored_rows_and_bytes_match_the_oracle_store(W, kv):
     assert got["dense_bf16_bytes"] == oracle.dense_kv_bytes(1, B * Hkv, D, T + S, 2)
     same = oracle.dense_kv_bytes(1, B * Hkv, D, T + S, oracle.bytes_per_elem(DT[kv]))
     assert abs(got["vs_dense_same_dtype"] - same / got["compact_kv_bytes"]) < 1e-3
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """The benchmark measures one device: asked for several (by flag or by a
+    launcher's WORLD_SIZE) it exits with status 2 and says so, before any
+    device work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv],
+                       env={**os.environ, **env}, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
