@@ -311,3 +311,26 @@ def test_noalloc_step_validates_before_any_hip_call(lib):
     a.op = lib.CDA_OP_COUNT
     assert L.decode_step_compact_noalloc(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0,
                                          None) == 1
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="needs a host without a GPU: with one, these fake pointers would "
+                           "reach a kernel")
+def test_failed_hip_call_returns_err_hip(lib):
+    """Arguments that pass every host check, on a host where the HIP runtime
+    finds no device: each entry point returns CDA_ERR_HIP (the status of a
+    failed HIP call or launch) rather than aborting."""
+    L = lib.load()
+    a = lib.CdaCompactArgs()
+    a.op, a.keep, a.k, a.v = lib.CDA_OP_APPEND, 0x100000, 0x100000, 0x100000
+    q = out = C.c_void_p(0x100000)
+    c = _cache(lib)
+    need = L.cda_attn_workspace_bytes(C.byref(c), 8, 0)
+    ws = C.c_void_p(0x200000)
+    assert L.kv_compact(C.byref(c), C.byref(a), None) == lib.CDA_ERR_HIP
+    assert L.decode_attn_compact(C.byref(c), q, 8, 0.0, out, 0, None, 0, ws, C.c_size_t(need),
+                                 None) == lib.CDA_ERR_HIP
+    assert L.decode_step_compact(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0, ws,
+                                 C.c_size_t(need), None) == lib.CDA_ERR_HIP
+    assert L.decode_step_compact_noalloc(C.byref(c), C.byref(a), q, 8, 0.0, out, 0, None, 0,
+                                         None) == lib.CDA_ERR_HIP
